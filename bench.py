@@ -1,0 +1,309 @@
+"""Benchmark of the gfx950 dense GEMM library on one MI355X.
+
+One step = one C = A x B on the headline workload (M = N = K = 8192, BF16
+inputs drawn from N(0,1) with a fixed seed, FP32 accumulation and output),
+with A, B and C resident in HBM before the timed region.  W untimed warm-up
+steps, then K timed steps between HIP events on the stream the library
+launches on; the line reports the mean time per step and TFLOP/s = 2MNK/t.
+
+Printed on stdout as one JSON line; progress goes to stderr.  Besides the
+headline it carries:
+  roofline      the dominant kernel against the MI355X dense BF16 matrix peak,
+                with HBM traffic from the committed rocprofv3 counter summary
+                (null once the kernel sources differ from the profiled ones);
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample of the
+                same workload (whole rows of C), with the GPU rows checked
+                against it;
+  by_workload   the other workloads (1024^3, 2048^3, 4096^3; FP32, FP16, BF16)
+                and the naive one-work-item-per-output kernel at 1024^3.
+
+`--gpus N` with N > 1 exits with an error: the library runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOPS (2MNK/s) and % of MI355X peak at M=N=K=1024/2048/8192"
+# MI355X datasheet peaks (dense): 256 CUs x 2.4 GHz x FLOP/clock/CU
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+EXTRA = ["c1-f32-1024", "c1-f32-1024-int", "c2-f16-1024", "c3-f16-2048", "c3-bf16-2048",
+         "c3r-f16-2050x2047x2056", "c4f-f32-4096"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the library sources; counter-derived traffic is only valid for this hash."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_16_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+class Problem:
+    """Device-resident operands of one workload and a launcher for it."""
+
+    def __init__(self, w, variant=-1, config=-1):
+        import torch
+        import dense_gemm_16_amd as mg
+        from dense_gemm_16_amd import inputs
+        self.w, self.mg = w, mg
+        self.A, self.B = w.make()
+        self.dA, self.dB = self.A.cuda(), self.B.cuda()
+        self.C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        self.code = inputs.DTYPE_CODES[w.dtype]
+        st, v, c = mg.migemm_select(w.M, w.N, w.K, self.code, self.dA.data_ptr(), w.K,
+                                    self.dB.data_ptr(), w.N, self.C.data_ptr(), w.N)
+        if variant < 0:
+            self.variant, self.config = v, c
+        else:
+            self.variant = variant
+            self.config = config if config >= 0 else (c if v == variant else 0)
+        self.stream = torch.cuda.current_stream()
+        self.sp = self.stream.cuda_stream
+        self.args = (self.variant, self.config, w.M, w.N, w.K, self.code, self.dA.data_ptr(), w.K,
+                     self.dB.data_ptr(), w.N, self.C.data_ptr(), w.N, self.sp)
+
+    def kernel_name(self):
+        return (f"{self.mg.migemm_variant_name(self.variant)}["
+                f"{self.mg.migemm_config_name(self.variant, self.config)}]")
+
+    def launch(self):
+        st = self.mg.migemm_gemm_variant(*self.args)
+        if st != self.mg.OK:
+            raise RuntimeError(f"{self.w.name}: {self.mg.migemm_status_string(st)} "
+                               f"(hip {self.mg.migemm_last_hip_error()})")
+
+    def time(self, steps, warmup):
+        import torch
+        for _ in range(warmup):
+            self.launch()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(steps):
+            self.launch()
+        t1.record(self.stream)
+        t1.synchronize()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def time_window(self, min_ms=50.0, lo=20, hi=2000):
+        """Mean ms per launch over a window of at least min_ms (lo..hi launches)."""
+        est = self.time(3, 2)
+        n = int(min(hi, max(lo, min_ms / max(est, 1e-4))))
+        return self.time(n, 0), n
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it still applies."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    e = t.get("entries", {}).get(workload)
+    if not e:
+        return None, "workload not profiled"
+    if e.get("source_hash") != source_hash() or e.get("kernel") != kernel:
+        return None, "kernel changed since the counters were taken"
+    return e["hbm_bytes_per_launch"], e.get("note", "")
+
+
+def cpu_baseline(p, seconds):
+    """Time the CPU oracle on whole rows of C and check the GPU's rows against it."""
+    import numpy as np
+    import oracle
+    from oracle.check import compare, tolerance
+    from dense_gemm_16_amd import inputs
+    w = p.w
+    bA, bB = inputs.to_bits(p.A), inputs.to_bits(p.B)
+    thr = oracle.default_threads()
+    used = oracle.threads_used(thr)
+    r0 = max(used, 8)
+    t = time.perf_counter()
+    oracle.gemm(bA[:r0], bB, p.code, nthreads=thr)
+    t_cal = time.perf_counter() - t
+    rows = int(min(w.M, max(r0, r0 * seconds / max(t_cal, 1e-3))))
+    rows = max(used, (rows // used) * used) if rows >= used else rows
+    log(f"cpu_baseline: calibration {r0} rows in {t_cal:.2f}s -> sample {rows} rows")
+    t = time.perf_counter()
+    ref, S = oracle.gemm(bA[:rows], bB, p.code, nthreads=thr)
+    dt = time.perf_counter() - t
+    flop = 2.0 * rows * w.N * w.K
+    got = p.C[:rows].cpu().numpy()
+    chk = compare(got, ref, S, tol=None if w.exact else tolerance(p.code), exact=w.exact)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": flop / dt / 1e12, "unit": "TFLOPS", "cores": used, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N} outputs, K={w.K}), "
+                      f"fp64 ascending-k sums over the same {w.dtype} inputs; {dt:.1f} s",
+            "seconds": round(dt, 3), "cpu_model": cpu_model,
+            "gpu_rows_vs_oracle": str(chk), "gpu_rows_ok": bool(chk.ok)}
+
+
+def device_info():
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""),
+            "cus": pr.multi_processor_count,
+            "hbm_gib": round(pr.total_memory / 2 ** 30, 1)}
+
+
+def profile_pass(p, reps):
+    """Untimed launches for rocprofv3 counter runs: a plain 1 GiB copy (the counter
+    calibration kernel: 1 GiB read, 1 GiB written) then the GEMM `reps` times."""
+    import torch
+    n = 1 << 28  # 2^28 floats = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        p.launch()
+    torch.cuda.synchronize()
+    log(f"profile pass: 3 x copy of {n * 4} bytes, {reps} x {p.kernel_name()}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4-bf16-8192")
+    ap.add_argument("--variant", type=int, default=-1)
+    ap.add_argument("--config", type=int, default=-1)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every configuration of every variant on the workload")
+    ap.add_argument("--profile-pass", type=int, default=0, metavar="REPS",
+                    help="only run the copy calibration and REPS launches (for rocprofv3)")
+    a = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {a.gpus} (WORLD_SIZE={world}) "
+              "is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_gemm_16_amd as mg
+    from dense_gemm_16_amd import inputs
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    mg.lib()  # fail loudly if the library is missing
+
+    w = inputs.WORKLOADS[a.workload]
+    log(f"bench: generating {w.name} inputs")
+    p = Problem(w, a.variant, a.config)
+    if a.profile_pass:
+        profile_pass(p, a.profile_pass)
+        return
+
+    log(f"bench: {w.name} on {p.kernel_name()}, warmup {a.warmup}, steps {a.steps}")
+    ms = p.time(a.steps, a.warmup)
+    tflops = w.flop / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"bench: {ms:.4f} ms/step, {tflops:.1f} TFLOPS ({100 * tflops / peak:.1f}% of {peak})")
+
+    traffic, tnote = traffic_for(p.kernel_name(), w.name)
+    roof = {"bound": "mfma", "kernel": p.kernel_name(), "achieved": round(tflops, 2),
+            "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+            "traffic": traffic, "traffic_note": tnote,
+            "algorithmic_flop_per_launch": w.flop,
+            "compulsory_bytes_per_launch": w.compulsory_bytes()}
+    if traffic:
+        roof["traffic_gbs"] = round(traffic / (ms * 1e-3) / 1e9, 1)
+        roof["traffic_frac_of_hbm_peak"] = round(traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+    sweep = {}
+    if a.sweep:
+        for v in range(mg.migemm_variant_count()):
+            if not mg.migemm_variant_supports(v, p.code) or v == mg.NAIVE and w.flop > 5e10:
+                continue
+            for c in range(mg.migemm_config_count(v)):
+                q = Problem.__new__(Problem)
+                q.__dict__.update(p.__dict__)
+                q.variant, q.config = v, c
+                q.args = (v, c) + p.args[2:]
+                t, n = q.time_window()
+                sweep[q.kernel_name()] = round(w.flop / (t * 1e-3) / 1e12, 2)
+                log(f"sweep {q.kernel_name()}: {sweep[q.kernel_name()]} TFLOPS")
+
+    extra = {}
+    if not a.no_extra:
+        for name in EXTRA:
+            wx = inputs.WORKLOADS[name]
+            px = Problem(wx)
+            t, n = px.time_window()
+            tf = wx.flop / (t * 1e-3) / 1e12
+            extra[name] = {"tflops": round(tf, 2), "ms": round(t, 5), "launches": n,
+                           "frac_of_peak": round(tf / PEAK_TFLOPS[wx.dtype], 4),
+                           "kernel": px.kernel_name()}
+            log(f"extra {name}: {tf:.1f} TFLOPS on {px.kernel_name()}")
+            if name == "c1-f32-1024":
+                pn = Problem(wx, mg.NAIVE, 0)
+                t, n = pn.time_window()
+                tf = wx.flop / (t * 1e-3) / 1e12
+                extra[name + "/naive"] = {"tflops": round(tf, 2), "ms": round(t, 5),
+                                          "launches": n,
+                                          "frac_of_peak": round(tf / PEAK_TFLOPS["f32"], 4),
+                                          "kernel": pn.kernel_name()}
+                log(f"extra {name}/naive: {tf:.2f} TFLOPS")
+            del px
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        # re-run once so C holds this workload's product for the row check
+        p.launch()
+        torch.cuda.synchronize()
+        cpu = cpu_baseline(p, a.cpu_seconds)
+        log(f"cpu_baseline: {cpu['value'] * 1e3:.2f} GFLOPS on {cpu['cores']} threads; "
+            f"GPU rows {cpu['gpu_rows_vs_oracle']}")
+
+    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+           "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": "synthetic",
+           "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "inputs": w.dtype,
+                      "accumulate": "f32", "output": "f32", "distribution": w.dist,
+                      "seed": w.seed, "layout": "row-major, dense leading dimensions",
+                      "parallelism": "single GPU"},
+           "frac_of_peak": round(tflops / peak, 4), "peak_tflops": peak,
+           "roofline": roof, "cpu_baseline": cpu, "by_workload": extra,
+           "device": device_info(), "source_hash": source_hash()}
+    if sweep:
+        out["sweep"] = sweep
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

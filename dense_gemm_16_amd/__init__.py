@@ -1,0 +1,180 @@
+"""Python binding of libmigemm (the gfx950 dense matrix-multiply library).
+
+Argument marshalling only: every step of the product runs in the library's HIP
+kernels.  The functions named ``migemm_*`` mirror the C ABI in
+``include/migemm.h`` one for one (integers and raw device pointers);
+``gemm`` is a convenience wrapper over torch tensors that derives the sizes,
+leading dimensions, pointers and the current stream and calls
+``migemm_gemm_variant``.
+
+The library is loaded on first use from this package's directory.  If it has
+not been built, every call raises ``RuntimeError``: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libmigemm.so")
+
+F32, F16, BF16 = 0, 1, 2
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+VARIANT_AUTO, NAIVE, LDS_TILED, REGTILE_VALU, REGTILE_MFMA, MFMA16 = -1, 0, 1, 2, 3, 4
+
+# Every symbol the header declares (checked by the CPU test suite).
+EXPORTS = ("migemm_gemm", "migemm_gemm_variant", "migemm_variant_count", "migemm_variant_name",
+           "migemm_variant_supports", "migemm_config_count", "migemm_config_name",
+           "migemm_select", "migemm_status_string", "migemm_last_hip_error", "migemm_version")
+
+_lib = None
+
+
+class MigemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = migemm_status_string(status)
+        if status == ERR_HIP:
+            msg += f" (hipError_t {migemm_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def lib():
+    """The loaded library (ctypes.CDLL); raises RuntimeError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY_PATH):
+        raise RuntimeError(f"libmigemm.so is not built ({LIBRARY_PATH}); run "
+                           "`python dense_gemm_16_amd/build.py` or __graft_entry__.build()")
+    L = ctypes.CDLL(LIBRARY_PATH)
+    i64, i32, vp, cp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_char_p
+    L.migemm_gemm.argtypes = [i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp]
+    L.migemm_gemm.restype = i32
+    L.migemm_gemm_variant.argtypes = [i32, i32, i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp]
+    L.migemm_gemm_variant.restype = i32
+    L.migemm_variant_count.argtypes = []
+    L.migemm_variant_count.restype = i32
+    L.migemm_variant_name.argtypes = [i32]
+    L.migemm_variant_name.restype = cp
+    L.migemm_variant_supports.argtypes = [i32, i32]
+    L.migemm_variant_supports.restype = i32
+    L.migemm_config_count.argtypes = [i32]
+    L.migemm_config_count.restype = i32
+    L.migemm_config_name.argtypes = [i32, i32]
+    L.migemm_config_name.restype = cp
+    L.migemm_select.argtypes = [i64, i64, i64, i32, vp, i64, vp, i64, vp, i64,
+                                ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.migemm_select.restype = i32
+    L.migemm_status_string.argtypes = [i32]
+    L.migemm_status_string.restype = cp
+    L.migemm_last_hip_error.argtypes = []
+    L.migemm_last_hip_error.restype = i32
+    L.migemm_version.argtypes = []
+    L.migemm_version.restype = i32
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- C ABI mirror
+
+def migemm_gemm(M, N, K, dtype, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return lib().migemm_gemm(M, N, K, dtype, A, lda, B, ldb, C, ldc, stream)
+
+
+def migemm_gemm_variant(variant, config, M, N, K, dtype, A, lda, B, ldb, C, ldc,
+                        stream=None) -> int:
+    return lib().migemm_gemm_variant(variant, config, M, N, K, dtype, A, lda, B, ldb, C, ldc,
+                                     stream)
+
+
+def migemm_variant_count() -> int:
+    return lib().migemm_variant_count()
+
+
+def migemm_variant_name(variant: int) -> str | None:
+    s = lib().migemm_variant_name(variant)
+    return s.decode() if s is not None else None
+
+
+def migemm_variant_supports(variant: int, dtype: int) -> bool:
+    return bool(lib().migemm_variant_supports(variant, dtype))
+
+
+def migemm_config_count(variant: int) -> int:
+    return lib().migemm_config_count(variant)
+
+
+def migemm_config_name(variant: int, config: int) -> str | None:
+    s = lib().migemm_config_name(variant, config)
+    return s.decode() if s is not None else None
+
+
+def migemm_select(M, N, K, dtype, A, lda, B, ldb, C, ldc):
+    """(status, variant, config) that migemm_gemm would use."""
+    v, c = ctypes.c_int(-9), ctypes.c_int(-9)
+    st = lib().migemm_select(M, N, K, dtype, A, lda, B, ldb, C, ldc, ctypes.byref(v),
+                             ctypes.byref(c))
+    return st, v.value, c.value
+
+
+def migemm_status_string(status: int) -> str:
+    return lib().migemm_status_string(status).decode()
+
+
+def migemm_last_hip_error() -> int:
+    return lib().migemm_last_hip_error()
+
+
+def migemm_version() -> int:
+    return lib().migemm_version()
+
+
+# ---------------------------------------------------------- torch convenience
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise ValueError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def _ld(t) -> int:
+    if t.dim() != 2:
+        raise ValueError("operands must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("operands must have unit stride along rows (row-major)")
+    return max(1, t.stride(0) if t.shape[0] > 1 else t.shape[1])
+
+
+def gemm(a, b, out=None, *, variant: int = VARIANT_AUTO, config: int = -1, stream=None):
+    """C = A x B on the GPU for row-major torch tensors (FP32 C).
+
+    ``a`` (M x K) and ``b`` (K x N) are CUDA tensors of the same dtype
+    (float32, float16 or bfloat16) with unit inner stride; ``out`` (M x N,
+    float32) is allocated if not given.  Runs on ``stream`` (default: torch's
+    current stream) and returns ``out`` without synchronising.
+    """
+    import torch
+    if a.device.type != "cuda" or b.device.type != "cuda":
+        raise ValueError("operands must be on the GPU")
+    if a.dtype != b.dtype:
+        raise ValueError(f"dtype mismatch: {a.dtype} vs {b.dtype}")
+    dt = _dtype_code(a)
+    M, K = a.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {tuple(a.shape)} x {tuple(b.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N):
+        raise ValueError("out must be float32 of shape (M, N)")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    st = migemm_gemm_variant(variant, config, M, N, K, dt, a.data_ptr() or None, _ld(a),
+                             b.data_ptr() or None, _ld(b), out.data_ptr() or None, _ld(out),
+                             stream)
+    if st != OK:
+        raise MigemmError(st, "migemm_gemm_variant")
+    return out

@@ -1,0 +1,199 @@
+// api.cpp -- the C ABI (migemm.h): argument checks, the variant registry,
+// the deterministic selection table, and stream-ordered launch.
+//
+// The library's interface is a status-returning call in the manner of the
+// vendor GEMM call on page "matmul_registers.cu" (section on the library
+// comparison, where the status goes back to the caller rather than aborting):
+// nothing here prints, throws, exits, allocates or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+#include "migemm.h"
+
+namespace migemm {
+namespace {
+
+// Sizes are limited so that every index product fits in 64 bits:
+// a dimension below 2^31 times a leading dimension below 2^32.
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxLd = int64_t(1) << 32;
+
+struct Variant {
+    const char* name;
+    unsigned dtype_mask;  // bit d set: takes dtype d
+    int (*count)();
+    const char* (*config_name)(int);
+    hipError_t (*launch)(const GemmArgs&, int);
+};
+
+const Variant kVariants[] = {
+    {"naive", 0x7u, naive_config_count, naive_config_name, launch_naive},
+    {"lds_tiled", 0x1u, lds_tiled_config_count, lds_tiled_config_name, launch_lds_tiled},
+    {"regtile_valu", 0x1u, regtile_valu_config_count, regtile_valu_config_name,
+     launch_regtile_valu},
+    {"regtile_mfma", 0x1u, regtile_mfma_config_count, regtile_mfma_config_name,
+     launch_regtile_mfma},
+    {"mfma16", 0x6u, mfma16_config_count, mfma16_config_name, launch_mfma16},
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+thread_local int g_last_hip_error = 0;
+
+int elem_size(int dtype) { return dtype == MIGEMM_F32 ? 4 : 2; }
+
+// Byte range [lo, hi) touched by a rows x cols row-major operand with leading dimension ld.
+void extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int es, uintptr_t& lo,
+            uintptr_t& hi) {
+    lo = reinterpret_cast<uintptr_t>(p);
+    hi = lo + static_cast<uintptr_t>(((rows - 1) * ld + cols) * es);
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+int check_args(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+               const void* B, int64_t ldb, const float* C, int64_t ldc, bool need_ptrs) {
+    if (dtype != MIGEMM_F32 && dtype != MIGEMM_F16 && dtype != MIGEMM_BF16)
+        return MIGEMM_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return MIGEMM_ERR_INVALID_ARG;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+        return MIGEMM_ERR_INVALID_ARG;
+    if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return MIGEMM_ERR_INVALID_ARG;
+    if (!need_ptrs) return MIGEMM_OK;
+    if ((M > 0 && K > 0 && !A) || (K > 0 && N > 0 && !B) || (M > 0 && N > 0 && !C))
+        return MIGEMM_ERR_INVALID_ARG;
+    if (M > 0 && N > 0) {
+        const int es = elem_size(dtype);
+        uintptr_t c0, c1;
+        extent(C, M, N, ldc, 4, c0, c1);
+        if (K > 0) {
+            uintptr_t a0, a1, b0, b1;
+            extent(A, M, K, lda, es, a0, a1);
+            extent(B, K, N, ldb, es, b0, b1);
+            if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return MIGEMM_ERR_INVALID_ARG;
+        }
+    }
+    return MIGEMM_OK;
+}
+
+// The selection table: a pure function of shape, dtype and alignment.
+// Sizes are bucketed by how many workgroup tiles a configuration would launch
+// against the 256 CUs of an MI355X.
+void select(int64_t M, int64_t N, int64_t K, int dtype, int& variant, int& config) {
+    (void)K;
+    auto tiles = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
+    if (dtype == MIGEMM_F32) {
+        variant = MIGEMM_REGTILE_MFMA;
+        config = tiles(128, 128) >= 256 ? 0 : 2;
+        return;
+    }
+    variant = MIGEMM_MFMA16;
+    if (tiles(256, 256) >= 512)
+        config = 0;
+    else if (tiles(128, 128) >= 256)
+        config = 3;
+    else
+        config = 4;
+}
+
+int run(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype, const void* A,
+        int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    int st = check_args(M, N, K, dtype, A, lda, B, ldb, C, ldc, true);
+    if (st != MIGEMM_OK) return st;
+    if (variant == MIGEMM_VARIANT_AUTO) {
+        if (config != -1) return MIGEMM_ERR_INVALID_ARG;
+        select(M, N, K, dtype, variant, config);
+    }
+    if (variant < 0 || variant >= kNumVariants) return MIGEMM_ERR_INVALID_ARG;
+    const Variant& v = kVariants[variant];
+    if (!(v.dtype_mask & (1u << dtype))) return MIGEMM_ERR_UNSUPPORTED;
+    if (config == -1) {
+        int sv, sc;
+        select(M, N, K, dtype, sv, sc);
+        config = (sv == variant) ? sc : 0;
+    }
+    if (config < 0 || config >= v.count()) return MIGEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MIGEMM_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (K == 0) {
+        err = launch_zero_fill(C, M, N, ldc, s);
+    } else {
+        GemmArgs g{M, N, K, dtype, A, lda, B, ldb, C, ldc, s};
+        err = v.launch(g, config);
+    }
+    if (err != hipSuccess) {
+        g_last_hip_error = static_cast<int>(err);
+        return MIGEMM_ERR_HIP;
+    }
+    return MIGEMM_OK;
+}
+
+}  // namespace
+}  // namespace migemm
+
+using namespace migemm;
+
+extern "C" {
+
+int migemm_gemm(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    return run(MIGEMM_VARIANT_AUTO, -1, M, N, K, dtype, A, lda, B, ldb, C, ldc, stream);
+}
+
+int migemm_gemm_variant(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                        int64_t ldc, void* stream) {
+    return run(variant, config, M, N, K, dtype, A, lda, B, ldb, C, ldc, stream);
+}
+
+int migemm_variant_count(void) { return kNumVariants; }
+
+const char* migemm_variant_name(int variant) {
+    return (variant >= 0 && variant < kNumVariants) ? kVariants[variant].name : nullptr;
+}
+
+int migemm_variant_supports(int variant, int dtype) {
+    if (variant < 0 || variant >= kNumVariants || dtype < 0 || dtype > 2) return 0;
+    return (kVariants[variant].dtype_mask >> dtype) & 1u;
+}
+
+int migemm_config_count(int variant) {
+    return (variant >= 0 && variant < kNumVariants) ? kVariants[variant].count() : 0;
+}
+
+const char* migemm_config_name(int variant, int config) {
+    if (variant < 0 || variant >= kNumVariants) return nullptr;
+    return kVariants[variant].config_name(config);
+}
+
+int migemm_select(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                  const void* B, int64_t ldb, const float* C, int64_t ldc, int* variant,
+                  int* config) {
+    (void)A;
+    (void)B;
+    (void)C;
+    int st = check_args(M, N, K, dtype, A, lda, B, ldb, C, ldc, false);
+    if (st != MIGEMM_OK) return st;
+    if (!variant || !config) return MIGEMM_ERR_INVALID_ARG;
+    select(M, N, K, dtype, *variant, *config);
+    return MIGEMM_OK;
+}
+
+const char* migemm_status_string(int status) {
+    switch (status) {
+        case MIGEMM_OK: return "ok";
+        case MIGEMM_ERR_INVALID_ARG: return "invalid argument";
+        case MIGEMM_ERR_UNSUPPORTED: return "variant does not support this dtype";
+        case MIGEMM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int migemm_last_hip_error(void) { return g_last_hip_error; }
+
+int migemm_version(void) { return 100; }
+
+}  // extern "C"

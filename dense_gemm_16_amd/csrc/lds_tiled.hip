@@ -1,0 +1,71 @@
+// lds_tiled.hip -- FP32 GEMM with square tiles of A and B staged in LDS.
+//
+// Per k-tile the workgroup copies a T x T tile of A and of B from global
+// memory into LDS with coalesced loads (consecutive work-items take
+// consecutive columns), waits at a barrier, lets every work-item accumulate
+// its one output over the T values of k from LDS, and waits again before the
+// tile is overwritten (page "matmul_registers.cu", matmulSharedTiled: two LDS
+// reads per multiply-add, two barriers per k-tile).  Unlike that kernel this
+// one guards every edge: out-of-range elements of A and B are loaded as zero
+// and out-of-range outputs are not stored, so any M, N, K and leading
+// dimension is accepted.
+//
+// LDS bank conflicts: a wavefront covers 64 / T rows of the tile, and its
+// work-items read A_s[row][p] for those rows at once.  Rows of T floats map
+// onto the same banks whenever T divides the bank count, so the A tile rows
+// are padded to T + 1 floats.  B_s[p][col] is read along a row, conflict-free.
+#include "common.hpp"
+
+namespace migemm {
+namespace {
+
+template <int T>
+__global__ __launch_bounds__(T* T) void lds_tiled_kernel(int64_t M, int64_t N, int64_t K,
+                                                        const float* __restrict__ A, int64_t lda,
+                                                        const float* __restrict__ B, int64_t ldb,
+                                                        float* __restrict__ C, int64_t ldc) {
+    __shared__ float As[T][T + 1];
+    __shared__ float Bs[T][T];
+    const int tx = threadIdx.x, ty = threadIdx.y;
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * T + tx;
+    const int64_t nrb = ceil_div(M, T);
+    for (int64_t rb = blockIdx.y; rb < nrb; rb += gridDim.y) {  // uniform over the workgroup
+        const int64_t row = rb * T + ty;
+        float acc = 0.0f;
+        for (int64_t k0 = 0; k0 < K; k0 += T) {
+            const int64_t ka = k0 + tx;  // column of A this work-item loads
+            const int64_t kb = k0 + ty;  // row of B this work-item loads
+            As[ty][tx] = (row < M && ka < K) ? A[row * lda + ka] : 0.0f;
+            Bs[ty][tx] = (kb < K && col < N) ? B[kb * ldb + col] : 0.0f;
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < T; ++p) acc = fmaf(As[ty][p], Bs[p][tx], acc);
+            __syncthreads();
+        }
+        if (row < M && col < N) C[row * ldc + col] = acc;
+    }
+}
+
+template <int T>
+hipError_t launch_tile(const GemmArgs& g) {
+    const int64_t gy = ceil_div(g.M, T);
+    dim3 grid(static_cast<unsigned>(ceil_div(g.N, T)),
+              static_cast<unsigned>(gy > 65535 ? 65535 : gy));
+    lds_tiled_kernel<T><<<grid, dim3(T, T), 0, g.stream>>>(
+        g.M, g.N, g.K, static_cast<const float*>(g.A), g.lda, static_cast<const float*>(g.B),
+        g.ldb, g.C, g.ldc);
+    return hipGetLastError();
+}
+
+const char* const kNames[] = {"32x32 tile", "16x16 tile"};
+
+}  // namespace
+
+int lds_tiled_config_count() { return 2; }
+const char* lds_tiled_config_name(int c) { return (c >= 0 && c < 2) ? kNames[c] : nullptr; }
+
+hipError_t launch_lds_tiled(const GemmArgs& g, int config) {
+    return config == 1 ? launch_tile<16>(g) : launch_tile<32>(g);
+}
+
+}  // namespace migemm

@@ -1,0 +1,154 @@
+/*
+ * migemm.h -- C ABI of the MI355X (gfx950) dense matrix-multiply library.
+ *
+ * Operation.  C = A x B, overwriting C, for row-major A (M x K), B (K x N) and
+ * C (M x N):
+ *
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j]
+ *
+ * (page "Tensor cores and matrix operations", section "Traditional Approach:
+ * Element-by-Element"; the product is a plain overwrite, alpha = 1 and
+ * beta = 0, as in the library call on page "matmul_registers.cu").  Two forms:
+ *
+ *   MIGEMM_F32   FP32 A and B, FP32 arithmetic, FP32 C (the FP32 GEMMs of
+ *                pages "matmul_registers.cu" and "04-wmma-matmul.cu");
+ *   MIGEMM_F16,  FP16 or BF16 A and B, products accumulated in FP32, FP32 C
+ *   MIGEMM_BF16  (page "CUDA-Practice 09", section on mixed precision: half
+ *                inputs halve the bytes read, FP32 accumulation keeps long sums
+ *                from losing small terms).
+ *
+ * Layout.  Row-major with leading dimensions in ELEMENTS: element (i, k) of A
+ * is at A[i * lda + k], (k, j) of B at B[k * ldb + j], (i, j) of C at
+ * C[i * ldc + j].  Requirements: lda >= max(1, K), ldb >= max(1, N),
+ * ldc >= max(1, N).  No alignment is required; 16-byte aligned pointers and
+ * leading dimensions that are multiples of 16 bytes take the vector-load path.
+ *
+ * Pointers.  A, B and C are DEVICE pointers on the current HIP device, owned
+ * by the caller.  The library allocates no memory, keeps no pointer after a
+ * call returns, and has no mutable global state, so calls are reentrant and
+ * may come from several host threads.  C must not overlap A or B.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Work is enqueued asynchronously on it; the library never
+ * synchronises.  The caller synchronises before reading C.
+ *
+ * Errors.  Every entry point returns a migemm_status; nothing prints, throws
+ * or exits.  Argument errors are detected before any HIP call.  Degenerate
+ * shapes: M == 0 or N == 0 is a no-op returning MIGEMM_OK; K == 0 writes
+ * C = 0 (an empty sum) over the M x N window.
+ */
+#ifndef MIGEMM_H
+#define MIGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of A and B.  C is always FP32. */
+typedef enum {
+    MIGEMM_F32 = 0,
+    MIGEMM_F16 = 1,  /* IEEE binary16 */
+    MIGEMM_BF16 = 2  /* bfloat16: the upper half of a binary32 word */
+} migemm_dtype;
+
+typedef enum {
+    MIGEMM_OK = 0,
+    MIGEMM_ERR_INVALID_ARG = 1, /* negative size, ld too small, unknown dtype, NULL with data,
+                                   size beyond the supported range, bad variant/config index */
+    MIGEMM_ERR_UNSUPPORTED = 2, /* a forced variant that does not take this dtype */
+    MIGEMM_ERR_HIP = 3          /* the HIP runtime reported an error at launch
+                                   (see migemm_last_hip_error) */
+} migemm_status;
+
+/*
+ * Kernel variants.  Each one computes the same product; they differ in how
+ * (and so in speed and in summation order, not in the tolerance they meet).
+ *
+ *   MIGEMM_NAIVE         one work-item per C element, FP32 fused multiply-adds
+ *                        over k (page "04-wmma-matmul.cu", naiveMatmul; page
+ *                        "CUDA-Practice 09", gemm_fp32_kernel).  All dtypes.
+ *   MIGEMM_LDS_TILED     square tiles of A and B staged in LDS, one output per
+ *                        work-item (page "matmul_registers.cu",
+ *                        matmulSharedTiled).  FP32 only.
+ *   MIGEMM_REGTILE_VALU  register micro-tiles per work-item with 16-byte global
+ *                        loads and the A tile stored k-major in LDS (page
+ *                        "matmul_registers.cu", matmulRegTile2d and
+ *                        matmulRegTile2dVec4), on VALU FMA.  FP32 only.
+ *   MIGEMM_REGTILE_MFMA  the same staging with the inner product on FP32
+ *                        matrix-core instructions.  FP32 only.
+ *   MIGEMM_MFMA16        FP16/BF16 matrix-core kernel with FP32 accumulation:
+ *                        double-buffered, swizzled LDS tiles, 16-byte
+ *                        coalesced staging (the tiled matrix-unit algorithm of
+ *                        page "Tensor cores and matrix operations", section
+ *                        "Complete Algorithm for Large Matrix Multiply").
+ *                        FP16 and BF16 only.
+ */
+typedef enum {
+    MIGEMM_VARIANT_AUTO = -1,
+    MIGEMM_NAIVE = 0,
+    MIGEMM_LDS_TILED = 1,
+    MIGEMM_REGTILE_VALU = 2,
+    MIGEMM_REGTILE_MFMA = 3,
+    MIGEMM_MFMA16 = 4
+} migemm_variant;
+
+/*
+ * C = A x B with the variant and tile configuration chosen by the library's
+ * selection table (deterministic: a pure function of the arguments).
+ */
+int migemm_gemm(int64_t M, int64_t N, int64_t K, int dtype,
+                const void* A, int64_t lda, const void* B, int64_t ldb,
+                float* C, int64_t ldc, void* stream);
+
+/*
+ * As migemm_gemm, with the variant forced (MIGEMM_VARIANT_AUTO selects as
+ * migemm_gemm does) and the tile configuration forced by index
+ * (config = -1: the selection table's choice for that variant).
+ * MIGEMM_ERR_UNSUPPORTED if the variant does not take `dtype`;
+ * MIGEMM_ERR_INVALID_ARG for an unknown variant or config index.
+ */
+int migemm_gemm_variant(int variant, int config,
+                        int64_t M, int64_t N, int64_t K, int dtype,
+                        const void* A, int64_t lda, const void* B, int64_t ldb,
+                        float* C, int64_t ldc, void* stream);
+
+/* Number of variants (they are numbered 0 .. count-1). */
+int migemm_variant_count(void);
+
+/* Short name of a variant, or NULL for an unknown index.  Static storage. */
+const char* migemm_variant_name(int variant);
+
+/* 1 if the variant takes this dtype, 0 if not (or if either is unknown). */
+int migemm_variant_supports(int variant, int dtype);
+
+/* Number of tile configurations of a variant (0 for an unknown index). */
+int migemm_config_count(int variant);
+
+/* Name of a configuration ("256x256x64 8w 16x16x32" ...), or NULL.  Static storage. */
+const char* migemm_config_name(int variant, int config);
+
+/*
+ * The selection for these arguments without launching anything: writes the
+ * variant and config indices migemm_gemm would use.  Same argument checks as
+ * migemm_gemm (pointers are only inspected for alignment and may be NULL).
+ */
+int migemm_select(int64_t M, int64_t N, int64_t K, int dtype,
+                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                  const float* C, int64_t ldc, int* variant, int* config);
+
+/* Text of a status code.  Static storage. */
+const char* migemm_status_string(int status);
+
+/* The hipError_t code behind the calling thread's last MIGEMM_ERR_HIP (0 if none). */
+int migemm_last_hip_error(void);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int migemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIGEMM_H */

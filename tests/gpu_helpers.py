@@ -1,0 +1,78 @@
+"""Helpers for the GPU parity tests: run the library through its C ABI on
+seeded inputs and compare element by element with the CPU oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import dense_gemm_16_amd as mg
+import oracle
+from oracle.check import compare, tolerance
+from dense_gemm_16_amd import inputs
+
+DT_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def say(msg: str):
+    """Name the case before a GPU step, flushed, so a fault report can be attributed."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device_with_ld(x: torch.Tensor, ld: int | None = None, offset: int = 0):
+    """Copy a CPU matrix to the GPU inside a larger buffer: row stride ``ld`` and a start
+    ``offset`` elements into the allocation (offset 1 makes the base misaligned)."""
+    rows, cols = x.shape
+    ld = ld or max(cols, 1)
+    buf = torch.full((offset + max(rows, 1) * ld + 8,), float("nan"), dtype=x.dtype,
+                     device="cuda")
+    view = buf[offset:offset + rows * ld].view(rows, ld)[:, :cols] if rows else \
+        buf[offset:offset].view(0, cols)
+    view.copy_(x.to("cuda"))
+    return view, buf
+
+
+def run_gemm(A: torch.Tensor, B: torch.Tensor, dtype: str, variant=-1, config=-1, lda=None,
+             ldb=None, ldc=None, a_off=0, b_off=0, c_off=0, poison=True):
+    """Run C = A x B through migemm_gemm_variant; returns (C on CPU as float32, C buffer)."""
+    M, K = A.shape
+    N = B.shape[1]
+    dA, _ = to_device_with_ld(A, lda, a_off)
+    dB, _ = to_device_with_ld(B, ldb, b_off)
+    ldc = ldc or max(N, 1)
+    cbuf = torch.full((c_off + max(M, 1) * ldc + 64,), float("nan") if poison else 0.0,
+                      dtype=torch.float32, device="cuda")
+    dC = cbuf[c_off:c_off + M * ldc].view(M, ldc)[:, :N] if M else cbuf[:0].view(0, N)
+    stream = torch.cuda.current_stream().cuda_stream
+    st = mg.migemm_gemm_variant(variant, config, M, N, K, DT_CODE[dtype],
+                                dA.data_ptr() if dA.numel() else None, lda or max(K, 1),
+                                dB.data_ptr() if dB.numel() else None, ldb or max(N, 1),
+                                dC.data_ptr() if dC.numel() else None, ldc, stream)
+    torch.cuda.synchronize()
+    assert st == mg.OK, f"status {st}: {mg.migemm_status_string(st)} hip={mg.migemm_last_hip_error()}"
+    return dC.cpu().clone(), cbuf
+
+
+def oracle_ref(A: torch.Tensor, B: torch.Tensor, dtype: str):
+    return oracle.gemm(inputs.to_bits(A), inputs.to_bits(B), DT_CODE[dtype])
+
+
+def check(Cgpu: torch.Tensor, A, B, dtype: str, exact=False, ref=None):
+    C, S = ref if ref is not None else oracle_ref(A, B, dtype)
+    r = compare(Cgpu.numpy(), C, S, tol=None if exact else tolerance(DT_CODE[dtype]), exact=exact)
+    assert r.ok, str(r)
+    return r
+
+
+def sampled_entries(M, N, n, seed=0, include_edges=True):
+    """Sampled (row, col) pairs: random plus the four corners and last row/col."""
+    rng = np.random.default_rng(seed)
+    rows = list(rng.integers(0, M, n))
+    cols = list(rng.integers(0, N, n))
+    if include_edges:
+        for r, c in [(0, 0), (0, N - 1), (M - 1, 0), (M - 1, N - 1)]:
+            rows.append(r)
+            cols.append(c)
+    return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)

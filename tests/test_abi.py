@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports what include/migemm.h declares, and checks its
+arguments before touching the GPU (CPU only: no call here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_16_amd as mg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "migemm.h")
+
+# Device pointers are never dereferenced on these paths; any non-null value will do.
+P = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(migemm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = mg.lib()
+    for n in names:
+        assert hasattr(lib, n), f"libmigemm.so does not export {n}"
+    assert sorted(mg.EXPORTS) == names
+
+
+def test_exports_are_c_symbols():
+    # extern "C": the dynamic symbol table holds the plain names
+    cdll = ctypes.CDLL(mg.LIBRARY_PATH)
+    for n in declared_functions():
+        getattr(cdll, n)
+
+
+def test_variant_registry():
+    assert mg.migemm_variant_count() == 5
+    names = [mg.migemm_variant_name(v) for v in range(5)]
+    assert names == ["naive", "lds_tiled", "regtile_valu", "regtile_mfma", "mfma16"]
+    assert mg.migemm_variant_name(5) is None and mg.migemm_variant_name(-1) is None
+    assert all(mg.migemm_variant_supports(mg.NAIVE, d) for d in (0, 1, 2))
+    for v in (mg.LDS_TILED, mg.REGTILE_VALU, mg.REGTILE_MFMA):
+        assert mg.migemm_variant_supports(v, 0)
+        assert not mg.migemm_variant_supports(v, 1) and not mg.migemm_variant_supports(v, 2)
+    assert not mg.migemm_variant_supports(mg.MFMA16, 0)
+    assert mg.migemm_variant_supports(mg.MFMA16, 1) and mg.migemm_variant_supports(mg.MFMA16, 2)
+    for v in range(5):
+        n = mg.migemm_config_count(v)
+        assert n >= 1
+        assert all(mg.migemm_config_name(v, c) for c in range(n))
+        assert mg.migemm_config_name(v, n) is None
+    assert mg.migemm_config_count(9) == 0
+    assert mg.migemm_version() >= 100
+
+
+def test_status_strings():
+    assert mg.migemm_status_string(mg.OK) == "ok"
+    for s in (1, 2, 3, 77):
+        assert mg.migemm_status_string(s)
+
+
+@pytest.mark.parametrize("args", [
+    dict(M=-1), dict(N=-1), dict(K=-1), dict(dtype=3), dict(dtype=-1),
+    dict(lda=3), dict(ldb=4), dict(ldc=4), dict(M=1 << 31), dict(lda=(1 << 32) + 1),
+    dict(A=None), dict(B=None), dict(C=None),
+])
+def test_invalid_arguments_rejected_before_any_launch(args):
+    a = dict(M=8, N=5, K=4, dtype=0, A=P, lda=4, B=2 * P, ldb=5, C=3 * P, ldc=5)
+    a.update(args)
+    st = mg.migemm_gemm(a["M"], a["N"], a["K"], a["dtype"], a["A"], a["lda"], a["B"], a["ldb"],
+                        a["C"], a["ldc"], None)
+    assert st == mg.ERR_INVALID_ARG
+
+
+def test_overlapping_output_rejected():
+    # C's byte range overlaps A's
+    st = mg.migemm_gemm(16, 16, 16, 0, P, 16, 2 * P, 16, P + 64, 16, None)
+    assert st == mg.ERR_INVALID_ARG
+    st = mg.migemm_gemm(16, 16, 16, 1, P, 16, 2 * P, 16, 2 * P + 100, 16, None)
+    assert st == mg.ERR_INVALID_ARG
+
+
+def test_empty_output_is_a_noop():
+    # M == 0 or N == 0: OK with no HIP call (null pointers allowed where there is no data)
+    assert mg.migemm_gemm(0, 5, 7, 0, None, 7, P, 5, None, 5, None) == mg.OK
+    assert mg.migemm_gemm(4, 0, 7, 2, P, 7, None, 1, None, 1, None) == mg.OK
+
+
+def test_forced_variant_checks():
+    base = (64, 64, 64, 1, P, 64, 2 * P, 64, 3 * P, 64, None)
+    assert mg.migemm_gemm_variant(mg.LDS_TILED, -1, *base) == mg.ERR_UNSUPPORTED
+    assert mg.migemm_gemm_variant(mg.REGTILE_MFMA, 0, *base) == mg.ERR_UNSUPPORTED
+    f32 = (64, 64, 64, 0, P, 64, 2 * P, 64, 3 * P, 64, None)
+    assert mg.migemm_gemm_variant(mg.MFMA16, -1, *f32) == mg.ERR_UNSUPPORTED
+    assert mg.migemm_gemm_variant(7, -1, *f32) == mg.ERR_INVALID_ARG
+    assert mg.migemm_gemm_variant(mg.NAIVE, 99, *f32) == mg.ERR_INVALID_ARG
+    assert mg.migemm_gemm_variant(mg.VARIANT_AUTO, 0, *f32) == mg.ERR_INVALID_ARG
+
+
+def test_selection_is_deterministic_and_valid():
+    for (M, N, K, dt) in [(256, 256, 256, 1), (1024, 1024, 1024, 0), (1024, 1024, 1024, 1),
+                          (2048, 2048, 2048, 2), (2050, 2047, 2056, 1), (8192, 8192, 8192, 2),
+                          (4096, 4096, 4096, 0), (1, 1, 1, 0), (3, 100000, 7, 2)]:
+        st, v, c = mg.migemm_select(M, N, K, dt, None, max(K, 1), None, N, None, N)
+        assert st == mg.OK
+        assert mg.migemm_variant_supports(v, dt)
+        assert 0 <= c < mg.migemm_config_count(v)
+        assert mg.migemm_select(M, N, K, dt, None, max(K, 1), None, N, None, N) == (st, v, c)
+    st, _, _ = mg.migemm_select(4, 4, 4, 9, None, 4, None, 4, None, 4)
+    assert st == mg.ERR_INVALID_ARG
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(mg, "_lib", None)
+    monkeypatch.setattr(mg, "LIBRARY_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        mg.migemm_variant_count()

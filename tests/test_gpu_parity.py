@@ -1,0 +1,151 @@
+"""GPU parity: every variant and configuration against the CPU oracle, through the C ABI.
+
+Bar: bit-exact where every partial sum is an integer below 2^24 (small-integer
+inputs, all-ones, identity, permutation); otherwise |C - C_ref| <= tol * S per
+element with S = sum_k |A[i][k] B[k][j]|, tol = 1e-4 (FP32) or 5e-4
+(FP16/BF16 with FP32 accumulation).  Inputs are seeded; C is poisoned with NaN
+before each call so an unwritten element fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_16_amd as mg
+from dense_gemm_16_amd import inputs
+from gpu_helpers import check, run_gemm, say
+
+pytestmark = pytest.mark.gpu
+
+# (variant, config) pairs per dtype: every configuration of every variant.
+def _cases(dtype):
+    code = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    out = []
+    for v in range(mg.migemm_variant_count()):
+        if mg.migemm_variant_supports(v, code):
+            out += [(v, c) for c in range(mg.migemm_config_count(v))]
+    return out
+
+
+SHAPES = [(1, 1, 1), (17, 33, 9), (64, 64, 64), (130, 70, 200), (300, 257, 129),
+          (512, 512, 512), (600, 520, 300)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_every_config_matches_oracle(dtype):
+    for (M, N, K) in SHAPES:
+        A, B = inputs.pair(M, N, K, dtype, "uniform", seed=M * 7 + N * 3 + K)
+        ref = None
+        for v, c in _cases(dtype):
+            if v == mg.NAIVE and M * N * K > 64 * 1024 * 1024:
+                continue
+            say(f"every_config {dtype} {M}x{N}x{K} variant={mg.migemm_variant_name(v)} cfg={c}")
+            C, _ = run_gemm(A, B, dtype, variant=v, config=c)
+            from gpu_helpers import oracle_ref
+            ref = ref or oracle_ref(A, B, dtype)
+            check(C, A, B, dtype, ref=ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_small_integers_bit_exact_every_config(dtype):
+    M, N, K = 200, 136, 1000
+    A, B = inputs.pair(M, N, K, dtype, "int", seed=5)
+    ref = None
+    for v, c in _cases(dtype):
+        say(f"int_exact {dtype} variant={mg.migemm_variant_name(v)} cfg={c}")
+        C, _ = run_gemm(A, B, dtype, variant=v, config=c)
+        from gpu_helpers import oracle_ref
+        ref = ref or oracle_ref(A, B, dtype)
+        check(C, A, B, dtype, exact=True, ref=ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_structured_cases_exact(dtype):
+    t = inputs.TORCH_DTYPES[dtype]
+    n, p = 96, 80
+    B = inputs.draw((n, p), dtype, "int", torch.Generator().manual_seed(1))
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(2))
+    P = torch.zeros(n, n)
+    P[torch.arange(n), perm] = 1.0
+    I = torch.eye(n)
+    for v, c in _cases(dtype):
+        say(f"structured {dtype} variant={mg.migemm_variant_name(v)} cfg={c}")
+        C, _ = run_gemm(I.to(t), B, dtype, variant=v, config=c)
+        assert torch.equal(C, B.float()), "identity"
+        C, _ = run_gemm(P.to(t), B, dtype, variant=v, config=c)
+        assert torch.equal(C, B.float()[perm]), "permutation"
+        ones_a, ones_b = torch.ones(33, 777).to(t), torch.ones(777, 65).to(t)
+        C, _ = run_gemm(ones_a, ones_b, dtype, variant=v, config=c)
+        assert torch.all(C == 777), "all-ones"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_edge_sweep_selected_path(dtype):
+    dims = [1, 15, 16, 17, 63, 65, 127, 129, 255, 257]
+    rng = np.random.default_rng(3)
+    for trial in range(24):
+        M, N, K = (int(x) for x in rng.choice(dims, 3))
+        A, B = inputs.pair(M, N, K, dtype, "normal", seed=trial)
+        say(f"edge_sweep {dtype} {M}x{N}x{K}")
+        C, _ = run_gemm(A, B, dtype)
+        check(C, A, B, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_leading_dims_misalignment_and_poison(dtype):
+    M, N, K = 197, 211, 233
+    A, B = inputs.pair(M, N, K, dtype, "uniform", seed=9)
+    for v, c in _cases(dtype):
+        if v == mg.NAIVE:
+            continue
+        for (lda, ldb, ldc, ao, bo, co) in [(K + 1, N + 3, N + 1, 0, 0, 0),
+                                            (K + 8, N + 8, N + 4, 1, 1, 1),
+                                            (K, N, N, 3, 5, 2)]:
+            say(f"ld {dtype} variant={mg.migemm_variant_name(v)} cfg={c} "
+                f"ld=({lda},{ldb},{ldc}) off=({ao},{bo},{co})")
+            C, cbuf = run_gemm(A, B, dtype, variant=v, config=c, lda=lda, ldb=ldb, ldc=ldc,
+                               a_off=ao, b_off=bo, c_off=co)
+            check(C, A, B, dtype)
+            # everything outside the M x N window is still the NaN poison
+            full = cbuf.cpu()
+            inside = torch.zeros_like(full, dtype=torch.bool)
+            for r in range(M):
+                inside[co + r * ldc: co + r * ldc + N] = True
+            assert torch.all(torch.isnan(full[~inside])), "wrote outside the C window"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_degenerate_shapes(dtype):
+    # K == 0 writes zeros; M == 0 / N == 0 are no-ops
+    A = torch.zeros(37, 0).to(inputs.TORCH_DTYPES[dtype])
+    B = torch.zeros(0, 41).to(inputs.TORCH_DTYPES[dtype])
+    for v, c in _cases(dtype):
+        say(f"degenerate K=0 {dtype} variant={v} cfg={c}")
+        C, _ = run_gemm(A, B, dtype, variant=v, config=c)
+        assert torch.all(C == 0)
+    C, _ = run_gemm(torch.zeros(0, 5).to(A.dtype), torch.zeros(5, 3).to(A.dtype), dtype)
+    assert C.shape == (0, 3)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_k_trip_counts(dtype):
+    # 1..5 k-tiles plus a tail: exercises the double-buffer hand-off
+    bk = 32 if dtype == "f32" else 64
+    for kt in range(1, 6):
+        for tail in (0, 1, bk - 1):
+            K = kt * bk + tail
+            A, B = inputs.pair(256, 256, K, dtype, "int", seed=K)
+            say(f"k_trips {dtype} K={K}")
+            C, _ = run_gemm(A, B, dtype)
+            check(C, A, B, dtype, exact=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_run_to_run_bitwise_determinism(dtype):
+    A, B = inputs.pair(700, 600, 900, dtype, "normal", seed=17)
+    for v, c in _cases(dtype):
+        if v == mg.NAIVE:
+            continue
+        say(f"determinism {dtype} variant={v} cfg={c}")
+        C1, _ = run_gemm(A, B, dtype, variant=v, config=c)
+        C2, _ = run_gemm(A, B, dtype, variant=v, config=c)
+        assert torch.equal(C1, C2)
