@@ -246,17 +246,28 @@ def main():
 
     sweep = {}
     if a.sweep:
-        for v in range(mg.migemm_variant_count()):
-            if not mg.migemm_variant_supports(v, p.code) or v == mg.NAIVE and w.flop > 5e10:
-                continue
-            for c in range(mg.migemm_config_count(v)):
-                q = Problem.__new__(Problem)
-                q.__dict__.update(p.__dict__)
-                q.variant, q.config = v, c
-                q.args = (v, c) + p.args[2:]
-                t, n = q.time_window()
-                sweep[q.kernel_name()] = round(w.flop / (t * 1e-3) / 1e12, 2)
-                log(f"sweep {q.kernel_name()}: {sweep[q.kernel_name()]} TFLOPS")
+        for name in [w.name] + EXTRA:
+            wx = inputs.WORKLOADS[name]
+            px = p if name == w.name else Problem(wx)
+            res = {}
+            for v in range(mg.migemm_variant_count()):
+                if not mg.migemm_variant_supports(v, px.code):
+                    continue
+                if v == mg.NAIVE and wx.flop > 5e10:
+                    continue
+                for c in range(mg.migemm_config_count(v)):
+                    q = Problem.__new__(Problem)
+                    q.__dict__.update(px.__dict__)
+                    q.variant, q.config = v, c
+                    q.args = (v, c) + px.args[2:]
+                    t, n = q.time_window()
+                    res[q.kernel_name()] = round(wx.flop / (t * 1e-3) / 1e12, 2)
+            best = max(res, key=res.get)
+            log(f"sweep {name}: best {best} {res[best]} TFLOPS; selected "
+                f"{px.kernel_name()} {res.get(px.kernel_name())}")
+            sweep[name] = res
+            if px is not p:
+                del px
 
     extra = {}
     if not a.no_extra:

@@ -77,11 +77,17 @@ int check_args(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_
     return MIGEMM_OK;
 }
 
+// 16-byte aligned operand pointers with leading dimensions of whole 16-byte
+// chunks (8 16-bit elements).  NULL pointers count as aligned (migemm_select).
+bool operands_aligned(const void* A, int64_t lda, const void* B, int64_t ldb) {
+    return aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
+}
+
 // The selection table: a pure function of shape, dtype and alignment.
 // Sizes are bucketed by how many workgroup tiles a configuration would launch
 // against the 256 CUs of an MI355X.
-void select(int64_t M, int64_t N, int64_t K, int dtype, int& variant, int& config) {
-    (void)K;
+void select(int64_t M, int64_t N, int64_t K, int dtype, bool aligned, int& variant,
+            int& config) {
     auto tiles = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
     if (dtype == MIGEMM_F32) {
         variant = MIGEMM_REGTILE_MFMA;
@@ -89,8 +95,14 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, int& variant, int& confi
         return;
     }
     variant = MIGEMM_MFMA16;
-    if (tiles(256, 256) >= 512)
-        config = 0;
+    // Direct global->LDS staging needs 16-byte aligned operands with leading
+    // dimensions a multiple of 8 elements, K a multiple of 64 and N a multiple
+    // of 8 (the launcher falls back to the register-staged kernel otherwise).
+    const bool direct = aligned && K % 64 == 0 && N % 8 == 0 && N >= 8;
+    if (direct && tiles(256, 256) >= 256)
+        config = 10;  // direct 256x256x64, 8 waves, 32x32x16
+    else if (direct)
+        config = 11;  // direct 128x128x64, 4 waves
     else if (tiles(128, 128) >= 256)
         config = 3;
     else
@@ -103,14 +115,14 @@ int run(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype, con
     if (st != MIGEMM_OK) return st;
     if (variant == MIGEMM_VARIANT_AUTO) {
         if (config != -1) return MIGEMM_ERR_INVALID_ARG;
-        select(M, N, K, dtype, variant, config);
+        select(M, N, K, dtype, operands_aligned(A, lda, B, ldb), variant, config);
     }
     if (variant < 0 || variant >= kNumVariants) return MIGEMM_ERR_INVALID_ARG;
     const Variant& v = kVariants[variant];
     if (!(v.dtype_mask & (1u << dtype))) return MIGEMM_ERR_UNSUPPORTED;
     if (config == -1) {
         int sv, sc;
-        select(M, N, K, dtype, sv, sc);
+        select(M, N, K, dtype, operands_aligned(A, lda, B, ldb), sv, sc);
         config = (sv == variant) ? sc : 0;
     }
     if (config < 0 || config >= v.count()) return MIGEMM_ERR_INVALID_ARG;
@@ -178,7 +190,7 @@ int migemm_select(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int
     int st = check_args(M, N, K, dtype, A, lda, B, ldb, C, ldc, false);
     if (st != MIGEMM_OK) return st;
     if (!variant || !config) return MIGEMM_ERR_INVALID_ARG;
-    select(M, N, K, dtype, *variant, *config);
+    select(M, N, K, dtype, operands_aligned(A, lda, B, ldb), *variant, *config);
     return MIGEMM_OK;
 }
 

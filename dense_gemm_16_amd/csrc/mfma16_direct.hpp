@@ -1,0 +1,294 @@
+// mfma16_direct.hpp -- FP16/BF16 GEMM for gfx950 with direct global->LDS
+// staging and transposing LDS reads.
+//
+// Same algorithm as mfma_gemm.hpp (tiles of C, k-tiles accumulated by the
+// matrix cores; page "Tensor cores and matrix operations", section "Complete
+// Algorithm for Large Matrix Multiply"), rebuilt around two gfx950 features:
+//
+// * global_load_lds_dwordx4 moves 16 bytes per lane from global memory
+//   straight into LDS (lane l's bytes land at the instruction's LDS base +
+//   16 l), so no registers hold staged tiles and no instructions copy them.
+//   Which global chunk a lane fetches is chosen so that the LDS image comes out
+//   swizzled.
+// * ds_read_b64_tr_b16 reads a 4-row x 16-column block of a row-major tile and
+//   hands lane j of each 16-lane group column j of those rows.  B therefore
+//   stays row-major in LDS (as it is in memory), and the k-contiguous operand
+//   the matrix instruction wants is produced by the read itself: two
+//   transposing reads give a lane the 8 consecutive k of one column of B.
+//
+// LDS images (per stage; two stages alternate):
+//   A: [BM rows][8 chunks of 16 B]; logical chunk c of row r at physical chunk
+//      c ^ ((r ^ (r >> 3)) & 7).  Sixteen consecutive rows reading one logical
+//      chunk (a fragment read) then fall on sixteen distinct 16-byte bank
+//      groups.
+//   B: [64 k-rows][BN/8 chunks of 16 B]; logical chunk c of k-row r at
+//      c ^ (2 f(r)), f(r) = (r & 3) | (((r >> 3) & 1) << 2).  A transposing
+//      read touches 32 bytes (two chunks) in each of the rows 8g + {0..3} of
+//      the four lane groups g; f gives the eight rows of two adjacent groups
+//      eight distinct chunk pairs, i.e. all 64 banks once.
+//
+// Work per workgroup: a BM x BN tile of C, WM x WN wavefronts each owning a
+// (BM/WM) x (BN/WN) block of accumulators.  k advances 64 at a time through
+// STAGES LDS buffers: the direct loads of k-tile kt + STAGES - 1 are issued
+// at the start of k-tile kt, so each load has STAGES - 1 k-tiles of matrix work
+// to land.  Matrix-core operands are software-pipelined: the fragments of the
+// next 32-k (or 16-k) slab are read from LDS while the current slab's
+// instructions run, including across the one barrier per k-tile.
+//
+// The direct loads are issued through inline assembly with explicit
+// vmcnt accounting: the compiler cannot see that they write a different LDS
+// stage from the one being read, and would otherwise wait for every load
+// before every LDS read.  They use an SGPR tile base plus a 32-bit per-lane
+// offset, so the per-lane offsets are computed once and no 64-bit addresses
+// occupy VGPRs.
+//
+// Preconditions (checked by the launcher; other shapes use mfma_gemm.hpp):
+// A and B 16-byte aligned, lda and ldb multiples of 8 elements, K a multiple
+// of 64, N a multiple of 8.  Rows of A past M and columns of B past N are
+// clamped to the last valid row / chunk, so every load is in bounds; those
+// lanes only feed outputs that are never stored.
+#pragma once
+
+#include "mfma_gemm.hpp"
+
+namespace migemm {
+
+#define MIGEMM_LDS __attribute__((address_space(3)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
+          int GM_ = 8>
+struct DirectCfg {
+    using E = E_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_, GM = GM_;
+    static constexpr int STAGES = STAGES_;
+    static constexpr int NW = WM * WN, NT = NW * kWave;
+    static constexpr int BK = 64;
+    static constexpr int BCH = BN / 8;                  // 16-byte chunks per k-row of B
+    static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+    static constexpr int TM = WTM / MF, TN = WTN / MF;
+    static constexpr int A_INSTR = BM / 8;   // one direct load = 64 chunks = 8 rows of A
+    static constexpr int B_INSTR = BCH;      // one direct load = 64 chunks = 512/BN k-rows of B
+    static constexpr int A_PER = A_INSTR / NW, B_PER = B_INSTR / NW;
+    static constexpr int NI = A_PER + B_PER;  // direct loads per wave per k-tile
+    static constexpr int STAGE_A = BM * 128, STAGE_B = BK * BN * 2;
+    static constexpr int STAGE_BYTES = STAGE_A + STAGE_B;
+    static_assert(sizeof(E) == 2, "16-bit inputs only");
+    static_assert(BN >= 128 && BN <= 512, "the B swizzle needs 16 to 64 chunks per k-row");
+    static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "loads split evenly over waves");
+    static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "whole blocks per wave");
+    static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "stages fit 160 KiB");
+    static_assert((STAGES - 2) * NI <= 63, "vmcnt counts at most 63 loads");
+};
+
+__device__ __forceinline__ int swz_a(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) | ((krow >> 1) & 4)) << 1; }
+
+// 16 bytes per lane from global memory (SGPR base + per-lane byte offset) into
+// LDS at lds_base + 16 * lane.  M0 carries the LDS base; nothing else in these
+// kernels uses M0.
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory");
+}
+
+// Wait until at most N of this wave's loads are outstanding and all its LDS
+// reads have returned, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_then_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
+    int64_t M, int64_t N, int64_t K, const typename Cfg::E* __restrict__ A, int64_t lda,
+    const typename Cfg::E* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
+    int tiles_m, int tiles_n) {
+    using E = typename Cfg::E;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, MF = Cfg::MF, TM = Cfg::TM, TN = Cfg::TN;
+    constexpr int NW = Cfg::NW, BCH = Cfg::BCH, S = Cfg::STAGES, NI = Cfg::NI;
+    using Op = MfmaOp<E, MF>;
+    using Acc = typename Op::Acc;
+    using L = AccLayout<MF>;
+
+    __shared__ __attribute__((aligned(1024))) char smem[S * Cfg::STAGE_BYTES];
+    // __shared__ arrays are generic pointers in HIP; an LDS pointer needs a C-style cast.
+    const MIGEMM_LDS char* const lds = (const MIGEMM_LDS char*)smem;
+    const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
+    const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
+
+    int pm, pn;
+    tile_coords<Cfg::GM>(blockIdx.x, tiles_m, tiles_n, pm, pn);
+    const int64_t m0 = static_cast<int64_t>(pm) * BM;
+    const int64_t n0 = static_cast<int64_t>(pn) * BN;
+
+    // Per-lane byte offsets of this wave's direct loads, relative to the tile
+    // origin (A + m0 * lda + k0, B + k0 * ldb + n0).  Rows of A past M and
+    // chunks of B past N are clamped, keeping every load in bounds.
+    uint32_t a_voff[Cfg::A_PER], b_voff[Cfg::B_PER];
+#pragma unroll
+    for (int q = 0; q < Cfg::A_PER; ++q) {
+        const int row = 8 * (wave + q * NW) + lane / 8;
+        const int chunk = (lane % 8) ^ swz_a(row);
+        const int64_t grow = min(m0 + row, M - 1);
+        a_voff[q] = static_cast<uint32_t>(((grow - m0) * lda + chunk * 8) * 2);
+    }
+#pragma unroll
+    for (int q = 0; q < Cfg::B_PER; ++q) {
+        const int krow = (wave + q * NW) * (64 / BCH) + lane / BCH;
+        const int chunk = (lane % BCH) ^ swz_b(krow);
+        const int64_t gcol = min(n0 + chunk * 8, N - 8);
+        b_voff[q] = static_cast<uint32_t>((krow * ldb + (gcol - n0)) * 2);
+    }
+    const E* const a_tile = A + m0 * lda;
+    const E* const b_tile = B + n0;
+
+    auto issue = [&](int kt) {
+        const int stage = kt % S;
+        const uint32_t sa = lds_addr + stage * Cfg::STAGE_BYTES;
+        const uint32_t sb = sa + Cfg::STAGE_A;
+        const E* ab = a_tile + static_cast<int64_t>(kt) * Cfg::BK;
+        const E* bb = b_tile + static_cast<int64_t>(kt) * Cfg::BK * ldb;
+#pragma unroll
+        for (int q = 0; q < Cfg::A_PER; ++q) dma16(sa + (wave + q * NW) * 1024, ab, a_voff[q]);
+#pragma unroll
+        for (int q = 0; q < Cfg::B_PER; ++q) dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q]);
+    };
+
+    Acc acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = Acc{};
+
+    // Fragment addressing.  MF = 16: lane (r + 16 g) feeds row r of a block and
+    // k = 8 g .. 8 g + 7 of a 32-k slab.  MF = 32: lane (r + 32 g), k = 8 g .. of
+    // a 16-k slab.  For B, lane j of each 16-lane group receives column j.
+    constexpr int G = kWave / MF;          // k-groups per slab
+    constexpr int SLAB_K = 8 * G;          // k per slab: 32 (MF 16) or 16 (MF 32)
+    constexpr int SLABS = Cfg::BK / SLAB_K;
+    const int ar = lane % MF, ag = lane / MF;
+    const int bj = lane % 16;
+    const int bcol = (MF == 16 ? 0 : 16 * ((lane % 32) / 16)) + 4 * (bj % 4);
+
+    struct Frags {
+        u32x4 a[TM];
+        u32x4 b[TN];
+    };
+    auto load_frags = [&](int kt, int s, Frags& f) {
+        const MIGEMM_LDS char* sa = lds + (kt % S) * Cfg::STAGE_BYTES;
+        const MIGEMM_LDS char* sb = sa + Cfg::STAGE_A;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm0 + i * MF + ar;
+            const int chunk = (s * G + ag) ^ swz_a(row);
+            f.a[i] = *(const MIGEMM_LDS u32x4*)(sa + row * 128 + chunk * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = wn0 + j * MF + bcol;
+            u32x2 h[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int krow = s * SLAB_K + 8 * ag + 4 * half + bj / 4;
+                const int chunk = (col / 8) ^ swz_b(krow);
+                const MIGEMM_LDS char* p = sb + krow * (BN * 2) + chunk * 16 + (col % 8) * 2;
+                h[half] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS s16x4*)p));
+            }
+            f.b[j] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+        }
+    };
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) Op::run(acc[i][j], f.a[i], f.b[j]);
+    };
+
+    const int KT = static_cast<int>(K / Cfg::BK);
+    // Prologue: k-tiles 0 .. S-2 in flight; wait for k-tile 0.
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+        if (t < KT) issue(t);
+    if (KT >= S - 1)
+        wait_then_barrier<(S - 2) * NI>();
+    else
+        wait_then_barrier<0>();
+
+    // Two fragment buffers: slab s of every k-tile runs from F[s & 1] while the
+    // next slab's fragments load into the other (SLABS is even, so slab 0 of
+    // the next k-tile lands in F[0] again and no registers are copied).
+    static_assert(SLABS % 2 == 0, "fragment ping-pong needs an even slab count");
+    Frags F[2];
+    load_frags(0, 0, F[0]);
+    for (int kt = 0; kt < KT; ++kt) {
+        const bool more = kt + S - 1 < KT;
+        if (more) issue(kt + S - 1);
+        // sched_barrier(0) fences keep each slab's prefetch ahead of the
+        // previous slab's matrix instructions instead of letting the scheduler
+        // sink the LDS reads next to their first use.
+#pragma unroll
+        for (int s = 0; s + 1 < SLABS; ++s) {
+            load_frags(kt, s + 1, F[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(F[s & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kt + 1 < KT) {
+            // k-tile kt+1 must have landed; later ones may still be in flight.
+            if (more)
+                wait_then_barrier<(S - 2) * NI>();
+            else
+                wait_then_barrier<0>();
+            load_frags(kt + 1, 0, F[0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma(F[1]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
+    const int lc = L::col(lane);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = n0 + wn0 + j * MF + lc;
+#pragma unroll
+            for (int r = 0; r < L::R; ++r) {
+                const int64_t row = m0 + wm0 + i * MF + L::row(lane, r);
+                if (full_mn || (row < M && col < N)) C[row * ldc + col] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+// True when the direct kernel's preconditions hold for these arguments: aligned
+// operands, whole 16-byte chunks, K a multiple of the k-tile, and per-lane
+// offsets (256 rows of A, 64 rows of B) that fit 31 bits.
+inline bool direct_ok(const GemmArgs& g) {
+    return aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+           g.K % 64 == 0 && g.N % 8 == 0 && g.K > 0 && g.M > 0 && g.N >= 8 &&
+           g.lda < (int64_t(1) << 21) && g.ldb < (int64_t(1) << 23);
+}
+
+template <class Cfg>
+hipError_t launch_direct_cfg(const GemmArgs& g) {
+    using E = typename Cfg::E;
+    const int64_t tm = ceil_div(g.M, Cfg::BM), tn = ceil_div(g.N, Cfg::BN);
+    if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
+    mfma16_direct_kernel<Cfg><<<dim3(static_cast<unsigned>(tm * tn)), dim3(Cfg::NT), 0,
+                                 g.stream>>>(g.M, g.N, g.K, static_cast<const E*>(g.A), g.lda,
+                                             static_cast<const E*>(g.B), g.ldb, g.C, g.ldc,
+                                             static_cast<int>(tm), static_cast<int>(tn));
+    return hipGetLastError();
+}
+
+}  // namespace migemm

@@ -149,3 +149,24 @@ def test_run_to_run_bitwise_determinism(dtype):
         C1, _ = run_gemm(A, B, dtype, variant=v, config=c)
         C2, _ = run_gemm(A, B, dtype, variant=v, config=c)
         assert torch.equal(C1, C2)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_direct_staging_edges(dtype):
+    """Configurations with direct global->LDS staging: ragged M, N a multiple of 8
+    that is not a multiple of the tile, K a multiple of 64, padded leading
+    dimensions (multiples of 8), and a K of one k-tile."""
+    names = [mg.migemm_config_name(mg.MFMA16, c) for c in range(mg.migemm_config_count(mg.MFMA16))]
+    direct = [c for c, n in enumerate(names) if n.startswith("direct")]
+    assert direct
+    shapes = [(300, 264, 128, None, None), (1000, 520, 640, None, None), (256, 256, 64, None, None),
+              (37, 8, 192, None, None), (513, 776, 256, 264, 784), (64, 1024, 1024, 1032, 1040)]
+    for (M, N, K, lda, ldb) in shapes:
+        A, B = inputs.pair(M, N, K, dtype, "normal", seed=M + N + K)
+        ref = None
+        for c in direct:
+            say(f"direct {dtype} {M}x{N}x{K} lda={lda} ldb={ldb} cfg={names[c]}")
+            C, _ = run_gemm(A, B, dtype, variant=mg.MFMA16, config=c, lda=lda, ldb=ldb)
+            from gpu_helpers import oracle_ref
+            ref = ref or oracle_ref(A, B, dtype)
+            check(C, A, B, dtype, ref=ref)
