@@ -201,7 +201,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--sweep", action="store_true",
-                    help="also time every configuration of every variant on the workload")
+                    help="also time every configuration of every variant on every workload")
+    ap.add_argument("--sweep-only", default="",
+                    help="comma-separated workloads the sweep covers (default: all)")
     ap.add_argument("--profile-pass", type=int, default=0, metavar="REPS",
                     help="only run the copy calibration and REPS launches (for rocprofv3)")
     a = ap.parse_args()
@@ -246,7 +248,10 @@ def main():
 
     sweep = {}
     if a.sweep:
-        for name in [w.name] + EXTRA:
+        names = [w.name] + EXTRA
+        if a.sweep_only:
+            names = [n for n in names if n in a.sweep_only.split(",")]
+        for name in names:
             wx = inputs.WORKLOADS[name]
             px = p if name == w.name else Problem(wx)
             res = {}

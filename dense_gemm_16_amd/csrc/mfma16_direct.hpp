@@ -56,24 +56,29 @@ namespace migemm {
 #define MIGEMM_LDS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// SCHED: 0 = prefetch block then matrix block per slab; 1 = as 0 with the wave's
+// priority raised during its matrix block (s_setprio); 2 = one LDS read issued
+// after each matrix instruction (sched_group_barrier); 3 = 2 with raised priority.
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
-          int GM_ = 8>
+          int BK_ = 64, int GM_ = 8, int SCHED_ = 0>
 struct DirectCfg {
     using E = E_;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_, GM = GM_;
-    static constexpr int STAGES = STAGES_;
+    static constexpr int STAGES = STAGES_, BK = BK_, SCHED = SCHED_;
     static constexpr int NW = WM * WN, NT = NW * kWave;
-    static constexpr int BK = 64;
+    static constexpr int CA = BK / 8;                   // 16-byte chunks per row of A
     static constexpr int BCH = BN / 8;                  // 16-byte chunks per k-row of B
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
     static constexpr int TM = WTM / MF, TN = WTN / MF;
-    static constexpr int A_INSTR = BM / 8;   // one direct load = 64 chunks = 8 rows of A
-    static constexpr int B_INSTR = BCH;      // one direct load = 64 chunks = 512/BN k-rows of B
+    static constexpr int A_RPI = 64 / CA;               // rows of A per direct load (64 chunks)
+    static constexpr int B_RPI = 64 / BCH;              // k-rows of B per direct load
+    static constexpr int A_INSTR = BM / A_RPI, B_INSTR = BK / B_RPI;
     static constexpr int A_PER = A_INSTR / NW, B_PER = B_INSTR / NW;
     static constexpr int NI = A_PER + B_PER;  // direct loads per wave per k-tile
-    static constexpr int STAGE_A = BM * 128, STAGE_B = BK * BN * 2;
+    static constexpr int STAGE_A = BM * BK * 2, STAGE_B = BK * BN * 2;
     static constexpr int STAGE_BYTES = STAGE_A + STAGE_B;
     static_assert(sizeof(E) == 2, "16-bit inputs only");
+    static_assert(BK == 32 || BK == 64, "A rows are 64 or 128 bytes");
     static_assert(BN >= 128 && BN <= 512, "the B swizzle needs 16 to 64 chunks per k-row");
     static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "loads split evenly over waves");
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "whole blocks per wave");
@@ -81,7 +86,15 @@ struct DirectCfg {
     static_assert((STAGES - 2) * NI <= 63, "vmcnt counts at most 63 loads");
 };
 
-__device__ __forceinline__ int swz_a(int row) { return (row ^ (row >> 3)) & 7; }
+// Physical chunk of logical chunk c in row `row` of the A image (CA chunks per row).
+// 128-byte rows: c ^ ((row ^ (row >> 3)) & 7).  64-byte rows (four rows per 256
+// bytes of banks): c ^ ((row >> 2) & 3), so sixteen consecutive rows reading one
+// logical chunk cover the 64 banks once.
+template <int CA>
+__device__ __forceinline__ int swz_a(int row) {
+    if constexpr (CA == 8) return (row ^ (row >> 3)) & 7;
+    return (row >> 2) & 3;
+}
 __device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) | ((krow >> 1) & 4)) << 1; }
 
 // 16 bytes per lane from global memory (SGPR base + per-lane byte offset) into
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     int tiles_m, int tiles_n) {
     using E = typename Cfg::E;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, MF = Cfg::MF, TM = Cfg::TM, TN = Cfg::TN;
-    constexpr int NW = Cfg::NW, BCH = Cfg::BCH, S = Cfg::STAGES, NI = Cfg::NI;
+    constexpr int NW = Cfg::NW, BCH = Cfg::BCH, S = Cfg::STAGES, NI = Cfg::NI, CA = Cfg::CA;
     using Op = MfmaOp<E, MF>;
     using Acc = typename Op::Acc;
     using L = AccLayout<MF>;
@@ -134,14 +147,14 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     uint32_t a_voff[Cfg::A_PER], b_voff[Cfg::B_PER];
 #pragma unroll
     for (int q = 0; q < Cfg::A_PER; ++q) {
-        const int row = 8 * (wave + q * NW) + lane / 8;
-        const int chunk = (lane % 8) ^ swz_a(row);
+        const int row = Cfg::A_RPI * (wave + q * NW) + lane / CA;
+        const int chunk = (lane % CA) ^ swz_a<CA>(row);
         const int64_t grow = min(m0 + row, M - 1);
         a_voff[q] = static_cast<uint32_t>(((grow - m0) * lda + chunk * 8) * 2);
     }
 #pragma unroll
     for (int q = 0; q < Cfg::B_PER; ++q) {
-        const int krow = (wave + q * NW) * (64 / BCH) + lane / BCH;
+        const int krow = (wave + q * NW) * Cfg::B_RPI + lane / BCH;
         const int chunk = (lane % BCH) ^ swz_b(krow);
         const int64_t gcol = min(n0 + chunk * 8, N - 8);
         b_voff[q] = static_cast<uint32_t>((krow * ldb + (gcol - n0)) * 2);
@@ -187,8 +200,8 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = wm0 + i * MF + ar;
-            const int chunk = (s * G + ag) ^ swz_a(row);
-            f.a[i] = *(const MIGEMM_LDS u32x4*)(sa + row * 128 + chunk * 16);
+            const int chunk = (s * G + ag) ^ swz_a<CA>(row);
+            f.a[i] = *(const MIGEMM_LDS u32x4*)(sa + row * (CA * 16) + chunk * 16);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -210,6 +223,33 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j) Op::run(acc[i][j], f.a[i], f.b[j]);
+    };
+    // One slab step: LDS reads of the next fragments (load) and this slab's
+    // matrix instructions (f), ordered as the SCHED policy says.  s_setprio is
+    // a scheduling boundary, so it brackets the whole step.
+    constexpr int kReads = TM + 2 * TN;  // LDS read instructions per slab
+    auto slab_step = [&](bool do_load, int lkt, int ls, Frags& fl, const Frags& f) {
+        constexpr bool prio = Cfg::SCHED == 1 || Cfg::SCHED == 3;
+        if constexpr (Cfg::SCHED == 3) __builtin_amdgcn_s_setprio(1);
+        if (do_load) load_frags(lkt, ls, fl);
+        if constexpr (Cfg::SCHED == 2 || Cfg::SCHED == 3) {
+            mma(f);
+            // one matrix instruction, then one LDS read, while reads remain
+#pragma unroll
+            for (int r = 0; r < kReads; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - kReads, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (prio) __builtin_amdgcn_s_setprio(1);
+            mma(f);
+            if constexpr (prio) __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (Cfg::SCHED == 3) __builtin_amdgcn_s_setprio(0);
     };
 
     const int KT = static_cast<int>(K / Cfg::BK);
@@ -235,23 +275,16 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         // previous slab's matrix instructions instead of letting the scheduler
         // sink the LDS reads next to their first use.
 #pragma unroll
-        for (int s = 0; s + 1 < SLABS; ++s) {
-            load_frags(kt, s + 1, F[(s + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(F[s & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (kt + 1 < KT) {
+        for (int s = 0; s + 1 < SLABS; ++s) slab_step(true, kt, s + 1, F[(s + 1) & 1], F[s & 1]);
+        const bool next = kt + 1 < KT;
+        if (next) {
             // k-tile kt+1 must have landed; later ones may still be in flight.
             if (more)
                 wait_then_barrier<(S - 2) * NI>();
             else
                 wait_then_barrier<0>();
-            load_frags(kt + 1, 0, F[0]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        mma(F[1]);
-        __builtin_amdgcn_sched_barrier(0);
+        slab_step(next, kt + 1, 0, F[0], F[1]);
     }
 
     const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
@@ -271,11 +304,11 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 }
 
 // True when the direct kernel's preconditions hold for these arguments: aligned
-// operands, whole 16-byte chunks, K a multiple of the k-tile, and per-lane
+// operands, whole 16-byte chunks, K a multiple of the k-tile (bk), and per-lane
 // offsets (256 rows of A, 64 rows of B) that fit 31 bits.
-inline bool direct_ok(const GemmArgs& g) {
+inline bool direct_ok(const GemmArgs& g, int bk = 64) {
     return aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
-           g.K % 64 == 0 && g.N % 8 == 0 && g.K > 0 && g.M > 0 && g.N >= 8 &&
+           g.K % bk == 0 && g.N % 8 == 0 && g.K > 0 && g.M > 0 && g.N >= 8 &&
            g.lda < (int64_t(1) << 21) && g.ldb < (int64_t(1) << 23);
 }
 
