@@ -52,6 +52,11 @@ template <typename E> struct Cfgs {
     using D24 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 0>;   // 4-row bands
     using D25 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 16, 0>;  // 16-row bands
     using D26 = DirectCfg<E, 256, 256, 2, 2, 32, 2, 64, 8, 3>;   // 4 waves, interleave + prio
+    using D27 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 1>;  // spread direct loads
+    using D28 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 2>;  // non-temporal C
+    using D29 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 3>;  // both
+    using D30 = DirectCfg<E, 256, 256, 2, 4, 32, 4, 32, 4, 2, 2>;  // BK 32 x 4 stages, nt C
+    using D31 = DirectCfg<E, 256, 256, 2, 2, 32, 2, 64, 4, 3, 3>;  // 4 waves, all of it
 };
 
 template <class D, class Fallback>
@@ -89,6 +94,11 @@ hipError_t launch_typed(const GemmArgs& g, int config) {
         case 24: return direct_or<typename T::D24, typename T::C0>(g);
         case 25: return direct_or<typename T::D25, typename T::C0>(g);
         case 26: return direct_or<typename T::D26, typename T::C0>(g);
+        case 27: return direct_or<typename T::D27, typename T::C0>(g);
+        case 28: return direct_or<typename T::D28, typename T::C0>(g);
+        case 29: return direct_or<typename T::D29, typename T::C0>(g);
+        case 30: return direct_or<typename T::D30, typename T::C0>(g);
+        case 31: return direct_or<typename T::D31, typename T::C0>(g);
         default: return launch_mfma_cfg<typename T::C0>(g);
     }
 }
@@ -107,7 +117,12 @@ const char* const kNames[] = {
     "direct 256x128x64 4w 32x32x16 s3", "direct 256x256x64 8w 32x32x16 prio",
     "direct 256x256x64 8w 32x32x16 ilv", "direct 256x256x64 8w 32x32x16 ilv+prio",
     "direct 256x256x64 8w 32x32x16 gm4", "direct 256x256x64 8w 32x32x16 gm16",
-    "direct 256x256x64 4w 32x32x16 ilv+prio"};
+    "direct 256x256x64 4w 32x32x16 ilv+prio",
+    "direct 256x256x64 8w 32x32x16 gm4 ilv spread",
+    "direct 256x256x64 8w 32x32x16 gm4 ilv ntC",
+    "direct 256x256x64 8w 32x32x16 gm4 ilv spread ntC",
+    "direct 256x256x32 8w 32x32x16 s4 gm4 ilv ntC",
+    "direct 256x256x64 4w 32x32x16 gm4 ilv+prio spread ntC"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace

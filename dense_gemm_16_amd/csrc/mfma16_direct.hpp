@@ -59,12 +59,14 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // SCHED: 0 = prefetch block then matrix block per slab; 1 = as 0 with the wave's
 // priority raised during its matrix block (s_setprio); 2 = one LDS read issued
 // after each matrix instruction (sched_group_barrier); 3 = 2 with raised priority.
+// FLAGS: bit 0 = spread each k-tile's direct loads over the slabs before the
+// barrier instead of issuing them in one burst; bit 1 = non-temporal C stores.
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
-          int BK_ = 64, int GM_ = 8, int SCHED_ = 0>
+          int BK_ = 64, int GM_ = 8, int SCHED_ = 0, int FLAGS_ = 0>
 struct DirectCfg {
     using E = E_;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_, GM = GM_;
-    static constexpr int STAGES = STAGES_, BK = BK_, SCHED = SCHED_;
+    static constexpr int STAGES = STAGES_, BK = BK_, SCHED = SCHED_, FLAGS = FLAGS_;
     static constexpr int NW = WM * WN, NT = NW * kWave;
     static constexpr int CA = BK / 8;                   // 16-byte chunks per row of A
     static constexpr int BCH = BN / 8;                  // 16-byte chunks per k-row of B
@@ -162,17 +164,23 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     const E* const a_tile = A + m0 * lda;
     const E* const b_tile = B + n0;
 
-    auto issue = [&](int kt) {
+    // Issues this wave's direct loads number lo .. hi-1 (of NI: A's first, then
+    // B's) of k-tile kt.
+    auto issue_range = [&](int kt, int lo, int hi) {
         const int stage = kt % S;
         const uint32_t sa = lds_addr + stage * Cfg::STAGE_BYTES;
         const uint32_t sb = sa + Cfg::STAGE_A;
         const E* ab = a_tile + static_cast<int64_t>(kt) * Cfg::BK;
         const E* bb = b_tile + static_cast<int64_t>(kt) * Cfg::BK * ldb;
 #pragma unroll
-        for (int q = 0; q < Cfg::A_PER; ++q) dma16(sa + (wave + q * NW) * 1024, ab, a_voff[q]);
+        for (int q = 0; q < Cfg::A_PER; ++q)
+            if (q >= lo && q < hi) dma16(sa + (wave + q * NW) * 1024, ab, a_voff[q]);
 #pragma unroll
-        for (int q = 0; q < Cfg::B_PER; ++q) dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q]);
+        for (int q = 0; q < Cfg::B_PER; ++q)
+            if (Cfg::A_PER + q >= lo && Cfg::A_PER + q < hi)
+                dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q]);
     };
+    auto issue = [&](int kt) { issue_range(kt, 0, NI); };
 
     Acc acc[TM][TN];
 #pragma unroll
@@ -268,14 +276,20 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     static_assert(SLABS % 2 == 0, "fragment ping-pong needs an even slab count");
     Frags F[2];
     load_frags(0, 0, F[0]);
+    constexpr bool spread = (Cfg::FLAGS & 1) && SLABS > 2;
     for (int kt = 0; kt < KT; ++kt) {
         const bool more = kt + S - 1 < KT;
-        if (more) issue(kt + S - 1);
+        if (!spread && more) issue(kt + S - 1);
         // sched_barrier(0) fences keep each slab's prefetch ahead of the
         // previous slab's matrix instructions instead of letting the scheduler
-        // sink the LDS reads next to their first use.
+        // sink the LDS reads next to their first use.  With spreading, the
+        // slabs before the barrier each issue their share of the direct loads.
 #pragma unroll
-        for (int s = 0; s + 1 < SLABS; ++s) slab_step(true, kt, s + 1, F[(s + 1) & 1], F[s & 1]);
+        for (int s = 0; s + 1 < SLABS; ++s) {
+            if (spread && more)
+                issue_range(kt + S - 1, s * NI / (SLABS - 1), (s + 1) * NI / (SLABS - 1));
+            slab_step(true, kt, s + 1, F[(s + 1) & 1], F[s & 1]);
+        }
         const bool next = kt + 1 < KT;
         if (next) {
             // k-tile kt+1 must have landed; later ones may still be in flight.
@@ -297,7 +311,12 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 #pragma unroll
             for (int r = 0; r < L::R; ++r) {
                 const int64_t row = m0 + wm0 + i * MF + L::row(lane, r);
-                if (full_mn || (row < M && col < N)) C[row * ldc + col] = acc[i][j][r];
+                if (full_mn || (row < M && col < N)) {
+                    if constexpr (Cfg::FLAGS & 2)
+                        __builtin_nontemporal_store(acc[i][j][r], C + row * ldc + col);
+                    else
+                        C[row * ldc + col] = acc[i][j][r];
+                }
             }
         }
     }
