@@ -192,8 +192,8 @@ def profile_pass(p, reps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4-bf16-8192")
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--config", type=int, default=-1)
