@@ -109,11 +109,18 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, const void* sbase, uint
                  : "memory");
 }
 
-// Wait until at most N of this wave's loads are outstanding and all its LDS
-// reads have returned, then meet the other waves.
+// Wait until at most N of this wave's direct loads are outstanding (inline asm:
+// the compiler does not track those loads), then until all its LDS reads have
+// returned, then meet the other waves.  The LDS wait and the barrier use the
+// builtins so the compiler's wait-count bookkeeping knows the reads completed;
+// the empty asm statements keep memory operations from moving across.
 template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+    // s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maxima (gfx9 encoding)
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" : : : "memory");
 }
 
 template <class Cfg>
@@ -205,12 +212,14 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     auto load_frags = [&](int kt, int s, Frags& f) {
         const MIGEMM_LDS char* sa = lds + (kt % S) * Cfg::STAGE_BYTES;
         const MIGEMM_LDS char* sb = sa + Cfg::STAGE_A;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        // Issued in the order the matrix instructions consume them (i-major):
+        // a[0], then every b[j], then a[1] ...
+        auto read_a = [&](int i) {
             const int row = wm0 + i * MF + ar;
             const int chunk = (s * G + ag) ^ swz_a<CA>(row);
             f.a[i] = *(const MIGEMM_LDS u32x4*)(sa + row * (CA * 16) + chunk * 16);
-        }
+        };
+        read_a(0);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int col = wn0 + j * MF + bcol;
@@ -225,6 +234,8 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
             }
             f.b[j] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
         }
+#pragma unroll
+        for (int i = 1; i < TM; ++i) read_a(i);
     };
     auto mma = [&](const Frags& f) {
 #pragma unroll
@@ -277,28 +288,36 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     Frags F[2];
     load_frags(0, 0, F[0]);
     constexpr bool spread = (Cfg::FLAGS & 1) && SLABS > 2;
-    for (int kt = 0; kt < KT; ++kt) {
-        const bool more = kt + S - 1 < KT;
-        if (!spread && more) issue(kt + S - 1);
-        // sched_barrier(0) fences keep each slab's prefetch ahead of the
-        // previous slab's matrix instructions instead of letting the scheduler
-        // sink the LDS reads next to their first use.  With spreading, the
-        // slabs before the barrier each issue their share of the direct loads.
+    // All slabs of k-tile kt but the last, each reading the next slab's fragments.
+    auto front_slabs = [&](int kt, bool more) {
 #pragma unroll
         for (int s = 0; s + 1 < SLABS; ++s) {
             if (spread && more)
                 issue_range(kt + S - 1, s * NI / (SLABS - 1), (s + 1) * NI / (SLABS - 1));
             slab_step(true, kt, s + 1, F[(s + 1) & 1], F[s & 1]);
         }
-        const bool next = kt + 1 < KT;
-        if (next) {
-            // k-tile kt+1 must have landed; later ones may still be in flight.
-            if (more)
-                wait_then_barrier<(S - 2) * NI>();
-            else
-                wait_then_barrier<0>();
-        }
-        slab_step(next, kt + 1, 0, F[0], F[1]);
+    };
+    // Every k-tile but the last ends with the barrier that makes k-tile kt+1
+    // visible, then runs its last slab while slab 0 of kt+1 is read.  The last
+    // k-tile is peeled off so that the code after the barrier has one
+    // predecessor and the compiler's wait counts stay exact there.
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+        const bool more = kt + S - 1 < KT;
+        if (!spread && more) issue(kt + S - 1);
+        // sched_barrier(0) fences keep each slab's prefetch ahead of the
+        // previous slab's matrix instructions instead of letting the scheduler
+        // sink the LDS reads next to their first use.
+        front_slabs(kt, more);
+        // k-tile kt+1 must have landed; later ones may still be in flight.
+        if (more)
+            wait_then_barrier<(S - 2) * NI>();
+        else
+            wait_then_barrier<0>();
+        slab_step(true, kt + 1, 0, F[0], F[1]);
+    }
+    if (KT > 0) {
+        front_slabs(KT - 1, false);
+        slab_step(false, 0, 0, F[0], F[1]);
     }
 
     const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
