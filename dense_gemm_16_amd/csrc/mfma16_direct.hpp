@@ -58,9 +58,13 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // SCHED: 0 = prefetch block then matrix block per slab; 1 = as 0 with the wave's
 // priority raised during its matrix block (s_setprio); 2 = one LDS read issued
-// after each matrix instruction (sched_group_barrier); 3 = 2 with raised priority.
+// after each matrix instruction (sched_group_barrier); 3 = 2 with raised priority;
+// 4 = ping-pong: two groups of four waves (one wave of each per SIMD) alternate
+// between a phase of matrix instructions and a phase of LDS reads and direct
+// loads, swapping at every barrier.
 // FLAGS: bit 0 = spread each k-tile's direct loads over the slabs before the
-// barrier instead of issuing them in one burst; bit 1 = non-temporal C stores.
+// barrier instead of issuing them in one burst; bit 1 = non-temporal C stores;
+// bit 2 = keep the accumulators in AGPRs (see below).
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
           int BK_ = 64, int GM_ = 8, int SCHED_ = 0, int FLAGS_ = 0>
 struct DirectCfg {
@@ -114,6 +118,13 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, const void* sbase, uint
 // returned, then meet the other waves.  The LDS wait and the barrier use the
 // builtins so the compiler's wait-count bookkeeping knows the reads completed;
 // the empty asm statements keep memory operations from moving across.
+__device__ __forceinline__ void lds_wait_then_barrier() {
+    asm volatile("" : : : "memory");
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" : : : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -173,7 +184,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 
     // Issues this wave's direct loads number lo .. hi-1 (of NI: A's first, then
     // B's) of k-tile kt.
-    auto issue_range = [&](int kt, int lo, int hi) {
+    auto issue_range = [&](int kt, int lo, int hi) __attribute__((always_inline)) {
         const int stage = kt % S;
         const uint32_t sa = lds_addr + stage * Cfg::STAGE_BYTES;
         const uint32_t sb = sa + Cfg::STAGE_A;
@@ -187,13 +198,22 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
             if (Cfg::A_PER + q >= lo && Cfg::A_PER + q < hi)
                 dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q]);
     };
-    auto issue = [&](int kt) { issue_range(kt, 0, NI); };
+    auto issue = [&](int kt) __attribute__((always_inline)) { issue_range(kt, 0, NI); };
 
     Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = Acc{};
+    if constexpr (Cfg::FLAGS & 4) {
+        // The compiler gives matrix instructions AGPR accumulators only in
+        // functions that may use AGPRs otherwise; an empty asm statement with an
+        // AGPR operand makes this one such a function.  Accumulators in AGPRs keep
+        // the C-operand traffic of the matrix instructions off the VGPR file that
+        // the LDS reads write into.
+        float agpr_hint = 0.0f;
+        asm volatile("" : "+a"(agpr_hint));
+    }
 
     // Fragment addressing.  MF = 16: lane (r + 16 g) feeds row r of a block and
     // k = 8 g .. 8 g + 7 of a 32-k slab.  MF = 32: lane (r + 32 g), k = 8 g .. of
@@ -209,7 +229,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         u32x4 a[TM];
         u32x4 b[TN];
     };
-    auto load_frags = [&](int kt, int s, Frags& f) {
+    auto load_frags = [&](int kt, int s, Frags& f) __attribute__((always_inline)) {
         const MIGEMM_LDS char* sa = lds + (kt % S) * Cfg::STAGE_BYTES;
         const MIGEMM_LDS char* sb = sa + Cfg::STAGE_A;
         // Issued in the order the matrix instructions consume them (i-major):
@@ -237,7 +257,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 #pragma unroll
         for (int i = 1; i < TM; ++i) read_a(i);
     };
-    auto mma = [&](const Frags& f) {
+    auto mma = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -247,11 +267,11 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     // matrix instructions (f), ordered as the SCHED policy says.  s_setprio is
     // a scheduling boundary, so it brackets the whole step.
     constexpr int kReads = TM + 2 * TN;  // LDS read instructions per slab
-    auto slab_step = [&](bool do_load, int lkt, int ls, Frags& fl, const Frags& f) {
+    auto slab_step = [&](bool do_load, int lkt, int ls, Frags& fl, const Frags& f) __attribute__((always_inline)) {
         constexpr bool prio = Cfg::SCHED == 1 || Cfg::SCHED == 3;
         if constexpr (Cfg::SCHED == 3) __builtin_amdgcn_s_setprio(1);
         if (do_load) load_frags(lkt, ls, fl);
-        if constexpr (Cfg::SCHED == 2 || Cfg::SCHED == 3) {
+        if constexpr (Cfg::SCHED == 2 || Cfg::SCHED == 3 || Cfg::SCHED == 6) {
             mma(f);
             // one matrix instruction, then one LDS read, while reads remain
 #pragma unroll
@@ -272,6 +292,117 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     };
 
     const int KT = static_cast<int>(K / Cfg::BK);
+    if constexpr (Cfg::SCHED == 4 || Cfg::SCHED == 5) {
+        // Ping-pong.  A k-tile has two halves h = 2 kt, 2 kt + 1 (SLABS / 2 slabs
+        // each).  Waves 0-3 (group X) and 4-7 (group Y) share the SIMDs pairwise.
+        // Phase p (one barrier after each): X computes half p/2 on even p and
+        // reads half (p+1)/2 on odd p; Y reads half p/2 on even p and computes
+        // half (p-1)/2 on odd p.  So on every SIMD one wave issues only matrix
+        // instructions while the other reads LDS, and the barrier that ends a
+        // phase is hidden behind the partner's matrix work.
+        // Direct loads: k-tile kt (>= 2) is issued in the read phase of half
+        // 2 (kt - 1), i.e. phases 4 kt - 5 (X) and 4 kt - 4 (Y); the barrier ending
+        // phase 4 kt - 2 waits for it (vmcnt(0): nothing later has been issued by
+        // then); its first reader is X in phase 4 kt - 1.  It overwrites the stage
+        // of k-tile kt - 2, whose last reads were in phase 4 kt - 6 and completed
+        // before that phase's barrier.
+        static_assert(S == 2 && NW == 8 && SLABS % 2 == 0, "ping-pong layout");
+        constexpr int HS = SLABS / 2;
+        const int grp = wave / 4;
+        Frags P[HS];
+        const int H = 2 * KT;
+        // SCHED 4 issues a k-tile's direct loads in the read phase; SCHED 5 in the
+        // compute phase of the same half (phases 4 kt - 4 for X, 4 kt - 3 for Y,
+        // inside the same legal window), one load after every other matrix
+        // instruction, so the address unit works while the matrix pipe does.
+        constexpr bool dma_in_compute = Cfg::SCHED == 5;
+        auto read_half = [&](int h) {
+            const int kt = h / 2;
+            if (!dma_in_compute && (h & 1) == 0 && h >= 2 && kt + 1 < KT) issue(kt + 1);
+#pragma unroll
+            for (int s = 0; s < HS; ++s) load_frags(kt, (h & 1) * HS + s, P[s]);
+        };
+        auto compute_half = [&](int h) {
+            const int kt = h / 2;
+            if (dma_in_compute && (h & 1) == 0 && h >= 2 && kt + 1 < KT) {
+                static_assert(HS * TM * TN >= 2 * NI, "room to interleave the loads");
+                int n = 0;
+#pragma unroll
+                for (int s = 0; s < HS; ++s)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) {
+                            Op::run(acc[i][j], P[s].a[i], P[s].b[j]);
+                            if ((n & 1) && n / 2 < NI) issue_range(kt + 1, n / 2, n / 2 + 1);
+                            ++n;
+                        }
+            } else {
+#pragma unroll
+                for (int s = 0; s < HS; ++s) mma(P[s]);
+            }
+        };
+        issue(0);
+        if (KT > 1) {
+            issue(1);
+            wait_then_barrier<NI>();
+        } else {
+            wait_then_barrier<0>();
+        }
+        if (grp == 0) read_half(0);
+        for (int p = 0; p < 2 * H; ++p) {
+            const bool compute = ((p & 1) == 0) == (grp == 0);
+            if (compute) {
+                compute_half(grp == 0 ? p / 2 : (p - 1) / 2);
+            } else {
+                const int h = grp == 0 ? (p + 1) / 2 : p / 2;
+                if (h < H) read_half(h);
+            }
+            if ((p & 3) == 2)
+                wait_then_barrier<0>();
+            else
+                lds_wait_then_barrier();
+        }
+    } else if constexpr (Cfg::SCHED == 6) {
+        // Fragments read two slabs ahead.  A k-tile has four slabs and slab s of
+        // every k-tile lives in register buffer F[s], so slab s loads slab s+2
+        // into F[(s+2) % 4], a buffer last used two slabs earlier.  The barrier
+        // that makes k-tile kt+1 visible sits after slab 1 of kt: by then every
+        // read of kt's stage has been issued (slabs 2 and 3 are read during slabs
+        // 0 and 1) and completed (the LDS wait before the barrier), so right
+        // after the barrier the direct loads of k-tile kt+S refill that stage;
+        // they have a whole k-tile to land before the barrier that needs them.
+        // Slabs 2 and 3 of kt read slabs 0 and 1 of kt+1.
+        static_assert(SLABS == 4, "four slabs per k-tile");
+        static_assert((S - 1) * NI <= 63, "vmcnt counts at most 63 loads");
+#pragma unroll
+        for (int t = 0; t < S; ++t)
+            if (t < KT) issue(t);
+        if (KT >= S)
+            wait_then_barrier<(S - 1) * NI>();
+        else
+            wait_then_barrier<0>();
+        Frags F[4];
+        load_frags(0, 0, F[0]);
+        load_frags(0, 1, F[1]);
+        for (int kt = 0; kt + 1 < KT; ++kt) {
+            slab_step(true, kt, 2, F[2], F[0]);
+            slab_step(true, kt, 3, F[3], F[1]);
+            // k-tile kt+1 must have landed: the loads issued after it are those of
+            // k-tiles kt+2 .. kt+S-1, when they exist.
+            if (kt + S - 1 < KT)
+                wait_then_barrier<(S - 2) * NI>();
+            else
+                wait_then_barrier<0>();
+            if (kt + S < KT) issue(kt + S);
+            slab_step(true, kt + 1, 0, F[0], F[2]);
+            slab_step(true, kt + 1, 1, F[1], F[3]);
+        }
+        slab_step(true, KT - 1, 2, F[2], F[0]);
+        slab_step(true, KT - 1, 3, F[3], F[1]);
+        slab_step(false, 0, 0, F[0], F[2]);
+        slab_step(false, 0, 0, F[1], F[3]);
+    } else {
     // Prologue: k-tiles 0 .. S-2 in flight; wait for k-tile 0.
 #pragma unroll
     for (int t = 0; t < S - 1; ++t)
@@ -319,6 +450,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         front_slabs(KT - 1, false);
         slab_step(false, 0, 0, F[0], F[1]);
     }
+    }  // SCHED != 4
 
     const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
     const int lc = L::col(lane);
