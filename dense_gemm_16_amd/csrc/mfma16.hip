@@ -57,13 +57,8 @@ template <typename E> struct Cfgs {
     using D29 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 3>;  // both
     using D30 = DirectCfg<E, 256, 256, 2, 4, 32, 4, 32, 4, 2, 2>;  // BK 32 x 4 stages, nt C
     using D31 = DirectCfg<E, 256, 256, 2, 2, 32, 2, 64, 4, 3, 3>;  // 4 waves, all of it
-    using D32 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 4, 2>;  // ping-pong, 32x32x16
-    using D33 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 2>;  // ping-pong, 16x16x32
-    using D34 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 5, 2>;  // ping-pong, loads in compute
-    using D35 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 6, 2>;  // fragments 2 slabs ahead
-    using D36 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 8, 6, 2>;  // same, gm8
-    using D37 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 6>;  // D28 + AGPR accumulators
-    using D38 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 6, 6>;  // D35 + AGPR accumulators
+    // 16x16x32 instructions with AGPR accumulators and early direct loads
+    using D32 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 14>;
 };
 
 template <class D, class Fallback>
@@ -107,12 +102,6 @@ hipError_t launch_typed(const GemmArgs& g, int config) {
         case 30: return direct_or<typename T::D30, typename T::C0>(g);
         case 31: return direct_or<typename T::D31, typename T::C0>(g);
         case 32: return direct_or<typename T::D32, typename T::C0>(g);
-        case 33: return direct_or<typename T::D33, typename T::C0>(g);
-        case 34: return direct_or<typename T::D34, typename T::C0>(g);
-        case 35: return direct_or<typename T::D35, typename T::C0>(g);
-        case 36: return direct_or<typename T::D36, typename T::C0>(g);
-        case 37: return direct_or<typename T::D37, typename T::C0>(g);
-        case 38: return direct_or<typename T::D38, typename T::C0>(g);
         default: return launch_mfma_cfg<typename T::C0>(g);
     }
 }
@@ -137,13 +126,7 @@ const char* const kNames[] = {
     "direct 256x256x64 8w 32x32x16 gm4 ilv spread ntC",
     "direct 256x256x32 8w 32x32x16 s4 gm4 ilv ntC",
     "direct 256x256x64 4w 32x32x16 gm4 ilv+prio spread ntC",
-    "direct 256x256x64 8w 32x32x16 gm4 pingpong ntC",
-    "direct 256x256x64 8w 16x16x32 gm4 pingpong ntC",
-    "direct 256x256x64 8w 32x32x16 gm4 pingpong dma-in-compute ntC",
-    "direct 256x256x64 8w 32x32x16 gm4 ilv prefetch2 ntC",
-    "direct 256x256x64 8w 32x32x16 gm8 ilv prefetch2 ntC",
-    "direct 256x256x64 8w 32x32x16 gm4 ilv ntC agpr",
-    "direct 256x256x64 8w 32x32x16 gm4 ilv prefetch2 ntC agpr"};
+    "direct 256x256x64 8w 16x16x32 gm4 ilv ntC agpr early"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace

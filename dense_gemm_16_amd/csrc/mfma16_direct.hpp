@@ -18,9 +18,11 @@
 //
 // LDS images (per stage; two stages alternate):
 //   A: [BM rows][8 chunks of 16 B]; logical chunk c of row r at physical chunk
-//      c ^ ((r ^ (r >> 3)) & 7).  Sixteen consecutive rows reading one logical
-//      chunk (a fragment read) then fall on sixteen distinct 16-byte bank
-//      groups.
+//      c ^ ((r >> 1) & 7).  Sixteen consecutive rows reading one logical chunk
+//      (a fragment read) then fall on sixteen distinct 16-byte bank groups: the
+//      eight even rows on one half of the banks, the eight odd rows on the other,
+//      each on its own chunk.  The pattern repeats every 16 rows, so fragments
+//      16 rows apart differ by a constant address offset.
 //   B: [64 k-rows][BN/8 chunks of 16 B]; logical chunk c of k-row r at
 //      c ^ (2 f(r)), f(r) = (r & 3) | (((r >> 3) & 1) << 2).  A transposing
 //      read touches 32 bytes (two chunks) in each of the rows 8g + {0..3} of
@@ -58,13 +60,12 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // SCHED: 0 = prefetch block then matrix block per slab; 1 = as 0 with the wave's
 // priority raised during its matrix block (s_setprio); 2 = one LDS read issued
-// after each matrix instruction (sched_group_barrier); 3 = 2 with raised priority;
-// 4 = ping-pong: two groups of four waves (one wave of each per SIMD) alternate
-// between a phase of matrix instructions and a phase of LDS reads and direct
-// loads, swapping at every barrier.
+// after each matrix instruction (sched_group_barrier); 3 = 2 with raised priority.
 // FLAGS: bit 0 = spread each k-tile's direct loads over the slabs before the
 // barrier instead of issuing them in one burst; bit 1 = non-temporal C stores;
-// bit 2 = keep the accumulators in AGPRs (see below).
+// bit 2 = keep the accumulators in AGPRs (see below); bit 3 = issue a k-tile's
+// direct loads right after the barrier that frees their stage instead of at the
+// start of the next k-tile, so they have a whole k-tile of matrix work to land.
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
           int BK_ = 64, int GM_ = 8, int SCHED_ = 0, int FLAGS_ = 0>
 struct DirectCfg {
@@ -90,15 +91,17 @@ struct DirectCfg {
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "whole blocks per wave");
     static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "stages fit 160 KiB");
     static_assert((STAGES - 2) * NI <= 63, "vmcnt counts at most 63 loads");
+    static_assert(!((FLAGS & 1) && (FLAGS & 8)), "spread and early loads exclude each other");
 };
 
 // Physical chunk of logical chunk c in row `row` of the A image (CA chunks per row).
-// 128-byte rows: c ^ ((row ^ (row >> 3)) & 7).  64-byte rows (four rows per 256
-// bytes of banks): c ^ ((row >> 2) & 3), so sixteen consecutive rows reading one
-// logical chunk cover the 64 banks once.
+// 128-byte rows (two rows per 256 bytes of banks): c ^ ((row >> 1) & 7).  64-byte
+// rows (four rows per 256 bytes): c ^ ((row >> 2) & 3).  Either way sixteen
+// consecutive rows reading one logical chunk cover the 64 banks once, and the
+// pattern depends on row % 16 only.
 template <int CA>
 __device__ __forceinline__ int swz_a(int row) {
-    if constexpr (CA == 8) return (row ^ (row >> 3)) & 7;
+    if constexpr (CA == 8) return (row >> 1) & 7;
     return (row >> 2) & 3;
 }
 __device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) | ((krow >> 1) & 4)) << 1; }
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         constexpr bool prio = Cfg::SCHED == 1 || Cfg::SCHED == 3;
         if constexpr (Cfg::SCHED == 3) __builtin_amdgcn_s_setprio(1);
         if (do_load) load_frags(lkt, ls, fl);
-        if constexpr (Cfg::SCHED == 2 || Cfg::SCHED == 3 || Cfg::SCHED == 6) {
+        if constexpr (Cfg::SCHED == 2 || Cfg::SCHED == 3) {
             mma(f);
             // one matrix instruction, then one LDS read, while reads remain
 #pragma unroll
@@ -292,123 +295,16 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     };
 
     const int KT = static_cast<int>(K / Cfg::BK);
-    if constexpr (Cfg::SCHED == 4 || Cfg::SCHED == 5) {
-        // Ping-pong.  A k-tile has two halves h = 2 kt, 2 kt + 1 (SLABS / 2 slabs
-        // each).  Waves 0-3 (group X) and 4-7 (group Y) share the SIMDs pairwise.
-        // Phase p (one barrier after each): X computes half p/2 on even p and
-        // reads half (p+1)/2 on odd p; Y reads half p/2 on even p and computes
-        // half (p-1)/2 on odd p.  So on every SIMD one wave issues only matrix
-        // instructions while the other reads LDS, and the barrier that ends a
-        // phase is hidden behind the partner's matrix work.
-        // Direct loads: k-tile kt (>= 2) is issued in the read phase of half
-        // 2 (kt - 1), i.e. phases 4 kt - 5 (X) and 4 kt - 4 (Y); the barrier ending
-        // phase 4 kt - 2 waits for it (vmcnt(0): nothing later has been issued by
-        // then); its first reader is X in phase 4 kt - 1.  It overwrites the stage
-        // of k-tile kt - 2, whose last reads were in phase 4 kt - 6 and completed
-        // before that phase's barrier.
-        static_assert(S == 2 && NW == 8 && SLABS % 2 == 0, "ping-pong layout");
-        constexpr int HS = SLABS / 2;
-        const int grp = wave / 4;
-        Frags P[HS];
-        const int H = 2 * KT;
-        // SCHED 4 issues a k-tile's direct loads in the read phase; SCHED 5 in the
-        // compute phase of the same half (phases 4 kt - 4 for X, 4 kt - 3 for Y,
-        // inside the same legal window), one load after every other matrix
-        // instruction, so the address unit works while the matrix pipe does.
-        constexpr bool dma_in_compute = Cfg::SCHED == 5;
-        auto read_half = [&](int h) {
-            const int kt = h / 2;
-            if (!dma_in_compute && (h & 1) == 0 && h >= 2 && kt + 1 < KT) issue(kt + 1);
+    // Prologue: k-tiles 0 .. S-2 in flight (0 .. S-1 with early loads, which
+    // refill a stage right after the barrier that frees it); wait for k-tile 0.
+    constexpr bool early = (Cfg::FLAGS & 8) != 0;
+    constexpr int kPro = early ? S : S - 1;
+    static_assert((kPro - 1) * NI <= 63, "vmcnt counts at most 63 loads");
 #pragma unroll
-            for (int s = 0; s < HS; ++s) load_frags(kt, (h & 1) * HS + s, P[s]);
-        };
-        auto compute_half = [&](int h) {
-            const int kt = h / 2;
-            if (dma_in_compute && (h & 1) == 0 && h >= 2 && kt + 1 < KT) {
-                static_assert(HS * TM * TN >= 2 * NI, "room to interleave the loads");
-                int n = 0;
-#pragma unroll
-                for (int s = 0; s < HS; ++s)
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j) {
-                            Op::run(acc[i][j], P[s].a[i], P[s].b[j]);
-                            if ((n & 1) && n / 2 < NI) issue_range(kt + 1, n / 2, n / 2 + 1);
-                            ++n;
-                        }
-            } else {
-#pragma unroll
-                for (int s = 0; s < HS; ++s) mma(P[s]);
-            }
-        };
-        issue(0);
-        if (KT > 1) {
-            issue(1);
-            wait_then_barrier<NI>();
-        } else {
-            wait_then_barrier<0>();
-        }
-        if (grp == 0) read_half(0);
-        for (int p = 0; p < 2 * H; ++p) {
-            const bool compute = ((p & 1) == 0) == (grp == 0);
-            if (compute) {
-                compute_half(grp == 0 ? p / 2 : (p - 1) / 2);
-            } else {
-                const int h = grp == 0 ? (p + 1) / 2 : p / 2;
-                if (h < H) read_half(h);
-            }
-            if ((p & 3) == 2)
-                wait_then_barrier<0>();
-            else
-                lds_wait_then_barrier();
-        }
-    } else if constexpr (Cfg::SCHED == 6) {
-        // Fragments read two slabs ahead.  A k-tile has four slabs and slab s of
-        // every k-tile lives in register buffer F[s], so slab s loads slab s+2
-        // into F[(s+2) % 4], a buffer last used two slabs earlier.  The barrier
-        // that makes k-tile kt+1 visible sits after slab 1 of kt: by then every
-        // read of kt's stage has been issued (slabs 2 and 3 are read during slabs
-        // 0 and 1) and completed (the LDS wait before the barrier), so right
-        // after the barrier the direct loads of k-tile kt+S refill that stage;
-        // they have a whole k-tile to land before the barrier that needs them.
-        // Slabs 2 and 3 of kt read slabs 0 and 1 of kt+1.
-        static_assert(SLABS == 4, "four slabs per k-tile");
-        static_assert((S - 1) * NI <= 63, "vmcnt counts at most 63 loads");
-#pragma unroll
-        for (int t = 0; t < S; ++t)
-            if (t < KT) issue(t);
-        if (KT >= S)
-            wait_then_barrier<(S - 1) * NI>();
-        else
-            wait_then_barrier<0>();
-        Frags F[4];
-        load_frags(0, 0, F[0]);
-        load_frags(0, 1, F[1]);
-        for (int kt = 0; kt + 1 < KT; ++kt) {
-            slab_step(true, kt, 2, F[2], F[0]);
-            slab_step(true, kt, 3, F[3], F[1]);
-            // k-tile kt+1 must have landed: the loads issued after it are those of
-            // k-tiles kt+2 .. kt+S-1, when they exist.
-            if (kt + S - 1 < KT)
-                wait_then_barrier<(S - 2) * NI>();
-            else
-                wait_then_barrier<0>();
-            if (kt + S < KT) issue(kt + S);
-            slab_step(true, kt + 1, 0, F[0], F[2]);
-            slab_step(true, kt + 1, 1, F[1], F[3]);
-        }
-        slab_step(true, KT - 1, 2, F[2], F[0]);
-        slab_step(true, KT - 1, 3, F[3], F[1]);
-        slab_step(false, 0, 0, F[0], F[2]);
-        slab_step(false, 0, 0, F[1], F[3]);
-    } else {
-    // Prologue: k-tiles 0 .. S-2 in flight; wait for k-tile 0.
-#pragma unroll
-    for (int t = 0; t < S - 1; ++t)
+    for (int t = 0; t < kPro; ++t)
         if (t < KT) issue(t);
-    if (KT >= S - 1)
-        wait_then_barrier<(S - 2) * NI>();
+    if (KT >= kPro)
+        wait_then_barrier<(kPro - 1) * NI>();
     else
         wait_then_barrier<0>();
 
@@ -434,23 +330,27 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     // predecessor and the compiler's wait counts stay exact there.
     for (int kt = 0; kt + 1 < KT; ++kt) {
         const bool more = kt + S - 1 < KT;
-        if (!spread && more) issue(kt + S - 1);
+        if (!early && !spread && more) issue(kt + S - 1);
         // sched_barrier(0) fences keep each slab's prefetch ahead of the
         // previous slab's matrix instructions instead of letting the scheduler
         // sink the LDS reads next to their first use.
-        front_slabs(kt, more);
-        // k-tile kt+1 must have landed; later ones may still be in flight.
+        front_slabs(kt, more && !early);
+        // k-tile kt+1 must have landed; later ones (k-tiles up to kt+S-1) may
+        // still be in flight.
         if (more)
             wait_then_barrier<(S - 2) * NI>();
         else
             wait_then_barrier<0>();
+        // Every read of k-tile kt's stage was issued before the barrier (the
+        // last slab's fragments are already in registers) and has completed, in
+        // every wave: the stage can take k-tile kt+S.
+        if (early && kt + S < KT) issue(kt + S);
         slab_step(true, kt + 1, 0, F[0], F[1]);
     }
     if (KT > 0) {
         front_slabs(KT - 1, false);
         slab_step(false, 0, 0, F[0], F[1]);
     }
-    }  // SCHED != 4
 
     const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
     const int lc = L::col(lane);
