@@ -189,6 +189,70 @@ def profile_pass(p, reps):
     log(f"profile pass: 3 x copy of {n * 4} bytes, {reps} x {p.kernel_name()}")
 
 
+def _counter_rows(d):
+    """(kernel name, counter value) per dispatch from a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"bench.py: expected one *counter_collection.csv under {d}, found {files}")
+    rows = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            k = int(r["Dispatch_Id"])
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            rows[k] = (name, rows.get(k, (name, 0.0))[1] + v)
+    return [rows[k] for k in sorted(rows)]
+
+
+def digest_counters(w, fetch_dir, write_dir, reps):
+    """HBM bytes per launch of the selected kernel from two profile-mode counter runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled so that the 1 GiB device
+    copy of the same run reads as 1 GiB; median of the last `reps` (GEMM) dispatches.
+    The entry is written to the traffic summary under this workload."""
+    import statistics
+    import dense_gemm_16_amd as mg
+    from dense_gemm_16_amd import inputs
+    code = inputs.DTYPE_CODES[w.dtype]
+    st, v, c = mg.migemm_select(w.M, w.N, w.K, code, None, w.K, None, w.N, None, w.N)
+    kernel = f"{mg.migemm_variant_name(v)}[{mg.migemm_config_name(v, c)}]"
+    gib_kib = float(1 << 20)
+    e = {"kernel": kernel, "source_hash": source_hash()}
+    for label, d in (("fetch", fetch_dir), ("write", write_dir)):
+        rows = _counter_rows(d)
+        copies = [x for n, x in rows if "copyBuffer" in n]
+        gemm = rows[-reps:]
+        if len(copies) < 2 or any("copyBuffer" in n for n, _ in gemm):
+            raise SystemExit(f"bench.py: {d} does not hold a profile pass (copies then GEMMs)")
+        cal = statistics.median(copies[-2:])
+        raw = statistics.median(x for _, x in gemm)
+        e[f"{label}_kib_raw"] = raw
+        e[f"copy_{label}_kib_raw"] = cal
+        e[f"{label}_factor"] = round(gib_kib / cal, 5)
+        e[f"{label}_bytes_per_launch"] = int(round(raw * gib_kib / cal * 1024))
+        e[f"{label}_kernel_in_csv"] = gemm[-1][0][:160]
+    e["hbm_bytes_per_launch"] = e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
+    e["note"] = (f"HBM read {e['fetch_bytes_per_launch'] / 1e9:.3f} GB + write "
+                 f"{e['write_bytes_per_launch'] / 1e9:.3f} GB per launch; compulsory "
+                 f"{w.compulsory_bytes() / 1e9:.3f} GB")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    t["note_general"] = (
+        "HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE and WRITE_SIZE "
+        "(KiB per dispatch), each scaled by the factor that makes the same counter read 1 GiB "
+        "for a plain 1 GiB device copy (__amd_rocclr_copyBuffer) in the same run; median over "
+        "the GEMM launches of the profile pass.  Valid only while the library sources hash to "
+        "source_hash.  Written by bench.py --digest-counters.")
+    t.setdefault("entries", {})[w.name] = e
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    log(f"digest: {kernel}: {e['note']}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +261,10 @@ def main():
     ap.add_argument("--workload", default="c4-bf16-8192")
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--config", type=int, default=-1)
+    ap.add_argument("--dist", default="",
+                    help="override the workload's input distribution (e.g. zeros: the same "
+                         "kernel on inputs whose products switch no bits, to separate clock "
+                         "and power effects from cycle counts)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -206,7 +274,16 @@ def main():
                     help="comma-separated workloads the sweep covers (default: all)")
     ap.add_argument("--profile-pass", type=int, default=0, metavar="REPS",
                     help="only run the copy calibration and REPS launches (for rocprofv3)")
+    ap.add_argument("--digest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn the CSV output of two profile-pass runs (rocprofv3 --pmc "
+                         "FETCH_SIZE, then WRITE_SIZE) into the traffic summary entry")
+    ap.add_argument("--digest-reps", type=int, default=3,
+                    help="GEMM launches per profile pass (the REPS given to --profile-pass)")
     a = ap.parse_args()
+    if a.digest_counters:
+        from dense_gemm_16_amd import inputs
+        digest_counters(inputs.WORKLOADS[a.workload], *a.digest_counters, a.digest_reps)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -224,7 +301,10 @@ def main():
     mg.lib()  # fail loudly if the library is missing
 
     w = inputs.WORKLOADS[a.workload]
-    log(f"bench: generating {w.name} inputs")
+    if a.dist and a.dist != w.dist:
+        import dataclasses
+        w = dataclasses.replace(w, dist=a.dist)
+    log(f"bench: generating {w.name} inputs ({w.dist})")
     p = Problem(w, a.variant, a.config)
     if a.profile_pass:
         profile_pass(p, a.profile_pass)

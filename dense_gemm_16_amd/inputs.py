@@ -48,6 +48,8 @@ def draw(shape, dtype: str, dist: str, g: torch.Generator, lo: int = -4, hi: int
         x = torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int32).to(torch.float32)
     elif dist == "ones":
         x = torch.ones(shape, dtype=torch.float32)
+    elif dist == "zeros":
+        x = torch.zeros(shape, dtype=torch.float32)
     else:
         raise ValueError(f"unknown distribution {dist!r}")
     return x.to(t)
