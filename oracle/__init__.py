@@ -10,6 +10,13 @@ B (K x N), row-major,
     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j]      (ascending k, binary64)
     S[i][j] = sum_{k=0}^{K-1} |A[i][k] * B[k][j]|
 
+and, for the scaled update with a previous C (``epilogue``),
+
+    out = alpha * C + beta * C_old,   scale = |alpha| S + |beta C_old|
+
+with ``encode`` rounding binary64 values to FP32, FP16 or BF16 (nearest, ties
+to even) for outputs stored in those formats.
+
 following the element-wise definition on page "Tensor cores and matrix
 operations" (section "Traditional Approach: Element-by-Element") and the fp64
 CPU reference on page "matmul_registers.cu".  This module only marshals
@@ -47,6 +54,11 @@ class Oracle:
         lib.oracle_gemm_entries.argtypes = [i64, i64, i64, i32, vp, i64, vp, i64, i64, vp, vp,
                                             vp, vp, i32]
         lib.oracle_gemm_entries.restype = i32
+        lib.oracle_encode_array.argtypes = [i32, i64, vp, vp]
+        lib.oracle_encode_array.restype = i32
+        lib.oracle_epilogue.argtypes = [i64, ctypes.c_double, ctypes.c_double, i32, vp, vp, vp,
+                                        vp, vp]
+        lib.oracle_epilogue.restype = i32
         self.lib = lib
         self.path = path
 
@@ -66,6 +78,45 @@ class Oracle:
         if st:
             raise ValueError(f"oracle_decode_array failed with status {st}")
         return out
+
+    def encode(self, values, dtype: int) -> np.ndarray:
+        """Round float64 values to the stored format, nearest with ties to even (the
+        oracle's own encoder): float32 for FP32, raw uint16 bits for FP16 and BF16."""
+        v = np.ascontiguousarray(np.asarray(values, dtype=np.float64))
+        out = np.empty(v.shape, dtype=np.uint32 if dtype == F32 else np.uint16)
+        st = self.lib.oracle_encode_array(dtype, v.size, _ptr(v), _ptr(out))
+        if st:
+            raise ValueError(f"oracle_encode_array failed with status {st}")
+        return out.view(np.float32) if dtype == F32 else out
+
+    def epilogue(self, acc, S, alpha: float, beta: float, c_dtype: int, c_old=None):
+        """out = alpha * acc + beta * C_old and scale = |alpha| S + |beta C_old|, element
+        by element in float64.  c_old holds the previous C in its stored format (float32
+        or raw uint16 bits) with acc's shape; it is not read when beta == 0."""
+        acc = np.ascontiguousarray(np.asarray(acc, dtype=np.float64))
+        S = np.ascontiguousarray(np.asarray(S, dtype=np.float64))
+        if S.shape != acc.shape:
+            raise ValueError("acc and S differ in shape")
+        old = None
+        if beta != 0.0:
+            if c_old is None:
+                raise ValueError("beta != 0 needs the previous C")
+            old = np.asarray(c_old)
+            if c_dtype == F32:
+                old = old if old.dtype == np.float32 else old.view(np.float32)
+            elif old.dtype == np.int16:
+                old = old.view(np.uint16)
+            old = np.ascontiguousarray(old)
+            if old.shape != acc.shape:
+                raise ValueError("previous C differs in shape from the product")
+        out = np.empty_like(acc)
+        scale = np.empty_like(acc)
+        st = self.lib.oracle_epilogue(acc.size, float(alpha), float(beta), c_dtype,
+                                      _ptr(old) if old is not None else None, _ptr(acc), _ptr(S),
+                                      _ptr(out), _ptr(scale))
+        if st:
+            raise ValueError(f"oracle_epilogue failed with status {st}")
+        return out, scale
 
     def gemm(self, A, B, dtype: int, nthreads: int | None = None, want_scale: bool = True):
         """Full product: (C, S) as float64 arrays of shape (M, N); S is None if not wanted."""
@@ -139,6 +190,14 @@ def decode(bits, dtype: int) -> np.ndarray:
 
 def gemm(A, B, dtype: int, nthreads: int | None = None, want_scale: bool = True):
     return _oracle().gemm(A, B, dtype, nthreads, want_scale)
+
+
+def encode(values, dtype: int) -> np.ndarray:
+    return _oracle().encode(values, dtype)
+
+
+def epilogue(acc, S, alpha: float, beta: float, c_dtype: int, c_old=None):
+    return _oracle().epilogue(acc, S, alpha, beta, c_dtype, c_old)
 
 
 def gemm_entries(A, B, dtype: int, rows, cols, nthreads: int | None = None):

@@ -16,6 +16,13 @@ exact in binary32) is off by at most about K * 2^-24 * S, so cancellation in
 C_ref never makes the rule unfair.  The first failing element is reported with
 its row and column, in the manner of the first-mismatch report on page
 "matmul_registers.cu".
+
+A result stored in a narrower format (``out_dtype`` FP16 or BF16, or FP32 after
+the scaled update) is also off by its final rounding: at most half a unit in the
+last place, u |C| with u = 2^-24, 2^-11, 2^-8 for FP32, FP16, BF16, or half the
+smallest subnormal (2^-150, 2^-25, 2^-134) near zero.  With ``out_dtype`` given
+the bound is tol * S * (1 + u) + u |C_ref| + that half subnormal, where S is the
+scale of the whole update (|alpha| S + |beta C_old| from the oracle).
 """
 from __future__ import annotations
 
@@ -25,6 +32,9 @@ import numpy as np
 
 TOL_F32 = 1e-4
 TOL_HALF = 5e-4
+# unit roundoff and half the smallest subnormal of each stored format
+OUT_UNIT = {0: 2.0 ** -24, 1: 2.0 ** -11, 2: 2.0 ** -8}
+OUT_TINY = {0: 2.0 ** -150, 1: 2.0 ** -25, 2: 2.0 ** -134}
 
 
 def tolerance(dtype: int) -> float:
@@ -46,8 +56,10 @@ class CheckResult:
                 f" S={s!r}; max |err|/S = {self.max_ratio:.3e}")
 
 
-def compare(got, want, scale, tol: float | None = None, exact: bool = False) -> CheckResult:
-    """Compare ``got`` (GPU, any float array) with ``want``/``scale`` (oracle, float64)."""
+def compare(got, want, scale, tol: float | None = None, exact: bool = False,
+            out_dtype: int | None = None) -> CheckResult:
+    """Compare ``got`` (GPU, any float array) with ``want``/``scale`` (oracle, float64);
+    ``out_dtype`` adds the final rounding of a result stored in that format."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     scale = np.asarray(scale, dtype=np.float64)
@@ -60,7 +72,12 @@ def compare(got, want, scale, tol: float | None = None, exact: bool = False) -> 
     else:
         if tol is None:
             raise ValueError("tol is required unless exact=True")
-        bad = ~(finite & (err <= tol * scale))
+        if out_dtype is None:
+            bound = tol * scale
+        else:
+            u = OUT_UNIT[out_dtype]
+            bound = tol * scale * (1.0 + u) + u * np.abs(want) + OUT_TINY[out_dtype]
+        bad = ~(finite & (err <= bound))
         bad |= (scale == 0) & (got != want)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(scale > 0, err / np.where(scale > 0, scale, 1.0), 0.0)

@@ -222,3 +222,133 @@ int oracle_gemm_entries(int64_t M, int64_t N, int64_t K, int dtype, const void* 
     }
     return ORACLE_OK;
 }
+
+/*
+ * Output rounding.  Page "CUDA-Practice 09" (section on why FP32 accumulation
+ * is used) has the FP32 accumulator written back as FP32 or rounded as
+ * required; the rounding taken here is IEEE round-to-nearest-even: the nearest
+ * value of the target format to x, ties to the value whose last significand
+ * bit is 0, magnitudes at or beyond the format's overflow threshold to
+ * infinity, NaN to a quiet NaN.
+ *
+ * A finite binary format with p significand bits (hidden bit included) and
+ * minimum normal exponent emin represents, in the binade [2^e, 2^(e+1)) for
+ * e >= emin, the multiples of q = 2^(e - p + 1); below 2^emin (subnormals) the
+ * multiples of 2^(emin - p + 1).  So: take e = max(floor(log2 |x|), emin),
+ * q = 2^(e - p + 1), round |x| / q to the nearest integer with ties to even
+ * (rint in the default rounding mode), and scale back; a result of 2^p * q has
+ * moved into the next binade, which is still exact.  |x| / q is exact: q is a
+ * power of two and the quotient stays far below 2^53.
+ */
+static double round_to_format(double x, int p, int emin, int emax)
+{
+    if (isnan(x)) return x;
+    const double ax = fabs(x);
+    /* overflow threshold: the largest finite value plus half its quantum */
+    const double maxv = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+    const double thresh = maxv + ldexp(1.0, emax - p);
+    if (ax >= thresh) return x > 0 ? INFINITY : -INFINITY;
+    if (ax == 0.0) return x;
+    int E;
+    frexp(ax, &E); /* ax = m * 2^E, m in [0.5, 1): floor(log2 ax) = E - 1 */
+    int e = E - 1;
+    if (e < emin) e = emin;
+    const double q = ldexp(1.0, e - p + 1);
+    const double r = rint(ax / q) * q;
+    return x < 0 ? -r : r;
+}
+
+/* binary64 -> binary16 bits (p = 11, emin = -14, emax = 15) */
+uint16_t oracle_encode_f16(double x)
+{
+    if (isnan(x)) return 0x7e00;
+    const double r = round_to_format(x, 11, -14, 15);
+    const uint16_t s = signbit(r) ? 0x8000 : 0;
+    const double a = fabs(r);
+    if (isinf(a)) return s | 0x7c00;
+    if (a == 0.0) return s;
+    if (a < ldexp(1.0, -14)) return s | (uint16_t)(a / ldexp(1.0, -24)); /* subnormal: f * 2^-24 */
+    int E;
+    const double m = frexp(a, &E);                 /* a = m * 2^E, m in [0.5, 1) */
+    const int e = E - 1;                           /* a = (1 + f/1024) * 2^e */
+    const uint16_t f = (uint16_t)(m * 2048.0 - 1024.0);
+    return s | (uint16_t)((e + 15) << 10) | f;
+}
+
+/* binary64 -> bfloat16 bits (p = 8, emin = -126, emax = 127) */
+uint16_t oracle_encode_bf16(double x)
+{
+    if (isnan(x)) return 0x7fc0;
+    const double r = round_to_format(x, 8, -126, 127);
+    const uint16_t s = signbit(r) ? 0x8000 : 0;
+    const double a = fabs(r);
+    if (isinf(a)) return s | 0x7f80;
+    if (a == 0.0) return s;
+    if (a < ldexp(1.0, -126)) return s | (uint16_t)(a / ldexp(1.0, -133)); /* f * 2^-133 */
+    int E;
+    const double m = frexp(a, &E);
+    const int e = E - 1;                           /* a = (1 + f/128) * 2^e */
+    const uint16_t f = (uint16_t)(m * 256.0 - 128.0);
+    return s | (uint16_t)((e + 127) << 7) | f;
+}
+
+/* binary64 -> binary32 bits (p = 24, emin = -126, emax = 127) */
+uint32_t oracle_encode_f32(double x)
+{
+    if (isnan(x)) return 0x7fc00000u;
+    const double r = round_to_format(x, 24, -126, 127);
+    const uint32_t s = signbit(r) ? 0x80000000u : 0;
+    const double a = fabs(r);
+    if (isinf(a)) return s | 0x7f800000u;
+    if (a == 0.0) return s;
+    if (a < ldexp(1.0, -126)) return s | (uint32_t)(a / ldexp(1.0, -149));
+    int E;
+    const double m = frexp(a, &E);
+    const int e = E - 1;
+    const uint32_t f = (uint32_t)(m * 16777216.0 - 8388608.0);
+    return s | ((uint32_t)(e + 127) << 23) | f;
+}
+
+/* Encodes n binary64 values into the stored format (4-byte words for dtype 0,
+ * 2-byte for 1 and 2). */
+int oracle_encode_array(int dtype, int64_t n, const double* in, void* out)
+{
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16) return ORACLE_BAD_ARG;
+    if (n < 0 || (n > 0 && (!in || !out))) return ORACLE_BAD_ARG;
+    for (int64_t e = 0; e < n; ++e) {
+        if (dtype == ORACLE_F32)
+            ((uint32_t*)out)[e] = oracle_encode_f32(in[e]);
+        else if (dtype == ORACLE_F16)
+            ((uint16_t*)out)[e] = oracle_encode_f16(in[e]);
+        else
+            ((uint16_t*)out)[e] = oracle_encode_bf16(in[e]);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * The general output step, element by element (the scaled update of page
+ * "matmul_registers.cu", section on the library call, whose alpha and beta
+ * multiply the product and the previous C):
+ *
+ *     out[e]   = alpha * acc[e] + beta * Cold[e]
+ *     scale[e] = |alpha| * S[e] + |beta * Cold[e]|
+ *
+ * acc and S are a product and its scale from oracle_gemm (or _entries); Cold
+ * holds n stored elements of dtype c_dtype and is not read when beta == 0
+ * (the previous C then takes no part, whatever it holds).  All in binary64;
+ * scale may be NULL.
+ */
+int oracle_epilogue(int64_t n, double alpha, double beta, int c_dtype, const void* Cold,
+                    const double* acc, const double* S, double* out, double* scale)
+{
+    if (c_dtype != ORACLE_F32 && c_dtype != ORACLE_F16 && c_dtype != ORACLE_BF16) return ORACLE_BAD_ARG;
+    if (n < 0 || (n > 0 && (!acc || !out || (scale && !S) || (beta != 0.0 && !Cold))))
+        return ORACLE_BAD_ARG;
+    for (int64_t e = 0; e < n; ++e) {
+        const double old = beta != 0.0 ? beta * decode_at(Cold, c_dtype, e) : 0.0;
+        out[e] = alpha * acc[e] + old;
+        if (scale) scale[e] = fabs(alpha) * S[e] + fabs(old);
+    }
+    return ORACLE_OK;
+}

@@ -268,3 +268,126 @@ def test_compare_rule_catches_planted_errors():
     # where S == 0 equality is required even in tolerance mode
     zero_scale = np.zeros((1, 1))
     assert not compare(np.array([[1e-30]]), np.zeros((1, 1)), zero_scale, tol=TOL_F32).ok
+
+
+# ---------------------------------------------------------------- output rounding and scaled update
+
+def _finite_patterns(code):
+    allbits = np.arange(65536, dtype=np.uint16)
+    return allbits[np.isfinite(oracle.decode(allbits, code))]
+
+
+@pytest.mark.parametrize("code", [oracle.F16, oracle.BF16])
+def test_encode_roundtrip_exhaustive(code):
+    """Every finite stored value (signed zeros and subnormals included) encodes back
+    to its own bits."""
+    pats = _finite_patterns(code)
+    assert np.array_equal(oracle.encode(oracle.decode(pats, code), code), pats)
+
+
+def test_encode_f32_roundtrip_sample():
+    g = np.random.default_rng(7)
+    w = g.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    w = np.concatenate([w, np.array([0, 0x80000000, 1, 0x807fffff, 0x7f7fffff, 0x00800000],
+                                    dtype=np.uint32)])
+    x = w.view(np.float32)
+    w = w[np.isfinite(x)]
+    got = oracle.encode(w.view(np.float32).astype(np.float64), oracle.F32).view(np.uint32)
+    assert np.array_equal(got, w)
+
+
+@pytest.mark.parametrize("code", [oracle.F16, oracle.BF16])
+def test_encode_ties_to_even_exhaustive(code):
+    """The midpoint of every pair of adjacent finite values goes to the one whose
+    last significand bit is 0; a hair either side goes to the nearer one."""
+    pats = _finite_patterns(code)
+    pos = np.sort(pats[(pats & 0x8000) == 0])               # +0 .. max, increasing bits
+    lo, hi = pos[:-1], pos[1:]
+    a, b = oracle.decode(lo, code), oracle.decode(hi, code)
+    mid = (a + b) / 2                                        # exact in binary64
+    even = np.where((lo & 1) == 0, lo, hi)
+    assert np.array_equal(oracle.encode(mid, code), even)
+    assert np.array_equal(oracle.encode(-mid, code), even | 0x8000)
+    gap = b - a
+    assert np.array_equal(oracle.encode(mid - gap / 64, code), lo)
+    assert np.array_equal(oracle.encode(mid + gap / 64, code), hi)
+
+
+def test_encode_overflow_thresholds():
+    # binary16: largest finite 65504, quantum 32 there: 65520 is the tie with 2^16 -> inf
+    assert oracle.encode([65519.99, 65520.0, -65520.0, 1e30], oracle.F16).tolist() == \
+        [0x7BFF, 0x7C00, 0xFC00, 0x7C00]
+    # bfloat16: largest finite (2 - 2^-7) 2^127, quantum 2^120: the tie with 2^128 -> inf
+    mx = (2 - 2 ** -7) * 2.0 ** 127
+    assert oracle.encode([mx, mx + 2.0 ** 119, mx + 2.0 ** 119 * 0.999], oracle.BF16).tolist() == \
+        [0x7F7F, 0x7F80, 0x7F7F]
+    assert oracle.encode([float("nan")], oracle.F16)[0] & 0x7C00 == 0x7C00
+
+
+def test_encode_matches_library_conversions():
+    """Single roundings done by independent implementations: numpy's binary64 ->
+    binary16 and binary64 -> binary32 casts, and torch's binary32 -> bfloat16 cast
+    (its input exact in binary64, so one rounding)."""
+    g = np.random.default_rng(11)
+    x = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-9, 5, 20000),
+                        g.uniform(-7e4, 7e4, 2000)])
+    with np.errstate(over="ignore"):                          # overflow to inf is intended
+        want16 = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.encode(x, oracle.F16), want16)
+    assert np.array_equal(oracle.encode(x, oracle.F32), x.astype(np.float32))
+    f = (g.standard_normal(20000) * 10.0 ** g.integers(-30, 30, 20000)).astype(np.float32)
+    wantbf = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.encode(f.astype(np.float64), oracle.BF16), wantbf)
+
+
+def test_epilogue_identity_and_unread_previous():
+    acc = np.array([1.5, -2.25, 0.0, 3e-30])
+    S = np.abs(acc) * 2
+    out, sc = oracle.epilogue(acc, S, 1.0, 0.0, oracle.F32)
+    assert np.array_equal(out, acc) and np.array_equal(sc, S)
+    # beta == 0: the previous C is never read, NaN or not
+    nan = np.full(acc.shape, np.nan, dtype=np.float32)
+    out, _ = oracle.epilogue(acc, S, 2.0, 0.0, oracle.F32, nan)
+    assert np.array_equal(out, 2 * acc)
+
+
+@pytest.mark.parametrize("code", [oracle.F32, oracle.F16, oracle.BF16])
+def test_epilogue_integers_exact(code):
+    """alpha = 3, beta = -2 on integer products and an integer previous C: the update
+    is exact integer arithmetic, and so is its scale."""
+    g = np.random.default_rng(5)
+    a = g.integers(-4, 5, (6, 9))
+    b = g.integers(-4, 5, (9, 7))
+    old = g.integers(-20, 21, (6, 7))
+    tdt = {oracle.F32: torch.float32, oracle.F16: torch.float16, oracle.BF16: torch.bfloat16}[code]
+    A, B = torch.from_numpy(a).to(tdt), torch.from_numpy(b).to(tdt)
+    acc, S = oracle.gemm(bits(A), bits(B), code)
+    old_bits = bits(torch.from_numpy(old).to(tdt))
+    out, sc = oracle.epilogue(acc, S, 3.0, -2.0, code, old_bits)
+    assert np.array_equal(out, (3 * (a @ b) - 2 * old).astype(float))
+    assert np.array_equal(sc, (3 * (np.abs(a) @ np.abs(b)) + 2 * np.abs(old)).astype(float))
+
+
+def test_epilogue_against_exact_rationals():
+    """Powers-of-two alpha and beta make both products exact, so the one binary64
+    addition is the only rounding: within half an ulp of the exact rational."""
+    g = np.random.default_rng(9)
+    acc = g.standard_normal(500)
+    old = g.standard_normal(500).astype(np.float32)
+    out, _ = oracle.epilogue(acc, np.abs(acc), 0.25, -8.0, oracle.F32, old)
+    for x, y, o in zip(acc, old, out):
+        exact = Fraction(0.25) * Fraction(float(x)) + Fraction(-8) * Fraction(float(y))
+        assert abs(Fraction(float(o)) - exact) <= abs(exact) * Fraction(1, 2 ** 53)
+
+
+def test_compare_output_rounding_term():
+    want = np.array([1000.3, -2.0 ** -20, 0.0])
+    got16 = oracle.decode(oracle.encode(want, oracle.F16), oracle.F16)
+    scale = np.abs(want) * 1e-6           # a product whose own error budget is tiny
+    assert compare(got16, want, scale, TOL_HALF, out_dtype=oracle.F16).ok
+    # without the output term the rounded values do not pass
+    assert not compare(got16, want, scale, TOL_HALF).ok
+    # off by a whole unit of the output format: fails
+    bad = got16.copy()
+    bad[0] += 0.5
+    assert not compare(bad, want, scale, TOL_HALF, out_dtype=oracle.F16).ok

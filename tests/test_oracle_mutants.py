@@ -36,6 +36,14 @@ MUTANTS = {
                       "decode_at(B, dtype, (j % K) * ldb + (k % N));\n            c += p;")],
     "scale_without_abs": [("s[j] += fabs(p);", "s[j] += p;"), ("s += fabs(p);", "s += p;")],
     "sign": [("c[j] += p;", "c[j] -= p;"), ("            c += p;", "            c -= p;")],
+    "encode_ties_away": [("const double r = rint(ax / q) * q;", "const double r = round(ax / q) * q;")],
+    "encode_truncate": [("const double r = rint(ax / q) * q;", "const double r = trunc(ax / q) * q;")],
+    "encode_f16_bias": [("((e + 15) << 10)", "((e + 14) << 10)")],
+    "encode_overflow_at_max": [("if (ax >= thresh)", "if (ax > maxv)")],
+    "encode_f16_subnormal": [("a / ldexp(1.0, -24)", "a / ldexp(1.0, -25)")],
+    "epilogue_drops_beta": [("out[e] = alpha * acc[e] + old;", "out[e] = alpha * acc[e];")],
+    "epilogue_alpha_on_old": [("beta * decode_at(Cold, c_dtype, e)", "alpha * decode_at(Cold, c_dtype, e)")],
+    "epilogue_scale_without_abs": [("fabs(alpha) * S[e] + fabs(old)", "fabs(alpha) * S[e] + old")],
 }
 
 
@@ -110,7 +118,41 @@ def pin_subnormal_inputs(o):
     return np.array_equal(C[:, 0], sub.double().numpy()[:, 0])
 
 
-PINS = [pin_decoders, pin_ones, pin_permutation, pin_small_int, pin_subnormal_inputs]
+def pin_encode_roundtrip_and_ties(o):
+    allbits = np.arange(65536, dtype=np.uint16)
+    for code in (oracle.F16, oracle.BF16):
+        vals = o.decode(allbits, code)
+        pats = allbits[np.isfinite(vals)]
+        if not np.array_equal(o.encode(o.decode(pats, code), code), pats):
+            return False
+        pos = np.sort(pats[(pats & 0x8000) == 0])
+        lo, hi = pos[:-1], pos[1:]
+        mid = (o.decode(lo, code) + o.decode(hi, code)) / 2
+        if not np.array_equal(o.encode(mid, code), np.where((lo & 1) == 0, lo, hi)):
+            return False
+    return True
+
+
+def pin_encode_overflow(o):
+    mx = (2 - 2 ** -7) * 2.0 ** 127
+    return (o.encode([65519.99, 65520.0], oracle.F16).tolist() == [0x7BFF, 0x7C00]
+            and o.encode([mx, mx + 2.0 ** 119 * 0.999], oracle.BF16).tolist() == [0x7F7F, 0x7F7F])
+
+
+def pin_epilogue_integers(o):
+    g = np.random.default_rng(5)
+    a = g.integers(-4, 5, (6, 9))
+    b = g.integers(-4, 5, (9, 7))
+    old = g.integers(-20, 21, (6, 7))
+    A, B = torch.from_numpy(a).half(), torch.from_numpy(b).half()
+    acc, S = o.gemm(_b(A), _b(B), oracle.F16)
+    out, sc = o.epilogue(acc, S, 3.0, -2.0, oracle.F16, _b(torch.from_numpy(old).half()))
+    return (np.array_equal(out, (3 * (a @ b) - 2 * old).astype(float))
+            and np.array_equal(sc, (3 * (np.abs(a) @ np.abs(b)) + 2 * np.abs(old)).astype(float)))
+
+
+PINS = [pin_decoders, pin_ones, pin_permutation, pin_small_int, pin_subnormal_inputs,
+        pin_encode_roundtrip_and_ties, pin_encode_overflow, pin_epilogue_integers]
 
 
 @pytest.mark.parametrize("name", list(MUTANTS))
