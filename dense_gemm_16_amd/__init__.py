@@ -5,7 +5,8 @@ kernels.  The functions named ``migemm_*`` mirror the C ABI in
 ``include/migemm.h`` one for one (integers and raw device pointers);
 ``gemm`` is a convenience wrapper over torch tensors that derives the sizes,
 leading dimensions, pointers and the current stream and calls
-``migemm_gemm_variant``.
+``migemm_gemm_variant`` (or ``migemm_gemm_ex_variant`` for a scaled update or an
+FP16/BF16 output).
 
 The library is loaded on first use from this package's directory.  If it has
 not been built, every call raises ``RuntimeError``: there is no fallback.
@@ -23,7 +24,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 VARIANT_AUTO, NAIVE, LDS_TILED, REGTILE_VALU, REGTILE_MFMA, MFMA16 = -1, 0, 1, 2, 3, 4
 
 # Every symbol the header declares (checked by the CPU test suite).
-EXPORTS = ("migemm_gemm", "migemm_gemm_variant", "migemm_variant_count", "migemm_variant_name",
+EXPORTS = ("migemm_gemm", "migemm_gemm_variant", "migemm_gemm_ex", "migemm_gemm_ex_variant",
+           "migemm_variant_count", "migemm_variant_name",
            "migemm_variant_supports", "migemm_config_count", "migemm_config_name",
            "migemm_select", "migemm_status_string", "migemm_last_hip_error", "migemm_version")
 
@@ -53,6 +55,12 @@ def lib():
     L.migemm_gemm.restype = i32
     L.migemm_gemm_variant.argtypes = [i32, i32, i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp]
     L.migemm_gemm_variant.restype = i32
+    f32 = ctypes.c_float
+    L.migemm_gemm_ex.argtypes = [i64, i64, i64, i32, vp, i64, vp, i64, f32, f32, i32, vp, i64, vp]
+    L.migemm_gemm_ex.restype = i32
+    L.migemm_gemm_ex_variant.argtypes = [i32, i32, i64, i64, i64, i32, vp, i64, vp, i64, f32, f32,
+                                         i32, vp, i64, vp]
+    L.migemm_gemm_ex_variant.restype = i32
     L.migemm_variant_count.argtypes = []
     L.migemm_variant_count.restype = i32
     L.migemm_variant_name.argtypes = [i32]
@@ -86,6 +94,18 @@ def migemm_gemm_variant(variant, config, M, N, K, dtype, A, lda, B, ldb, C, ldc,
                         stream=None) -> int:
     return lib().migemm_gemm_variant(variant, config, M, N, K, dtype, A, lda, B, ldb, C, ldc,
                                      stream)
+
+
+def migemm_gemm_ex(M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype, C, ldc,
+                   stream=None) -> int:
+    return lib().migemm_gemm_ex(M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype, C, ldc,
+                                stream)
+
+
+def migemm_gemm_ex_variant(variant, config, M, N, K, dtype, A, lda, B, ldb, alpha, beta,
+                           c_dtype, C, ldc, stream=None) -> int:
+    return lib().migemm_gemm_ex_variant(variant, config, M, N, K, dtype, A, lda, B, ldb, alpha,
+                                        beta, c_dtype, C, ldc, stream)
 
 
 def migemm_variant_count() -> int:
@@ -148,13 +168,17 @@ def _ld(t) -> int:
     return max(1, t.stride(0) if t.shape[0] > 1 else t.shape[1])
 
 
-def gemm(a, b, out=None, *, variant: int = VARIANT_AUTO, config: int = -1, stream=None):
-    """C = A x B on the GPU for row-major torch tensors (FP32 C).
+def gemm(a, b, out=None, *, alpha: float = 1.0, beta: float = 0.0, out_dtype=None,
+         variant: int = VARIANT_AUTO, config: int = -1, stream=None):
+    """out = alpha * (A x B) + beta * out on the GPU for row-major torch tensors.
 
     ``a`` (M x K) and ``b`` (K x N) are CUDA tensors of the same dtype
-    (float32, float16 or bfloat16) with unit inner stride; ``out`` (M x N,
-    float32) is allocated if not given.  Runs on ``stream`` (default: torch's
-    current stream) and returns ``out`` without synchronising.
+    (float32, float16 or bfloat16) with unit inner stride.  ``out`` (M x N) may
+    be float32, float16 or bfloat16; if not given it is allocated with
+    ``out_dtype`` (default float32), which beta == 0 requires.  With alpha = 1,
+    beta = 0 and a float32 ``out`` this is migemm_gemm_variant, otherwise
+    migemm_gemm_ex_variant.  Runs on ``stream`` (default: torch's current stream)
+    and returns ``out`` without synchronising.
     """
     import torch
     if a.device.type != "cuda" or b.device.type != "cuda":
@@ -167,14 +191,23 @@ def gemm(a, b, out=None, *, variant: int = VARIANT_AUTO, config: int = -1, strea
     if K != K2:
         raise ValueError(f"inner dimensions differ: {tuple(a.shape)} x {tuple(b.shape)}")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
-    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N):
-        raise ValueError("out must be float32 of shape (M, N)")
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an existing out")
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    elif tuple(out.shape) != (M, N) or (out_dtype is not None and out.dtype != out_dtype):
+        raise ValueError("out must have shape (M, N) (and out_dtype, if given)")
+    cd = _dtype_code(out)
     if stream is None:
         stream = torch.cuda.current_stream(a.device).cuda_stream
-    st = migemm_gemm_variant(variant, config, M, N, K, dt, a.data_ptr() or None, _ld(a),
-                             b.data_ptr() or None, _ld(b), out.data_ptr() or None, _ld(out),
-                             stream)
+    pa, pb, pc = a.data_ptr() or None, b.data_ptr() or None, out.data_ptr() or None
+    if alpha == 1.0 and beta == 0.0 and cd == F32:
+        st = migemm_gemm_variant(variant, config, M, N, K, dt, pa, _ld(a), pb, _ld(b), pc,
+                                 _ld(out), stream)
+        where = "migemm_gemm_variant"
+    else:
+        st = migemm_gemm_ex_variant(variant, config, M, N, K, dt, pa, _ld(a), pb, _ld(b),
+                                    float(alpha), float(beta), cd, pc, _ld(out), stream)
+        where = "migemm_gemm_ex_variant"
     if st != OK:
-        raise MigemmError(st, "migemm_gemm_variant")
+        raise MigemmError(st, where)
     return out

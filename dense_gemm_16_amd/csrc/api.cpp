@@ -51,10 +51,12 @@ void extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int es, uintp
 
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
 
+bool known_dtype(int d) { return d == MIGEMM_F32 || d == MIGEMM_F16 || d == MIGEMM_BF16; }
+
 int check_args(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
-               const void* B, int64_t ldb, const float* C, int64_t ldc, bool need_ptrs) {
-    if (dtype != MIGEMM_F32 && dtype != MIGEMM_F16 && dtype != MIGEMM_BF16)
-        return MIGEMM_ERR_INVALID_ARG;
+               const void* B, int64_t ldb, const void* C, int64_t ldc, int c_dtype,
+               bool need_ptrs) {
+    if (!known_dtype(dtype) || !known_dtype(c_dtype)) return MIGEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return MIGEMM_ERR_INVALID_ARG;
     if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
@@ -66,7 +68,7 @@ int check_args(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_
     if (M > 0 && N > 0) {
         const int es = elem_size(dtype);
         uintptr_t c0, c1;
-        extent(C, M, N, ldc, 4, c0, c1);
+        extent(C, M, N, ldc, elem_size(c_dtype), c0, c1);
         if (K > 0) {
             uintptr_t a0, a1, b0, b1;
             extent(A, M, K, lda, es, a0, a1);
@@ -110,8 +112,9 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool aligned, int& varia
 }
 
 int run(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype, const void* A,
-        int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-    int st = check_args(M, N, K, dtype, A, lda, B, ldb, C, ldc, true);
+        int64_t lda, const void* B, int64_t ldb, float alpha, float beta, int c_dtype, void* C,
+        int64_t ldc, void* stream) {
+    int st = check_args(M, N, K, dtype, A, lda, B, ldb, C, ldc, c_dtype, true);
     if (st != MIGEMM_OK) return st;
     if (variant == MIGEMM_VARIANT_AUTO) {
         if (config != -1) return MIGEMM_ERR_INVALID_ARG;
@@ -128,14 +131,9 @@ int run(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype, con
     if (config < 0 || config >= v.count()) return MIGEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return MIGEMM_OK;
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err;
-    if (K == 0) {
-        err = launch_zero_fill(C, M, N, ldc, s);
-    } else {
-        GemmArgs g{M, N, K, dtype, A, lda, B, ldb, C, ldc, s};
-        err = v.launch(g, config);
-    }
+    const GemmArgs g{M, N, K, dtype, A, lda, B, ldb, Epi{C, ldc, alpha, beta, c_dtype},
+                     static_cast<hipStream_t>(stream)};
+    const hipError_t err = K == 0 ? launch_empty_product(g) : v.launch(g, config);
     if (err != hipSuccess) {
         g_last_hip_error = static_cast<int>(err);
         return MIGEMM_ERR_HIP;
@@ -152,13 +150,29 @@ extern "C" {
 
 int migemm_gemm(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
                 const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-    return run(MIGEMM_VARIANT_AUTO, -1, M, N, K, dtype, A, lda, B, ldb, C, ldc, stream);
+    return run(MIGEMM_VARIANT_AUTO, -1, M, N, K, dtype, A, lda, B, ldb, 1.0f, 0.0f, MIGEMM_F32,
+               C, ldc, stream);
 }
 
 int migemm_gemm_variant(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype,
                         const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
                         int64_t ldc, void* stream) {
-    return run(variant, config, M, N, K, dtype, A, lda, B, ldb, C, ldc, stream);
+    return run(variant, config, M, N, K, dtype, A, lda, B, ldb, 1.0f, 0.0f, MIGEMM_F32, C, ldc,
+               stream);
+}
+
+int migemm_gemm_ex(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                   const void* B, int64_t ldb, float alpha, float beta, int c_dtype, void* C,
+                   int64_t ldc, void* stream) {
+    return run(MIGEMM_VARIANT_AUTO, -1, M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype, C,
+               ldc, stream);
+}
+
+int migemm_gemm_ex_variant(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, float alpha,
+                           float beta, int c_dtype, void* C, int64_t ldc, void* stream) {
+    return run(variant, config, M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype, C, ldc,
+               stream);
 }
 
 int migemm_variant_count(void) { return kNumVariants; }
@@ -187,7 +201,7 @@ int migemm_select(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int
     (void)A;
     (void)B;
     (void)C;
-    int st = check_args(M, N, K, dtype, A, lda, B, ldb, C, ldc, false);
+    int st = check_args(M, N, K, dtype, A, lda, B, ldb, C, ldc, MIGEMM_F32, false);
     if (st != MIGEMM_OK) return st;
     if (!variant || !config) return MIGEMM_ERR_INVALID_ARG;
     select(M, N, K, dtype, operands_aligned(A, lda, B, ldb), *variant, *config);
@@ -206,6 +220,6 @@ const char* migemm_status_string(int status) {
 
 int migemm_last_hip_error(void) { return g_last_hip_error; }
 
-int migemm_version(void) { return 100; }
+int migemm_version(void) { return 200; }
 
 }  // extern "C"

@@ -7,6 +7,20 @@
 
 namespace migemm {
 
+// The output step of one product: where C lives and how the FP32 sum of
+// products v of each element becomes that element.  Plain (alpha = 1, beta = 0,
+// FP32 C): C = v.  General: C = alpha v + beta C_old, in FP32 (beta == 0 leaves
+// C_old unread), then rounded to nearest even into the output format (page
+// "CUDA-Practice 09", section on FP32 accumulation: the accumulator is written
+// back as FP32 or rounded as required; page "matmul_registers.cu", the library
+// call scaling the product by alpha and the previous C by beta).
+struct Epi {
+    void* C;
+    int64_t ldc;
+    float alpha, beta;
+    int c_dtype;  // 0 FP32, 1 FP16, 2 BF16
+};
+
 // Arguments of one product, already validated by the C ABI.
 struct GemmArgs {
     int64_t M, N, K;
@@ -15,9 +29,10 @@ struct GemmArgs {
     int64_t lda;
     const void* B;
     int64_t ldb;
-    float* C;
-    int64_t ldc;
+    Epi out;
     hipStream_t stream;
+    // True unless the output step is the plain FP32 overwrite.
+    bool general() const { return !(out.alpha == 1.0f && out.beta == 0.0f && out.c_dtype == 0); }
 };
 
 // Storage of a bfloat16 element: its 16 bits.
@@ -31,6 +46,55 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(_Float16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ float to_f32(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+
+// FP32 -> BF16 bits, round to nearest even (gfx950 converts in hardware; NaN
+// stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Writes v, the FP32 sum of products of element idx (row * ldc + col) of C, as
+// the output step says.  GEN == false is the plain FP32 overwrite (the only
+// form the kernels compile for the default call); NT selects non-temporal
+// stores.
+template <bool GEN, bool NT = false>
+__device__ __forceinline__ void store_out(const Epi& e, int64_t idx, float v) {
+    if constexpr (!GEN) {
+        float* p = static_cast<float*>(e.C) + idx;
+        if constexpr (NT)
+            __builtin_nontemporal_store(v, p);
+        else
+            *p = v;
+    } else {
+        if (e.c_dtype == 0) {
+            float* p = static_cast<float*>(e.C) + idx;
+            const float r = e.beta != 0.0f ? fmaf(e.alpha, v, e.beta * *p) : e.alpha * v;
+            if constexpr (NT)
+                __builtin_nontemporal_store(r, p);
+            else
+                *p = r;
+        } else if (e.c_dtype == 1) {
+            _Float16* p = static_cast<_Float16*>(e.C) + idx;
+            const float r =
+                e.beta != 0.0f ? fmaf(e.alpha, v, e.beta * static_cast<float>(*p)) : e.alpha * v;
+            const _Float16 h = static_cast<_Float16>(r);
+            if constexpr (NT)
+                __builtin_nontemporal_store(h, p);
+            else
+                *p = h;
+        } else {
+            uint16_t* p = static_cast<uint16_t*>(e.C) + idx;
+            const float r = e.beta != 0.0f
+                                ? fmaf(e.alpha, v, e.beta * __uint_as_float(static_cast<uint32_t>(*p) << 16))
+                                : e.alpha * v;
+            const uint16_t b = f32_to_bf16_bits(r);
+            if constexpr (NT)
+                __builtin_nontemporal_store(b, p);
+            else
+                *p = b;
+        }
+    }
 }
 
 template <typename T> struct ZeroOf { static __device__ __forceinline__ T get() { return T(0); } };
@@ -60,7 +124,8 @@ hipError_t launch_lds_tiled(const GemmArgs& a, int config);
 hipError_t launch_regtile_valu(const GemmArgs& a, int config);
 hipError_t launch_regtile_mfma(const GemmArgs& a, int config);
 hipError_t launch_mfma16(const GemmArgs& a, int config);
-hipError_t launch_zero_fill(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s);
+// K == 0: the sum of products is 0 for every element; applies the output step to it.
+hipError_t launch_empty_product(const GemmArgs& a);
 
 // Configuration tables, one per variant (names, and the count).
 int naive_config_count();

@@ -1,27 +1,34 @@
-// fill.hip -- C = 0 over an M x N window with leading dimension ldc: the
-// product with K == 0 (an empty sum).  A kernel rather than a memset so that
-// the padding between rows is left untouched and the call stays capturable.
+// fill.hip -- the product with K == 0: every sum of products is empty, so each
+// element of the M x N window of C receives the output step applied to 0
+// (C = 0 for the plain overwrite, C = beta C_old in general).  A kernel rather
+// than a memset so that the padding between rows is left untouched and the
+// call stays capturable.
 #include "common.hpp"
 
 namespace migemm {
 namespace {
 
-__global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ C, int64_t M,
-                                                        int64_t N, int64_t ldc) {
+template <bool GEN>
+__global__ __launch_bounds__(256) void empty_product_kernel(Epi out, int64_t M, int64_t N) {
     const int64_t total = M * N;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total;
          e += static_cast<int64_t>(gridDim.x) * 256) {
         const int64_t r = e / N, c = e % N;
-        C[r * ldc + c] = 0.0f;
+        store_out<GEN>(out, r * out.ldc + c, 0.0f);
     }
 }
 
 }  // namespace
 
-hipError_t launch_zero_fill(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t s) {
-    int64_t blocks = ceil_div(M * N, 256);
+hipError_t launch_empty_product(const GemmArgs& g) {
+    int64_t blocks = ceil_div(g.M * g.N, 256);
     if (blocks > 65536) blocks = 65536;
-    zero_fill_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(C, M, N, ldc);
+    if (g.general())
+        empty_product_kernel<true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, g.stream>>>(
+            g.out, g.M, g.N);
+    else
+        empty_product_kernel<false><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, g.stream>>>(
+            g.out, g.M, g.N);
     return hipGetLastError();
 }
 

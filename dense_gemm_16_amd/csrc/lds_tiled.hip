@@ -19,11 +19,11 @@
 namespace migemm {
 namespace {
 
-template <int T>
+template <int T, bool GEN>
 __global__ __launch_bounds__(T* T) void lds_tiled_kernel(int64_t M, int64_t N, int64_t K,
                                                         const float* __restrict__ A, int64_t lda,
                                                         const float* __restrict__ B, int64_t ldb,
-                                                        float* __restrict__ C, int64_t ldc) {
+                                                        Epi out) {
     __shared__ float As[T][T + 1];
     __shared__ float Bs[T][T];
     const int tx = threadIdx.x, ty = threadIdx.y;
@@ -42,18 +42,18 @@ __global__ __launch_bounds__(T* T) void lds_tiled_kernel(int64_t M, int64_t N, i
             for (int p = 0; p < T; ++p) acc = fmaf(As[ty][p], Bs[p][tx], acc);
             __syncthreads();
         }
-        if (row < M && col < N) C[row * ldc + col] = acc;
+        if (row < M && col < N) store_out<GEN>(out, row * out.ldc + col, acc);
     }
 }
 
-template <int T>
+template <int T, bool GEN>
 hipError_t launch_tile(const GemmArgs& g) {
     const int64_t gy = ceil_div(g.M, T);
     dim3 grid(static_cast<unsigned>(ceil_div(g.N, T)),
               static_cast<unsigned>(gy > 65535 ? 65535 : gy));
-    lds_tiled_kernel<T><<<grid, dim3(T, T), 0, g.stream>>>(
+    lds_tiled_kernel<T, GEN><<<grid, dim3(T, T), 0, g.stream>>>(
         g.M, g.N, g.K, static_cast<const float*>(g.A), g.lda, static_cast<const float*>(g.B),
-        g.ldb, g.C, g.ldc);
+        g.ldb, g.out);
     return hipGetLastError();
 }
 
@@ -65,7 +65,8 @@ int lds_tiled_config_count() { return 2; }
 const char* lds_tiled_config_name(int c) { return (c >= 0 && c < 2) ? kNames[c] : nullptr; }
 
 hipError_t launch_lds_tiled(const GemmArgs& g, int config) {
-    return config == 1 ? launch_tile<16>(g) : launch_tile<32>(g);
+    if (g.general()) return config == 1 ? launch_tile<16, true>(g) : launch_tile<32, true>(g);
+    return config == 1 ? launch_tile<16, false>(g) : launch_tile<32, false>(g);
 }
 
 }  // namespace migemm

@@ -137,11 +137,10 @@ __device__ __forceinline__ void wait_then_barrier() {
     asm volatile("" : : : "memory");
 }
 
-template <class Cfg>
+template <class Cfg, bool GEN>
 __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     int64_t M, int64_t N, int64_t K, const typename Cfg::E* __restrict__ A, int64_t lda,
-    const typename Cfg::E* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
-    int tiles_m, int tiles_n) {
+    const typename Cfg::E* __restrict__ B, int64_t ldb, Epi out, int tiles_m, int tiles_n) {
     using E = typename Cfg::E;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, MF = Cfg::MF, TM = Cfg::TM, TN = Cfg::TN;
     constexpr int NW = Cfg::NW, BCH = Cfg::BCH, S = Cfg::STAGES, NI = Cfg::NI, CA = Cfg::CA;
@@ -362,12 +361,8 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 #pragma unroll
             for (int r = 0; r < L::R; ++r) {
                 const int64_t row = m0 + wm0 + i * MF + L::row(lane, r);
-                if (full_mn || (row < M && col < N)) {
-                    if constexpr (Cfg::FLAGS & 2)
-                        __builtin_nontemporal_store(acc[i][j][r], C + row * ldc + col);
-                    else
-                        C[row * ldc + col] = acc[i][j][r];
-                }
+                if (full_mn || (row < M && col < N))
+                    store_out<GEN, (Cfg::FLAGS & 2) != 0>(out, row * out.ldc + col, acc[i][j][r]);
             }
         }
     }
@@ -382,15 +377,16 @@ inline bool direct_ok(const GemmArgs& g, int bk = 64) {
            g.lda < (int64_t(1) << 21) && g.ldb < (int64_t(1) << 23);
 }
 
-template <class Cfg>
+template <class Cfg, bool GEN>
 hipError_t launch_direct_cfg(const GemmArgs& g) {
     using E = typename Cfg::E;
     const int64_t tm = ceil_div(g.M, Cfg::BM), tn = ceil_div(g.N, Cfg::BN);
     if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-    mfma16_direct_kernel<Cfg><<<dim3(static_cast<unsigned>(tm * tn)), dim3(Cfg::NT), 0,
-                                 g.stream>>>(g.M, g.N, g.K, static_cast<const E*>(g.A), g.lda,
-                                             static_cast<const E*>(g.B), g.ldb, g.C, g.ldc,
-                                             static_cast<int>(tm), static_cast<int>(tn));
+    mfma16_direct_kernel<Cfg, GEN><<<dim3(static_cast<unsigned>(tm * tn)), dim3(Cfg::NT), 0,
+                                      g.stream>>>(g.M, g.N, g.K, static_cast<const E*>(g.A),
+                                                  g.lda, static_cast<const E*>(g.B), g.ldb,
+                                                  g.out, static_cast<int>(tm),
+                                                  static_cast<int>(tn));
     return hipGetLastError();
 }
 

@@ -219,11 +219,10 @@ struct MfmaCfg {
     static_assert(NT <= 1024, "at most 1024 work-items per workgroup");
 };
 
-template <class Cfg, bool AV, bool BV>
+template <class Cfg, bool AV, bool BV, bool GEN>
 __global__ __launch_bounds__(Cfg::NT) void mfma_gemm_kernel(
     int64_t M, int64_t N, int64_t K, const typename Cfg::E* __restrict__ A, int64_t lda,
-    const typename Cfg::E* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
-    int tiles_m, int tiles_n) {
+    const typename Cfg::E* __restrict__ B, int64_t ldb, Epi out, int tiles_m, int tiles_n) {
     using E = typename Cfg::E;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, MF = Cfg::MF, NT = Cfg::NT, VEC = Cfg::VEC;
     constexpr int CH = Cfg::CH, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN, G = Cfg::G;
@@ -350,7 +349,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma_gemm_kernel(
         __syncthreads();
     }
 
-    // Epilogue: FP32 accumulators -> C (overwrite).
+    // Epilogue: FP32 accumulators -> C through the output step.
     const int lc = L::col(lane);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -360,14 +359,16 @@ __global__ __launch_bounds__(Cfg::NT) void mfma_gemm_kernel(
 #pragma unroll
             for (int r = 0; r < L::R; ++r) {
                 const int64_t row = m0 + wm0 + i * MF + L::row(lane, r);
-                if (full_mn || (row < M && col < N)) C[row * ldc + col] = acc[i][j][r];
+                if (full_mn || (row < M && col < N))
+                    store_out<GEN>(out, row * out.ldc + col, acc[i][j][r]);
             }
         }
     }
 }
 
-// Host side: launches configuration Cfg on the given arguments.
-template <class Cfg>
+// Host side: launches configuration Cfg on the given arguments, with the
+// plain FP32 overwrite (GEN == false) or the general output step.
+template <class Cfg, bool GEN>
 hipError_t launch_mfma_cfg(const GemmArgs& g) {
     using E = typename Cfg::E;
     constexpr int VEC = Cfg::VEC;
@@ -379,18 +380,27 @@ hipError_t launch_mfma_cfg(const GemmArgs& g) {
     const E* B = static_cast<const E*>(g.B);
     dim3 grid(static_cast<unsigned>(tm * tn)), block(Cfg::NT);
     const int itm = static_cast<int>(tm), itn = static_cast<int>(tn);
-    if (av && bv)
-        mfma_gemm_kernel<Cfg, true, true><<<grid, block, 0, g.stream>>>(
-            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, itm, itn);
+    // The general output step is compiled for the two common load forms only
+    // (both operands vectorised, or neither), which bounds the instantiations.
+    if constexpr (GEN) {
+        if (av && bv)
+            mfma_gemm_kernel<Cfg, true, true, true><<<grid, block, 0, g.stream>>>(
+                g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
+        else
+            mfma_gemm_kernel<Cfg, false, false, true><<<grid, block, 0, g.stream>>>(
+                g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
+    } else if (av && bv)
+        mfma_gemm_kernel<Cfg, true, true, false><<<grid, block, 0, g.stream>>>(
+            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
     else if (av)
-        mfma_gemm_kernel<Cfg, true, false><<<grid, block, 0, g.stream>>>(
-            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, itm, itn);
+        mfma_gemm_kernel<Cfg, true, false, false><<<grid, block, 0, g.stream>>>(
+            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
     else if (bv)
-        mfma_gemm_kernel<Cfg, false, true><<<grid, block, 0, g.stream>>>(
-            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, itm, itn);
+        mfma_gemm_kernel<Cfg, false, true, false><<<grid, block, 0, g.stream>>>(
+            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
     else
-        mfma_gemm_kernel<Cfg, false, false><<<grid, block, 0, g.stream>>>(
-            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, itm, itn);
+        mfma_gemm_kernel<Cfg, false, false, false><<<grid, block, 0, g.stream>>>(
+            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
     return hipGetLastError();
 }
 

@@ -17,11 +17,11 @@
 namespace migemm {
 namespace {
 
-template <typename T, int BX, int BY>
+template <typename T, int BX, int BY, bool GEN>
 __global__ __launch_bounds__(BX* BY) void naive_kernel(int64_t M, int64_t N, int64_t K,
                                                        const T* __restrict__ A, int64_t lda,
                                                        const T* __restrict__ B, int64_t ldb,
-                                                       float* __restrict__ C, int64_t ldc) {
+                                                       Epi out) {
     const int64_t col = static_cast<int64_t>(blockIdx.x) * BX + threadIdx.x;
     if (col >= N) return;
     // grid.y is capped at 65535 by the launcher; rows beyond it loop.
@@ -31,11 +31,11 @@ __global__ __launch_bounds__(BX* BY) void naive_kernel(int64_t M, int64_t N, int
         const T* b = B + col;
         float acc = 0.0f;
         for (int64_t k = 0; k < K; ++k) acc = fmaf(to_f32(a[k]), to_f32(b[k * ldb]), acc);
-        C[row * ldc + col] = acc;
+        store_out<GEN>(out, row * out.ldc + col, acc);
     }
 }
 
-template <int BX, int BY>
+template <int BX, int BY, bool GEN>
 hipError_t launch_shape(const GemmArgs& g) {
     const int64_t gy = ceil_div(g.M, BY);
     dim3 grid(static_cast<unsigned>(ceil_div(g.N, BX)),
@@ -43,19 +43,19 @@ hipError_t launch_shape(const GemmArgs& g) {
     dim3 block(BX, BY);
     switch (g.dtype) {
         case 0:
-            naive_kernel<float, BX, BY><<<grid, block, 0, g.stream>>>(
+            naive_kernel<float, BX, BY, GEN><<<grid, block, 0, g.stream>>>(
                 g.M, g.N, g.K, static_cast<const float*>(g.A), g.lda,
-                static_cast<const float*>(g.B), g.ldb, g.C, g.ldc);
+                static_cast<const float*>(g.B), g.ldb, g.out);
             break;
         case 1:
-            naive_kernel<_Float16, BX, BY><<<grid, block, 0, g.stream>>>(
+            naive_kernel<_Float16, BX, BY, GEN><<<grid, block, 0, g.stream>>>(
                 g.M, g.N, g.K, static_cast<const _Float16*>(g.A), g.lda,
-                static_cast<const _Float16*>(g.B), g.ldb, g.C, g.ldc);
+                static_cast<const _Float16*>(g.B), g.ldb, g.out);
             break;
         default:
-            naive_kernel<bf16_t, BX, BY><<<grid, block, 0, g.stream>>>(
+            naive_kernel<bf16_t, BX, BY, GEN><<<grid, block, 0, g.stream>>>(
                 g.M, g.N, g.K, static_cast<const bf16_t*>(g.A), g.lda,
-                static_cast<const bf16_t*>(g.B), g.ldb, g.C, g.ldc);
+                static_cast<const bf16_t*>(g.B), g.ldb, g.out);
             break;
     }
     return hipGetLastError();
@@ -70,7 +70,8 @@ const char* naive_config_name(int c) { return (c >= 0 && c < 2) ? kNames[c] : nu
 
 hipError_t launch_naive(const GemmArgs& g, int config) {
     // The grid's x extent must fit 32 bits; N < 2^31 is checked by the caller.
-    return config == 1 ? launch_shape<16, 16>(g) : launch_shape<64, 4>(g);
+    if (g.general()) return config == 1 ? launch_shape<16, 16, true>(g) : launch_shape<64, 4, true>(g);
+    return config == 1 ? launch_shape<16, 16, false>(g) : launch_shape<64, 4, false>(g);
 }
 
 }  // namespace migemm

@@ -24,19 +24,24 @@ const char* const kNames[] = {"128x128x32 4w 16x16x4", "128x128x32 4w 32x32x2",
                               "64x64x32 4w 16x16x4", "256x128x32 4w 32x32x2",
                               "128x64x32 4w 16x16x4"};
 
+template <bool GEN>
+hipError_t launch_gen(const GemmArgs& g, int config) {
+    switch (config) {
+        case 1: return launch_mfma_cfg<F1, GEN>(g);
+        case 2: return launch_mfma_cfg<F2, GEN>(g);
+        case 3: return launch_mfma_cfg<F3, GEN>(g);
+        case 4: return launch_mfma_cfg<F4, GEN>(g);
+        default: return launch_mfma_cfg<F0, GEN>(g);
+    }
+}
+
 }  // namespace
 
 int regtile_mfma_config_count() { return 5; }
 const char* regtile_mfma_config_name(int c) { return (c >= 0 && c < 5) ? kNames[c] : nullptr; }
 
 hipError_t launch_regtile_mfma(const GemmArgs& g, int config) {
-    switch (config) {
-        case 1: return launch_mfma_cfg<F1>(g);
-        case 2: return launch_mfma_cfg<F2>(g);
-        case 3: return launch_mfma_cfg<F3>(g);
-        case 4: return launch_mfma_cfg<F4>(g);
-        default: return launch_mfma_cfg<F0>(g);
-    }
+    return g.general() ? launch_gen<true>(g, config) : launch_gen<false>(g, config);
 }
 
 }  // namespace migemm

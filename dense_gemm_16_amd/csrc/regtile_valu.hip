@@ -38,11 +38,11 @@ __device__ __forceinline__ f32x4 ld4_guarded(const float* __restrict__ base, int
     return v;
 }
 
-template <int BM, int BN, int BK, int TM, int TN>
+template <int BM, int BN, int BK, int TM, int TN, bool GEN>
 __global__ __launch_bounds__((BM / TM) * (BN / TN)) void regtile_valu_kernel(
     int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
-    const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc, bool av,
-    bool bv, bool cv, unsigned tiles_n) {
+    const float* __restrict__ B, int64_t ldb, Epi out, bool av, bool bv, bool cv,
+    unsigned tiles_n) {
     constexpr int NC = BN / TN, NR = BM / TM, NT = NC * NR;
     constexpr int PAD = 4;  // keeps k-major A rows 16-byte aligned while shifting banks
     constexpr int A_V4 = BM * BK / 4, B_V4 = BK * BN / 4;
@@ -153,32 +153,38 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void regtile_valu_kernel(
                 const int64_t col = n0 + 4 * (tc + j * NC);
                 f32x4 v = {acc[4 * i + ii][4 * j], acc[4 * i + ii][4 * j + 1],
                            acc[4 * i + ii][4 * j + 2], acc[4 * i + ii][4 * j + 3]};
-                float* p = C + row * ldc + col;
-                if (cv && (full_mn || col + 4 <= N)) {
-                    *reinterpret_cast<f32x4*>(p) = v;
+                const int64_t idx = row * out.ldc + col;
+                if (!GEN && cv && (full_mn || col + 4 <= N)) {
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(out.C) + idx) = v;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (col + e < N) p[e] = v[e];
+                        if (col + e < N) store_out<GEN>(out, idx + e, v[e]);
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, int BK, int TM, int TN>
-hipError_t launch_cfg(const GemmArgs& g) {
+template <int BM, int BN, int BK, int TM, int TN, bool GEN>
+hipError_t launch_gen(const GemmArgs& g) {
     const int64_t gx = ceil_div(g.N, BN), gy = ceil_div(g.M, BM);
     if (gx * gy > 0x7fffffff) return hipErrorInvalidValue;
     const bool av = aligned16(g.A) && g.lda % 4 == 0;
     const bool bv = aligned16(g.B) && g.ldb % 4 == 0;
-    const bool cv = aligned16(g.C) && g.ldc % 4 == 0;
-    regtile_valu_kernel<BM, BN, BK, TM, TN>
+    const bool cv = aligned16(g.out.C) && g.out.ldc % 4 == 0;
+    regtile_valu_kernel<BM, BN, BK, TM, TN, GEN>
         <<<dim3(static_cast<unsigned>(gx * gy)), dim3((BM / TM) * (BN / TN)), 0, g.stream>>>(
             g.M, g.N, g.K, static_cast<const float*>(g.A), g.lda,
-            static_cast<const float*>(g.B), g.ldb, g.C, g.ldc, av, bv, cv,
+            static_cast<const float*>(g.B), g.ldb, g.out, av, bv, cv,
             static_cast<unsigned>(gx));
     return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int TM, int TN>
+hipError_t launch_cfg(const GemmArgs& g) {
+    return g.general() ? launch_gen<BM, BN, BK, TM, TN, true>(g)
+                       : launch_gen<BM, BN, BK, TM, TN, false>(g);
 }
 
 const char* const kNames[] = {"128x128x8 8x8", "128x128x16 8x8", "64x64x16 4x4",

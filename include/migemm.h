@@ -36,6 +36,9 @@
  * or exits.  Argument errors are detected before any HIP call.  Degenerate
  * shapes: M == 0 or N == 0 is a no-op returning MIGEMM_OK; K == 0 writes
  * C = 0 (an empty sum) over the M x N window.
+ *
+ * The general form migemm_gemm_ex adds the scaled update C = alpha A B + beta C
+ * and FP16/BF16 storage of C (below).
  */
 #ifndef MIGEMM_H
 #define MIGEMM_H
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-/* Element type of A and B.  C is always FP32. */
+/* Element type of A and B (and of C for migemm_gemm_ex; migemm_gemm's C is FP32). */
 typedef enum {
     MIGEMM_F32 = 0,
     MIGEMM_F16 = 1,  /* IEEE binary16 */
@@ -113,6 +116,42 @@ int migemm_gemm_variant(int variant, int config,
                         int64_t M, int64_t N, int64_t K, int dtype,
                         const void* A, int64_t lda, const void* B, int64_t ldb,
                         float* C, int64_t ldc, void* stream);
+
+/*
+ * The general product:
+ *
+ *     C[i][j] = alpha * (sum_{k=0}^{K-1} A[i][k] * B[k][j]) + beta * C[i][j]
+ *
+ * the scaled update of the library call on page "matmul_registers.cu" (its
+ * alpha multiplies the product, its beta the previous C), with C stored as FP32
+ * or rounded into FP16 or BF16 (page "CUDA-Practice 09", section on FP32
+ * accumulation: the FP32 accumulator is written back as FP32 or rounded as
+ * required).
+ *
+ * The sum of products is the same FP32 accumulation, by the same kernels, as
+ * migemm_gemm.  Per element the update is then computed in FP32 (beta * C_old
+ * first, fused with alpha * sum) and rounded to nearest even into c_dtype
+ * (MIGEMM_F32, MIGEMM_F16 or MIGEMM_BF16; magnitudes beyond the format's range
+ * become +-infinity).  When beta == 0 the previous C is not read and may hold
+ * anything, NaN included.  C points to c_dtype elements, row-major with leading
+ * dimension ldc (elements).  K == 0 gives C = beta * C_old (or 0).
+ * alpha == 1, beta == 0, c_dtype == MIGEMM_F32 is exactly migemm_gemm.
+ * Same pointer, stream, ownership and error rules as migemm_gemm; an unknown
+ * c_dtype is MIGEMM_ERR_INVALID_ARG, and C must not overlap A or B.  The
+ * selection depends on A, B and the sizes only, as for migemm_gemm.
+ */
+int migemm_gemm_ex(int64_t M, int64_t N, int64_t K, int dtype,
+                   const void* A, int64_t lda, const void* B, int64_t ldb,
+                   float alpha, float beta, int c_dtype, void* C, int64_t ldc,
+                   void* stream);
+
+/* As migemm_gemm_ex, with the variant and configuration forced as in
+ * migemm_gemm_variant. */
+int migemm_gemm_ex_variant(int variant, int config,
+                           int64_t M, int64_t N, int64_t K, int dtype,
+                           const void* A, int64_t lda, const void* B, int64_t ldb,
+                           float alpha, float beta, int c_dtype, void* C, int64_t ldc,
+                           void* stream);
 
 /* Number of variants (they are numbered 0 .. count-1). */
 int migemm_variant_count(void);

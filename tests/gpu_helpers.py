@@ -76,3 +76,57 @@ def sampled_entries(M, N, n, seed=0, include_edges=True):
             rows.append(r)
             cols.append(c)
     return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
+
+
+TORCH_OF = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}
+
+
+def run_gemm_ex(A: torch.Tensor, B: torch.Tensor, dtype: str, alpha: float, beta: float,
+                c_code: int, c_old: torch.Tensor | None = None, variant=-1, config=-1,
+                ldc=None, c_off=0):
+    """C = alpha * A x B + beta * C_old through migemm_gemm_ex_variant, C stored as
+    c_code (0 FP32, 1 FP16, 2 BF16).  C sits inside a NaN-filled buffer (row stride
+    ``ldc``, ``c_off`` elements in); with beta == 0 the window starts as NaN too, so a
+    read of the previous C would show.  Returns (C on the CPU in its own dtype,
+    buffer, the window's mask in the buffer)."""
+    M, K = A.shape
+    N = B.shape[1]
+    dA, _ = to_device_with_ld(A)
+    dB, _ = to_device_with_ld(B)
+    ldc = ldc or max(N, 1)
+    tdt = TORCH_OF[c_code]
+    cbuf = torch.full((c_off + max(M, 1) * ldc + 64,), float("nan"), dtype=tdt, device="cuda")
+    dC = cbuf[c_off:c_off + M * ldc].view(M, ldc)[:, :N] if M else cbuf[:0].view(0, N)
+    if beta != 0.0:
+        assert c_old is not None and c_old.dtype == tdt
+        dC.copy_(c_old.to("cuda"))
+    mask = torch.zeros(cbuf.shape, dtype=torch.bool)
+    if M:
+        mask[c_off:c_off + M * ldc].view(M, ldc)[:, :N] = True
+    stream = torch.cuda.current_stream().cuda_stream
+    st = mg.migemm_gemm_ex_variant(variant, config, M, N, K, DT_CODE[dtype],
+                                   dA.data_ptr() if dA.numel() else None, max(K, 1),
+                                   dB.data_ptr() if dB.numel() else None, max(N, 1),
+                                   alpha, beta, c_code,
+                                   dC.data_ptr() if dC.numel() else None, ldc, stream)
+    torch.cuda.synchronize()
+    assert st == mg.OK, f"status {st}: {mg.migemm_status_string(st)} hip={mg.migemm_last_hip_error()}"
+    return dC.cpu().clone(), cbuf.cpu(), mask
+
+
+def check_ex(Cgpu: torch.Tensor, A, B, dtype: str, alpha, beta, c_code, c_old=None, ref=None,
+             exact=False):
+    """Compare a general-form result with the oracle's update (tolerance plus the final
+    rounding of the output format, or exact)."""
+    acc, S = ref if ref is not None else oracle_ref(A, B, dtype)
+    old = inputs.to_bits(c_old) if (c_old is not None and beta != 0.0) else None
+    want, scale = oracle.epilogue(acc, S, alpha, beta, c_code, old)
+    got = Cgpu.double().numpy()
+    r = compare(got, want, scale, tol=None if exact else tolerance(DT_CODE[dtype]), exact=exact,
+                out_dtype=None if exact else c_code)
+    assert r.ok, str(r)
+    return r
+
+
+def padding_untouched(cbuf: torch.Tensor, mask: torch.Tensor) -> bool:
+    return bool(torch.isnan(cbuf[~mask].float()).all())
