@@ -57,14 +57,19 @@ def source_hash() -> str:
 class Problem:
     """Device-resident operands of one workload and a launcher for it."""
 
-    def __init__(self, w, variant=-1, config=-1):
+    def __init__(self, w, variant=-1, config=-1, alpha=1.0, beta=0.0, c_code=0):
         import torch
         import dense_gemm_16_amd as mg
         from dense_gemm_16_amd import inputs
         self.w, self.mg = w, mg
         self.A, self.B = w.make()
         self.dA, self.dB = self.A.cuda(), self.B.cuda()
-        self.C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        cdt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[c_code]
+        self.C = torch.empty((w.M, w.N), dtype=cdt, device="cuda")
+        if beta != 0.0:
+            self.C.copy_(torch.randn((w.M, w.N), generator=torch.Generator().manual_seed(w.seed + 1)))
+        self.epi = (float(alpha), float(beta), c_code)
+        self.general = not (alpha == 1.0 and beta == 0.0 and c_code == 0)
         self.code = inputs.DTYPE_CODES[w.dtype]
         st, v, c = mg.migemm_select(w.M, w.N, w.K, self.code, self.dA.data_ptr(), w.K,
                                     self.dB.data_ptr(), w.N, self.C.data_ptr(), w.N)
@@ -83,7 +88,11 @@ class Problem:
                 f"{self.mg.migemm_config_name(self.variant, self.config)}]")
 
     def launch(self):
-        st = self.mg.migemm_gemm_variant(*self.args)
+        if self.general:
+            a = self.args
+            st = self.mg.migemm_gemm_ex_variant(*a[:10], *self.epi, *a[10:])
+        else:
+            st = self.mg.migemm_gemm_variant(*self.args)
         if st != self.mg.OK:
             raise RuntimeError(f"{self.w.name}: {self.mg.migemm_status_string(st)} "
                                f"(hip {self.mg.migemm_last_hip_error()})")
@@ -374,6 +383,18 @@ def main():
                                           "frac_of_peak": round(tf / PEAK_TFLOPS["f32"], 4),
                                           "kernel": pn.kernel_name()}
                 log(f"extra {name}/naive: {tf:.2f} TFLOPS")
+            del px
+        # the general output step on the headline shape: scaled update, BF16 C
+        if w.name == "c4-bf16-8192":
+            px = Problem(w, alpha=0.5, beta=-1.0, c_code=2)
+            t, n = px.time_window()
+            tf = w.flop / (t * 1e-3) / 1e12
+            extra[w.name + "/alpha-beta-bf16-out"] = {
+                "tflops": round(tf, 2), "ms": round(t, 5), "launches": n,
+                "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
+                "kernel": px.kernel_name() + " general output step",
+                "update": "C = 0.5 A B - 1.0 C, C stored as BF16"}
+            log(f"extra {w.name} general (alpha 0.5, beta -1, BF16 C): {tf:.1f} TFLOPS")
             del px
 
     cpu = None

@@ -54,6 +54,41 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// The previous value of element idx of C, widened to FP32 (general form, beta != 0).
+__device__ __forceinline__ float load_prev(const Epi& e, int64_t idx) {
+    if (e.c_dtype == 0) return static_cast<const float*>(e.C)[idx];
+    if (e.c_dtype == 1) return static_cast<float>(static_cast<const _Float16*>(e.C)[idx]);
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(e.C)[idx]) << 16);
+}
+
+// Stores alpha v + beta prev (alpha v when beta == 0), computed in FP32 and
+// rounded to nearest even into the output format; NT selects non-temporal stores.
+template <bool NT>
+__device__ __forceinline__ void store_update(const Epi& e, int64_t idx, float v, float prev) {
+    const float r = e.beta != 0.0f ? fmaf(e.alpha, v, e.beta * prev) : e.alpha * v;
+    if (e.c_dtype == 0) {
+        float* p = static_cast<float*>(e.C) + idx;
+        if constexpr (NT)
+            __builtin_nontemporal_store(r, p);
+        else
+            *p = r;
+    } else if (e.c_dtype == 1) {
+        _Float16* p = static_cast<_Float16*>(e.C) + idx;
+        const _Float16 h = static_cast<_Float16>(r);
+        if constexpr (NT)
+            __builtin_nontemporal_store(h, p);
+        else
+            *p = h;
+    } else {
+        uint16_t* p = static_cast<uint16_t*>(e.C) + idx;
+        const uint16_t b = f32_to_bf16_bits(r);
+        if constexpr (NT)
+            __builtin_nontemporal_store(b, p);
+        else
+            *p = b;
+    }
+}
+
 // Writes v, the FP32 sum of products of element idx (row * ldc + col) of C, as
 // the output step says.  GEN == false is the plain FP32 overwrite (the only
 // form the kernels compile for the default call); NT selects non-temporal
@@ -67,33 +102,7 @@ __device__ __forceinline__ void store_out(const Epi& e, int64_t idx, float v) {
         else
             *p = v;
     } else {
-        if (e.c_dtype == 0) {
-            float* p = static_cast<float*>(e.C) + idx;
-            const float r = e.beta != 0.0f ? fmaf(e.alpha, v, e.beta * *p) : e.alpha * v;
-            if constexpr (NT)
-                __builtin_nontemporal_store(r, p);
-            else
-                *p = r;
-        } else if (e.c_dtype == 1) {
-            _Float16* p = static_cast<_Float16*>(e.C) + idx;
-            const float r =
-                e.beta != 0.0f ? fmaf(e.alpha, v, e.beta * static_cast<float>(*p)) : e.alpha * v;
-            const _Float16 h = static_cast<_Float16>(r);
-            if constexpr (NT)
-                __builtin_nontemporal_store(h, p);
-            else
-                *p = h;
-        } else {
-            uint16_t* p = static_cast<uint16_t*>(e.C) + idx;
-            const float r = e.beta != 0.0f
-                                ? fmaf(e.alpha, v, e.beta * __uint_as_float(static_cast<uint32_t>(*p) << 16))
-                                : e.alpha * v;
-            const uint16_t b = f32_to_bf16_bits(r);
-            if constexpr (NT)
-                __builtin_nontemporal_store(b, p);
-            else
-                *p = b;
-        }
+        store_update<NT>(e, idx, v, e.beta != 0.0f ? load_prev(e, idx) : 0.0f);
     }
 }
 

@@ -353,17 +353,50 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 
     const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
     const int lc = L::col(lane);
+    constexpr bool NT = (Cfg::FLAGS & 2) != 0;
+    auto inside = [&](int i, int j, int r) __attribute__((always_inline)) {
+        return full_mn || (m0 + wm0 + i * MF + L::row(lane, r) < M && n0 + wn0 + j * MF + lc < N);
+    };
+    auto index = [&](int i, int j, int r) __attribute__((always_inline)) {
+        return (m0 + wm0 + i * MF + L::row(lane, r)) * out.ldc + n0 + wn0 + j * MF + lc;
+    };
+    if constexpr (!GEN) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + wn0 + j * MF + lc;
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < L::R; ++r) {
-                const int64_t row = m0 + wm0 + i * MF + L::row(lane, r);
-                if (full_mn || (row < M && col < N))
-                    store_out<GEN, (Cfg::FLAGS & 2) != 0>(out, row * out.ldc + col, acc[i][j][r]);
-            }
+                for (int r = 0; r < L::R; ++r)
+                    if (inside(i, j, r)) store_out<false, NT>(out, index(i, j, r), acc[i][j][r]);
+    } else {
+        // The general step reads the previous C (beta != 0) one row of fragments
+        // at a time, keeping the loads of the next kAhead rows in flight while a
+        // row is stored: the end-of-tile memory latency is paid about TM / kAhead
+        // times per wave instead of once per element.  The fragment registers of
+        // the main loop are free by now and hold the ring.
+        constexpr int kAhead = TM >= 4 ? 3 : TM - 1;
+        constexpr int kRing = kAhead + 1;
+        const bool rd = out.beta != 0.0f;
+        float prev[kRing][TN][L::R];
+        auto load_row = [&](int i, float (&p)[TN][L::R]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < L::R; ++r)
+                    p[j][r] = (rd && inside(i, j, r)) ? load_prev(out, index(i, j, r)) : 0.0f;
+        };
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) load_row(i, prev[i]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i + kAhead < TM) load_row(i + kAhead, prev[(i + kAhead) % kRing]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < L::R; ++r)
+                    if (inside(i, j, r))
+                        store_update<NT>(out, index(i, j, r), acc[i][j][r],
+                                         prev[i % kRing][j][r]);
         }
     }
 }
