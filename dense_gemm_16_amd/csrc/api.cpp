@@ -102,13 +102,13 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool aligned, int& varia
     // of 8 (the launcher falls back to the register-staged kernel otherwise).
     const bool direct = aligned && K % 64 == 0 && N % 8 == 0 && N >= 8;
     if (direct && tiles(256, 256) >= 256)
-        config = 32;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads
+        config = 10;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads
     else if (direct)
-        config = 19;  // direct 128x128x64, 4 waves, 4 stages
+        config = 8;   // direct 128x128x64, 4 waves, 4 stages
     else if (tiles(128, 128) >= 256)
-        config = 3;
+        config = 2;   // register-staged 128x128x64
     else
-        config = 4;
+        config = 3;   // register-staged 64x64x64
 }
 
 int run(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype, const void* A,

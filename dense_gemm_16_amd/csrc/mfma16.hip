@@ -23,25 +23,16 @@ namespace migemm {
 namespace {
 
 const char* const kNames[] = {
-    "256x256x64 8w 16x16x32",          "256x256x64 4w 16x16x32",
-    "256x128x64 4w 16x16x32",          "128x128x64 4w 16x16x32",
-    "64x64x64 4w 16x16x32",            "256x256x64 8w 32x32x16",
-    "128x128x64 4w 32x32x16",          "direct 256x256x64 4w 16x16x32",
-    "direct 256x256x64 4w 32x32x16",   "direct 256x256x64 8w 16x16x32",
-    "direct 256x256x64 8w 32x32x16",   "direct 128x128x64 4w 16x16x32",
-    "direct 256x128x64 4w 16x16x32",   "direct 128x256x64 4w 16x16x32",
-    "direct 256x256x32 8w 32x32x16 s4", "direct 256x256x32 8w 32x32x16 s5",
-    "direct 256x256x32 4w 32x32x16 s4", "direct 256x256x32 4w 32x32x16 s5",
-    "direct 128x128x64 4w 16x16x32 s3", "direct 128x128x64 4w 16x16x32 s4",
-    "direct 256x128x64 4w 32x32x16 s3", "direct 256x256x64 8w 32x32x16 prio",
-    "direct 256x256x64 8w 32x32x16 ilv", "direct 256x256x64 8w 32x32x16 ilv+prio",
-    "direct 256x256x64 8w 32x32x16 gm4", "direct 256x256x64 8w 32x32x16 gm16",
-    "direct 256x256x64 4w 32x32x16 ilv+prio",
-    "direct 256x256x64 8w 32x32x16 gm4 ilv spread",
+    "256x256x64 8w 16x16x32",
+    "256x128x64 4w 16x16x32",
+    "128x128x64 4w 16x16x32",
+    "64x64x64 4w 16x16x32",
+    "256x256x64 8w 32x32x16",
+    "direct 256x256x64 8w 16x16x32",
+    "direct 256x256x64 8w 32x32x16",
+    "direct 128x128x64 4w 16x16x32",
+    "direct 128x128x64 4w 16x16x32 s4",
     "direct 256x256x64 8w 32x32x16 gm4 ilv ntC",
-    "direct 256x256x64 8w 32x32x16 gm4 ilv spread ntC",
-    "direct 256x256x32 8w 32x32x16 s4 gm4 ilv ntC",
-    "direct 256x256x64 4w 32x32x16 gm4 ilv+prio spread ntC",
     "direct 256x256x64 8w 16x16x32 gm4 ilv ntC agpr early"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 

@@ -58,14 +58,12 @@ namespace migemm {
 #define MIGEMM_LDS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// SCHED: 0 = prefetch block then matrix block per slab; 1 = as 0 with the wave's
-// priority raised during its matrix block (s_setprio); 2 = one LDS read issued
-// after each matrix instruction (sched_group_barrier); 3 = 2 with raised priority.
-// FLAGS: bit 0 = spread each k-tile's direct loads over the slabs before the
-// barrier instead of issuing them in one burst; bit 1 = non-temporal C stores;
-// bit 2 = keep the accumulators in AGPRs (see below); bit 3 = issue a k-tile's
-// direct loads right after the barrier that frees their stage instead of at the
-// start of the next k-tile, so they have a whole k-tile of matrix work to land.
+// SCHED: 0 = a slab's LDS reads as one block, then its matrix instructions;
+// 2 = one LDS read issued after each matrix instruction (sched_group_barrier).
+// FLAGS: bit 1 = non-temporal C stores; bit 2 = keep the accumulators in AGPRs
+// (see below); bit 3 = issue a k-tile's direct loads right after the barrier
+// that frees their stage instead of at the start of the next k-tile, so they
+// have a whole k-tile of matrix work to land.
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
           int BK_ = 64, int GM_ = 8, int SCHED_ = 0, int FLAGS_ = 0>
 struct DirectCfg {
@@ -91,7 +89,8 @@ struct DirectCfg {
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "whole blocks per wave");
     static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "stages fit 160 KiB");
     static_assert((STAGES - 2) * NI <= 63, "vmcnt counts at most 63 loads");
-    static_assert(!((FLAGS & 1) && (FLAGS & 8)), "spread and early loads exclude each other");
+    static_assert(SCHED == 0 || SCHED == 2, "scheduling policy 0 or 2");
+    static_assert((FLAGS & ~14) == 0, "flags: bits 1, 2 and 3");
 };
 
 // Physical chunk of logical chunk c in row `row` of the A image (CA chunks per row).
@@ -184,23 +183,18 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     const E* const a_tile = A + m0 * lda;
     const E* const b_tile = B + n0;
 
-    // Issues this wave's direct loads number lo .. hi-1 (of NI: A's first, then
-    // B's) of k-tile kt.
-    auto issue_range = [&](int kt, int lo, int hi) __attribute__((always_inline)) {
+    // Issues this wave's NI direct loads of k-tile kt (A's, then B's) into its stage.
+    auto issue = [&](int kt) __attribute__((always_inline)) {
         const int stage = kt % S;
         const uint32_t sa = lds_addr + stage * Cfg::STAGE_BYTES;
         const uint32_t sb = sa + Cfg::STAGE_A;
         const E* ab = a_tile + static_cast<int64_t>(kt) * Cfg::BK;
         const E* bb = b_tile + static_cast<int64_t>(kt) * Cfg::BK * ldb;
 #pragma unroll
-        for (int q = 0; q < Cfg::A_PER; ++q)
-            if (q >= lo && q < hi) dma16(sa + (wave + q * NW) * 1024, ab, a_voff[q]);
+        for (int q = 0; q < Cfg::A_PER; ++q) dma16(sa + (wave + q * NW) * 1024, ab, a_voff[q]);
 #pragma unroll
-        for (int q = 0; q < Cfg::B_PER; ++q)
-            if (Cfg::A_PER + q >= lo && Cfg::A_PER + q < hi)
-                dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q]);
+        for (int q = 0; q < Cfg::B_PER; ++q) dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q]);
     };
-    auto issue = [&](int kt) __attribute__((always_inline)) { issue_range(kt, 0, NI); };
 
     Acc acc[TM][TN];
 #pragma unroll
@@ -266,14 +260,11 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
             for (int j = 0; j < TN; ++j) Op::run(acc[i][j], f.a[i], f.b[j]);
     };
     // One slab step: LDS reads of the next fragments (load) and this slab's
-    // matrix instructions (f), ordered as the SCHED policy says.  s_setprio is
-    // a scheduling boundary, so it brackets the whole step.
+    // matrix instructions (f), ordered as the SCHED policy says.
     constexpr int kReads = TM + 2 * TN;  // LDS read instructions per slab
     auto slab_step = [&](bool do_load, int lkt, int ls, Frags& fl, const Frags& f) __attribute__((always_inline)) {
-        constexpr bool prio = Cfg::SCHED == 1 || Cfg::SCHED == 3;
-        if constexpr (Cfg::SCHED == 3) __builtin_amdgcn_s_setprio(1);
         if (do_load) load_frags(lkt, ls, fl);
-        if constexpr (Cfg::SCHED == 2 || Cfg::SCHED == 3) {
+        if constexpr (Cfg::SCHED == 2) {
             mma(f);
             // one matrix instruction, then one LDS read, while reads remain
 #pragma unroll
@@ -281,16 +272,14 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - kReads, 0);
+            if constexpr (TM * TN > kReads)
+                __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - kReads, 0);
             __builtin_amdgcn_sched_barrier(0);
         } else {
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (prio) __builtin_amdgcn_s_setprio(1);
             mma(f);
-            if constexpr (prio) __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (Cfg::SCHED == 3) __builtin_amdgcn_s_setprio(0);
     };
 
     const int KT = static_cast<int>(K / Cfg::BK);
@@ -313,15 +302,10 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     static_assert(SLABS % 2 == 0, "fragment ping-pong needs an even slab count");
     Frags F[2];
     load_frags(0, 0, F[0]);
-    constexpr bool spread = (Cfg::FLAGS & 1) && SLABS > 2;
     // All slabs of k-tile kt but the last, each reading the next slab's fragments.
-    auto front_slabs = [&](int kt, bool more) {
+    auto front_slabs = [&](int kt) {
 #pragma unroll
-        for (int s = 0; s + 1 < SLABS; ++s) {
-            if (spread && more)
-                issue_range(kt + S - 1, s * NI / (SLABS - 1), (s + 1) * NI / (SLABS - 1));
-            slab_step(true, kt, s + 1, F[(s + 1) & 1], F[s & 1]);
-        }
+        for (int s = 0; s + 1 < SLABS; ++s) slab_step(true, kt, s + 1, F[(s + 1) & 1], F[s & 1]);
     };
     // Every k-tile but the last ends with the barrier that makes k-tile kt+1
     // visible, then runs its last slab while slab 0 of kt+1 is read.  The last
@@ -329,11 +313,11 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     // predecessor and the compiler's wait counts stay exact there.
     for (int kt = 0; kt + 1 < KT; ++kt) {
         const bool more = kt + S - 1 < KT;
-        if (!early && !spread && more) issue(kt + S - 1);
+        if (!early && more) issue(kt + S - 1);
         // sched_barrier(0) fences keep each slab's prefetch ahead of the
         // previous slab's matrix instructions instead of letting the scheduler
         // sink the LDS reads next to their first use.
-        front_slabs(kt, more && !early);
+        front_slabs(kt);
         // k-tile kt+1 must have landed; later ones (k-tiles up to kt+S-1) may
         // still be in flight.
         if (more)
@@ -347,7 +331,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         slab_step(true, kt + 1, 0, F[0], F[1]);
     }
     if (KT > 0) {
-        front_slabs(KT - 1, false);
+        front_slabs(KT - 1);
         slab_step(false, 0, 0, F[0], F[1]);
     }
 
