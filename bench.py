@@ -57,22 +57,27 @@ def source_hash() -> str:
 class Problem:
     """Device-resident operands of one workload and a launcher for it."""
 
-    def __init__(self, w, variant=-1, config=-1, alpha=1.0, beta=0.0, c_code=0):
+    def __init__(self, w, variant=-1, config=-1, alpha=1.0, beta=0.0, c_code=0, ta=False,
+                 tb=False):
         import torch
         import dense_gemm_16_amd as mg
         from dense_gemm_16_amd import inputs
         self.w, self.mg = w, mg
         self.A, self.B = w.make()
-        self.dA, self.dB = self.A.cuda(), self.B.cuda()
+        # operands given transposed are stored K x M (A) and N x K (B)
+        self.dA = (self.A.t().contiguous() if ta else self.A).cuda()
+        self.dB = (self.B.t().contiguous() if tb else self.B).cuda()
+        lda, ldb = (w.M if ta else w.K), (w.K if tb else w.N)
+        self.ops = (int(ta), int(tb))
         cdt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[c_code]
         self.C = torch.empty((w.M, w.N), dtype=cdt, device="cuda")
         if beta != 0.0:
             self.C.copy_(torch.randn((w.M, w.N), generator=torch.Generator().manual_seed(w.seed + 1)))
         self.epi = (float(alpha), float(beta), c_code)
-        self.general = not (alpha == 1.0 and beta == 0.0 and c_code == 0)
+        self.general = not (alpha == 1.0 and beta == 0.0 and c_code == 0 and not ta and not tb)
         self.code = inputs.DTYPE_CODES[w.dtype]
-        st, v, c = mg.migemm_select(w.M, w.N, w.K, self.code, self.dA.data_ptr(), w.K,
-                                    self.dB.data_ptr(), w.N, self.C.data_ptr(), w.N)
+        st, v, c = mg.migemm_select(w.M, w.N, w.K, self.code, self.dA.data_ptr(), lda,
+                                    self.dB.data_ptr(), ldb, self.C.data_ptr(), w.N)
         if variant < 0:
             self.variant, self.config = v, c
         else:
@@ -80,17 +85,20 @@ class Problem:
             self.config = config if config >= 0 else (c if v == variant else 0)
         self.stream = torch.cuda.current_stream()
         self.sp = self.stream.cuda_stream
-        self.args = (self.variant, self.config, w.M, w.N, w.K, self.code, self.dA.data_ptr(), w.K,
-                     self.dB.data_ptr(), w.N, self.C.data_ptr(), w.N, self.sp)
+        self.args = (self.variant, self.config, w.M, w.N, w.K, self.code, self.dA.data_ptr(), lda,
+                     self.dB.data_ptr(), ldb, self.C.data_ptr(), w.N, self.sp)
 
     def kernel_name(self):
         return (f"{self.mg.migemm_variant_name(self.variant)}["
                 f"{self.mg.migemm_config_name(self.variant, self.config)}]")
 
+    def layout(self):
+        return "".join("T" if t else "N" for t in self.ops)
+
     def launch(self):
         if self.general:
             a = self.args
-            st = self.mg.migemm_gemm_ex_variant(*a[:10], *self.epi, *a[10:])
+            st = self.mg.migemm_gemm_ex_variant(*a[:2], *self.ops, *a[2:10], *self.epi, *a[10:])
         else:
             st = self.mg.migemm_gemm_variant(*self.args)
         if st != self.mg.OK:
@@ -384,6 +392,20 @@ def main():
                                           "kernel": pn.kernel_name()}
                 log(f"extra {name}/naive: {tf:.2f} TFLOPS")
             del px
+        # operands given transposed on the headline shape
+        if w.name == "c4-bf16-8192":
+            for ta, tb in ((False, True), (True, False), (True, True)):
+                px = Problem(w, ta=ta, tb=tb)
+                t, n = px.time_window()
+                tf = w.flop / (t * 1e-3) / 1e12
+                extra[f"{w.name}/{px.layout()}"] = {
+                    "tflops": round(tf, 2), "ms": round(t, 5), "launches": n,
+                    "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
+                    "kernel": px.kernel_name(),
+                    "layout": f"A {'K x M (given transposed)' if ta else 'M x K'}, "
+                              f"B {'N x K (given transposed)' if tb else 'K x N'}"}
+                log(f"extra {w.name} layout {px.layout()}: {tf:.1f} TFLOPS")
+                del px
         # the general output step on the headline shape: scaled update, BF16 C
         if w.name == "c4-bf16-8192":
             px = Problem(w, alpha=0.5, beta=-1.0, c_code=2)

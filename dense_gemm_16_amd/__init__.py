@@ -21,6 +21,7 @@ LIBRARY_PATH = os.path.join(_HERE, "libmigemm.so")
 
 F32, F16, BF16 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+OP_N, OP_T = 0, 1
 VARIANT_AUTO, NAIVE, LDS_TILED, REGTILE_VALU, REGTILE_MFMA, MFMA16 = -1, 0, 1, 2, 3, 4
 
 # Every symbol the header declares (checked by the CPU test suite).
@@ -56,10 +57,11 @@ def lib():
     L.migemm_gemm_variant.argtypes = [i32, i32, i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp]
     L.migemm_gemm_variant.restype = i32
     f32 = ctypes.c_float
-    L.migemm_gemm_ex.argtypes = [i64, i64, i64, i32, vp, i64, vp, i64, f32, f32, i32, vp, i64, vp]
+    L.migemm_gemm_ex.argtypes = [i32, i32, i64, i64, i64, i32, vp, i64, vp, i64, f32, f32, i32,
+                                 vp, i64, vp]
     L.migemm_gemm_ex.restype = i32
-    L.migemm_gemm_ex_variant.argtypes = [i32, i32, i64, i64, i64, i32, vp, i64, vp, i64, f32, f32,
-                                         i32, vp, i64, vp]
+    L.migemm_gemm_ex_variant.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, vp, i64, vp, i64,
+                                         f32, f32, i32, vp, i64, vp]
     L.migemm_gemm_ex_variant.restype = i32
     L.migemm_variant_count.argtypes = []
     L.migemm_variant_count.restype = i32
@@ -96,16 +98,16 @@ def migemm_gemm_variant(variant, config, M, N, K, dtype, A, lda, B, ldb, C, ldc,
                                      stream)
 
 
-def migemm_gemm_ex(M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype, C, ldc,
+def migemm_gemm_ex(op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype, C, ldc,
                    stream=None) -> int:
-    return lib().migemm_gemm_ex(M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype, C, ldc,
-                                stream)
+    return lib().migemm_gemm_ex(op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha, beta,
+                                c_dtype, C, ldc, stream)
 
 
-def migemm_gemm_ex_variant(variant, config, M, N, K, dtype, A, lda, B, ldb, alpha, beta,
-                           c_dtype, C, ldc, stream=None) -> int:
-    return lib().migemm_gemm_ex_variant(variant, config, M, N, K, dtype, A, lda, B, ldb, alpha,
-                                        beta, c_dtype, C, ldc, stream)
+def migemm_gemm_ex_variant(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha,
+                           beta, c_dtype, C, ldc, stream=None) -> int:
+    return lib().migemm_gemm_ex_variant(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B,
+                                        ldb, alpha, beta, c_dtype, C, ldc, stream)
 
 
 def migemm_variant_count() -> int:
@@ -168,12 +170,27 @@ def _ld(t) -> int:
     return max(1, t.stride(0) if t.shape[0] > 1 else t.shape[1])
 
 
+def _operand(t):
+    """(op, ld) of a 2-D operand: row-major (unit column stride) is OP_N with
+    ld = stride(0); a transposed view (unit row stride) is OP_T with ld = stride(1)."""
+    if t.dim() != 2:
+        raise ValueError("operands must be 2-D")
+    rows, cols = t.shape
+    if cols <= 1 or t.stride(1) == 1:
+        return OP_N, max(1, t.stride(0) if rows > 1 else cols)
+    if rows <= 1 or t.stride(0) == 1:
+        return OP_T, max(1, t.stride(1) if cols > 1 else rows)
+    raise ValueError("operands must be row-major or transposed views of row-major storage")
+
+
 def gemm(a, b, out=None, *, alpha: float = 1.0, beta: float = 0.0, out_dtype=None,
          variant: int = VARIANT_AUTO, config: int = -1, stream=None):
-    """out = alpha * (A x B) + beta * out on the GPU for row-major torch tensors.
+    """out = alpha * (A x B) + beta * out on the GPU for torch tensors.
 
     ``a`` (M x K) and ``b`` (K x N) are CUDA tensors of the same dtype
-    (float32, float16 or bfloat16) with unit inner stride.  ``out`` (M x N) may
+    (float32, float16 or bfloat16), each row-major or a transposed view of
+    row-major storage (``x.t()``, or a column-major tensor), passed as stored:
+    no copy is made.  ``out`` (M x N, row-major) may
     be float32, float16 or bfloat16; if not given it is allocated with
     ``out_dtype`` (default float32), which beta == 0 requires.  With alpha = 1,
     beta = 0 and a float32 ``out`` this is migemm_gemm_variant, otherwise
@@ -200,12 +217,13 @@ def gemm(a, b, out=None, *, alpha: float = 1.0, beta: float = 0.0, out_dtype=Non
     if stream is None:
         stream = torch.cuda.current_stream(a.device).cuda_stream
     pa, pb, pc = a.data_ptr() or None, b.data_ptr() or None, out.data_ptr() or None
-    if alpha == 1.0 and beta == 0.0 and cd == F32:
-        st = migemm_gemm_variant(variant, config, M, N, K, dt, pa, _ld(a), pb, _ld(b), pc,
-                                 _ld(out), stream)
+    (op_a, lda), (op_b, ldb) = _operand(a), _operand(b)
+    if alpha == 1.0 and beta == 0.0 and cd == F32 and op_a == OP_N and op_b == OP_N:
+        st = migemm_gemm_variant(variant, config, M, N, K, dt, pa, lda, pb, ldb, pc, _ld(out),
+                                 stream)
         where = "migemm_gemm_variant"
     else:
-        st = migemm_gemm_ex_variant(variant, config, M, N, K, dt, pa, _ld(a), pb, _ld(b),
+        st = migemm_gemm_ex_variant(variant, config, op_a, op_b, M, N, K, dt, pa, lda, pb, ldb,
                                     float(alpha), float(beta), cd, pc, _ld(out), stream)
         where = "migemm_gemm_ex_variant"
     if st != OK:

@@ -53,13 +53,18 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a
 
 bool known_dtype(int d) { return d == MIGEMM_F32 || d == MIGEMM_F16 || d == MIGEMM_BF16; }
 
-int check_args(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
-               const void* B, int64_t ldb, const void* C, int64_t ldc, int c_dtype,
+bool known_op(int op) { return op == MIGEMM_OP_N || op == MIGEMM_OP_T; }
+
+// ta / tb: the operand is given transposed, so its stored rows run along k (A,
+// stored K x M) or along n (B, stored N x K).
+int check_args(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, const void* A,
+               int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, int c_dtype,
                bool need_ptrs) {
     if (!known_dtype(dtype) || !known_dtype(c_dtype)) return MIGEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return MIGEMM_ERR_INVALID_ARG;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    auto at_least = [](int64_t ld, int64_t cols) { return ld >= (cols > 1 ? cols : 1); };
+    if (!at_least(lda, ta ? M : K) || !at_least(ldb, tb ? K : N) || !at_least(ldc, N))
         return MIGEMM_ERR_INVALID_ARG;
     if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return MIGEMM_ERR_INVALID_ARG;
     if (!need_ptrs) return MIGEMM_OK;
@@ -71,8 +76,14 @@ int check_args(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_
         extent(C, M, N, ldc, elem_size(c_dtype), c0, c1);
         if (K > 0) {
             uintptr_t a0, a1, b0, b1;
-            extent(A, M, K, lda, es, a0, a1);
-            extent(B, K, N, ldb, es, b0, b1);
+            if (ta)
+                extent(A, K, M, lda, es, a0, a1);
+            else
+                extent(A, M, K, lda, es, a0, a1);
+            if (tb)
+                extent(B, N, K, ldb, es, b0, b1);
+            else
+                extent(B, K, N, ldb, es, b0, b1);
             if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return MIGEMM_ERR_INVALID_ARG;
         }
     }
@@ -85,11 +96,11 @@ bool operands_aligned(const void* A, int64_t lda, const void* B, int64_t ldb) {
     return aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
 }
 
-// The selection table: a pure function of shape, dtype and alignment.
-// Sizes are bucketed by how many workgroup tiles a configuration would launch
-// against the 256 CUs of an MI355X.
-void select(int64_t M, int64_t N, int64_t K, int dtype, bool aligned, int& variant,
-            int& config) {
+// The selection table: a pure function of shape, dtype, operand layout and
+// alignment.  Sizes are bucketed by how many workgroup tiles a configuration
+// would launch against the 256 CUs of an MI355X.
+void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool aligned,
+            int& variant, int& config) {
     auto tiles = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
     if (dtype == MIGEMM_F32) {
         variant = MIGEMM_REGTILE_MFMA;
@@ -98,9 +109,10 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool aligned, int& varia
     }
     variant = MIGEMM_MFMA16;
     // Direct global->LDS staging needs 16-byte aligned operands with leading
-    // dimensions a multiple of 8 elements, K a multiple of 64 and N a multiple
-    // of 8 (the launcher falls back to the register-staged kernel otherwise).
-    const bool direct = aligned && K % 64 == 0 && N % 8 == 0 && N >= 8;
+    // dimensions a multiple of 8 elements, K a multiple of 64, and N (row-major
+    // B) or M (A given transposed) a multiple of 8; the launcher falls back to
+    // the register-staged kernel otherwise.
+    const bool direct = aligned && K % 64 == 0 && (tb || N % 8 == 0) && (!ta || M % 8 == 0);
     if (direct && tiles(256, 256) >= 256)
         config = 10;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads
     else if (direct)
@@ -111,28 +123,31 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool aligned, int& varia
         config = 3;   // register-staged 64x64x64
 }
 
-int run(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype, const void* A,
-        int64_t lda, const void* B, int64_t ldb, float alpha, float beta, int c_dtype, void* C,
-        int64_t ldc, void* stream) {
-    int st = check_args(M, N, K, dtype, A, lda, B, ldb, C, ldc, c_dtype, true);
+int run(int variant, int config, int op_a, int op_b, int64_t M, int64_t N, int64_t K,
+        int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, float alpha,
+        float beta, int c_dtype, void* C, int64_t ldc, void* stream) {
+    if (!known_op(op_a) || !known_op(op_b)) return MIGEMM_ERR_INVALID_ARG;
+    const bool ta = op_a == MIGEMM_OP_T, tb = op_b == MIGEMM_OP_T;
+    int st = check_args(M, N, K, dtype, ta, tb, A, lda, B, ldb, C, ldc, c_dtype, true);
     if (st != MIGEMM_OK) return st;
+    const bool aligned = operands_aligned(A, lda, B, ldb);
     if (variant == MIGEMM_VARIANT_AUTO) {
         if (config != -1) return MIGEMM_ERR_INVALID_ARG;
-        select(M, N, K, dtype, operands_aligned(A, lda, B, ldb), variant, config);
+        select(M, N, K, dtype, ta, tb, aligned, variant, config);
     }
     if (variant < 0 || variant >= kNumVariants) return MIGEMM_ERR_INVALID_ARG;
     const Variant& v = kVariants[variant];
     if (!(v.dtype_mask & (1u << dtype))) return MIGEMM_ERR_UNSUPPORTED;
     if (config == -1) {
         int sv, sc;
-        select(M, N, K, dtype, operands_aligned(A, lda, B, ldb), sv, sc);
+        select(M, N, K, dtype, ta, tb, aligned, sv, sc);
         config = (sv == variant) ? sc : 0;
     }
     if (config < 0 || config >= v.count()) return MIGEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return MIGEMM_OK;
 
-    const GemmArgs g{M, N, K, dtype, A, lda, B, ldb, Epi{C, ldc, alpha, beta, c_dtype},
-                     static_cast<hipStream_t>(stream)};
+    const GemmArgs g{M,   N,   K, dtype, ta, tb, A, lda, B, ldb,
+                     Epi{C, ldc, alpha, beta, c_dtype}, static_cast<hipStream_t>(stream)};
     const hipError_t err = K == 0 ? launch_empty_product(g) : v.launch(g, config);
     if (err != hipSuccess) {
         g_last_hip_error = static_cast<int>(err);
@@ -150,29 +165,30 @@ extern "C" {
 
 int migemm_gemm(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
                 const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-    return run(MIGEMM_VARIANT_AUTO, -1, M, N, K, dtype, A, lda, B, ldb, 1.0f, 0.0f, MIGEMM_F32,
-               C, ldc, stream);
+    return run(MIGEMM_VARIANT_AUTO, -1, MIGEMM_OP_N, MIGEMM_OP_N, M, N, K, dtype, A, lda, B, ldb,
+               1.0f, 0.0f, MIGEMM_F32, C, ldc, stream);
 }
 
 int migemm_gemm_variant(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype,
                         const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
                         int64_t ldc, void* stream) {
-    return run(variant, config, M, N, K, dtype, A, lda, B, ldb, 1.0f, 0.0f, MIGEMM_F32, C, ldc,
-               stream);
+    return run(variant, config, MIGEMM_OP_N, MIGEMM_OP_N, M, N, K, dtype, A, lda, B, ldb, 1.0f,
+               0.0f, MIGEMM_F32, C, ldc, stream);
 }
 
-int migemm_gemm_ex(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
-                   const void* B, int64_t ldb, float alpha, float beta, int c_dtype, void* C,
-                   int64_t ldc, void* stream) {
-    return run(MIGEMM_VARIANT_AUTO, -1, M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype, C,
-               ldc, stream);
+int migemm_gemm_ex(int op_a, int op_b, int64_t M, int64_t N, int64_t K, int dtype, const void* A,
+                   int64_t lda, const void* B, int64_t ldb, float alpha, float beta, int c_dtype,
+                   void* C, int64_t ldc, void* stream) {
+    return run(MIGEMM_VARIANT_AUTO, -1, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha, beta,
+               c_dtype, C, ldc, stream);
 }
 
-int migemm_gemm_ex_variant(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype,
-                           const void* A, int64_t lda, const void* B, int64_t ldb, float alpha,
-                           float beta, int c_dtype, void* C, int64_t ldc, void* stream) {
-    return run(variant, config, M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype, C, ldc,
-               stream);
+int migemm_gemm_ex_variant(int variant, int config, int op_a, int op_b, int64_t M, int64_t N,
+                           int64_t K, int dtype, const void* A, int64_t lda, const void* B,
+                           int64_t ldb, float alpha, float beta, int c_dtype, void* C,
+                           int64_t ldc, void* stream) {
+    return run(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype,
+               C, ldc, stream);
 }
 
 int migemm_variant_count(void) { return kNumVariants; }
@@ -201,10 +217,10 @@ int migemm_select(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int
     (void)A;
     (void)B;
     (void)C;
-    int st = check_args(M, N, K, dtype, A, lda, B, ldb, C, ldc, MIGEMM_F32, false);
+    int st = check_args(M, N, K, dtype, false, false, A, lda, B, ldb, C, ldc, MIGEMM_F32, false);
     if (st != MIGEMM_OK) return st;
     if (!variant || !config) return MIGEMM_ERR_INVALID_ARG;
-    select(M, N, K, dtype, operands_aligned(A, lda, B, ldb), *variant, *config);
+    select(M, N, K, dtype, false, false, operands_aligned(A, lda, B, ldb), *variant, *config);
     return MIGEMM_OK;
 }
 
@@ -220,6 +236,6 @@ const char* migemm_status_string(int status) {
 
 int migemm_last_hip_error(void) { return g_last_hip_error; }
 
-int migemm_version(void) { return 200; }
+int migemm_version(void) { return 300; }
 
 }  // extern "C"

@@ -21,10 +21,13 @@ struct Epi {
     int c_dtype;  // 0 FP32, 1 FP16, 2 BF16
 };
 
-// Arguments of one product, already validated by the C ABI.
+// Arguments of one product, already validated by the C ABI.  ta: A is given
+// transposed, stored K x M (element (i, k) at A[k * lda + i]); tb: B is given
+// transposed, stored N x K (element (k, j) at B[j * ldb + k]).
 struct GemmArgs {
     int64_t M, N, K;
     int dtype;
+    bool ta, tb;
     const void* A;
     int64_t lda;
     const void* B;

@@ -20,19 +20,21 @@ template <typename E> struct Cfgs {
     using D5 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64>;
     using D6 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64>;
     using D7 = DirectCfg<E, 128, 128, 2, 2, 16, 2, 64>;
-    using D8 = DirectCfg<E, 128, 128, 2, 2, 16, 4, 64>;             // 4 stages
+    using D8 = DirectCfg<E, 128, 128, 2, 2, 16, 4, 64, 8, 0, 16>;   // 4 stages; all layouts
     using D9 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 2>;    // gm4, interleave, nt C
-    using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 14>;  // + AGPRs, early loads
+    using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 30>;  // + AGPRs, early loads; all layouts
 };
 
 template <class D, class Fallback, bool GEN>
 hipError_t direct_or(const GemmArgs& g) {
-    return direct_ok(g, D::BK) ? launch_direct_cfg<D, GEN>(g) : launch_mfma_cfg<Fallback, GEN>(g);
+    return direct_ok(g, D::BK, D::LAYOUTS) ? launch_direct_cfg<D, GEN>(g)
+                                           : launch_mfma_cfg<Fallback, GEN>(g);
 }
 
 // Configuration `config` of the table (indices as named in mfma16.hip).  A
-// direct-staged configuration whose preconditions do not hold runs the
-// register-staged one with the same or the nearest tile.
+// direct-staged configuration whose preconditions do not hold (or that is not
+// compiled for the operands' layout) runs the register-staged one with the same
+// or the nearest tile.
 template <typename E, bool GEN>
 hipError_t launch_typed(const GemmArgs& g, int config) {
     using T = Cfgs<E>;

@@ -44,11 +44,19 @@
 // offset, so the per-lane offsets are computed once and no 64-bit addresses
 // occupy VGPRs.
 //
+// Operands given transposed swap image kinds: A stored K x M (m contiguous)
+// becomes a k-row image like B's and is read with transposing reads; B stored
+// N x K (k contiguous) becomes a row image like A's and is read with
+// ds_read_b128.  Both reads hand a lane the same fragment (a run of 8 k of one
+// row of A or column of B), so the matrix instructions do not change.
+//
 // Preconditions (checked by the launcher; other shapes use mfma_gemm.hpp):
 // A and B 16-byte aligned, lda and ldb multiples of 8 elements, K a multiple
-// of 64, N a multiple of 8.  Rows of A past M and columns of B past N are
-// clamped to the last valid row / chunk, so every load is in bounds; those
-// lanes only feed outputs that are never stored.
+// of 64, and the side of a k-row image (N for row-major B, M for A given
+// transposed) a multiple of 8.  Rows of a row image past M or N, and chunks
+// of a k-row image past its side, are clamped to the last valid row / chunk,
+// so every load is in bounds; those lanes only feed outputs that are never
+// stored.
 #pragma once
 
 #include "mfma_gemm.hpp"
@@ -63,7 +71,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // FLAGS: bit 1 = non-temporal C stores; bit 2 = keep the accumulators in AGPRs
 // (see below); bit 3 = issue a k-tile's direct loads right after the barrier
 // that frees their stage instead of at the start of the next k-tile, so they
-// have a whole k-tile of matrix work to land.
+// have a whole k-tile of matrix work to land; bit 4 = also compiled for
+// operands given transposed (without it those run the register-staged kernel).
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
           int BK_ = 64, int GM_ = 8, int SCHED_ = 0, int FLAGS_ = 0>
 struct DirectCfg {
@@ -71,29 +80,36 @@ struct DirectCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_, GM = GM_;
     static constexpr int STAGES = STAGES_, BK = BK_, SCHED = SCHED_, FLAGS = FLAGS_;
     static constexpr int NW = WM * WN, NT = NW * kWave;
-    static constexpr int CA = BK / 8;                   // 16-byte chunks per row of A
-    static constexpr int BCH = BN / 8;                  // 16-byte chunks per k-row of B
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
     static constexpr int TM = WTM / MF, TN = WTN / MF;
-    static constexpr int A_RPI = 64 / CA;               // rows of A per direct load (64 chunks)
-    static constexpr int B_RPI = 64 / BCH;              // k-rows of B per direct load
-    static constexpr int A_INSTR = BM / A_RPI, B_INSTR = BK / B_RPI;
-    static constexpr int A_PER = A_INSTR / NW, B_PER = B_INSTR / NW;
-    static constexpr int NI = A_PER + B_PER;  // direct loads per wave per k-tile
     static constexpr int STAGE_A = BM * BK * 2, STAGE_B = BK * BN * 2;
     static constexpr int STAGE_BYTES = STAGE_A + STAGE_B;
+    static constexpr bool LAYOUTS = (FLAGS & 16) != 0;
     static_assert(sizeof(E) == 2, "16-bit inputs only");
-    static_assert(BK == 32 || BK == 64, "A rows are 64 or 128 bytes");
-    static_assert(BN >= 128 && BN <= 512, "the B swizzle needs 16 to 64 chunks per k-row");
-    static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "loads split evenly over waves");
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "whole blocks per wave");
     static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "stages fit 160 KiB");
-    static_assert((STAGES - 2) * NI <= 63, "vmcnt counts at most 63 loads");
     static_assert(SCHED == 0 || SCHED == 2, "scheduling policy 0 or 2");
-    static_assert((FLAGS & ~14) == 0, "flags: bits 1, 2 and 3");
+    static_assert((FLAGS & ~30) == 0, "flags: bits 1 to 4");
 };
 
-// Physical chunk of logical chunk c in row `row` of the A image (CA chunks per row).
+// One operand's LDS image (BX rows of M or N by BK of k, 16-bit elements).
+// KROW: [BX rows][BK / 8 chunks], k contiguous (row-major A, or B given
+// transposed).  Otherwise a k-row image [BK k-rows][BX / 8 chunks], the BX side
+// contiguous (row-major B, or A given transposed).  A direct load fills 64
+// chunks: RPI image rows.
+template <int BX, int BK, int NW, bool KROW>
+struct DirectOperand {
+    static constexpr bool ROWS = KROW;
+    static constexpr int CH = KROW ? BK / 8 : BX / 8;  // 16-byte chunks per image row
+    static constexpr int RPI = 64 / CH;
+    static constexpr int INSTR = (KROW ? BX : BK) / RPI;
+    static constexpr int PER = INSTR / NW;             // direct loads per wave per k-tile
+    static_assert(!KROW || BK == 32 || BK == 64, "row images are 64 or 128 bytes wide");
+    static_assert(KROW || (BX >= 128 && BX <= 512), "the k-row swizzle needs 16 to 64 chunks");
+    static_assert(INSTR % NW == 0, "loads split evenly over waves");
+};
+
+// Physical chunk of logical chunk c in row `row` of a row image (CA chunks per row).
 // 128-byte rows (two rows per 256 bytes of banks): c ^ ((row >> 1) & 7).  64-byte
 // rows (four rows per 256 bytes): c ^ ((row >> 2) & 3).  Either way sixteen
 // consecutive rows reading one logical chunk cover the 64 banks once, and the
@@ -103,7 +119,30 @@ __device__ __forceinline__ int swz_a(int row) {
     if constexpr (CA == 8) return (row >> 1) & 7;
     return (row >> 2) & 3;
 }
+// Physical chunk of logical chunk c in k-row `krow` of a k-row image: c ^ swz_b(krow).
 __device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) | ((krow >> 1) & 4)) << 1; }
+
+// Per-lane byte offsets of a wave's direct loads of one operand O, relative to
+// its tile origin (row image: P + x0 * ld + k0; k-row image: P + k0 * ld + x0).
+// Rows past the operand's extent `ext` (row image) and chunks past it (k-row
+// image) are clamped, keeping every load in bounds.
+template <class O>
+__device__ __forceinline__ void direct_offsets(uint32_t (&voff)[O::PER], int wave, int lane, int nw,
+                                               int64_t x0, int64_t ext, int64_t ld) {
+#pragma unroll
+    for (int q = 0; q < O::PER; ++q) {
+        const int r = O::RPI * (wave + q * nw) + lane / O::CH;
+        if constexpr (O::ROWS) {
+            const int chunk = (lane % O::CH) ^ swz_a<O::CH>(r);
+            const int64_t gr = min(x0 + r, ext - 1);
+            voff[q] = static_cast<uint32_t>(((gr - x0) * ld + chunk * 8) * 2);
+        } else {
+            const int chunk = (lane % O::CH) ^ swz_b(r);
+            const int64_t gc = min(x0 + chunk * 8, ext - 8);
+            voff[q] = static_cast<uint32_t>((r * ld + (gc - x0)) * 2);
+        }
+    }
+}
 
 // 16 bytes per lane from global memory (SGPR base + per-lane byte offset) into
 // LDS at lds_base + 16 * lane.  M0 carries the LDS base; nothing else in these
@@ -136,13 +175,18 @@ __device__ __forceinline__ void wait_then_barrier() {
     asm volatile("" : : : "memory");
 }
 
-template <class Cfg, bool GEN>
+// TA: A given transposed (stored K x M); TB: B given transposed (stored N x K).
+template <class Cfg, bool GEN, bool TA, bool TB>
 __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     int64_t M, int64_t N, int64_t K, const typename Cfg::E* __restrict__ A, int64_t lda,
     const typename Cfg::E* __restrict__ B, int64_t ldb, Epi out, int tiles_m, int tiles_n) {
     using E = typename Cfg::E;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, MF = Cfg::MF, TM = Cfg::TM, TN = Cfg::TN;
-    constexpr int NW = Cfg::NW, BCH = Cfg::BCH, S = Cfg::STAGES, NI = Cfg::NI, CA = Cfg::CA;
+    constexpr int NW = Cfg::NW, S = Cfg::STAGES, BK = Cfg::BK;
+    using OA = DirectOperand<BM, BK, NW, !TA>;
+    using OB = DirectOperand<BN, BK, NW, TB>;
+    constexpr int NI = OA::PER + OB::PER;  // direct loads per wave per k-tile
+    static_assert((S - 2) * NI <= 63, "vmcnt counts at most 63 loads");
     using Op = MfmaOp<E, MF>;
     using Acc = typename Op::Acc;
     using L = AccLayout<MF>;
@@ -162,38 +206,26 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     const int64_t m0 = static_cast<int64_t>(pm) * BM;
     const int64_t n0 = static_cast<int64_t>(pn) * BN;
 
-    // Per-lane byte offsets of this wave's direct loads, relative to the tile
-    // origin (A + m0 * lda + k0, B + k0 * ldb + n0).  Rows of A past M and
-    // chunks of B past N are clamped, keeping every load in bounds.
-    uint32_t a_voff[Cfg::A_PER], b_voff[Cfg::B_PER];
-#pragma unroll
-    for (int q = 0; q < Cfg::A_PER; ++q) {
-        const int row = Cfg::A_RPI * (wave + q * NW) + lane / CA;
-        const int chunk = (lane % CA) ^ swz_a<CA>(row);
-        const int64_t grow = min(m0 + row, M - 1);
-        a_voff[q] = static_cast<uint32_t>(((grow - m0) * lda + chunk * 8) * 2);
-    }
-#pragma unroll
-    for (int q = 0; q < Cfg::B_PER; ++q) {
-        const int krow = (wave + q * NW) * Cfg::B_RPI + lane / BCH;
-        const int chunk = (lane % BCH) ^ swz_b(krow);
-        const int64_t gcol = min(n0 + chunk * 8, N - 8);
-        b_voff[q] = static_cast<uint32_t>((krow * ldb + (gcol - n0)) * 2);
-    }
-    const E* const a_tile = A + m0 * lda;
-    const E* const b_tile = B + n0;
+    uint32_t a_voff[OA::PER], b_voff[OB::PER];
+    direct_offsets<OA>(a_voff, wave, lane, NW, m0, M, lda);
+    direct_offsets<OB>(b_voff, wave, lane, NW, n0, N, ldb);
+    // tile origins and the step from one k-tile to the next, in elements
+    const E* const a_tile = TA ? A + m0 : A + m0 * lda;
+    const E* const b_tile = TB ? B + n0 * ldb : B + n0;
+    const int64_t a_step = TA ? BK * lda : BK;
+    const int64_t b_step = TB ? BK : BK * ldb;
 
     // Issues this wave's NI direct loads of k-tile kt (A's, then B's) into its stage.
     auto issue = [&](int kt) __attribute__((always_inline)) {
         const int stage = kt % S;
         const uint32_t sa = lds_addr + stage * Cfg::STAGE_BYTES;
         const uint32_t sb = sa + Cfg::STAGE_A;
-        const E* ab = a_tile + static_cast<int64_t>(kt) * Cfg::BK;
-        const E* bb = b_tile + static_cast<int64_t>(kt) * Cfg::BK * ldb;
+        const E* ab = a_tile + static_cast<int64_t>(kt) * a_step;
+        const E* bb = b_tile + static_cast<int64_t>(kt) * b_step;
 #pragma unroll
-        for (int q = 0; q < Cfg::A_PER; ++q) dma16(sa + (wave + q * NW) * 1024, ab, a_voff[q]);
+        for (int q = 0; q < OA::PER; ++q) dma16(sa + (wave + q * NW) * 1024, ab, a_voff[q]);
 #pragma unroll
-        for (int q = 0; q < Cfg::B_PER; ++q) dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q]);
+        for (int q = 0; q < OB::PER; ++q) dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q]);
     };
 
     Acc acc[TM][TN];
@@ -211,15 +243,41 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         asm volatile("" : "+a"(agpr_hint));
     }
 
-    // Fragment addressing.  MF = 16: lane (r + 16 g) feeds row r of a block and
-    // k = 8 g .. 8 g + 7 of a 32-k slab.  MF = 32: lane (r + 32 g), k = 8 g .. of
-    // a 16-k slab.  For B, lane j of each 16-lane group receives column j.
+    // Fragment addressing.  MF = 16: lane (r + 16 g) feeds row r of a block (of A,
+    // or column r of B) and k = 8 g .. 8 g + 7 of a 32-k slab.  MF = 32: lane
+    // (r + 32 g), k = 8 g .. of a 16-k slab.  From a row image that is one 16-byte
+    // read; from a k-row image two transposing reads, arranged so that lane j of
+    // each 16-lane group receives column j of four k-rows each time.
     constexpr int G = kWave / MF;          // k-groups per slab
     constexpr int SLAB_K = 8 * G;          // k per slab: 32 (MF 16) or 16 (MF 32)
-    constexpr int SLABS = Cfg::BK / SLAB_K;
+    constexpr int SLABS = BK / SLAB_K;
     const int ar = lane % MF, ag = lane / MF;
     const int bj = lane % 16;
     const int bcol = (MF == 16 ? 0 : 16 * ((lane % 32) / 16)) + 4 * (bj % 4);
+
+    // Fragment `t` (block t of the wave tile starting at w0) of slab s from the
+    // image `img` of a BX-wide operand.
+    auto read_row_image = [&](const MIGEMM_LDS char* img, int w0, int t, int s)
+        __attribute__((always_inline)) {
+        constexpr int CA = BK / 8;
+        const int row = w0 + t * MF + ar;
+        const int chunk = (s * G + ag) ^ swz_a<CA>(row);
+        return *(const MIGEMM_LDS u32x4*)(img + row * (CA * 16) + chunk * 16);
+    };
+    auto read_krow_image = [&](const MIGEMM_LDS char* img, int bx, int w0, int t, int s)
+        __attribute__((always_inline)) {
+        const int col = w0 + t * MF + bcol;
+        u32x2 h[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int krow = s * SLAB_K + 8 * ag + 4 * half + bj / 4;
+            const int chunk = (col / 8) ^ swz_b(krow);
+            const MIGEMM_LDS char* p = img + krow * (bx * 2) + chunk * 16 + (col % 8) * 2;
+            h[half] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS s16x4*)p));
+        }
+        return u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+    };
 
     struct Frags {
         u32x4 a[TM];
@@ -228,28 +286,17 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     auto load_frags = [&](int kt, int s, Frags& f) __attribute__((always_inline)) {
         const MIGEMM_LDS char* sa = lds + (kt % S) * Cfg::STAGE_BYTES;
         const MIGEMM_LDS char* sb = sa + Cfg::STAGE_A;
+        auto read_a = [&](int i) __attribute__((always_inline)) {
+            f.a[i] = TA ? read_krow_image(sa, BM, wm0, i, s) : read_row_image(sa, wm0, i, s);
+        };
+        auto read_b = [&](int j) __attribute__((always_inline)) {
+            f.b[j] = TB ? read_row_image(sb, wn0, j, s) : read_krow_image(sb, BN, wn0, j, s);
+        };
         // Issued in the order the matrix instructions consume them (i-major):
         // a[0], then every b[j], then a[1] ...
-        auto read_a = [&](int i) {
-            const int row = wm0 + i * MF + ar;
-            const int chunk = (s * G + ag) ^ swz_a<CA>(row);
-            f.a[i] = *(const MIGEMM_LDS u32x4*)(sa + row * (CA * 16) + chunk * 16);
-        };
         read_a(0);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = wn0 + j * MF + bcol;
-            u32x2 h[2];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int krow = s * SLAB_K + 8 * ag + 4 * half + bj / 4;
-                const int chunk = (col / 8) ^ swz_b(krow);
-                const MIGEMM_LDS char* p = sb + krow * (BN * 2) + chunk * 16 + (col % 8) * 2;
-                h[half] = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS s16x4*)p));
-            }
-            f.b[j] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
-        }
+        for (int j = 0; j < TN; ++j) read_b(j);
 #pragma unroll
         for (int i = 1; i < TM; ++i) read_a(i);
     };
@@ -261,7 +308,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     };
     // One slab step: LDS reads of the next fragments (load) and this slab's
     // matrix instructions (f), ordered as the SCHED policy says.
-    constexpr int kReads = TM + 2 * TN;  // LDS read instructions per slab
+    constexpr int kReads = (TA ? 2 : 1) * TM + (TB ? 1 : 2) * TN;  // LDS read instructions per slab
     auto slab_step = [&](bool do_load, int lkt, int ls, Frags& fl, const Frags& f) __attribute__((always_inline)) {
         if (do_load) load_frags(lkt, ls, fl);
         if constexpr (Cfg::SCHED == 2) {
@@ -282,7 +329,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         }
     };
 
-    const int KT = static_cast<int>(K / Cfg::BK);
+    const int KT = static_cast<int>(K / BK);
     // Prologue: k-tiles 0 .. S-2 in flight (0 .. S-1 with early loads, which
     // refill a stage right after the barrier that frees it); wait for k-tile 0.
     constexpr bool early = (Cfg::FLAGS & 8) != 0;
@@ -386,12 +433,18 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 }
 
 // True when the direct kernel's preconditions hold for these arguments: aligned
-// operands, whole 16-byte chunks, K a multiple of the k-tile (bk), and per-lane
-// offsets (256 rows of A, 64 rows of B) that fit 31 bits.
-inline bool direct_ok(const GemmArgs& g, int bk = 64) {
+// operands in whole 16-byte chunks per row, K a multiple of the k-tile (bk),
+// the side of a k-row image (N for row-major B, M for A given transposed) in
+// whole chunks, and per-lane offsets (BX <= 256 rows of a row image, 64 k-rows of
+// a k-row image) that fit 31 bits.  `layouts`: the configuration is compiled for
+// operands given transposed.
+inline bool direct_ok(const GemmArgs& g, int bk, bool layouts) {
+    if ((g.ta || g.tb) && !layouts) return false;
+    const int64_t row_ld = int64_t(1) << 21, krow_ld = int64_t(1) << 23;
     return aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
-           g.K % bk == 0 && g.N % 8 == 0 && g.K > 0 && g.M > 0 && g.N >= 8 &&
-           g.lda < (int64_t(1) << 21) && g.ldb < (int64_t(1) << 23);
+           g.K % bk == 0 && g.K > 0 && g.M > 0 && g.N > 0 &&
+           (g.ta ? (g.M % 8 == 0 && g.lda < krow_ld) : g.lda < row_ld) &&
+           (g.tb ? g.ldb < row_ld : (g.N % 8 == 0 && g.ldb < krow_ld));
 }
 
 template <class Cfg, bool GEN>
@@ -399,11 +452,27 @@ hipError_t launch_direct_cfg(const GemmArgs& g) {
     using E = typename Cfg::E;
     const int64_t tm = ceil_div(g.M, Cfg::BM), tn = ceil_div(g.N, Cfg::BN);
     if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-    mfma16_direct_kernel<Cfg, GEN><<<dim3(static_cast<unsigned>(tm * tn)), dim3(Cfg::NT), 0,
-                                      g.stream>>>(g.M, g.N, g.K, static_cast<const E*>(g.A),
-                                                  g.lda, static_cast<const E*>(g.B), g.ldb,
-                                                  g.out, static_cast<int>(tm),
-                                                  static_cast<int>(tn));
+    const dim3 grid(static_cast<unsigned>(tm * tn)), block(Cfg::NT);
+    const E* A = static_cast<const E*>(g.A);
+    const E* B = static_cast<const E*>(g.B);
+    const int itm = static_cast<int>(tm), itn = static_cast<int>(tn);
+#define MIGEMM_LAUNCH(TA_, TB_)                                                                \
+    mfma16_direct_kernel<Cfg, GEN, TA_, TB_><<<grid, block, 0, g.stream>>>(                    \
+        g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn)
+    if constexpr (Cfg::LAYOUTS) {
+        if (g.ta && g.tb)
+            MIGEMM_LAUNCH(true, true);
+        else if (g.ta)
+            MIGEMM_LAUNCH(true, false);
+        else if (g.tb)
+            MIGEMM_LAUNCH(false, true);
+        else
+            MIGEMM_LAUNCH(false, false);
+    } else {
+        if (g.ta || g.tb) return hipErrorInvalidValue;  // direct_ok sends these elsewhere
+        MIGEMM_LAUNCH(false, false);
+    }
+#undef MIGEMM_LAUNCH
     return hipGetLastError();
 }
 

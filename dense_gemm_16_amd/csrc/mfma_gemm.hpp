@@ -19,12 +19,13 @@
 //   the other half of a double-buffered LDS tile afterwards: one barrier per
 //   k-tile.
 // * Operand layout.  A matrix-core instruction wants, in every lane, a run of
-//   consecutive k for one row of A and for one column of B.  Row-major A
-//   already has k contiguous.  Row-major B has n contiguous, so each work-item
-//   loads a VEC x VEC block of B (VEC rows of k, one 16-byte chunk of columns)
-//   and transposes it in registers before the LDS write; in LDS both operands
-//   are stored as [row][k] with 16-byte chunks, and every fragment read is one
-//   16-byte LDS read per lane.
+//   consecutive k for one row of A and for one column of B.  An operand stored
+//   with k contiguous (row-major A, or B given transposed) is copied in 16-byte
+//   chunks along k.  One stored with its M or N side contiguous (row-major B, or
+//   A given transposed) is loaded in VEC x VEC blocks (VEC rows of k, one
+//   16-byte chunk across) and transposed in registers before the LDS write.
+//   Either way both operands sit in LDS as [row][k] with 16-byte chunks, and
+//   every fragment read is one 16-byte LDS read per lane.
 // * Bank conflicts.  Rows are 128 bytes long, so without care every row of a
 //   fragment read would hit the same banks.  The chunk index is XOR-swizzled
 //   with (row ^ (row >> 3)) & 7: sixteen consecutive rows reading the same
@@ -196,6 +197,66 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
     pn = in / gm;
 }
 
+// One operand's staging: a BX x BK tile (BX rows of M or N, BK of k) from global
+// memory through registers into a swizzled [row][k] LDS image.  KC: the operand
+// is stored with k contiguous; otherwise with the BX side contiguous (loaded in
+// VEC x VEC blocks and transposed in registers).  VECOK: rows are 16-byte
+// aligned, so in-range chunks take one vector load.
+template <typename E, int BX, int NT, bool KC, bool VECOK>
+struct Stage {
+    static constexpr int VEC = Elem<E>::VEC, CH = 8;
+    static constexpr int UNITS = KC ? BX * CH : CH * (BX / VEC);  // chunks, or VEC x VEC blocks
+    static constexpr int PER = (UNITS + NT - 1) / NT;
+    static_assert(BX % VEC == 0, "tile side must be whole chunks");
+    u32x4 r[PER][KC ? 1 : VEC];
+
+    // Tile rows x0 .. x0+BX-1 (of ext) and k0 .. k0+BK-1 (of K); p and ld as stored.
+    // fast: the tile lies inside the matrix, no guards needed.
+    __device__ __forceinline__ void load(const E* __restrict__ p, int64_t ld, int tid, int64_t x0,
+                                         int64_t k0, int64_t ext, int64_t K, bool fast) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int id = tid + q * NT;
+            if (UNITS % NT != 0 && id >= UNITS) continue;
+            if constexpr (KC) {
+                const int64_t gr = x0 + id / CH, gc = k0 + (id % CH) * VEC;
+                r[q][0] = (VECOK && fast) ? *reinterpret_cast<const u32x4*>(p + gr * ld + gc)
+                                          : load_chunk_guarded<E, VECOK>(p, gr, gc, ext, K, ld);
+            } else {
+                const int64_t gc = x0 + (id % (BX / VEC)) * VEC;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int64_t gr = k0 + (id / (BX / VEC)) * VEC + e;
+                    r[q][e] = (VECOK && fast) ? *reinterpret_cast<const u32x4*>(p + gr * ld + gc)
+                                              : load_chunk_guarded<E, VECOK>(p, gr, gc, K, ext, ld);
+                }
+            }
+        }
+    }
+
+    // Registers -> LDS image `img` ([BX rows][CH chunks], chunks swizzled per row).
+    __device__ __forceinline__ void store(u32x4* img, int tid) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int id = tid + q * NT;
+            if (UNITS % NT != 0 && id >= UNITS) continue;
+            if constexpr (KC) {
+                const int row = id / CH, ch = id % CH;
+                img[row * CH + swz(row, ch)] = r[q][0];
+            } else {
+                const int xb = id % (BX / VEC), kb = id / (BX / VEC);
+                u32x4 t[VEC];
+                Transpose<VEC>::run(r[q], t);
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) {
+                    const int row = xb * VEC + c;
+                    img[row * CH + swz(row, kb)] = t[c];
+                }
+            }
+        }
+    }
+};
+
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int GM_ = 8>
 struct MfmaCfg {
     using E = E_;
@@ -208,18 +269,15 @@ struct MfmaCfg {
     static constexpr int TM = WTM / MF, TN = WTN / MF;  // matrix-core blocks per wave
     static constexpr int G = kWave / MF;                // lane groups
     static constexpr int SLABS = CH / G;                // k-slabs per k-tile
-    static constexpr int A_CHUNKS = BM * CH;
-    static constexpr int A_PER = (A_CHUNKS + NT - 1) / NT;
-    static constexpr int B_BLOCKS = CH * (BN / VEC);
-    static constexpr int B_PER = (B_BLOCKS + NT - 1) / NT;
     static constexpr int LDS_BYTES = 2 * (BM + BN) * CH * 16;
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "wave tiles must be whole blocks");
-    static_assert(BN % VEC == 0, "B tile must be whole chunks");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KiB per CU on gfx950");
     static_assert(NT <= 1024, "at most 1024 work-items per workgroup");
 };
 
-template <class Cfg, bool AV, bool BV, bool GEN>
+// TA: A is given transposed (stored K x M, m contiguous); TB: B is given
+// transposed (stored N x K, k contiguous).
+template <class Cfg, bool AV, bool BV, bool GEN, bool TA, bool TB>
 __global__ __launch_bounds__(Cfg::NT) void mfma_gemm_kernel(
     int64_t M, int64_t N, int64_t K, const typename Cfg::E* __restrict__ A, int64_t lda,
     const typename Cfg::E* __restrict__ B, int64_t ldb, Epi out, int tiles_m, int tiles_n) {
@@ -251,67 +309,22 @@ __global__ __launch_bounds__(Cfg::NT) void mfma_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = Acc{};
 
-    u32x4 ra[Cfg::A_PER];
-    u32x4 rb[Cfg::B_PER][VEC];
+    // A is k-contiguous unless given transposed; B only when given transposed.
+    Stage<E, BM, NT, !TA, AV> stA;
+    Stage<E, BN, NT, TB, BV> stB;
 
     // Global -> registers for k-tile kt.
     auto load_tile = [&](int kt) {
         const int64_t k0 = static_cast<int64_t>(kt) * BK;
         const bool fast = full_mn && (k0 + BK <= K);
-#pragma unroll
-        for (int q = 0; q < Cfg::A_PER; ++q) {
-            const int id = tid + q * NT;
-            if (Cfg::A_CHUNKS % NT == 0 || id < Cfg::A_CHUNKS) {
-                const int row = id / CH, ch = id % CH;
-                const int64_t gr = m0 + row, gc = k0 + ch * VEC;
-                if (AV && fast)
-                    ra[q] = *reinterpret_cast<const u32x4*>(A + gr * lda + gc);
-                else
-                    ra[q] = load_chunk_guarded<E, AV>(A, gr, gc, M, K, lda);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < Cfg::B_PER; ++q) {
-            const int id = tid + q * NT;
-            if (Cfg::B_BLOCKS % NT == 0 || id < Cfg::B_BLOCKS) {
-                const int nb = id % (BN / VEC), kb = id / (BN / VEC);
-                const int64_t gc = n0 + nb * VEC;
-#pragma unroll
-                for (int r = 0; r < VEC; ++r) {
-                    const int64_t gr = k0 + kb * VEC + r;
-                    if (BV && fast)
-                        rb[q][r] = *reinterpret_cast<const u32x4*>(B + gr * ldb + gc);
-                    else
-                        rb[q][r] = load_chunk_guarded<E, BV>(B, gr, gc, K, N, ldb);
-                }
-            }
-        }
+        stA.load(A, lda, tid, m0, k0, M, K, fast);
+        stB.load(B, ldb, tid, n0, k0, N, K, fast);
     };
 
-    // Registers -> LDS buffer `buf` (B transposed to [n][k]).
+    // Registers -> LDS buffer `buf`, both operands as [row][k].
     auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < Cfg::A_PER; ++q) {
-            const int id = tid + q * NT;
-            if (Cfg::A_CHUNKS % NT == 0 || id < Cfg::A_CHUNKS) {
-                const int row = id / CH, ch = id % CH;
-                sA[buf][row * CH + swz(row, ch)] = ra[q];
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < Cfg::B_PER; ++q) {
-            const int id = tid + q * NT;
-            if (Cfg::B_BLOCKS % NT == 0 || id < Cfg::B_BLOCKS) {
-                const int nb = id % (BN / VEC), kb = id / (BN / VEC);
-                u32x4 t[VEC];
-                Transpose<VEC>::run(rb[q], t);
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) {
-                    const int row = nb * VEC + c;
-                    sB[buf][row * CH + swz(row, kb)] = t[c];
-                }
-            }
-        }
+        stA.store(sA[buf], tid);
+        stB.store(sB[buf], tid);
     };
 
     const int KT = static_cast<int>(ceil_div(K, BK));
@@ -380,27 +393,31 @@ hipError_t launch_mfma_cfg(const GemmArgs& g) {
     const E* B = static_cast<const E*>(g.B);
     dim3 grid(static_cast<unsigned>(tm * tn)), block(Cfg::NT);
     const int itm = static_cast<int>(tm), itn = static_cast<int>(tn);
-    // The general output step is compiled for the two common load forms only
+    // The plain row-major product is compiled for all four load forms; the
+    // general output step and the transposed layouts for the two common ones
     // (both operands vectorised, or neither), which bounds the instantiations.
-    if constexpr (GEN) {
-        if (av && bv)
-            mfma_gemm_kernel<Cfg, true, true, true><<<grid, block, 0, g.stream>>>(
-                g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
-        else
-            mfma_gemm_kernel<Cfg, false, false, true><<<grid, block, 0, g.stream>>>(
-                g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
-    } else if (av && bv)
-        mfma_gemm_kernel<Cfg, true, true, false><<<grid, block, 0, g.stream>>>(
-            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
-    else if (av)
-        mfma_gemm_kernel<Cfg, true, false, false><<<grid, block, 0, g.stream>>>(
-            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
-    else if (bv)
-        mfma_gemm_kernel<Cfg, false, true, false><<<grid, block, 0, g.stream>>>(
-            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
-    else
-        mfma_gemm_kernel<Cfg, false, false, false><<<grid, block, 0, g.stream>>>(
-            g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn);
+#define MIGEMM_LAUNCH(AV_, BV_, TA_, TB_)                                                      \
+    mfma_gemm_kernel<Cfg, AV_, BV_, GEN, TA_, TB_><<<grid, block, 0, g.stream>>>(              \
+        g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn)
+    const bool vec = av && bv;
+    if (g.ta || g.tb) {
+        if (g.ta && g.tb) {
+            if (vec) MIGEMM_LAUNCH(true, true, true, true); else MIGEMM_LAUNCH(false, false, true, true);
+        } else if (g.ta) {
+            if (vec) MIGEMM_LAUNCH(true, true, true, false); else MIGEMM_LAUNCH(false, false, true, false);
+        } else {
+            if (vec) MIGEMM_LAUNCH(true, true, false, true); else MIGEMM_LAUNCH(false, false, false, true);
+        }
+    } else if (GEN || vec) {
+        if (vec) MIGEMM_LAUNCH(true, true, false, false); else MIGEMM_LAUNCH(false, false, false, false);
+    } else if (av) {
+        MIGEMM_LAUNCH(true, false, false, false);
+    } else if (bv) {
+        MIGEMM_LAUNCH(false, true, false, false);
+    } else {
+        MIGEMM_LAUNCH(false, false, false, false);
+    }
+#undef MIGEMM_LAUNCH
     return hipGetLastError();
 }
 

@@ -7,6 +7,9 @@
 // are widened exactly to FP32 before the multiply, so the mixed-precision
 // semantics are those of the matrix-core kernels.
 //
+// Either operand may be given transposed: the kernel walks k with the
+// operands' own strides (A: 1 or lda, B: ldb or 1).
+//
 // Launch shape for wave64: a 64 x 4 workgroup, so each wavefront covers 64
 // consecutive columns of one row of C -- its B loads are one 256-byte
 // coalesced read per k and its A load is a single broadcast address.  The
@@ -21,16 +24,17 @@ template <typename T, int BX, int BY, bool GEN>
 __global__ __launch_bounds__(BX* BY) void naive_kernel(int64_t M, int64_t N, int64_t K,
                                                        const T* __restrict__ A, int64_t lda,
                                                        const T* __restrict__ B, int64_t ldb,
-                                                       Epi out) {
+                                                       bool ta, bool tb, Epi out) {
     const int64_t col = static_cast<int64_t>(blockIdx.x) * BX + threadIdx.x;
     if (col >= N) return;
     // grid.y is capped at 65535 by the launcher; rows beyond it loop.
     for (int64_t row = static_cast<int64_t>(blockIdx.y) * BY + threadIdx.y; row < M;
          row += static_cast<int64_t>(gridDim.y) * BY) {
-        const T* a = A + row * lda;
-        const T* b = B + col;
+        const T* a = ta ? A + row : A + row * lda;
+        const T* b = tb ? B + col * ldb : B + col;
+        const int64_t sa = ta ? lda : 1, sb = tb ? 1 : ldb;  // step along k
         float acc = 0.0f;
-        for (int64_t k = 0; k < K; ++k) acc = fmaf(to_f32(a[k]), to_f32(b[k * ldb]), acc);
+        for (int64_t k = 0; k < K; ++k) acc = fmaf(to_f32(a[k * sa]), to_f32(b[k * sb]), acc);
         store_out<GEN>(out, row * out.ldc + col, acc);
     }
 }
@@ -45,17 +49,17 @@ hipError_t launch_shape(const GemmArgs& g) {
         case 0:
             naive_kernel<float, BX, BY, GEN><<<grid, block, 0, g.stream>>>(
                 g.M, g.N, g.K, static_cast<const float*>(g.A), g.lda,
-                static_cast<const float*>(g.B), g.ldb, g.out);
+                static_cast<const float*>(g.B), g.ldb, g.ta, g.tb, g.out);
             break;
         case 1:
             naive_kernel<_Float16, BX, BY, GEN><<<grid, block, 0, g.stream>>>(
                 g.M, g.N, g.K, static_cast<const _Float16*>(g.A), g.lda,
-                static_cast<const _Float16*>(g.B), g.ldb, g.out);
+                static_cast<const _Float16*>(g.B), g.ldb, g.ta, g.tb, g.out);
             break;
         default:
             naive_kernel<bf16_t, BX, BY, GEN><<<grid, block, 0, g.stream>>>(
                 g.M, g.N, g.K, static_cast<const bf16_t*>(g.A), g.lda,
-                static_cast<const bf16_t*>(g.B), g.ldb, g.out);
+                static_cast<const bf16_t*>(g.B), g.ldb, g.ta, g.tb, g.out);
             break;
     }
     return hipGetLastError();

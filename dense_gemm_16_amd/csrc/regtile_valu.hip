@@ -21,6 +21,10 @@
 // * Every edge is guarded: tiles inside the matrix take unguarded vector
 //   loads; edge tiles and the K tail load zeros out of range; rows not 16-byte
 //   aligned are read element by element.
+// * Either operand may be given transposed.  Both LDS tiles are k-major, so an
+//   operand stored with its M or N side contiguous (row-major B, or A given
+//   transposed) is copied row for row, and one stored with k contiguous
+//   (row-major A, or B given transposed) is transposed on its way into LDS.
 #include "common.hpp"
 
 namespace migemm {
@@ -38,19 +42,63 @@ __device__ __forceinline__ f32x4 ld4_guarded(const float* __restrict__ base, int
     return v;
 }
 
-template <int BM, int BN, int BK, int TM, int TN, bool GEN>
+// One operand's BX x BK tile into a k-major LDS tile img[BK][LD].  KC: stored
+// with k contiguous (transposed on the way in); otherwise stored with the BX
+// side contiguous (copied as 16-byte row pieces).
+template <int BX, int BK, int NT, int LD, bool KC>
+struct ValuStage {
+    static constexpr int UNITS = BX * BK / 4;
+    static constexpr int PER = (UNITS + NT - 1) / NT;
+    f32x4 r[PER];
+
+    // Tile rows x0.. (of ext) and k0.. (of K); p and ld as stored.
+    __device__ __forceinline__ void load(const float* __restrict__ p, int64_t ld, int tid,
+                                         int64_t x0, int64_t k0, int64_t ext, int64_t K,
+                                         bool fast, bool vec) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int id = tid + q * NT;
+            if (UNITS % NT != 0 && id >= UNITS) continue;
+            if constexpr (KC) {
+                const int64_t x = x0 + id / (BK / 4), k = k0 + (id % (BK / 4)) * 4;
+                r[q] = (fast && vec) ? *reinterpret_cast<const f32x4*>(p + x * ld + k)
+                                     : ld4_guarded(p, x, k, ext, K, ld, vec);
+            } else {
+                const int64_t k = k0 + id / (BX / 4), x = x0 + (id % (BX / 4)) * 4;
+                r[q] = (fast && vec) ? *reinterpret_cast<const f32x4*>(p + k * ld + x)
+                                     : ld4_guarded(p, k, x, K, ext, ld, vec);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(float (*img)[LD], int tid) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int id = tid + q * NT;
+            if (UNITS % NT != 0 && id >= UNITS) continue;
+            if constexpr (KC) {
+                const int x = id / (BK / 4), kc = id % (BK / 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) img[kc * 4 + e][x] = r[q][e];
+            } else {
+                const int kr = id / (BX / 4), xc = id % (BX / 4);
+                *reinterpret_cast<f32x4*>(&img[kr][xc * 4]) = r[q];
+            }
+        }
+    }
+};
+
+template <int BM, int BN, int BK, int TM, int TN, bool GEN, bool TA, bool TB>
 __global__ __launch_bounds__((BM / TM) * (BN / TN)) void regtile_valu_kernel(
     int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
     const float* __restrict__ B, int64_t ldb, Epi out, bool av, bool bv, bool cv,
     unsigned tiles_n) {
     constexpr int NC = BN / TN, NR = BM / TM, NT = NC * NR;
     constexpr int PAD = 4;  // keeps k-major A rows 16-byte aligned while shifting banks
-    constexpr int A_V4 = BM * BK / 4, B_V4 = BK * BN / 4;
-    constexpr int A_PER = (A_V4 + NT - 1) / NT, B_PER = (B_V4 + NT - 1) / NT;
     static_assert(TM % 4 == 0 && TN % 4 == 0 && BK % 4 == 0, "16-byte groups");
 
     __shared__ __attribute__((aligned(16))) float sAt[2][BK][BM + PAD];
-    __shared__ __attribute__((aligned(16))) float sB[2][BK][BN];
+    __shared__ __attribute__((aligned(16))) float sB[2][BK][BN + PAD];
 
     const int tid = threadIdx.x;
     const int tc = tid % NC, tr = tid / NC;
@@ -64,50 +112,17 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void regtile_valu_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
 
-    f32x4 ra[A_PER], rb[B_PER];
+    // A is k-contiguous unless given transposed; B only when given transposed.
+    ValuStage<BM, BK, NT, BM + PAD, !TA> stA;
+    ValuStage<BN, BK, NT, BN + PAD, TB> stB;
     auto load_tile = [&](int64_t k0) {
         const bool fast = full_mn && (k0 + BK <= K);
-#pragma unroll
-        for (int q = 0; q < A_PER; ++q) {
-            const int id = tid + q * NT;
-            if (A_V4 % NT == 0 || id < A_V4) {
-                const int row = id / (BK / 4), kc = id % (BK / 4);
-                if (fast && av)
-                    ra[q] = *reinterpret_cast<const f32x4*>(A + (m0 + row) * lda + k0 + kc * 4);
-                else
-                    ra[q] = ld4_guarded(A, m0 + row, k0 + kc * 4, M, K, lda, av);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < B_PER; ++q) {
-            const int id = tid + q * NT;
-            if (B_V4 % NT == 0 || id < B_V4) {
-                const int kr = id / (BN / 4), nc = id % (BN / 4);
-                if (fast && bv)
-                    rb[q] = *reinterpret_cast<const f32x4*>(B + (k0 + kr) * ldb + n0 + nc * 4);
-                else
-                    rb[q] = ld4_guarded(B, k0 + kr, n0 + nc * 4, K, N, ldb, bv);
-            }
-        }
+        stA.load(A, lda, tid, m0, k0, M, K, fast, av);
+        stB.load(B, ldb, tid, n0, k0, N, K, fast, bv);
     };
     auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < A_PER; ++q) {
-            const int id = tid + q * NT;
-            if (A_V4 % NT == 0 || id < A_V4) {
-                const int row = id / (BK / 4), kc = id % (BK / 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sAt[buf][kc * 4 + e][row] = ra[q][e];
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < B_PER; ++q) {
-            const int id = tid + q * NT;
-            if (B_V4 % NT == 0 || id < B_V4) {
-                const int kr = id / (BN / 4), nc = id % (BN / 4);
-                *reinterpret_cast<f32x4*>(&sB[buf][kr][nc * 4]) = rb[q];
-            }
-        }
+        stA.store(sAt[buf], tid);
+        stB.store(sB[buf], tid);
     };
 
     const int64_t KT = ceil_div(K, BK);
@@ -166,14 +181,14 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void regtile_valu_kernel(
     }
 }
 
-template <int BM, int BN, int BK, int TM, int TN, bool GEN>
+template <int BM, int BN, int BK, int TM, int TN, bool GEN, bool TA, bool TB>
 hipError_t launch_gen(const GemmArgs& g) {
     const int64_t gx = ceil_div(g.N, BN), gy = ceil_div(g.M, BM);
     if (gx * gy > 0x7fffffff) return hipErrorInvalidValue;
     const bool av = aligned16(g.A) && g.lda % 4 == 0;
     const bool bv = aligned16(g.B) && g.ldb % 4 == 0;
     const bool cv = aligned16(g.out.C) && g.out.ldc % 4 == 0;
-    regtile_valu_kernel<BM, BN, BK, TM, TN, GEN>
+    regtile_valu_kernel<BM, BN, BK, TM, TN, GEN, TA, TB>
         <<<dim3(static_cast<unsigned>(gx * gy)), dim3((BM / TM) * (BN / TN)), 0, g.stream>>>(
             g.M, g.N, g.K, static_cast<const float*>(g.A), g.lda,
             static_cast<const float*>(g.B), g.ldb, g.out, av, bv, cv,
@@ -181,10 +196,19 @@ hipError_t launch_gen(const GemmArgs& g) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int TM, int TN, bool GEN>
+hipError_t launch_layout(const GemmArgs& g) {
+    if (g.ta)
+        return g.tb ? launch_gen<BM, BN, BK, TM, TN, GEN, true, true>(g)
+                    : launch_gen<BM, BN, BK, TM, TN, GEN, true, false>(g);
+    return g.tb ? launch_gen<BM, BN, BK, TM, TN, GEN, false, true>(g)
+                : launch_gen<BM, BN, BK, TM, TN, GEN, false, false>(g);
+}
+
 template <int BM, int BN, int BK, int TM, int TN>
 hipError_t launch_cfg(const GemmArgs& g) {
-    return g.general() ? launch_gen<BM, BN, BK, TM, TN, true>(g)
-                       : launch_gen<BM, BN, BK, TM, TN, false>(g);
+    return g.general() ? launch_layout<BM, BN, BK, TM, TN, true>(g)
+                       : launch_layout<BM, BN, BK, TM, TN, false>(g);
 }
 
 const char* const kNames[] = {"128x128x8 8x8", "128x128x16 8x8", "64x64x16 4x4",

@@ -56,6 +56,21 @@ typedef enum {
     MIGEMM_BF16 = 2  /* bfloat16: the upper half of a binary32 word */
 } migemm_dtype;
 
+/*
+ * Operand layout for migemm_gemm_ex (page "Tensor cores and matrix operations":
+ * matrix-unit operands declared row-major or column-major; page
+ * "matmul_registers.cu", library comparison: row-major operands handed to a
+ * column-major library by swapping them).
+ * MIGEMM_OP_N: the operand as stored is the one multiplied (A: M x K, element
+ * (i, k) at A[i * lda + k]; B: K x N, element (k, j) at B[k * ldb + j]).
+ * MIGEMM_OP_T: the operand is given transposed (A stored K x M: element (i, k)
+ * at A[k * lda + i], lda >= max(1, M); B stored N x K: element (k, j) at
+ * B[j * ldb + k], ldb >= max(1, K)).  A column-major operand is the transpose of
+ * a row-major one with the same leading dimension, so OP_T also takes
+ * column-major A or B.
+ */
+typedef enum { MIGEMM_OP_N = 0, MIGEMM_OP_T = 1 } migemm_op;
+
 typedef enum {
     MIGEMM_OK = 0,
     MIGEMM_ERR_INVALID_ARG = 1, /* negative size, ld too small, unknown dtype, NULL with data,
@@ -126,7 +141,8 @@ int migemm_gemm_variant(int variant, int config,
  * alpha multiplies the product, its beta the previous C), with C stored as FP32
  * or rounded into FP16 or BF16 (page "CUDA-Practice 09", section on FP32
  * accumulation: the FP32 accumulator is written back as FP32 or rounded as
- * required).
+ * required), and A and B each as stored or given transposed (op_a, op_b, see
+ * migemm_op).
  *
  * The sum of products is the same FP32 accumulation, by the same kernels, as
  * migemm_gemm.  Per element the update is then computed in FP32 (beta * C_old
@@ -135,19 +151,20 @@ int migemm_gemm_variant(int variant, int config,
  * become +-infinity).  When beta == 0 the previous C is not read and may hold
  * anything, NaN included.  C points to c_dtype elements, row-major with leading
  * dimension ldc (elements).  K == 0 gives C = beta * C_old (or 0).
- * alpha == 1, beta == 0, c_dtype == MIGEMM_F32 is exactly migemm_gemm.
  * Same pointer, stream, ownership and error rules as migemm_gemm; an unknown
- * c_dtype is MIGEMM_ERR_INVALID_ARG, and C must not overlap A or B.  The
- * selection depends on A, B and the sizes only, as for migemm_gemm.
+ * c_dtype or op is MIGEMM_ERR_INVALID_ARG, and C must not overlap A or B.
+ * The selection depends on A, B, their layouts and the sizes only.
+ * op_a == op_b == MIGEMM_OP_N with alpha == 1, beta == 0 and FP32 C is exactly
+ * migemm_gemm.
  */
-int migemm_gemm_ex(int64_t M, int64_t N, int64_t K, int dtype,
+int migemm_gemm_ex(int op_a, int op_b, int64_t M, int64_t N, int64_t K, int dtype,
                    const void* A, int64_t lda, const void* B, int64_t ldb,
                    float alpha, float beta, int c_dtype, void* C, int64_t ldc,
                    void* stream);
 
 /* As migemm_gemm_ex, with the variant and configuration forced as in
  * migemm_gemm_variant. */
-int migemm_gemm_ex_variant(int variant, int config,
+int migemm_gemm_ex_variant(int variant, int config, int op_a, int op_b,
                            int64_t M, int64_t N, int64_t K, int dtype,
                            const void* A, int64_t lda, const void* B, int64_t ldb,
                            float alpha, float beta, int c_dtype, void* C, int64_t ldc,

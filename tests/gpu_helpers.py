@@ -83,16 +83,22 @@ TORCH_OF = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}
 
 def run_gemm_ex(A: torch.Tensor, B: torch.Tensor, dtype: str, alpha: float, beta: float,
                 c_code: int, c_old: torch.Tensor | None = None, variant=-1, config=-1,
-                ldc=None, c_off=0):
+                ldc=None, c_off=0, ta=False, tb=False, lda=None, ldb=None, a_off=0, b_off=0):
     """C = alpha * A x B + beta * C_old through migemm_gemm_ex_variant, C stored as
-    c_code (0 FP32, 1 FP16, 2 BF16).  C sits inside a NaN-filled buffer (row stride
-    ``ldc``, ``c_off`` elements in); with beta == 0 the window starts as NaN too, so a
-    read of the previous C would show.  Returns (C on the CPU in its own dtype,
-    buffer, the window's mask in the buffer)."""
+    c_code (0 FP32, 1 FP16, 2 BF16).  A (M x K) and B (K x N) are the operands of
+    the product; with ta / tb they are stored transposed (K x M, N x K) on the GPU
+    and passed with MIGEMM_OP_T.  Operands and C sit inside NaN-filled buffers
+    (row strides lda, ldb, ldc; offsets in elements); with beta == 0 the C window
+    starts as NaN too, so a read of the previous C would show.  Returns (C on the
+    CPU in its own dtype, C buffer, the window's mask in the buffer)."""
     M, K = A.shape
     N = B.shape[1]
-    dA, _ = to_device_with_ld(A)
-    dB, _ = to_device_with_ld(B)
+    sA = A.t().contiguous() if ta else A
+    sB = B.t().contiguous() if tb else B
+    dA, _ = to_device_with_ld(sA, lda, a_off)
+    dB, _ = to_device_with_ld(sB, ldb, b_off)
+    lda = lda or max(sA.shape[1], 1)
+    ldb = ldb or max(sB.shape[1], 1)
     ldc = ldc or max(N, 1)
     tdt = TORCH_OF[c_code]
     cbuf = torch.full((c_off + max(M, 1) * ldc + 64,), float("nan"), dtype=tdt, device="cuda")
@@ -104,9 +110,9 @@ def run_gemm_ex(A: torch.Tensor, B: torch.Tensor, dtype: str, alpha: float, beta
     if M:
         mask[c_off:c_off + M * ldc].view(M, ldc)[:, :N] = True
     stream = torch.cuda.current_stream().cuda_stream
-    st = mg.migemm_gemm_ex_variant(variant, config, M, N, K, DT_CODE[dtype],
-                                   dA.data_ptr() if dA.numel() else None, max(K, 1),
-                                   dB.data_ptr() if dB.numel() else None, max(N, 1),
+    st = mg.migemm_gemm_ex_variant(variant, config, int(ta), int(tb), M, N, K, DT_CODE[dtype],
+                                   dA.data_ptr() if dA.numel() else None, lda,
+                                   dB.data_ptr() if dB.numel() else None, ldb,
                                    alpha, beta, c_code,
                                    dC.data_ptr() if dC.numel() else None, ldc, stream)
     torch.cuda.synchronize()

@@ -86,31 +86,45 @@ def test_overlapping_output_rejected():
 
 @pytest.mark.parametrize("args", [
     dict(c_dtype=3), dict(c_dtype=-1), dict(dtype=5), dict(ldc=4), dict(C=None), dict(M=-2),
+    dict(op_a=2), dict(op_b=-1),
+    # given transposed, A is stored K x M (lda >= M = 8) and B N x K (ldb >= K = 4)
+    dict(op_a=1, lda=7), dict(op_b=1, ldb=3),
 ])
 def test_general_form_invalid_arguments(args):
     a = dict(M=8, N=5, K=4, dtype=1, A=P, lda=4, B=2 * P, ldb=5, alpha=1.5, beta=0.5, c_dtype=2,
              C=3 * P, ldc=5)
     a.update(args)
-    st = mg.migemm_gemm_ex(a["M"], a["N"], a["K"], a["dtype"], a["A"], a["lda"], a["B"],
-                           a["ldb"], a["alpha"], a["beta"], a["c_dtype"], a["C"], a["ldc"], None)
+    st = mg.migemm_gemm_ex(a.get("op_a", 0), a.get("op_b", 0), a["M"], a["N"], a["K"], a["dtype"],
+                           a["A"], a["lda"], a["B"], a["ldb"], a["alpha"], a["beta"],
+                           a["c_dtype"], a["C"], a["ldc"], None)
     assert st == mg.ERR_INVALID_ARG
-    st = mg.migemm_gemm_ex_variant(mg.NAIVE, 0, a["M"], a["N"], a["K"], a["dtype"], a["A"],
-                                   a["lda"], a["B"], a["ldb"], a["alpha"], a["beta"],
-                                   a["c_dtype"], a["C"], a["ldc"], None)
+    st = mg.migemm_gemm_ex_variant(mg.NAIVE, 0, a.get("op_a", 0), a.get("op_b", 0), a["M"],
+                                   a["N"], a["K"], a["dtype"], a["A"], a["lda"], a["B"],
+                                   a["ldb"], a["alpha"], a["beta"], a["c_dtype"], a["C"],
+                                   a["ldc"], None)
     assert st == mg.ERR_INVALID_ARG
 
 
 def test_general_form_overlap_uses_output_element_size():
     # a 16 x 16 C spans 512 bytes as BF16 and 1024 as FP32: starting 400 (BF16) or
     # 1000 (FP32) bytes before A, it reaches into A
-    st = mg.migemm_gemm_ex(16, 16, 16, 1, P, 16, 2 * P, 16, 1.0, 0.0, 2, P - 400, 16, None)
+    st = mg.migemm_gemm_ex(0, 0, 16, 16, 16, 1, P, 16, 2 * P, 16, 1.0, 0.0, 2, P - 400, 16, None)
     assert st == mg.ERR_INVALID_ARG
-    st = mg.migemm_gemm_ex(16, 16, 16, 1, P, 16, 2 * P, 16, 1.0, 0.0, 0, P - 1000, 16, None)
+    st = mg.migemm_gemm_ex(0, 0, 16, 16, 16, 1, P, 16, 2 * P, 16, 1.0, 0.0, 0, P - 1000, 16, None)
+    assert st == mg.ERR_INVALID_ARG
+
+
+def test_transposed_operand_extent_in_overlap_check():
+    # A given transposed (M = 8, K = 40, lda = 100) is stored K x M and spans
+    # 39 * 100 + 8 = 3908 FP16 elements (7816 bytes); read as M x K it would span
+    # only 7 * 100 + 40 = 740.  A C starting 3000 bytes after A overlaps the
+    # stored extent only.
+    st = mg.migemm_gemm_ex(1, 0, 8, 4, 40, 1, P, 100, 3 * P, 4, 1.0, 0.0, 0, P + 3000, 4, None)
     assert st == mg.ERR_INVALID_ARG
 
 
 def test_general_form_forced_variant_checks():
-    f16 = (64, 64, 64, 1, P, 64, 2 * P, 64, 2.0, 1.0, 1, 3 * P, 64, None)
+    f16 = (0, 1, 64, 64, 64, 1, P, 64, 2 * P, 64, 2.0, 1.0, 1, 3 * P, 64, None)
     assert mg.migemm_gemm_ex_variant(mg.LDS_TILED, -1, *f16) == mg.ERR_UNSUPPORTED
     assert mg.migemm_gemm_ex_variant(9, -1, *f16) == mg.ERR_INVALID_ARG
     assert mg.migemm_gemm_ex_variant(mg.MFMA16, 999, *f16) == mg.ERR_INVALID_ARG
