@@ -181,6 +181,65 @@ def cpu_baseline(p, seconds):
             "gpu_rows_vs_oracle": str(chk), "gpu_rows_ok": bool(chk.ok)}
 
 
+def conversion_lines(w):
+    """migemm_convert FP32 -> BF16 on the workload's A (HBM GB/s: 4 bytes read and
+    2 written per element), and FP32 operands converted then multiplied in BF16."""
+    import torch
+    import dense_gemm_16_amd as mg
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    a32 = torch.randn((w.M, w.K), generator=g, device="cuda")
+    b32 = torch.randn((w.K, w.N), generator=g, device="cuda")
+    a16 = torch.empty((w.M, w.K), dtype=torch.bfloat16, device="cuda")
+    b16 = torch.empty((w.K, w.N), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+
+    def conv_a():
+        st = mg.migemm_convert(0, 2, w.M, w.K, a32.data_ptr(), w.K, a16.data_ptr(), w.K, s)
+        if st != mg.OK:
+            raise RuntimeError(mg.migemm_status_string(st))
+
+    def full():
+        conv_a()
+        st = mg.migemm_convert(0, 2, w.K, w.N, b32.data_ptr(), w.N, b16.data_ptr(), w.N, s)
+        st = st or mg.migemm_gemm(w.M, w.N, w.K, 2, a16.data_ptr(), w.K, b16.data_ptr(), w.N,
+                                  c.data_ptr(), w.N, s)
+        if st != mg.OK:
+            raise RuntimeError(mg.migemm_status_string(st))
+
+    def timed(f, reps):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            f()
+        t1.record()
+        t1.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    out = {}
+    ms = timed(conv_a, 200)
+    nbytes = w.M * w.K * (4 + 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["convert-f32-to-bf16-" + f"{w.M}x{w.K}"] = {
+        "gbs": round(gbs, 1), "ms": round(ms, 5), "bound": "hbm",
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "bytes_per_launch": nbytes, "kernel": "migemm_convert f32->bf16"}
+    log(f"extra convert f32->bf16 {w.M}x{w.K}: {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+    ms = timed(full, 40)
+    tf = w.flop / (ms * 1e-3) / 1e12
+    out[w.name + "/from-f32"] = {
+        "tflops": round(tf, 2), "ms": round(ms, 5),
+        "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
+        "kernel": "migemm_convert x2 + migemm_gemm (BF16)",
+        "note": "FP32 A and B converted to BF16 on the device, then the BF16 product"}
+    log(f"extra {w.name} from FP32 data (convert A, B + BF16 product): {tf:.1f} TFLOPS")
+    return out
+
+
 def device_info():
     import torch
     pr = torch.cuda.get_device_properties(0)
@@ -406,6 +465,9 @@ def main():
                               f"B {'N x K (given transposed)' if tb else 'K x N'}"}
                 log(f"extra {w.name} layout {px.layout()}: {tf:.1f} TFLOPS")
                 del px
+        # FP32 data on the 16-bit path: device conversion, alone and followed by the product
+        if w.name == "c4-bf16-8192":
+            extra.update(conversion_lines(w))
         # the general output step on the headline shape: scaled update, BF16 C
         if w.name == "c4-bf16-8192":
             px = Problem(w, alpha=0.5, beta=-1.0, c_code=2)

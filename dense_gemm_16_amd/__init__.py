@@ -26,6 +26,7 @@ VARIANT_AUTO, NAIVE, LDS_TILED, REGTILE_VALU, REGTILE_MFMA, MFMA16 = -1, 0, 1, 2
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ("migemm_gemm", "migemm_gemm_variant", "migemm_gemm_ex", "migemm_gemm_ex_variant",
+           "migemm_convert",
            "migemm_variant_count", "migemm_variant_name",
            "migemm_variant_supports", "migemm_config_count", "migemm_config_name",
            "migemm_select", "migemm_status_string", "migemm_last_hip_error", "migemm_version")
@@ -63,6 +64,8 @@ def lib():
     L.migemm_gemm_ex_variant.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, vp, i64, vp, i64,
                                          f32, f32, i32, vp, i64, vp]
     L.migemm_gemm_ex_variant.restype = i32
+    L.migemm_convert.argtypes = [i32, i32, i64, i64, vp, i64, vp, i64, vp]
+    L.migemm_convert.restype = i32
     L.migemm_variant_count.argtypes = []
     L.migemm_variant_count.restype = i32
     L.migemm_variant_name.argtypes = [i32]
@@ -108,6 +111,10 @@ def migemm_gemm_ex_variant(variant, config, op_a, op_b, M, N, K, dtype, A, lda, 
                            beta, c_dtype, C, ldc, stream=None) -> int:
     return lib().migemm_gemm_ex_variant(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B,
                                         ldb, alpha, beta, c_dtype, C, ldc, stream)
+
+
+def migemm_convert(src_dtype, dst_dtype, rows, cols, src, lds, dst, ldd, stream=None) -> int:
+    return lib().migemm_convert(src_dtype, dst_dtype, rows, cols, src, lds, dst, ldd, stream)
 
 
 def migemm_variant_count() -> int:
@@ -181,6 +188,27 @@ def _operand(t):
     if rows <= 1 or t.stride(0) == 1:
         return OP_T, max(1, t.stride(1) if cols > 1 else rows)
     raise ValueError("operands must be row-major or transposed views of row-major storage")
+
+
+def convert(src, dtype, out=None, *, stream=None):
+    """``src`` (a 2-D CUDA tensor, float32/float16/bfloat16, unit column stride)
+    converted to ``dtype`` on the GPU (round to nearest even when narrowing);
+    ``out`` is allocated if not given.  Returns ``out`` without synchronising."""
+    import torch
+    if src.device.type != "cuda":
+        raise ValueError("src must be on the GPU")
+    rows, cols = src.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=dtype, device=src.device)
+    elif out.dtype != dtype or tuple(out.shape) != (rows, cols):
+        raise ValueError("out must have src's shape and the requested dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device).cuda_stream
+    st = migemm_convert(_dtype_code(src), _dtype_code(out), rows, cols, src.data_ptr() or None,
+                        _ld(src), out.data_ptr() or None, _ld(out), stream)
+    if st != OK:
+        raise MigemmError(st, "migemm_convert")
+    return out
 
 
 def gemm(a, b, out=None, *, alpha: float = 1.0, beta: float = 0.0, out_dtype=None,

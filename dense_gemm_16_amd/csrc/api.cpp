@@ -191,6 +191,27 @@ int migemm_gemm_ex_variant(int variant, int config, int op_a, int op_b, int64_t 
                C, ldc, stream);
 }
 
+int migemm_convert(int src_dtype, int dst_dtype, int64_t rows, int64_t cols, const void* src,
+                   int64_t lds, void* dst, int64_t ldd, void* stream) {
+    if (!known_dtype(src_dtype) || !known_dtype(dst_dtype)) return MIGEMM_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return MIGEMM_ERR_INVALID_ARG;
+    const int64_t min_ld = cols > 1 ? cols : 1;
+    if (lds < min_ld || ldd < min_ld || lds > kMaxLd || ldd > kMaxLd) return MIGEMM_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return MIGEMM_OK;
+    if (!src || !dst) return MIGEMM_ERR_INVALID_ARG;
+    uintptr_t s0, s1, d0, d1;
+    extent(src, rows, cols, lds, elem_size(src_dtype), s0, s1);
+    extent(dst, rows, cols, ldd, elem_size(dst_dtype), d0, d1);
+    if (overlaps(s0, s1, d0, d1)) return MIGEMM_ERR_INVALID_ARG;
+    const hipError_t err = launch_convert(src_dtype, dst_dtype, rows, cols, src, lds, dst, ldd,
+                                          static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        g_last_hip_error = static_cast<int>(err);
+        return MIGEMM_ERR_HIP;
+    }
+    return MIGEMM_OK;
+}
+
 int migemm_variant_count(void) { return kNumVariants; }
 
 const char* migemm_variant_name(int variant) {

@@ -139,6 +139,11 @@ hipError_t launch_mfma16(const GemmArgs& a, int config);
 // K == 0: the sum of products is 0 for every element; applies the output step to it.
 hipError_t launch_empty_product(const GemmArgs& a);
 
+// dst (rows x cols, ldd, dst_dtype) = src (rows x cols, lds, src_dtype) converted,
+// round to nearest even where narrower.
+hipError_t launch_convert(int src_dtype, int dst_dtype, int64_t rows, int64_t cols,
+                          const void* src, int64_t lds, void* dst, int64_t ldd, hipStream_t s);
+
 // Configuration tables, one per variant (names, and the count).
 int naive_config_count();
 const char* naive_config_name(int c);

@@ -170,6 +170,26 @@ int migemm_gemm_ex_variant(int variant, int config, int op_a, int op_b,
                            float alpha, float beta, int c_dtype, void* C, int64_t ldc,
                            void* stream);
 
+/*
+ * Element-type conversion of a matrix on the device, the step before the
+ * product for FP32 data headed for the 16-bit matrix-core path (page
+ * "04-wmma-matmul.cu": its FP32 inputs are converted to half before the
+ * product; page "CUDA-Practice 09", section on mixed precision: 16-bit inputs
+ * halve the bytes read):
+ *
+ *     dst[i][j] = src[i][j],  i < rows, j < cols
+ *
+ * from src_dtype to dst_dtype (any of MIGEMM_F32, MIGEMM_F16, MIGEMM_BF16).
+ * Widening is exact; narrowing rounds to nearest even (magnitudes beyond the
+ * target's range become +-infinity, NaN stays NaN).  Both matrices are
+ * row-major device arrays with leading dimensions lds, ldd >= max(1, cols)
+ * (elements); elements between rows are not touched.  src and dst must not
+ * overlap.  Same stream, ownership and error rules as migemm_gemm; rows == 0
+ * or cols == 0 is a no-op.
+ */
+int migemm_convert(int src_dtype, int dst_dtype, int64_t rows, int64_t cols,
+                   const void* src, int64_t lds, void* dst, int64_t ldd, void* stream);
+
 /* Number of variants (they are numbered 0 .. count-1). */
 int migemm_variant_count(void);
 

@@ -130,6 +130,24 @@ def test_general_form_forced_variant_checks():
     assert mg.migemm_gemm_ex_variant(mg.MFMA16, 999, *f16) == mg.ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("args", [
+    dict(src_dtype=3), dict(dst_dtype=-1), dict(rows=-1), dict(cols=-1), dict(lds=9),
+    dict(ldd=9), dict(src=None), dict(dst=None), dict(rows=1 << 31),
+    dict(dst=P + 100),  # overlaps src (8 x 10 FP32 from P spans 320 bytes)
+])
+def test_convert_invalid_arguments(args):
+    a = dict(src_dtype=0, dst_dtype=2, rows=8, cols=10, src=P, lds=10, dst=3 * P, ldd=10)
+    a.update(args)
+    st = mg.migemm_convert(a["src_dtype"], a["dst_dtype"], a["rows"], a["cols"], a["src"],
+                           a["lds"], a["dst"], a["ldd"], None)
+    assert st == mg.ERR_INVALID_ARG
+
+
+def test_convert_empty_is_a_noop():
+    assert mg.migemm_convert(0, 1, 0, 10, None, 10, None, 10, None) == mg.OK
+    assert mg.migemm_convert(2, 0, 5, 0, None, 1, None, 1, None) == mg.OK
+
+
 def test_empty_output_is_a_noop():
     # M == 0 or N == 0: OK with no HIP call (null pointers allowed where there is no data)
     assert mg.migemm_gemm(0, 5, 7, 0, None, 7, P, 5, None, 5, None) == mg.OK
