@@ -23,8 +23,8 @@ CPU reference on page "matmul_registers.cu".  This module only marshals
 numpy arrays into that library.
 
 Inputs are passed as their stored encodings: ``float32`` arrays for FP32,
-``uint16`` (or ``int16``) arrays of raw bits for FP16 and BF16.  The oracle
-decodes the bits itself.
+``uint16`` (or ``int16``) arrays of raw bits for FP16 and BF16, ``int8`` (or
+``uint8``) arrays for INT8.  The oracle decodes the bits itself.
 """
 from __future__ import annotations
 
@@ -35,8 +35,8 @@ import numpy as np
 
 from .build import build, library_path
 
-F32, F16, BF16 = 0, 1, 2
-DTYPES = {"f32": F32, "f16": F16, "bf16": BF16}
+F32, F16, BF16, I8 = 0, 1, 2, 3
+DTYPES = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8}
 
 
 class Oracle:
@@ -71,6 +71,8 @@ class Oracle:
         arr = np.ascontiguousarray(np.asarray(bits))
         if dtype == F32:
             arr = arr if arr.dtype == np.float32 else arr.view(np.float32)
+        elif dtype == I8:
+            arr = arr.view(np.uint8)
         elif arr.dtype == np.int16:
             arr = arr.view(np.uint16)
         out = np.empty(arr.shape, dtype=np.float64)
@@ -209,6 +211,10 @@ def _as_stored(x, dtype: int) -> np.ndarray:
     if dtype == F32:
         if x.dtype != np.float32:
             raise TypeError(f"FP32 operand must be float32, got {x.dtype}")
+    elif dtype == I8:
+        if x.dtype not in (np.int8, np.uint8):
+            raise TypeError(f"INT8 operand must be int8/uint8, got {x.dtype}")
+        x = x.view(np.uint8)
     else:
         if x.dtype == np.int16:
             x = x.view(np.uint16)

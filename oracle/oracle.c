@@ -29,6 +29,9 @@
  *   dtype 0  IEEE binary32: sign, 8-bit exponent (bias 127), 23-bit fraction
  *   dtype 1  IEEE binary16: sign, 5-bit exponent (bias 15), 10-bit fraction
  *   dtype 2  bfloat16: the upper 16 bits of a binary32 word
+ *   dtype 3  8-bit two's-complement integer (-128 .. 127); every product and
+ *            every sum of at most 2^17 of them is an integer below 2^31, exact
+ *            in binary64
  * All arrays are row-major with leading dimensions lda, ldb (in elements).
  * C and S are written densely with leading dimension N.
  *
@@ -44,7 +47,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_I8 = 3 };
 enum { ORACLE_OK = 0, ORACLE_BAD_ARG = 1, ORACLE_NO_MEMORY = 2 };
 
 /* binary16: value = (-1)^s * 2^(e-15) * (1 + f/1024) for 0 < e < 31,
@@ -81,6 +84,12 @@ double oracle_decode_bf16(uint16_t h)
     return s ? -v : v;
 }
 
+/* 8-bit two's complement: bit 7 weighs -128, bits 0..6 weigh 1 .. 64. */
+double oracle_decode_i8(uint8_t b)
+{
+    return (double)((int)(b & 0x7f) - (int)(b & 0x80));
+}
+
 /* binary32 widened to binary64: exact. */
 double oracle_decode_f32(uint32_t w)
 {
@@ -94,7 +103,7 @@ static double decode_at(const void* base, int dtype, int64_t idx);
 /* Decodes n stored elements of the given dtype to binary64. */
 int oracle_decode_array(int dtype, int64_t n, const void* in, double* out)
 {
-    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16) return ORACLE_BAD_ARG;
+    if (dtype < ORACLE_F32 || dtype > ORACLE_I8) return ORACLE_BAD_ARG;
     if (n < 0 || (n > 0 && (!in || !out))) return ORACLE_BAD_ARG;
     for (int64_t e = 0; e < n; ++e) out[e] = decode_at(in, dtype, e);
     return ORACLE_OK;
@@ -106,6 +115,8 @@ static double decode_at(const void* base, int dtype, int64_t idx)
         return oracle_decode_f32(((const uint32_t*)base)[idx]);
     if (dtype == ORACLE_F16)
         return oracle_decode_f16(((const uint16_t*)base)[idx]);
+    if (dtype == ORACLE_I8)
+        return oracle_decode_i8(((const uint8_t*)base)[idx]);
     return oracle_decode_bf16(((const uint16_t*)base)[idx]);
 }
 
@@ -113,7 +124,7 @@ static int check_args(int64_t M, int64_t N, int64_t K, int dtype, const void* A,
                       const void* B, int64_t ldb)
 {
     if (M < 0 || N < 0 || K < 0) return ORACLE_BAD_ARG;
-    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16) return ORACLE_BAD_ARG;
+    if (dtype < ORACLE_F32 || dtype > ORACLE_I8) return ORACLE_BAD_ARG;
     if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1)) return ORACLE_BAD_ARG;
     if (M > 0 && K > 0 && !A) return ORACLE_BAD_ARG;
     if (K > 0 && N > 0 && !B) return ORACLE_BAD_ARG;

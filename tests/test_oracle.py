@@ -391,3 +391,32 @@ def test_compare_output_rounding_term():
     bad = got16.copy()
     bad[0] += 0.5
     assert not compare(bad, want, scale, TOL_HALF, out_dtype=oracle.F16).ok
+
+
+# ---------------------------------------------------------------- INT8
+
+def test_decode_i8_all_patterns_matches_numpy():
+    allb = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(oracle.decode(allb, oracle.I8), allb.view(np.int8).astype(np.float64))
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 9, 13), (64, 48, 300), (33, 70, 2048)])
+def test_i8_product_exact_against_numpy_int64(M, N, K):
+    """numpy's int64 matmul is exact; the oracle's binary64 sums of int8 products
+    are exact too (every partial sum is an integer below 2^31)."""
+    g = np.random.default_rng(M + N + K)
+    A = g.integers(-128, 128, (M, K), dtype=np.int64).astype(np.int8)
+    B = g.integers(-128, 128, (K, N), dtype=np.int64).astype(np.int8)
+    C, S = oracle.gemm(A, B, oracle.I8)
+    assert np.array_equal(C, (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float64))
+    assert np.array_equal(S, (np.abs(A.astype(np.int64)) @ np.abs(B.astype(np.int64))).astype(np.float64))
+
+
+def test_i8_extremes_exact():
+    """-128 * -128 summed 2^17 times is 2^31: still exact in binary64."""
+    K = 1 << 17
+    A = np.full((1, K), -128, dtype=np.int8)
+    B = np.full((K, 2), -128, dtype=np.int8)
+    B[:, 1] = 127
+    C, _ = oracle.gemm(A, B, oracle.I8)
+    assert C[0, 0] == 2.0 ** 31 and C[0, 1] == -128 * 127 * K

@@ -44,6 +44,7 @@ MUTANTS = {
     "epilogue_drops_beta": [("out[e] = alpha * acc[e] + old;", "out[e] = alpha * acc[e];")],
     "epilogue_alpha_on_old": [("beta * decode_at(Cold, c_dtype, e)", "alpha * decode_at(Cold, c_dtype, e)")],
     "epilogue_scale_without_abs": [("fabs(alpha) * S[e] + fabs(old)", "fabs(alpha) * S[e] + old")],
+    "i8_unsigned": [("return (double)((int)(b & 0x7f) - (int)(b & 0x80));", "return (double)b;")],
 }
 
 
@@ -151,7 +152,18 @@ def pin_epilogue_integers(o):
             and np.array_equal(sc, (3 * (np.abs(a) @ np.abs(b)) + 2 * np.abs(old)).astype(float)))
 
 
-PINS = [pin_decoders, pin_ones, pin_permutation, pin_small_int, pin_subnormal_inputs,
+def pin_i8(o):
+    allb = np.arange(256, dtype=np.uint8)
+    if not np.array_equal(o.decode(allb, oracle.I8), allb.view(np.int8).astype(np.float64)):
+        return False
+    g = np.random.default_rng(2)
+    A = g.integers(-128, 128, (9, 40)).astype(np.int8)
+    B = g.integers(-128, 128, (40, 11)).astype(np.int8)
+    C, _ = o.gemm(A, B, oracle.I8)
+    return np.array_equal(C, (A.astype(np.int64) @ B.astype(np.int64)).astype(float))
+
+
+PINS = [pin_decoders, pin_ones, pin_permutation, pin_small_int, pin_subnormal_inputs, pin_i8,
         pin_encode_roundtrip_and_ties, pin_encode_overflow, pin_epilogue_integers]
 
 
