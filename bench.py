@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOPS (2MNK/s) and % of MI355X peak at M=N=K=1024/2048/8192"
 # MI355X datasheet peaks (dense): 256 CUs x 2.4 GHz x FLOP/clock/CU
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3,
+               "i8": 5033.2}  # INT8: TOPS, twice the 16-bit matrix rate
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EXTRA = ["c1-f32-1024", "c1-f32-1024-int", "c2-f16-1024", "c3-f16-2048", "c3-bf16-2048",
@@ -69,10 +70,14 @@ class Problem:
         self.dB = (self.B.t().contiguous() if tb else self.B).cuda()
         lda, ldb = (w.M if ta else w.K), (w.K if tb else w.N)
         self.ops = (int(ta), int(tb))
-        cdt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[c_code]
+        if w.dtype == "i8":
+            c_code = 4  # INT32 C, the only output of an INT8 product
+        cdt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16, 4: torch.int32}[c_code]
         self.C = torch.empty((w.M, w.N), dtype=cdt, device="cuda")
         if beta != 0.0:
             self.C.copy_(torch.randn((w.M, w.N), generator=torch.Generator().manual_seed(w.seed + 1)))
+        if self.C.dtype == torch.int32:
+            self.C.zero_()
         self.epi = (float(alpha), float(beta), c_code)
         self.general = not (alpha == 1.0 and beta == 0.0 and c_code == 0 and not ta and not tb)
         self.code = inputs.DTYPE_CODES[w.dtype]
@@ -465,6 +470,18 @@ def main():
                               f"B {'N x K (given transposed)' if tb else 'K x N'}"}
                 log(f"extra {w.name} layout {px.layout()}: {tf:.1f} TFLOPS")
                 del px
+        # INT8 -> INT32 at the headline size
+        if w.name == "c4-bf16-8192":
+            wi = inputs.WORKLOADS["i8-8192"]
+            px = Problem(wi)
+            t, n = px.time_window()
+            tf = wi.flop / (t * 1e-3) / 1e12
+            extra[wi.name] = {"tops": round(tf, 2), "ms": round(t, 5), "launches": n,
+                              "frac_of_peak": round(tf / PEAK_TFLOPS["i8"], 4),
+                              "peak_tops": PEAK_TFLOPS["i8"], "kernel": px.kernel_name()}
+            log(f"extra {wi.name}: {tf:.1f} TOPS ({100 * tf / PEAK_TFLOPS['i8']:.1f}% of "
+                f"{PEAK_TFLOPS['i8']}) on {px.kernel_name()}")
+            del px
         # FP32 data on the 16-bit path: device conversion, alone and followed by the product
         if w.name == "c4-bf16-8192":
             extra.update(conversion_lines(w))

@@ -19,10 +19,10 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_HERE, "libmigemm.so")
 
-F32, F16, BF16 = 0, 1, 2
+F32, F16, BF16, I8, I32 = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 OP_N, OP_T = 0, 1
-VARIANT_AUTO, NAIVE, LDS_TILED, REGTILE_VALU, REGTILE_MFMA, MFMA16 = -1, 0, 1, 2, 3, 4
+VARIANT_AUTO, NAIVE, LDS_TILED, REGTILE_VALU, REGTILE_MFMA, MFMA16, MFMA_I8 = -1, 0, 1, 2, 3, 4, 5
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ("migemm_gemm", "migemm_gemm_variant", "migemm_gemm_ex", "migemm_gemm_ex_variant",
@@ -163,9 +163,11 @@ def migemm_version() -> int:
 
 def _dtype_code(t) -> int:
     import torch
-    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
+             torch.int32: I32}
     if t.dtype not in codes:
-        raise ValueError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+        raise ValueError(f"unsupported dtype {t.dtype}; expected float32, float16, bfloat16, "
+                         "int8 (operands) or int32 (output of an int8 product)")
     return codes[t.dtype]
 
 
@@ -238,7 +240,8 @@ def gemm(a, b, out=None, *, alpha: float = 1.0, beta: float = 0.0, out_dtype=Non
     if out is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an existing out")
-        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+        default = torch.int32 if a.dtype == torch.int8 else torch.float32
+        out = torch.empty((M, N), dtype=out_dtype or default, device=a.device)
     elif tuple(out.shape) != (M, N) or (out_dtype is not None and out.dtype != out_dtype):
         raise ValueError("out must have shape (M, N) (and out_dtype, if given)")
     cd = _dtype_code(out)

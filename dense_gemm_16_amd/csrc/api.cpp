@@ -35,12 +35,19 @@ const Variant kVariants[] = {
     {"regtile_mfma", 0x1u, regtile_mfma_config_count, regtile_mfma_config_name,
      launch_regtile_mfma},
     {"mfma16", 0x6u, mfma16_config_count, mfma16_config_name, launch_mfma16},
+    {"mfma_i8", 0x8u, mfma_i8_config_count, mfma_i8_config_name, launch_mfma_i8},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 thread_local int g_last_hip_error = 0;
 
-int elem_size(int dtype) { return dtype == MIGEMM_F32 ? 4 : 2; }
+int elem_size(int dtype) {
+    return (dtype == MIGEMM_F32 || dtype == MIGEMM_I32) ? 4 : dtype == MIGEMM_I8 ? 1 : 2;
+}
+
+// INT8: each product is at most 2^14 in magnitude ((-128)(-128)), so sums of at
+// most 2^17 - 1 of them stay below 2^31 and fit INT32 exactly.
+constexpr int64_t kMaxKi8 = (int64_t(1) << 17) - 1;
 
 // Byte range [lo, hi) touched by a rows x cols row-major operand with leading dimension ld.
 void extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int es, uintptr_t& lo,
@@ -52,6 +59,8 @@ void extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int es, uintp
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
 
 bool known_dtype(int d) { return d == MIGEMM_F32 || d == MIGEMM_F16 || d == MIGEMM_BF16; }
+bool known_input(int d) { return known_dtype(d) || d == MIGEMM_I8; }
+bool known_output(int d) { return known_dtype(d) || d == MIGEMM_I32; }
 
 bool known_op(int op) { return op == MIGEMM_OP_N || op == MIGEMM_OP_T; }
 
@@ -60,9 +69,12 @@ bool known_op(int op) { return op == MIGEMM_OP_N || op == MIGEMM_OP_T; }
 int check_args(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, const void* A,
                int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, int c_dtype,
                bool need_ptrs) {
-    if (!known_dtype(dtype) || !known_dtype(c_dtype)) return MIGEMM_ERR_INVALID_ARG;
+    if (!known_input(dtype) || !known_output(c_dtype)) return MIGEMM_ERR_INVALID_ARG;
+    // INT8 inputs go with INT32 C and nothing else does
+    if ((dtype == MIGEMM_I8) != (c_dtype == MIGEMM_I32)) return MIGEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return MIGEMM_ERR_INVALID_ARG;
+    if (dtype == MIGEMM_I8 && K > kMaxKi8) return MIGEMM_ERR_INVALID_ARG;
     auto at_least = [](int64_t ld, int64_t cols) { return ld >= (cols > 1 ? cols : 1); };
     if (!at_least(lda, ta ? M : K) || !at_least(ldb, tb ? K : N) || !at_least(ldc, N))
         return MIGEMM_ERR_INVALID_ARG;
@@ -102,6 +114,12 @@ bool operands_aligned(const void* A, int64_t lda, const void* B, int64_t ldb) {
 void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool aligned,
             int& variant, int& config) {
     auto tiles = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
+    if (dtype == MIGEMM_I8) {
+        variant = MIGEMM_MFMA_I8;
+        // 256x256 with 32x32x32 instructions measured best in every layout at 8192^3
+        config = tiles(256, 256) >= 256 ? 3 : tiles(128, 128) >= 256 ? 1 : 2;
+        return;
+    }
     if (dtype == MIGEMM_F32) {
         variant = MIGEMM_REGTILE_MFMA;
         config = tiles(128, 128) >= 256 ? 0 : 2;
@@ -130,6 +148,8 @@ int run(int variant, int config, int op_a, int op_b, int64_t M, int64_t N, int64
     const bool ta = op_a == MIGEMM_OP_T, tb = op_b == MIGEMM_OP_T;
     int st = check_args(M, N, K, dtype, ta, tb, A, lda, B, ldb, C, ldc, c_dtype, true);
     if (st != MIGEMM_OK) return st;
+    // INT32 C takes the plain product only
+    if (c_dtype == MIGEMM_I32 && (alpha != 1.0f || beta != 0.0f)) return MIGEMM_ERR_UNSUPPORTED;
     const bool aligned = operands_aligned(A, lda, B, ldb);
     if (variant == MIGEMM_VARIANT_AUTO) {
         if (config != -1) return MIGEMM_ERR_INVALID_ARG;
@@ -219,7 +239,7 @@ const char* migemm_variant_name(int variant) {
 }
 
 int migemm_variant_supports(int variant, int dtype) {
-    if (variant < 0 || variant >= kNumVariants || dtype < 0 || dtype > 2) return 0;
+    if (variant < 0 || variant >= kNumVariants || !known_input(dtype)) return 0;
     return (kVariants[variant].dtype_mask >> dtype) & 1u;
 }
 
@@ -238,7 +258,8 @@ int migemm_select(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int
     (void)A;
     (void)B;
     (void)C;
-    int st = check_args(M, N, K, dtype, false, false, A, lda, B, ldb, C, ldc, MIGEMM_F32, false);
+    const int c_dtype = dtype == MIGEMM_I8 ? MIGEMM_I32 : MIGEMM_F32;
+    int st = check_args(M, N, K, dtype, false, false, A, lda, B, ldb, C, ldc, c_dtype, false);
     if (st != MIGEMM_OK) return st;
     if (!variant || !config) return MIGEMM_ERR_INVALID_ARG;
     select(M, N, K, dtype, false, false, operands_aligned(A, lda, B, ldb), *variant, *config);
@@ -257,6 +278,6 @@ const char* migemm_status_string(int status) {
 
 int migemm_last_hip_error(void) { return g_last_hip_error; }
 
-int migemm_version(void) { return 300; }
+int migemm_version(void) { return 400; }
 
 }  // extern "C"

@@ -18,7 +18,7 @@ struct Epi {
     void* C;
     int64_t ldc;
     float alpha, beta;
-    int c_dtype;  // 0 FP32, 1 FP16, 2 BF16
+    int c_dtype;  // 0 FP32, 1 FP16, 2 BF16, 4 INT32 (INT8 products only; plain overwrite)
 };
 
 // Arguments of one product, already validated by the C ABI.  ta: A is given
@@ -69,7 +69,9 @@ __device__ __forceinline__ float load_prev(const Epi& e, int64_t idx) {
 template <bool NT>
 __device__ __forceinline__ void store_update(const Epi& e, int64_t idx, float v, float prev) {
     const float r = e.beta != 0.0f ? fmaf(e.alpha, v, e.beta * prev) : e.alpha * v;
-    if (e.c_dtype == 0) {
+    if (e.c_dtype == 4) {  // INT32 C: only the empty product (K == 0) comes here, with v == 0
+        static_cast<int32_t*>(e.C)[idx] = static_cast<int32_t>(r);
+    } else if (e.c_dtype == 0) {
         float* p = static_cast<float*>(e.C) + idx;
         if constexpr (NT)
             __builtin_nontemporal_store(r, p);
@@ -119,6 +121,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -136,6 +140,7 @@ hipError_t launch_lds_tiled(const GemmArgs& a, int config);
 hipError_t launch_regtile_valu(const GemmArgs& a, int config);
 hipError_t launch_regtile_mfma(const GemmArgs& a, int config);
 hipError_t launch_mfma16(const GemmArgs& a, int config);
+hipError_t launch_mfma_i8(const GemmArgs& a, int config);
 // K == 0: the sum of products is 0 for every element; applies the output step to it.
 hipError_t launch_empty_product(const GemmArgs& a);
 
@@ -155,5 +160,7 @@ int regtile_mfma_config_count();
 const char* regtile_mfma_config_name(int c);
 int mfma16_config_count();
 const char* mfma16_config_name(int c);
+int mfma_i8_config_count();
+const char* mfma_i8_config_name(int c);
 
 }  // namespace migemm

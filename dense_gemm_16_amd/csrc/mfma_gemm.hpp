@@ -48,6 +48,8 @@
 //   aligned are read element by element.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace migemm {
@@ -56,6 +58,7 @@ template <typename E> struct Elem;
 template <> struct Elem<float> { static constexpr int VEC = 4; };     // elements per 16 bytes
 template <> struct Elem<_Float16> { static constexpr int VEC = 8; };
 template <> struct Elem<bf16_t> { static constexpr int VEC = 8; };
+template <> struct Elem<int8_t> { static constexpr int VEC = 16; };
 
 // One matrix-core step consuming one 16-byte chunk of A and of B in each lane.
 template <typename E, int MF> struct MfmaOp;
@@ -107,6 +110,22 @@ template <> struct MfmaOp<float, 32> {
     }
 };
 
+// INT8: one instruction per 16-byte chunk (16 k per lane), exact INT32 sums.
+template <> struct MfmaOp<int8_t, 16> {
+    using Acc = i32x4;
+    static __device__ __forceinline__ void run(Acc& c, u32x4 a, u32x4 b) {
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                                  __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+    }
+};
+template <> struct MfmaOp<int8_t, 32> {
+    using Acc = i32x16;
+    static __device__ __forceinline__ void run(Acc& c, u32x4 a, u32x4 b) {
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                  __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+    }
+};
+
 // Accumulator element r of lane `lane` in an MF x MF block: (row, col) in the block.
 template <int MF> struct AccLayout;
 template <> struct AccLayout<16> {  // 4 rows per lane: rows 4g..4g+3 of column lane % 16
@@ -130,6 +149,7 @@ template <typename E> struct Scalar { using T = E; };
 template <> struct Scalar<bf16_t> { using T = uint16_t; };
 template <> struct Scalar<_Float16> { using T = uint16_t; };
 template <> struct Scalar<float> { using T = uint32_t; };
+template <> struct Scalar<int8_t> { using T = uint8_t; };
 
 // Loads the 16-byte chunk of VEC elements at (r, c0 .. c0+VEC-1) of a row-major
 // nrows x ncols matrix; out-of-range elements read as zero.
@@ -147,6 +167,10 @@ __device__ __forceinline__ u32x4 load_chunk_guarded(const E* __restrict__ base, 
     if constexpr (sizeof(S) == 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (c0 + e < ncols) ? ps[e] : 0u;
+    } else if constexpr (sizeof(S) == 1) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (c0 + e < ncols) v[e / 4] |= static_cast<uint32_t>(ps[e]) << (8 * (e % 4));
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -202,13 +226,21 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // is stored with k contiguous; otherwise with the BX side contiguous (loaded in
 // VEC x VEC blocks and transposed in registers).  VECOK: rows are 16-byte
 // aligned, so in-range chunks take one vector load.
+//
+// 8-bit elements (VEC = 16) not k-contiguous are staged in quarter blocks: a
+// work-item loads 4 k-rows of one 16-byte piece, transposes them as four 4 x 4
+// byte blocks and writes 4-byte column pieces, so every work-item takes one
+// quarter instead of a quarter of the work-items taking whole 16 x 16 blocks.
 template <typename E, int BX, int NT, bool KC, bool VECOK>
 struct Stage {
     static constexpr int VEC = Elem<E>::VEC, CH = 8;
-    static constexpr int UNITS = KC ? BX * CH : CH * (BX / VEC);  // chunks, or VEC x VEC blocks
+    static constexpr bool QUARTER = !KC && VEC == 16;
+    static constexpr int ROWS = KC ? 1 : QUARTER ? 4 : VEC;  // rows per staging unit
+    // chunks, VEC x VEC blocks, or quarter blocks
+    static constexpr int UNITS = KC ? BX * CH : QUARTER ? CH * (BX / VEC) * 4 : CH * (BX / VEC);
     static constexpr int PER = (UNITS + NT - 1) / NT;
     static_assert(BX % VEC == 0, "tile side must be whole chunks");
-    u32x4 r[PER][KC ? 1 : VEC];
+    u32x4 r[PER][ROWS];
 
     // Tile rows x0 .. x0+BX-1 (of ext) and k0 .. k0+BK-1 (of K); p and ld as stored.
     // fast: the tile lies inside the matrix, no guards needed.
@@ -222,6 +254,17 @@ struct Stage {
                 const int64_t gr = x0 + id / CH, gc = k0 + (id % CH) * VEC;
                 r[q][0] = (VECOK && fast) ? *reinterpret_cast<const u32x4*>(p + gr * ld + gc)
                                           : load_chunk_guarded<E, VECOK>(p, gr, gc, ext, K, ld);
+            } else if constexpr (QUARTER) {
+                // id -> piece across the row (fastest, for coalescing), quarter, k-block
+                const int xb = id % (BX / VEC), qq = (id / (BX / VEC)) % 4;
+                const int kb = id / (BX / VEC) / 4;
+                const int64_t gc = x0 + xb * VEC;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t gr = k0 + kb * VEC + 4 * qq + e;
+                    r[q][e] = (VECOK && fast) ? *reinterpret_cast<const u32x4*>(p + gr * ld + gc)
+                                              : load_chunk_guarded<E, VECOK>(p, gr, gc, K, ext, ld);
+                }
             } else {
                 const int64_t gc = x0 + (id % (BX / VEC)) * VEC;
 #pragma unroll
@@ -243,6 +286,29 @@ struct Stage {
             if constexpr (KC) {
                 const int row = id / CH, ch = id % CH;
                 img[row * CH + swz(row, ch)] = r[q][0];
+            } else if constexpr (QUARTER) {
+                const int xb = id % (BX / VEC), qq = (id / (BX / VEC)) % 4;
+                const int kb = id / (BX / VEC) / 4;
+                uint32_t* words = reinterpret_cast<uint32_t*>(img);
+#pragma unroll
+                for (int cw = 0; cw < 4; ++cw) {
+                    // 4 x 4 bytes: k-rows 4qq .. 4qq+3 of columns 16 xb + 4 cw .. + 3
+                    const uint32_t r0 = r[q][0][cw], r1 = r[q][1][cw];
+                    const uint32_t r2 = r[q][2][cw], r3 = r[q][3][cw];
+                    const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
+                    const uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
+                    const uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+                    const uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+                    const uint32_t col[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u),
+                                             __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                                             __builtin_amdgcn_perm(t3, t1, 0x05040100u),
+                                             __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int row = xb * VEC + 4 * cw + j;
+                        words[(row * CH + swz(row, kb)) * 4 + qq] = col[j];
+                    }
+                }
             } else {
                 const int xb = id % (BX / VEC), kb = id / (BX / VEC);
                 u32x4 t[VEC];
@@ -372,8 +438,12 @@ __global__ __launch_bounds__(Cfg::NT) void mfma_gemm_kernel(
 #pragma unroll
             for (int r = 0; r < L::R; ++r) {
                 const int64_t row = m0 + wm0 + i * MF + L::row(lane, r);
-                if (full_mn || (row < M && col < N))
-                    store_out<GEN>(out, row * out.ldc + col, acc[i][j][r]);
+                if (full_mn || (row < M && col < N)) {
+                    if constexpr (std::is_same<E, int8_t>::value)  // exact INT32 sums
+                        static_cast<int32_t*>(out.C)[row * out.ldc + col] = acc[i][j][r];
+                    else
+                        store_out<GEN>(out, row * out.ldc + col, acc[i][j][r]);
+                }
             }
         }
     }

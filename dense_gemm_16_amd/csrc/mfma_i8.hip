@@ -1,0 +1,40 @@
+// mfma_i8.hip -- INT8 inputs, exact INT32 sums, on the gfx950 integer matrix-core
+// instructions (v_mfma_i32_16x16x64_i8, v_mfma_i32_32x32x32_i8).
+//
+// The tiled matrix-unit algorithm of page "Tensor cores and matrix operations"
+// (section "Complete Algorithm for Large Matrix Multiply") on 8-bit operands:
+// the register-staged pipeline of mfma_gemm.hpp with 16-element (16-byte)
+// chunks, so a k-tile is 128 deep and one instruction consumes one chunk of A
+// and of B per lane (16 k).  Operands whose M or N side is contiguous (row-major
+// B, or A given transposed) are transposed in registers as 16 x 16 byte blocks.
+// Every product of two int8 values is at most 2^14 in magnitude, so a sum of at
+// most 2^17 - 1 of them is below 2^31 and the INT32 result is exact (the C ABI
+// limits K to 2^17 - 1 for this type); C is written as INT32.
+#include "mfma_gemm.hpp"
+
+namespace migemm {
+namespace {
+
+using I0 = MfmaCfg<int8_t, 256, 256, 2, 4, 16>;  // 8 waves, 128x64 per wave
+using I1 = MfmaCfg<int8_t, 128, 128, 2, 2, 16>;  // 4 waves, 64x64 per wave
+using I2 = MfmaCfg<int8_t, 64, 64, 2, 2, 16>;    // small problems: 4x the workgroups
+using I3 = MfmaCfg<int8_t, 256, 256, 2, 4, 32>;  // 8 waves, 32x32x32 instructions
+
+const char* const kNames[] = {"256x256x128 8w 16x16x64", "128x128x128 4w 16x16x64",
+                              "64x64x128 4w 16x16x64", "256x256x128 8w 32x32x32"};
+
+}  // namespace
+
+int mfma_i8_config_count() { return 4; }
+const char* mfma_i8_config_name(int c) { return (c >= 0 && c < 4) ? kNames[c] : nullptr; }
+
+hipError_t launch_mfma_i8(const GemmArgs& g, int config) {
+    switch (config) {
+        case 1: return launch_mfma_cfg<I1, false>(g);
+        case 2: return launch_mfma_cfg<I2, false>(g);
+        case 3: return launch_mfma_cfg<I3, false>(g);
+        default: return launch_mfma_cfg<I0, false>(g);
+    }
+}
+
+}  // namespace migemm

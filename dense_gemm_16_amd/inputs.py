@@ -18,6 +18,9 @@ Recipes (one CPU ``torch.Generator`` per draw, seeded; A is drawn before B):
   extended to rectangular shapes with the same row/col formula.
 * ``p1``: the modular pattern of page "04-wmma-matmul.cu" in flat index i:
   a = ((7 i + 1) mod 13)/13 - 0.5, b = ((5 i + 3) mod 11)/11 - 0.5.
+
+INT8 (``i8``) takes integers only: ``uniform`` is uniform over -128 .. 127 and
+``int`` over [lo, hi]; nothing is rounded.
 """
 from __future__ import annotations
 
@@ -26,9 +29,11 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+                "i8": torch.int8}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
+OUT_BYTES = {"f32": 4, "f16": 4, "bf16": 4, "i8": 4}  # C: FP32, or INT32 for INT8
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -40,6 +45,12 @@ def _gen(seed: int) -> torch.Generator:
 def draw(shape, dtype: str, dist: str, g: torch.Generator, lo: int = -4, hi: int = 4):
     """One matrix of ``shape`` in storage type ``dtype`` (CPU tensor)."""
     t = TORCH_DTYPES[dtype]
+    if dtype == "i8":
+        if dist == "uniform":
+            lo, hi = -128, 127
+        elif dist != "int":
+            raise ValueError(f"INT8 inputs take the uniform or int distributions, not {dist!r}")
+        return torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int32).to(torch.int8)
     if dist == "uniform":
         x = torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
     elif dist == "normal":
@@ -90,9 +101,10 @@ def with_ld(x: torch.Tensor, ld: int) -> torch.Tensor:
 
 
 def to_bits(x: torch.Tensor) -> np.ndarray:
-    """The stored encoding as numpy: float32 for FP32, raw uint16 bits for FP16/BF16."""
+    """The stored encoding as numpy: float32 for FP32, raw uint16 bits for FP16/BF16,
+    int8 for INT8."""
     x = x.detach().cpu()
-    if x.dtype == torch.float32:
+    if x.dtype in (torch.float32, torch.int8):
         return x.numpy()
     return x.view(torch.int16).numpy().view(np.uint16)
 
@@ -114,7 +126,7 @@ class Workload:
 
     def compulsory_bytes(self) -> int:
         e = ELEM_BYTES[self.dtype]
-        return e * (self.M * self.K + self.K * self.N) + 4 * self.M * self.N
+        return e * (self.M * self.K + self.K * self.N) + OUT_BYTES[self.dtype] * self.M * self.N
 
     def make(self):
         return pair(self.M, self.N, self.K, self.dtype, self.dist, self.seed)
@@ -131,4 +143,7 @@ WORKLOADS = {w.name: w for w in [
     Workload("c3r-f16-2050x2047x2056", 2050, 2047, 2056, "f16", "normal", 23),
     Workload("c4-bf16-8192", 8192, 8192, 8192, "bf16", "normal", 4),
     Workload("c4f-f32-4096", 4096, 4096, 4096, "f32", "uniform", 14),
+    # INT8 -> INT32 at the headline size (not one of the measured configurations of the
+    # pages; timed as an extra line)
+    Workload("i8-8192", 8192, 8192, 8192, "i8", "uniform", 5, exact=True),
 ]}

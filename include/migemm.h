@@ -53,7 +53,9 @@ extern "C" {
 typedef enum {
     MIGEMM_F32 = 0,
     MIGEMM_F16 = 1,  /* IEEE binary16 */
-    MIGEMM_BF16 = 2  /* bfloat16: the upper half of a binary32 word */
+    MIGEMM_BF16 = 2, /* bfloat16: the upper half of a binary32 word */
+    MIGEMM_I8 = 3,   /* 8-bit two's-complement integer (inputs of migemm_gemm_ex only) */
+    MIGEMM_I32 = 4   /* 32-bit integer (C of an INT8 product only) */
 } migemm_dtype;
 
 /*
@@ -102,6 +104,8 @@ typedef enum {
  *                        page "Tensor cores and matrix operations", section
  *                        "Complete Algorithm for Large Matrix Multiply").
  *                        FP16 and BF16 only.
+ *   MIGEMM_MFMA_I8       the same algorithm on INT8 operands with exact INT32
+ *                        sums (integer matrix-core instructions).  INT8 only.
  */
 typedef enum {
     MIGEMM_VARIANT_AUTO = -1,
@@ -109,7 +113,8 @@ typedef enum {
     MIGEMM_LDS_TILED = 1,
     MIGEMM_REGTILE_VALU = 2,
     MIGEMM_REGTILE_MFMA = 3,
-    MIGEMM_MFMA16 = 4
+    MIGEMM_MFMA16 = 4,
+    MIGEMM_MFMA_I8 = 5
 } migemm_variant;
 
 /*
@@ -153,6 +158,13 @@ int migemm_gemm_variant(int variant, int config,
  * dimension ldc (elements).  K == 0 gives C = beta * C_old (or 0).
  * Same pointer, stream, ownership and error rules as migemm_gemm; an unknown
  * c_dtype or op is MIGEMM_ERR_INVALID_ARG, and C must not overlap A or B.
+ *
+ * INT8 (the integer variant of the matrix-unit product; the pages reach it only
+ * through a link): dtype == MIGEMM_I8 takes c_dtype == MIGEMM_I32 and no other
+ * (and MIGEMM_I32 only goes with MIGEMM_I8): C = A B exactly, in 32-bit two's
+ * complement.  K is limited to 2^17 - 1, where no sum can overflow (each product
+ * is at most 2^14 in magnitude); larger K is MIGEMM_ERR_INVALID_ARG.  Only the plain
+ * product: alpha != 1 or beta != 0 is MIGEMM_ERR_UNSUPPORTED.
  * The selection depends on A, B, their layouts and the sizes only.
  * op_a == op_b == MIGEMM_OP_N with alpha == 1, beta == 0 and FP32 C is exactly
  * migemm_gemm.

@@ -38,17 +38,21 @@ def test_exports_are_c_symbols():
 
 
 def test_variant_registry():
-    assert mg.migemm_variant_count() == 5
-    names = [mg.migemm_variant_name(v) for v in range(5)]
-    assert names == ["naive", "lds_tiled", "regtile_valu", "regtile_mfma", "mfma16"]
-    assert mg.migemm_variant_name(5) is None and mg.migemm_variant_name(-1) is None
+    assert mg.migemm_variant_count() == 6
+    names = [mg.migemm_variant_name(v) for v in range(6)]
+    assert names == ["naive", "lds_tiled", "regtile_valu", "regtile_mfma", "mfma16", "mfma_i8"]
+    assert mg.migemm_variant_name(6) is None and mg.migemm_variant_name(-1) is None
     assert all(mg.migemm_variant_supports(mg.NAIVE, d) for d in (0, 1, 2))
+    assert mg.migemm_variant_supports(mg.MFMA_I8, mg.I8)
+    assert not any(mg.migemm_variant_supports(mg.MFMA_I8, d) for d in (0, 1, 2))
+    assert not any(mg.migemm_variant_supports(v, mg.I8) for v in range(5))
+    assert not mg.migemm_variant_supports(mg.NAIVE, mg.I32)
     for v in (mg.LDS_TILED, mg.REGTILE_VALU, mg.REGTILE_MFMA):
         assert mg.migemm_variant_supports(v, 0)
         assert not mg.migemm_variant_supports(v, 1) and not mg.migemm_variant_supports(v, 2)
     assert not mg.migemm_variant_supports(mg.MFMA16, 0)
     assert mg.migemm_variant_supports(mg.MFMA16, 1) and mg.migemm_variant_supports(mg.MFMA16, 2)
-    for v in range(5):
+    for v in range(6):
         n = mg.migemm_config_count(v)
         assert n >= 1
         assert all(mg.migemm_config_name(v, c) for c in range(n))
@@ -146,6 +150,29 @@ def test_convert_invalid_arguments(args):
 def test_convert_empty_is_a_noop():
     assert mg.migemm_convert(0, 1, 0, 10, None, 10, None, 10, None) == mg.OK
     assert mg.migemm_convert(2, 0, 5, 0, None, 1, None, 1, None) == mg.OK
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(c_dtype=0), "invalid"),            # INT8 inputs need INT32 C
+    (dict(dtype=1), "invalid"),              # INT32 C needs INT8 inputs
+    (dict(K=1 << 17, lda=1 << 17), "invalid"),  # 2^17 products of 2^14 reach 2^31
+    (dict(alpha=2.0), "unsupported"),        # INT32 C: plain product only
+    (dict(beta=1.0), "unsupported"),
+])
+def test_int8_argument_rules(args, status):
+    a = dict(M=8, N=16, K=64, dtype=3, A=P, lda=64, B=2 * P, ldb=16, alpha=1.0, beta=0.0,
+             c_dtype=4, C=3 * P, ldc=16)
+    a.update(args)
+    st = mg.migemm_gemm_ex(0, 0, a["M"], a["N"], a["K"], a["dtype"], a["A"], a["lda"], a["B"],
+                           a["ldb"], a["alpha"], a["beta"], a["c_dtype"], a["C"], a["ldc"], None)
+    assert st == {"invalid": mg.ERR_INVALID_ARG, "unsupported": mg.ERR_UNSUPPORTED}[status]
+
+
+def test_int8_selection():
+    st, v, c = mg.migemm_select(8192, 8192, 8192, mg.I8, None, 8192, None, 8192, None, 8192)
+    assert st == mg.OK and v == mg.MFMA_I8 and mg.migemm_config_name(v, c)
+    st, v, c = mg.migemm_select(64, 64, 64, mg.I8, None, 64, None, 64, None, 64)
+    assert st == mg.OK and v == mg.MFMA_I8
 
 
 def test_empty_output_is_a_noop():
