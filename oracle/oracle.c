@@ -29,9 +29,9 @@
  *   dtype 0  IEEE binary32: sign, 8-bit exponent (bias 127), 23-bit fraction
  *   dtype 1  IEEE binary16: sign, 5-bit exponent (bias 15), 10-bit fraction
  *   dtype 2  bfloat16: the upper 16 bits of a binary32 word
- *   dtype 3  8-bit two's-complement integer (-128 .. 127); every product and
- *            every sum of at most 2^17 of them is an integer below 2^31, exact
- *            in binary64
+ *   dtype 3  8-bit two's-complement integer (-128 .. 127); every product is
+ *            an integer of magnitude at most 2^14, so sums of up to 2^39 of
+ *            them are exact in binary64
  * All arrays are row-major with leading dimensions lda, ldb (in elements).
  * C and S are written densely with leading dimension N.
  *
