@@ -134,7 +134,7 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool a
     if (direct && tiles(256, 256) >= 256)
         config = 10;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads
     else if (direct)
-        config = 8;   // direct 128x128x64, 4 waves, 4 stages
+        config = 7;   // direct 128x128x64, 8 waves, 4 stages, interleaved
     else if (tiles(128, 128) >= 256)
         config = 2;   // register-staged 128x128x64
     else
