@@ -24,7 +24,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmigemm.so")
 # the two FP16/BF16 units first: they take longest
 SOURCES = ["mfma16.hip", "mfma16_general.hip", "mfma_i8.hip", "api.cpp", "naive.hip", "lds_tiled.hip",
-           "regtile_valu.hip", "regtile_mfma.hip", "fill.hip", "convert.hip"]
+           "regtile_valu.hip", "regtile_mfma.hip", "fill.hip", "convert.hip", "pack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

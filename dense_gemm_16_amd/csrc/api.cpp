@@ -4,7 +4,10 @@
 // The library's interface is a status-returning call in the manner of the
 // vendor GEMM call on page "matmul_registers.cu" (section on the library
 // comparison, where the status goes back to the caller rather than aborting):
-// nothing here prints, throws, exits, allocates or synchronises.
+// nothing here prints, throws or exits.  The one allocation is the workspace of
+// the packed FP16/BF16 configurations (pack.hip): a buffer per device, allocated
+// on first use and kept; a call that needs a larger one waits for the previous
+// user of the buffer before reallocating it, the only host-side wait.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -18,6 +21,9 @@ namespace {
 // a dimension below 2^31 times a leading dimension below 2^32.
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxLd = int64_t(1) << 32;
+// M * N * K from which a 16-bit product the direct kernel cannot read in place
+// is run on packed copies (pack.hip) rather than by the register-staged kernel.
+constexpr double kPackMinWork = 134217728.0;  // 2^27, e.g. 512^3
 
 struct Variant {
     const char* name;
@@ -129,12 +135,18 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool a
     // Direct global->LDS staging needs 16-byte aligned operands with leading
     // dimensions a multiple of 8 elements, K a multiple of 64, and N (row-major
     // B) or M (A given transposed) a multiple of 8; the launcher falls back to
-    // the register-staged kernel otherwise.
+    // the register-staged kernel otherwise.  Other operands are packed into
+    // zero-padded copies for the direct kernel once the product is large
+    // enough for the two extra copy launches to pay.
     const bool direct = aligned && K % 64 == 0 && (tb || N % 8 == 0) && (!ta || M % 8 == 0);
+    const double work = static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K);
+    const bool pack = work >= kPackMinWork && packed_k(K) < (int64_t(1) << 21);
     if (direct && tiles(256, 256) >= 256)
         config = 10;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads
     else if (direct)
         config = 7;   // direct 128x128x64, 8 waves, 4 stages, interleaved
+    else if (pack)
+        config = tiles(256, 256) >= 256 ? 11 : 12;  // packed copies, then config 10 or 7
     else if (tiles(128, 128) >= 256)
         config = 2;   // register-staged 128x128x64
     else

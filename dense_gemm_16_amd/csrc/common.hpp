@@ -140,6 +140,12 @@ hipError_t launch_lds_tiled(const GemmArgs& a, int config);
 hipError_t launch_regtile_valu(const GemmArgs& a, int config);
 hipError_t launch_regtile_mfma(const GemmArgs& a, int config);
 hipError_t launch_mfma16(const GemmArgs& a, int config);
+// Packs A and B into zero-padded k-contiguous copies (workspace from a
+// per-device stream-ordered pool) and runs mfma16 configuration inner_config on
+// them; runs fallback_config in place if no workspace can be had (pack.hip).
+hipError_t launch_packed16(const GemmArgs& a, int inner_config, int fallback_config);
+// K rounded up to the 64-k tile of the packed copies.
+int64_t packed_k(int64_t K);
 hipError_t launch_mfma_i8(const GemmArgs& a, int config);
 // K == 0: the sum of products is 0 for every element; applies the output step to it.
 hipError_t launch_empty_product(const GemmArgs& a);

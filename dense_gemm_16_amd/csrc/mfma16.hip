@@ -17,6 +17,9 @@
 //   dimensions in whole 16-byte chunks, K a multiple of the k-tile and N a
 //   multiple of 8.  A direct configuration asked to run where these do not hold
 //   runs the register-staged kernel with the nearest tile instead.
+// Configurations 11 and 12 (pack.hip) first copy A and B into zero-padded
+// k-contiguous images in a workspace, so that the direct kernel applies to any
+// layout, alignment and K.
 #include "mfma16_configs.hpp"
 
 namespace migemm {
@@ -33,7 +36,9 @@ const char* const kNames[] = {
     "direct 128x128x64 8w 16x16x32 s4 ilv",
     "direct 128x128x64 4w 16x16x32 s4",
     "direct 256x256x64 8w 32x32x16 gm4 ilv ntC",
-    "direct 256x256x64 8w 16x16x32 gm4 ilv ntC agpr early"};
+    "direct 256x256x64 8w 16x16x32 gm4 ilv ntC agpr early",
+    "packed: zero-padded copies, then config 10 as A x B^T",
+    "packed: zero-padded copies, then config 7 as A x B^T"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace
@@ -42,6 +47,10 @@ int mfma16_config_count() { return kCount; }
 const char* mfma16_config_name(int c) { return (c >= 0 && c < kCount) ? kNames[c] : nullptr; }
 
 hipError_t launch_mfma16(const GemmArgs& g, int config) {
+    if (config == 11 || config == 12) {
+        const int fallback = ceil_div(g.M, 128) * ceil_div(g.N, 128) >= 256 ? 2 : 3;
+        return launch_packed16(g, config == 11 ? 10 : 7, fallback);
+    }
     if (g.general()) return launch_mfma16_general(g, config);
     return g.dtype == 1 ? launch_typed<_Float16, false>(g, config)
                         : launch_typed<bf16_t, false>(g, config);

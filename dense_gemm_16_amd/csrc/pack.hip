@@ -1,0 +1,237 @@
+// pack.hip -- FP16/BF16 products whose operands the direct-staged kernel cannot
+// read in place: rows not in whole 16-byte chunks (an odd leading dimension, a
+// pointer off a 16-byte boundary), K not a multiple of the 64-k tile, or a
+// k-row image side (N of row-major B, M of A given transposed) not a multiple
+// of 8.
+//
+// The product C = A x B (page "CUDA-Practice 09", the definition of the
+// row-major product) is unchanged by padding the k sum with zeros: each extra
+// term is an exact zero product.  So each operand the direct kernel cannot read
+// in place is first copied into a workspace as a k-contiguous row image, A'
+// (M x K') or B' (N x K', that is B transposed), with K' = K rounded up to 64
+// and zero fill for k >= K; when K is not a multiple of 64 that is both.  The
+// direct kernel then multiplies the copies (and any operand left in place); it
+// clamps ragged M and N rows itself, and the output step writes C exactly as
+// for the unpacked call.
+//
+// The copy is memory-bound: 2 bytes read and 2 written per element copied,
+// small beside the product for the shapes this path is selected for.  One
+// launch copies both operands, a workgroup one 64 x 64 tile at a time, through
+// LDS so that the reads (2 bytes per lane, any alignment) and the writes (16
+// bytes per lane) are contiguous across a wavefront in either orientation.
+//
+// Workspace: at most (M + N) * K' * 2 bytes of one device buffer that the
+// library allocates on first use and keeps, growing it (after the previous
+// user has finished) when a call needs more.  Calls on one stream follow each
+// other in stream order; a call on another stream first waits for an event
+// recorded after the last product that used the buffer.  Host threads take
+// turns through a mutex.  If the buffer cannot be had, the product runs on the
+// register-staged kernel instead, which reads any layout in place.
+#include <mutex>
+
+#include "common.hpp"
+
+namespace migemm {
+namespace {
+
+constexpr int kTile = 64;
+
+// One operand copy: dst (rows x cols_out, leading dimension ldd, 16-byte
+// aligned rows) from src,
+//   dst[r][c] = src(r, c) for c < cols, 0 for cols <= c < cols_out,
+//   src(r, c) = trans ? src[c * lds + r] : src[r * lds + c].
+struct PackJob {
+    const uint16_t* src;
+    int64_t lds, rows, cols;
+    uint16_t* dst;
+    int64_t ldd, cols_out, tiles_c, tiles;
+    int trans;
+};
+
+// Workgroups stride over the 64 x 64 tiles of both jobs (job 0's tiles first).
+// Reads are 2-byte loads, a wavefront covering 128 contiguous source bytes
+// (any alignment); writes are 16-byte stores of 8 consecutive dst columns.
+__global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
+    __shared__ uint32_t tile[kTile][kTile + 1];
+    const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;   // reads: ty in 0..3
+    const int wx = threadIdx.x % 8, wy = threadIdx.x / 8;           // writes: wy in 0..31
+    const int64_t total = j0.tiles + j1.tiles;
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+        const bool second = t >= j0.tiles;
+        const PackJob& j = second ? j1 : j0;
+        const int64_t tt = second ? t - j0.tiles : t;
+        const int64_t r0 = (tt / j.tiles_c) * kTile, c0 = (tt % j.tiles_c) * kTile;
+        // tile[c - c0][r - r0] = src(r, c), zero outside the source.  Every
+        // load reads a clamped in-bounds address and the zero is selected
+        // afterwards, so the sixteen loads of a lane are in flight together.
+        uint32_t v[kTile / 4];
+        if (j.trans) {
+            const int64_t r = r0 + tx, rc = r < j.rows ? r : j.rows - 1;
+#pragma unroll
+            for (int i = 0; i < kTile / 4; ++i) {
+                const int64_t c = c0 + ty + 4 * i, cc = c < j.cols ? c : j.cols - 1;
+                v[i] = j.src[cc * j.lds + rc];
+            }
+#pragma unroll
+            for (int i = 0; i < kTile / 4; ++i) {
+                const bool in = r < j.rows && c0 + ty + 4 * i < j.cols;
+                tile[ty + 4 * i][tx] = in ? v[i] : 0u;
+            }
+        } else {
+            const int64_t c = c0 + tx, cc = c < j.cols ? c : j.cols - 1;
+#pragma unroll
+            for (int i = 0; i < kTile / 4; ++i) {
+                const int64_t r = r0 + ty + 4 * i, rc = r < j.rows ? r : j.rows - 1;
+                v[i] = j.src[rc * j.lds + cc];
+            }
+#pragma unroll
+            for (int i = 0; i < kTile / 4; ++i) {
+                const bool in = r0 + ty + 4 * i < j.rows && c < j.cols;
+                tile[tx][ty + 4 * i] = in ? v[i] : 0u;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kTile / 32; ++i) {
+            const int rr = wy + 32 * i;
+            const int64_t r = r0 + rr, c = c0 + 8 * wx;
+            if (r < j.rows && c < j.cols_out) {  // cols_out is a multiple of 8
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = tile[8 * wx + 2 * e][rr] | (tile[8 * wx + 2 * e + 1][rr] << 16);
+                *reinterpret_cast<u32x4*>(j.dst + r * j.ldd + c) = w;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+PackJob make_job(const void* src, int64_t lds, int64_t rows, int64_t cols, bool trans, void* dst,
+                 int64_t ldd, int64_t cols_out) {
+    PackJob j;
+    j.src = static_cast<const uint16_t*>(src);
+    j.lds = lds;
+    j.rows = rows;
+    j.cols = cols;
+    j.dst = static_cast<uint16_t*>(dst);
+    j.ldd = ldd;
+    j.cols_out = cols_out;
+    j.tiles_c = ceil_div(cols_out, kTile);
+    j.tiles = ceil_div(rows, kTile) * j.tiles_c;
+    j.trans = trans ? 1 : 0;
+    return j;
+}
+
+hipError_t launch_pack16(const PackJob& j0, const PackJob& j1, hipStream_t s) {
+    const int64_t tiles = j0.tiles + j1.tiles;
+    if (tiles == 0) return hipSuccess;
+    const unsigned grid = static_cast<unsigned>(tiles < 65536 ? tiles : 65536);
+    pack16_kernel<<<grid, 256, 0, s>>>(j0, j1);
+    return hipGetLastError();
+}
+
+// One workspace per device, kept until the process ends and only ever grown.
+// `last` is recorded on `last_stream` after each product that used it; a call
+// on another stream waits for it before its copy overwrites the workspace.
+struct Workspace {
+    void* ptr = nullptr;
+    size_t size = 0;
+    hipEvent_t last = nullptr;
+    hipStream_t last_stream = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mutex;
+Workspace g_ws[kMaxDevices];
+
+// Makes `w` at least `bytes` long, usable on stream s.  Growing waits for the
+// previous user to finish, frees the old block and allocates max(bytes, twice
+// the old size, 16 MiB).
+hipError_t reserve(Workspace& w, size_t bytes) {
+    if (!w.last) {
+        const hipError_t e = hipEventCreateWithFlags(&w.last, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            w.last = nullptr;
+            return e;
+        }
+    }
+    if (w.size >= bytes) return hipSuccess;
+    if (w.ptr) {
+        hipError_t e = hipEventSynchronize(w.last);
+        if (e == hipSuccess) e = hipFree(w.ptr);
+        if (e != hipSuccess) return e;
+        w.ptr = nullptr;
+        w.size = 0;
+    }
+    size_t want = bytes;
+    if (want < 2 * w.size) want = 2 * w.size;
+    if (want < (size_t(16) << 20)) want = size_t(16) << 20;
+    const hipError_t e = hipMalloc(&w.ptr, want);
+    if (e != hipSuccess) {
+        w.ptr = nullptr;
+        return e;
+    }
+    w.size = want;
+    return hipSuccess;
+}
+
+}  // namespace
+
+int64_t packed_k(int64_t K) { return ceil_div(K, 64) * 64; }
+
+hipError_t launch_packed16(const GemmArgs& g, int inner_config, int fallback_config) {
+    const int64_t Kp = packed_k(g.K);
+    // An operand the direct kernel reads in place is left where it is: a
+    // 16-byte aligned row image (row-major A, B given transposed) or k-row
+    // image (A given transposed, row-major B) with rows in whole 16-byte
+    // chunks, a k-row image side a multiple of 8, and K a multiple of 64.
+    const bool k_ok = g.K == Kp;
+    const bool a_in_place = k_ok && aligned16(g.A) && g.lda % 8 == 0 && (!g.ta || g.M % 8 == 0);
+    const bool b_in_place = k_ok && aligned16(g.B) && g.ldb % 8 == 0 && (g.tb || g.N % 8 == 0);
+    const int64_t a_bytes = a_in_place ? 0 : ((g.M * Kp * 2 + 255) / 256) * 256;
+    const int64_t b_bytes = b_in_place ? 0 : g.N * Kp * 2;
+    if (a_bytes + b_bytes == 0) return launch_mfma16(g, inner_config);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return launch_mfma16(g, fallback_config);
+    }
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& w = g_ws[dev];
+    if (reserve(w, static_cast<size_t>(a_bytes + b_bytes)) != hipSuccess) {
+        (void)hipGetLastError();  // clear the failed call's error; run in place instead
+        return launch_mfma16(g, fallback_config);
+    }
+    if (w.last_stream != g.stream) {
+        const hipError_t e = hipStreamWaitEvent(g.stream, w.last, 0);
+        if (e != hipSuccess) return e;
+    }
+    char* const wa = static_cast<char*>(w.ptr);  // hipMalloc: 256-byte aligned
+    char* const wb = wa + a_bytes;
+    // A' (M x K'): row-major A is copied, A given transposed (K x M) is transposed.
+    // B' (N x K'): row-major B (K x N) is transposed, B given transposed is copied.
+    const PackJob none = make_job(nullptr, 1, 0, 0, false, nullptr, 8, 8);
+    const PackJob ja = a_in_place ? none : make_job(g.A, g.lda, g.M, g.K, g.ta, wa, Kp, Kp);
+    const PackJob jb = b_in_place ? none : make_job(g.B, g.ldb, g.N, g.K, !g.tb, wb, Kp, Kp);
+    hipError_t e = launch_pack16(ja, jb, g.stream);
+    if (e == hipSuccess) {
+        GemmArgs p = g;
+        p.K = Kp;
+        if (!a_in_place) {
+            p.ta = false;
+            p.A = wa;
+            p.lda = Kp;
+        }
+        if (!b_in_place) {
+            p.tb = true;
+            p.B = wb;
+            p.ldb = Kp;
+        }
+        e = launch_mfma16(p, inner_config);
+    }
+    const hipError_t r = hipEventRecord(w.last, g.stream);
+    w.last_stream = g.stream;
+    return e != hipSuccess ? e : r;
+}
+
+}  // namespace migemm

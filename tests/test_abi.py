@@ -205,6 +205,21 @@ def test_selection_is_deterministic_and_valid():
     assert st == mg.ERR_INVALID_ARG
 
 
+def test_selection_packs_unreadable_16bit_operands():
+    """FP16/BF16 operands the direct kernel cannot read in place (K not a
+    multiple of 64, an odd leading dimension) go to the packed configurations
+    once the product is large enough; small ones stay on the register-staged
+    kernel, and aligned ones on the direct kernel."""
+    sel = lambda M, N, K, dt, lda, ldb: mg.migemm_select(M, N, K, dt, None, lda, None, ldb, None, N)
+    assert sel(2050, 2047, 2056, 1, 2056, 2047) == (mg.OK, mg.MFMA16, 12)
+    assert sel(8192, 8192, 8200, 2, 8200, 8192) == (mg.OK, mg.MFMA16, 11)
+    assert sel(4096, 4096, 4096, 2, 4096, 4097) == (mg.OK, mg.MFMA16, 11)
+    assert sel(2048, 2048, 2048, 2, 2048, 2048) == (mg.OK, mg.MFMA16, 7)
+    assert sel(8192, 8192, 8192, 2, 8192, 8192) == (mg.OK, mg.MFMA16, 10)
+    assert sel(100, 100, 100, 1, 100, 100) == (mg.OK, mg.MFMA16, 3)
+    assert sel(2048, 2048, 2048, 0, 2049, 2048)[1] == mg.REGTILE_MFMA
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(mg, "_lib", None)
     monkeypatch.setattr(mg, "LIBRARY_PATH", str(tmp_path / "absent.so"))

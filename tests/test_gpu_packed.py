@@ -1,0 +1,137 @@
+"""The packed FP16/BF16 path (mfma16 configurations 11 and 12): A and B are
+copied into zero-padded k-contiguous images in a workspace and the direct
+kernel multiplies those as A x B^T.
+
+Checked against the oracle: K not a multiple of the 64-k tile (down to K = 1),
+odd leading dimensions and operands that start off a 16-byte boundary (the
+operand buffers are NaN-filled around each window, so a read outside an operand
+shows up in C), all four storage layouts, the general output step, exact
+integer inputs, the automatic selection for shapes that need packing, and calls
+on two streams with workspaces of changing size.
+"""
+import pytest
+import torch
+
+import dense_gemm_16_amd as mg
+from dense_gemm_16_amd import inputs
+from gpu_helpers import (DT_CODE, check_ex, oracle_ref, padding_untouched, run_gemm_ex, say,
+                         to_device_with_ld)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
+PACKED = [11, 12]
+
+
+def _name(ta, tb):
+    return ("T" if ta else "N") + ("T" if tb else "N")
+
+
+def test_packed_configs_named():
+    for c in PACKED:
+        assert mg.migemm_config_name(mg.MFMA16, c).startswith("packed")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_packed_ragged_k_every_layout(dtype, ta, tb):
+    for (M, N, K) in [(1, 1, 1), (7, 9, 5), (130, 97, 65), (300, 264, 200), (257, 513, 130)]:
+        A, B = inputs.pair(M, N, K, dtype, "normal", seed=M + 2 * N + 3 * K + 5 * ta + 7 * tb)
+        ref = oracle_ref(A, B, dtype)
+        for c in PACKED:
+            say(f"packed {_name(ta, tb)} {dtype} {M}x{N}x{K} cfg={c}")
+            C, _, _ = run_gemm_ex(A, B, dtype, 1.0, 0.0, 0, None, variant=mg.MFMA16, config=c,
+                                  ta=ta, tb=tb)
+            check_ex(C, A, B, dtype, 1.0, 0.0, 0, None, ref=ref)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_packed_odd_ld_and_misaligned(ta, tb):
+    M, N, K = 203, 170, 301
+    for dtype in ("f16", "bf16"):
+        A, B = inputs.pair(M, N, K, dtype, "normal", seed=31 + ta + 2 * tb)
+        ref = oracle_ref(A, B, dtype)
+        lda = (M if ta else K) + 3
+        ldb = (K if tb else N) + 5
+        for a_off, b_off in ((1, 3), (0, 1), (7, 0)):
+            for c in PACKED:
+                say(f"packed odd-ld {_name(ta, tb)} {dtype} offs={a_off},{b_off} cfg={c}")
+                C, _, _ = run_gemm_ex(A, B, dtype, 1.0, 0.0, 0, None, variant=mg.MFMA16,
+                                      config=c, ta=ta, tb=tb, lda=lda, ldb=ldb, a_off=a_off,
+                                      b_off=b_off)
+                check_ex(C, A, B, dtype, 1.0, 0.0, 0, None, ref=ref)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_packed_general_output(dtype):
+    M, N, K = 190, 321, 77
+    A, B = inputs.pair(M, N, K, dtype, "normal", seed=8)
+    ref = oracle_ref(A, B, dtype)
+    for c_code in (0, 1, 2):
+        old = (torch.rand((M, N), generator=torch.Generator().manual_seed(c_code)) - 0.5).to(
+            {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[c_code])
+        for ta, tb in LAYOUTS:
+            for c in PACKED:
+                say(f"packed general {_name(ta, tb)} {dtype} c_dtype={c_code} cfg={c}")
+                C, buf, mask = run_gemm_ex(A, B, dtype, -1.5, 0.75, c_code, old,
+                                           variant=mg.MFMA16, config=c, ta=ta, tb=tb,
+                                           ldc=N + 3, c_off=1)
+                check_ex(C, A, B, dtype, -1.5, 0.75, c_code, old, ref=ref)
+                assert padding_untouched(buf, mask)
+
+
+def test_packed_integer_inputs_exact():
+    M, N, K = 150, 90, 1000
+    for dtype in ("f16", "bf16"):
+        A, B = inputs.pair(M, N, K, dtype, "int", seed=12)
+        ref = oracle_ref(A, B, dtype)
+        for ta, tb in LAYOUTS:
+            for c in PACKED:
+                say(f"packed int {_name(ta, tb)} {dtype} cfg={c}")
+                C, _, _ = run_gemm_ex(A, B, dtype, 1.0, 0.0, 0, None, variant=mg.MFMA16,
+                                      config=c, ta=ta, tb=tb, lda=(M if ta else K) + 1)
+                check_ex(C, A, B, dtype, 1.0, 0.0, 0, None, ref=ref, exact=True)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_auto_selects_packing_where_needed(ta, tb):
+    """K = 1000 (not a multiple of 64) and an odd leading dimension: the
+    selection takes a packed configuration, and the result matches."""
+    M, N, K = 600, 520, 1000
+    st, v, c = mg.migemm_select(M, N, K, 1, None, K, None, N + 1, None, N)
+    assert st == mg.OK and v == mg.MFMA16 and c in PACKED
+    A, B = inputs.pair(M, N, K, "f16", "normal", seed=44 + ta + 2 * tb)
+    ref = oracle_ref(A, B, "f16")
+    say(f"packed auto {_name(ta, tb)} {M}x{N}x{K}")
+    C, _, _ = run_gemm_ex(A, B, "f16", 1.0, 0.0, 0, None, ta=ta, tb=tb,
+                          ldb=(K if tb else N) + 1)
+    check_ex(C, A, B, "f16", 1.0, 0.0, 0, None, ref=ref)
+
+
+def test_packed_two_streams_changing_workspace():
+    """Calls alternating between two streams, workspaces growing and shrinking,
+    launched back to back and checked after one synchronisation."""
+    shapes = [(64, 72, 130), (700, 300, 513), (33, 40, 9), (512, 640, 1001), (120, 8, 70),
+              (900, 257, 333)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runs = []
+    for i, (M, N, K) in enumerate(shapes):
+        dtype = ("f16", "bf16")[i % 2]
+        A, B = inputs.pair(M, N, K, dtype, "normal", seed=100 + i)
+        dA, _ = to_device_with_ld(A, K + 1, 1)
+        dB, _ = to_device_with_ld(B, N + 1, 1)
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        runs.append((A, B, dtype, dA, dB, C, K + 1, N + 1))
+    torch.cuda.synchronize()
+    for i, (A, B, dtype, dA, dB, C, lda, ldb) in enumerate(runs):
+        M, K = A.shape
+        N = B.shape[1]
+        s = streams[i % 2]
+        say(f"packed stream {i % 2} {dtype} {M}x{N}x{K}")
+        st = mg.migemm_gemm_ex_variant(mg.MFMA16, PACKED[i % 2], 0, 0, M, N, K, DT_CODE[dtype],
+                                       dA.data_ptr(), lda, dB.data_ptr(), ldb, 1.0, 0.0, 0,
+                                       C.data_ptr(), N, s.cuda_stream)
+        assert st == mg.OK
+    torch.cuda.synchronize()
+    for (A, B, dtype, dA, dB, C, lda, ldb) in runs:
+        check_ex(C.cpu(), A, B, dtype, 1.0, 0.0, 0, None)
