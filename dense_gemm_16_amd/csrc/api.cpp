@@ -290,6 +290,6 @@ const char* migemm_status_string(int status) {
 
 int migemm_last_hip_error(void) { return g_last_hip_error; }
 
-int migemm_version(void) { return 400; }
+int migemm_version(void) { return 500; }
 
 }  // extern "C"

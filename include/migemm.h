@@ -24,13 +24,25 @@
  * leading dimensions that are multiples of 16 bytes take the vector-load path.
  *
  * Pointers.  A, B and C are DEVICE pointers on the current HIP device, owned
- * by the caller.  The library allocates no memory, keeps no pointer after a
- * call returns, and has no mutable global state, so calls are reentrant and
- * may come from several host threads.  C must not overlap A or B.
+ * by the caller.  The library keeps no pointer of the caller's after a call
+ * returns.  Calls are reentrant and may come from several host threads.  C
+ * must not overlap A or B.
+ *
+ * Workspace.  FP16/BF16 operands that the direct-staged kernel cannot read in
+ * place (K not a multiple of 64, rows not 16-byte aligned in whole 16-byte
+ * chunks, a k-row image side not a multiple of 8) are, for large products,
+ * first copied into zero-padded k-contiguous images (mfma16 configurations 11
+ * and 12).  The copies live in one device buffer per device that the library
+ * allocates on first use and keeps until the process ends; it grows (at least
+ * doubling) when a call needs more.  Calls on different streams that use it
+ * are ordered through an event; host threads take turns through a mutex.  If
+ * the buffer cannot be allocated, the product runs in place on the
+ * register-staged kernel.  No other path allocates device memory.
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
- * stream).  Work is enqueued asynchronously on it; the library never
- * synchronises.  The caller synchronises before reading C.
+ * stream).  Work is enqueued asynchronously on it.  The only host-side wait
+ * is a workspace growth, which waits for the previous product that used the
+ * buffer before freeing it.  The caller synchronises before reading C.
  *
  * Errors.  Every entry point returns a migemm_status; nothing prints, throws
  * or exits.  Argument errors are detected before any HIP call.  Degenerate
