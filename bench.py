@@ -157,10 +157,15 @@ def cpu_baseline(p, seconds):
     bA, bB = inputs.to_bits(p.A), inputs.to_bits(p.B)
     thr = oracle.default_threads()
     used = oracle.threads_used(thr)
+    # Two calibration passes: a few rows, then about an eighth of the budget
+    # (the first pass alone overstates the per-row time: fixed costs dominate it).
     r0 = max(used, 8)
-    t = time.perf_counter()
-    oracle.gemm(bA[:r0], bB, p.code, nthreads=thr)
-    t_cal = time.perf_counter() - t
+    for frac in (None, 0.125):
+        if frac is not None:
+            r0 = int(min(w.M, max(r0, r0 * seconds * frac / max(t_cal, 1e-3))))
+        t = time.perf_counter()
+        oracle.gemm(bA[:r0], bB, p.code, nthreads=thr)
+        t_cal = time.perf_counter() - t
     rows = int(min(w.M, max(r0, r0 * seconds / max(t_cal, 1e-3))))
     rows = max(used, (rows // used) * used) if rows >= used else rows
     log(f"cpu_baseline: calibration {r0} rows in {t_cal:.2f}s -> sample {rows} rows")
