@@ -38,7 +38,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3,
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EXTRA = ["c1-f32-1024", "c1-f32-1024-int", "c2-f16-1024", "c3-f16-2048", "c3-bf16-2048",
-         "c3r-f16-2050x2047x2056", "c4f-f32-4096"]
+         "c3r-f16-2050x2047x2056", "c4f-f32-4096", "s8-bf16-1024x8192x8192",
+         "s2x4-bf16-4096x2048x8192"]
 
 
 def log(msg):

@@ -38,7 +38,8 @@ const char* const kNames[] = {
     "direct 256x256x64 8w 32x32x16 gm4 ilv ntC",
     "direct 256x256x64 8w 16x16x32 gm4 ilv ntC agpr early",
     "packed: zero-padded copies, then config 10 as A x B^T",
-    "packed: zero-padded copies, then config 7 as A x B^T"};
+    "packed: zero-padded copies, then config 7 as A x B^T",
+    "direct 128x256x64 8w 16x16x32 s3 ilv"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace

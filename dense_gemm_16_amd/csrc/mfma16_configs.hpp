@@ -23,6 +23,7 @@ template <typename E> struct Cfgs {
     using D8 = DirectCfg<E, 128, 128, 2, 2, 16, 4, 64>;             // 4 waves, 4 stages
     using D9 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 2>;    // gm4, interleave, nt C
     using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 30>;  // + AGPRs, early loads; all layouts
+    using D13 = DirectCfg<E, 128, 256, 2, 4, 16, 3, 64, 8, 2, 16>;  // 8 waves of 64x64, 3 stages; all layouts
 };
 
 template <class D, class Fallback, bool GEN>
@@ -49,6 +50,7 @@ hipError_t launch_typed(const GemmArgs& g, int config) {
         case 8: return direct_or<typename T::D8, typename T::R2, GEN>(g);
         case 9: return direct_or<typename T::D9, typename T::R0, GEN>(g);
         case 10: return direct_or<typename T::D10, typename T::R0, GEN>(g);
+        case 13: return direct_or<typename T::D13, typename T::R2, GEN>(g);
         default: return launch_mfma_cfg<typename T::R0, GEN>(g);
     }
 }

@@ -146,4 +146,8 @@ WORKLOADS = {w.name: w for w in [
     # INT8 -> INT32 at the headline size (not one of the measured configurations of the
     # pages; timed as an extra line)
     Workload("i8-8192", 8192, 8192, 8192, "i8", "uniform", 5, exact=True),
+    # one GPU's share of the 8192^3 BF16 product split over rows of C across 8 GPUs,
+    # and over a 2 x 4 grid of (rows, columns) (timed as extra lines)
+    Workload("s8-bf16-1024x8192x8192", 1024, 8192, 8192, "bf16", "normal", 6),
+    Workload("s2x4-bf16-4096x2048x8192", 4096, 2048, 8192, "bf16", "normal", 7),
 ]}

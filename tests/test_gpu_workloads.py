@@ -31,7 +31,8 @@ def test_workload_full_compare(name):
     check(C, A, B, w.dtype, exact=w.exact)
 
 
-@pytest.mark.parametrize("name", ["c4-bf16-8192", "c4f-f32-4096"])
+@pytest.mark.parametrize("name", ["c4-bf16-8192", "c4f-f32-4096", "s8-bf16-1024x8192x8192",
+                                  "s2x4-bf16-4096x2048x8192"])
 def test_workload_large_sampled(name):
     w = inputs.WORKLOADS[name]
     A, B = w.make()
