@@ -141,14 +141,17 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool a
     const bool direct = aligned && K % 64 == 0 && (tb || N % 8 == 0) && (!ta || M % 8 == 0);
     const double work = static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K);
     const bool pack = work >= kPackMinWork && packed_k(K) < (int64_t(1) << 21);
-    if (direct && tiles(256, 256) >= 256)
+    const bool whole256 = M % 256 == 0 && N % 256 == 0;
+    if (direct && tiles(256, 256) >= 256 && whole256)
+        config = 14;  // direct 256x256x64, ping-pong wave groups (whole tiles only)
+    else if (direct && tiles(256, 256) >= 256)
         config = 10;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads
     else if (direct && tiles(128, 256) >= 256)
         config = 13;  // direct 128x256x64, 8 waves of 64x64, 3 stages (e.g. 1024x8192, 4096x2048)
     else if (direct)
         config = 7;   // direct 128x128x64, 8 waves, 4 stages, interleaved
     else if (pack)
-        config = tiles(256, 256) >= 256 ? 11 : 12;  // packed copies, then config 10 or 7
+        config = tiles(256, 256) >= 256 ? 11 : 12;  // packed copies, then config 14/10 or 7
     else if (tiles(128, 128) >= 256)
         config = 2;   // register-staged 128x128x64
     else

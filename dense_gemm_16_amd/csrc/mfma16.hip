@@ -37,9 +37,10 @@ const char* const kNames[] = {
     "direct 128x128x64 4w 16x16x32 s4",
     "direct 256x256x64 8w 32x32x16 gm4 ilv ntC",
     "direct 256x256x64 8w 16x16x32 gm4 ilv ntC agpr early",
-    "packed: zero-padded copies, then config 10 as A x B^T",
+    "packed: zero-padded copies, then config 14 (whole tiles) or 10 as A x B^T",
     "packed: zero-padded copies, then config 7 as A x B^T",
-    "direct 128x256x64 8w 16x16x32 s3 ilv"};
+    "direct 128x256x64 8w 16x16x32 s3 ilv",
+    "direct 256x256x64 8w 16x16x32 gm4 pingpong ntC agpr"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace
@@ -50,7 +51,8 @@ const char* mfma16_config_name(int c) { return (c >= 0 && c < kCount) ? kNames[c
 hipError_t launch_mfma16(const GemmArgs& g, int config) {
     if (config == 11 || config == 12) {
         const int fallback = ceil_div(g.M, 128) * ceil_div(g.N, 128) >= 256 ? 2 : 3;
-        return launch_packed16(g, config == 11 ? 10 : 7, fallback);
+        const bool whole256 = g.M % 256 == 0 && g.N % 256 == 0;
+        return launch_packed16(g, config == 11 ? (whole256 ? 14 : 10) : 7, fallback);
     }
     if (g.general()) return launch_mfma16_general(g, config);
     return g.dtype == 1 ? launch_typed<_Float16, false>(g, config)

@@ -24,12 +24,12 @@ template <typename E> struct Cfgs {
     using D9 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 2>;    // gm4, interleave, nt C
     using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 30>;  // + AGPRs, early loads; all layouts
     using D13 = DirectCfg<E, 128, 256, 2, 4, 16, 3, 64, 8, 2, 16>;  // 8 waves of 64x64, 3 stages; all layouts
+    using D14 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 22>;  // ping-pong (whole tiles), AGPRs, nt C; all layouts
 };
 
 template <class D, class Fallback, bool GEN>
 hipError_t direct_or(const GemmArgs& g) {
-    return direct_ok(g, D::BK, D::LAYOUTS) ? launch_direct_cfg<D, GEN>(g)
-                                           : launch_mfma_cfg<Fallback, GEN>(g);
+    return direct_fits<D>(g) ? launch_direct_cfg<D, GEN>(g) : launch_mfma_cfg<Fallback, GEN>(g);
 }
 
 // Configuration `config` of the table (indices as named in mfma16.hip).  A
@@ -51,6 +51,7 @@ hipError_t launch_typed(const GemmArgs& g, int config) {
         case 9: return direct_or<typename T::D9, typename T::R0, GEN>(g);
         case 10: return direct_or<typename T::D10, typename T::R0, GEN>(g);
         case 13: return direct_or<typename T::D13, typename T::R2, GEN>(g);
+        case 14: return direct_or<typename T::D14, typename T::R0, GEN>(g);
         default: return launch_mfma_cfg<typename T::R0, GEN>(g);
     }
 }

@@ -67,7 +67,11 @@ namespace migemm {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // SCHED: 0 = a slab's LDS reads as one block, then its matrix instructions;
-// 2 = one LDS read issued after each matrix instruction (sched_group_barrier).
+// 2 = one LDS read issued after each matrix instruction (sched_group_barrier);
+// 4 = ping-pong: the two waves on each SIMD take turns, one issuing a whole
+// k-tile of matrix instructions while the other reads its next k-tile of
+// fragments (and, for the first group, issues the direct loads), with a
+// barrier at each turn.
 // FLAGS: bit 1 = non-temporal C stores; bit 2 = keep the accumulators in AGPRs
 // (see below); bit 3 = issue a k-tile's direct loads right after the barrier
 // that frees their stage instead of at the start of the next k-tile, so they
@@ -85,10 +89,23 @@ struct DirectCfg {
     static constexpr int STAGE_A = BM * BK * 2, STAGE_B = BK * BN * 2;
     static constexpr int STAGE_BYTES = STAGE_A + STAGE_B;
     static constexpr bool LAYOUTS = (FLAGS & 16) != 0;
+    // LDS placement.  Stage s of the other schedules is [A | B] at s * STAGE_BYTES.
+    // Ping-pong keeps three B stages and two A stages: [B0 | B1 | B2 | A0 | A1].
+    // B goes first so that a B fragment's slab and half offsets (up to 18 KiB)
+    // stay within the 16-bit offset field of the LDS reads.
+    static constexpr int LDS_BYTES = SCHED == 4 ? 2 * STAGE_A + 3 * STAGE_B : STAGES * STAGE_BYTES;
+    __device__ static int a_stage(int kt) {
+        return SCHED == 4 ? 3 * STAGE_B + (kt & 1) * STAGE_A : (kt % STAGES) * STAGE_BYTES;
+    }
+    __device__ static int b_stage(int kt) {
+        return SCHED == 4 ? (kt % 3) * STAGE_B : (kt % STAGES) * STAGE_BYTES + STAGE_A;
+    }
     static_assert(sizeof(E) == 2, "16-bit inputs only");
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "whole blocks per wave");
-    static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "stages fit 160 KiB");
-    static_assert(SCHED == 0 || SCHED == 2, "scheduling policy 0 or 2");
+    static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "stages fit 160 KiB");
+    static_assert(SCHED == 0 || SCHED == 2 || SCHED == 4, "scheduling policy 0, 2 or 4");
+    static_assert(SCHED != 4 || (WM == 2 && WN == 4 && STAGES == 2 && (FLAGS & 8) == 0),
+                  "ping-pong: two groups of four waves, two stages, no early-load flag");
     static_assert((FLAGS & ~30) == 0, "flags: bits 1 to 4");
 };
 
@@ -127,30 +144,43 @@ __device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) | ((krow >> 
 // Rows past the operand's extent `ext` (row image) and chunks past it (k-row
 // image) are clamped, keeping every load in bounds.
 template <class O>
+__device__ __forceinline__ uint32_t direct_offset(int q, int wave, int lane, int nw, int64_t x0,
+                                                  int64_t ext, int64_t ld) {
+    const int r = O::RPI * (wave + q * nw) + lane / O::CH;
+    if constexpr (O::ROWS) {
+        const int chunk = (lane % O::CH) ^ swz_a<O::CH>(r);
+        const int64_t gr = min(x0 + r, ext - 1);
+        return static_cast<uint32_t>(((gr - x0) * ld + chunk * 8) * 2);
+    } else {
+        const int chunk = (lane % O::CH) ^ swz_b(r);
+        const int64_t gc = min(x0 + chunk * 8, ext - 8);
+        return static_cast<uint32_t>((r * ld + (gc - x0)) * 2);
+    }
+}
+template <class O>
 __device__ __forceinline__ void direct_offsets(uint32_t (&voff)[O::PER], int wave, int lane, int nw,
                                                int64_t x0, int64_t ext, int64_t ld) {
 #pragma unroll
-    for (int q = 0; q < O::PER; ++q) {
-        const int r = O::RPI * (wave + q * nw) + lane / O::CH;
-        if constexpr (O::ROWS) {
-            const int chunk = (lane % O::CH) ^ swz_a<O::CH>(r);
-            const int64_t gr = min(x0 + r, ext - 1);
-            voff[q] = static_cast<uint32_t>(((gr - x0) * ld + chunk * 8) * 2);
-        } else {
-            const int chunk = (lane % O::CH) ^ swz_b(r);
-            const int64_t gc = min(x0 + chunk * 8, ext - 8);
-            voff[q] = static_cast<uint32_t>((r * ld + (gc - x0)) * 2);
-        }
-    }
+    for (int q = 0; q < O::PER; ++q) voff[q] = direct_offset<O>(q, wave, lane, nw, x0, ext, ld);
+}
+
+// A wave-uniform address, moved to scalar registers (the direct loads take
+// their base from an SGPR pair).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // 16 bytes per lane from global memory (SGPR base + per-lane byte offset) into
 // LDS at lds_base + 16 * lane.  M0 carries the LDS base; nothing else in these
-// kernels uses M0.
+// kernels uses M0.  The base is wave-uniform by construction; passing it through
+// uniform_ptr keeps the compiler from handing the asm a VGPR copy of it.
 __device__ __forceinline__ void dma16(uint32_t lds_base, const void* sbase, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds_base), "v"(voff), "s"(sbase)
+                 : "s"(lds_base), "v"(voff), "s"(uniform_ptr(sbase))
                  : "memory");
 }
 
@@ -191,7 +221,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     using Acc = typename Op::Acc;
     using L = AccLayout<MF>;
 
-    __shared__ __attribute__((aligned(1024))) char smem[S * Cfg::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS_BYTES];
     // __shared__ arrays are generic pointers in HIP; an LDS pointer needs a C-style cast.
     const MIGEMM_LDS char* const lds = (const MIGEMM_LDS char*)smem;
     const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
@@ -256,36 +286,53 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     const int bcol = (MF == 16 ? 0 : 16 * ((lane % 32) / 16)) + 4 * (bj % 4);
 
     // Fragment `t` (block t of the wave tile starting at w0) of slab s from the
-    // image `img` of a BX-wide operand.
+    // image `img` of a BX-wide operand.  Each address is written as the image
+    // base, plus a per-lane part that stays the same for the whole loop, plus
+    // a constant, so the compiler keeps a few per-lane offsets in registers and
+    // folds the rest into instruction offsets:
+    //  * row image: w0 + t MF is a multiple of 16 and the swizzle depends on
+    //    row % 16 only, so the fragment's chunk is fixed by the lane and the
+    //    slab, and t only adds t MF rows;
+    //  * k-row image: the swizzle depends on k-row bits 0, 1 and 3, which come
+    //    from the lane alone (8 ag + bj / 4); the slab and half add whole
+    //    k-rows; and with a power-of-two fragment count t sets column-chunk
+    //    bits that nothing else sets, so it XORs the chunk index with t MF / 8.
     auto read_row_image = [&](const MIGEMM_LDS char* img, int w0, int t, int s)
         __attribute__((always_inline)) {
         constexpr int CA = BK / 8;
-        const int row = w0 + t * MF + ar;
-        const int chunk = (s * G + ag) ^ swz_a<CA>(row);
-        return *(const MIGEMM_LDS u32x4*)(img + row * (CA * 16) + chunk * 16);
+        const int chunk = (s * G + ag) ^ swz_a<CA>(ar);
+        const int lane_off = (w0 + ar) * (CA * 16) + chunk * 16;
+        return *(const MIGEMM_LDS u32x4*)(img + lane_off + t * MF * (CA * 16));
     };
     auto read_krow_image = [&](const MIGEMM_LDS char* img, int bx, int w0, int t, int s)
         __attribute__((always_inline)) {
-        const int col = w0 + t * MF + bcol;
+        const int klane = 8 * ag + bj / 4;
+        const int c0 = ((w0 + bcol) / 8) ^ swz_b(klane);
+        const int lane_off = klane * (bx * 2) + ((c0 ^ (t * MF / 8)) * 16) + (bcol % 8) * 2;
         u32x2 h[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const int krow = s * SLAB_K + 8 * ag + 4 * half + bj / 4;
-            const int chunk = (col / 8) ^ swz_b(krow);
-            const MIGEMM_LDS char* p = img + krow * (bx * 2) + chunk * 16 + (col % 8) * 2;
+            const MIGEMM_LDS char* p = img + lane_off + (s * SLAB_K + 4 * half) * (bx * 2);
             h[half] = __builtin_bit_cast(
                 u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS s16x4*)p));
         }
         return u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
     };
+    static_assert((TA ? (TM & (TM - 1)) : 0) == 0 && (TB ? 0 : (TN & (TN - 1))) == 0,
+                  "k-row images need a power-of-two fragment count per wave");
 
     struct Frags {
         u32x4 a[TM];
         u32x4 b[TN];
     };
     auto load_frags = [&](int kt, int s, Frags& f) __attribute__((always_inline)) {
-        const MIGEMM_LDS char* sa = lds + (kt % S) * Cfg::STAGE_BYTES;
-        const MIGEMM_LDS char* sb = sa + Cfg::STAGE_A;
+        // The stage offsets pass through an empty asm statement: otherwise loop
+        // strength reduction turns every fragment address into an induction
+        // variable of its own, and those registers spill.
+        int a_off = Cfg::a_stage(kt), b_off = Cfg::b_stage(kt);
+        asm("" : "+s"(a_off), "+s"(b_off));
+        const MIGEMM_LDS char* sa = lds + a_off;
+        const MIGEMM_LDS char* sb = lds + b_off;
         auto read_a = [&](int i) __attribute__((always_inline)) {
             f.a[i] = TA ? read_krow_image(sa, BM, wm0, i, s) : read_row_image(sa, wm0, i, s);
         };
@@ -329,7 +376,214 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         }
     };
 
+    // Epilogue: the wave's accumulators to C (guarded at the matrix edges).
+    auto store_tile = [&]() __attribute__((always_inline)) {
+        const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
+        const int lc = L::col(lane);
+        constexpr bool NT = (Cfg::FLAGS & 2) != 0;
+        auto inside = [&](int i, int j, int r) __attribute__((always_inline)) {
+            return full_mn || (m0 + wm0 + i * MF + L::row(lane, r) < M && n0 + wn0 + j * MF + lc < N);
+        };
+        auto index = [&](int i, int j, int r) __attribute__((always_inline)) {
+            return (m0 + wm0 + i * MF + L::row(lane, r)) * out.ldc + n0 + wn0 + j * MF + lc;
+        };
+        if constexpr (!GEN) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < L::R; ++r)
+                        if (inside(i, j, r)) store_out<false, NT>(out, index(i, j, r), acc[i][j][r]);
+        } else {
+            // The general step reads the previous C (beta != 0) one row of fragments
+            // at a time, keeping the loads of the next kAhead rows in flight while a
+            // row is stored: the end-of-tile memory latency is paid about TM / kAhead
+            // times per wave instead of once per element.  The fragment registers of
+            // the main loop are free by now and hold the ring.
+            constexpr int kAhead = TM >= 4 ? 3 : TM - 1;
+            constexpr int kRing = kAhead + 1;
+            const bool rd = out.beta != 0.0f;
+            float prev[kRing][TN][L::R];
+            auto load_row = [&](int i, float (&p)[TN][L::R]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < L::R; ++r)
+                        p[j][r] = (rd && inside(i, j, r)) ? load_prev(out, index(i, j, r)) : 0.0f;
+            };
+#pragma unroll
+            for (int i = 0; i < kAhead; ++i) load_row(i, prev[i]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                if (i + kAhead < TM) load_row(i + kAhead, prev[(i + kAhead) % kRing]);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < L::R; ++r)
+                        if (inside(i, j, r))
+                            store_update<NT>(out, index(i, j, r), acc[i][j][r],
+                                             prev[i % kRing][j][r]);
+            }
+        }
+    };
+
     const int KT = static_cast<int>(K / BK);
+    if constexpr (Cfg::SCHED == 4) {
+        // Ping-pong.  Waves 0-3 (group X, the upper BM/2 rows of the tile) and
+        // waves 4-7 (group Y, the lower rows) share the four SIMDs pairwise.
+        // Every wave holds a whole k-tile of fragments (both slabs).  Turns,
+        // each ended by a barrier:
+        //   turn 2 kt:     X runs k-tile kt's matrix instructions and issues
+        //                  B's direct loads for k-tile kt + 2;
+        //                  Y reads k-tile kt's fragments;
+        //   turn 2 kt + 1: X reads k-tile kt + 1's fragments;
+        //                  Y runs k-tile kt's matrix instructions and issues
+        //                  A's direct loads for k-tile kt + 2.
+        // So on each SIMD one wave issues matrix instructions while the other
+        // reads LDS.  The direct loads ride in the matrix turns, one after every
+        // few matrix instructions: issued as one burst they would stall the
+        // issuing wave for longer than a turn, since a CU's vector memory path
+        // takes about 48 bytes a clock.  A has two LDS stages and B three: B's
+        // loads for kt + 2 go to the stage of k-tile kt - 1 (last read by Y in
+        // turn 2 kt - 2), A's to the stage of k-tile kt (last read by Y in turn
+        // 2 kt).  Both are waited for at the end of turn 2 kt + 2, before X
+        // reads k-tile kt + 2 in turn 2 kt + 3.
+        constexpr int NL = 4;  // waves per group
+        using PA = DirectOperand<BM, BK, NL, !TA>;
+        using PB = DirectOperand<BN, BK, NL, TB>;
+        static_assert(PA::PER <= 16 && PB::PER <= 16, "direct loads per wave per k-tile");
+        static_assert(SLABS == 2, "a k-tile is two slabs of fragments");
+        static_assert(Cfg::LDS_BYTES <= 160 * 1024, "two A and three B stages fit");
+        const bool gx = wave < NL;
+        // Whole tiles only (the launcher checks), so a wave's successive loads
+        // of one operand are its first load moved by a fixed number of image
+        // rows: that step goes into the scalar base, and only one per-lane
+        // offset per swizzle pattern stays in a VGPR.  The row-image swizzle
+        // repeats every 16 rows and a step is RPI * NL = 32 rows, so one
+        // pattern; the k-row swizzle repeats every 16 k-rows and a step is 8
+        // k-rows, so two (even and odd loads).
+        static_assert(PA::ROWS ? (PA::RPI * NL) % 16 == 0 : (2 * PA::RPI * NL) % 16 == 0,
+                      "swizzle patterns repeat with the load step");
+        static_assert(PB::ROWS ? (PB::RPI * NL) % 16 == 0 : (2 * PB::RPI * NL) % 16 == 0,
+                      "swizzle patterns repeat with the load step");
+        const int wx = wave % NL;
+        // X loads B, Y loads A: each wave keeps only its own operand's offsets.
+        const uint32_t v0 = gx ? direct_offset<PB>(0, wx, lane, NL, n0, N, ldb)
+                               : direct_offset<PA>(0, wx, lane, NL, m0, M, lda);
+        const uint32_t v1 = gx ? direct_offset<PB>(1, wx, lane, NL, n0, N, ldb)
+                               : direct_offset<PA>(1, wx, lane, NL, m0, M, lda);
+        // Load q of this wave's share of operand O for k-tile kt: row image,
+        // base moved q steps, pattern 0; k-row image, base moved 2 (q / 2)
+        // steps, pattern q % 2.  A step is RPI * NL image rows, ld apart.
+        auto dma_a = [&](int kt, int q) __attribute__((always_inline)) {
+            const int64_t d = (PA::ROWS ? q : (q & ~1)) * int64_t(PA::RPI * NL) * lda;
+            dma16(lds_addr + Cfg::a_stage(kt) + (wx + q * NL) * 1024,
+                  a_tile + static_cast<int64_t>(kt) * a_step + d,
+                  (PA::ROWS || (q & 1) == 0) ? v0 : v1);
+        };
+        auto dma_b = [&](int kt, int q) __attribute__((always_inline)) {
+            const int64_t d = (PB::ROWS ? q : (q & ~1)) * int64_t(PB::RPI * NL) * ldb;
+            dma16(lds_addr + Cfg::b_stage(kt) + (wx + q * NL) * 1024,
+                  b_tile + static_cast<int64_t>(kt) * b_step + d,
+                  (PB::ROWS || (q & 1) == 0) ? v0 : v1);
+        };
+        Frags P[2];
+        auto read_ktile = [&](int kt) __attribute__((always_inline)) {
+            load_frags(kt, 0, P[0]);
+            load_frags(kt, 1, P[1]);
+        };
+        // A k-tile of matrix instructions; with kt_load >= 0 (a wave-uniform
+        // value; OPA selects the operand) one direct load of k-tile kt_load
+        // after every EVERY-th instruction.
+        constexpr int kMma = 2 * TM * TN;
+        auto run_ktile = [&](auto loads, int kt_load) __attribute__((always_inline)) {
+            constexpr int NQ = decltype(loads)::value == 1 ? PA::PER
+                             : decltype(loads)::value == 2 ? PB::PER : 0;
+            constexpr int EVERY = NQ ? (kMma / NQ < 8 ? kMma / NQ : 8) : 1;
+            __builtin_amdgcn_sched_barrier(0);
+            int n = 0;
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        Op::run(acc[i][j], P[sl].a[i], P[sl].b[j]);
+                        if (NQ && n % EVERY == 0 && n / EVERY < NQ) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            if constexpr (decltype(loads)::value == 1) dma_a(kt_load, n / EVERY);
+                            if constexpr (decltype(loads)::value == 2) dma_b(kt_load, n / EVERY);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        ++n;
+                    }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        using NoLoads = std::integral_constant<int, 0>;
+        using ALoads = std::integral_constant<int, 1>;
+        using BLoads = std::integral_constant<int, 2>;
+        // Prologue: k-tiles 0 and 1 (X loads B, Y loads A); wait for k-tile 0.
+        constexpr int PW = PA::PER;  // loads per wave per k-tile
+        static_assert(PA::PER == PB::PER, "both groups issue the same number of loads");
+        const int pro = KT > 1 ? 2 : 1;
+        if (gx) {
+            for (int t = 0; t < pro; ++t)
+#pragma unroll
+                for (int q = 0; q < PB::PER; ++q) dma_b(t, q);
+        } else {
+            for (int t = 0; t < pro; ++t)
+#pragma unroll
+                for (int q = 0; q < PA::PER; ++q) dma_a(t, q);
+        }
+        if (KT > 1)
+            wait_then_barrier<PW>();
+        else
+            wait_then_barrier<0>();
+        // Each group runs its own straight-line loop (2 KT + 1 barriers in all
+        // for both groups); the last two k-tiles, which load nothing, are
+        // peeled so no branch splits a run of matrix instructions.
+        if (gx) {
+            read_ktile(0);
+            lds_wait_then_barrier();
+            for (int kt = 0; kt + 2 < KT; ++kt) {
+                run_ktile(BLoads{}, kt + 2);
+                // B of k-tile kt + 1 has landed; B of kt + 2 may still fly
+                wait_then_barrier<PW>();
+                read_ktile(kt + 1);
+                lds_wait_then_barrier();
+            }
+            if (KT >= 2) {
+                run_ktile(NoLoads{}, -1);
+                wait_then_barrier<0>();
+                read_ktile(KT - 1);
+                lds_wait_then_barrier();
+            }
+            run_ktile(NoLoads{}, -1);
+            wait_then_barrier<0>();
+            store_tile();
+        } else {
+            lds_wait_then_barrier();
+            for (int kt = 0; kt + 2 < KT; ++kt) {
+                read_ktile(kt);
+                // A of k-tile kt + 1 has landed
+                wait_then_barrier<0>();
+                run_ktile(ALoads{}, kt + 2);
+                lds_wait_then_barrier();
+            }
+            if (KT >= 2) {
+                read_ktile(KT - 2);
+                wait_then_barrier<0>();
+                run_ktile(NoLoads{}, -1);
+                lds_wait_then_barrier();
+            }
+            read_ktile(KT - 1);
+            wait_then_barrier<0>();
+            run_ktile(NoLoads{}, -1);
+            store_tile();
+        }
+        return;
+    } else {
     // Prologue: k-tiles 0 .. S-2 in flight (0 .. S-1 with early loads, which
     // refill a stage right after the barrier that frees it); wait for k-tile 0.
     constexpr bool early = (Cfg::FLAGS & 8) != 0;
@@ -381,55 +635,9 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         front_slabs(KT - 1);
         slab_step(false, 0, 0, F[0], F[1]);
     }
+    store_tile();
+    }  // SCHED != 4
 
-    const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
-    const int lc = L::col(lane);
-    constexpr bool NT = (Cfg::FLAGS & 2) != 0;
-    auto inside = [&](int i, int j, int r) __attribute__((always_inline)) {
-        return full_mn || (m0 + wm0 + i * MF + L::row(lane, r) < M && n0 + wn0 + j * MF + lc < N);
-    };
-    auto index = [&](int i, int j, int r) __attribute__((always_inline)) {
-        return (m0 + wm0 + i * MF + L::row(lane, r)) * out.ldc + n0 + wn0 + j * MF + lc;
-    };
-    if constexpr (!GEN) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int r = 0; r < L::R; ++r)
-                    if (inside(i, j, r)) store_out<false, NT>(out, index(i, j, r), acc[i][j][r]);
-    } else {
-        // The general step reads the previous C (beta != 0) one row of fragments
-        // at a time, keeping the loads of the next kAhead rows in flight while a
-        // row is stored: the end-of-tile memory latency is paid about TM / kAhead
-        // times per wave instead of once per element.  The fragment registers of
-        // the main loop are free by now and hold the ring.
-        constexpr int kAhead = TM >= 4 ? 3 : TM - 1;
-        constexpr int kRing = kAhead + 1;
-        const bool rd = out.beta != 0.0f;
-        float prev[kRing][TN][L::R];
-        auto load_row = [&](int i, float (&p)[TN][L::R]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int r = 0; r < L::R; ++r)
-                    p[j][r] = (rd && inside(i, j, r)) ? load_prev(out, index(i, j, r)) : 0.0f;
-        };
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) load_row(i, prev[i]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if (i + kAhead < TM) load_row(i + kAhead, prev[(i + kAhead) % kRing]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int r = 0; r < L::R; ++r)
-                    if (inside(i, j, r))
-                        store_update<NT>(out, index(i, j, r), acc[i][j][r],
-                                         prev[i % kRing][j][r]);
-        }
-    }
 }
 
 // True when the direct kernel's preconditions hold for these arguments: aligned
@@ -447,9 +655,19 @@ inline bool direct_ok(const GemmArgs& g, int bk, bool layouts) {
            (g.tb ? g.ldb < row_ld : (g.N % 8 == 0 && g.ldb < krow_ld));
 }
 
+// direct_ok for configuration D.  The ping-pong schedule also needs whole
+// tiles: its successive loads of a row image step whole image rows from the
+// first one, with no clamp at the matrix edge.
+template <class D>
+bool direct_fits(const GemmArgs& g) {
+    return direct_ok(g, D::BK, D::LAYOUTS) &&
+           (D::SCHED != 4 || (g.M % D::BM == 0 && g.N % D::BN == 0));
+}
+
 template <class Cfg, bool GEN>
 hipError_t launch_direct_cfg(const GemmArgs& g) {
     using E = typename Cfg::E;
+    if (!direct_fits<Cfg>(g)) return hipErrorInvalidValue;
     const int64_t tm = ceil_div(g.M, Cfg::BM), tn = ceil_div(g.N, Cfg::BN);
     if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(tm * tn)), block(Cfg::NT);
