@@ -434,25 +434,27 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         // waves 4-7 (group Y, the lower rows) share the four SIMDs pairwise.
         // Every wave holds a whole k-tile of fragments (both slabs).  Turns,
         // each ended by a barrier:
-        //   turn 2 kt:     X runs k-tile kt's matrix instructions and issues
-        //                  B's direct loads for k-tile kt + 2;
-        //                  Y reads k-tile kt's fragments;
-        //   turn 2 kt + 1: X reads k-tile kt + 1's fragments;
-        //                  Y runs k-tile kt's matrix instructions and issues
-        //                  A's direct loads for k-tile kt + 2.
-        // So on each SIMD one wave issues matrix instructions while the other
-        // reads LDS.  The direct loads ride in the matrix turns, one after every
-        // few matrix instructions: issued as one burst they would stall the
-        // issuing wave for longer than a turn, since a CU's vector memory path
-        // takes about 48 bytes a clock.  A has two LDS stages and B three: B's
-        // loads for kt + 2 go to the stage of k-tile kt - 1 (last read by Y in
-        // turn 2 kt - 2), A's to the stage of k-tile kt (last read by Y in turn
-        // 2 kt).  Both are waited for at the end of turn 2 kt + 2, before X
-        // reads k-tile kt + 2 in turn 2 kt + 3.
+        //   turn 2 kt:     X runs k-tile kt's matrix instructions;
+        //                  Y reads k-tile kt's fragments and issues B's direct
+        //                  loads for k-tile kt + 2;
+        //   turn 2 kt + 1: X reads k-tile kt + 1's fragments and issues A's
+        //                  direct loads for k-tile kt + 2;
+        //                  Y runs k-tile kt's matrix instructions.
+        // So on each SIMD one wave issues nothing but matrix instructions while
+        // the other reads LDS.  A direct load holds its wave's instruction issue
+        // for about as long as a matrix instruction takes, so the loads ride in
+        // the reading turns (one after every few fragment reads), which have
+        // time to spare.  A has two LDS stages and B three: A's loads for
+        // kt + 2 go to the stage of k-tile kt (last read by Y in turn 2 kt), B's
+        // to the stage of k-tile kt - 1 (last read by Y in turn 2 kt - 2).  X
+        // waits for its A loads at the end of turn 2 kt + 2, Y for its B loads
+        // at the end of the same turn, before X reads k-tile kt + 2 in turn
+        // 2 kt + 3.
         constexpr int NL = 4;  // waves per group
         using PA = DirectOperand<BM, BK, NL, !TA>;
         using PB = DirectOperand<BN, BK, NL, TB>;
-        static_assert(PA::PER <= 16 && PB::PER <= 16, "direct loads per wave per k-tile");
+        static_assert(PA::PER == PB::PER && PA::PER <= 16, "direct loads per wave per k-tile");
+        constexpr int PW = PA::PER;  // direct loads per wave per k-tile
         static_assert(SLABS == 2, "a k-tile is two slabs of fragments");
         static_assert(Cfg::LDS_BYTES <= 160 * 1024, "two A and three B stages fit");
         const bool gx = wave < NL;
@@ -468,11 +470,11 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         static_assert(PB::ROWS ? (PB::RPI * NL) % 16 == 0 : (2 * PB::RPI * NL) % 16 == 0,
                       "swizzle patterns repeat with the load step");
         const int wx = wave % NL;
-        // X loads B, Y loads A: each wave keeps only its own operand's offsets.
-        const uint32_t v0 = gx ? direct_offset<PB>(0, wx, lane, NL, n0, N, ldb)
-                               : direct_offset<PA>(0, wx, lane, NL, m0, M, lda);
-        const uint32_t v1 = gx ? direct_offset<PB>(1, wx, lane, NL, n0, N, ldb)
-                               : direct_offset<PA>(1, wx, lane, NL, m0, M, lda);
+        // X loads A, Y loads B: each wave keeps only its own operand's offsets.
+        const uint32_t v0 = gx ? direct_offset<PA>(0, wx, lane, NL, m0, M, lda)
+                               : direct_offset<PB>(0, wx, lane, NL, n0, N, ldb);
+        const uint32_t v1 = gx ? direct_offset<PA>(1, wx, lane, NL, m0, M, lda)
+                               : direct_offset<PB>(1, wx, lane, NL, n0, N, ldb);
         // Load q of this wave's share of operand O for k-tile kt: row image,
         // base moved q steps, pattern 0; k-row image, base moved 2 (q / 2)
         // steps, pattern q % 2.  A step is RPI * NL image rows, ld apart.
@@ -489,52 +491,70 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
                   (PB::ROWS || (q & 1) == 0) ? v0 : v1);
         };
         Frags P[2];
-        auto read_ktile = [&](int kt) __attribute__((always_inline)) {
-            load_frags(kt, 0, P[0]);
-            load_frags(kt, 1, P[1]);
+        // A k-tile of fragment reads; with `loads` 1 (A) or 2 (B) also the
+        // wave's PW direct loads of k-tile kt_load, one after every few
+        // fragments.
+        constexpr int kFrags = 2 * (TM + TN);
+        auto read_ktile = [&](int kt, auto loads, int kt_load) __attribute__((always_inline)) {
+            constexpr int L = decltype(loads)::value;
+            constexpr int EVERY = L ? (kFrags / PW > 0 ? kFrags / PW : 1) : 1;
+            int r = 0, q = 0;
+            auto after_read = [&]() __attribute__((always_inline)) {
+                ++r;
+                if (L && r % EVERY == 0 && q < PW) {
+                    if constexpr (L == 1) dma_a(kt_load, q);
+                    if constexpr (L == 2) dma_b(kt_load, q);
+                    ++q;
+                }
+            };
+            int a_off = Cfg::a_stage(kt), b_off = Cfg::b_stage(kt);
+            asm("" : "+s"(a_off), "+s"(b_off));
+            const MIGEMM_LDS char* sa = lds + a_off;
+            const MIGEMM_LDS char* sb = lds + b_off;
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                Frags& f = P[sl];
+                auto read_a = [&](int i) __attribute__((always_inline)) {
+                    f.a[i] = TA ? read_krow_image(sa, BM, wm0, i, sl) : read_row_image(sa, wm0, i, sl);
+                    after_read();
+                };
+                auto read_b = [&](int j) __attribute__((always_inline)) {
+                    f.b[j] = TB ? read_row_image(sb, wn0, j, sl) : read_krow_image(sb, BN, wn0, j, sl);
+                    after_read();
+                };
+                read_a(0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) read_b(j);
+#pragma unroll
+                for (int i = 1; i < TM; ++i) read_a(i);
+            }
+            // loads not yet issued (fewer fragments than loads x EVERY)
+#pragma unroll
+            for (int qq = 0; qq < PW; ++qq)
+                if (qq >= q) {
+                    if constexpr (L == 1) dma_a(kt_load, qq);
+                    if constexpr (L == 2) dma_b(kt_load, qq);
+                }
         };
-        // A k-tile of matrix instructions; with kt_load >= 0 (a wave-uniform
-        // value; OPA selects the operand) one direct load of k-tile kt_load
-        // after every EVERY-th instruction.
-        constexpr int kMma = 2 * TM * TN;
-        auto run_ktile = [&](auto loads, int kt_load) __attribute__((always_inline)) {
-            constexpr int NQ = decltype(loads)::value == 1 ? PA::PER
-                             : decltype(loads)::value == 2 ? PB::PER : 0;
-            constexpr int EVERY = NQ ? (kMma / NQ < 8 ? kMma / NQ : 8) : 1;
+        auto run_ktile = [&]() __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
-            int n = 0;
-#pragma unroll
-            for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        Op::run(acc[i][j], P[sl].a[i], P[sl].b[j]);
-                        if (NQ && n % EVERY == 0 && n / EVERY < NQ) {
-                            __builtin_amdgcn_sched_barrier(0);
-                            if constexpr (decltype(loads)::value == 1) dma_a(kt_load, n / EVERY);
-                            if constexpr (decltype(loads)::value == 2) dma_b(kt_load, n / EVERY);
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                        ++n;
-                    }
+            mma(P[0]);
+            mma(P[1]);
             __builtin_amdgcn_sched_barrier(0);
         };
         using NoLoads = std::integral_constant<int, 0>;
         using ALoads = std::integral_constant<int, 1>;
         using BLoads = std::integral_constant<int, 2>;
-        // Prologue: k-tiles 0 and 1 (X loads B, Y loads A); wait for k-tile 0.
-        constexpr int PW = PA::PER;  // loads per wave per k-tile
-        static_assert(PA::PER == PB::PER, "both groups issue the same number of loads");
+        // Prologue: k-tiles 0 and 1 (X loads A, Y loads B); wait for k-tile 0.
         const int pro = KT > 1 ? 2 : 1;
         if (gx) {
             for (int t = 0; t < pro; ++t)
 #pragma unroll
-                for (int q = 0; q < PB::PER; ++q) dma_b(t, q);
+                for (int q = 0; q < PW; ++q) dma_a(t, q);
         } else {
             for (int t = 0; t < pro; ++t)
 #pragma unroll
-                for (int q = 0; q < PA::PER; ++q) dma_a(t, q);
+                for (int q = 0; q < PW; ++q) dma_b(t, q);
         }
         if (KT > 1)
             wait_then_barrier<PW>();
@@ -544,42 +564,42 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         // for both groups); the last two k-tiles, which load nothing, are
         // peeled so no branch splits a run of matrix instructions.
         if (gx) {
-            read_ktile(0);
+            read_ktile(0, NoLoads{}, -1);
             lds_wait_then_barrier();
             for (int kt = 0; kt + 2 < KT; ++kt) {
-                run_ktile(BLoads{}, kt + 2);
-                // B of k-tile kt + 1 has landed; B of kt + 2 may still fly
-                wait_then_barrier<PW>();
-                read_ktile(kt + 1);
+                run_ktile();
+                // A of k-tile kt + 1 has landed
+                wait_then_barrier<0>();
+                read_ktile(kt + 1, ALoads{}, kt + 2);
                 lds_wait_then_barrier();
             }
             if (KT >= 2) {
-                run_ktile(NoLoads{}, -1);
+                run_ktile();
                 wait_then_barrier<0>();
-                read_ktile(KT - 1);
+                read_ktile(KT - 1, NoLoads{}, -1);
                 lds_wait_then_barrier();
             }
-            run_ktile(NoLoads{}, -1);
+            run_ktile();
             wait_then_barrier<0>();
             store_tile();
         } else {
             lds_wait_then_barrier();
             for (int kt = 0; kt + 2 < KT; ++kt) {
-                read_ktile(kt);
-                // A of k-tile kt + 1 has landed
-                wait_then_barrier<0>();
-                run_ktile(ALoads{}, kt + 2);
+                read_ktile(kt, BLoads{}, kt + 2);
+                // B of k-tile kt + 1 has landed; B of kt + 2 may still fly
+                wait_then_barrier<PW>();
+                run_ktile();
                 lds_wait_then_barrier();
             }
             if (KT >= 2) {
-                read_ktile(KT - 2);
+                read_ktile(KT - 2, NoLoads{}, -1);
                 wait_then_barrier<0>();
-                run_ktile(NoLoads{}, -1);
+                run_ktile();
                 lds_wait_then_barrier();
             }
-            read_ktile(KT - 1);
+            read_ktile(KT - 1, NoLoads{}, -1);
             wait_then_barrier<0>();
-            run_ktile(NoLoads{}, -1);
+            run_ktile();
             store_tile();
         }
         return;
