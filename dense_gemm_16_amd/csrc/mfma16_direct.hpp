@@ -536,12 +536,40 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
                     if constexpr (L == 2) dma_b(kt_load, qq);
                 }
         };
-        auto run_ktile = [&]() __attribute__((always_inline)) {
+        // A k-tile of matrix instructions.  With bar 1 (X: wait for its direct
+        // loads, then the barrier) or 2 (Y: the barrier), the wave meets the
+        // barrier that ends its turn kEarly instructions before its last one,
+        // at raised priority: the other group then starts its turn while these
+        // last instructions still fill the matrix pipe, and the raised priority
+        // keeps them ahead of the other wave's first ones, so the barrier's
+        // latency is hidden behind matrix work instead of leaving the pipe idle.
+        constexpr int kEarly = 8;
+        auto run_ktile = [&](auto bar) __attribute__((always_inline)) {
+            constexpr int BK_ = decltype(bar)::value;
             __builtin_amdgcn_sched_barrier(0);
-            mma(P[0]);
-            mma(P[1]);
+            int n = 0;
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        Op::run(acc[i][j], P[sl].a[i], P[sl].b[j]);
+                        if (BK_ && n == 2 * TM * TN - 1 - kEarly) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            __builtin_amdgcn_s_setprio(1);
+                            if constexpr (BK_ == 1) wait_then_barrier<0>();
+                            if constexpr (BK_ == 2) lds_wait_then_barrier();
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        ++n;
+                    }
             __builtin_amdgcn_sched_barrier(0);
+            if (BK_) __builtin_amdgcn_s_setprio(0);
         };
+        using NoBarrier = std::integral_constant<int, 0>;
+        using XBarrier = std::integral_constant<int, 1>;
+        using YBarrier = std::integral_constant<int, 2>;
         using NoLoads = std::integral_constant<int, 0>;
         using ALoads = std::integral_constant<int, 1>;
         using BLoads = std::integral_constant<int, 2>;
@@ -567,20 +595,16 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
             read_ktile(0, NoLoads{}, -1);
             lds_wait_then_barrier();
             for (int kt = 0; kt + 2 < KT; ++kt) {
-                run_ktile();
-                // A of k-tile kt + 1 has landed
-                wait_then_barrier<0>();
+                run_ktile(XBarrier{});
                 read_ktile(kt + 1, ALoads{}, kt + 2);
                 lds_wait_then_barrier();
             }
             if (KT >= 2) {
-                run_ktile();
-                wait_then_barrier<0>();
+                run_ktile(XBarrier{});
                 read_ktile(KT - 1, NoLoads{}, -1);
                 lds_wait_then_barrier();
             }
-            run_ktile();
-            wait_then_barrier<0>();
+            run_ktile(XBarrier{});
             store_tile();
         } else {
             lds_wait_then_barrier();
@@ -588,18 +612,16 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
                 read_ktile(kt, BLoads{}, kt + 2);
                 // B of k-tile kt + 1 has landed; B of kt + 2 may still fly
                 wait_then_barrier<PW>();
-                run_ktile();
-                lds_wait_then_barrier();
+                run_ktile(YBarrier{});
             }
             if (KT >= 2) {
                 read_ktile(KT - 2, NoLoads{}, -1);
                 wait_then_barrier<0>();
-                run_ktile();
-                lds_wait_then_barrier();
+                run_ktile(YBarrier{});
             }
             read_ktile(KT - 1, NoLoads{}, -1);
             wait_then_barrier<0>();
-            run_ktile();
+            run_ktile(NoBarrier{});
             store_tile();
         }
         return;
