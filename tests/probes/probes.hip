@@ -20,6 +20,22 @@ __global__ __launch_bounds__(64) void tr16_kernel(const int* addr, uint16_t* out
     for (int e = 0; e < 4; ++e) out[threadIdx.x * 4 + e] = static_cast<uint16_t>(v[e]);
 }
 
+// ds_read_b64_tr_b8: LDS holds 8192 bytes, byte i = (mode == 0 ? i & 255 : i >> 8);
+// lane l reads the 8-byte word at byte offset addr[l] (a multiple of 8 below
+// 8192) with transpose.  The two modes together give the source offset of every
+// byte a lane receives.
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+__global__ __launch_bounds__(64) void tr8_kernel(const int* addr, uint8_t* out, int mode) {
+    __shared__ uint8_t lds[8192];
+    for (int i = threadIdx.x; i < 8192; i += 64)
+        lds[i] = static_cast<uint8_t>(mode == 0 ? (i & 255) : (i >> 8));
+    __syncthreads();
+    const int a = addr[threadIdx.x] & 8184;  // in bounds whatever the host passed
+    i32x2v v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2v*)((LDS_AS char*)lds + a));
+    for (int e = 0; e < 8; ++e)
+        out[threadIdx.x * 8 + e] = static_cast<uint8_t>(static_cast<uint32_t>(v[e / 4]) >> (8 * (e % 4)));
+}
+
 // global_load_lds_dwordx4: lane l loads the 16 bytes at src + 4*off[l] dwords
 // (off[l] < 64) into LDS at a base of 64 dwords; the whole 1024-dword LDS array
 // (pre-filled with 0xffffffff) is copied out.
@@ -33,6 +49,11 @@ __global__ __launch_bounds__(64) void lds_load_kernel(const uint32_t* src, const
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int i = threadIdx.x; i < 1024; i += 64) out[i] = lds[i];
+}
+
+extern "C" int probe_tr8(const int* addr, uint8_t* out, int mode, void* stream) {
+    tr8_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>(addr, out, mode);
+    return static_cast<int>(hipGetLastError());
 }
 
 extern "C" int probe_tr16(const int* addr, uint16_t* out, void* stream) {
