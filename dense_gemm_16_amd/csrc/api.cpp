@@ -109,9 +109,11 @@ int check_args(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, con
 }
 
 // 16-byte aligned operand pointers with leading dimensions of whole 16-byte
-// chunks (8 16-bit elements).  NULL pointers count as aligned (migemm_select).
-bool operands_aligned(const void* A, int64_t lda, const void* B, int64_t ldb) {
-    return aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0;
+// chunks (8 16-bit or 16 8-bit elements).  NULL pointers count as aligned
+// (migemm_select).
+bool operands_aligned(const void* A, int64_t lda, const void* B, int64_t ldb, int dtype) {
+    const int64_t epc = dtype == MIGEMM_I8 ? 16 : 8;
+    return aligned16(A) && aligned16(B) && lda % epc == 0 && ldb % epc == 0;
 }
 
 // The selection table: a pure function of shape, dtype, operand layout and
@@ -122,8 +124,11 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool a
     auto tiles = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
     if (dtype == MIGEMM_I8) {
         variant = MIGEMM_MFMA_I8;
-        // 256x256 with 32x32x32 instructions measured best in every layout at 8192^3
-        config = tiles(256, 256) >= 256 ? 3 : tiles(128, 128) >= 256 ? 1 : 2;
+        // whole 256x256 tiles with aligned operands: the direct ping-pong kernel;
+        // otherwise the register-staged 256x256 with 32x32x32 instructions
+        // measured best in every layout at 8192^3
+        const bool whole = M % 256 == 0 && N % 256 == 0 && K % 128 == 0 && aligned;
+        config = tiles(256, 256) >= 256 ? (whole ? 4 : 3) : tiles(128, 128) >= 256 ? 1 : 2;
         return;
     }
     if (dtype == MIGEMM_F32) {
@@ -167,7 +172,7 @@ int run(int variant, int config, int op_a, int op_b, int64_t M, int64_t N, int64
     if (st != MIGEMM_OK) return st;
     // INT32 C takes the plain product only
     if (c_dtype == MIGEMM_I32 && (alpha != 1.0f || beta != 0.0f)) return MIGEMM_ERR_UNSUPPORTED;
-    const bool aligned = operands_aligned(A, lda, B, ldb);
+    const bool aligned = operands_aligned(A, lda, B, ldb, dtype);
     if (variant == MIGEMM_VARIANT_AUTO) {
         if (config != -1) return MIGEMM_ERR_INVALID_ARG;
         select(M, N, K, dtype, ta, tb, aligned, variant, config);
@@ -279,7 +284,7 @@ int migemm_select(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int
     int st = check_args(M, N, K, dtype, false, false, A, lda, B, ldb, C, ldc, c_dtype, false);
     if (st != MIGEMM_OK) return st;
     if (!variant || !config) return MIGEMM_ERR_INVALID_ARG;
-    select(M, N, K, dtype, false, false, operands_aligned(A, lda, B, ldb), *variant, *config);
+    select(M, N, K, dtype, false, false, operands_aligned(A, lda, B, ldb, dtype), *variant, *config);
     return MIGEMM_OK;
 }
 

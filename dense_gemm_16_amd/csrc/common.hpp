@@ -103,6 +103,11 @@ __device__ __forceinline__ void store_f32_stream(float* p, float v) {
     asm volatile("global_store_dword %0, %1, off sc1 nt" : : "v"(p), "v"(v) : "memory");
 }
 
+// The same streaming store for INT32 C.
+__device__ __forceinline__ void store_i32_stream(int32_t* p, int32_t v) {
+    asm volatile("global_store_dword %0, %1, off sc1 nt" : : "v"(p), "v"(v) : "memory");
+}
+
 // Writes v, the FP32 sum of products of element idx (row * ldc + col) of C, as
 // the output step says.  GEN == false is the plain FP32 overwrite (the only
 // form the kernels compile for the default call); NT selects streaming

@@ -65,6 +65,7 @@ namespace migemm {
 
 #define MIGEMM_LDS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // SCHED: 0 = a slab's LDS reads as one block, then its matrix instructions;
 // 2 = one LDS read issued after each matrix instruction (sched_group_barrier);
@@ -86,7 +87,8 @@ struct DirectCfg {
     static constexpr int NW = WM * WN, NT = NW * kWave;
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
     static constexpr int TM = WTM / MF, TN = WTN / MF;
-    static constexpr int STAGE_A = BM * BK * 2, STAGE_B = BK * BN * 2;
+    static constexpr int EB = sizeof(E);  // bytes per element: 2 (FP16/BF16) or 1 (INT8)
+    static constexpr int STAGE_A = BM * BK * EB, STAGE_B = BK * BN * EB;
     static constexpr int STAGE_BYTES = STAGE_A + STAGE_B;
     static constexpr bool LAYOUTS = (FLAGS & 16) != 0;
     // LDS placement.  Stage s of the other schedules is [A | B] at s * STAGE_BYTES.
@@ -100,7 +102,7 @@ struct DirectCfg {
     __device__ static int b_stage(int kt) {
         return SCHED == 4 ? (kt % 3) * STAGE_B : (kt % STAGES) * STAGE_BYTES + STAGE_A;
     }
-    static_assert(sizeof(E) == 2, "16-bit inputs only");
+    static_assert(EB == 2 || EB == 1, "16-bit or 8-bit inputs");
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "whole blocks per wave");
     static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "stages fit 160 KiB");
     static_assert(SCHED == 0 || SCHED == 2 || SCHED == 4, "scheduling policy 0, 2 or 4");
@@ -109,20 +111,24 @@ struct DirectCfg {
     static_assert((FLAGS & ~30) == 0, "flags: bits 1 to 4");
 };
 
-// One operand's LDS image (BX rows of M or N by BK of k, 16-bit elements).
-// KROW: [BX rows][BK / 8 chunks], k contiguous (row-major A, or B given
-// transposed).  Otherwise a k-row image [BK k-rows][BX / 8 chunks], the BX side
-// contiguous (row-major B, or A given transposed).  A direct load fills 64
-// chunks: RPI image rows.
-template <int BX, int BK, int NW, bool KROW>
+// One operand's LDS image (BX rows of M or N by BK of k, EB-byte elements).
+// KROW: [BX rows][BK EB / 16 chunks], k contiguous (row-major A, or B given
+// transposed).  Otherwise a k-row image [BK k-rows][BX EB / 16 chunks], the BX
+// side contiguous (row-major B, or A given transposed).  A direct load fills 64
+// chunks: RPI image rows.  SWZ_PERIOD: the k-row swizzle repeats every so many
+// k-rows.
+template <int BX, int BK, int NW, bool KROW, int EB = 2>
 struct DirectOperand {
     static constexpr bool ROWS = KROW;
-    static constexpr int CH = KROW ? BK / 8 : BX / 8;  // 16-byte chunks per image row
+    static constexpr int EPC = 16 / EB;                      // elements per 16-byte chunk
+    static constexpr int CH = (KROW ? BK : BX) / EPC;        // 16-byte chunks per image row
     static constexpr int RPI = 64 / CH;
     static constexpr int INSTR = (KROW ? BX : BK) / RPI;
-    static constexpr int PER = INSTR / NW;             // direct loads per wave per k-tile
-    static_assert(!KROW || BK == 32 || BK == 64, "row images are 64 or 128 bytes wide");
-    static_assert(KROW || (BX >= 128 && BX <= 512), "the k-row swizzle needs 16 to 64 chunks");
+    static constexpr int PER = INSTR / NW;                   // direct loads per wave per k-tile
+    static constexpr int SWZ_PERIOD = EB == 2 ? 16 : 32;
+    static_assert(!KROW || CH == 4 || CH == 8, "row images are 64 or 128 bytes wide");
+    static_assert(KROW || (EB == 2 ? (CH >= 16 && CH <= 64) : CH == 16),
+                  "k-row images: 16 to 64 chunks (16-bit), 16 chunks (8-bit)");
     static_assert(INSTR % NW == 0, "loads split evenly over waves");
 };
 
@@ -138,6 +144,18 @@ __device__ __forceinline__ int swz_a(int row) {
 }
 // Physical chunk of logical chunk c in k-row `krow` of a k-row image: c ^ swz_b(krow).
 __device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) | ((krow >> 1) & 4)) << 1; }
+// The same for 8-bit elements, 256-byte k-rows (16 chunks, one pass over the 64
+// banks each).  A transposing 8-bit read takes one chunk from each of eight
+// consecutive k-rows per lane group, rows 16g + 8h .. 16g + 8h + 7 for the four
+// groups g: XOR with (krow & 7) | (bit 4 of krow) << 3 puts those 32 reads on 16
+// distinct chunk positions, two each, the minimum for 512 bytes.
+__device__ __forceinline__ int swz_b8(int krow) { return (krow & 7) | (((krow >> 4) & 1) << 3); }
+// The k-row swizzle for operand O's element size.
+template <class O>
+__device__ __forceinline__ int swz_krow(int krow) {
+    if constexpr (O::EPC == 8) return swz_b(krow);
+    return swz_b8(krow);
+}
 
 // Per-lane byte offsets of a wave's direct loads of one operand O, relative to
 // its tile origin (row image: P + x0 * ld + k0; k-row image: P + k0 * ld + x0).
@@ -146,15 +164,16 @@ __device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) | ((krow >> 
 template <class O>
 __device__ __forceinline__ uint32_t direct_offset(int q, int wave, int lane, int nw, int64_t x0,
                                                   int64_t ext, int64_t ld) {
+    constexpr int EPC = O::EPC, EB = 16 / EPC;
     const int r = O::RPI * (wave + q * nw) + lane / O::CH;
     if constexpr (O::ROWS) {
         const int chunk = (lane % O::CH) ^ swz_a<O::CH>(r);
         const int64_t gr = min(x0 + r, ext - 1);
-        return static_cast<uint32_t>(((gr - x0) * ld + chunk * 8) * 2);
+        return static_cast<uint32_t>(((gr - x0) * ld + chunk * EPC) * EB);
     } else {
-        const int chunk = (lane % O::CH) ^ swz_b(r);
-        const int64_t gc = min(x0 + chunk * 8, ext - 8);
-        return static_cast<uint32_t>((r * ld + (gc - x0)) * 2);
+        const int chunk = (lane % O::CH) ^ swz_krow<O>(r);
+        const int64_t gc = min(x0 + chunk * EPC, ext - EPC);
+        return static_cast<uint32_t>((r * ld + (gc - x0)) * EB);
     }
 }
 template <class O>
@@ -213,8 +232,8 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     using E = typename Cfg::E;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, MF = Cfg::MF, TM = Cfg::TM, TN = Cfg::TN;
     constexpr int NW = Cfg::NW, S = Cfg::STAGES, BK = Cfg::BK;
-    using OA = DirectOperand<BM, BK, NW, !TA>;
-    using OB = DirectOperand<BN, BK, NW, TB>;
+    using OA = DirectOperand<BM, BK, NW, !TA, Cfg::EB>;
+    using OB = DirectOperand<BN, BK, NW, TB, Cfg::EB>;
     constexpr int NI = OA::PER + OB::PER;  // direct loads per wave per k-tile
     static_assert((S - 2) * NI <= 63, "vmcnt counts at most 63 loads");
     using Op = MfmaOp<E, MF>;
@@ -274,12 +293,16 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     }
 
     // Fragment addressing.  MF = 16: lane (r + 16 g) feeds row r of a block (of A,
-    // or column r of B) and k = 8 g .. 8 g + 7 of a 32-k slab.  MF = 32: lane
-    // (r + 32 g), k = 8 g .. of a 16-k slab.  From a row image that is one 16-byte
-    // read; from a k-row image two transposing reads, arranged so that lane j of
-    // each 16-lane group receives column j of four k-rows each time.
+    // or column r of B) and the g-th 16-byte run of k of a slab: k = 8 g .. 8 g + 7
+    // of a 32-k slab for 16-bit elements, k = 16 g .. 16 g + 15 of a 64-k slab for
+    // 8-bit ones.  MF = 32 (16-bit only): lane (r + 32 g), k = 8 g .. of a 16-k
+    // slab.  From a row image that is one 16-byte read; from a k-row image two
+    // transposing reads, arranged so that lane j of each 16-lane group receives
+    // column j of four (16-bit) or eight (8-bit) k-rows each time.
+    constexpr int EB = Cfg::EB;
+    static_assert(EB == 2 || MF == 16, "8-bit inputs use 16 x 16 x 64 instructions");
     constexpr int G = kWave / MF;          // k-groups per slab
-    constexpr int SLAB_K = 8 * G;          // k per slab: 32 (MF 16) or 16 (MF 32)
+    constexpr int SLAB_K = (16 / EB) * G;  // k per slab: 32 or 16 (16-bit), 64 (8-bit)
     constexpr int SLABS = BK / SLAB_K;
     const int ar = lane % MF, ag = lane / MF;
     const int bj = lane % 16;
@@ -293,28 +316,45 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     //  * row image: w0 + t MF is a multiple of 16 and the swizzle depends on
     //    row % 16 only, so the fragment's chunk is fixed by the lane and the
     //    slab, and t only adds t MF rows;
-    //  * k-row image: the swizzle depends on k-row bits 0, 1 and 3, which come
-    //    from the lane alone (8 ag + bj / 4); the slab and half add whole
+    //  * k-row image: the swizzle depends on k-row bits that come from the lane
+    //    alone (bits 0, 1 and 3 of 8 ag + bj / 4 for 16-bit elements; bits 0-2
+    //    and 4 of 16 ag + bj / 2 for 8-bit ones); the slab and half add whole
     //    k-rows; and with a power-of-two fragment count t sets column-chunk
-    //    bits that nothing else sets, so it XORs the chunk index with t MF / 8.
+    //    bits that nothing else sets, so it XORs the chunk index with the
+    //    fragment's width in chunks times t.
     auto read_row_image = [&](const MIGEMM_LDS char* img, int w0, int t, int s)
         __attribute__((always_inline)) {
-        constexpr int CA = BK / 8;
+        constexpr int CA = BK * EB / 16;
         const int chunk = (s * G + ag) ^ swz_a<CA>(ar);
         const int lane_off = (w0 + ar) * (CA * 16) + chunk * 16;
         return *(const MIGEMM_LDS u32x4*)(img + lane_off + t * MF * (CA * 16));
     };
     auto read_krow_image = [&](const MIGEMM_LDS char* img, int bx, int w0, int t, int s)
         __attribute__((always_inline)) {
-        const int klane = 8 * ag + bj / 4;
-        const int c0 = ((w0 + bcol) / 8) ^ swz_b(klane);
-        const int lane_off = klane * (bx * 2) + ((c0 ^ (t * MF / 8)) * 16) + (bcol % 8) * 2;
         u32x2 h[2];
+        if constexpr (EB == 2) {
+            // lane j of a group: column j of k-rows 4 half .. 4 half + 3 of its 8
+            const int klane = 8 * ag + bj / 4;
+            const int c0 = ((w0 + bcol) / 8) ^ swz_b(klane);
+            const int lane_off = klane * (bx * 2) + ((c0 ^ (t * MF / 8)) * 16) + (bcol % 8) * 2;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const MIGEMM_LDS char* p = img + lane_off + (s * SLAB_K + 4 * half) * (bx * 2);
-            h[half] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS s16x4*)p));
+            for (int half = 0; half < 2; ++half) {
+                const MIGEMM_LDS char* p = img + lane_off + (s * SLAB_K + 4 * half) * (bx * 2);
+                h[half] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS s16x4*)p));
+            }
+        } else {
+            // lane j of a group: column j of k-rows 8 half .. 8 half + 7 of its 16;
+            // lanes 2e and 2e + 1 address the two 8-byte halves of k-row e's chunk
+            const int klane = 16 * ag + bj / 2;
+            const int c0 = (w0 / 16) ^ swz_b8(klane);
+            const int lane_off = klane * bx + ((c0 ^ t) * 16) + 8 * (bj % 2);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const MIGEMM_LDS char* p = img + lane_off + (s * SLAB_K + 8 * half) * bx;
+                h[half] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((MIGEMM_LDS i32x2*)p));
+            }
         }
         return u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
     };
@@ -394,7 +434,12 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
                     for (int r = 0; r < L::R; ++r)
-                        if (inside(i, j, r)) store_out<false, NT>(out, index(i, j, r), acc[i][j][r]);
+                        if (inside(i, j, r)) {
+                        if constexpr (EB == 1)  // exact INT32 sums of 8-bit products
+                            store_i32_stream(static_cast<int32_t*>(out.C) + index(i, j, r), acc[i][j][r]);
+                        else
+                            store_out<false, NT>(out, index(i, j, r), acc[i][j][r]);
+                    }
         } else {
             // The general step reads the previous C (beta != 0) one row of fragments
             // at a time, keeping the loads of the next kAhead rows in flight while a
@@ -451,8 +496,8 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         // at the end of the same turn, before X reads k-tile kt + 2 in turn
         // 2 kt + 3.
         constexpr int NL = 4;  // waves per group
-        using PA = DirectOperand<BM, BK, NL, !TA>;
-        using PB = DirectOperand<BN, BK, NL, TB>;
+        using PA = DirectOperand<BM, BK, NL, !TA, Cfg::EB>;
+        using PB = DirectOperand<BN, BK, NL, TB, Cfg::EB>;
         static_assert(PA::PER == PB::PER && PA::PER <= 16, "direct loads per wave per k-tile");
         constexpr int PW = PA::PER;  // direct loads per wave per k-tile
         static_assert(SLABS == 2, "a k-tile is two slabs of fragments");
@@ -463,11 +508,11 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         // rows: that step goes into the scalar base, and only one per-lane
         // offset per swizzle pattern stays in a VGPR.  The row-image swizzle
         // repeats every 16 rows and a step is RPI * NL = 32 rows, so one
-        // pattern; the k-row swizzle repeats every 16 k-rows and a step is 8
-        // k-rows, so two (even and odd loads).
-        static_assert(PA::ROWS ? (PA::RPI * NL) % 16 == 0 : (2 * PA::RPI * NL) % 16 == 0,
+        // pattern; the k-row swizzle repeats every 16 (16-bit) or 32 (8-bit)
+        // k-rows and a step is half that, so two (even and odd loads).
+        static_assert(PA::ROWS ? (PA::RPI * NL) % 16 == 0 : (2 * PA::RPI * NL) % PA::SWZ_PERIOD == 0,
                       "swizzle patterns repeat with the load step");
-        static_assert(PB::ROWS ? (PB::RPI * NL) % 16 == 0 : (2 * PB::RPI * NL) % 16 == 0,
+        static_assert(PB::ROWS ? (PB::RPI * NL) % 16 == 0 : (2 * PB::RPI * NL) % PB::SWZ_PERIOD == 0,
                       "swizzle patterns repeat with the load step");
         const int wx = wave % NL;
         // X loads A, Y loads B: each wave keeps only its own operand's offsets.
@@ -683,18 +728,19 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 }
 
 // True when the direct kernel's preconditions hold for these arguments: aligned
-// operands in whole 16-byte chunks per row, K a multiple of the k-tile (bk),
-// the side of a k-row image (N for row-major B, M for A given transposed) in
-// whole chunks, and per-lane offsets (BX <= 256 rows of a row image, 64 k-rows of
-// a k-row image) that fit 31 bits.  `layouts`: the configuration is compiled for
-// operands given transposed.
-inline bool direct_ok(const GemmArgs& g, int bk, bool layouts) {
+// operands in whole 16-byte chunks per row (epc elements per chunk: 8 for 16-bit
+// inputs, 16 for 8-bit ones), K a multiple of the k-tile (bk), the side of a
+// k-row image (N for row-major B, M for A given transposed) in whole chunks, and
+// per-lane offsets (BX <= 256 rows of a row image, up to 128 k-rows of a k-row
+// image) that fit 31 bits.  `layouts`: the configuration is compiled for operands
+// given transposed.
+inline bool direct_ok(const GemmArgs& g, int bk, bool layouts, int epc = 8) {
     if ((g.ta || g.tb) && !layouts) return false;
     const int64_t row_ld = int64_t(1) << 21, krow_ld = int64_t(1) << 23;
-    return aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+    return aligned16(g.A) && aligned16(g.B) && g.lda % epc == 0 && g.ldb % epc == 0 &&
            g.K % bk == 0 && g.K > 0 && g.M > 0 && g.N > 0 &&
-           (g.ta ? (g.M % 8 == 0 && g.lda < krow_ld) : g.lda < row_ld) &&
-           (g.tb ? g.ldb < row_ld : (g.N % 8 == 0 && g.ldb < krow_ld));
+           (g.ta ? (g.M % epc == 0 && g.lda < krow_ld) : g.lda < row_ld) &&
+           (g.tb ? g.ldb < row_ld : (g.N % epc == 0 && g.ldb < krow_ld));
 }
 
 // direct_ok for configuration D.  The ping-pong schedule also needs whole
@@ -702,7 +748,7 @@ inline bool direct_ok(const GemmArgs& g, int bk, bool layouts) {
 // first one, with no clamp at the matrix edge.
 template <class D>
 bool direct_fits(const GemmArgs& g) {
-    return direct_ok(g, D::BK, D::LAYOUTS) &&
+    return direct_ok(g, D::BK, D::LAYOUTS, 16 / D::EB) &&
            (D::SCHED != 4 || (g.M % D::BM == 0 && g.N % D::BN == 0));
 }
 

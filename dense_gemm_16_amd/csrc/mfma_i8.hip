@@ -10,7 +10,15 @@
 // Every product of two int8 values is at most 2^14 in magnitude, so a sum of at
 // most 2^17 - 1 of them is below 2^31 and the INT32 result is exact (the C ABI
 // limits K to 2^17 - 1 for this type); C is written as INT32.
-#include "mfma_gemm.hpp"
+//
+// Configuration 4 is the direct-staged ping-pong kernel of mfma16_direct.hpp on
+// 8-bit elements: a 128-deep k-tile is a 128-byte row of A and a 256-byte k-row
+// of B, as wide in bytes as the 64-deep 16-bit k-tile, so the LDS stages, the
+// schedule and the 16-byte fragments carry over; row-major B is transposed by
+// 8-bit transposing LDS reads.  It needs whole 256 x 256 tiles, K a multiple of
+// 128, 16-byte aligned operands and leading dimensions in whole 16-byte chunks;
+// other shapes run configuration 0.
+#include "mfma16_direct.hpp"
 
 namespace migemm {
 namespace {
@@ -19,20 +27,25 @@ using I0 = MfmaCfg<int8_t, 256, 256, 2, 4, 16>;  // 8 waves, 128x64 per wave
 using I1 = MfmaCfg<int8_t, 128, 128, 2, 2, 16>;  // 4 waves, 64x64 per wave
 using I2 = MfmaCfg<int8_t, 64, 64, 2, 2, 16>;    // small problems: 4x the workgroups
 using I3 = MfmaCfg<int8_t, 256, 256, 2, 4, 32>;  // 8 waves, 32x32x32 instructions
+// direct-staged ping-pong, whole tiles only, every layout
+using D4 = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 4, 22>;
 
 const char* const kNames[] = {"256x256x128 8w 16x16x64", "128x128x128 4w 16x16x64",
-                              "64x64x128 4w 16x16x64", "256x256x128 8w 32x32x32"};
+                              "64x64x128 4w 16x16x64", "256x256x128 8w 32x32x32",
+                              "direct 256x256x128 8w 16x16x64 gm4 pingpong ntC agpr"};
+constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace
 
-int mfma_i8_config_count() { return 4; }
-const char* mfma_i8_config_name(int c) { return (c >= 0 && c < 4) ? kNames[c] : nullptr; }
+int mfma_i8_config_count() { return kCount; }
+const char* mfma_i8_config_name(int c) { return (c >= 0 && c < kCount) ? kNames[c] : nullptr; }
 
 hipError_t launch_mfma_i8(const GemmArgs& g, int config) {
     switch (config) {
         case 1: return launch_mfma_cfg<I1, false>(g);
         case 2: return launch_mfma_cfg<I2, false>(g);
         case 3: return launch_mfma_cfg<I3, false>(g);
+        case 4: return direct_fits<D4>(g) ? launch_direct_cfg<D4, false>(g) : launch_mfma_cfg<I0, false>(g);
         default: return launch_mfma_cfg<I0, false>(g);
     }
 }

@@ -173,6 +173,11 @@ def test_int8_selection():
     assert st == mg.OK and v == mg.MFMA_I8 and mg.migemm_config_name(v, c)
     st, v, c = mg.migemm_select(64, 64, 64, mg.I8, None, 64, None, 64, None, 64)
     assert st == mg.OK and v == mg.MFMA_I8
+    # whole 256 x 256 tiles, K a multiple of 128, 16-byte rows: the direct ping-pong
+    # configuration; a leading dimension of half a chunk sends it to the register-staged one
+    assert mg.migemm_select(8192, 8192, 8192, mg.I8, None, 8192, None, 8192, None, 8192)[2] == 4
+    assert mg.migemm_select(8192, 8192, 8192, mg.I8, None, 8192, None, 8200, None, 8192)[2] == 3
+    assert mg.migemm_select(8192, 8192, 8000, mg.I8, None, 8000, None, 8192, None, 8192)[2] == 3
 
 
 def test_empty_output_is_a_noop():

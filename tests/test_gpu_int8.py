@@ -80,6 +80,53 @@ def test_every_config_exact(ta, tb):
             assert bad.size == 0, f"{bad.size} differ; first {np.unravel_index(bad[0], C.shape)}"
 
 
+WHOLE = [(256, 256, 128, None, None), (256, 512, 256, None, None), (512, 256, 384, None, None),
+         (768, 512, 1024, 1056, 528), (512, 768, 640, 656, 784)]
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_whole_tiles_exact(ta, tb):
+    """Whole 256 x 256 tiles with 1, 2, 3 and more 128-deep k-tiles, dense and
+    padded leading dimensions (multiples of 16): the shapes the direct ping-pong
+    configuration runs itself, in every layout, bit-exact."""
+    direct = [c for c in range(mg.migemm_config_count(mg.MFMA_I8))
+              if "pingpong" in mg.migemm_config_name(mg.MFMA_I8, c)]
+    assert direct
+    for (M, N, K, lda, ldb) in WHOLE:
+        A, B = inputs.pair(M, N, K, "i8", "uniform", seed=M + 2 * N + 3 * K + 7 * ta + 11 * tb)
+        want = _want(A, B)
+        if ta and lda:
+            lda = M + 32
+        if tb and ldb:
+            ldb = K + 16
+        for c in [-1] + direct:
+            v = -1 if c == -1 else mg.MFMA_I8
+            say(f"i8 whole {_name(ta, tb)} {M}x{N}x{K} lda={lda} ldb={ldb} cfg={c}")
+            C, intact = run_i8(A, B, v, c, ta=ta, tb=tb, lda=lda, ldb=ldb)
+            assert intact
+            bad = np.flatnonzero(C != want)
+            assert bad.size == 0, f"{bad.size} differ; first {np.unravel_index(bad[0], C.shape)}"
+
+
+def test_whole_tiles_extreme_sums():
+    """The largest K the direct configuration takes itself (a multiple of 128
+    below 2^17): (-128)(-128) summed 130944 times is 2^31 - 2^21, still exact."""
+    M = N = 256
+    K = (1 << 17) - 128
+    A = torch.full((M, K), -128, dtype=torch.int8)
+    A[M // 2:] = 127
+    B = torch.full((K, N), -128, dtype=torch.int8)
+    B[:, N // 2:] = 127
+    want = np.empty((M, N), dtype=np.int64)
+    want[:M // 2, :N // 2] = 16384 * K
+    want[:M // 2, N // 2:] = -128 * 127 * K
+    want[M // 2:, :N // 2] = -128 * 127 * K
+    want[M // 2:, N // 2:] = 127 * 127 * K
+    say("i8 whole-tile extremes K=130944")
+    C, intact = run_i8(A, B)
+    assert intact and np.array_equal(C, want)
+
+
 def test_extreme_sums_at_the_k_limit():
     """K = 2^17 - 1: (-128)(-128) sums to 2^31 - 2^14 and (-128)(127) to its negative
     counterpart, the largest magnitudes an INT32 result can take here."""
