@@ -151,8 +151,10 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool a
         config = 14;  // direct 256x256x64, ping-pong wave groups (whole tiles only)
     else if (direct && tiles(256, 256) >= 256)
         config = 10;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads
+    else if (direct && tiles(128, 256) >= 256 && M % 128 == 0 && N % 256 == 0)
+        config = 15;  // direct 128x256x64, ping-pong wave groups (e.g. 1024x8192, 4096x2048)
     else if (direct && tiles(128, 256) >= 256)
-        config = 13;  // direct 128x256x64, 8 waves of 64x64, 3 stages (e.g. 1024x8192, 4096x2048)
+        config = 13;  // direct 128x256x64, 8 waves of 64x64, 3 stages
     else if (direct)
         config = 7;   // direct 128x128x64, 8 waves, 4 stages, interleaved
     else if (pack)

@@ -216,6 +216,11 @@ __device__ __forceinline__ void lds_wait_then_barrier() {
 }
 
 template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
     // s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maxima (gfx9 encoding)
@@ -498,8 +503,8 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         constexpr int NL = 4;  // waves per group
         using PA = DirectOperand<BM, BK, NL, !TA, Cfg::EB>;
         using PB = DirectOperand<BN, BK, NL, TB, Cfg::EB>;
-        static_assert(PA::PER == PB::PER && PA::PER <= 16, "direct loads per wave per k-tile");
-        constexpr int PW = PA::PER;  // direct loads per wave per k-tile
+        static_assert(PA::PER <= 16 && PB::PER <= 16, "direct loads per wave per k-tile");
+        constexpr int PWA = PA::PER, PWB = PB::PER;  // direct loads per X / Y wave per k-tile
         static_assert(SLABS == 2, "a k-tile is two slabs of fragments");
         static_assert(Cfg::LDS_BYTES <= 160 * 1024, "two A and three B stages fit");
         const bool gx = wave < NL;
@@ -537,11 +542,13 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         };
         Frags P[2];
         // A k-tile of fragment reads; with `loads` 1 (A) or 2 (B) also the
-        // wave's PW direct loads of k-tile kt_load, one after every few
+        // wave's direct loads of k-tile kt_load (PWA of A or PWB of B), one after
+        // every few
         // fragments.
         constexpr int kFrags = 2 * (TM + TN);
         auto read_ktile = [&](int kt, auto loads, int kt_load) __attribute__((always_inline)) {
             constexpr int L = decltype(loads)::value;
+            constexpr int PW = L == 1 ? PWA : PWB;
             constexpr int EVERY = L ? (kFrags / PW > 0 ? kFrags / PW : 1) : 1;
             int r = 0, q = 0;
             auto after_read = [&]() __attribute__((always_inline)) {
@@ -623,16 +630,22 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         if (gx) {
             for (int t = 0; t < pro; ++t)
 #pragma unroll
-                for (int q = 0; q < PW; ++q) dma_a(t, q);
+                for (int q = 0; q < PWA; ++q) dma_a(t, q);
         } else {
             for (int t = 0; t < pro; ++t)
 #pragma unroll
-                for (int q = 0; q < PW; ++q) dma_b(t, q);
+                for (int q = 0; q < PWB; ++q) dma_b(t, q);
         }
-        if (KT > 1)
-            wait_then_barrier<PW>();
-        else
-            wait_then_barrier<0>();
+        // each group waits for its own loads of k-tile 0
+        if (KT > 1) {
+            if (gx)
+                vm_wait<PWA>();
+            else
+                vm_wait<PWB>();
+        } else {
+            vm_wait<0>();
+        }
+        lds_wait_then_barrier();
         // Each group runs its own straight-line loop (2 KT + 1 barriers in all
         // for both groups); the last two k-tiles, which load nothing, are
         // peeled so no branch splits a run of matrix instructions.
@@ -656,7 +669,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
             for (int kt = 0; kt + 2 < KT; ++kt) {
                 read_ktile(kt, BLoads{}, kt + 2);
                 // B of k-tile kt + 1 has landed; B of kt + 2 may still fly
-                wait_then_barrier<PW>();
+                wait_then_barrier<PWB>();
                 run_ktile(YBarrier{});
             }
             if (KT >= 2) {

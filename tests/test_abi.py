@@ -225,8 +225,9 @@ def test_selection_packs_unreadable_16bit_operands():
     assert sel(8192, 8192, 8192, 2, 8192, 8192) == (mg.OK, mg.MFMA16, 14)
     assert sel(8192, 8200, 8192, 2, 8192, 8200) == (mg.OK, mg.MFMA16, 10)
     assert sel(8000, 8192, 8192, 2, 8192, 8192) == (mg.OK, mg.MFMA16, 10)
-    assert sel(1024, 8192, 8192, 2, 8192, 8192) == (mg.OK, mg.MFMA16, 13)
-    assert sel(4096, 2048, 8192, 1, 8192, 2048) == (mg.OK, mg.MFMA16, 13)
+    assert sel(1024, 8192, 8192, 2, 8192, 8192) == (mg.OK, mg.MFMA16, 15)
+    assert sel(4096, 2048, 8192, 1, 8192, 2048) == (mg.OK, mg.MFMA16, 15)
+    assert sel(1000, 8192, 8192, 2, 8192, 8192) == (mg.OK, mg.MFMA16, 13)
     assert sel(4096, 4096, 4096, 2, 4096, 4096) == (mg.OK, mg.MFMA16, 14)
     assert sel(100, 100, 100, 1, 100, 100) == (mg.OK, mg.MFMA16, 3)
     assert sel(2048, 2048, 2048, 0, 2049, 2048)[1] == mg.REGTILE_MFMA
