@@ -41,7 +41,8 @@ const char* const kNames[] = {
     "packed: zero-padded copies, then config 7 as A x B^T",
     "direct 128x256x64 8w 16x16x32 s3 ilv",
     "direct 256x256x64 8w 16x16x32 gm4 pingpong ntC agpr",
-    "direct 128x256x64 8w 16x16x32 gm8 pingpong ntC agpr"};
+    "direct 128x256x64 8w 16x16x32 gm8 pingpong ntC agpr",
+    "direct 64x64x64 4w 16x16x32 s4"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace

@@ -26,6 +26,7 @@ template <typename E> struct Cfgs {
     using D13 = DirectCfg<E, 128, 256, 2, 4, 16, 3, 64, 8, 2, 16>;  // 8 waves of 64x64, 3 stages; all layouts
     using D14 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 22>;  // ping-pong (whole tiles), AGPRs, nt C; all layouts
     using D15 = DirectCfg<E, 128, 256, 2, 4, 16, 2, 64, 8, 4, 22>;  // ping-pong 128x256 (whole tiles); all layouts
+    using D16 = DirectCfg<E, 64, 64, 2, 2, 16, 4, 64, 8, 0, 16>;    // 4 waves of 32x32, 4 stages; all layouts
 };
 
 template <class D, class Fallback, bool GEN>
@@ -54,6 +55,7 @@ hipError_t launch_typed(const GemmArgs& g, int config) {
         case 13: return direct_or<typename T::D13, typename T::R2, GEN>(g);
         case 14: return direct_or<typename T::D14, typename T::R0, GEN>(g);
         case 15: return direct_or<typename T::D15, typename T::R2, GEN>(g);
+        case 16: return direct_or<typename T::D16, typename T::R3, GEN>(g);
         default: return launch_mfma_cfg<typename T::R0, GEN>(g);
     }
 }

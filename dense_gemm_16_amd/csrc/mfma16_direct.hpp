@@ -127,8 +127,8 @@ struct DirectOperand {
     static constexpr int PER = INSTR / NW;                   // direct loads per wave per k-tile
     static constexpr int SWZ_PERIOD = EB == 2 ? 16 : 32;
     static_assert(!KROW || CH == 4 || CH == 8, "row images are 64 or 128 bytes wide");
-    static_assert(KROW || (EB == 2 ? (CH >= 16 && CH <= 64) : CH == 16),
-                  "k-row images: 16 to 64 chunks (16-bit), 16 chunks (8-bit)");
+    static_assert(KROW || (EB == 2 ? (CH >= 8 && CH <= 64) : CH == 16),
+                  "k-row images: 8 to 64 chunks (16-bit), 16 chunks (8-bit)");
     static_assert(INSTR % NW == 0, "loads split evenly over waves");
 };
 
@@ -144,6 +144,12 @@ __device__ __forceinline__ int swz_a(int row) {
 }
 // Physical chunk of logical chunk c in k-row `krow` of a k-row image: c ^ swz_b(krow).
 __device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) | ((krow >> 1) & 4)) << 1; }
+// For 16-bit k-row images 64 elements wide (128-byte k-rows, two per 256 bytes of
+// banks): XOR the chunk pair with ((krow >> 1) & 1) | ((krow >> 3) & 1) << 1.  Of
+// the 16 k-rows a transposing read takes (8 g + 4 h + 0..3 for the four groups
+// g), each parity's eight rows then spread over the four chunk pairs of their
+// half of the banks, two each: every bank twice, the minimum for 512 bytes.
+__device__ __forceinline__ int swz_b64(int krow) { return (((krow >> 1) & 1) | (((krow >> 3) & 1) << 1)) << 1; }
 // The same for 8-bit elements, 256-byte k-rows (16 chunks, one pass over the 64
 // banks each).  A transposing 8-bit read takes one chunk from each of eight
 // consecutive k-rows per lane group, rows 16g + 8h .. 16g + 8h + 7 for the four
@@ -153,6 +159,7 @@ __device__ __forceinline__ int swz_b8(int krow) { return (krow & 7) | (((krow >>
 // The k-row swizzle for operand O's element size.
 template <class O>
 __device__ __forceinline__ int swz_krow(int krow) {
+    if constexpr (O::EPC == 8 && O::CH == 8) return swz_b64(krow);
     if constexpr (O::EPC == 8) return swz_b(krow);
     return swz_b8(krow);
 }
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         if constexpr (EB == 2) {
             // lane j of a group: column j of k-rows 4 half .. 4 half + 3 of its 8
             const int klane = 8 * ag + bj / 4;
-            const int c0 = ((w0 + bcol) / 8) ^ swz_b(klane);
+            const int c0 = ((w0 + bcol) / 8) ^ (bx == 64 ? swz_b64(klane) : swz_b(klane));
             const int lane_off = klane * (bx * 2) + ((c0 ^ (t * MF / 8)) * 16) + (bcol % 8) * 2;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {

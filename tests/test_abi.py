@@ -230,6 +230,9 @@ def test_selection_packs_unreadable_16bit_operands():
     assert sel(1000, 8192, 8192, 2, 8192, 8192) == (mg.OK, mg.MFMA16, 13)
     assert sel(4096, 4096, 4096, 2, 4096, 4096) == (mg.OK, mg.MFMA16, 14)
     assert sel(100, 100, 100, 1, 100, 100) == (mg.OK, mg.MFMA16, 3)
+    # fewer than 256 tiles of 128x128: the 64x64 direct tile
+    assert sel(1024, 1024, 1024, 1, 1024, 1024) == (mg.OK, mg.MFMA16, 16)
+    assert sel(256, 256, 256, 1, 256, 256) == (mg.OK, mg.MFMA16, 16)
     assert sel(2048, 2048, 2048, 0, 2049, 2048)[1] == mg.REGTILE_MFMA
 
 
