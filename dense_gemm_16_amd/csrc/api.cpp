@@ -158,7 +158,7 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool a
     else if (direct && tiles(128, 128) >= 256)
         config = 7;   // direct 128x128x64, 8 waves, 4 stages, interleaved
     else if (direct)
-        config = 16;  // direct 64x64x64, 4 waves: four times the workgroups (e.g. 1024^3)
+        config = 16;  // direct 64x64x64, 8 waves: four times the workgroups (e.g. 1024^3)
     else if (pack)
         config = tiles(256, 256) >= 256 ? 11 : 12;  // packed copies, then config 14/10 or 7
     else if (tiles(128, 128) >= 256)

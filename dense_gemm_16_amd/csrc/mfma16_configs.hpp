@@ -26,7 +26,7 @@ template <typename E> struct Cfgs {
     using D13 = DirectCfg<E, 128, 256, 2, 4, 16, 3, 64, 8, 2, 16>;  // 8 waves of 64x64, 3 stages; all layouts
     using D14 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 22>;  // ping-pong (whole tiles), AGPRs, nt C; all layouts
     using D15 = DirectCfg<E, 128, 256, 2, 4, 16, 2, 64, 8, 4, 22>;  // ping-pong 128x256 (whole tiles); all layouts
-    using D16 = DirectCfg<E, 64, 64, 2, 2, 16, 4, 64, 8, 0, 16>;    // 4 waves of 32x32, 4 stages; all layouts
+    using D16 = DirectCfg<E, 64, 64, 2, 4, 16, 4, 64, 8, 0, 24>;    // 8 waves of 32x16, 4 stages, early loads; all layouts
 };
 
 template <class D, class Fallback, bool GEN>
