@@ -1,5 +1,5 @@
-// mfma16_direct.hpp -- FP16/BF16 GEMM for gfx950 with direct global->LDS
-// staging and transposing LDS reads.
+// mfma16_direct.hpp -- FP16/BF16 (and INT8) GEMM for gfx950 with direct
+// global->LDS staging and transposing LDS reads.
 //
 // Same algorithm as mfma_gemm.hpp (tiles of C, k-tiles accumulated by the
 // matrix cores; page "Tensor cores and matrix operations", section "Complete
@@ -11,31 +11,42 @@
 //   Which global chunk a lane fetches is chosen so that the LDS image comes out
 //   swizzled.
 // * ds_read_b64_tr_b16 reads a 4-row x 16-column block of a row-major tile and
-//   hands lane j of each 16-lane group column j of those rows.  B therefore
-//   stays row-major in LDS (as it is in memory), and the k-contiguous operand
-//   the matrix instruction wants is produced by the read itself: two
-//   transposing reads give a lane the 8 consecutive k of one column of B.
+//   hands lane j of each 16-lane group column j of those rows (ds_read_b64_tr_b8:
+//   an 8-row x 16-byte block, for 8-bit elements).  B therefore stays row-major
+//   in LDS (as it is in memory), and the k-contiguous operand the matrix
+//   instruction wants is produced by the read itself: two transposing reads
+//   give a lane the 16 bytes of consecutive k of one column of B.
 //
-// LDS images (per stage; two stages alternate):
+// Everything is counted in 16-byte chunks, so the code serves 2-byte and
+// 1-byte elements alike: a 64-deep 16-bit k-tile and a 128-deep 8-bit one are
+// both 128 bytes per row.
+//
+// LDS images (per stage):
 //   A: [BM rows][8 chunks of 16 B]; logical chunk c of row r at physical chunk
 //      c ^ ((r >> 1) & 7).  Sixteen consecutive rows reading one logical chunk
 //      (a fragment read) then fall on sixteen distinct 16-byte bank groups: the
 //      eight even rows on one half of the banks, the eight odd rows on the other,
 //      each on its own chunk.  The pattern repeats every 16 rows, so fragments
 //      16 rows apart differ by a constant address offset.
-//   B: [64 k-rows][BN/8 chunks of 16 B]; logical chunk c of k-row r at
-//      c ^ (2 f(r)), f(r) = (r & 3) | (((r >> 3) & 1) << 2).  A transposing
-//      read touches 32 bytes (two chunks) in each of the rows 8g + {0..3} of
-//      the four lane groups g; f gives the eight rows of two adjacent groups
-//      eight distinct chunk pairs, i.e. all 64 banks once.
+//   B: [k-rows][BN elements]; logical chunk c of k-row r at c ^ swizzle(r):
+//      16-bit, BN >= 128: 2 f(r), f(r) = (r & 3) | (((r >> 3) & 1) << 2).  A
+//      transposing read touches 32 bytes (two chunks) in each of the rows
+//      8g + {0..3} of the four lane groups g; f gives the eight rows of two
+//      adjacent groups eight distinct chunk pairs, i.e. all 64 banks once.
+//      16-bit, BN = 64, and 8-bit: see swz_b64 and swz_b8 below.
 //
 // Work per workgroup: a BM x BN tile of C, WM x WN wavefronts each owning a
-// (BM/WM) x (BN/WN) block of accumulators.  k advances 64 at a time through
-// STAGES LDS buffers: the direct loads of k-tile kt + STAGES - 1 are issued
-// at the start of k-tile kt, so each load has STAGES - 1 k-tiles of matrix work
-// to land.  Matrix-core operands are software-pipelined: the fragments of the
-// next 32-k (or 16-k) slab are read from LDS while the current slab's
-// instructions run, including across the one barrier per k-tile.
+// (BM/WM) x (BN/WN) block of accumulators.  Two schedules:
+// * interleaved (SCHED 0 or 2): k advances one k-tile at a time through
+//   STAGES LDS buffers; the direct loads of k-tile kt + STAGES - 1 are issued
+//   at the start of k-tile kt (or, with early loads, right after the barrier
+//   that frees their stage), and the fragments of the next slab are read from
+//   LDS while the current slab's instructions run, including across the one
+//   barrier per k-tile;
+// * ping-pong (SCHED 4, whole tiles only): two groups of four waves take
+//   turns on each SIMD, one running a whole k-tile of matrix instructions
+//   while the other reads its next k-tile of fragments and issues direct
+//   loads (see the kernel body).
 //
 // The direct loads are issued through inline assembly with explicit
 // vmcnt accounting: the compiler cannot see that they write a different LDS
@@ -47,15 +58,16 @@
 // Operands given transposed swap image kinds: A stored K x M (m contiguous)
 // becomes a k-row image like B's and is read with transposing reads; B stored
 // N x K (k contiguous) becomes a row image like A's and is read with
-// ds_read_b128.  Both reads hand a lane the same fragment (a run of 8 k of one
-// row of A or column of B), so the matrix instructions do not change.
+// ds_read_b128.  Both reads hand a lane the same fragment (a 16-byte run of k
+// of one row of A or column of B), so the matrix instructions do not change.
 //
 // Preconditions (checked by the launcher; other shapes use mfma_gemm.hpp):
-// A and B 16-byte aligned, lda and ldb multiples of 8 elements, K a multiple
-// of 64, and the side of a k-row image (N for row-major B, M for A given
-// transposed) a multiple of 8.  Rows of a row image past M or N, and chunks
-// of a k-row image past its side, are clamped to the last valid row / chunk,
-// so every load is in bounds; those lanes only feed outputs that are never
+// A and B 16-byte aligned, lda and ldb in whole 16-byte chunks, K a multiple
+// of the k-tile, and the side of a k-row image (N for row-major B, M for A
+// given transposed) in whole chunks; the ping-pong schedule also needs M and N
+// to be multiples of the tile.  Rows of a row image past M or N, and chunks of
+// a k-row image past its side, are clamped to the last valid row / chunk, so
+// every load is in bounds; those lanes only feed outputs that are never
 // stored.
 #pragma once
 
