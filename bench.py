@@ -488,6 +488,15 @@ def main():
             log(f"extra {wi.name}: {tf:.1f} TOPS ({100 * tf / PEAK_TFLOPS['i8']:.1f}% of "
                 f"{PEAK_TFLOPS['i8']}) on {px.kernel_name()}")
             del px
+            for ta, tb in ((False, True), (True, False), (True, True)):
+                px = Problem(wi, ta=ta, tb=tb)
+                t, n = px.time_window()
+                tf = wi.flop / (t * 1e-3) / 1e12
+                extra[f"{wi.name}/{px.layout()}"] = {
+                    "tops": round(tf, 2), "ms": round(t, 5), "launches": n,
+                    "frac_of_peak": round(tf / PEAK_TFLOPS["i8"], 4), "kernel": px.kernel_name()}
+                log(f"extra {wi.name} layout {px.layout()}: {tf:.1f} TOPS")
+                del px
         # FP32 data on the 16-bit path: device conversion, alone and followed by the product
         if w.name == "c4-bf16-8192":
             extra.update(conversion_lines(w))
