@@ -33,7 +33,7 @@ const char* const kNames[] = {
     "256x256x64 8w 32x32x16",
     "direct 256x256x64 8w 16x16x32",
     "direct 256x256x64 8w 32x32x16",
-    "direct 128x128x64 8w 16x16x32 s4 ilv",
+    "direct 128x128x64 8w 16x16x32 s4 ilv ntC",
     "direct 128x128x64 4w 16x16x32 s4",
     "direct 256x256x64 8w 32x32x16 gm4 ilv ntC",
     "direct 256x256x64 8w 16x16x32 gm4 ilv ntC agpr early",
@@ -42,7 +42,7 @@ const char* const kNames[] = {
     "direct 128x256x64 8w 16x16x32 s3 ilv",
     "direct 256x256x64 8w 16x16x32 gm4 pingpong ntC agpr",
     "direct 128x256x64 8w 16x16x32 gm8 pingpong ntC agpr",
-    "direct 64x64x64 8w 16x16x32 s4 early"};
+    "direct 64x64x64 8w 16x16x32 s4 early ntC"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace
