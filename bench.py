@@ -185,7 +185,8 @@ def cpu_baseline(p, seconds):
                     break
     except OSError:
         pass
-    return {"value": flop / dt / 1e12, "unit": "TFLOPS", "cores": used, "kind": "oracle",
+    return {"value": flop / dt / 1e12, "unit": "TOPS" if w.dtype == "i8" else "TFLOPS",
+            "cores": used, "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N} outputs, K={w.K}), "
                       f"fp64 ascending-k sums over the same {w.dtype} inputs; {dt:.1f} s",
             "seconds": round(dt, 3), "cpu_model": cpu_model,
@@ -405,7 +406,8 @@ def main():
 
     traffic, tnote = traffic_for(p.kernel_name(), w.name)
     roof = {"bound": "mfma", "kernel": p.kernel_name(), "achieved": round(tflops, 2),
-            "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+            "peak": peak, "unit": "TOP/s" if w.dtype == "i8" else "TFLOP/s",
+            "frac": round(tflops / peak, 4),
             "traffic": traffic, "traffic_note": tnote,
             "algorithmic_flop_per_launch": w.flop,
             "compulsory_bytes_per_launch": w.compulsory_bytes()}
@@ -522,12 +524,16 @@ def main():
         log(f"cpu_baseline: {cpu['value'] * 1e3:.2f} GFLOPS on {cpu['cores']} threads; "
             f"GPU rows {cpu['gpu_rows_vs_oracle']}")
 
-    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1,
+    # INT8 products count integer operations and accumulate and output in INT32
+    integer = w.dtype == "i8"
+    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TOPS" if integer else "TFLOPS",
+           "n_gpus": 1,
            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
            "data": "synthetic",
            "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "inputs": w.dtype,
-                      "accumulate": "f32", "output": "f32", "distribution": w.dist,
+                      "accumulate": "i32" if integer else "f32",
+                      "output": "i32" if integer else "f32", "distribution": w.dist,
                       "seed": w.seed, "layout": "row-major, dense leading dimensions",
                       "parallelism": "single GPU"},
            "frac_of_peak": round(tflops / peak, 4), "peak_tflops": peak,

@@ -46,10 +46,12 @@ def draw(shape, dtype: str, dist: str, g: torch.Generator, lo: int = -4, hi: int
     """One matrix of ``shape`` in storage type ``dtype`` (CPU tensor)."""
     t = TORCH_DTYPES[dtype]
     if dtype == "i8":
+        if dist == "zeros":
+            return torch.zeros(shape, dtype=torch.int8)
         if dist == "uniform":
             lo, hi = -128, 127
         elif dist != "int":
-            raise ValueError(f"INT8 inputs take the uniform or int distributions, not {dist!r}")
+            raise ValueError(f"INT8 inputs take the uniform, int or zeros distributions, not {dist!r}")
         return torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int32).to(torch.int8)
     if dist == "uniform":
         x = torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
