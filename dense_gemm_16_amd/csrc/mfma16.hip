@@ -33,7 +33,7 @@ const char* const kNames[] = {
     "256x256x64 8w 32x32x16",
     "direct 256x256x64 8w 16x16x32",
     "direct 256x256x64 8w 32x32x16",
-    "direct 128x128x64 8w 16x16x32 s4 ilv ntC",
+    "direct 128x128x64 8w 16x16x32 gm4 s4 ilv ntC",
     "direct 128x128x64 4w 16x16x32 s4",
     "direct 256x256x64 8w 32x32x16 gm4 ilv ntC",
     "direct 256x256x64 8w 16x16x32 gm4 ilv ntC agpr early",
