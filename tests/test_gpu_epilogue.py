@@ -56,6 +56,24 @@ def test_every_config_general_update(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_every_config_general_update_whole_line_rows(dtype):
+    """Rows of C that start whole 128-byte lines (N = 512 for FP32 and 16-bit C):
+    the configurations that pick their store policy by C's layout take the
+    non-temporal one here, the shapes above take plain stores."""
+    M, N, K = 256, 512, 192
+    A, B = inputs.pair(M, N, K, dtype, "uniform", seed=41)
+    ref = oracle_ref(A, B, dtype)
+    for c_code in C_CODES:
+        old = _old(M, N, c_code, seed=43 + c_code)
+        for v, c in _cases(dtype):
+            say(f"general whole-line {dtype} {M}x{N}x{K} out={c_code} "
+                f"variant={mg.migemm_variant_name(v)} cfg={c}")
+            C, buf, mask = run_gemm_ex(A, B, dtype, 1.5, -0.75, c_code, old, variant=v, config=c)
+            check_ex(C, A, B, dtype, 1.5, -0.75, c_code, old, ref=ref)
+            assert padding_untouched(buf, mask)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("c_code", C_CODES)
 def test_auto_selection_general_update(dtype, c_code):
     for (M, N, K) in [(1, 1, 1), (64, 64, 64), (513, 776, 256), (1000, 520, 640)]:
