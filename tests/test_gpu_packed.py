@@ -135,3 +135,31 @@ def test_packed_two_streams_changing_workspace():
     torch.cuda.synchronize()
     for (A, B, dtype, dA, dB, C, lda, ldb) in runs:
         check_ex(C.cpu(), A, B, dtype, 1.0, 0.0, 0, None)
+
+
+def test_packed_last_row_band_split():
+    """With the 128x128 tile, a last band of tile rows that would start a second
+    round of workgroups (17 x 16 tiles for 2050 x 2047) runs as a launch of its
+    own on the 64x64 tile, after the whole 128-row bands.  Cases: both operands
+    packed (ragged K, odd ldb); both read in place (aligned, K a multiple of 64),
+    also with A given transposed (the tail starts at a column of A); and the
+    general output step into 16-bit C with a padded ldc (the tail starts at a row
+    of C)."""
+    dtype = "f16"
+    cases = [(2050, 2047, 200, False, False, 0, 0),
+             (2050, 2048, 256, False, False, 0, 0),
+             (2056, 2048, 128, True, False, 0, 0),
+             (2050, 2047, 136, False, True, 2, 3)]
+    for (M, N, K, ta, tb, c_code, pad) in cases:
+        A, B = inputs.pair(M, N, K, dtype, "normal", seed=M + N + K)
+        ref = oracle_ref(A, B, dtype)
+        alpha, beta = (1.0, 0.0) if c_code == 0 else (0.5, -1.0)
+        old = None
+        if c_code:
+            old = (torch.rand((M, N), generator=torch.Generator().manual_seed(K)) - 0.5).to(
+                {1: torch.float16, 2: torch.bfloat16}[c_code])
+        say(f"packed split {_name(ta, tb)} {M}x{N}x{K} c_dtype={c_code} ldc=N+{pad}")
+        C, buf, mask = run_gemm_ex(A, B, dtype, alpha, beta, c_code, old, variant=mg.MFMA16,
+                                   config=12, ta=ta, tb=tb, ldc=N + pad)
+        check_ex(C, A, B, dtype, alpha, beta, c_code, old, ref=ref)
+        assert padding_untouched(buf, mask)
