@@ -56,6 +56,29 @@ hipError_t launch_mfma16(const GemmArgs& g, int config) {
         const bool whole256 = g.M % 256 == 0 && g.N % 256 == 0;
         return launch_packed16(g, config == 11 ? (whole256 ? 14 : 10) : 7, fallback);
     }
+    // Configuration 7 (128x128 tiles): a last band of tile rows that takes the
+    // tile count just past a whole number of rounds of workgroups on the 256
+    // CUs would run nearly alone in a round of its own (a 2050-row product: 16
+    // of 272 tiles, about two thirds of a round's time).  Those rows go to the
+    // 64x64 tile (configuration 16) in a launch of their own, after the whole
+    // 128-row bands, on the same stream.
+    if (config == 7) {
+        constexpr int64_t kCus = 256;
+        const int64_t tn = ceil_div(g.N, 128), m_main = (g.M / 128) * 128;
+        if (m_main > 0 && m_main < g.M &&
+            ceil_div((m_main / 128) * tn, kCus) < ceil_div(ceil_div(g.M, 128) * tn, kCus)) {
+            GemmArgs head = g, tail = g;
+            head.M = m_main;
+            tail.M = g.M - m_main;
+            // row m_main of A: a column offset when A is given transposed (K x M)
+            const int64_t a_off = g.ta ? m_main : m_main * g.lda;
+            tail.A = static_cast<const char*>(g.A) + a_off * 2;  // FP16/BF16 elements
+            const int64_t c_es = (g.out.c_dtype == 1 || g.out.c_dtype == 2) ? 2 : 4;
+            tail.out.C = static_cast<char*>(g.out.C) + m_main * g.out.ldc * c_es;
+            const hipError_t e = launch_mfma16(head, 7);
+            return e != hipSuccess ? e : launch_mfma16(tail, 16);
+        }
+    }
     if (g.general()) return launch_mfma16_general(g, config);
     return g.dtype == 1 ? launch_typed<_Float16, false>(g, config)
                         : launch_typed<bf16_t, false>(g, config);

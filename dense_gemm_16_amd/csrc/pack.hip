@@ -175,31 +175,6 @@ hipError_t reserve(Workspace& w, size_t bytes) {
     return hipSuccess;
 }
 
-// The product on operands the direct kernel reads in place.  With the 128x128
-// tile, a last band of tile rows that pushes the tile count just past one
-// round of workgroups on the 256 CUs would run nearly alone in a second round
-// (a 2050-row product: 16 of 272 tiles, about two thirds of a round's time).
-// Those rows go to the 64x64 tile in a launch of their own, after the whole
-// 128-row bands, on the same stream.
-hipError_t launch_inner(const GemmArgs& p, int inner_config) {
-    constexpr int64_t kCus = 256;
-    const int64_t tn = ceil_div(p.N, 128);
-    const int64_t m_main = (p.M / 128) * 128;
-    if (inner_config != 7 || m_main == 0 || m_main == p.M || (m_main / 128) * tn > kCus ||
-        ceil_div(p.M, 128) * tn <= kCus)
-        return launch_mfma16(p, inner_config);
-    GemmArgs head = p, tail = p;
-    head.M = m_main;
-    tail.M = p.M - m_main;
-    // row m_main of A: a column offset when A is given transposed (K x M)
-    const int64_t a_off = p.ta ? m_main : m_main * p.lda;
-    tail.A = static_cast<const char*>(p.A) + a_off * 2;  // FP16/BF16 elements
-    const int64_t c_es = (p.out.c_dtype == 1 || p.out.c_dtype == 2) ? 2 : 4;
-    tail.out.C = static_cast<char*>(p.out.C) + m_main * p.out.ldc * c_es;
-    const hipError_t e = launch_mfma16(head, 7);
-    return e != hipSuccess ? e : launch_mfma16(tail, 16);
-}
-
 }  // namespace
 
 int64_t packed_k(int64_t K) { return ceil_div(K, 64) * 64; }
@@ -215,7 +190,7 @@ hipError_t launch_packed16(const GemmArgs& g, int inner_config, int fallback_con
     const bool b_in_place = k_ok && aligned16(g.B) && g.ldb % 8 == 0 && (g.tb || g.N % 8 == 0);
     const int64_t a_bytes = a_in_place ? 0 : ((g.M * Kp * 2 + 255) / 256) * 256;
     const int64_t b_bytes = b_in_place ? 0 : g.N * Kp * 2;
-    if (a_bytes + b_bytes == 0) return launch_inner(g, inner_config);
+    if (a_bytes + b_bytes == 0) return launch_mfma16(g, inner_config);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
         (void)hipGetLastError();
@@ -252,7 +227,7 @@ hipError_t launch_packed16(const GemmArgs& g, int inner_config, int fallback_con
             p.B = wb;
             p.ldb = Kp;
         }
-        e = launch_inner(p, inner_config);
+        e = launch_mfma16(p, inner_config);
     }
     const hipError_t r = hipEventRecord(w.last, g.stream);
     w.last_stream = g.stream;

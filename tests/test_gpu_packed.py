@@ -142,15 +142,20 @@ def test_packed_last_row_band_split():
     round of workgroups (17 x 16 tiles for 2050 x 2047) runs as a launch of its
     own on the 64x64 tile, after the whole 128-row bands.  Cases: both operands
     packed (ragged K, odd ldb); both read in place (aligned, K a multiple of 64),
-    also with A given transposed (the tail starts at a column of A); and the
-    general output step into 16-bit C with a padded ldc (the tail starts at a row
-    of C)."""
+    also with A given transposed (the tail starts at a column of A); the general
+    output step into 16-bit C with a padded ldc (the tail starts at a row of C);
+    and the same split on the direct path (configuration 7 called on aligned
+    operands)."""
     dtype = "f16"
-    cases = [(2050, 2047, 200, False, False, 0, 0),
-             (2050, 2048, 256, False, False, 0, 0),
-             (2056, 2048, 128, True, False, 0, 0),
-             (2050, 2047, 136, False, True, 2, 3)]
-    for (M, N, K, ta, tb, c_code, pad) in cases:
+    # (M, N, K, ta, tb, C dtype code, ldc padding, configuration): 12 packs or
+    # reads in place, then runs 7; 7 on aligned operands is the direct path
+    cases = [(2050, 2047, 200, False, False, 0, 0, 12),
+             (2050, 2048, 256, False, False, 0, 0, 12),
+             (2056, 2048, 128, True, False, 0, 0, 12),
+             (2050, 2047, 136, False, True, 2, 3, 12),
+             (2050, 2048, 256, False, False, 0, 0, 7),
+             (2056, 2048, 192, True, False, 1, 8, 7)]
+    for (M, N, K, ta, tb, c_code, pad, cfg) in cases:
         A, B = inputs.pair(M, N, K, dtype, "normal", seed=M + N + K)
         ref = oracle_ref(A, B, dtype)
         alpha, beta = (1.0, 0.0) if c_code == 0 else (0.5, -1.0)
@@ -158,8 +163,8 @@ def test_packed_last_row_band_split():
         if c_code:
             old = (torch.rand((M, N), generator=torch.Generator().manual_seed(K)) - 0.5).to(
                 {1: torch.float16, 2: torch.bfloat16}[c_code])
-        say(f"packed split {_name(ta, tb)} {M}x{N}x{K} c_dtype={c_code} ldc=N+{pad}")
+        say(f"last-band split cfg={cfg} {_name(ta, tb)} {M}x{N}x{K} c_dtype={c_code} ldc=N+{pad}")
         C, buf, mask = run_gemm_ex(A, B, dtype, alpha, beta, c_code, old, variant=mg.MFMA16,
-                                   config=12, ta=ta, tb=tb, ldc=N + pad)
+                                   config=cfg, ta=ta, tb=tb, ldc=N + pad)
         check_ex(C, A, B, dtype, alpha, beta, c_code, old, ref=ref)
         assert padding_untouched(buf, mask)
