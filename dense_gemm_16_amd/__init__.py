@@ -4,9 +4,9 @@ Argument marshalling only: every step of the product runs in the library's HIP
 kernels.  The functions named ``migemm_*`` mirror the C ABI in
 ``include/migemm.h`` one for one (integers and raw device pointers);
 ``gemm`` is a convenience wrapper over torch tensors that derives the sizes,
-leading dimensions, pointers and the current stream and calls
-``migemm_gemm_variant`` (or ``migemm_gemm_ex_variant`` for a scaled update or an
-FP16/BF16 output).
+leading dimensions, pointers and the current stream, lends the workspace that
+``migemm_workspace_size`` asks for (a torch allocation on the same stream) and
+calls ``migemm_gemm_ws``.
 
 The library is loaded on first use from this package's directory.  If it has
 not been built, every call raises ``RuntimeError``: there is no fallback.
@@ -20,12 +20,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_HERE, "libmigemm.so")
 
 F32, F16, BF16, I8, I32 = 0, 1, 2, 3, 4
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 OP_N, OP_T = 0, 1
 VARIANT_AUTO, NAIVE, LDS_TILED, REGTILE_VALU, REGTILE_MFMA, MFMA16, MFMA_I8 = -1, 0, 1, 2, 3, 4, 5
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ("migemm_gemm", "migemm_gemm_variant", "migemm_gemm_ex", "migemm_gemm_ex_variant",
+           "migemm_gemm_ws", "migemm_workspace_size", "migemm_describe", "migemm_describe_ex",
            "migemm_convert",
            "migemm_variant_count", "migemm_variant_name",
            "migemm_variant_supports", "migemm_config_count", "migemm_config_name",
@@ -64,6 +65,17 @@ def lib():
     L.migemm_gemm_ex_variant.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, vp, i64, vp, i64,
                                          f32, f32, i32, vp, i64, vp]
     L.migemm_gemm_ex_variant.restype = i32
+    L.migemm_gemm_ws.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, vp, i64, vp, i64,
+                                 f32, f32, i32, vp, i64, vp, i64, vp]
+    L.migemm_gemm_ws.restype = i32
+    L.migemm_workspace_size.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, vp, i64, vp,
+                                        i64, ctypes.POINTER(i64)]
+    L.migemm_workspace_size.restype = i32
+    L.migemm_describe.argtypes = [i64, i64, i64, i32, i64, i64, i64, cp, i32]
+    L.migemm_describe.restype = i32
+    L.migemm_describe_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, vp, i64, vp, i64,
+                                     i32, i64, i64, cp, i32]
+    L.migemm_describe_ex.restype = i32
     L.migemm_convert.argtypes = [i32, i32, i64, i64, vp, i64, vp, i64, vp]
     L.migemm_convert.restype = i32
     L.migemm_variant_count.argtypes = []
@@ -111,6 +123,53 @@ def migemm_gemm_ex_variant(variant, config, op_a, op_b, M, N, K, dtype, A, lda, 
                            beta, c_dtype, C, ldc, stream=None) -> int:
     return lib().migemm_gemm_ex_variant(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B,
                                         ldb, alpha, beta, c_dtype, C, ldc, stream)
+
+
+def migemm_gemm_ws(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha, beta,
+                   c_dtype, C, ldc, workspace, workspace_bytes, stream=None) -> int:
+    return lib().migemm_gemm_ws(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb,
+                                alpha, beta, c_dtype, C, ldc, workspace, workspace_bytes, stream)
+
+
+def migemm_workspace_size(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb):
+    """(status, bytes) of the workspace migemm_gemm_ws would use."""
+    n = ctypes.c_int64(-1)
+    st = lib().migemm_workspace_size(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb,
+                                     ctypes.byref(n))
+    return st, n.value
+
+
+def _parse_description(text: str) -> dict:
+    out = {}
+    for item in text.split(";"):
+        if "=" in item:
+            k, v = item.split("=", 1)
+            out[k] = int(v) if v.lstrip("-").isdigit() else v
+    return out
+
+
+def migemm_describe(M, N, K, dtype, lda, ldb, ldc, buflen=8192):
+    """(status, text) describing what migemm_gemm would run."""
+    buf = ctypes.create_string_buffer(buflen)
+    st = lib().migemm_describe(M, N, K, dtype, lda, ldb, ldc, buf, buflen)
+    return st, buf.value.decode()
+
+
+def migemm_describe_ex(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, c_dtype,
+                       ldc, workspace_bytes, buflen=8192):
+    """(status, text) describing what migemm_gemm_ws would run."""
+    buf = ctypes.create_string_buffer(buflen)
+    st = lib().migemm_describe_ex(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb,
+                                  c_dtype, ldc, workspace_bytes, buf, buflen)
+    return st, buf.value.decode()
+
+
+def describe(*args, **kw) -> dict:
+    """migemm_describe_ex's text parsed into a dict (integers where numeric)."""
+    st, text = migemm_describe_ex(*args, **kw)
+    if st != OK:
+        raise MigemmError(st, "migemm_describe_ex")
+    return _parse_description(text)
 
 
 def migemm_convert(src_dtype, dst_dtype, rows, cols, src, lds, dst, ldd, stream=None) -> int:
@@ -213,23 +272,45 @@ def convert(src, dtype, out=None, *, stream=None):
     return out
 
 
+def _check_device(name, t, device):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the operands on {device}")
+
+
+def workspace(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, device):
+    """A torch byte tensor on `device` large enough for migemm_gemm_ws with these
+    arguments (None when the call needs none)."""
+    import torch
+    st, n = migemm_workspace_size(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb)
+    if st != OK:
+        raise MigemmError(st, "migemm_workspace_size")
+    if n == 0:
+        return None
+    # torch's allocations are 512-byte aligned, beyond the 256 the library asks
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def gemm(a, b, out=None, *, alpha: float = 1.0, beta: float = 0.0, out_dtype=None,
          variant: int = VARIANT_AUTO, config: int = -1, stream=None):
     """out = alpha * (A x B) + beta * out on the GPU for torch tensors.
 
     ``a`` (M x K) and ``b`` (K x N) are CUDA tensors of the same dtype
-    (float32, float16 or bfloat16), each row-major or a transposed view of
-    row-major storage (``x.t()``, or a column-major tensor), passed as stored:
-    no copy is made.  ``out`` (M x N, row-major) may
-    be float32, float16 or bfloat16; if not given it is allocated with
-    ``out_dtype`` (default float32), which beta == 0 requires.  With alpha = 1,
-    beta = 0 and a float32 ``out`` this is migemm_gemm_variant, otherwise
-    migemm_gemm_ex_variant.  Runs on ``stream`` (default: torch's current stream)
-    and returns ``out`` without synchronising.
+    (float32, float16, bfloat16, or int8 with an int32 ``out``) on one device,
+    each row-major or a transposed view of row-major storage (``x.t()``, or a
+    column-major tensor), passed as stored: no copy is made.  ``out`` (M x N,
+    row-major, on the same device) may be float32, float16 or bfloat16; if not
+    given it is allocated with ``out_dtype`` (default float32), which beta == 0
+    requires.  The workspace the call asks for (migemm_workspace_size) is
+    allocated by torch on the same stream and lent to migemm_gemm_ws.  Runs on
+    ``stream`` (default: torch's current stream) and returns ``out`` without
+    synchronising.
     """
     import torch
-    if a.device.type != "cuda" or b.device.type != "cuda":
-        raise ValueError("operands must be on the GPU")
+    device = a.device
+    _check_device("a", a, device)
+    _check_device("b", b, device)
     if a.dtype != b.dtype:
         raise ValueError(f"dtype mismatch: {a.dtype} vs {b.dtype}")
     dt = _dtype_code(a)
@@ -241,22 +322,25 @@ def gemm(a, b, out=None, *, alpha: float = 1.0, beta: float = 0.0, out_dtype=Non
         if beta != 0.0:
             raise ValueError("beta != 0 needs an existing out")
         default = torch.int32 if a.dtype == torch.int8 else torch.float32
-        out = torch.empty((M, N), dtype=out_dtype or default, device=a.device)
-    elif tuple(out.shape) != (M, N) or (out_dtype is not None and out.dtype != out_dtype):
-        raise ValueError("out must have shape (M, N) (and out_dtype, if given)")
+        out = torch.empty((M, N), dtype=out_dtype or default, device=device)
+    else:
+        _check_device("out", out, device)
+        if tuple(out.shape) != (M, N) or (out_dtype is not None and out.dtype != out_dtype):
+            raise ValueError("out must have shape (M, N) (and out_dtype, if given)")
     cd = _dtype_code(out)
     if stream is None:
-        stream = torch.cuda.current_stream(a.device).cuda_stream
+        stream = torch.cuda.current_stream(device).cuda_stream
     pa, pb, pc = a.data_ptr() or None, b.data_ptr() or None, out.data_ptr() or None
     (op_a, lda), (op_b, ldb) = _operand(a), _operand(b)
-    if alpha == 1.0 and beta == 0.0 and cd == F32 and op_a == OP_N and op_b == OP_N:
-        st = migemm_gemm_variant(variant, config, M, N, K, dt, pa, lda, pb, ldb, pc, _ld(out),
-                                 stream)
-        where = "migemm_gemm_variant"
-    else:
-        st = migemm_gemm_ex_variant(variant, config, op_a, op_b, M, N, K, dt, pa, lda, pb, ldb,
-                                    float(alpha), float(beta), cd, pc, _ld(out), stream)
-        where = "migemm_gemm_ex_variant"
+    ws = workspace(variant, config, op_a, op_b, M, N, K, dt, pa, lda, pb, ldb, device)
+    if ws is not None and stream != torch.cuda.current_stream(device).cuda_stream:
+        # the block goes back to torch's pool when `ws` dies; keep it from being
+        # reused before the work queued on `stream` has finished
+        ws.record_stream(torch.cuda.ExternalStream(stream, device=device))
+    st = migemm_gemm_ws(variant, config, op_a, op_b, M, N, K, dt, pa, lda, pb, ldb,
+                        float(alpha), float(beta), cd, pc, _ld(out),
+                        ws.data_ptr() if ws is not None else None,
+                        ws.numel() if ws is not None else 0, stream)
     if st != OK:
-        raise MigemmError(st, where)
+        raise MigemmError(st, "migemm_gemm_ws")
     return out

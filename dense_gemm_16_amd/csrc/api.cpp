@@ -1,15 +1,19 @@
 // api.cpp -- the C ABI (migemm.h): argument checks, the variant registry,
-// the deterministic selection table, and stream-ordered launch.
+// the deterministic selection table, stream-ordered launch, and the
+// description of a call's kernels.
 //
 // The library's interface is a status-returning call in the manner of the
 // vendor GEMM call on page "matmul_registers.cu" (section on the library
 // comparison, where the status goes back to the caller rather than aborting):
-// nothing here prints, throws or exits.  The one allocation is the workspace of
-// the packed FP16/BF16 configurations (pack.hip): a buffer per device, allocated
-// on first use and kept; a call that needs a larger one waits for the previous
-// user of the buffer before reallocating it, the only host-side wait.
+// nothing here prints, throws or exits.  The library allocates no device
+// memory: the one path that needs scratch memory (packed FP16/BF16 operands,
+// pack.hip) takes it from a workspace the caller lends to migemm_gemm_ws, and
+// runs a path that needs none when no workspace is lent.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+
+#include <string>
 
 #include "common.hpp"
 #include "migemm.h"
@@ -20,7 +24,7 @@ namespace {
 // Sizes are limited so that every index product fits in 64 bits:
 // a dimension below 2^31 times a leading dimension below 2^32.
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
-constexpr int64_t kMaxLd = int64_t(1) << 32;
+constexpr int64_t kMaxLd = int64_t(1) << 32;  // leading dimensions must be below this
 // M * N * K from which a 16-bit product the direct kernel cannot read in place
 // is run on packed copies (pack.hip) rather than by the register-staged kernel.
 constexpr double kPackMinWork = 134217728.0;  // 2^27, e.g. 512^3
@@ -55,11 +59,19 @@ int elem_size(int dtype) {
 // most 2^17 - 1 of them stay below 2^31 and fit INT32 exactly.
 constexpr int64_t kMaxKi8 = (int64_t(1) << 17) - 1;
 
-// Byte range [lo, hi) touched by a rows x cols row-major operand with leading dimension ld.
-void extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int es, uintptr_t& lo,
+// Byte range [lo, hi) touched by a rows x cols row-major operand (rows, cols >= 1)
+// with leading dimension ld.  False when the range does not fit the address
+// space: (rows - 1) ld + cols reaches 2^63 at the size limits, so the bytes are
+// counted in 128 bits.
+bool extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int es, uintptr_t& lo,
             uintptr_t& hi) {
     lo = reinterpret_cast<uintptr_t>(p);
-    hi = lo + static_cast<uintptr_t>(((rows - 1) * ld + cols) * es);
+    const unsigned __int128 bytes =
+        (static_cast<unsigned __int128>(rows - 1) * static_cast<unsigned __int128>(ld) +
+         static_cast<unsigned __int128>(cols)) * static_cast<unsigned __int128>(es);
+    if (bytes > static_cast<unsigned __int128>(UINTPTR_MAX - lo)) return false;
+    hi = lo + static_cast<uintptr_t>(bytes);
+    return true;
 }
 
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
@@ -84,24 +96,19 @@ int check_args(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, con
     auto at_least = [](int64_t ld, int64_t cols) { return ld >= (cols > 1 ? cols : 1); };
     if (!at_least(lda, ta ? M : K) || !at_least(ldb, tb ? K : N) || !at_least(ldc, N))
         return MIGEMM_ERR_INVALID_ARG;
-    if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return MIGEMM_ERR_INVALID_ARG;
+    if (lda >= kMaxLd || ldb >= kMaxLd || ldc >= kMaxLd) return MIGEMM_ERR_INVALID_ARG;
     if (!need_ptrs) return MIGEMM_OK;
     if ((M > 0 && K > 0 && !A) || (K > 0 && N > 0 && !B) || (M > 0 && N > 0 && !C))
         return MIGEMM_ERR_INVALID_ARG;
     if (M > 0 && N > 0) {
         const int es = elem_size(dtype);
         uintptr_t c0, c1;
-        extent(C, M, N, ldc, elem_size(c_dtype), c0, c1);
+        if (!extent(C, M, N, ldc, elem_size(c_dtype), c0, c1)) return MIGEMM_ERR_INVALID_ARG;
         if (K > 0) {
             uintptr_t a0, a1, b0, b1;
-            if (ta)
-                extent(A, K, M, lda, es, a0, a1);
-            else
-                extent(A, M, K, lda, es, a0, a1);
-            if (tb)
-                extent(B, N, K, ldb, es, b0, b1);
-            else
-                extent(B, K, N, ldb, es, b0, b1);
+            const bool fit_a = ta ? extent(A, K, M, lda, es, a0, a1) : extent(A, M, K, lda, es, a0, a1);
+            const bool fit_b = tb ? extent(B, N, K, ldb, es, b0, b1) : extent(B, K, N, ldb, es, b0, b1);
+            if (!fit_a || !fit_b) return MIGEMM_ERR_INVALID_ARG;
             if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return MIGEMM_ERR_INVALID_ARG;
         }
     }
@@ -117,10 +124,13 @@ bool operands_aligned(const void* A, int64_t lda, const void* B, int64_t ldb, in
 }
 
 // The selection table: a pure function of shape, dtype, operand layout and
-// alignment.  Sizes are bucketed by how many workgroup tiles a configuration
+// alignment, and of whether the call lent a workspace large enough for the
+// packed path.  Sizes are bucketed by how many workgroup tiles a configuration
 // would launch against the 256 CUs of an MI355X.
-void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool aligned,
-            int& variant, int& config) {
+void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
+    const int64_t M = g.M, N = g.N, K = g.K;
+    const int dtype = g.dtype;
+    const bool ta = g.ta, tb = g.tb;
     auto tiles = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
     if (dtype == MIGEMM_I8) {
         variant = MIGEMM_MFMA_I8;
@@ -145,7 +155,8 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool a
     // enough for the two extra copy launches to pay.
     const bool direct = aligned && K % 64 == 0 && (tb || N % 8 == 0) && (!ta || M % 8 == 0);
     const double work = static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K);
-    const bool pack = work >= kPackMinWork && packed_k(K) < (int64_t(1) << 21);
+    const bool pack = work >= kPackMinWork && packed_k(K) < (int64_t(1) << 21) &&
+                      packed16_workspace_ok(g);
     const bool whole256 = M % 256 == 0 && N % 256 == 0;
     if (direct && tiles(256, 256) >= 256 && whole256)
         config = 14;  // direct 256x256x64, ping-pong wave groups (whole tiles only)
@@ -167,34 +178,139 @@ void select(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, bool a
         config = 3;   // register-staged 64x64x64
 }
 
-int run(int variant, int config, int op_a, int op_b, int64_t M, int64_t N, int64_t K,
-        int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, float alpha,
-        float beta, int c_dtype, void* C, int64_t ldc, void* stream) {
+// Validates one call and resolves its variant and configuration into g.
+// need_ptrs: check pointers and overlap (a launch); false for the queries,
+// where NULL pointers stand for 256-byte aligned ones.
+int prepare(int& variant, int& config, int op_a, int op_b, int64_t M, int64_t N, int64_t K,
+            int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, float alpha,
+            float beta, int c_dtype, void* C, int64_t ldc, void* ws, int64_t ws_bytes,
+            void* stream, bool need_ptrs, GemmArgs& g) {
     if (!known_op(op_a) || !known_op(op_b)) return MIGEMM_ERR_INVALID_ARG;
     const bool ta = op_a == MIGEMM_OP_T, tb = op_b == MIGEMM_OP_T;
-    int st = check_args(M, N, K, dtype, ta, tb, A, lda, B, ldb, C, ldc, c_dtype, true);
+    int st = check_args(M, N, K, dtype, ta, tb, A, lda, B, ldb, C, ldc, c_dtype, need_ptrs);
     if (st != MIGEMM_OK) return st;
+    if (ws_bytes < 0) return MIGEMM_ERR_INVALID_ARG;
     // INT32 C takes the plain product only
     if (c_dtype == MIGEMM_I32 && (alpha != 1.0f || beta != 0.0f)) return MIGEMM_ERR_UNSUPPORTED;
+    if (!need_ptrs) {
+        // stand-ins with the alignment a fresh allocation has (pointer arithmetic only)
+        if (!A) A = reinterpret_cast<const void*>(uintptr_t(1) << 40);
+        if (!B) B = reinterpret_cast<const void*>(uintptr_t(2) << 40);
+        if (!C) C = reinterpret_cast<void*>(uintptr_t(3) << 40);
+        if (!ws && ws_bytes > 0) ws = reinterpret_cast<void*>(uintptr_t(4) << 40);
+    }
+    g = GemmArgs{M,   N,   K, dtype, ta, tb, A, lda, B, ldb,
+                 Epi{C, ldc, alpha, beta, c_dtype}, static_cast<hipStream_t>(stream)};
+    g.ws = ws;
+    g.ws_bytes = ws ? ws_bytes : 0;
     const bool aligned = operands_aligned(A, lda, B, ldb, dtype);
     if (variant == MIGEMM_VARIANT_AUTO) {
         if (config != -1) return MIGEMM_ERR_INVALID_ARG;
-        select(M, N, K, dtype, ta, tb, aligned, variant, config);
+        select(g, aligned, variant, config);
     }
     if (variant < 0 || variant >= kNumVariants) return MIGEMM_ERR_INVALID_ARG;
     const Variant& v = kVariants[variant];
     if (!(v.dtype_mask & (1u << dtype))) return MIGEMM_ERR_UNSUPPORTED;
     if (config == -1) {
         int sv, sc;
-        select(M, N, K, dtype, ta, tb, aligned, sv, sc);
+        select(g, aligned, sv, sc);
         config = (sv == variant) ? sc : 0;
     }
     if (config < 0 || config >= v.count()) return MIGEMM_ERR_INVALID_ARG;
-    if (M == 0 || N == 0) return MIGEMM_OK;
+    return MIGEMM_OK;
+}
 
-    const GemmArgs g{M,   N,   K, dtype, ta, tb, A, lda, B, ldb,
-                     Epi{C, ldc, alpha, beta, c_dtype}, static_cast<hipStream_t>(stream)};
-    const hipError_t err = K == 0 ? launch_empty_product(g) : v.launch(g, config);
+// Launches the product g with the variant's configuration (or, for K == 0, the
+// empty product; nothing for an empty C).
+hipError_t launch(const GemmArgs& g, int variant, int config) {
+    if (g.M == 0 || g.N == 0) return hipSuccess;
+    return g.K == 0 ? launch_empty_product(g) : kVariants[variant].launch(g, config);
+}
+
+// Workspace bytes the call's configuration uses when lent at least that many:
+// the packed FP16/BF16 configurations' copies, nothing for the others.
+int64_t config_workspace_bytes(const GemmArgs& g, int variant, int config) {
+    if (variant != MIGEMM_MFMA16 || (config != 11 && config != 12)) return 0;
+    if (g.M == 0 || g.N == 0 || g.K == 0) return 0;
+    return packed16_workspace_bytes(g);
+}
+
+// key=value pairs, separated by ';', describing the call's kernels.
+std::string describe(const GemmArgs& g0, int variant, int config) {
+    GemmArgs g = g0;
+    LaunchInfo info;
+    g.query = &info;
+    (void)launch(g, variant, config);
+    char tmp[256];
+    std::string out;
+    auto put = [&](const char* key, const std::string& value) {
+        if (!out.empty()) out += ';';
+        out += key;
+        out += '=';
+        out += value;
+    };
+    auto num = [&](long long v) {
+        snprintf(tmp, sizeof tmp, "%lld", v);
+        return std::string(tmp);
+    };
+    put("variant", kVariants[variant].name);
+    put("config", num(config));
+    put("config_name", kVariants[variant].config_name(config));
+    put("workspace_bytes", num(config_workspace_bytes(g0, variant, config)));
+    put("workspace_lent", num(g0.ws ? g0.ws_bytes : 0));
+    put("launches", num(info.count));
+    for (int i = 0; i < info.count && i < LaunchInfo::kMax; ++i) {
+        const std::string k = num(i);
+        put(("grid" + k).c_str(), num(info.grid[i]));
+        put(("block" + k).c_str(), num(info.block[i]));
+        hipFuncAttributes attr{};
+        hipError_t e = hipFuncGetAttributes(&attr, info.fn[i]);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            put(("resources" + k).c_str(), "unavailable (hipError_t " + num(e) + ")");
+            continue;
+        }
+        const char* name = hipKernelNameRefByPtr(info.fn[i], nullptr);
+        (void)hipGetLastError();
+        if (name) put(("kernel" + k).c_str(), name);
+        put(("regs" + k).c_str(), num(attr.numRegs));
+        put(("lds_bytes" + k).c_str(), num(static_cast<long long>(attr.sharedSizeBytes)));
+        put(("scratch_bytes" + k).c_str(), num(static_cast<long long>(attr.localSizeBytes)));
+        put(("max_block" + k).c_str(), num(attr.maxThreadsPerBlock));
+        int blocks = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, info.fn[i],
+                                                         static_cast<int>(info.block[i]), 0) ==
+            hipSuccess) {
+            put(("workgroups_per_cu" + k).c_str(), num(blocks));
+            put(("waves_per_simd" + k).c_str(),
+                num(static_cast<long long>(blocks) * ((info.block[i] + kWave - 1) / kWave) / 4));
+        } else {
+            (void)hipGetLastError();
+        }
+    }
+    return out;
+}
+
+int write_text(const std::string& text, char* buf, int buflen) {
+    if (!buf || buflen <= 0) return MIGEMM_ERR_INVALID_ARG;
+    const size_t n = text.size() < static_cast<size_t>(buflen - 1) ? text.size()
+                                                                    : static_cast<size_t>(buflen - 1);
+    text.copy(buf, n);
+    buf[n] = '\0';
+    return n == text.size() ? MIGEMM_OK : MIGEMM_ERR_INVALID_ARG;
+}
+
+}  // namespace
+
+int run_gemm(int variant, int config, int op_a, int op_b, int64_t M, int64_t N, int64_t K,
+             int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, float alpha,
+             float beta, int c_dtype, void* C, int64_t ldc, void* ws, int64_t ws_bytes,
+             void* stream) {
+    GemmArgs g{};
+    const int st = prepare(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha,
+                           beta, c_dtype, C, ldc, ws, ws_bytes, stream, true, g);
+    if (st != MIGEMM_OK) return st;
+    const hipError_t err = launch(g, variant, config);
     if (err != hipSuccess) {
         g_last_hip_error = static_cast<int>(err);
         return MIGEMM_ERR_HIP;
@@ -202,7 +318,21 @@ int run(int variant, int config, int op_a, int op_b, int64_t M, int64_t N, int64
     return MIGEMM_OK;
 }
 
-}  // namespace
+int workspace_bytes(int variant, int config, int op_a, int op_b, int64_t M, int64_t N,
+                    int64_t K, int dtype, const void* A, int64_t lda, const void* B,
+                    int64_t ldb, int64_t* bytes) {
+    if (!bytes) return MIGEMM_ERR_INVALID_ARG;
+    GemmArgs g{};
+    // as if an unbounded workspace were lent, so the selection may pick the packed path
+    const int c_dtype = dtype == MIGEMM_I8 ? MIGEMM_I32 : MIGEMM_F32;
+    const int st = prepare(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, 1.0f,
+                           0.0f, c_dtype, nullptr, N > 1 ? N : 1, nullptr, INT64_MAX, nullptr,
+                           false, g);
+    if (st != MIGEMM_OK) return st;
+    *bytes = config_workspace_bytes(g, variant, config);
+    return MIGEMM_OK;
+}
+
 }  // namespace migemm
 
 using namespace migemm;
@@ -211,30 +341,66 @@ extern "C" {
 
 int migemm_gemm(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
                 const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-    return run(MIGEMM_VARIANT_AUTO, -1, MIGEMM_OP_N, MIGEMM_OP_N, M, N, K, dtype, A, lda, B, ldb,
-               1.0f, 0.0f, MIGEMM_F32, C, ldc, stream);
+    return run_gemm(MIGEMM_VARIANT_AUTO, -1, MIGEMM_OP_N, MIGEMM_OP_N, M, N, K, dtype, A, lda, B,
+                    ldb, 1.0f, 0.0f, MIGEMM_F32, C, ldc, nullptr, 0, stream);
 }
 
 int migemm_gemm_variant(int variant, int config, int64_t M, int64_t N, int64_t K, int dtype,
                         const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
                         int64_t ldc, void* stream) {
-    return run(variant, config, MIGEMM_OP_N, MIGEMM_OP_N, M, N, K, dtype, A, lda, B, ldb, 1.0f,
-               0.0f, MIGEMM_F32, C, ldc, stream);
+    return run_gemm(variant, config, MIGEMM_OP_N, MIGEMM_OP_N, M, N, K, dtype, A, lda, B, ldb,
+                    1.0f, 0.0f, MIGEMM_F32, C, ldc, nullptr, 0, stream);
 }
 
 int migemm_gemm_ex(int op_a, int op_b, int64_t M, int64_t N, int64_t K, int dtype, const void* A,
                    int64_t lda, const void* B, int64_t ldb, float alpha, float beta, int c_dtype,
                    void* C, int64_t ldc, void* stream) {
-    return run(MIGEMM_VARIANT_AUTO, -1, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha, beta,
-               c_dtype, C, ldc, stream);
+    return run_gemm(MIGEMM_VARIANT_AUTO, -1, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha,
+                    beta, c_dtype, C, ldc, nullptr, 0, stream);
 }
 
 int migemm_gemm_ex_variant(int variant, int config, int op_a, int op_b, int64_t M, int64_t N,
                            int64_t K, int dtype, const void* A, int64_t lda, const void* B,
                            int64_t ldb, float alpha, float beta, int c_dtype, void* C,
                            int64_t ldc, void* stream) {
-    return run(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha, beta, c_dtype,
-               C, ldc, stream);
+    return run_gemm(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha, beta,
+                    c_dtype, C, ldc, nullptr, 0, stream);
+}
+
+int migemm_gemm_ws(int variant, int config, int op_a, int op_b, int64_t M, int64_t N, int64_t K,
+                   int dtype, const void* A, int64_t lda, const void* B, int64_t ldb,
+                   float alpha, float beta, int c_dtype, void* C, int64_t ldc, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
+    return run_gemm(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha, beta,
+                    c_dtype, C, ldc, workspace, workspace_bytes, stream);
+}
+
+int migemm_workspace_size(int variant, int config, int op_a, int op_b, int64_t M, int64_t N,
+                          int64_t K, int dtype, const void* A, int64_t lda, const void* B,
+                          int64_t ldb, int64_t* bytes) {
+    return workspace_bytes(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, bytes);
+}
+
+int migemm_describe(int64_t M, int64_t N, int64_t K, int dtype, int64_t lda, int64_t ldb,
+                    int64_t ldc, char* buf, int buflen) {
+    const int c_dtype = dtype == MIGEMM_I8 ? MIGEMM_I32 : MIGEMM_F32;
+    return migemm_describe_ex(MIGEMM_VARIANT_AUTO, -1, MIGEMM_OP_N, MIGEMM_OP_N, M, N, K, dtype,
+                              nullptr, lda, nullptr, ldb, c_dtype, ldc, 0, buf, buflen);
+}
+
+int migemm_describe_ex(int variant, int config, int op_a, int op_b, int64_t M, int64_t N,
+                       int64_t K, int dtype, const void* A, int64_t lda, const void* B,
+                       int64_t ldb, int c_dtype, int64_t ldc, int64_t workspace_bytes, char* buf,
+                       int buflen) {
+    if (!buf || buflen <= 0) return MIGEMM_ERR_INVALID_ARG;
+    buf[0] = '\0';
+    GemmArgs g{};
+    const float alpha = 1.0f, beta = 0.0f;
+    const int st = prepare(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha,
+                           beta, c_dtype, nullptr, ldc, nullptr, workspace_bytes, nullptr, false,
+                           g);
+    if (st != MIGEMM_OK) return st;
+    return write_text(describe(g, variant, config), buf, buflen);
 }
 
 int migemm_convert(int src_dtype, int dst_dtype, int64_t rows, int64_t cols, const void* src,
@@ -281,14 +447,16 @@ const char* migemm_config_name(int variant, int config) {
 int migemm_select(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
                   const void* B, int64_t ldb, const float* C, int64_t ldc, int* variant,
                   int* config) {
-    (void)A;
-    (void)B;
-    (void)C;
-    const int c_dtype = dtype == MIGEMM_I8 ? MIGEMM_I32 : MIGEMM_F32;
-    int st = check_args(M, N, K, dtype, false, false, A, lda, B, ldb, C, ldc, c_dtype, false);
-    if (st != MIGEMM_OK) return st;
     if (!variant || !config) return MIGEMM_ERR_INVALID_ARG;
-    select(M, N, K, dtype, false, false, operands_aligned(A, lda, B, ldb, dtype), *variant, *config);
+    const int c_dtype = dtype == MIGEMM_I8 ? MIGEMM_I32 : MIGEMM_F32;
+    int v = MIGEMM_VARIANT_AUTO, c = -1;
+    GemmArgs g{};
+    const int st = prepare(v, c, MIGEMM_OP_N, MIGEMM_OP_N, M, N, K, dtype, A, lda, B, ldb, 1.0f,
+                           0.0f, c_dtype, const_cast<float*>(C), ldc, nullptr, 0, nullptr, false,
+                           g);
+    if (st != MIGEMM_OK) return st;
+    *variant = v;
+    *config = c;
     return MIGEMM_OK;
 }
 
@@ -298,12 +466,14 @@ const char* migemm_status_string(int status) {
         case MIGEMM_ERR_INVALID_ARG: return "invalid argument";
         case MIGEMM_ERR_UNSUPPORTED: return "variant does not support this dtype";
         case MIGEMM_ERR_HIP: return "HIP runtime error";
+        case MIGEMM_ERR_WORKSPACE:
+            return "the product needs more scratch memory than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }
 
 int migemm_last_hip_error(void) { return g_last_hip_error; }
 
-int migemm_version(void) { return 500; }
+int migemm_version(void) { return 600; }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace migemm {
 
 // The output step of one product: where C lives and how the FP32 sum of
@@ -21,9 +23,28 @@ struct Epi {
     int c_dtype;  // 0 FP32, 1 FP16, 2 BF16, 4 INT32 (INT8 products only; plain overwrite)
 };
 
+// The kernels one call would launch, recorded instead of launched when a
+// GemmArgs carries a query (migemm_describe): host stubs for the HIP attribute
+// queries, with each launch's workgroup count and size.
+struct LaunchInfo {
+    static constexpr int kMax = 4;
+    int count = 0;
+    const void* fn[kMax] = {};
+    unsigned grid[kMax] = {}, block[kMax] = {};
+    void add(const void* f, unsigned g, unsigned b) {
+        if (count < kMax) {
+            fn[count] = f;
+            grid[count] = g;
+            block[count] = b;
+        }
+        ++count;
+    }
+};
+
 // Arguments of one product, already validated by the C ABI.  ta: A is given
 // transposed, stored K x M (element (i, k) at A[k * lda + i]); tb: B is given
-// transposed, stored N x K (element (k, j) at B[j * ldb + k]).
+// transposed, stored N x K (element (k, j) at B[j * ldb + k]).  ws / ws_bytes:
+// device workspace the caller lent to this call (packed operands), or none.
 struct GemmArgs {
     int64_t M, N, K;
     int dtype;
@@ -34,9 +55,26 @@ struct GemmArgs {
     int64_t ldb;
     Epi out;
     hipStream_t stream;
+    void* ws = nullptr;
+    int64_t ws_bytes = 0;
+    LaunchInfo* query = nullptr;
     // True unless the output step is the plain FP32 overwrite.
     bool general() const { return !(out.alpha == 1.0f && out.beta == 0.0f && out.c_dtype == 0); }
 };
+
+// Launches fn<<<grid, block>>>(args...) on the call's stream, or, when the call
+// is a query, records the launch instead.
+template <typename... P, typename... Args>
+hipError_t launch_kernel(const GemmArgs& g, void (*fn)(P...), dim3 grid, dim3 block,
+                         Args&&... args) {
+    if (g.query) {
+        g.query->add(reinterpret_cast<const void*>(fn), grid.x * grid.y * grid.z,
+                     block.x * block.y * block.z);
+        return hipSuccess;
+    }
+    fn<<<grid, block, 0, g.stream>>>(std::forward<Args>(args)...);
+    return hipGetLastError();
+}
 
 // Storage of a bfloat16 element: its 16 bits.
 struct bf16_t {
@@ -154,12 +192,20 @@ hipError_t launch_lds_tiled(const GemmArgs& a, int config);
 hipError_t launch_regtile_valu(const GemmArgs& a, int config);
 hipError_t launch_regtile_mfma(const GemmArgs& a, int config);
 hipError_t launch_mfma16(const GemmArgs& a, int config);
-// Packs A and B into zero-padded k-contiguous copies (workspace from a
-// per-device stream-ordered pool) and runs mfma16 configuration inner_config on
-// them; runs fallback_config in place if no workspace can be had (pack.hip).
+// Packs the operands the direct kernel cannot read in place into zero-padded
+// k-contiguous copies in the call's workspace and runs mfma16 configuration
+// inner_config on them; runs fallback_config in place when the call lent no
+// workspace of packed16_workspace_bytes(a) bytes (pack.hip).
 hipError_t launch_packed16(const GemmArgs& a, int inner_config, int fallback_config);
-// K rounded up to the 64-k tile of the packed copies.
+// Workspace bytes the packed path needs for these arguments (0: both operands
+// are read in place), and K rounded up to the 64-k tile of the packed copies.
+int64_t packed16_workspace_bytes(const GemmArgs& a);
+// True when the call lent a workspace the packed path can use: non-null,
+// kWorkspaceAlign-aligned and at least packed16_workspace_bytes(a) long.
+bool packed16_workspace_ok(const GemmArgs& a);
 int64_t packed_k(int64_t K);
+// Alignment the packed path asks of a workspace.
+constexpr int64_t kWorkspaceAlign = 256;
 hipError_t launch_mfma_i8(const GemmArgs& a, int config);
 // K == 0: the sum of products is 0 for every element; applies the output step to it.
 hipError_t launch_empty_product(const GemmArgs& a);
@@ -168,6 +214,19 @@ hipError_t launch_empty_product(const GemmArgs& a);
 // round to nearest even where narrower.
 hipError_t launch_convert(int src_dtype, int dst_dtype, int64_t rows, int64_t cols,
                           const void* src, int64_t lds, void* dst, int64_t ldd, hipStream_t s);
+
+// The C ABI's common path (api.cpp): validates one call, selects its variant
+// and configuration (variant -1: the selection table's; config -1: the table's
+// choice for the variant), and launches it with the workspace lent (ws may be
+// NULL).  Returns a migemm_status.
+int run_gemm(int variant, int config, int op_a, int op_b, int64_t M, int64_t N, int64_t K,
+             int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, float alpha,
+             float beta, int c_dtype, void* C, int64_t ldc, void* ws, int64_t ws_bytes,
+             void* stream);
+// The workspace bytes such a call uses when lent enough (api.cpp).
+int workspace_bytes(int variant, int config, int op_a, int op_b, int64_t M, int64_t N,
+                    int64_t K, int dtype, const void* A, int64_t lda, const void* B,
+                    int64_t ldb, int64_t* bytes);
 
 // Configuration tables, one per variant (names, and the count).
 int naive_config_count();

@@ -23,13 +23,9 @@ __global__ __launch_bounds__(256) void empty_product_kernel(Epi out, int64_t M, 
 hipError_t launch_empty_product(const GemmArgs& g) {
     int64_t blocks = ceil_div(g.M * g.N, 256);
     if (blocks > 65536) blocks = 65536;
-    if (g.general())
-        empty_product_kernel<true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, g.stream>>>(
-            g.out, g.M, g.N);
-    else
-        empty_product_kernel<false><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, g.stream>>>(
-            g.out, g.M, g.N);
-    return hipGetLastError();
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    if (g.general()) return launch_kernel(g, empty_product_kernel<true>, grid, block, g.out, g.M, g.N);
+    return launch_kernel(g, empty_product_kernel<false>, grid, block, g.out, g.M, g.N);
 }
 
 }  // namespace migemm

@@ -66,10 +66,9 @@ hipError_t launch_layout(const GemmArgs& g) {
     const int64_t gy = ceil_div(g.M, T);
     dim3 grid(static_cast<unsigned>(ceil_div(g.N, T)),
               static_cast<unsigned>(gy > 65535 ? 65535 : gy));
-    lds_tiled_kernel<T, GEN, TA, TB><<<grid, dim3(T, T), 0, g.stream>>>(
-        g.M, g.N, g.K, static_cast<const float*>(g.A), g.lda, static_cast<const float*>(g.B),
-        g.ldb, g.out);
-    return hipGetLastError();
+    return launch_kernel(g, lds_tiled_kernel<T, GEN, TA, TB>, grid, dim3(T, T), g.M, g.N, g.K,
+                         static_cast<const float*>(g.A), g.lda, static_cast<const float*>(g.B),
+                         g.ldb, g.out);
 }
 
 template <int T, bool GEN>

@@ -1,7 +1,7 @@
 // mfma16.hip -- FP16/BF16 inputs, FP32 accumulation, on the gfx950 matrix
 // cores (v_mfma_f32_16x16x32_{f16,bf16} and v_mfma_f32_32x32x16_{f16,bf16}):
-// the configuration names, and the launcher for the plain FP32 overwrite of C
-// (the general output step is compiled in mfma16_general.hip).
+// the configuration names and the launcher, for the plain FP32 overwrite of C
+// and for the general output step.
 //
 // Mixed precision as on page "CUDA-Practice 09" (section on why FP32
 // accumulation is used): 16-bit inputs halve the bytes read, every product of
@@ -18,8 +18,11 @@
 //   multiple of 8.  A direct configuration asked to run where these do not hold
 //   runs the register-staged kernel with the nearest tile instead.
 // Configurations 11 and 12 (pack.hip) first copy A and B into zero-padded
-// k-contiguous images in a workspace, so that the direct kernel applies to any
-// layout, alignment and K.
+// k-contiguous images in a workspace the caller lends, so that the direct
+// kernel applies to any layout, alignment and K.
+//
+// Every other configuration's kernels are compiled in mfma16_part.hip, one
+// object per (element type, output form, configuration).
 #include "mfma16_configs.hpp"
 
 namespace migemm {
@@ -45,10 +48,29 @@ const char* const kNames[] = {
     "direct 64x64x64 8w 16x16x32 s4 early ntC"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
+template <typename E, bool GEN>
+hipError_t launch_typed(const GemmArgs& g, int config) {
+    switch (config) {
+#define MIGEMM_CASE(C) \
+    case C: return launch_cfg16<E, GEN, C>(g);
+        MIGEMM_CFG16_LIST(MIGEMM_CASE)
+#undef MIGEMM_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 int mfma16_config_count() { return kCount; }
 const char* mfma16_config_name(int c) { return (c >= 0 && c < kCount) ? kNames[c] : nullptr; }
+
+hipError_t launch_cfg16_any(const GemmArgs& g, int config) {
+    if (g.general())
+        return g.dtype == 1 ? launch_typed<_Float16, true>(g, config)
+                            : launch_typed<bf16_t, true>(g, config);
+    return g.dtype == 1 ? launch_typed<_Float16, false>(g, config)
+                        : launch_typed<bf16_t, false>(g, config);
+}
 
 hipError_t launch_mfma16(const GemmArgs& g, int config) {
     if (config == 11 || config == 12) {
@@ -79,9 +101,7 @@ hipError_t launch_mfma16(const GemmArgs& g, int config) {
             return e != hipSuccess ? e : launch_mfma16(tail, 16);
         }
     }
-    if (g.general()) return launch_mfma16_general(g, config);
-    return g.dtype == 1 ? launch_typed<_Float16, false>(g, config)
-                        : launch_typed<bf16_t, false>(g, config);
+    return launch_cfg16_any(g, config);
 }
 
 }  // namespace migemm

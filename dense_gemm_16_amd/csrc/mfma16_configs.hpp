@@ -1,82 +1,28 @@
-// mfma16_configs.hpp -- the FP16/BF16 configuration table and its launcher,
-// compiled once per output form: mfma16.hip for the plain FP32 overwrite,
-// mfma16_general.hip for the general output step (alpha, beta, FP16/BF16 C).
-// Two translation units keep each compile to one set of kernels and let the
-// build run them in parallel.
+// mfma16_configs.hpp -- the FP16/BF16 configuration table's dispatch.  Each
+// configuration is compiled on its own, once per element type and output form
+// (mfma16_part.hip, built once per (type, form, configuration) so that the
+// compiles run in parallel); mfma16.hip holds the names and the launcher.
 #pragma once
 
-#include "mfma16_direct.hpp"
+#include "common.hpp"
 
 namespace migemm {
 
-template <typename E> struct Cfgs {
-    // register-staged: any shape, leading dimension and alignment
-    using R0 = MfmaCfg<E, 256, 256, 2, 4, 16>;  // 8 waves, 128x64 per wave
-    using R1 = MfmaCfg<E, 256, 128, 2, 2, 16>;  // 4 waves, 128x64 per wave
-    using R2 = MfmaCfg<E, 128, 128, 2, 2, 16>;  // 4 waves, 64x64 per wave
-    using R3 = MfmaCfg<E, 64, 64, 2, 2, 16>;    // 4 waves, 32x32 per wave
-    using R4 = MfmaCfg<E, 256, 256, 2, 4, 32>;  // 8 waves, 32x32x16 instructions
-    // direct-staged: <E, BM, BN, WM, WN, MF, STAGES, BK, GM, SCHED, FLAGS>
-    using D5 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64>;
-    using D6 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64>;
-    using D7 = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 18>;   // 8 waves, interleave, gm4, nt C; all layouts
-    using D7P = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 16>;  // D7 with plain C stores
-    using D8 = DirectCfg<E, 128, 128, 2, 2, 16, 4, 64>;             // 4 waves, 4 stages
-    using D9 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 2>;    // gm4, interleave, nt C
-    using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 30>;  // + AGPRs, early loads; all layouts
-    using D13 = DirectCfg<E, 128, 256, 2, 4, 16, 3, 64, 8, 2, 16>;  // 8 waves of 64x64, 3 stages; all layouts
-    using D14 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 22>;  // ping-pong (whole tiles), AGPRs, nt C; all layouts
-    using D15 = DirectCfg<E, 128, 256, 2, 4, 16, 2, 64, 8, 4, 22>;  // ping-pong 128x256 (whole tiles); all layouts
-    using D16 = DirectCfg<E, 64, 64, 2, 4, 16, 4, 64, 8, 0, 26>;    // 8 waves of 32x16, 4 stages, early loads, nt C; all layouts
-    using D16P = DirectCfg<E, 64, 64, 2, 4, 16, 4, 64, 8, 0, 24>;   // D16 with plain C stores
-};
+// Configuration C of the table (indices as named in mfma16.hip) for element
+// type E, with the plain FP32 overwrite (GEN false) or the general output step.
+// Defined in mfma16_part.hip, explicitly instantiated there per part.
+template <typename E, bool GEN, int C>
+hipError_t launch_cfg16(const GemmArgs& g);
 
-template <class D, class Fallback, bool GEN>
-hipError_t direct_or(const GemmArgs& g) {
-    return direct_fits<D>(g) ? launch_direct_cfg<D, GEN>(g) : launch_mfma_cfg<Fallback, GEN>(g);
-}
+// Any configuration by index, for the element type and output form of g
+// (mfma16.hip).  A direct-staged configuration whose preconditions do not hold
+// calls this with its register-staged fallback's index.
+hipError_t launch_cfg16_any(const GemmArgs& g, int config);
 
-// Non-temporal C stores pay when every row of C starts a 128-byte line: the row
-// pieces that neighbouring 16x16 blocks store then fill whole lines.  Rows that
-// straddle lines (an odd ldc, say) split every piece into two partial-line
-// writes, which plain stores merge in L2 and non-temporal ones send on as they
-// are (the 2050 x 2047 FP16 product ran 18% slower with them).
-inline bool c_whole_lines(const Epi& o) {
-    const int64_t eb = (o.c_dtype == 1 || o.c_dtype == 2) ? 2 : 4;
-    return (o.ldc * eb) % 128 == 0 && (reinterpret_cast<uintptr_t>(o.C) & 127) == 0;
-}
-
-// Configuration `config` of the table (indices as named in mfma16.hip).  A
-// direct-staged configuration whose preconditions do not hold (or that is not
-// compiled for the operands' layout) runs the register-staged one with the same
-// or the nearest tile.
-template <typename E, bool GEN>
-hipError_t launch_typed(const GemmArgs& g, int config) {
-    using T = Cfgs<E>;
-    switch (config) {
-        case 1: return launch_mfma_cfg<typename T::R1, GEN>(g);
-        case 2: return launch_mfma_cfg<typename T::R2, GEN>(g);
-        case 3: return launch_mfma_cfg<typename T::R3, GEN>(g);
-        case 4: return launch_mfma_cfg<typename T::R4, GEN>(g);
-        case 5: return direct_or<typename T::D5, typename T::R0, GEN>(g);
-        case 6: return direct_or<typename T::D6, typename T::R0, GEN>(g);
-        case 7:
-            return c_whole_lines(g.out) ? direct_or<typename T::D7, typename T::R2, GEN>(g)
-                                        : direct_or<typename T::D7P, typename T::R2, GEN>(g);
-        case 8: return direct_or<typename T::D8, typename T::R2, GEN>(g);
-        case 9: return direct_or<typename T::D9, typename T::R0, GEN>(g);
-        case 10: return direct_or<typename T::D10, typename T::R0, GEN>(g);
-        case 13: return direct_or<typename T::D13, typename T::R2, GEN>(g);
-        case 14: return direct_or<typename T::D14, typename T::R0, GEN>(g);
-        case 15: return direct_or<typename T::D15, typename T::R2, GEN>(g);
-        case 16:
-            return c_whole_lines(g.out) ? direct_or<typename T::D16, typename T::R3, GEN>(g)
-                                        : direct_or<typename T::D16P, typename T::R3, GEN>(g);
-        default: return launch_mfma_cfg<typename T::R0, GEN>(g);
-    }
-}
-
-// The general output step over the same table (mfma16_general.hip).
-hipError_t launch_mfma16_general(const GemmArgs& g, int config);
+// Every configuration index that has a kernel of its own: the register-staged
+// 0-4 and the direct-staged 5-10 and 13-16 (11 and 12 pack, then run one of
+// these).
+#define MIGEMM_CFG16_LIST(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) \
+    X(13) X(14) X(15) X(16)
 
 }  // namespace migemm

@@ -212,14 +212,16 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 }
 
 // 16 bytes per lane from global memory (SGPR base + per-lane byte offset) into
-// LDS at lds_base + 16 * lane.  M0 carries the LDS base; nothing else in these
-// kernels uses M0.  The base is wave-uniform by construction; passing it through
-// uniform_ptr keeps the compiler from handing the asm a VGPR copy of it.
+// LDS at lds_base + 16 * lane.  M0 carries the LDS base and is declared
+// clobbered, so the compiler neither keeps a value of its own in M0 across
+// these statements nor assumes M0 unchanged after them.  The base is
+// wave-uniform by construction; passing it through uniform_ptr keeps the
+// compiler from handing the asm a VGPR copy of it.
 __device__ __forceinline__ void dma16(uint32_t lds_base, const void* sbase, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
                  : "s"(lds_base), "v"(voff), "s"(uniform_ptr(sbase))
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Wait until at most N of this wave's direct loads are outstanding (inline asm:
@@ -795,8 +797,8 @@ hipError_t launch_direct_cfg(const GemmArgs& g) {
     const E* B = static_cast<const E*>(g.B);
     const int itm = static_cast<int>(tm), itn = static_cast<int>(tn);
 #define MIGEMM_LAUNCH(TA_, TB_)                                                                \
-    mfma16_direct_kernel<Cfg, GEN, TA_, TB_><<<grid, block, 0, g.stream>>>(                    \
-        g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn)
+    return launch_kernel(g, mfma16_direct_kernel<Cfg, GEN, TA_, TB_>, grid, block, g.M, g.N,    \
+                         g.K, A, g.lda, B, g.ldb, g.out, itm, itn)
     if constexpr (Cfg::LAYOUTS) {
         if (g.ta && g.tb)
             MIGEMM_LAUNCH(true, true);
@@ -811,7 +813,6 @@ hipError_t launch_direct_cfg(const GemmArgs& g) {
         MIGEMM_LAUNCH(false, false);
     }
 #undef MIGEMM_LAUNCH
-    return hipGetLastError();
 }
 
 }  // namespace migemm

@@ -467,8 +467,8 @@ hipError_t launch_mfma_cfg(const GemmArgs& g) {
     // general output step and the transposed layouts for the two common ones
     // (both operands vectorised, or neither), which bounds the instantiations.
 #define MIGEMM_LAUNCH(AV_, BV_, TA_, TB_)                                                      \
-    mfma_gemm_kernel<Cfg, AV_, BV_, GEN, TA_, TB_><<<grid, block, 0, g.stream>>>(              \
-        g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn)
+    return launch_kernel(g, mfma_gemm_kernel<Cfg, AV_, BV_, GEN, TA_, TB_>, grid, block, g.M,   \
+                         g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn)
     const bool vec = av && bv;
     if (g.ta || g.tb) {
         if (g.ta && g.tb) {
@@ -488,7 +488,6 @@ hipError_t launch_mfma_cfg(const GemmArgs& g) {
         MIGEMM_LAUNCH(false, false, false, false);
     }
 #undef MIGEMM_LAUNCH
-    return hipGetLastError();
 }
 
 }  // namespace migemm

@@ -1,5 +1,7 @@
 // mfma_i8.hip -- INT8 inputs, exact INT32 sums, on the gfx950 integer matrix-core
-// instructions (v_mfma_i32_16x16x64_i8, v_mfma_i32_32x32x32_i8).
+// instructions (v_mfma_i32_16x16x64_i8, v_mfma_i32_32x32x32_i8): configuration
+// names and dispatch (the kernels of each configuration are compiled in
+// mfma_i8_part.hip, one object per configuration).
 //
 // The tiled matrix-unit algorithm of page "Tensor cores and matrix operations"
 // (section "Complete Algorithm for Large Matrix Multiply") on 8-bit operands:
@@ -18,17 +20,14 @@
 // 8-bit transposing LDS reads.  It needs whole 256 x 256 tiles, K a multiple of
 // 128, 16-byte aligned operands and leading dimensions in whole 16-byte chunks;
 // other shapes run configuration 0.
-#include "mfma16_direct.hpp"
+#include "common.hpp"
 
 namespace migemm {
-namespace {
 
-using I0 = MfmaCfg<int8_t, 256, 256, 2, 4, 16>;  // 8 waves, 128x64 per wave
-using I1 = MfmaCfg<int8_t, 128, 128, 2, 2, 16>;  // 4 waves, 64x64 per wave
-using I2 = MfmaCfg<int8_t, 64, 64, 2, 2, 16>;    // small problems: 4x the workgroups
-using I3 = MfmaCfg<int8_t, 256, 256, 2, 4, 32>;  // 8 waves, 32x32x32 instructions
-// direct-staged ping-pong, whole tiles only, every layout
-using D4 = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 4, 22>;
+template <int C>
+hipError_t launch_i8_cfg(const GemmArgs& g);
+
+namespace {
 
 const char* const kNames[] = {"256x256x128 8w 16x16x64", "128x128x128 4w 16x16x64",
                               "64x64x128 4w 16x16x64", "256x256x128 8w 32x32x32",
@@ -42,11 +41,11 @@ const char* mfma_i8_config_name(int c) { return (c >= 0 && c < kCount) ? kNames[
 
 hipError_t launch_mfma_i8(const GemmArgs& g, int config) {
     switch (config) {
-        case 1: return launch_mfma_cfg<I1, false>(g);
-        case 2: return launch_mfma_cfg<I2, false>(g);
-        case 3: return launch_mfma_cfg<I3, false>(g);
-        case 4: return direct_fits<D4>(g) ? launch_direct_cfg<D4, false>(g) : launch_mfma_cfg<I0, false>(g);
-        default: return launch_mfma_cfg<I0, false>(g);
+        case 1: return launch_i8_cfg<1>(g);
+        case 2: return launch_i8_cfg<2>(g);
+        case 3: return launch_i8_cfg<3>(g);
+        case 4: return launch_i8_cfg<4>(g);
+        default: return launch_i8_cfg<0>(g);
     }
 }
 

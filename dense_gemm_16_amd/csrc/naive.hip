@@ -47,22 +47,18 @@ hipError_t launch_shape(const GemmArgs& g) {
     dim3 block(BX, BY);
     switch (g.dtype) {
         case 0:
-            naive_kernel<float, BX, BY, GEN><<<grid, block, 0, g.stream>>>(
-                g.M, g.N, g.K, static_cast<const float*>(g.A), g.lda,
-                static_cast<const float*>(g.B), g.ldb, g.ta, g.tb, g.out);
-            break;
+            return launch_kernel(g, naive_kernel<float, BX, BY, GEN>, grid, block, g.M, g.N, g.K,
+                                 static_cast<const float*>(g.A), g.lda,
+                                 static_cast<const float*>(g.B), g.ldb, g.ta, g.tb, g.out);
         case 1:
-            naive_kernel<_Float16, BX, BY, GEN><<<grid, block, 0, g.stream>>>(
-                g.M, g.N, g.K, static_cast<const _Float16*>(g.A), g.lda,
-                static_cast<const _Float16*>(g.B), g.ldb, g.ta, g.tb, g.out);
-            break;
+            return launch_kernel(g, naive_kernel<_Float16, BX, BY, GEN>, grid, block, g.M, g.N,
+                                 g.K, static_cast<const _Float16*>(g.A), g.lda,
+                                 static_cast<const _Float16*>(g.B), g.ldb, g.ta, g.tb, g.out);
         default:
-            naive_kernel<bf16_t, BX, BY, GEN><<<grid, block, 0, g.stream>>>(
-                g.M, g.N, g.K, static_cast<const bf16_t*>(g.A), g.lda,
-                static_cast<const bf16_t*>(g.B), g.ldb, g.ta, g.tb, g.out);
-            break;
+            return launch_kernel(g, naive_kernel<bf16_t, BX, BY, GEN>, grid, block, g.M, g.N,
+                                 g.K, static_cast<const bf16_t*>(g.A), g.lda,
+                                 static_cast<const bf16_t*>(g.B), g.ldb, g.ta, g.tb, g.out);
     }
-    return hipGetLastError();
 }
 
 const char* const kNames[] = {"64x4 wave-per-row", "16x16 square"};

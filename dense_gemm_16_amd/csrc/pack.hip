@@ -20,14 +20,11 @@
 // LDS so that the reads (2 bytes per lane, any alignment) and the writes (16
 // bytes per lane) are contiguous across a wavefront in either orientation.
 //
-// Workspace: at most (M + N) * K' * 2 bytes of one device buffer that the
-// library allocates on first use and keeps, growing it (after the previous
-// user has finished) when a call needs more.  Calls on one stream follow each
-// other in stream order; a call on another stream first waits for an event
-// recorded after the last product that used the buffer.  Host threads take
-// turns through a mutex.  If the buffer cannot be had, the product runs on the
-// register-staged kernel instead, which reads any layout in place.
-#include <mutex>
+// Workspace: (M + N) * K' * 2 bytes at most (each copied operand, A' first,
+// rounded up to 256 bytes), lent by the caller for this one call and
+// 256-byte aligned; the library allocates nothing and keeps no pointer to it.
+// Without a large enough workspace the product runs on the register-staged
+// kernel instead, which reads any layout in place.
 
 #include "common.hpp"
 
@@ -123,115 +120,74 @@ PackJob make_job(const void* src, int64_t lds, int64_t rows, int64_t cols, bool 
     return j;
 }
 
-hipError_t launch_pack16(const PackJob& j0, const PackJob& j1, hipStream_t s) {
+hipError_t launch_pack16(const GemmArgs& g, const PackJob& j0, const PackJob& j1) {
     const int64_t tiles = j0.tiles + j1.tiles;
     if (tiles == 0) return hipSuccess;
     const unsigned grid = static_cast<unsigned>(tiles < 65536 ? tiles : 65536);
-    pack16_kernel<<<grid, 256, 0, s>>>(j0, j1);
-    return hipGetLastError();
+    return launch_kernel(g, pack16_kernel, dim3(grid), dim3(256), j0, j1);
 }
 
-// One workspace per device, kept until the process ends and only ever grown.
-// `last` is recorded on `last_stream` after each product that used it; a call
-// on another stream waits for it before its copy overwrites the workspace.
-struct Workspace {
-    void* ptr = nullptr;
-    size_t size = 0;
-    hipEvent_t last = nullptr;
-    hipStream_t last_stream = nullptr;
+// Which operands the direct kernel reads in place: a 16-byte aligned row
+// image (row-major A, B given transposed) or k-row image (A given transposed,
+// row-major B) with rows in whole 16-byte chunks, a k-row image side a
+// multiple of 8, and K a multiple of 64.
+struct PackPlan {
+    int64_t Kp, a_bytes, b_bytes;
+    bool a_in_place, b_in_place;
 };
-constexpr int kMaxDevices = 64;
-std::mutex g_ws_mutex;
-Workspace g_ws[kMaxDevices];
 
-// Makes `w` at least `bytes` long, usable on stream s.  Growing waits for the
-// previous user to finish, frees the old block and allocates max(bytes, twice
-// the old size, 16 MiB).
-hipError_t reserve(Workspace& w, size_t bytes) {
-    if (!w.last) {
-        const hipError_t e = hipEventCreateWithFlags(&w.last, hipEventDisableTiming);
-        if (e != hipSuccess) {
-            w.last = nullptr;
-            return e;
-        }
-    }
-    if (w.size >= bytes) return hipSuccess;
-    if (w.ptr) {
-        hipError_t e = hipEventSynchronize(w.last);
-        if (e == hipSuccess) e = hipFree(w.ptr);
-        if (e != hipSuccess) return e;
-        w.ptr = nullptr;
-        w.size = 0;
-    }
-    size_t want = bytes;
-    if (want < 2 * w.size) want = 2 * w.size;
-    if (want < (size_t(16) << 20)) want = size_t(16) << 20;
-    const hipError_t e = hipMalloc(&w.ptr, want);
-    if (e != hipSuccess) {
-        w.ptr = nullptr;
-        return e;
-    }
-    w.size = want;
-    return hipSuccess;
+PackPlan plan_pack(const GemmArgs& g) {
+    PackPlan p;
+    p.Kp = packed_k(g.K);
+    const bool k_ok = g.K == p.Kp;
+    p.a_in_place = k_ok && aligned16(g.A) && g.lda % 8 == 0 && (!g.ta || g.M % 8 == 0);
+    p.b_in_place = k_ok && aligned16(g.B) && g.ldb % 8 == 0 && (g.tb || g.N % 8 == 0);
+    p.a_bytes = p.a_in_place ? 0 : ceil_div(g.M * p.Kp * 2, kWorkspaceAlign) * kWorkspaceAlign;
+    p.b_bytes = p.b_in_place ? 0 : g.N * p.Kp * 2;
+    return p;
 }
 
 }  // namespace
 
 int64_t packed_k(int64_t K) { return ceil_div(K, 64) * 64; }
 
+int64_t packed16_workspace_bytes(const GemmArgs& g) {
+    const PackPlan p = plan_pack(g);
+    return p.a_bytes + p.b_bytes;
+}
+
+bool packed16_workspace_ok(const GemmArgs& g) {
+    return g.ws != nullptr && (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) == 0 &&
+           g.ws_bytes >= packed16_workspace_bytes(g);
+}
+
 hipError_t launch_packed16(const GemmArgs& g, int inner_config, int fallback_config) {
-    const int64_t Kp = packed_k(g.K);
-    // An operand the direct kernel reads in place is left where it is: a
-    // 16-byte aligned row image (row-major A, B given transposed) or k-row
-    // image (A given transposed, row-major B) with rows in whole 16-byte
-    // chunks, a k-row image side a multiple of 8, and K a multiple of 64.
-    const bool k_ok = g.K == Kp;
-    const bool a_in_place = k_ok && aligned16(g.A) && g.lda % 8 == 0 && (!g.ta || g.M % 8 == 0);
-    const bool b_in_place = k_ok && aligned16(g.B) && g.ldb % 8 == 0 && (g.tb || g.N % 8 == 0);
-    const int64_t a_bytes = a_in_place ? 0 : ((g.M * Kp * 2 + 255) / 256) * 256;
-    const int64_t b_bytes = b_in_place ? 0 : g.N * Kp * 2;
-    if (a_bytes + b_bytes == 0) return launch_mfma16(g, inner_config);
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-        (void)hipGetLastError();
-        return launch_mfma16(g, fallback_config);
-    }
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& w = g_ws[dev];
-    if (reserve(w, static_cast<size_t>(a_bytes + b_bytes)) != hipSuccess) {
-        (void)hipGetLastError();  // clear the failed call's error; run in place instead
-        return launch_mfma16(g, fallback_config);
-    }
-    if (w.last_stream != g.stream) {
-        const hipError_t e = hipStreamWaitEvent(g.stream, w.last, 0);
-        if (e != hipSuccess) return e;
-    }
-    char* const wa = static_cast<char*>(w.ptr);  // hipMalloc: 256-byte aligned
-    char* const wb = wa + a_bytes;
+    const PackPlan pl = plan_pack(g);
+    const int64_t Kp = pl.Kp;
+    if (pl.a_bytes + pl.b_bytes == 0) return launch_mfma16(g, inner_config);
+    if (!packed16_workspace_ok(g)) return launch_mfma16(g, fallback_config);
+    char* const wa = static_cast<char*>(g.ws);
+    char* const wb = wa + pl.a_bytes;
     // A' (M x K'): row-major A is copied, A given transposed (K x M) is transposed.
     // B' (N x K'): row-major B (K x N) is transposed, B given transposed is copied.
     const PackJob none = make_job(nullptr, 1, 0, 0, false, nullptr, 8, 8);
-    const PackJob ja = a_in_place ? none : make_job(g.A, g.lda, g.M, g.K, g.ta, wa, Kp, Kp);
-    const PackJob jb = b_in_place ? none : make_job(g.B, g.ldb, g.N, g.K, !g.tb, wb, Kp, Kp);
-    hipError_t e = launch_pack16(ja, jb, g.stream);
-    if (e == hipSuccess) {
-        GemmArgs p = g;
-        p.K = Kp;
-        if (!a_in_place) {
-            p.ta = false;
-            p.A = wa;
-            p.lda = Kp;
-        }
-        if (!b_in_place) {
-            p.tb = true;
-            p.B = wb;
-            p.ldb = Kp;
-        }
-        e = launch_mfma16(p, inner_config);
+    const PackJob ja = pl.a_in_place ? none : make_job(g.A, g.lda, g.M, g.K, g.ta, wa, Kp, Kp);
+    const PackJob jb = pl.b_in_place ? none : make_job(g.B, g.ldb, g.N, g.K, !g.tb, wb, Kp, Kp);
+    hipError_t e = launch_pack16(g, ja, jb);
+    if (e != hipSuccess) return e;
+    GemmArgs p = g;
+    p.K = Kp;
+    if (!pl.a_in_place) {
+        p.ta = false;
+        p.A = wa;
+        p.lda = Kp;
     }
-    const hipError_t r = hipEventRecord(w.last, g.stream);
-    w.last_stream = g.stream;
-    return e != hipSuccess ? e : r;
+    if (!pl.b_in_place) {
+        p.tb = true;
+        p.B = wb;
+        p.ldb = Kp;
+    }
+    return launch_mfma16(p, inner_config);
 }
 
 }  // namespace migemm

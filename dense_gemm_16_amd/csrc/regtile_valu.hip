@@ -188,12 +188,11 @@ hipError_t launch_gen(const GemmArgs& g) {
     const bool av = aligned16(g.A) && g.lda % 4 == 0;
     const bool bv = aligned16(g.B) && g.ldb % 4 == 0;
     const bool cv = aligned16(g.out.C) && g.out.ldc % 4 == 0;
-    regtile_valu_kernel<BM, BN, BK, TM, TN, GEN, TA, TB>
-        <<<dim3(static_cast<unsigned>(gx * gy)), dim3((BM / TM) * (BN / TN)), 0, g.stream>>>(
-            g.M, g.N, g.K, static_cast<const float*>(g.A), g.lda,
-            static_cast<const float*>(g.B), g.ldb, g.out, av, bv, cv,
-            static_cast<unsigned>(gx));
-    return hipGetLastError();
+    return launch_kernel(g, regtile_valu_kernel<BM, BN, BK, TM, TN, GEN, TA, TB>,
+                         dim3(static_cast<unsigned>(gx * gy)), dim3((BM / TM) * (BN / TN)), g.M,
+                         g.N, g.K, static_cast<const float*>(g.A), g.lda,
+                         static_cast<const float*>(g.B), g.ldb, g.out, av, bv, cv,
+                         static_cast<unsigned>(gx));
 }
 
 template <int BM, int BN, int BK, int TM, int TN, bool GEN>

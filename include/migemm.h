@@ -20,7 +20,9 @@
  * Layout.  Row-major with leading dimensions in ELEMENTS: element (i, k) of A
  * is at A[i * lda + k], (k, j) of B at B[k * ldb + j], (i, j) of C at
  * C[i * ldc + j].  Requirements: lda >= max(1, K), ldb >= max(1, N),
- * ldc >= max(1, N).  No alignment is required; 16-byte aligned pointers and
+ * ldc >= max(1, N), each leading dimension below 2^32 and M, N, K below 2^31
+ * (so every index product fits in 64 bits), and every operand's byte range
+ * inside the address space.  No alignment is required; 16-byte aligned pointers and
  * leading dimensions that are multiples of 16 bytes take the vector-load path.
  *
  * Pointers.  A, B and C are DEVICE pointers on the current HIP device, owned
@@ -28,21 +30,18 @@
  * returns.  Calls are reentrant and may come from several host threads.  C
  * must not overlap A or B.
  *
- * Workspace.  FP16/BF16 operands that the direct-staged kernel cannot read in
- * place (K not a multiple of 64, rows not 16-byte aligned in whole 16-byte
- * chunks, a k-row image side not a multiple of 8) are, for large products,
- * first copied into zero-padded k-contiguous images (mfma16 configurations 11
- * and 12).  The copies live in one device buffer per device that the library
- * allocates on first use and keeps until the process ends; it grows (at least
- * doubling) when a call needs more.  Calls on different streams that use it
- * are ordered through an event; host threads take turns through a mutex.  If
- * the buffer cannot be allocated, the product runs in place on the
- * register-staged kernel.  No other path allocates device memory.
+ * Memory.  The library allocates no device memory.  FP16/BF16 operands that
+ * the direct-staged kernel cannot read in place (K not a multiple of 64, rows
+ * not 16-byte aligned in whole 16-byte chunks, a k-row image side not a
+ * multiple of 8) are, for large products, best first copied into zero-padded
+ * k-contiguous images; that path needs device scratch memory, which the caller
+ * lends to migemm_gemm_ws (its size from migemm_workspace_size).  The other
+ * entry points lend none, and such products then run in place on the
+ * register-staged kernel: same result rules, lower speed.
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
- * stream).  Work is enqueued asynchronously on it.  The only host-side wait
- * is a workspace growth, which waits for the previous product that used the
- * buffer before freeing it.  The caller synchronises before reading C.
+ * stream).  Work is enqueued asynchronously on it; no entry point waits on the
+ * host.  The caller synchronises before reading C.
  *
  * Errors.  Every entry point returns a migemm_status; nothing prints, throws
  * or exits.  Argument errors are detected before any HIP call.  Degenerate
@@ -90,8 +89,10 @@ typedef enum {
     MIGEMM_ERR_INVALID_ARG = 1, /* negative size, ld too small, unknown dtype, NULL with data,
                                    size beyond the supported range, bad variant/config index */
     MIGEMM_ERR_UNSUPPORTED = 2, /* a forced variant that does not take this dtype */
-    MIGEMM_ERR_HIP = 3          /* the HIP runtime reported an error at launch
+    MIGEMM_ERR_HIP = 3,         /* the HIP runtime reported an error at launch
                                    (see migemm_last_hip_error) */
+    MIGEMM_ERR_WORKSPACE = 4    /* the product needs more scratch memory than the
+                                   allocation-free entry point holds */
 } migemm_status;
 
 /*
@@ -193,6 +194,74 @@ int migemm_gemm_ex_variant(int variant, int config, int op_a, int op_b,
                            const void* A, int64_t lda, const void* B, int64_t ldb,
                            float alpha, float beta, int c_dtype, void* C, int64_t ldc,
                            void* stream);
+
+/*
+ * The most general product: migemm_gemm_ex_variant (variant and config forced,
+ * or -1 for the selection table's choice) with device scratch memory lent by
+ * the caller for this one call.
+ *
+ * workspace: NULL or a device pointer on the current device, 256-byte aligned,
+ * of workspace_bytes bytes (>= 0), owned by the caller; the call's kernels
+ * write it in stream order on `stream`, and the caller must not use it for
+ * anything else until the work enqueued by this call has finished (stream
+ * order on `stream` guarantees that for later work on the same stream).  The
+ * library keeps no pointer to it after the call returns.  With at least the
+ * size migemm_workspace_size reports for the same arguments, FP16/BF16
+ * operands the direct-staged kernel cannot read in place are copied into
+ * zero-padded k-contiguous images there (the padding adds only exact zero
+ * terms to each sum, page "CUDA-Practice 09", the definition of the
+ * row-major product); a smaller, misaligned or NULL workspace is not used and
+ * the call runs a configuration that needs none.  The selection depends on
+ * whether a usable workspace was lent.  Negative workspace_bytes is
+ * MIGEMM_ERR_INVALID_ARG; otherwise the rules of migemm_gemm_ex apply.
+ */
+int migemm_gemm_ws(int variant, int config, int op_a, int op_b,
+                   int64_t M, int64_t N, int64_t K, int dtype,
+                   const void* A, int64_t lda, const void* B, int64_t ldb,
+                   float alpha, float beta, int c_dtype, void* C, int64_t ldc,
+                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Writes to *bytes the workspace migemm_gemm_ws uses for these arguments when
+ * lent at least that much (0: none; the selection that lent workspace leads
+ * to).  Pointers are only inspected for alignment and may be NULL (read as
+ * 16-byte aligned).  Same argument checks as migemm_gemm_ex, and NULL `bytes`
+ * is MIGEMM_ERR_INVALID_ARG.
+ */
+int migemm_workspace_size(int variant, int config, int op_a, int op_b,
+                          int64_t M, int64_t N, int64_t K, int dtype,
+                          const void* A, int64_t lda, const void* B, int64_t ldb,
+                          int64_t* bytes);
+
+/*
+ * A description of what migemm_gemm would run for these sizes with 16-byte
+ * aligned operands, for reports: the selected variant and configuration, the
+ * workspace it would use, and for each kernel launch its workgroup count and
+ * size and, where a GPU is present, the kernel's name, registers
+ * (hipFuncGetAttributes numRegs), LDS and scratch bytes per workgroup and
+ * workgroups per CU (occupancy).  The text is `key=value` pairs separated by
+ * ';' (keys: variant, config, config_name, workspace_bytes, workspace_lent,
+ * launches, then per launch i: grid<i>, block<i>, kernel<i>, regs<i>,
+ * lds_bytes<i>, scratch_bytes<i>, max_block<i>, workgroups_per_cu<i>,
+ * waves_per_simd<i>, or resources<i> when the attributes cannot be read).
+ * Nothing is launched.  buf receives at most buflen - 1 characters and a
+ * terminating NUL; MIGEMM_ERR_INVALID_ARG when buf is NULL, buflen < 1, the
+ * text was cut short, or the arguments fail migemm_gemm's checks.
+ */
+int migemm_describe(int64_t M, int64_t N, int64_t K, int dtype,
+                    int64_t lda, int64_t ldb, int64_t ldc, char* buf, int buflen);
+
+/*
+ * As migemm_describe, for the general call migemm_gemm_ws would make with
+ * these arguments (variant and config forced or -1, operand layouts, operand
+ * pointers inspected for alignment only, NULL read as 16-byte aligned, the
+ * output type, and the workspace size that would be lent).
+ */
+int migemm_describe_ex(int variant, int config, int op_a, int op_b,
+                       int64_t M, int64_t N, int64_t K, int dtype,
+                       const void* A, int64_t lda, const void* B, int64_t ldb,
+                       int c_dtype, int64_t ldc, int64_t workspace_bytes,
+                       char* buf, int buflen);
 
 /*
  * Element-type conversion of a matrix on the device, the step before the

@@ -34,9 +34,29 @@ def to_device_with_ld(x: torch.Tensor, ld: int | None = None, offset: int = 0):
     return view, buf
 
 
+def lend_workspace(variant, config, op_a, op_b, M, N, K, dt, pa, lda, pb, ldb, ws):
+    """(pointer, bytes, tensor) of the workspace a test lends: ws == "auto" lends
+    what migemm_workspace_size asks for (None when it asks for none), None lends
+    nothing, an int lends that many bytes."""
+    if ws is None:
+        return None, 0, None
+    if ws == "auto":
+        st, n = mg.migemm_workspace_size(variant, config, op_a, op_b, M, N, K, dt, pa, lda, pb,
+                                         ldb)
+        assert st == mg.OK
+    else:
+        n = int(ws)
+    if n == 0:
+        return None, 0, None
+    t = torch.empty(n, dtype=torch.uint8, device="cuda")
+    return t.data_ptr(), n, t
+
+
 def run_gemm(A: torch.Tensor, B: torch.Tensor, dtype: str, variant=-1, config=-1, lda=None,
-             ldb=None, ldc=None, a_off=0, b_off=0, c_off=0, poison=True):
-    """Run C = A x B through migemm_gemm_variant; returns (C on CPU as float32, C buffer)."""
+             ldb=None, ldc=None, a_off=0, b_off=0, c_off=0, poison=True, ws="auto"):
+    """Run C = A x B through migemm_gemm_ws, lending the workspace the call asks
+    for (ws="auto"; ws=None lends none, as migemm_gemm_variant does); returns (C
+    on CPU as float32, C buffer)."""
     M, K = A.shape
     N = B.shape[1]
     dA, _ = to_device_with_ld(A, lda, a_off)
@@ -46,10 +66,18 @@ def run_gemm(A: torch.Tensor, B: torch.Tensor, dtype: str, variant=-1, config=-1
                       dtype=torch.float32, device="cuda")
     dC = cbuf[c_off:c_off + M * ldc].view(M, ldc)[:, :N] if M else cbuf[:0].view(0, N)
     stream = torch.cuda.current_stream().cuda_stream
-    st = mg.migemm_gemm_variant(variant, config, M, N, K, DT_CODE[dtype],
-                                dA.data_ptr() if dA.numel() else None, lda or max(K, 1),
-                                dB.data_ptr() if dB.numel() else None, ldb or max(N, 1),
-                                dC.data_ptr() if dC.numel() else None, ldc, stream)
+    pa = dA.data_ptr() if dA.numel() else None
+    pb = dB.data_ptr() if dB.numel() else None
+    lda, ldb = lda or max(K, 1), ldb or max(N, 1)
+    wp, wn, _wt = lend_workspace(variant, config, 0, 0, M, N, K, DT_CODE[dtype], pa, lda, pb,
+                                 ldb, ws)
+    if wp is None:
+        st = mg.migemm_gemm_variant(variant, config, M, N, K, DT_CODE[dtype], pa, lda, pb, ldb,
+                                    dC.data_ptr() if dC.numel() else None, ldc, stream)
+    else:
+        st = mg.migemm_gemm_ws(variant, config, 0, 0, M, N, K, DT_CODE[dtype], pa, lda, pb, ldb,
+                               1.0, 0.0, 0, dC.data_ptr() if dC.numel() else None, ldc, wp, wn,
+                               stream)
     torch.cuda.synchronize()
     assert st == mg.OK, f"status {st}: {mg.migemm_status_string(st)} hip={mg.migemm_last_hip_error()}"
     return dC.cpu().clone(), cbuf
@@ -83,8 +111,10 @@ TORCH_OF = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}
 
 def run_gemm_ex(A: torch.Tensor, B: torch.Tensor, dtype: str, alpha: float, beta: float,
                 c_code: int, c_old: torch.Tensor | None = None, variant=-1, config=-1,
-                ldc=None, c_off=0, ta=False, tb=False, lda=None, ldb=None, a_off=0, b_off=0):
-    """C = alpha * A x B + beta * C_old through migemm_gemm_ex_variant, C stored as
+                ldc=None, c_off=0, ta=False, tb=False, lda=None, ldb=None, a_off=0, b_off=0,
+                ws="auto"):
+    """C = alpha * A x B + beta * C_old through migemm_gemm_ws (lending the
+    workspace as run_gemm does; without one, migemm_gemm_ex_variant), C stored as
     c_code (0 FP32, 1 FP16, 2 BF16).  A (M x K) and B (K x N) are the operands of
     the product; with ta / tb they are stored transposed (K x M, N x K) on the GPU
     and passed with MIGEMM_OP_T.  Operands and C sit inside NaN-filled buffers
@@ -110,11 +140,18 @@ def run_gemm_ex(A: torch.Tensor, B: torch.Tensor, dtype: str, alpha: float, beta
     if M:
         mask[c_off:c_off + M * ldc].view(M, ldc)[:, :N] = True
     stream = torch.cuda.current_stream().cuda_stream
-    st = mg.migemm_gemm_ex_variant(variant, config, int(ta), int(tb), M, N, K, DT_CODE[dtype],
-                                   dA.data_ptr() if dA.numel() else None, lda,
-                                   dB.data_ptr() if dB.numel() else None, ldb,
-                                   alpha, beta, c_code,
-                                   dC.data_ptr() if dC.numel() else None, ldc, stream)
+    pa = dA.data_ptr() if dA.numel() else None
+    pb = dB.data_ptr() if dB.numel() else None
+    pc = dC.data_ptr() if dC.numel() else None
+    wp, wn, _wt = lend_workspace(variant, config, int(ta), int(tb), M, N, K, DT_CODE[dtype], pa,
+                                 lda, pb, ldb, ws)
+    if wp is None:
+        st = mg.migemm_gemm_ex_variant(variant, config, int(ta), int(tb), M, N, K,
+                                       DT_CODE[dtype], pa, lda, pb, ldb, alpha, beta, c_code, pc,
+                                       ldc, stream)
+    else:
+        st = mg.migemm_gemm_ws(variant, config, int(ta), int(tb), M, N, K, DT_CODE[dtype], pa,
+                               lda, pb, ldb, alpha, beta, c_code, pc, ldc, wp, wn, stream)
     torch.cuda.synchronize()
     assert st == mg.OK, f"status {st}: {mg.migemm_status_string(st)} hip={mg.migemm_last_hip_error()}"
     return dC.cpu().clone(), cbuf.cpu(), mask

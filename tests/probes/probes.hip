@@ -65,58 +65,3 @@ extern "C" int probe_lds_load(const uint32_t* src, const int* off, uint32_t* out
     lds_load_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>(src, off, out);
     return static_cast<int>(hipGetLastError());
 }
-
-// Matrix-core throughput with no memory traffic: every wave runs 8 independent
-// accumulator chains of one MFMA shape for `iters` rounds, from operands held in
-// registers.  mode 0: zero operands; 1: all ones; 2: hashed values in [-0.5, 0.5)
-// (random bits, as GEMM inputs have).  Each thread stores the sum of its
-// accumulators, so for mode 1 every output is 8 * R * iters * k (R accumulator
-// registers per lane, k the instruction's depth).  512 threads per workgroup: two
-// waves per SIMD, as in the GEMM kernels.
-typedef __bf16 probe_bf16x8 __attribute__((ext_vector_type(8)));
-typedef float probe_f32x16 __attribute__((ext_vector_type(16)));
-typedef float probe_f32x4 __attribute__((ext_vector_type(4)));
-
-template <int MF>
-__global__ __launch_bounds__(512) void mfma_ceiling_kernel(float* out, int iters, int mode) {
-    using Acc = typename std::conditional<MF == 32, probe_f32x16, probe_f32x4>::type;
-    constexpr int NACC = 8;
-    Acc acc[NACC];
-    for (int i = 0; i < NACC; ++i) acc[i] = Acc{};
-    probe_bf16x8 a[2], b[2];
-    for (int v = 0; v < 2; ++v)
-        for (int e = 0; e < 8; ++e) {
-            uint32_t h = (threadIdx.x * 8u + e + v * 977u) * 2654435761u ^ (blockIdx.x * 40503u);
-            h ^= h >> 13;
-            h *= 0x5bd1e995u;
-            h ^= h >> 15;
-            float x = mode == 0 ? 0.0f : mode == 1 ? 1.0f : (float)(h & 0xffff) / 65536.0f - 0.5f;
-            float y = mode == 0 ? 0.0f : mode == 1 ? 1.0f : (float)(h >> 16) / 65536.0f - 0.5f;
-            a[v][e] = (__bf16)x;
-            b[v][e] = (__bf16)y;
-        }
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int i = 0; i < NACC; ++i) {
-            if constexpr (MF == 32)
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 1], b[(i >> 1) & 1], acc[i], 0, 0, 0);
-            else
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i & 1], b[(i >> 1) & 1], acc[i], 0, 0, 0);
-        }
-    }
-    float s = 0.f;
-    for (int i = 0; i < NACC; ++i)
-        for (int r = 0; r < (MF == 32 ? 16 : 4); ++r) s += acc[i][r];
-    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
-}
-
-// out holds blocks * 512 floats.
-extern "C" int probe_mfma_ceiling(int mf, float* out, int blocks, int iters, int mode, void* stream) {
-    if ((mf != 16 && mf != 32) || blocks <= 0 || iters <= 0 || mode < 0 || mode > 2) return -1;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (mf == 32)
-        mfma_ceiling_kernel<32><<<blocks, 512, 0, s>>>(out, iters, mode);
-    else
-        mfma_ceiling_kernel<16><<<blocks, 512, 0, s>>>(out, iters, mode);
-    return static_cast<int>(hipGetLastError());
-}

@@ -63,8 +63,33 @@ def test_variant_registry():
 
 def test_status_strings():
     assert mg.migemm_status_string(mg.OK) == "ok"
-    for s in (1, 2, 3, 77):
+    for s in (1, 2, 3, 4, 77):
         assert mg.migemm_status_string(s)
+    assert "scratch" in mg.migemm_status_string(mg.ERR_WORKSPACE)
+
+
+def test_extent_beyond_address_space_rejected():
+    # M = 2^31 - 1 rows of FP32 with lda = 2^32 - 1 span about 2^65 bytes: counted
+    # in 64 bits the extent would wrap and could pass the overlap check
+    big = (1 << 31) - 1
+    st = mg.migemm_gemm(big, 1, 1, 0, P, (1 << 32) - 1, 2 * P, 1, 3 * P, 1, None)
+    assert st == mg.ERR_INVALID_ARG
+    st = mg.migemm_gemm_ex(1, 0, 1, 1, big, 0, P, (1 << 32) - 1, 2 * P, 1, 1.0, 0.0, 0, 3 * P, 1,
+                           None)
+    assert st == mg.ERR_INVALID_ARG
+    # an extent that fits but ends past the top of the address space
+    st = mg.migemm_gemm(2, 1, 1 << 20, 0, (1 << 64) - (1 << 20), 1 << 20, 2 * P, 1, 3 * P, 1, None)
+    assert st == mg.ERR_INVALID_ARG
+
+
+def test_leading_dimension_limit():
+    # leading dimensions must be below 2^32
+    for ld in ((1 << 32), (1 << 32) + 1):
+        assert mg.migemm_gemm(1, 1, 1, 0, P, ld, 2 * P, 1, 3 * P, 1, None) == mg.ERR_INVALID_ARG
+        assert mg.migemm_gemm(1, 1, 1, 0, P, 1, 2 * P, ld, 3 * P, 1, None) == mg.ERR_INVALID_ARG
+        assert mg.migemm_gemm(1, 1, 1, 0, P, 1, 2 * P, 1, 3 * P, ld, None) == mg.ERR_INVALID_ARG
+    st, v, c = mg.migemm_select(1, 1, 1, 0, None, (1 << 32) - 1, None, 1, None, 1)
+    assert st == mg.OK
 
 
 @pytest.mark.parametrize("args", [
@@ -210,15 +235,30 @@ def test_selection_is_deterministic_and_valid():
     assert st == mg.ERR_INVALID_ARG
 
 
+def _selected(M, N, K, dt, lda, ldb, ws_bytes, op_a=0, op_b=0):
+    st, text = mg.migemm_describe_ex(-1, -1, op_a, op_b, M, N, K, dt, None, lda, None, ldb,
+                                     0, N, ws_bytes)
+    assert st == mg.OK, text
+    d = mg._parse_description(text)
+    return d["variant"], d["config"]
+
+
 def test_selection_packs_unreadable_16bit_operands():
     """FP16/BF16 operands the direct kernel cannot read in place (K not a
     multiple of 64, an odd leading dimension) go to the packed configurations
-    once the product is large enough; small ones stay on the register-staged
-    kernel, and aligned ones on the direct kernel."""
+    once the product is large enough and a large enough workspace is lent;
+    without one, or when small, they stay on the register-staged kernel, and
+    aligned ones on the direct kernel."""
     sel = lambda M, N, K, dt, lda, ldb: mg.migemm_select(M, N, K, dt, None, lda, None, ldb, None, N)
-    assert sel(2050, 2047, 2056, 1, 2056, 2047) == (mg.OK, mg.MFMA16, 12)
-    assert sel(8192, 8192, 8200, 2, 8200, 8192) == (mg.OK, mg.MFMA16, 11)
-    assert sel(4096, 4096, 4096, 2, 4096, 4097) == (mg.OK, mg.MFMA16, 11)
+    big = 1 << 40
+    assert _selected(2050, 2047, 2056, 1, 2056, 2047, big) == ("mfma16", 12)
+    assert _selected(8192, 8192, 8200, 2, 8200, 8192, big) == ("mfma16", 11)
+    assert _selected(4096, 4096, 4096, 2, 4096, 4097, big) == ("mfma16", 11)
+    # no workspace (migemm_gemm, migemm_select) or too little: register-staged
+    assert sel(2050, 2047, 2056, 1, 2056, 2047) == (mg.OK, mg.MFMA16, 2)
+    assert _selected(2050, 2047, 2056, 1, 2056, 2047, 17305727) == ("mfma16", 2)
+    assert _selected(2050, 2047, 2056, 1, 2056, 2047, 17305728) == ("mfma16", 12)
+    assert sel(4096, 4096, 4096, 2, 4096, 4097) == (mg.OK, mg.MFMA16, 2)
     assert sel(2048, 2048, 2048, 2, 2048, 2048) == (mg.OK, mg.MFMA16, 7)
     # whole 256x256 tiles take the ping-pong configuration, other shapes with as
     # many tiles the early-load one
@@ -234,6 +274,107 @@ def test_selection_packs_unreadable_16bit_operands():
     assert sel(1024, 1024, 1024, 1, 1024, 1024) == (mg.OK, mg.MFMA16, 16)
     assert sel(256, 256, 256, 1, 256, 256) == (mg.OK, mg.MFMA16, 16)
     assert sel(2048, 2048, 2048, 0, 2049, 2048)[1] == mg.REGTILE_MFMA
+    # aligned operands need no workspace: lending one changes nothing
+    assert _selected(8192, 8192, 8192, 2, 8192, 8192, big) == ("mfma16", 14)
+
+
+def test_workspace_size():
+    ws = lambda *a: mg.migemm_workspace_size(*a)
+    # 2050 x 2047 x 2056 FP16, ldb = 2047: both operands packed with K' = 2112,
+    # A' (2050 x 2112, rounded to 256 bytes) then B' (2047 x 2112)
+    assert ws(-1, -1, 0, 0, 2050, 2047, 2056, 1, None, 2056, None, 2047) == (mg.OK, 17305728)
+    # K a multiple of 64 and A aligned: only B is copied
+    assert ws(-1, -1, 0, 0, 4096, 4096, 4096, 2, None, 4096, None, 4097) == (mg.OK, 4096 * 4096 * 2)
+    # aligned, FP32, INT8, small, empty: none
+    for a in [(8192, 8192, 8192, 2, 8192, 8192), (1024, 1024, 1024, 0, 1025, 1024),
+              (8192, 8192, 8192, 3, 8192, 8192), (100, 100, 100, 1, 101, 100),
+              (0, 4096, 4096, 1, 4097, 4096), (4096, 4096, 0, 1, 1, 4097)]:
+        M, N, K, dt, lda, ldb = a
+        assert ws(-1, -1, 0, 0, M, N, K, dt, None, lda, None, ldb) == (mg.OK, 0), a
+    # a forced packed configuration reports its copies; any other forced one none
+    assert ws(mg.MFMA16, 12, 0, 0, 512, 512, 200, 1, None, 200, None, 512)[1] == \
+        512 * 256 * 2 * 2
+    assert ws(mg.MFMA16, 2, 0, 0, 2050, 2047, 2056, 1, None, 2056, None, 2047) == (mg.OK, 0)
+    # argument errors as for the product
+    assert ws(-1, -1, 0, 0, -1, 4, 4, 1, None, 4, None, 4)[0] == mg.ERR_INVALID_ARG
+    assert mg.lib().migemm_workspace_size(-1, -1, 0, 0, 4, 4, 4, 1, None, 4, None, 4,
+                                          None) == mg.ERR_INVALID_ARG
+
+
+def test_describe():
+    st, text = mg.migemm_describe(8192, 8192, 8192, mg.BF16, 8192, 8192, 8192)
+    assert st == mg.OK
+    d = mg._parse_description(text)
+    assert d["variant"] == "mfma16" and d["config"] == 14
+    assert d["config_name"] == mg.migemm_config_name(mg.MFMA16, 14)
+    assert d["workspace_bytes"] == 0 and d["launches"] == 1
+    assert d["grid0"] == 1024 and d["block0"] == 512
+    # on a machine with a GPU the kernel's attributes follow; without one, a note
+    assert "regs0" in d or "resources0" in d
+    # the ragged product with a workspace: the copy, then 256 tiles of 128 x 128
+    # over rows 0..2047, then the last 2 rows on 32 tiles of 64 x 64
+    st, text = mg.migemm_describe_ex(-1, -1, 0, 0, 2050, 2047, 2056, mg.F16, None, 2056, None,
+                                     2047, mg.F32, 2047, 1 << 30)
+    d = mg._parse_description(text)
+    assert st == mg.OK and d["config"] == 12 and d["workspace_bytes"] == 17305728
+    assert d["launches"] == 3 and d["grid1"] == 256 and d["grid2"] == 32
+    assert d["workspace_lent"] == 1 << 30
+    # FP32 and INT8
+    d = mg._parse_description(mg.migemm_describe(1024, 1024, 1024, mg.F32, 1024, 1024, 1024)[1])
+    assert d["variant"] == "regtile_mfma" and d["launches"] == 1
+    d = mg._parse_description(mg.migemm_describe(8192, 8192, 8192, mg.I8, 8192, 8192, 8192)[1])
+    assert d["variant"] == "mfma_i8" and d["config"] == 4
+    # K == 0 launches the empty product, M == 0 nothing
+    assert mg._parse_description(mg.migemm_describe(64, 64, 0, 0, 1, 64, 64)[1])["launches"] == 1
+    assert mg._parse_description(mg.migemm_describe(0, 64, 64, 0, 64, 64, 64)[1])["launches"] == 0
+    # a buffer too small: cut short, status says so; bad arguments: no text
+    st, text = mg.migemm_describe(8192, 8192, 8192, mg.BF16, 8192, 8192, 8192, buflen=20)
+    assert st == mg.ERR_INVALID_ARG and len(text) == 19
+    assert mg.migemm_describe(8, 8, 8, 9, 8, 8, 8)[0] == mg.ERR_INVALID_ARG
+    assert mg.lib().migemm_describe(8, 8, 8, 0, 8, 8, 8, None, 10) == mg.ERR_INVALID_ARG
+
+
+def test_gemm_ws_argument_checks():
+    a = (-1, -1, 0, 0, 8, 5, 4, 1, P, 4, 2 * P, 5, 1.0, 0.0, 0, 3 * P, 5)
+    assert mg.migemm_gemm_ws(*a, None, -1, None) == mg.ERR_INVALID_ARG
+    bad = list(a)
+    bad[4] = -1
+    assert mg.migemm_gemm_ws(*bad, None, 0, None) == mg.ERR_INVALID_ARG
+    assert mg.migemm_gemm_ws(mg.LDS_TILED, -1, *a[2:], None, 0, None) == mg.ERR_UNSUPPORTED
+
+
+class _FakeCudaTensor:
+    """Enough of a torch tensor on cuda:0 for gemm()'s argument checks, on a
+    machine without a GPU (never dereferenced: the checks fail first)."""
+
+    def __init__(self, rows, cols):
+        import torch
+        self.device = torch.device("cuda", 0)
+        self.dtype = torch.float32
+        self.shape = (rows, cols)
+
+    def stride(self, d=None):
+        s = (self.shape[1], 1)
+        return s if d is None else s[d]
+
+    def dim(self):
+        return 2
+
+    def data_ptr(self):
+        return P
+
+
+def test_gemm_rejects_output_on_another_device():
+    import torch
+    a, b = _FakeCudaTensor(8, 4), _FakeCudaTensor(4, 5)
+    with pytest.raises(ValueError, match="out must be on the GPU"):
+        mg.gemm(a, b, out=torch.empty((8, 5)))
+    with pytest.raises(ValueError, match="b must be on the GPU"):
+        mg.gemm(a, torch.empty((4, 5)))
+    other = _FakeCudaTensor(8, 5)
+    other.device = torch.device("cuda", 1)
+    with pytest.raises(ValueError, match="out is on cuda:1"):
+        mg.gemm(a, b, out=other)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -1,13 +1,14 @@
 """The packed FP16/BF16 path (mfma16 configurations 11 and 12): A and B are
-copied into zero-padded k-contiguous images in a workspace and the direct
-kernel multiplies those as A x B^T.
+copied into zero-padded k-contiguous images in a workspace the caller lends
+(migemm_gemm_ws) and the direct kernel multiplies those as A x B^T.
 
 Checked against the oracle: K not a multiple of the 64-k tile (down to K = 1),
 odd leading dimensions and operands that start off a 16-byte boundary (the
 operand buffers are NaN-filled around each window, so a read outside an operand
 shows up in C), all four storage layouts, the general output step, exact
-integer inputs, the automatic selection for shapes that need packing, and calls
-on two streams with workspaces of changing size.
+integer inputs, the automatic selection for shapes that need packing, calls on
+two streams each with its own workspace, and calls that lend no, too little or
+a misaligned workspace (the product then runs in place).
 """
 import pytest
 import torch
@@ -95,22 +96,29 @@ def test_packed_integer_inputs_exact():
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 def test_auto_selects_packing_where_needed(ta, tb):
-    """K = 1000 (not a multiple of 64) and an odd leading dimension: the
-    selection takes a packed configuration, and the result matches."""
+    """K = 1000 (not a multiple of 64) and an odd leading dimension: with a
+    workspace lent the selection takes a packed configuration, without one the
+    register-staged kernel, and both results match."""
     M, N, K = 600, 520, 1000
-    st, v, c = mg.migemm_select(M, N, K, 1, None, K, None, N + 1, None, N)
-    assert st == mg.OK and v == mg.MFMA16 and c in PACKED
+    lda, ldb = (M if ta else K), (K if tb else N) + 1
+    st, text = mg.migemm_describe_ex(-1, -1, int(ta), int(tb), M, N, K, 1, None, lda, None, ldb,
+                                     0, N, 1 << 30)
+    assert st == mg.OK and mg._parse_description(text)["config"] in PACKED
+    st, text = mg.migemm_describe_ex(-1, -1, int(ta), int(tb), M, N, K, 1, None, lda, None, ldb,
+                                     0, N, 0)
+    assert st == mg.OK and mg._parse_description(text)["config"] not in PACKED
     A, B = inputs.pair(M, N, K, "f16", "normal", seed=44 + ta + 2 * tb)
     ref = oracle_ref(A, B, "f16")
-    say(f"packed auto {_name(ta, tb)} {M}x{N}x{K}")
-    C, _, _ = run_gemm_ex(A, B, "f16", 1.0, 0.0, 0, None, ta=ta, tb=tb,
-                          ldb=(K if tb else N) + 1)
-    check_ex(C, A, B, "f16", 1.0, 0.0, 0, None, ref=ref)
+    for ws in ("auto", None):
+        say(f"packed auto {_name(ta, tb)} {M}x{N}x{K} workspace={ws}")
+        C, _, _ = run_gemm_ex(A, B, "f16", 1.0, 0.0, 0, None, ta=ta, tb=tb, ldb=ldb, ws=ws)
+        check_ex(C, A, B, "f16", 1.0, 0.0, 0, None, ref=ref)
 
 
-def test_packed_two_streams_changing_workspace():
-    """Calls alternating between two streams, workspaces growing and shrinking,
-    launched back to back and checked after one synchronisation."""
+def test_packed_two_streams_own_workspaces():
+    """Calls alternating between two streams, each lent its own workspace
+    (allocated on its stream), launched back to back and checked after one
+    synchronisation."""
     shapes = [(64, 72, 130), (700, 300, 513), (33, 40, 9), (512, 640, 1001), (120, 8, 70),
               (900, 257, 333)]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
@@ -123,18 +131,64 @@ def test_packed_two_streams_changing_workspace():
         C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
         runs.append((A, B, dtype, dA, dB, C, K + 1, N + 1))
     torch.cuda.synchronize()
+    keep = []
     for i, (A, B, dtype, dA, dB, C, lda, ldb) in enumerate(runs):
         M, K = A.shape
         N = B.shape[1]
         s = streams[i % 2]
-        say(f"packed stream {i % 2} {dtype} {M}x{N}x{K}")
-        st = mg.migemm_gemm_ex_variant(mg.MFMA16, PACKED[i % 2], 0, 0, M, N, K, DT_CODE[dtype],
-                                       dA.data_ptr(), lda, dB.data_ptr(), ldb, 1.0, 0.0, 0,
-                                       C.data_ptr(), N, s.cuda_stream)
+        cfg = PACKED[i % 2]
+        st, n = mg.migemm_workspace_size(mg.MFMA16, cfg, 0, 0, M, N, K, DT_CODE[dtype],
+                                         dA.data_ptr(), lda, dB.data_ptr(), ldb)
+        assert st == mg.OK and n > 0
+        with torch.cuda.stream(s):
+            ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        keep.append(ws)
+        say(f"packed stream {i % 2} {dtype} {M}x{N}x{K} workspace {n}")
+        st = mg.migemm_gemm_ws(mg.MFMA16, cfg, 0, 0, M, N, K, DT_CODE[dtype], dA.data_ptr(),
+                               lda, dB.data_ptr(), ldb, 1.0, 0.0, 0, C.data_ptr(), N,
+                               ws.data_ptr(), n, s.cuda_stream)
         assert st == mg.OK
     torch.cuda.synchronize()
     for (A, B, dtype, dA, dB, C, lda, ldb) in runs:
         check_ex(C.cpu(), A, B, dtype, 1.0, 0.0, 0, None)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_packed_without_usable_workspace_runs_in_place(dtype):
+    """A packed configuration lent no workspace, one byte too little, or a
+    workspace off a 256-byte boundary runs in place (register-staged kernel);
+    a workspace exactly as large as asked is used, and nothing past the size
+    migemm_workspace_size reports is written."""
+    M, N, K = 300, 264, 200
+    A, B = inputs.pair(M, N, K, dtype, "normal", seed=71)
+    ref = oracle_ref(A, B, dtype)
+    for cfg in PACKED:
+        st, need = mg.migemm_workspace_size(mg.MFMA16, cfg, 0, 0, M, N, K, DT_CODE[dtype], None,
+                                            K + 1, None, N)
+        assert st == mg.OK and need > 0
+        for case, ws in (("none", None), ("short", need - 1), ("exact", need)):
+            say(f"packed {dtype} cfg={cfg} workspace {case}")
+            C, _, _ = run_gemm_ex(A, B, dtype, 1.0, 0.0, 0, None, variant=mg.MFMA16, config=cfg,
+                                  lda=K + 1, ws=ws)
+            check_ex(C, A, B, dtype, 1.0, 0.0, 0, None, ref=ref)
+        # a misaligned workspace and a guarded one, lent directly
+        dA, _ = to_device_with_ld(A, K + 1, 0)
+        dB, _ = to_device_with_ld(B, N, 0)
+        stream = torch.cuda.current_stream().cuda_stream
+        guard = 4096
+        buf = torch.full((need + 256 + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+        for off, label in ((16, "misaligned"), (0, "aligned")):
+            C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+            say(f"packed {dtype} cfg={cfg} workspace {label}")
+            st = mg.migemm_gemm_ws(mg.MFMA16, cfg, 0, 0, M, N, K, DT_CODE[dtype], dA.data_ptr(),
+                                   K + 1, dB.data_ptr(), N, 1.0, 0.0, 0, C.data_ptr(), N,
+                                   buf.data_ptr() + off, need + 256, stream)
+            torch.cuda.synchronize()
+            assert st == mg.OK
+            check_ex(C.cpu(), A, B, dtype, 1.0, 0.0, 0, None, ref=ref)
+        tail = buf[need:].cpu()
+        assert bool((tail == 0xA5).all()), "workspace written past the reported size"
+        assert not bool((buf[:need].cpu() == 0xA5).all()), "aligned workspace not used"
 
 
 def test_packed_last_row_band_split():

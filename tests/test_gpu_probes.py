@@ -131,24 +131,3 @@ def test_global_load_lds_lane_placement():
     for lane in range(64):
         want[64 + 4 * lane: 64 + 4 * lane + 4] = np.arange(4 * perm[lane], 4 * perm[lane] + 4)
     assert np.array_equal(got, want)
-
-
-@pytest.mark.parametrize("mf", [16, 32])
-def test_mfma_ceiling_probe_counts(mf):
-    """The throughput probe does the matrix work it claims: with all-ones operands
-    every accumulator element is iters * k, so each thread's sum is
-    8 accumulators * R registers * iters * k; with zero operands it is 0."""
-    L = ctypes.CDLL(LIB)
-    L.probe_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                     ctypes.c_int, ctypes.c_void_p]
-    blocks, iters = 2, 8
-    R, k = (16, 16) if mf == 32 else (4, 32)
-    out = torch.full((blocks * 512,), -1.0, device="cuda")
-    s = torch.cuda.current_stream().cuda_stream
-    assert L.probe_mfma_ceiling(mf, out.data_ptr(), blocks, iters, 1, s) == 0
-    torch.cuda.synchronize()
-    assert torch.all(out == 8 * R * iters * k)
-    assert L.probe_mfma_ceiling(mf, out.data_ptr(), blocks, iters, 0, s) == 0
-    torch.cuda.synchronize()
-    assert torch.all(out == 0)
-    assert L.probe_mfma_ceiling(8, out.data_ptr(), blocks, iters, 0, s) == -1
