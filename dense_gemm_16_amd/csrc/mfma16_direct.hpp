@@ -212,16 +212,25 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 }
 
 // 16 bytes per lane from global memory (SGPR base + per-lane byte offset) into
-// LDS at lds_base + 16 * lane.  M0 carries the LDS base and is declared
-// clobbered, so the compiler neither keeps a value of its own in M0 across
-// these statements nor assumes M0 unchanged after them.  The base is
-// wave-uniform by construction; passing it through uniform_ptr keeps the
-// compiler from handing the asm a VGPR copy of it.
+// LDS at lds_base + 16 * lane.  M0 carries the LDS base.  It is an input operand
+// bound to M0 ("{m0}"), so the compiler itself writes M0 before the statement
+// and knows what it holds afterwards: nothing the compiler keeps in M0 is
+// overwritten behind its back.  The base is wave-uniform by construction;
+// passing it through uniform_ptr keeps the compiler from handing the asm a VGPR
+// copy of it, but the compiler often produces that SGPR pair with
+// v_readfirstlane_b32 (a VALU instruction) right before the statement.
+//
+// Wait states.  The compiler inserts the waits its hazard rules require only
+// around instructions it can see, not inside an asm statement, so the
+// statement starts with its own: s_nop 4 is five wait states, what a vector
+// memory instruction needs after a VALU instruction wrote an SGPR it reads (the
+// address base here), and more than the one an LDS DMA needs after an SALU
+// write of M0.  With fewer, the load can read a stale base and fault.
 __device__ __forceinline__ void dma16(uint32_t lds_base, const void* sbase, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "s"(lds_base), "v"(voff), "s"(uniform_ptr(sbase))
-                 : "memory", "m0");
+                 : "v"(voff), "s"(uniform_ptr(sbase)), "{m0}"(lds_base)
+                 : "memory");
 }
 
 // Wait until at most N of this wave's direct loads are outstanding (inline asm:
