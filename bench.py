@@ -2,20 +2,36 @@
 
 One step = one C = A x B on the headline workload (M = N = K = 8192, BF16
 inputs drawn from N(0,1) with a fixed seed, FP32 accumulation and output),
-with A, B and C resident in HBM before the timed region.  W untimed warm-up
-steps, then K timed steps between HIP events on the stream the library
-launches on; the line reports the mean time per step and TFLOP/s = 2MNK/t.
+with A, B and C resident in HBM before the timed region.
+
+Timing protocol for the headline:
+  1. one launch into a NaN-filled C, checked for unwritten outputs;
+  2. settle: back-to-back launches from idle for at least 200 ms.  The board's
+     power controller clamps the clock hard when a heavy load starts and
+     relaxes it over the next few tens of milliseconds (a kernel trace shows
+     launches 3-6 at 880-1030 us against 714 us once settled), so a window
+     taken straight after idle measures that transient, not the kernel.  The
+     first K of these launches are timed and reported as `cold_first_k_ms`;
+  3. W untimed warm-up steps, then exactly K timed steps between HIP events
+     on the stream the library launches on: `value` = 2MNK / mean step time;
+  4. the steady state: the median over 5 windows of at least 50 ms each,
+     reported beside `value` (with the board's clock and power sampled through
+     amdsmi meanwhile, where the box allows it).
 
 Printed on stdout as one JSON line; progress goes to stderr.  Besides the
 headline it carries:
   roofline      the dominant kernel against the MI355X dense BF16 matrix peak,
                 with HBM traffic from the committed rocprofv3 counter summary
-                (null once the kernel sources differ from the profiled ones);
+                (null once the kernel sources differ from the profiled ones)
+                and the kernel's resources (registers, LDS, scratch, occupancy);
   cpu_baseline  the CPU oracle timed on this host on a bounded sample of the
                 same workload (whole rows of C), with the GPU rows checked
                 against it;
-  by_workload   the other workloads (1024^3, 2048^3, 4096^3; FP32, FP16, BF16)
-                and the naive one-work-item-per-output kernel at 1024^3.
+  by_workload   the other workloads (256^3 to 8192^3; FP32, FP16, BF16, INT8;
+                operand layouts, the general output step, device conversion)
+                and the naive one-work-item-per-output kernel at 1024^3, each
+                with its kernel's resources and, for the plain products, the
+                oracle timed on a bounded sample with the GPU rows checked.
 
 `--gpus N` with N > 1 exits with an error: the library runs on one GPU.
 """
@@ -25,7 +41,9 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +55,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3,
                "i8": 5033.2}  # INT8: TOPS, twice the 16-bit matrix rate
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-EXTRA = ["c1-f32-1024", "c1-f32-1024-int", "c2-f16-1024", "c3-f16-2048", "c3-bf16-2048",
+RESOURCES_FILE = os.path.join(ROOT, "dense_gemm_16_amd", "kernel_resources.json")
+SETTLE_MS = 200.0
+EXTRA = ["c0-f16-256", "c1-f32-1024", "c1-f32-1024-int", "c2-f16-1024", "c3-f16-2048", "c3-bf16-2048",
          "c3r-f16-2050x2047x2056", "c4f-f32-4096", "s8-bf16-1024x8192x8192",
          "s2x4-bf16-4096x2048x8192"]
 
@@ -56,8 +76,18 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def _compiler_figures():
+    try:
+        with open(RESOURCES_FILE) as f:
+            return json.load(f).get("kernels", {})
+    except (OSError, ValueError):
+        return {}
+
+
 class Problem:
-    """Device-resident operands of one workload and a launcher for it."""
+    """Device-resident operands of one workload and a launcher for it.  The
+    workspace the call asks for (migemm_workspace_size) is allocated once and
+    lent to every launch (migemm_gemm_ws)."""
 
     def __init__(self, w, variant=-1, config=-1, alpha=1.0, beta=0.0, c_code=0, ta=False,
                  tb=False):
@@ -69,7 +99,7 @@ class Problem:
         # operands given transposed are stored K x M (A) and N x K (B)
         self.dA = (self.A.t().contiguous() if ta else self.A).cuda()
         self.dB = (self.B.t().contiguous() if tb else self.B).cuda()
-        lda, ldb = (w.M if ta else w.K), (w.K if tb else w.N)
+        self.lda, self.ldb = (w.M if ta else w.K), (w.K if tb else w.N)
         self.ops = (int(ta), int(tb))
         if w.dtype == "i8":
             c_code = 4  # INT32 C, the only output of an INT8 product
@@ -80,19 +110,22 @@ class Problem:
         if self.C.dtype == torch.int32:
             self.C.zero_()
         self.epi = (float(alpha), float(beta), c_code)
-        self.general = not (alpha == 1.0 and beta == 0.0 and c_code == 0 and not ta and not tb)
+        self.general = not (alpha == 1.0 and beta == 0.0 and c_code == 0)
         self.code = inputs.DTYPE_CODES[w.dtype]
-        st, v, c = mg.migemm_select(w.M, w.N, w.K, self.code, self.dA.data_ptr(), lda,
-                                    self.dB.data_ptr(), ldb, self.C.data_ptr(), w.N)
-        if variant < 0:
-            self.variant, self.config = v, c
-        else:
-            self.variant = variant
-            self.config = config if config >= 0 else (c if v == variant else 0)
+        shape = (w.M, w.N, w.K, self.code, self.dA.data_ptr(), self.lda, self.dB.data_ptr(),
+                 self.ldb)
+        st, n = mg.migemm_workspace_size(variant, config, *self.ops, *shape)
+        if st != mg.OK:
+            raise RuntimeError(f"{w.name}: {mg.migemm_status_string(st)}")
+        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+        self.ws_args = (self.ws.data_ptr(), n) if n else (None, 0)
+        self.desc = mg.describe(variant, config, *self.ops, *shape, c_code, w.N, n)
+        names = [mg.migemm_variant_name(v) for v in range(mg.migemm_variant_count())]
+        self.variant, self.config = names.index(self.desc["variant"]), self.desc["config"]
         self.stream = torch.cuda.current_stream()
         self.sp = self.stream.cuda_stream
-        self.args = (self.variant, self.config, w.M, w.N, w.K, self.code, self.dA.data_ptr(), lda,
-                     self.dB.data_ptr(), ldb, self.C.data_ptr(), w.N, self.sp)
+        self.args = (self.variant, self.config, *self.ops, *shape, *self.epi, self.C.data_ptr(),
+                     w.N, *self.ws_args, self.sp)
 
     def kernel_name(self):
         return (f"{self.mg.migemm_variant_name(self.variant)}["
@@ -101,36 +134,175 @@ class Problem:
     def layout(self):
         return "".join("T" if t else "N" for t in self.ops)
 
+    def resources(self):
+        """Per launch of one call: workgroups, workgroup size, the runtime's
+        register / LDS / scratch / occupancy figures and the compiler's."""
+        d, figs = self.desc, _compiler_figures()
+        by_demangled = {v.get("demangled"): v for v in figs.values()}
+        out = {"workspace_bytes": d.get("workspace_bytes", 0), "launches": []}
+        for i in range(d.get("launches", 0)):
+            e = {"grid": d.get(f"grid{i}"), "block": d.get(f"block{i}")}
+            for key in ("kernel", "regs", "lds_bytes", "scratch_bytes", "workgroups_per_cu",
+                        "waves_per_simd", "resources"):
+                if f"{key}{i}" in d:
+                    e[key] = d[f"{key}{i}"]
+            name = e.get("kernel", "")
+            comp = figs.get(name) or by_demangled.get(name)
+            if comp:
+                e["compiler"] = {k: v for k, v in comp.items() if k != "demangled"}
+            out["launches"].append(e)
+        return out
+
     def launch(self):
-        if self.general:
-            a = self.args
-            st = self.mg.migemm_gemm_ex_variant(*a[:2], *self.ops, *a[2:10], *self.epi, *a[10:])
-        else:
-            st = self.mg.migemm_gemm_variant(*self.args)
+        st = self.mg.migemm_gemm_ws(*self.args)
         if st != self.mg.OK:
             raise RuntimeError(f"{self.w.name}: {self.mg.migemm_status_string(st)} "
                                f"(hip {self.mg.migemm_last_hip_error()})")
+
+    def _window(self, n):
+        """Mean ms per launch over n back-to-back launches (HIP events on the stream)."""
+        import torch
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(n):
+            self.launch()
+        t1.record(self.stream)
+        t1.synchronize()
+        return t0.elapsed_time(t1) / n
 
     def time(self, steps, warmup):
         import torch
         for _ in range(warmup):
             self.launch()
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(self.stream)
-        for _ in range(steps):
-            self.launch()
-        t1.record(self.stream)
-        t1.synchronize()
+        ms = self._window(steps)
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps
+        return ms
 
     def time_window(self, min_ms=50.0, lo=20, hi=2000):
         """Mean ms per launch over a window of at least min_ms (lo..hi launches)."""
         est = self.time(3, 2)
         n = int(min(hi, max(lo, min_ms / max(est, 1e-4))))
         return self.time(n, 0), n
+
+    def settle(self, k, min_ms=SETTLE_MS):
+        """Back-to-back launches from idle until min_ms have run.  Returns the
+        mean ms of the first k (the cold window), and the launches and ms in all."""
+        import torch
+        torch.cuda.synchronize()
+        cold = self._window(k)
+        n, total = k, cold * k
+        while total < min_ms:
+            m = int(max(10, min(2000, (min_ms - total) / max(cold, 1e-3) + 1)))
+            total += self._window(m) * m
+            n += m
+        return cold, n, total
+
+    def steady(self, windows=5, min_ms=50.0):
+        """Median ms per launch over `windows` windows of at least min_ms each."""
+        t = [self.time_window(min_ms) for _ in range(windows)]
+        return statistics.median(x for x, _ in t), [round(x, 5) for x, _ in t], t[0][1]
+
+
+class ClockSampler:
+    """Samples the board's graphics clock and socket power (amdsmi GPU metrics)
+    in a background thread while the steady-state windows run.  Reports null
+    when amdsmi is not usable on the box or the GPU cannot be matched."""
+
+    def __init__(self, period_s=0.002):
+        self.period, self.samples, self.error = period_s, [], None
+        self._stop = threading.Event()
+        self._thread = None
+        self._h = None
+        self.max_clk = None
+        try:
+            import amdsmi
+            import torch
+            self._smi = amdsmi
+            amdsmi.amdsmi_init()
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if int(bdf.split(":")[1], 16) == int(bus):
+                    self._h = h
+            if self._h is None:
+                self.error = f"no amdsmi device on PCI bus {bus}"
+            else:
+                info = amdsmi.amdsmi_get_clock_info(self._h, amdsmi.AmdSmiClkType.GFX)
+                self.max_clk = info.get("max_clk")
+        except Exception as e:  # amdsmi missing, no permission, older torch ...
+            self.error = f"{type(e).__name__}: {e}"[:200]
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int)]
+                self.samples.append((clks, m.get("current_socket_power"),
+                                     m.get("temperature_hotspot")))
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self._h is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join(timeout=2.0)
+        return False
+
+    def summary(self):
+        clk = [statistics.mean(c) for c, _, _ in self.samples if c]
+        pw = [p for _, p, _ in self.samples if isinstance(p, (int, float))]
+        tmp = [t for _, _, t in self.samples if isinstance(t, (int, float))]
+        if not clk:
+            return {"source": "amdsmi GPU metrics", "samples": 0,
+                    "note": self.error or "no samples"}
+        return {"source": "amdsmi GPU metrics (current_gfxclks averaged over XCDs, "
+                          "current_socket_power), sampled during the steady-state windows",
+                "samples": len(self.samples),
+                "gfxclk_mhz_mean": round(statistics.mean(clk), 1),
+                "gfxclk_mhz_min": round(min(clk), 1), "gfxclk_mhz_max": round(max(clk), 1),
+                "gfxclk_limit_mhz": self.max_clk,
+                "socket_power_w_mean": round(statistics.mean(pw), 1) if pw else None,
+                "hotspot_c_max": max(tmp) if tmp else None}
+
+
+def oracle_check(p, seconds=2.0):
+    """The CPU oracle on a bounded sample of p's product (whole rows of C, all of
+    them when it fits the budget), timed, and p's GPU rows checked against it."""
+    import numpy as np
+    import oracle
+    from oracle.check import compare, tolerance
+    from dense_gemm_16_amd import inputs
+    w = p.w
+    bA, bB = inputs.to_bits(p.A), inputs.to_bits(p.B)
+    thr = oracle.default_threads()
+    used = oracle.threads_used(thr)
+    per_row = 2.0 * w.N * w.K
+    if w.M * per_row <= 2e10:
+        rows = w.M
+    else:
+        r0 = max(used, 8)
+        t = time.perf_counter()
+        oracle.gemm(bA[:r0], bB, p.code, nthreads=thr)
+        rate = r0 / max(time.perf_counter() - t, 1e-4)
+        rows = int(min(w.M, max(used, rate * seconds)))
+    t = time.perf_counter()
+    ref, S = oracle.gemm(bA[:rows], bB, p.code, nthreads=thr)
+    dt = time.perf_counter() - t
+    got = p.C[:rows].cpu().numpy().astype(np.float64)
+    chk = compare(got, ref, S, tol=None if w.exact else tolerance(p.code), exact=w.exact)
+    return {"rows": rows, "seconds": round(dt, 3),
+            "gflops": round(2.0 * rows * w.N * w.K / dt / 1e9, 2), "cores": used,
+            "gpu_rows_vs_oracle": str(chk), "gpu_rows_ok": bool(chk.ok)}
 
 
 def traffic_for(kernel: str, workload: str):
@@ -302,8 +474,10 @@ def digest_counters(w, fetch_dir, write_dir, reps):
     import dense_gemm_16_amd as mg
     from dense_gemm_16_amd import inputs
     code = inputs.DTYPE_CODES[w.dtype]
-    st, v, c = mg.migemm_select(w.M, w.N, w.K, code, None, w.K, None, w.N, None, w.N)
-    kernel = f"{mg.migemm_variant_name(v)}[{mg.migemm_config_name(v, c)}]"
+    c_code = 4 if w.dtype == "i8" else 0
+    d = mg.describe(-1, -1, 0, 0, w.M, w.N, w.K, code, None, w.K, None, w.N, c_code, w.N,
+                    1 << 40)
+    kernel = f"{d['variant']}[{d['config_name']}]"
     gib_kib = float(1 << 20)
     e = {"kernel": kernel, "source_hash": source_hash()}
     for label, d in (("fetch", fetch_dir), ("write", write_dir)):
@@ -398,11 +572,40 @@ def main():
         profile_pass(p, a.profile_pass)
         return
 
+    # correctness launch into a NaN-filled C (integer C: a sentinel)
+    p.C.fill_(-2147483647 if p.C.dtype == torch.int32 else float("nan"))
+    p.launch()
+    torch.cuda.synchronize()
+    unwritten = int((p.C == -2147483647).sum() if p.C.dtype == torch.int32
+                    else torch.isnan(p.C).sum())
+    if unwritten:
+        raise SystemExit(f"bench.py: {unwritten} outputs of {w.name} left unwritten")
+    cold, settle_n, settle_ms = p.settle(a.steps)
+    log(f"bench: settled over {settle_n} launches ({settle_ms:.0f} ms); the first {a.steps} "
+        f"from idle took {cold:.4f} ms each")
     log(f"bench: {w.name} on {p.kernel_name()}, warmup {a.warmup}, steps {a.steps}")
     ms = p.time(a.steps, a.warmup)
     tflops = w.flop / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log(f"bench: {ms:.4f} ms/step, {tflops:.1f} TFLOPS ({100 * tflops / peak:.1f}% of {peak})")
+    sampler = ClockSampler()
+    with sampler:
+        st_med, st_windows, st_n = p.steady()
+    clock = sampler.summary()
+    st_tf = w.flop / (st_med * 1e-3) / 1e12
+    log(f"bench: steady state {st_med:.4f} ms ({st_tf:.1f} TFLOPS), median of "
+        f"{len(st_windows)} windows of {st_n} launches; clock {clock.get('gfxclk_mhz_mean')} MHz")
+    timing = {"protocol": f"NaN-filled correctness launch; {settle_n} back-to-back launches "
+                          f"({settle_ms:.0f} ms) so the power controller settles; {a.warmup} "
+                          f"warm-up and {a.steps} timed steps (value); 5 windows of at least "
+                          "50 ms (steady_state)",
+              "cold_first_k_ms": round(cold, 5),
+              "cold_first_k_tflops": round(w.flop / (cold * 1e-3) / 1e12, 2),
+              "settle_launches": settle_n, "settle_ms": round(settle_ms, 1),
+              "steady_state": {"median_ms": round(st_med, 5), "windows_ms": st_windows,
+                               "launches_per_window": st_n, "tflops": round(st_tf, 2),
+                               "frac_of_peak": round(st_tf / peak, 4)},
+              "clock": clock}
 
     traffic, tnote = traffic_for(p.kernel_name(), w.name)
     roof = {"bound": "mfma", "kernel": p.kernel_name(), "achieved": round(tflops, 2),
@@ -410,7 +613,8 @@ def main():
             "frac": round(tflops / peak, 4),
             "traffic": traffic, "traffic_note": tnote,
             "algorithmic_flop_per_launch": w.flop,
-            "compulsory_bytes_per_launch": w.compulsory_bytes()}
+            "compulsory_bytes_per_launch": w.compulsory_bytes(),
+            "resources": p.resources()}
     if traffic:
         roof["traffic_gbs"] = round(traffic / (ms * 1e-3) / 1e9, 1)
         roof["traffic_frac_of_hbm_peak"] = round(traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
@@ -445,58 +649,64 @@ def main():
 
     extra = {}
     if not a.no_extra:
+        def line(px, unit="tflops"):
+            """Settled, then the median of 3 windows of at least 50 ms."""
+            px.settle(5, 50.0)
+            t, windows, n = px.steady(3)
+            tf = px.w.flop / (t * 1e-3) / 1e12
+            return {unit: round(tf, 2), "ms": round(t, 5), "launches": n,
+                    "windows_ms": windows,
+                    "frac_of_peak": round(tf / PEAK_TFLOPS[px.w.dtype], 4),
+                    "kernel": px.kernel_name(), "resources": px.resources()}, tf
+
         for name in EXTRA:
             wx = inputs.WORKLOADS[name]
             px = Problem(wx)
-            t, n = px.time_window()
-            tf = wx.flop / (t * 1e-3) / 1e12
-            extra[name] = {"tflops": round(tf, 2), "ms": round(t, 5), "launches": n,
-                           "frac_of_peak": round(tf / PEAK_TFLOPS[wx.dtype], 4),
-                           "kernel": px.kernel_name()}
-            log(f"extra {name}: {tf:.1f} TFLOPS on {px.kernel_name()}")
+            extra[name], tf = line(px)
+            px.launch()
+            torch.cuda.synchronize()
+            extra[name]["oracle"] = oracle_check(px)
+            log(f"extra {name}: {tf:.1f} TFLOPS on {px.kernel_name()}; oracle "
+                f"{extra[name]['oracle']['gflops']} GFLOPS on {extra[name]['oracle']['rows']} "
+                f"rows, {extra[name]['oracle']['gpu_rows_vs_oracle']}")
+            if not extra[name]["oracle"]["gpu_rows_ok"]:
+                raise SystemExit(f"bench.py: {name} does not match the oracle")
             if name == "c1-f32-1024":
-                pn = Problem(wx, mg.NAIVE, 0)
-                t, n = pn.time_window()
-                tf = wx.flop / (t * 1e-3) / 1e12
-                extra[name + "/naive"] = {"tflops": round(tf, 2), "ms": round(t, 5),
-                                          "launches": n,
-                                          "frac_of_peak": round(tf / PEAK_TFLOPS["f32"], 4),
-                                          "kernel": pn.kernel_name()}
-                log(f"extra {name}/naive: {tf:.2f} TFLOPS")
+                for v, label in ((mg.NAIVE, "naive"), (mg.LDS_TILED, "lds_tiled"),
+                                 (mg.REGTILE_VALU, "regtile_valu")):
+                    pn = Problem(wx, v, -1)
+                    extra[f"{name}/{label}"], tf = line(pn)
+                    log(f"extra {name}/{label}: {tf:.2f} TFLOPS on {pn.kernel_name()}")
+                    del pn
             del px
         # operands given transposed on the headline shape
         if w.name == "c4-bf16-8192":
             for ta, tb in ((False, True), (True, False), (True, True)):
                 px = Problem(w, ta=ta, tb=tb)
-                t, n = px.time_window()
-                tf = w.flop / (t * 1e-3) / 1e12
-                extra[f"{w.name}/{px.layout()}"] = {
-                    "tflops": round(tf, 2), "ms": round(t, 5), "launches": n,
-                    "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
-                    "kernel": px.kernel_name(),
-                    "layout": f"A {'K x M (given transposed)' if ta else 'M x K'}, "
-                              f"B {'N x K (given transposed)' if tb else 'K x N'}"}
+                e, tf = line(px)
+                e["layout"] = (f"A {'K x M (given transposed)' if ta else 'M x K'}, "
+                               f"B {'N x K (given transposed)' if tb else 'K x N'}")
+                extra[f"{w.name}/{px.layout()}"] = e
                 log(f"extra {w.name} layout {px.layout()}: {tf:.1f} TFLOPS")
                 del px
         # INT8 -> INT32 at the headline size
         if w.name == "c4-bf16-8192":
             wi = inputs.WORKLOADS["i8-8192"]
             px = Problem(wi)
-            t, n = px.time_window()
-            tf = wi.flop / (t * 1e-3) / 1e12
-            extra[wi.name] = {"tops": round(tf, 2), "ms": round(t, 5), "launches": n,
-                              "frac_of_peak": round(tf / PEAK_TFLOPS["i8"], 4),
-                              "peak_tops": PEAK_TFLOPS["i8"], "kernel": px.kernel_name()}
+            e, tf = line(px, "tops")
+            e["peak_tops"] = PEAK_TFLOPS["i8"]
+            px.launch()
+            torch.cuda.synchronize()
+            e["oracle"] = oracle_check(px)
+            extra[wi.name] = e
             log(f"extra {wi.name}: {tf:.1f} TOPS ({100 * tf / PEAK_TFLOPS['i8']:.1f}% of "
-                f"{PEAK_TFLOPS['i8']}) on {px.kernel_name()}")
+                f"{PEAK_TFLOPS['i8']}) on {px.kernel_name()}; oracle {e['oracle']['gpu_rows_vs_oracle']}")
+            if not e["oracle"]["gpu_rows_ok"]:
+                raise SystemExit(f"bench.py: {wi.name} does not match the oracle")
             del px
             for ta, tb in ((False, True), (True, False), (True, True)):
                 px = Problem(wi, ta=ta, tb=tb)
-                t, n = px.time_window()
-                tf = wi.flop / (t * 1e-3) / 1e12
-                extra[f"{wi.name}/{px.layout()}"] = {
-                    "tops": round(tf, 2), "ms": round(t, 5), "launches": n,
-                    "frac_of_peak": round(tf / PEAK_TFLOPS["i8"], 4), "kernel": px.kernel_name()}
+                extra[f"{wi.name}/{px.layout()}"], tf = line(px, "tops")
                 log(f"extra {wi.name} layout {px.layout()}: {tf:.1f} TOPS")
                 del px
         # FP32 data on the 16-bit path: device conversion, alone and followed by the product
@@ -505,13 +715,10 @@ def main():
         # the general output step on the headline shape: scaled update, BF16 C
         if w.name == "c4-bf16-8192":
             px = Problem(w, alpha=0.5, beta=-1.0, c_code=2)
-            t, n = px.time_window()
-            tf = w.flop / (t * 1e-3) / 1e12
-            extra[w.name + "/alpha-beta-bf16-out"] = {
-                "tflops": round(tf, 2), "ms": round(t, 5), "launches": n,
-                "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
-                "kernel": px.kernel_name() + " general output step",
-                "update": "C = 0.5 A B - 1.0 C, C stored as BF16"}
+            e, tf = line(px)
+            e["kernel"] += " general output step"
+            e["update"] = "C = 0.5 A B - 1.0 C, C stored as BF16"
+            extra[w.name + "/alpha-beta-bf16-out"] = e
             log(f"extra {w.name} general (alpha 0.5, beta -1, BF16 C): {tf:.1f} TFLOPS")
             del px
 
@@ -537,7 +744,7 @@ def main():
                       "seed": w.seed, "layout": "row-major, dense leading dimensions",
                       "parallelism": "single GPU"},
            "frac_of_peak": round(tflops / peak, 4), "peak_tflops": peak,
-           "roofline": roof, "cpu_baseline": cpu, "by_workload": extra,
+           "roofline": roof, "cpu_baseline": cpu, "timing": timing, "by_workload": extra,
            "device": device_info(), "source_hash": source_hash()}
     if sweep:
         out["sweep"] = sweep

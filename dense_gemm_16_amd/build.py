@@ -7,13 +7,17 @@ into ``libmigemm.so`` next to this file.  Flags:
 * ``-Xclang -target-feature -Xclang -packed-fp32-ops``: no packed FP32
   instructions in the device code (hipcc's host pass warns that it does not
   know the feature; the device pass honours it);
-* ``-Rpass-analysis=kernel-resource-usage`` (optional): per-kernel VGPR, AGPR,
-  LDS and scratch use, written to ``_build/resource_usage.txt``.
+* ``-Rpass-analysis=kernel-resource-usage``: the compiler's per-kernel SGPR,
+  VGPR, AGPR, scratch, spill, LDS and occupancy figures, collected into
+  ``kernel_resources.json`` next to the library (keyed by the kernel's symbol,
+  with its demangled name), which the benchmark reports per timed kernel.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
+import json
 import os
+import re
 import subprocess
 import sys
 
@@ -22,6 +26,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmigemm.so")
+RESOURCES = os.path.join(PKG, "kernel_resources.json")
 SOURCES = ["api.cpp", "mfma16.hip", "mfma_i8.hip", "regtile_mfma.hip", "naive.hip",
            "lds_tiled.hip", "regtile_valu.hip", "fill.hip", "convert.hip", "pack.hip"]
 # The configuration tables' kernels are built from *_part.hip sources, once per
@@ -48,19 +53,67 @@ FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-W
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(job, resource_usage: bool, force: bool) -> tuple[str, str]:
+def _compile(job, force: bool) -> str:
     src, name, defines = job
     obj = os.path.join(BUILD, name + ".o")
-    if not force and not resource_usage and _up_to_date(obj, os.path.join(CSRC, src)):
-        return obj, ""
-    cmd = [HIPCC, *FLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
-    if resource_usage:
-        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    res = os.path.join(BUILD, name + ".res.json")
+    if not force and _up_to_date(obj, os.path.join(CSRC, src)) and os.path.exists(res):
+        return obj
+    cmd = [HIPCC, "-Rpass-analysis=kernel-resource-usage", *FLAGS, *defines, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     log = p.stdout + p.stderr
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src} ({name}):\n{log}")
-    return obj, log
+    with open(res, "w") as f:
+        json.dump(_parse_remarks(log), f)
+    return obj
+
+
+_FIELDS = {"TotalSGPRs": "sgpr", "VGPRs": "vgpr", "AGPRs": "agpr",
+           "ScratchSize [bytes/lane]": "scratch_bytes_per_lane",
+           "Occupancy [waves/SIMD]": "occupancy_waves_per_simd", "SGPRs Spill": "sgpr_spill",
+           "VGPRs Spill": "vgpr_spill", "LDS Size [bytes/block]": "lds_bytes"}
+
+
+def _parse_remarks(log: str) -> dict:
+    """Per-kernel figures from the kernel-resource-usage remarks of one compile."""
+    out, cur = {}, None
+    for line in log.splitlines():
+        m = re.search(r"remark: (?:Function Name: (\S+)|\s+([^:]+): (\S+))", line)
+        if not m or "kernel-resource-usage" not in line:
+            continue
+        if m.group(1):
+            cur = out.setdefault(m.group(1), {})
+        elif cur is not None and m.group(2).strip() in _FIELDS:
+            v = m.group(3)
+            cur[_FIELDS[m.group(2).strip()]] = int(v) if v.isdigit() else v
+    return out
+
+
+def _write_resources(objs) -> None:
+    """Merges the per-object remark figures into kernel_resources.json, with
+    demangled names (c++filt, where present)."""
+    table = {}
+    for obj in objs:
+        try:
+            with open(os.path.splitext(obj)[0] + ".res.json") as f:
+                table.update(json.load(f))
+        except (OSError, ValueError):
+            pass
+    names = sorted(table)
+    try:
+        p = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True,
+                           check=True)
+        demangled = p.stdout.splitlines()
+    except (OSError, subprocess.CalledProcessError):
+        demangled = []
+    if len(demangled) == len(names):
+        for n, d in zip(names, demangled):
+            table[n]["demangled"] = d
+    with open(RESOURCES, "w") as f:
+        json.dump({"note": "compiler figures per kernel (-Rpass-analysis=kernel-resource-usage)",
+                   "kernels": table}, f, indent=0)
 
 
 def _up_to_date(obj: str, src: str) -> bool:
@@ -81,7 +134,7 @@ def units():
     return sorted(u, key=lambda x: rank.get(x[1], len(rank)))
 
 
-def build(resource_usage: bool = False, jobs: int | None = None, force: bool = True) -> str:
+def build(jobs: int | None = None, force: bool = True) -> str:
     """Compile all sources and link libmigemm.so; returns the library path.
 
     force=False recompiles only objects older than their source or any header."""
@@ -89,21 +142,16 @@ def build(resource_usage: bool = False, jobs: int | None = None, force: bool = T
     us = units()
     jobs = jobs or max(1, len(os.sched_getaffinity(0)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(lambda u: _compile(u, resource_usage, force), us))
-    if resource_usage:
-        with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
-            for (_, name, _), (_, log) in zip(us, results):
-                f.write(f"==== {name}\n")
-                f.write("\n".join(l for l in log.splitlines() if "remark:" in l) + "\n")
+        objs = list(ex.map(lambda u: _compile(u, force), us))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
-           *[obj for obj, _ in results]]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stdout}{p.stderr}")
     os.replace(tmp, LIB)
+    _write_resources(objs)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(resource_usage="--resource-usage" in sys.argv, force="--incremental" not in sys.argv))
+    print(build(force="--incremental" not in sys.argv))
