@@ -21,12 +21,14 @@ LIBRARY_PATH = os.path.join(_HERE, "libmigemm.so")
 
 F32, F16, BF16, I8, I32 = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # the allocation-free entry point's scratch per GPU
 OP_N, OP_T = 0, 1
 VARIANT_AUTO, NAIVE, LDS_TILED, REGTILE_VALU, REGTILE_MFMA, MFMA16, MFMA_I8 = -1, 0, 1, 2, 3, 4, 5
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ("migemm_gemm", "migemm_gemm_variant", "migemm_gemm_ex", "migemm_gemm_ex_variant",
-           "migemm_gemm_ws", "migemm_workspace_size", "migemm_describe", "migemm_describe_ex",
+           "migemm_gemm_ws", "migemm_gemm_noalloc", "migemm_workspace_size", "migemm_describe",
+           "migemm_describe_ex",
            "migemm_convert",
            "migemm_variant_count", "migemm_variant_name",
            "migemm_variant_supports", "migemm_config_count", "migemm_config_name",
@@ -68,6 +70,9 @@ def lib():
     L.migemm_gemm_ws.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, vp, i64, vp, i64,
                                  f32, f32, i32, vp, i64, vp, i64, vp]
     L.migemm_gemm_ws.restype = i32
+    L.migemm_gemm_noalloc.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, vp, i64, vp, i64,
+                                      f32, f32, i32, vp, i64, vp]
+    L.migemm_gemm_noalloc.restype = i32
     L.migemm_workspace_size.argtypes = [i32, i32, i32, i32, i64, i64, i64, i32, vp, i64, vp,
                                         i64, ctypes.POINTER(i64)]
     L.migemm_workspace_size.restype = i32
@@ -129,6 +134,12 @@ def migemm_gemm_ws(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, 
                    c_dtype, C, ldc, workspace, workspace_bytes, stream=None) -> int:
     return lib().migemm_gemm_ws(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb,
                                 alpha, beta, c_dtype, C, ldc, workspace, workspace_bytes, stream)
+
+
+def migemm_gemm_noalloc(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb, alpha,
+                        beta, c_dtype, C, ldc, stream=None) -> int:
+    return lib().migemm_gemm_noalloc(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb,
+                                     alpha, beta, c_dtype, C, ldc, stream)
 
 
 def migemm_workspace_size(variant, config, op_a, op_b, M, N, K, dtype, A, lda, B, ldb):

@@ -222,6 +222,28 @@ int migemm_gemm_ws(int variant, int config, int op_a, int op_b,
                    void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * migemm_gemm_ws without a workspace argument, for callers that cannot
+ * allocate device memory or lend a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  The scratch memory
+ * comes from a fixed array of 64 MiB that the library's code object holds on
+ * every GPU it runs on, from the time the library is first used there until the
+ * process ends; the call itself allocates nothing.  A product that needs more
+ * scratch than that (migemm_workspace_size reports more than 64 MiB) is
+ * rejected with MIGEMM_ERR_WORKSPACE before any launch; products that need none
+ * run at any size.  All calls on one GPU share its array, and each call's
+ * kernels overwrite what they read of it, so nothing carries over between calls;
+ * but calls whose work overlaps in time on one GPU (on different streams, or
+ * from different host threads) race on the array: the caller orders them.
+ * Otherwise exactly migemm_gemm_ws, with the same selection as a call lent a
+ * 64 MiB workspace.
+ */
+int migemm_gemm_noalloc(int variant, int config, int op_a, int op_b,
+                        int64_t M, int64_t N, int64_t K, int dtype,
+                        const void* A, int64_t lda, const void* B, int64_t ldb,
+                        float alpha, float beta, int c_dtype, void* C, int64_t ldc,
+                        void* stream);
+
+/*
  * Writes to *bytes the workspace migemm_gemm_ws uses for these arguments when
  * lent at least that much (0: none; the selection that lent workspace leads
  * to).  Pointers are only inspected for alignment and may be NULL (read as
