@@ -124,6 +124,7 @@ class Problem:
         self.variant, self.config = names.index(self.desc["variant"]), self.desc["config"]
         self.stream = torch.cuda.current_stream()
         self.sp = self.stream.cuda_stream
+        self.launches = 0  # launches of this problem so far (to find the timed ones in a trace)
         self.args = (self.variant, self.config, *self.ops, *shape, *self.epi, self.C.data_ptr(),
                      w.N, *self.ws_args, self.sp)
 
@@ -154,6 +155,7 @@ class Problem:
         return out
 
     def launch(self):
+        self.launches += 1
         st = self.mg.migemm_gemm_ws(*self.args)
         if st != self.mg.OK:
             raise RuntimeError(f"{self.w.name}: {self.mg.migemm_status_string(st)} "
@@ -259,6 +261,8 @@ class ClockSampler:
         return False
 
     def summary(self):
+        # per sample: the mean over the XCDs; idle samples (before the first launch
+        # reaches the board, between windows) are kept, so the median is the figure
         clk = [statistics.mean(c) for c, _, _ in self.samples if c]
         pw = [p for _, p, _ in self.samples if isinstance(p, (int, float))]
         tmp = [t for _, _, t in self.samples if isinstance(t, (int, float))]
@@ -268,10 +272,11 @@ class ClockSampler:
         return {"source": "amdsmi GPU metrics (current_gfxclks averaged over XCDs, "
                           "current_socket_power), sampled during the steady-state windows",
                 "samples": len(self.samples),
-                "gfxclk_mhz_mean": round(statistics.mean(clk), 1),
+                "gfxclk_mhz_median": round(statistics.median(clk), 1),
                 "gfxclk_mhz_min": round(min(clk), 1), "gfxclk_mhz_max": round(max(clk), 1),
                 "gfxclk_limit_mhz": self.max_clk,
-                "socket_power_w_mean": round(statistics.mean(pw), 1) if pw else None,
+                "socket_power_w_median": round(statistics.median(pw), 1) if pw else None,
+                "socket_power_w_max": max(pw) if pw else None,
                 "hotspot_c_max": max(tmp) if tmp else None}
 
 
@@ -584,7 +589,10 @@ def main():
     log(f"bench: settled over {settle_n} launches ({settle_ms:.0f} ms); the first {a.steps} "
         f"from idle took {cold:.4f} ms each")
     log(f"bench: {w.name} on {p.kernel_name()}, warmup {a.warmup}, steps {a.steps}")
+    first_timed = p.launches + a.warmup + 1
     ms = p.time(a.steps, a.warmup)
+    log(f"bench: the timed steps are launches {first_timed}..{p.launches} of this kernel "
+        "in this process")
     tflops = w.flop / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log(f"bench: {ms:.4f} ms/step, {tflops:.1f} TFLOPS ({100 * tflops / peak:.1f}% of {peak})")
@@ -594,11 +602,13 @@ def main():
     clock = sampler.summary()
     st_tf = w.flop / (st_med * 1e-3) / 1e12
     log(f"bench: steady state {st_med:.4f} ms ({st_tf:.1f} TFLOPS), median of "
-        f"{len(st_windows)} windows of {st_n} launches; clock {clock.get('gfxclk_mhz_mean')} MHz")
+        f"{len(st_windows)} windows of {st_n} launches; clock {clock.get('gfxclk_mhz_median')} MHz, "
+        f"power {clock.get('socket_power_w_median')} W")
     timing = {"protocol": f"NaN-filled correctness launch; {settle_n} back-to-back launches "
                           f"({settle_ms:.0f} ms) so the power controller settles; {a.warmup} "
                           f"warm-up and {a.steps} timed steps (value); 5 windows of at least "
                           "50 ms (steady_state)",
+              "timed_launches": [first_timed, first_timed + a.steps - 1],
               "cold_first_k_ms": round(cold, 5),
               "cold_first_k_tflops": round(w.flop / (cold * 1e-3) / 1e12, 2),
               "settle_launches": settle_n, "settle_ms": round(settle_ms, 1),
@@ -672,9 +682,11 @@ def main():
             if not extra[name]["oracle"]["gpu_rows_ok"]:
                 raise SystemExit(f"bench.py: {name} does not match the oracle")
             if name == "c1-f32-1024":
-                for v, label in ((mg.NAIVE, "naive"), (mg.LDS_TILED, "lds_tiled"),
-                                 (mg.REGTILE_VALU, "regtile_valu")):
-                    pn = Problem(wx, v, -1)
+                # the baselines, each in its fastest configuration at this size
+                # (configuration sweep: naive 64x4, LDS 32x32, VALU 64x64x16 4x4)
+                for v, c, label in ((mg.NAIVE, 0, "naive"), (mg.LDS_TILED, 0, "lds_tiled"),
+                                    (mg.REGTILE_VALU, 2, "regtile_valu")):
+                    pn = Problem(wx, v, c)
                     extra[f"{name}/{label}"], tf = line(pn)
                     log(f"extra {name}/{label}: {tf:.2f} TFLOPS on {pn.kernel_name()}")
                     del pn

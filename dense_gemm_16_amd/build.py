@@ -29,7 +29,7 @@ LIB = os.path.join(PKG, "libmigemm.so")
 RESOURCES = os.path.join(PKG, "kernel_resources.json")
 SOURCES = ["api.cpp", "mfma16.hip", "mfma_i8.hip", "regtile_mfma.hip", "naive.hip",
            "lds_tiled.hip", "regtile_valu.hip", "fill.hip", "convert.hip", "pack.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "skinny16.hip"]
 # The configuration tables' kernels are built from *_part.hip sources, once per
 # configuration (and element type and output form), so that the compiles run in
 # parallel and a change rebuilds only what it touches.
@@ -41,7 +41,7 @@ PARTS = ([("mfma16_part.hip", f"mfma16_{et}_{'gen' if gen else 'plain'}_{c}",
           for gen in (False, True) for c in CFG16] +
          [("regtile_mfma_part.hip", f"regtile_mfma_{'gen' if gen else 'plain'}_{c}",
            [f"-DMIGEMM_PART_GEN={'true' if gen else 'false'}", f"-DMIGEMM_PART_C={c}"])
-          for gen in (False, True) for c in range(8)] +
+          for gen in (False, True) for c in range(12)] +
          [("mfma_i8_part.hip", f"mfma_i8_{c}", [f"-DMIGEMM_PART_C={c}"]) for c in range(5)])
 # Units that take longest, started first (measured compile times, seconds).
 SLOW_FIRST = ("mfma16_f16_gen_14", "mfma16_bf16_gen_14", "mfma_i8_4", "mfma16_f16_gen_4",

@@ -116,10 +116,10 @@ int check_args(int64_t M, int64_t N, int64_t K, int dtype, bool ta, bool tb, con
 }
 
 // 16-byte aligned operand pointers with leading dimensions of whole 16-byte
-// chunks (8 16-bit or 16 8-bit elements).  NULL pointers count as aligned
-// (migemm_select).
+// chunks (4 FP32, 8 16-bit or 16 8-bit elements).  NULL pointers count as
+// aligned (migemm_select).
 bool operands_aligned(const void* A, int64_t lda, const void* B, int64_t ldb, int dtype) {
-    const int64_t epc = dtype == MIGEMM_I8 ? 16 : 8;
+    const int64_t epc = 16 / elem_size(dtype);
     return aligned16(A) && aligned16(B) && lda % epc == 0 && ldb % epc == 0;
 }
 
@@ -142,8 +142,18 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
         return;
     }
     if (dtype == MIGEMM_F32) {
+        // Direct global->LDS staging (configurations 8-11) needs 16-byte aligned
+        // operands in whole 16-byte rows, K a multiple of 32 and the k-row image
+        // side (N for row-major B, M for A given transposed) a multiple of 4; it
+        // measured 105 against 66 TFLOPS at 1024^3 (64x64 tiles, 8 waves) and 142
+        // against 124 at 4096^3 (128x128 tiles).  Other operands stage through
+        // registers.
         variant = MIGEMM_REGTILE_MFMA;
-        config = tiles(128, 128) >= 256 ? 0 : 2;
+        const bool direct = aligned && K % 32 == 0 && (tb || N % 4 == 0) && (!ta || M % 4 == 0);
+        if (direct)
+            config = tiles(128, 128) >= 256 ? 10 : 8;
+        else
+            config = tiles(128, 128) >= 256 ? 0 : 2;
         return;
     }
     variant = MIGEMM_MFMA16;

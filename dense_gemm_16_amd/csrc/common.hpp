@@ -207,6 +207,11 @@ int64_t packed_k(int64_t K);
 // Alignment the packed path asks of a workspace.
 constexpr int64_t kWorkspaceAlign = 256;
 hipError_t launch_mfma_i8(const GemmArgs& a, int config);
+// FP16/BF16 products with 1 <= M <= 16 and K a multiple of 32, K split over the
+// waves of each workgroup (skinny16.hip); skinny16_fits says whether these and
+// its alignment needs hold (hipErrorInvalidValue from the launcher otherwise).
+bool skinny16_fits(const GemmArgs& a);
+hipError_t launch_skinny16(const GemmArgs& a);
 // K == 0: the sum of products is 0 for every element; applies the output step to it.
 hipError_t launch_empty_product(const GemmArgs& a);
 

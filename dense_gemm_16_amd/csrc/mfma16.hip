@@ -81,9 +81,10 @@ hipError_t launch_mfma16(const GemmArgs& g, int config) {
     // Configuration 7 (128x128 tiles): a last band of tile rows that takes the
     // tile count just past a whole number of rounds of workgroups on the 256
     // CUs would run nearly alone in a round of its own (a 2050-row product: 16
-    // of 272 tiles, about two thirds of a round's time).  Those rows go to the
-    // 64x64 tile (configuration 16) in a launch of their own, after the whole
-    // 128-row bands, on the same stream.
+    // of 272 tiles, about two thirds of a round's time).  Those rows go to a
+    // launch of their own, after the whole 128-row bands, on the same stream:
+    // up to 16 rows to the skinny kernel (K split over the waves of each
+    // workgroup), more to the 64x64 tile (configuration 16).
     if (config == 7) {
         constexpr int64_t kCus = 256;
         const int64_t tn = ceil_div(g.N, 128), m_main = (g.M / 128) * 128;
@@ -98,7 +99,8 @@ hipError_t launch_mfma16(const GemmArgs& g, int config) {
             const int64_t c_es = (g.out.c_dtype == 1 || g.out.c_dtype == 2) ? 2 : 4;
             tail.out.C = static_cast<char*>(g.out.C) + m_main * g.out.ldc * c_es;
             const hipError_t e = launch_mfma16(head, 7);
-            return e != hipSuccess ? e : launch_mfma16(tail, 16);
+            if (e != hipSuccess) return e;
+            return skinny16_fits(tail) ? launch_skinny16(tail) : launch_mfma16(tail, 16);
         }
     }
     return launch_cfg16_any(g, config);

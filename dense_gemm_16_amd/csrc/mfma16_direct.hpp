@@ -17,9 +17,17 @@
 //   instruction wants is produced by the read itself: two transposing reads
 //   give a lane the 16 bytes of consecutive k of one column of B.
 //
-// Everything is counted in 16-byte chunks, so the code serves 2-byte and
-// 1-byte elements alike: a 64-deep 16-bit k-tile and a 128-deep 8-bit one are
-// both 128 bytes per row.
+// Everything is counted in 16-byte chunks, so the code serves 4-, 2- and
+// 1-byte elements alike: a 32-deep FP32 k-tile, a 64-deep 16-bit one and a
+// 128-deep 8-bit one are all 128 bytes per row.
+//
+// FP32 (v_mfma_f32_16x16x4_f32, one element per lane and instruction): a 16-byte
+// row-image read hands a lane four consecutive k of one row of A, which feed
+// four instructions (element e to instruction e).  The matching B values are
+// four k-rows of one column; a k-row image has no 32-bit transposing read, so
+// they come from four 4-byte LDS reads, one per k-row.  The k-row swizzle
+// (swz_b32) puts the four lane groups of such a read on four distinct 16-bank
+// quarters.
 //
 // LDS images (per stage):
 //   A: [BM rows][8 chunks of 16 B]; logical chunk c of row r at physical chunk
@@ -114,7 +122,7 @@ struct DirectCfg {
     __device__ static int b_stage(int kt) {
         return SCHED == 4 ? (kt % 3) * STAGE_B : (kt % STAGES) * STAGE_BYTES + STAGE_A;
     }
-    static_assert(EB == 2 || EB == 1, "16-bit or 8-bit inputs");
+    static_assert(EB == 4 || EB == 2 || EB == 1, "32-, 16- or 8-bit inputs");
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "whole blocks per wave");
     static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "stages fit 160 KiB");
     static_assert(SCHED == 0 || SCHED == 2 || SCHED == 4, "scheduling policy 0, 2 or 4");
@@ -137,10 +145,11 @@ struct DirectOperand {
     static constexpr int RPI = 64 / CH;
     static constexpr int INSTR = (KROW ? BX : BK) / RPI;
     static constexpr int PER = INSTR / NW;                   // direct loads per wave per k-tile
-    static constexpr int SWZ_PERIOD = EB == 2 ? 16 : 32;
+    static constexpr int SWZ_PERIOD = EB == 1 ? 32 : 16;
     static_assert(!KROW || CH == 4 || CH == 8, "row images are 64 or 128 bytes wide");
-    static_assert(KROW || (EB == 2 ? (CH >= 8 && CH <= 64) : CH == 16),
-                  "k-row images: 8 to 64 chunks (16-bit), 16 chunks (8-bit)");
+    static_assert(KROW || (EB == 2 ? (CH >= 8 && CH <= 64) : EB == 4 ? (CH >= 16 && CH <= 64)
+                                                            : CH == 16),
+                  "k-row images: 8 to 64 chunks (16-bit), 16 to 64 (32-bit), 16 (8-bit)");
     static_assert(INSTR % NW == 0, "loads split evenly over waves");
 };
 
@@ -168,11 +177,17 @@ __device__ __forceinline__ int swz_b64(int krow) { return (((krow >> 1) & 1) | (
 // groups g: XOR with (krow & 7) | (bit 4 of krow) << 3 puts those 32 reads on 16
 // distinct chunk positions, two each, the minimum for 512 bytes.
 __device__ __forceinline__ int swz_b8(int krow) { return (krow & 7) | (((krow >> 4) & 1) << 3); }
+// The same for 32-bit elements (k-rows of 16 or more chunks).  A fragment read
+// takes, in lane group g, column j of k-row 16 s + 4 g + e (e = 0..3, one 4-byte
+// read each): XOR with 4 ((krow >> 2) & 3) moves group g's four chunks to a
+// quarter of the 64 banks of its own.
+__device__ __forceinline__ int swz_b32(int krow) { return ((krow >> 2) & 3) << 2; }
 // The k-row swizzle for operand O's element size.
 template <class O>
 __device__ __forceinline__ int swz_krow(int krow) {
     if constexpr (O::EPC == 8 && O::CH == 8) return swz_b64(krow);
     if constexpr (O::EPC == 8) return swz_b(krow);
+    if constexpr (O::EPC == 4) return swz_b32(krow);
     return swz_b8(krow);
 }
 
@@ -335,7 +350,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     // transposing reads, arranged so that lane j of each 16-lane group receives
     // column j of four (16-bit) or eight (8-bit) k-rows each time.
     constexpr int EB = Cfg::EB;
-    static_assert(EB == 2 || MF == 16, "8-bit inputs use 16 x 16 x 64 instructions");
+    static_assert(EB == 2 || MF == 16, "8-bit and 32-bit inputs use 16 x 16 instructions");
     constexpr int G = kWave / MF;          // k-groups per slab
     constexpr int SLAB_K = (16 / EB) * G;  // k per slab: 32 or 16 (16-bit), 64 (8-bit)
     constexpr int SLABS = BK / SLAB_K;
@@ -367,7 +382,18 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     auto read_krow_image = [&](const MIGEMM_LDS char* img, int bx, int w0, int t, int s)
         __attribute__((always_inline)) {
         u32x2 h[2];
-        if constexpr (EB == 2) {
+        if constexpr (EB == 4) {
+            // lane (j, g): column w0 + t MF + j of k-rows 16 s + 4 g + e, e = 0..3;
+            // (k-row >> 2) & 3 = g, so the swizzle is the lane's own
+            const int col = w0 + t * MF + bj;
+            const int phys = (col >> 2) ^ (ag << 2);
+            const int lane_off = (4 * ag) * (bx * 4) + phys * 16 + (col & 3) * 4;
+            u32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = *(const MIGEMM_LDS uint32_t*)(img + lane_off + (s * SLAB_K + e) * (bx * 4));
+            return v;
+        } else if constexpr (EB == 2) {
             // lane j of a group: column j of k-rows 4 half .. 4 half + 3 of its 8
             const int klane = 8 * ag + bj / 4;
             const int c0 = ((w0 + bcol) / 8) ^ (bx == 64 ? swz_b64(klane) : swz_b(klane));
@@ -430,7 +456,13 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     };
     // One slab step: LDS reads of the next fragments (load) and this slab's
     // matrix instructions (f), ordered as the SCHED policy says.
-    constexpr int kReads = (TA ? 2 : 1) * TM + (TB ? 1 : 2) * TN;  // LDS read instructions per slab
+    // LDS read instructions per slab: a row-image fragment is one 16-byte read,
+    // a k-row-image one two transposing reads (16- and 8-bit) or four 4-byte
+    // reads (32-bit); and matrix instructions per slab (four per fragment pair
+    // for 32-bit elements)
+    constexpr int kKrowReads = EB == 4 ? 4 : 2;
+    constexpr int kReads = (TA ? kKrowReads : 1) * TM + (TB ? 1 : kKrowReads) * TN;
+    constexpr int kMfma = TM * TN * (EB == 4 ? 4 : 1);
     auto slab_step = [&](bool do_load, int lkt, int ls, Frags& fl, const Frags& f) __attribute__((always_inline)) {
         if (do_load) load_frags(lkt, ls, fl);
         if constexpr (Cfg::SCHED == 2) {
@@ -441,8 +473,8 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            if constexpr (TM * TN > kReads)
-                __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - kReads, 0);
+            if constexpr (kMfma > kReads)
+                __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
             __builtin_amdgcn_sched_barrier(0);
         } else {
             __builtin_amdgcn_sched_barrier(0);

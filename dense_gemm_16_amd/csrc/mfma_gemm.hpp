@@ -348,7 +348,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma_gemm_kernel(
     int64_t M, int64_t N, int64_t K, const typename Cfg::E* __restrict__ A, int64_t lda,
     const typename Cfg::E* __restrict__ B, int64_t ldb, Epi out, int tiles_m, int tiles_n) {
     using E = typename Cfg::E;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, MF = Cfg::MF, NT = Cfg::NT, VEC = Cfg::VEC;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, MF = Cfg::MF, NT = Cfg::NT;
     constexpr int CH = Cfg::CH, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN, G = Cfg::G;
     using Op = MfmaOp<E, MF>;
     using Acc = typename Op::Acc;

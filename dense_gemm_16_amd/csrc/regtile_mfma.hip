@@ -1,7 +1,11 @@
 // regtile_mfma.hip -- FP32 GEMM on the FP32 matrix-core instructions: the
 // configuration names and the dispatch (each configuration's kernels are
 // compiled in regtile_mfma_part.hip, one object per configuration and output
-// form).
+// form).  Configurations 0-7 stage tiles through registers; 8-11 load them
+// straight into LDS (the direct-staged kernel of mfma16_direct.hpp on 32-bit
+// elements) and need 16-byte aligned operands in whole 16-byte rows, K a
+// multiple of 32 and the k-row image side (N for row-major B) a multiple of 4;
+// other shapes run their register-staged fallback.
 //
 // The register-micro-tiled FP32 design (page "matmul_registers.cu",
 // matmulRegTile2dVec4: 16-byte global loads, a k-major operand in LDS,
@@ -24,7 +28,11 @@ namespace {
 const char* const kNames[] = {"128x128x32 4w 16x16x4", "128x128x32 4w 32x32x2",
                               "64x64x32 4w 16x16x4", "256x128x32 4w 32x32x2",
                               "128x64x32 4w 16x16x4", "64x64x32 8w 16x16x4",
-                              "128x128x32 8w 16x16x4", "64x32x32 4w 16x16x4"};
+                              "128x128x32 8w 16x16x4", "64x32x32 4w 16x16x4",
+                              "direct 64x64x32 8w 16x16x4 s4 ilv ntC",
+                              "direct 64x64x32 4w 16x16x4 s4 ilv ntC",
+                              "direct 128x128x32 8w 16x16x4 gm4 s4 ilv ntC",
+                              "direct 128x64x32 8w 16x16x4 s4 ilv ntC"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 template <bool GEN>
@@ -37,6 +45,10 @@ hipError_t launch_gen(const GemmArgs& g, int config) {
         case 5: return launch_f32_cfg<GEN, 5>(g);
         case 6: return launch_f32_cfg<GEN, 6>(g);
         case 7: return launch_f32_cfg<GEN, 7>(g);
+        case 8: return launch_f32_cfg<GEN, 8>(g);
+        case 9: return launch_f32_cfg<GEN, 9>(g);
+        case 10: return launch_f32_cfg<GEN, 10>(g);
+        case 11: return launch_f32_cfg<GEN, 11>(g);
         default: return launch_f32_cfg<GEN, 0>(g);
     }
 }

@@ -2,7 +2,7 @@
 // (see regtile_mfma.hip).  Built once per (output form, configuration): the
 // build passes MIGEMM_PART_GEN (false: plain FP32 overwrite; true: the general
 // output step) and MIGEMM_PART_C (the configuration index).
-#include "mfma_gemm.hpp"
+#include "mfma16_direct.hpp"
 
 namespace migemm {
 namespace {
@@ -15,6 +15,31 @@ using F4 = MfmaCfg<float, 128, 64, 2, 2, 16>;
 using F5 = MfmaCfg<float, 64, 64, 2, 4, 16>;    // 8 waves of 32x16: two waves per SIMD
 using F6 = MfmaCfg<float, 128, 128, 2, 4, 16>;  // 8 waves of 64x32
 using F7 = MfmaCfg<float, 64, 32, 2, 2, 16>;    // 4 waves of 32x16, twice F2's workgroups
+// direct-staged (global -> LDS without registers, mfma16_direct.hpp with 32-bit
+// elements): <E, BM, BN, WM, WN, MF, STAGES, BK, GM, SCHED, FLAGS>; FLAGS 16: all
+// operand layouts, | 2: non-temporal C stores (chosen when C rows are whole lines)
+using D8 = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 18>;     // 8 waves of 32x16
+using D8P = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 16>;
+using D9 = DirectCfg<float, 64, 64, 2, 2, 16, 4, 32, 8, 2, 18>;     // 4 waves of 32x32
+using D9P = DirectCfg<float, 64, 64, 2, 2, 16, 4, 32, 8, 2, 16>;
+using D10 = DirectCfg<float, 128, 128, 2, 4, 16, 4, 32, 4, 2, 18>;  // 8 waves of 64x32
+using D10P = DirectCfg<float, 128, 128, 2, 4, 16, 4, 32, 4, 2, 16>;
+using D11 = DirectCfg<float, 128, 64, 2, 4, 16, 4, 32, 8, 2, 18>;   // 8 waves of 64x16
+using D11P = DirectCfg<float, 128, 64, 2, 4, 16, 4, 32, 8, 2, 16>;
+
+// Rows of C that start whole 128-byte lines take non-temporal stores.
+inline bool c_whole_lines(const Epi& o) {
+    const int64_t eb = (o.c_dtype == 1 || o.c_dtype == 2) ? 2 : 4;
+    return (o.ldc * eb) % 128 == 0 && (reinterpret_cast<uintptr_t>(o.C) & 127) == 0;
+}
+
+// The direct-staged configuration (NT stores or plain) where its preconditions
+// hold, else the register-staged configuration with index F.
+template <class D, class DP, int F, bool GEN>
+hipError_t direct_or(const GemmArgs& g) {
+    if (!direct_fits<D>(g)) return launch_regtile_mfma(g, F);
+    return c_whole_lines(g.out) ? launch_direct_cfg<D, GEN>(g) : launch_direct_cfg<DP, GEN>(g);
+}
 
 }  // namespace
 
@@ -28,6 +53,10 @@ hipError_t launch_f32_cfg(const GemmArgs& g) {
     else if constexpr (C == 5) return launch_mfma_cfg<F5, GEN>(g);
     else if constexpr (C == 6) return launch_mfma_cfg<F6, GEN>(g);
     else if constexpr (C == 7) return launch_mfma_cfg<F7, GEN>(g);
+    else if constexpr (C == 8) return direct_or<D8, D8P, 2, GEN>(g);
+    else if constexpr (C == 9) return direct_or<D9, D9P, 2, GEN>(g);
+    else if constexpr (C == 10) return direct_or<D10, D10P, 0, GEN>(g);
+    else if constexpr (C == 11) return direct_or<D11, D11P, 4, GEN>(g);
     else
         static_assert(C == 0, "no such configuration");
 }

@@ -278,6 +278,20 @@ def test_selection_packs_unreadable_16bit_operands():
     assert _selected(8192, 8192, 8192, 2, 8192, 8192, big) == ("mfma16", 14)
 
 
+def test_fp32_selection():
+    sel = lambda M, N, K, lda, ldb: mg.migemm_select(M, N, K, mg.F32, None, lda, None, ldb, None, N)
+    # direct-staged FP32: 64x64 tiles below a round of 128x128 tiles, 128x128 above
+    assert sel(1024, 1024, 1024, 1024, 1024) == (mg.OK, mg.REGTILE_MFMA, 8)
+    assert sel(4096, 4096, 4096, 4096, 4096) == (mg.OK, mg.REGTILE_MFMA, 10)
+    # rows not in whole 16-byte chunks, K not a multiple of 32, N not a multiple of 4:
+    # register-staged
+    assert sel(1024, 1024, 1024, 1025, 1024) == (mg.OK, mg.REGTILE_MFMA, 2)
+    assert sel(1024, 1024, 1000, 1000, 1024) == (mg.OK, mg.REGTILE_MFMA, 2)
+    assert sel(4096, 4094, 4096, 4096, 4094) == (mg.OK, mg.REGTILE_MFMA, 0)
+    for c in (8, 9, 10, 11):
+        assert mg.migemm_config_name(mg.REGTILE_MFMA, c).startswith("direct")
+
+
 def test_workspace_size():
     ws = lambda *a: mg.migemm_workspace_size(*a)
     # 2050 x 2047 x 2056 FP16, ldb = 2047: both operands packed with K' = 2112,
@@ -312,12 +326,12 @@ def test_describe():
     # on a machine with a GPU the kernel's attributes follow; without one, a note
     assert "regs0" in d or "resources0" in d
     # the ragged product with a workspace: the copy, then 256 tiles of 128 x 128
-    # over rows 0..2047, then the last 2 rows on 32 tiles of 64 x 64
+    # over rows 0..2047, then the last 2 rows on 128 workgroups of 16 columns
     st, text = mg.migemm_describe_ex(-1, -1, 0, 0, 2050, 2047, 2056, mg.F16, None, 2056, None,
                                      2047, mg.F32, 2047, 1 << 30)
     d = mg._parse_description(text)
     assert st == mg.OK and d["config"] == 12 and d["workspace_bytes"] == 17305728
-    assert d["launches"] == 3 and d["grid1"] == 256 and d["grid2"] == 32
+    assert d["launches"] == 3 and d["grid1"] == 256 and d["grid2"] == 128
     assert d["workspace_lent"] == 1 << 30
     # FP32 and INT8
     d = mg._parse_description(mg.migemm_describe(1024, 1024, 1024, mg.F32, 1024, 1024, 1024)[1])
