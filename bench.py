@@ -43,7 +43,6 @@ import json
 import os
 import statistics
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -207,17 +206,15 @@ class Problem:
         return statistics.median(x for x, _ in t), [round(x, 5) for x, _ in t], t[0][1]
 
 
-class ClockSampler:
-    """Samples the board's graphics clock and socket power (amdsmi GPU metrics)
-    in a background thread while the steady-state windows run.  Reports null
-    when amdsmi is not usable on the box or the GPU cannot be matched."""
+class ClockProbe:
+    """The board's graphics clock and socket power (amdsmi GPU metrics) while a
+    problem runs back to back: the launches of a window of about `ms` are queued
+    first, then the host samples the metrics until the window's end event has
+    passed.  Reports a note instead of figures when amdsmi is not usable on the
+    box or the GPU cannot be matched to an amdsmi device."""
 
-    def __init__(self, period_s=0.002):
-        self.period, self.samples, self.error = period_s, [], None
-        self._stop = threading.Event()
-        self._thread = None
-        self._h = None
-        self.max_clk = None
+    def __init__(self):
+        self.error, self._h, self.max_clk = None, None, None
         try:
             import amdsmi
             import torch
@@ -236,42 +233,46 @@ class ClockSampler:
         except Exception as e:  # amdsmi missing, no permission, older torch ...
             self.error = f"{type(e).__name__}: {e}"[:200]
 
-    def _run(self):
-        while not self._stop.is_set():
+    def during(self, p, ms=400.0):
+        import torch
+        if self._h is None:
+            return {"source": "amdsmi GPU metrics", "samples": 0, "note": self.error}
+        est = p.time(3, 1)
+        n = int(max(20, min(5000, ms / max(est, 1e-3))))
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(p.stream)
+        for _ in range(n):
+            p.launch()
+        t1.record(p.stream)
+        samples = []
+        while not t1.query():
             try:
                 m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
-                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int)]
-                self.samples.append((clks, m.get("current_socket_power"),
-                                     m.get("temperature_hotspot")))
             except Exception as e:
                 self.error = f"{type(e).__name__}: {e}"[:200]
-                return
-            time.sleep(self.period)
-
-    def __enter__(self):
-        if self._h is not None:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread:
-            self._thread.join(timeout=2.0)
-        return False
-
-    def summary(self):
-        # per sample: the mean over the XCDs; idle samples (before the first launch
-        # reaches the board, between windows) are kept, so the median is the figure
-        clk = [statistics.mean(c) for c, _, _ in self.samples if c]
-        pw = [p for _, p, _ in self.samples if isinstance(p, (int, float))]
-        tmp = [t for _, _, t in self.samples if isinstance(t, (int, float))]
+                break
+            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int)]
+            pw = m.get("current_socket_power")
+            if clks:
+                samples.append((statistics.mean(clks), pw if isinstance(pw, (int, float)) else None,
+                                m.get("temperature_hotspot")))
+            time.sleep(0.002)
+        t1.synchronize()
+        window_ms = t0.elapsed_time(t1) / n
+        # the first and last samples can fall before the first launch reaches the
+        # board or after the last: the middle half is the figure
+        mid = samples[len(samples) // 4: max(len(samples) // 4 + 1, 3 * len(samples) // 4)]
+        clk = [c for c, _, _ in mid]
+        pw = [x for _, x, _ in mid if x is not None]
+        tmp = [t for _, _, t in mid if isinstance(t, (int, float))]
         if not clk:
             return {"source": "amdsmi GPU metrics", "samples": 0,
                     "note": self.error or "no samples"}
-        return {"source": "amdsmi GPU metrics (current_gfxclks averaged over XCDs, "
-                          "current_socket_power), sampled during the steady-state windows",
-                "samples": len(self.samples),
+        return {"source": "amdsmi GPU metrics (current_gfxclks averaged over the XCDs, "
+                          "current_socket_power), sampled by the host during a window of "
+                          f"{n} back-to-back launches; middle half of the samples",
+                "samples": len(mid), "window_ms_per_launch": round(window_ms, 5),
                 "gfxclk_mhz_median": round(statistics.median(clk), 1),
                 "gfxclk_mhz_min": round(min(clk), 1), "gfxclk_mhz_max": round(max(clk), 1),
                 "gfxclk_limit_mhz": self.max_clk,
@@ -596,10 +597,8 @@ def main():
     tflops = w.flop / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     log(f"bench: {ms:.4f} ms/step, {tflops:.1f} TFLOPS ({100 * tflops / peak:.1f}% of {peak})")
-    sampler = ClockSampler()
-    with sampler:
-        st_med, st_windows, st_n = p.steady()
-    clock = sampler.summary()
+    st_med, st_windows, st_n = p.steady()
+    clock = ClockProbe().during(p)
     st_tf = w.flop / (st_med * 1e-3) / 1e12
     log(f"bench: steady state {st_med:.4f} ms ({st_tf:.1f} TFLOPS), median of "
         f"{len(st_windows)} windows of {st_n} launches; clock {clock.get('gfxclk_mhz_median')} MHz, "

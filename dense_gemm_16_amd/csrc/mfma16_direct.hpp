@@ -484,6 +484,129 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     };
 
     // Epilogue: the wave's accumulators to C (guarded at the matrix edges).
+    // The general output step through LDS, for wave tiles 64 columns wide (see
+    // store_tile).  Each wave uses 4 KiB of LDS of its own, 16 rows x 64 FP32
+    // values, with the 16-byte chunk index XORed by (row >> 2) & 3 so that the
+    // accumulator writes (lane group g: rows 4 g .. 4 g + 3) spread over four
+    // bank quarters.  The LDS is free by then: in the ping-pong schedule every
+    // wave's last fragment reads completed before the barrier that ended its
+    // group's last reading turn; the other schedules meet a barrier first.
+    // Per 16-row block i: the accumulators are written, then read back a row
+    // piece per lane (8 outputs for 16-bit C, 4 for FP32 C: 16 bytes of C), with
+    // the previous C of blocks i + 1 .. i + kAhead already loading.  The update
+    // is store_update's arithmetic, so results are bit-identical to it.
+    auto lds_epilogue = [&]() __attribute__((always_inline)) {
+        if constexpr (Cfg::SCHED != 4) __syncthreads();
+        constexpr bool NT = (Cfg::FLAGS & 2) != 0;
+        constexpr int kAhead = TM >= 3 ? 2 : TM - 1, kRing = kAhead + 1;
+        MIGEMM_LDS float* const scr =
+            (MIGEMM_LDS float*)((MIGEMM_LDS char*)smem + wave * (16 * 64 * 4));
+        const bool rd = out.beta != 0.0f;
+        const int g = lane >> 4, jl = lane & 15;
+        // HALF: 16-bit C, 2 passes of 8 rows x 8 columns per lane; otherwise FP32
+        // C, 4 passes of 4 rows x 4 columns.  Pass p: this lane's row and first
+        // column in the wave tile's 16 x 64 block.
+        auto body = [&](auto half_tag) __attribute__((always_inline)) {
+            constexpr bool HALF = decltype(half_tag)::value;
+            constexpr int P = HALF ? 2 : 4, VE = HALF ? 8 : 4, ES = HALF ? 2 : 4;
+            const int prow = HALF ? (lane >> 3) : (lane >> 4);
+            const int c0 = HALF ? 8 * (lane & 7) : 4 * (lane & 15);
+            const bool vec_c = (out.ldc * ES) % 16 == 0 &&
+                               (reinterpret_cast<uintptr_t>(out.C) & 15) == 0;
+            const int64_t gcol = n0 + wn0 + c0;
+            const bool col_ok = vec_c && gcol + VE <= N;
+            auto load_old = [&](int i, u32x4 (&o)[P]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    const int64_t grow = m0 + wm0 + i * 16 + (16 / P) * p + prow;
+                    o[p] = u32x4{0u, 0u, 0u, 0u};
+                    if (rd && col_ok && grow < M)
+                        o[p] = *reinterpret_cast<const u32x4*>(
+                            static_cast<const char*>(out.C) + (grow * out.ldc + gcol) * ES);
+                }
+            };
+            u32x4 ring[kRing][P];
+#pragma unroll
+            for (int i = 0; i < kAhead; ++i) load_old(i, ring[i]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                if (i + kAhead < TM) load_old(i + kAhead, ring[(i + kAhead) % kRing]);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        scr[(4 * g + r) * 64 + ((16 * j + jl) ^ (g << 4))] = acc[i][j][r];
+                asm volatile("" : : : "memory");
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    const int row = (16 / P) * p + prow;
+                    const int phys = c0 ^ (((row >> 2) & 3) << 4);
+                    const int64_t grow = m0 + wm0 + i * 16 + row;
+                    const int64_t idx = grow * out.ldc + gcol;
+                    float v[VE];
+                    {
+                        const f32x4 v0 = *(const MIGEMM_LDS f32x4*)(scr + row * 64 + phys);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = v0[e];
+                        if constexpr (HALF) {
+                            const f32x4 v1 = *(const MIGEMM_LDS f32x4*)(scr + row * 64 + phys + 4);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[4 + e] = v1[e];
+                        }
+                    }
+                    if (grow < M) {
+                        if (col_ok) {
+                            const u32x4 old = ring[i % kRing][p];
+                            u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+                            for (int e = 0; e < VE; ++e) {
+                                if constexpr (HALF) {
+                                    const uint32_t ob = (old[e / 2] >> (16 * (e % 2))) & 0xffffu;
+                                    const float prev =
+                                        out.c_dtype == 1
+                                            ? static_cast<float>(__builtin_bit_cast(
+                                                  _Float16, static_cast<uint16_t>(ob)))
+                                            : __uint_as_float(ob << 16);
+                                    const float res = rd ? fmaf(out.alpha, v[e], out.beta * prev)
+                                                         : out.alpha * v[e];
+                                    const uint32_t nb =
+                                        out.c_dtype == 1
+                                            ? static_cast<uint32_t>(__builtin_bit_cast(
+                                                  uint16_t, static_cast<_Float16>(res)))
+                                            : static_cast<uint32_t>(f32_to_bf16_bits(res));
+                                    w[e / 2] |= nb << (16 * (e % 2));
+                                } else {
+                                    const float res =
+                                        rd ? fmaf(out.alpha, v[e], out.beta * __uint_as_float(old[e]))
+                                           : out.alpha * v[e];
+                                    w[e] = __float_as_uint(res);
+                                }
+                            }
+                            u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(out.C) + idx * ES);
+                            if constexpr (NT)
+                                __builtin_nontemporal_store(w, dst);
+                            else
+                                *dst = w;
+                        } else {
+                            // edges and unaligned C, element by element (the values
+                            // reread from LDS keep this loop rolled and small)
+#pragma nounroll
+                            for (int e = 0; e < VE; ++e)
+                                if (gcol + e < N)
+                                    store_update<NT>(out, idx + e, scr[row * 64 + (phys + e)],
+                                                     rd ? load_prev(out, idx + e) : 0.0f);
+                        }
+                    }
+                }
+                asm volatile("" : : : "memory");
+            }
+        };
+        if (out.c_dtype == 1 || out.c_dtype == 2)
+            body(std::integral_constant<bool, true>{});
+        else
+            body(std::integral_constant<bool, false>{});
+    };
+
     auto store_tile = [&]() __attribute__((always_inline)) {
         const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
         const int lc = L::col(lane);
@@ -494,7 +617,16 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         auto index = [&](int i, int j, int r) __attribute__((always_inline)) {
             return (m0 + wm0 + i * MF + L::row(lane, r)) * out.ldc + n0 + wn0 + j * MF + lc;
         };
-        if constexpr (!GEN) {
+        // The general step for wave tiles 64 columns wide (16x16 instructions,
+        // 16- and 32-bit inputs): each 16-row block of the wave's accumulators
+        // goes through LDS into row-major order, so the previous C is read and the
+        // result written 16 bytes per lane in whole 128-byte lines, instead of 2- or
+        // 4-byte accesses in 32- or 64-byte row pieces (the 16x16 accumulator
+        // layout: four rows of one column per lane).
+        constexpr bool kLdsEpilogue = GEN && MF == 16 && Cfg::WTN == 64 && EB != 1;
+        if constexpr (kLdsEpilogue) {
+            lds_epilogue();
+        } else if constexpr (!GEN) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll

@@ -16,9 +16,12 @@
 //
 // The copy is memory-bound: 2 bytes read and 2 written per element copied,
 // small beside the product for the shapes this path is selected for.  One
-// launch copies both operands, a workgroup one 64 x 64 tile at a time, through
-// LDS so that the reads (2 bytes per lane, any alignment) and the writes (16
-// bytes per lane) are contiguous across a wavefront in either orientation.
+// launch copies both operands, a workgroup one 64 x 64 tile at a time.  An
+// operand that is transposed on the way (or whose rows are not 16-byte
+// aligned) goes through LDS, so that the reads (2 bytes per lane, any
+// alignment) and the writes (16 bytes per lane) are contiguous across a
+// wavefront in either orientation; one that keeps its orientation and has
+// aligned rows (A with only K to pad, say) is copied 16 bytes at a time.
 //
 // Workspace: (M + N) * K' * 2 bytes at most (each copied operand, A' first,
 // rounded up to 256 bytes), lent by the caller for this one call and
@@ -43,6 +46,7 @@ struct PackJob {
     uint16_t* dst;
     int64_t ldd, cols_out, tiles_c, tiles;
     int trans;
+    int vec;  // not transposed, rows 16-byte aligned: straight 16-byte copies
 };
 
 // Workgroups stride over the 64 x 64 tiles of both jobs (job 0's tiles first).
@@ -58,6 +62,26 @@ __global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
         const PackJob& j = second ? j1 : j0;
         const int64_t tt = second ? t - j0.tiles : t;
         const int64_t r0 = (tt / j.tiles_c) * kTile, c0 = (tt % j.tiles_c) * kTile;
+        if (j.vec) {
+            // 64 rows x 8 chunks of 16 bytes, two per work-item; the chunk that
+            // straddles cols (cols not a multiple of 8) is read element by element
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int q = threadIdx.x + 256 * i;
+                const int64_t r = r0 + q / 8, c = c0 + 8 * (q % 8);
+                if (r >= j.rows || c >= j.cols_out) continue;
+                u32x4 w = {0u, 0u, 0u, 0u};
+                const uint16_t* s = j.src + r * j.lds + c;
+                if (c + 8 <= j.cols) {
+                    w = *reinterpret_cast<const u32x4*>(s);
+                } else if (c < j.cols) {
+                    for (int e = 0; e < 8 && c + e < j.cols; ++e)
+                        w[e / 2] |= static_cast<uint32_t>(s[e]) << (16 * (e % 2));
+                }
+                *reinterpret_cast<u32x4*>(j.dst + r * j.ldd + c) = w;
+            }
+            continue;  // the whole workgroup takes this branch: no barrier is skipped
+        }
         // tile[c - c0][r - r0] = src(r, c), zero outside the source.  Every
         // load reads a clamped in-bounds address and the zero is selected
         // afterwards, so the sixteen loads of a lane are in flight together.
@@ -117,6 +141,7 @@ PackJob make_job(const void* src, int64_t lds, int64_t rows, int64_t cols, bool 
     j.tiles_c = ceil_div(cols_out, kTile);
     j.tiles = ceil_div(rows, kTile) * j.tiles_c;
     j.trans = trans ? 1 : 0;
+    j.vec = !trans && aligned16(src) && lds % 8 == 0;
     return j;
 }
 
