@@ -233,7 +233,7 @@ class ClockProbe:
         except Exception as e:  # amdsmi missing, no permission, older torch ...
             self.error = f"{type(e).__name__}: {e}"[:200]
 
-    def during(self, p, ms=400.0):
+    def during(self, p, ms=1500.0):
         import torch
         if self._h is None:
             return {"source": "amdsmi GPU metrics", "samples": 0, "note": self.error}
@@ -260,9 +260,9 @@ class ClockProbe:
             time.sleep(0.002)
         t1.synchronize()
         window_ms = t0.elapsed_time(t1) / n
-        # the first and last samples can fall before the first launch reaches the
-        # board or after the last: the middle half is the figure
-        mid = samples[len(samples) // 4: max(len(samples) // 4 + 1, 3 * len(samples) // 4)]
+        # the firmware refreshes these metrics every few hundred milliseconds, and the
+        # first samples can still show the idle board: the second half is the figure
+        mid = samples[len(samples) // 2:]
         clk = [c for c, _, _ in mid]
         pw = [x for _, x, _ in mid if x is not None]
         tmp = [t for _, _, t in mid if isinstance(t, (int, float))]
@@ -271,7 +271,8 @@ class ClockProbe:
                     "note": self.error or "no samples"}
         return {"source": "amdsmi GPU metrics (current_gfxclks averaged over the XCDs, "
                           "current_socket_power), sampled by the host during a window of "
-                          f"{n} back-to-back launches; middle half of the samples",
+                          f"{n} back-to-back launches; second half of the samples (the "
+                          "firmware refreshes them every few hundred milliseconds)",
                 "samples": len(mid), "window_ms_per_launch": round(window_ms, 5),
                 "gfxclk_mhz_median": round(statistics.median(clk), 1),
                 "gfxclk_mhz_min": round(min(clk), 1), "gfxclk_mhz_max": round(max(clk), 1),

@@ -57,11 +57,23 @@ __global__ __launch_bounds__(kWaves * kWave) void skinny16_kernel(int64_t M, int
     const bool a_in = r < M;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int64_t steps = K / 32;
-    for (int64_t s = wave; s < steps; s += kWaves) {
-        const int64_t k0 = s * 32 + 8 * g;
-        const u32x4 a = a_in ? krun<E, !TA>(A, lda, r, k0) : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 b = krun<E, TB>(B, ldb, n, k0);
-        Op::run(acc, a, b);
+    // kBatch of this wave's steps per round, all their loads issued before the
+    // first matrix instruction: one memory latency per round instead of per step
+    constexpr int kBatch = 4;
+    for (int64_t s0 = wave; s0 < steps; s0 += kBatch * kWaves) {
+        u32x4 a[kBatch], b[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int64_t s = s0 + q * kWaves;
+            a[q] = b[q] = u32x4{0u, 0u, 0u, 0u};
+            if (s < steps) {
+                const int64_t k0 = s * 32 + 8 * g;
+                if (a_in) a[q] = krun<E, !TA>(A, lda, r, k0);
+                b[q] = krun<E, TB>(B, ldb, n, k0);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) Op::run(acc, a[q], b[q]);
     }
     part[wave][lane] = acc;
     __syncthreads();
