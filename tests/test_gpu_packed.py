@@ -222,3 +222,41 @@ def test_packed_last_row_band_split():
                                    config=cfg, ta=ta, tb=tb, ldc=N + pad)
         check_ex(C, A, B, dtype, alpha, beta, c_code, old, ref=ref)
         assert padding_untouched(buf, mask)
+
+
+def test_split_tail_on_the_skinny_kernel():
+    """The rows past the last whole 128-row band, when they would start a second
+    round of workgroups: 1 to 16 rows go to the skinny kernel (K split over the
+    waves of each workgroup), more to the 64x64 tile.  Cases: 1, 4, 16 and 17 tail
+    rows on the direct path; B given transposed (k-contiguous skinny loads); A
+    given transposed; the general output step into FP32 and BF16 C; and the
+    packed path (ragged K)."""
+    dtype = "bf16"
+    # (M, N, K, ta, tb, C dtype code, configuration)
+    cases = [(2049, 2048, 128, False, False, 0, 7),
+             (2052, 2000, 192, False, False, 0, 7),
+             (2064, 2048, 64, False, True, 0, 7),
+             (2065, 2048, 128, False, False, 0, 7),
+             (2056, 2040, 128, True, False, 0, 7),
+             (2049, 2048, 128, False, False, 2, 7),
+             (2051, 2047, 100, False, False, 0, 12),
+             (2053, 2048, 96, True, True, 1, 12)]
+    for (M, N, K, ta, tb, c_code, cfg) in cases:
+        A, B = inputs.pair(M, N, K, dtype, "normal", seed=M + 3 * N + K + ta + 2 * tb)
+        ref = oracle_ref(A, B, dtype)
+        alpha, beta = (1.0, 0.0) if c_code == 0 else (-0.5, 1.5)
+        old = None
+        if c_code:
+            old = (torch.rand((M, N), generator=torch.Generator().manual_seed(K)) - 0.5).to(
+                {1: torch.float16, 2: torch.bfloat16}[c_code])
+        say(f"split tail cfg={cfg} {_name(ta, tb)} {M}x{N}x{K} c_dtype={c_code}")
+        C, buf, mask = run_gemm_ex(A, B, dtype, alpha, beta, c_code, old, variant=mg.MFMA16,
+                                   config=cfg, ta=ta, tb=tb)
+        check_ex(C, A, B, dtype, alpha, beta, c_code, old, ref=ref)
+        assert padding_untouched(buf, mask)
+    # what runs: the main launch, then the tail on 16-column workgroups (or 64x64 tiles)
+    for (M, tail_grid) in [(2049, 128), (2064, 128), (2065, 32)]:
+        st, text = mg.migemm_describe_ex(mg.MFMA16, 7, 0, 0, M, 2048, 128, 2, None, 128, None,
+                                         2048, 0, 2048, 0)
+        d = mg._parse_description(text)
+        assert st == mg.OK and d["launches"] == 2 and d["grid1"] == tail_grid, text
