@@ -143,13 +143,13 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
     }
     if (dtype == MIGEMM_F32) {
         // Direct global->LDS staging (configurations 8-11) needs 16-byte aligned
-        // operands in whole 16-byte rows, K a multiple of 32 and the k-row image
-        // side (N for row-major B, M for A given transposed) a multiple of 4; it
-        // measured 105 against 66 TFLOPS at 1024^3 (64x64 tiles, 8 waves) and 142
-        // against 124 at 4096^3 (128x128 tiles).  Other operands stage through
-        // registers.
+        // operands in whole 16-byte rows, K a multiple of 4 (a last k-tile that K
+        // ends inside is zero-filled in LDS) and the k-row image side (N for
+        // row-major B, M for A given transposed) a multiple of 4; it measured 105
+        // against 66 TFLOPS at 1024^3 (64x64 tiles, 8 waves) and 142 against 124
+        // at 4096^3 (128x128 tiles).  Other operands stage through registers.
         variant = MIGEMM_REGTILE_MFMA;
-        const bool direct = aligned && K % 32 == 0 && (tb || N % 4 == 0) && (!ta || M % 4 == 0);
+        const bool direct = aligned && K % 4 == 0 && (tb || N % 4 == 0) && (!ta || M % 4 == 0);
         if (direct)
             config = tiles(128, 128) >= 256 ? 10 : 8;
         else
@@ -158,21 +158,28 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
     }
     variant = MIGEMM_MFMA16;
     // Direct global->LDS staging needs 16-byte aligned operands with leading
-    // dimensions a multiple of 8 elements, K a multiple of 64, and N (row-major
-    // B) or M (A given transposed) a multiple of 8; the launcher falls back to
-    // the register-staged kernel otherwise.  Other operands are packed into
+    // dimensions a multiple of 8 elements, K a multiple of 8 (of the 64-deep
+    // k-tile for configurations 10, 14 and 15; configurations 7, 13 and 16
+    // zero-fill a last k-tile that K ends inside), and N (row-major B) or M (A
+    // given transposed) a multiple of 8; the launcher falls back to the
+    // register-staged kernel otherwise.  Other operands are packed into
     // zero-padded copies for the direct kernel once the product is large
-    // enough for the two extra copy launches to pay.
-    const bool direct = aligned && K % 64 == 0 && (tb || N % 8 == 0) && (!ta || M % 8 == 0);
+    // enough for the extra copy launch to pay.
+    const bool direct = aligned && K % 8 == 0 && (tb || N % 8 == 0) && (!ta || M % 8 == 0);
+    const bool ktiles = K % 64 == 0;
     const double work = static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K);
+    const int pc = tiles(256, 256) >= 256 ? 11 : 12;  // packed copies, then config 14/10 or 7
+    // (copies' leading dimensions: K, M or N rounded up to 64, within the direct
+    // kernel's offset limits)
     const bool pack = work >= kPackMinWork && packed_k(K) < (int64_t(1) << 21) &&
-                      packed16_workspace_ok(g);
+                      packed_k(M > N ? M : N) < (int64_t(1) << 23) &&
+                      packed16_workspace_ok(g, pc);
     const bool whole256 = M % 256 == 0 && N % 256 == 0;
-    if (direct && tiles(256, 256) >= 256 && whole256)
+    if (direct && ktiles && tiles(256, 256) >= 256 && whole256)
         config = 14;  // direct 256x256x64, ping-pong wave groups (whole tiles only)
-    else if (direct && tiles(256, 256) >= 256)
+    else if (direct && ktiles && tiles(256, 256) >= 256)
         config = 10;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads
-    else if (direct && tiles(128, 256) >= 256 && M % 128 == 0 && N % 256 == 0)
+    else if (direct && ktiles && tiles(128, 256) >= 256 && M % 128 == 0 && N % 256 == 0)
         config = 15;  // direct 128x256x64, ping-pong wave groups (e.g. 1024x8192, 4096x2048)
     else if (direct && tiles(128, 256) >= 256)
         config = 13;  // direct 128x256x64, 8 waves of 64x64, 3 stages
@@ -181,7 +188,7 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
     else if (direct)
         config = 16;  // direct 64x64x64, 8 waves: four times the workgroups (e.g. 1024^3)
     else if (pack)
-        config = tiles(256, 256) >= 256 ? 11 : 12;  // packed copies, then config 14/10 or 7
+        config = pc;
     else if (tiles(128, 128) >= 256)
         config = 2;   // register-staged 128x128x64
     else
@@ -242,7 +249,7 @@ hipError_t launch(const GemmArgs& g, int variant, int config) {
 int64_t config_workspace_bytes(const GemmArgs& g, int variant, int config) {
     if (variant != MIGEMM_MFMA16 || (config != 11 && config != 12)) return 0;
     if (g.M == 0 || g.N == 0 || g.K == 0) return 0;
-    return packed16_workspace_bytes(g);
+    return packed16_workspace_bytes(g, config);
 }
 
 // key=value pairs, separated by ';', describing the call's kernels.

@@ -58,6 +58,11 @@ struct GemmArgs {
     void* ws = nullptr;
     int64_t ws_bytes = 0;
     LaunchInfo* query = nullptr;
+    // The operand is a copy made by the packed path: its contiguous side (k of a
+    // row-major A or of B given transposed, m or n of the others) is zero-filled
+    // up to a whole 16-byte chunk inside its leading dimension, so a kernel may
+    // read that last chunk whole.
+    bool pad_a = false, pad_b = false;
     // True unless the output step is the plain FP32 overwrite.
     bool general() const { return !(out.alpha == 1.0f && out.beta == 0.0f && out.c_dtype == 0); }
 };
@@ -192,22 +197,25 @@ hipError_t launch_lds_tiled(const GemmArgs& a, int config);
 hipError_t launch_regtile_valu(const GemmArgs& a, int config);
 hipError_t launch_regtile_mfma(const GemmArgs& a, int config);
 hipError_t launch_mfma16(const GemmArgs& a, int config);
-// Packs the operands the direct kernel cannot read in place into zero-padded
-// k-contiguous copies in the call's workspace and runs mfma16 configuration
-// inner_config on them; runs fallback_config in place when the call lent no
-// workspace of packed16_workspace_bytes(a) bytes (pack.hip).
-hipError_t launch_packed16(const GemmArgs& a, int inner_config, int fallback_config);
-// Workspace bytes the packed path needs for these arguments (0: both operands
-// are read in place), and K rounded up to the 64-k tile of the packed copies.
-int64_t packed16_workspace_bytes(const GemmArgs& a);
-// True when the call lent a workspace the packed path can use: non-null,
-// kWorkspaceAlign-aligned and at least packed16_workspace_bytes(a) long.
-bool packed16_workspace_ok(const GemmArgs& a);
+// Packed configuration pc (11 or 12 of mfma16): packs the operands the direct
+// kernel cannot read in place into zero-padded k-contiguous copies in the call's
+// workspace and runs the configuration's direct kernel on them; runs
+// fallback_config in place when the call lent no workspace of
+// packed16_workspace_bytes(a, pc) bytes (pack.hip).
+hipError_t launch_packed16(const GemmArgs& a, int pc, int fallback_config);
+// Workspace bytes packed configuration pc needs for these arguments (0: both
+// operands are read in place).
+int64_t packed16_workspace_bytes(const GemmArgs& a, int pc);
+// True when the call lent a workspace packed configuration pc can use:
+// non-null, kWorkspaceAlign-aligned and at least packed16_workspace_bytes long.
+bool packed16_workspace_ok(const GemmArgs& a, int pc);
+// K rounded up to 64: the largest k extent of a packed copy.
 int64_t packed_k(int64_t K);
 // Alignment the packed path asks of a workspace.
 constexpr int64_t kWorkspaceAlign = 256;
 hipError_t launch_mfma_i8(const GemmArgs& a, int config);
-// FP16/BF16 products with 1 <= M <= 16 and K a multiple of 32, K split over the
+// FP16/BF16 products with 1 <= M <= 16 (k-contiguous operands: K a multiple of
+// 8, or zero-filled copies), K split over the
 // waves of each workgroup (skinny16.hip); skinny16_fits says whether these and
 // its alignment needs hold (hipErrorInvalidValue from the launcher otherwise).
 bool skinny16_fits(const GemmArgs& a);

@@ -14,12 +14,15 @@
 //   swizzled double-buffered LDS;
 // * direct-staged (mfma16_direct.hpp): global->LDS without registers and
 //   transposing LDS reads for B; needs 16-byte aligned operands, leading
-//   dimensions in whole 16-byte chunks, K a multiple of the k-tile and N a
-//   multiple of 8.  A direct configuration asked to run where these do not hold
-//   runs the register-staged kernel with the nearest tile instead.
-// Configurations 11 and 12 (pack.hip) first copy A and B into zero-padded
-// k-contiguous images in a workspace the caller lends, so that the direct
-// kernel applies to any layout, alignment and K.
+//   dimensions in whole 16-byte chunks, K a multiple of 8 (configurations 7,
+//   13 and 16, which zero-fill a partial last k-tile) or of the 64-deep k-tile
+//   (the others), and N a multiple of 8.  A direct configuration asked to run
+//   where these do not hold runs the register-staged kernel with the nearest
+//   tile instead.
+// Configurations 11 and 12 (pack.hip) first copy the operands the direct
+// kernel cannot read in place (or reads slowly) into zero-padded k-contiguous
+// images in a workspace the caller lends, so that the direct kernel applies to
+// any layout, alignment and K.
 //
 // Every other configuration's kernels are compiled in mfma16_part.hip, one
 // object per (element type, output form, configuration).
@@ -40,7 +43,7 @@ const char* const kNames[] = {
     "direct 128x128x64 4w 16x16x32 s4",
     "direct 256x256x64 8w 32x32x16 gm4 ilv ntC",
     "direct 256x256x64 8w 16x16x32 gm4 ilv ntC agpr early",
-    "packed: zero-padded copies, then config 14 (whole tiles) or 10 as A x B^T",
+    "packed: zero-padded copies, then config 14 (whole tiles), 10 or 13 as A x B^T",
     "packed: zero-padded copies, then config 7 as A x B^T",
     "direct 128x256x64 8w 16x16x32 s3 ilv",
     "direct 256x256x64 8w 16x16x32 gm4 pingpong ntC agpr",
@@ -75,8 +78,7 @@ hipError_t launch_cfg16_any(const GemmArgs& g, int config) {
 hipError_t launch_mfma16(const GemmArgs& g, int config) {
     if (config == 11 || config == 12) {
         const int fallback = ceil_div(g.M, 128) * ceil_div(g.N, 128) >= 256 ? 2 : 3;
-        const bool whole256 = g.M % 256 == 0 && g.N % 256 == 0;
-        return launch_packed16(g, config == 11 ? (whole256 ? 14 : 10) : 7, fallback);
+        return launch_packed16(g, config, fallback);
     }
     // Configuration 7 (128x128 tiles): a last band of tile rows that takes the
     // tile count just past a whole number of rounds of workgroups on the 256

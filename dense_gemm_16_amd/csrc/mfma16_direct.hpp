@@ -70,13 +70,15 @@
 // of one row of A or column of B), so the matrix instructions do not change.
 //
 // Preconditions (checked by the launcher; other shapes use mfma_gemm.hpp):
-// A and B 16-byte aligned, lda and ldb in whole 16-byte chunks, K a multiple
-// of the k-tile, and the side of a k-row image (N for row-major B, M for A
-// given transposed) in whole chunks; the ping-pong schedule also needs M and N
-// to be multiples of the tile.  Rows of a row image past M or N, and chunks of
-// a k-row image past its side, are clamped to the last valid row / chunk, so
-// every load is in bounds; those lanes only feed outputs that are never
-// stored.
+// A and B 16-byte aligned, lda and ldb in whole 16-byte chunks, K in whole
+// chunks (a multiple of the k-tile without flag bit 5), and the side of a k-row
+// image (N for row-major B, M for A given transposed) in whole chunks; the
+// ping-pong schedule also needs M and N to be multiples of the tile.  Rows of a row image
+// past M or N, and chunks of a k-row image past its side, are clamped to the
+// last valid row / chunk, so every load is in bounds; those lanes only feed
+// outputs that are never stored.  A last k-tile that K ends inside is loaded
+// with its chunks (row image) or k-rows (k-row image) past K clamped the same
+// way, and those LDS slots are then overwritten with zeros.
 #pragma once
 
 #include "mfma_gemm.hpp"
@@ -97,7 +99,9 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // (see below); bit 3 = issue a k-tile's direct loads right after the barrier
 // that frees their stage instead of at the start of the next k-tile, so they
 // have a whole k-tile of matrix work to land; bit 4 = also compiled for
-// operands given transposed (without it those run the register-staged kernel).
+// operands given transposed (without it those run the register-staged kernel);
+// bit 5 = K need only be whole chunks: a last k-tile that K ends inside is
+// zero-filled in LDS past K (interleaved schedules).
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
           int BK_ = 64, int GM_ = 8, int SCHED_ = 0, int FLAGS_ = 0>
 struct DirectCfg {
@@ -128,7 +132,8 @@ struct DirectCfg {
     static_assert(SCHED == 0 || SCHED == 2 || SCHED == 4, "scheduling policy 0, 2 or 4");
     static_assert(SCHED != 4 || (WM == 2 && WN == 4 && STAGES == 2 && (FLAGS & 8) == 0),
                   "ping-pong: two groups of four waves, two stages, no early-load flag");
-    static_assert((FLAGS & ~30) == 0, "flags: bits 1 to 4");
+    static_assert((FLAGS & ~62) == 0, "flags: bits 1 to 5");
+    static_assert(SCHED != 4 || (FLAGS & 32) == 0, "ping-pong: whole k-tiles");
 };
 
 // One operand's LDS image (BX rows of M or N by BK of k, EB-byte elements).
@@ -215,6 +220,33 @@ __device__ __forceinline__ void direct_offsets(uint32_t (&voff)[O::PER], int wav
                                                int64_t x0, int64_t ext, int64_t ld) {
 #pragma unroll
     for (int q = 0; q < O::PER; ++q) voff[q] = direct_offset<O>(q, wave, lane, nw, x0, ext, ld);
+}
+
+// A last k-tile that K ends inside (K not a multiple of the k-tile, `tail` = K
+// mod BK elements).  Whether the chunk that lane fetches in its q-th load
+// starts below K: in a row image the lane's logical chunk of k (K is a whole
+// number of chunks, or the operand a copy zero-filled past K to a whole chunk),
+// in a k-row image its k-row.
+template <class O>
+__device__ __forceinline__ bool tail_valid(int q, int wave, int lane, int nw, int tail) {
+    const int r = O::RPI * (wave + q * nw) + lane / O::CH;
+    if constexpr (O::ROWS) return ((lane % O::CH) ^ swz_a<O::CH>(r)) * O::EPC < tail;
+    return r < tail;
+}
+// The lane's offset (voff, from direct_offset) for that last k-tile: a chunk
+// or k-row past K is replaced by the last one below K, so the load stays inside
+// the operand; its LDS slot is zeroed once the load has landed.
+template <class O>
+__device__ __forceinline__ uint32_t tail_offset(uint32_t voff, int q, int wave, int lane, int nw,
+                                                int tail, int64_t ld) {
+    const int r = O::RPI * (wave + q * nw) + lane / O::CH;
+    if constexpr (O::ROWS) {
+        // the chunk holding k = K - 1 (zero-filled past K in a padded copy)
+        const int chunk = (lane % O::CH) ^ swz_a<O::CH>(r), last = (tail - 1) / O::EPC;
+        return chunk > last ? voff - static_cast<uint32_t>((chunk - last) * 16) : voff;
+    } else {
+        return r >= tail ? voff - static_cast<uint32_t>((r - (tail - 1)) * ld * (16 / O::EPC)) : voff;
+    }
 }
 
 // A wave-uniform address, moved to scalar registers (the direct loads take
@@ -305,26 +337,86 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     const int64_t m0 = static_cast<int64_t>(pm) * BM;
     const int64_t n0 = static_cast<int64_t>(pn) * BN;
 
+    // A k-row image's side is read in whole chunks: M or N rounded up (a no-op
+    // unless the operand is a copy zero-filled to a whole chunk).
+    constexpr int EPC = 16 / Cfg::EB;
+    const int64_t ext_a = TA ? ceil_div(M, EPC) * EPC : M;
+    const int64_t ext_b = TB ? N : ceil_div(N, EPC) * EPC;
     uint32_t a_voff[OA::PER], b_voff[OB::PER];
-    direct_offsets<OA>(a_voff, wave, lane, NW, m0, M, lda);
-    direct_offsets<OB>(b_voff, wave, lane, NW, n0, N, ldb);
+    direct_offsets<OA>(a_voff, wave, lane, NW, m0, ext_a, lda);
+    direct_offsets<OB>(b_voff, wave, lane, NW, n0, ext_b, ldb);
     // tile origins and the step from one k-tile to the next, in elements
     const E* const a_tile = TA ? A + m0 : A + m0 * lda;
     const E* const b_tile = TB ? B + n0 * ldb : B + n0;
     const int64_t a_step = TA ? BK * lda : BK;
     const int64_t b_step = TB ? BK : BK * ldb;
 
-    // Issues this wave's NI direct loads of k-tile kt (A's, then B's) into its stage.
+    // With flag bit 5, K need not be a multiple of the k-tile: the last k-tile
+    // then holds `tail` of its BK k, and the rest of its LDS image is zeroed
+    // (zero_tail) before it is read, so those k add exact zero products.
+    // Without it tail is 0 and none of that code is compiled.
+    const int KT = static_cast<int>(ceil_div(K, BK));
+    const int tail = (Cfg::FLAGS & 32) ? static_cast<int>(K % BK) : 0;
+
+    // For the last k-tile when K ends inside it: how far each of this wave's
+    // per-lane load offsets moves back so that chunks or k-rows past K are
+    // replaced by the last one below K (0 otherwise, and for whole k-tiles).
+    // Held in registers and applied with a select, so the k loop has no branch
+    // for it.
+    uint32_t a_back[OA::PER], b_back[OB::PER];
+#pragma unroll
+    for (int q = 0; q < OA::PER; ++q)
+        a_back[q] = tail ? a_voff[q] - tail_offset<OA>(a_voff[q], q, wave, lane, NW, tail, lda) : 0u;
+#pragma unroll
+    for (int q = 0; q < OB::PER; ++q)
+        b_back[q] = tail ? b_voff[q] - tail_offset<OB>(b_voff[q], q, wave, lane, NW, tail, ldb) : 0u;
+
+    // Issues this wave's NI direct loads of k-tile kt (A's, then B's) into its
+    // stage; always NI loads, so the vmcnt accounting holds for the last k-tile too.
     auto issue = [&](int kt) __attribute__((always_inline)) {
         const int stage = kt % S;
         const uint32_t sa = lds_addr + stage * Cfg::STAGE_BYTES;
         const uint32_t sb = sa + Cfg::STAGE_A;
         const E* ab = a_tile + static_cast<int64_t>(kt) * a_step;
         const E* bb = b_tile + static_cast<int64_t>(kt) * b_step;
+        const bool last = kt == KT - 1;
 #pragma unroll
-        for (int q = 0; q < OA::PER; ++q) dma16(sa + (wave + q * NW) * 1024, ab, a_voff[q]);
+        for (int q = 0; q < OA::PER; ++q)
+            dma16(sa + (wave + q * NW) * 1024, ab, a_voff[q] - (last ? a_back[q] : 0u));
 #pragma unroll
-        for (int q = 0; q < OB::PER; ++q) dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q]);
+        for (int q = 0; q < OB::PER; ++q)
+            dma16(sb + (wave + q * NW) * 1024, bb, b_voff[q] - (last ? b_back[q] : 0u));
+    };
+    // Zeroes the LDS slots of the last k-tile that hold chunks or k-rows past K
+    // (each lane its own slots: a direct load puts lane l's 16 bytes at the
+    // load's LDS base + 16 l).  Called once that k-tile's loads have landed.
+    auto zero_tail = [&]() __attribute__((always_inline)) {
+        MIGEMM_LDS char* const st = (MIGEMM_LDS char*)smem + ((KT - 1) % S) * Cfg::STAGE_BYTES;
+#pragma unroll
+        for (int q = 0; q < OA::PER; ++q)
+            if (!tail_valid<OA>(q, wave, lane, NW, tail))
+                *(MIGEMM_LDS u32x4*)(st + (wave + q * NW) * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < OB::PER; ++q)
+            if (!tail_valid<OB>(q, wave, lane, NW, tail))
+                *(MIGEMM_LDS u32x4*)(st + Cfg::STAGE_A + (wave + q * NW) * 1024 + 16 * lane) =
+                    u32x4{0u, 0u, 0u, 0u};
+    };
+    // The wait and barrier before the last k-tile is read, with at most P direct
+    // loads left in flight.  Nothing is loaded after the last k-tile, so P is 0
+    // whenever that k-tile is partial; then every load has landed and its slots
+    // past K are zeroed before the barrier.
+    auto land_last = [&](auto pending) __attribute__((always_inline)) {
+        constexpr int P = decltype(pending)::value;
+        if constexpr (P == 0) {
+            if (tail != 0) {
+                vm_wait<0>();
+                zero_tail();
+                lds_wait_then_barrier();
+                return;
+            }
+        }
+        wait_then_barrier<P>();
     };
 
     Acc acc[TM][TN];
@@ -672,7 +764,6 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         }
     };
 
-    const int KT = static_cast<int>(K / BK);
     if constexpr (Cfg::SCHED == 4) {
         // Ping-pong.  Waves 0-3 (group X, the upper BM/2 rows of the tile) and
         // waves 4-7 (group Y, the lower rows) share the four SIMDs pairwise.
@@ -886,7 +977,9 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 #pragma unroll
     for (int t = 0; t < kPro; ++t)
         if (t < KT) issue(t);
-    if (KT >= kPro)
+    if (KT == 1)
+        land_last(std::integral_constant<int, 0>{});
+    else if (KT >= kPro)
         wait_then_barrier<(kPro - 1) * NI>();
     else
         wait_then_barrier<0>();
@@ -905,8 +998,11 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     // Every k-tile but the last ends with the barrier that makes k-tile kt+1
     // visible, then runs its last slab while slab 0 of kt+1 is read.  The last
     // k-tile is peeled off so that the code after the barrier has one
-    // predecessor and the compiler's wait counts stay exact there.
-    for (int kt = 0; kt + 1 < KT; ++kt) {
+    // predecessor and the compiler's wait counts stay exact there.  With flag
+    // bit 5 so is the step into it (LAST), whose wait also zero-fills a partial
+    // last k-tile, so the loop itself has no branch for that.
+    auto kstep = [&](int kt, auto last_tag) __attribute__((always_inline)) {
+        constexpr bool LAST = decltype(last_tag)::value;
         const bool more = kt + S - 1 < KT;
         if (!early && more) issue(kt + S - 1);
         // sched_barrier(0) fences keep each slab's prefetch ahead of the
@@ -915,15 +1011,30 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         front_slabs(kt);
         // k-tile kt+1 must have landed; later ones (k-tiles up to kt+S-1) may
         // still be in flight.
-        if (more)
-            wait_then_barrier<(S - 2) * NI>();
-        else
-            wait_then_barrier<0>();
+        if constexpr (LAST) {
+            if (more)
+                land_last(std::integral_constant<int, (S - 2) * NI>{});
+            else
+                land_last(std::integral_constant<int, 0>{});
+        } else {
+            if (more)
+                wait_then_barrier<(S - 2) * NI>();
+            else
+                wait_then_barrier<0>();
+        }
         // Every read of k-tile kt's stage was issued before the barrier (the
         // last slab's fragments are already in registers) and has completed, in
         // every wave: the stage can take k-tile kt+S.
         if (early && kt + S < KT) issue(kt + S);
         slab_step(true, kt + 1, 0, F[0], F[1]);
+    };
+    if constexpr ((Cfg::FLAGS & 32) != 0) {
+        for (int kt = 0; kt + 2 < KT; ++kt) kstep(kt, std::false_type{});
+        if (KT >= 2) kstep(KT - 2, std::true_type{});
+    } else {
+        // whole k-tiles: no step needs the zero fill, and one loop keeps the
+        // code (and the registers live across it) as small as it can be
+        for (int kt = 0; kt + 1 < KT; ++kt) kstep(kt, std::false_type{});
     }
     if (KT > 0) {
         front_slabs(KT - 1);
@@ -935,27 +1046,34 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 }
 
 // True when the direct kernel's preconditions hold for these arguments: aligned
-// operands in whole 16-byte chunks per row (epc elements per chunk: 8 for 16-bit
-// inputs, 16 for 8-bit ones), K a multiple of the k-tile (bk), the side of a
-// k-row image (N for row-major B, M for A given transposed) in whole chunks, and
-// per-lane offsets (BX <= 256 rows of a row image, up to 128 k-rows of a k-row
-// image) that fit 31 bits.  `layouts`: the configuration is compiled for operands
-// given transposed.
-inline bool direct_ok(const GemmArgs& g, int bk, bool layouts, int epc = 8) {
+// operands with leading dimensions in whole 16-byte chunks (epc elements per
+// chunk: 4 for 32-bit inputs, 8 for 16-bit ones, 16 for 8-bit ones), each
+// operand's contiguous side (K for a row image, N for row-major B, M for A given
+// transposed) in whole chunks unless the operand is a zero-filled copy (pad_a,
+// pad_b), K a multiple of kq (the k-tile, for configurations without the
+// partial last k-tile; kq = epc for those with it), and per-lane offsets
+// (BX <= 256 rows of a row image, up to 128 k-rows of a k-row image) that fit
+// 31 bits.  `layouts`: the configuration is compiled for operands given
+// transposed.
+inline bool direct_ok(const GemmArgs& g, int kq, bool layouts, int epc = 8) {
     if ((g.ta || g.tb) && !layouts) return false;
     const int64_t row_ld = int64_t(1) << 21, krow_ld = int64_t(1) << 23;
+    // a padded copy's contiguous side may end inside a chunk (zero-filled)
+    const bool a_whole = g.pad_a || (g.ta ? g.M : g.K) % epc == 0;
+    const bool b_whole = g.pad_b || (g.tb ? g.K : g.N) % epc == 0;
+    const bool k_ok = kq == epc || g.K % kq == 0;
     return aligned16(g.A) && aligned16(g.B) && g.lda % epc == 0 && g.ldb % epc == 0 &&
-           g.K % bk == 0 && g.K > 0 && g.M > 0 && g.N > 0 &&
-           (g.ta ? (g.M % epc == 0 && g.lda < krow_ld) : g.lda < row_ld) &&
-           (g.tb ? g.ldb < row_ld : (g.N % epc == 0 && g.ldb < krow_ld));
+           k_ok && a_whole && b_whole && g.K > 0 && g.M > 0 && g.N > 0 &&
+           (g.ta ? g.lda < krow_ld : g.lda < row_ld) && (g.tb ? g.ldb < row_ld : g.ldb < krow_ld);
 }
 
-// direct_ok for configuration D.  The ping-pong schedule also needs whole
-// tiles: its successive loads of a row image step whole image rows from the
-// first one, with no clamp at the matrix edge.
+// direct_ok for configuration D: K a whole number of chunks with flag bit 5,
+// of k-tiles without.  The ping-pong schedule also needs whole tiles: its
+// successive loads of a row image step whole image rows from the first one,
+// with no clamp at the matrix edge.
 template <class D>
 bool direct_fits(const GemmArgs& g) {
-    return direct_ok(g, D::BK, D::LAYOUTS, 16 / D::EB) &&
+    return direct_ok(g, (D::FLAGS & 32) ? 16 / D::EB : D::BK, D::LAYOUTS, 16 / D::EB) &&
            (D::SCHED != 4 || (g.M % D::BM == 0 && g.N % D::BN == 0));
 }
 

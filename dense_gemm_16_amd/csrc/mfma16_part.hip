@@ -22,16 +22,16 @@ template <typename E> struct Cfgs {
     // direct-staged: <E, BM, BN, WM, WN, MF, STAGES, BK, GM, SCHED, FLAGS>
     using D5 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64>;
     using D6 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64>;
-    using D7 = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 18>;   // 8 waves, interleave, gm4, nt C; all layouts
-    using D7P = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 16>;  // D7 with plain C stores
+    using D7 = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 50>;   // 8 waves, interleave, gm4, nt C; all layouts; ragged K
+    using D7P = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 48>;  // D7 with plain C stores
     using D8 = DirectCfg<E, 128, 128, 2, 2, 16, 4, 64>;             // 4 waves, 4 stages
     using D9 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 2>;    // gm4, interleave, nt C
     using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 30>;  // + AGPRs, early loads; all layouts
-    using D13 = DirectCfg<E, 128, 256, 2, 4, 16, 3, 64, 8, 2, 16>;  // 8 waves of 64x64, 3 stages; all layouts
+    using D13 = DirectCfg<E, 128, 256, 2, 4, 16, 3, 64, 8, 2, 48>;  // 8 waves of 64x64, 3 stages; all layouts; ragged K
     using D14 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 22>;  // ping-pong (whole tiles), AGPRs, nt C; all layouts
     using D15 = DirectCfg<E, 128, 256, 2, 4, 16, 2, 64, 8, 4, 22>;  // ping-pong 128x256 (whole tiles); all layouts
-    using D16 = DirectCfg<E, 64, 64, 2, 4, 16, 4, 64, 8, 0, 26>;    // 8 waves of 32x16, 4 stages, early loads, nt C; all layouts
-    using D16P = DirectCfg<E, 64, 64, 2, 4, 16, 4, 64, 8, 0, 24>;   // D16 with plain C stores
+    using D16 = DirectCfg<E, 64, 64, 2, 4, 16, 4, 64, 8, 0, 58>;    // 8 waves of 32x16, 4 stages, early loads, nt C; all layouts; ragged K
+    using D16P = DirectCfg<E, 64, 64, 2, 4, 16, 4, 64, 8, 0, 56>;   // D16 with plain C stores
 };
 
 // The direct-staged configuration D where its preconditions hold, else the

@@ -1,18 +1,21 @@
 // pack.hip -- FP16/BF16 products whose operands the direct-staged kernel cannot
-// read in place: rows not in whole 16-byte chunks (an odd leading dimension, a
-// pointer off a 16-byte boundary), K not a multiple of the 64-k tile, or a
-// k-row image side (N of row-major B, M of A given transposed) not a multiple
-// of 8.
+// read in place, or reads slowly: a pointer off a 16-byte boundary, a leading
+// dimension that is not a whole number of 16-byte chunks, a contiguous side (K
+// of a row-major A or of B given transposed, N of row-major B, M of A given
+// transposed) that ends inside a chunk, or k-contiguous rows that do not start
+// on 128-byte lines (each 128-byte k-tile row would then span two lines).
 //
 // The product C = A x B (page "CUDA-Practice 09", the definition of the
-// row-major product) is unchanged by padding the k sum with zeros: each extra
-// term is an exact zero product.  So each operand the direct kernel cannot read
-// in place is first copied into a workspace as a k-contiguous row image, A'
-// (M x K') or B' (N x K', that is B transposed), with K' = K rounded up to 64
-// and zero fill for k >= K; when K is not a multiple of 64 that is both.  The
-// direct kernel then multiplies the copies (and any operand left in place); it
-// clamps ragged M and N rows itself, and the output step writes C exactly as
-// for the unpacked call.
+// row-major product) does not depend on where the operands sit in memory, and
+// padding the k sum with zeros adds nothing to it: each extra term is an exact
+// zero product.  So each such operand is first copied into a workspace as a
+// k-contiguous row image, A' (M x K) or B' (N x K, that is B transposed), rows
+// starting on 128-byte lines (leading dimension K rounded up to 64) and
+// zero-filled from K to the end of the row.  The direct kernel then multiplies the
+// copies and any operand left in place with the call's own M, N and K: it
+// clamps ragged M and N rows, zero-fills a partial last k-tile, and reads a
+// copy's last chunk whole; the output step writes C exactly as for the
+// unpacked call.
 //
 // The copy is memory-bound: 2 bytes read and 2 written per element copied,
 // small beside the product for the shapes this path is selected for.  One
@@ -21,13 +24,13 @@
 // aligned) goes through LDS, so that the reads (2 bytes per lane, any
 // alignment) and the writes (16 bytes per lane) are contiguous across a
 // wavefront in either orientation; one that keeps its orientation and has
-// aligned rows (A with only K to pad, say) is copied 16 bytes at a time.
+// aligned rows is copied 16 bytes at a time.
 //
-// Workspace: (M + N) * K' * 2 bytes at most (each copied operand, A' first,
-// rounded up to 256 bytes), lent by the caller for this one call and
-// 256-byte aligned; the library allocates nothing and keeps no pointer to it.
-// Without a large enough workspace the product runs on the register-staged
-// kernel instead, which reads any layout in place.
+// Workspace: each copied operand's rows x leading dimension x 2 bytes, A' first
+// (rounded up to 256 bytes), lent by the caller for this one call and 256-byte
+// aligned; the library allocates nothing and keeps no pointer to it.  Without a
+// large enough workspace the product runs on the register-staged kernel
+// instead, which reads any layout in place.
 
 #include "common.hpp"
 
@@ -36,8 +39,8 @@ namespace {
 
 constexpr int kTile = 64;
 
-// One operand copy: dst (rows x cols_out, leading dimension ldd, 16-byte
-// aligned rows) from src,
+// One operand copy: dst (rows x cols_out, leading dimension ldd, rows on
+// 128-byte lines) from src,
 //   dst[r][c] = src(r, c) for c < cols, 0 for cols <= c < cols_out,
 //   src(r, c) = trans ? src[c * lds + r] : src[r * lds + c].
 struct PackJob {
@@ -128,8 +131,12 @@ __global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
     }
 }
 
-PackJob make_job(const void* src, int64_t lds, int64_t rows, int64_t cols, bool trans, void* dst,
-                 int64_t ldd, int64_t cols_out) {
+int64_t round_up(int64_t x, int64_t m) { return ceil_div(x, m) * m; }
+
+// Rows of dst start on 128-byte lines and are written whole (zero-filled from
+// cols to the leading dimension), so every line of the copy is written in full.
+PackJob make_job(const void* src, int64_t lds, int64_t rows, int64_t cols, bool trans, void* dst) {
+    const int64_t ldd = round_up(cols, 64), cols_out = ldd;
     PackJob j;
     j.src = static_cast<const uint16_t*>(src);
     j.lds = lds;
@@ -152,23 +159,49 @@ hipError_t launch_pack16(const GemmArgs& g, const PackJob& j0, const PackJob& j1
     return launch_kernel(g, pack16_kernel, dim3(grid), dim3(256), j0, j1);
 }
 
-// Which operands the direct kernel reads in place: a 16-byte aligned row
-// image (row-major A, B given transposed) or k-row image (A given transposed,
-// row-major B) with rows in whole 16-byte chunks, a k-row image side a
-// multiple of 8, and K a multiple of 64.
-struct PackPlan {
-    int64_t Kp, a_bytes, b_bytes;
-    bool a_in_place, b_in_place;
+// The direct configuration that packed configuration pc (11 or 12) runs.  11:
+// the 256x256 ping-pong kernel on whole tiles and whole k-tiles (configuration
+// 14), the 256x256 interleaved one (10) on other shapes with whole k-tiles, and
+// the 128x256 one (13, which zero-fills a partial last k-tile) when K is not a
+// multiple of 64.  12: the 128x128 one (7, with the partial k-tile too).
+int inner_config(const GemmArgs& g, int pc) {
+    if (pc == 12) return 7;
+    if (g.K % 64 != 0) return 13;
+    return (g.M % 256 == 0 && g.N % 256 == 0) ? 14 : 10;
+}
+
+// One operand's plan.  A row image (row-major A, B given transposed) is read in
+// place when 16-byte aligned, K is whole chunks and its rows start on 128-byte
+// lines; otherwise it is copied as it is.  A k-row image (A given transposed,
+// row-major B) is read in place when 16-byte aligned with its side (M or N) in
+// whole chunks; otherwise it is transposed into a row image.
+struct Operand {
+    bool in_place, trans;
+    int64_t rows, bytes;  // rows: M or N
 };
 
-PackPlan plan_pack(const GemmArgs& g) {
+Operand plan_operand(const void* p, int64_t ld, int64_t rows, int64_t K, bool row_image) {
+    Operand o;
+    o.rows = rows;
+    o.trans = !row_image;
+    o.in_place = aligned16(p) && ld % 8 == 0 &&
+                 (row_image ? (K % 8 == 0 && (ld * 2) % 128 == 0) : rows % 8 == 0);
+    o.bytes = o.in_place ? 0 : rows * round_up(K, 64) * 2;
+    return o;
+}
+
+struct PackPlan {
+    int inner;
+    Operand a, b;
+    int64_t a_bytes;  // A' rounded up to the workspace alignment (B' follows it)
+};
+
+PackPlan plan_pack(const GemmArgs& g, int pc) {
     PackPlan p;
-    p.Kp = packed_k(g.K);
-    const bool k_ok = g.K == p.Kp;
-    p.a_in_place = k_ok && aligned16(g.A) && g.lda % 8 == 0 && (!g.ta || g.M % 8 == 0);
-    p.b_in_place = k_ok && aligned16(g.B) && g.ldb % 8 == 0 && (g.tb || g.N % 8 == 0);
-    p.a_bytes = p.a_in_place ? 0 : ceil_div(g.M * p.Kp * 2, kWorkspaceAlign) * kWorkspaceAlign;
-    p.b_bytes = p.b_in_place ? 0 : g.N * p.Kp * 2;
+    p.inner = inner_config(g, pc);
+    p.a = plan_operand(g.A, g.lda, g.M, g.K, !g.ta);
+    p.b = plan_operand(g.B, g.ldb, g.N, g.K, g.tb);
+    p.a_bytes = round_up(p.a.bytes, kWorkspaceAlign);
     return p;
 }
 
@@ -176,43 +209,43 @@ PackPlan plan_pack(const GemmArgs& g) {
 
 int64_t packed_k(int64_t K) { return ceil_div(K, 64) * 64; }
 
-int64_t packed16_workspace_bytes(const GemmArgs& g) {
-    const PackPlan p = plan_pack(g);
-    return p.a_bytes + p.b_bytes;
+int64_t packed16_workspace_bytes(const GemmArgs& g, int pc) {
+    const PackPlan p = plan_pack(g, pc);
+    return p.b.bytes ? p.a_bytes + p.b.bytes : p.a.bytes;
 }
 
-bool packed16_workspace_ok(const GemmArgs& g) {
+bool packed16_workspace_ok(const GemmArgs& g, int pc) {
     return g.ws != nullptr && (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) == 0 &&
-           g.ws_bytes >= packed16_workspace_bytes(g);
+           g.ws_bytes >= packed16_workspace_bytes(g, pc);
 }
 
-hipError_t launch_packed16(const GemmArgs& g, int inner_config, int fallback_config) {
-    const PackPlan pl = plan_pack(g);
-    const int64_t Kp = pl.Kp;
-    if (pl.a_bytes + pl.b_bytes == 0) return launch_mfma16(g, inner_config);
-    if (!packed16_workspace_ok(g)) return launch_mfma16(g, fallback_config);
+hipError_t launch_packed16(const GemmArgs& g, int pc, int fallback_config) {
+    const PackPlan pl = plan_pack(g, pc);
+    if (pl.a.in_place && pl.b.in_place) return launch_mfma16(g, pl.inner);
+    if (!packed16_workspace_ok(g, pc)) return launch_mfma16(g, fallback_config);
     char* const wa = static_cast<char*>(g.ws);
     char* const wb = wa + pl.a_bytes;
-    // A' (M x K'): row-major A is copied, A given transposed (K x M) is transposed.
-    // B' (N x K'): row-major B (K x N) is transposed, B given transposed is copied.
-    const PackJob none = make_job(nullptr, 1, 0, 0, false, nullptr, 8, 8);
-    const PackJob ja = pl.a_in_place ? none : make_job(g.A, g.lda, g.M, g.K, g.ta, wa, Kp, Kp);
-    const PackJob jb = pl.b_in_place ? none : make_job(g.B, g.ldb, g.N, g.K, !g.tb, wb, Kp, Kp);
+    // A' (M x K): row-major A is copied, A given transposed (K x M) is transposed.
+    // B' (N x K): row-major B (K x N) is transposed, B given transposed is copied.
+    const PackJob none = make_job(nullptr, 8, 0, 0, false, nullptr);
+    const PackJob ja = pl.a.in_place ? none : make_job(g.A, g.lda, g.M, g.K, g.ta, wa);
+    const PackJob jb = pl.b.in_place ? none : make_job(g.B, g.ldb, g.N, g.K, !g.tb, wb);
     hipError_t e = launch_pack16(g, ja, jb);
     if (e != hipSuccess) return e;
     GemmArgs p = g;
-    p.K = Kp;
-    if (!pl.a_in_place) {
+    if (!pl.a.in_place) {
         p.ta = false;
         p.A = wa;
-        p.lda = Kp;
+        p.lda = ja.ldd;
+        p.pad_a = true;
     }
-    if (!pl.b_in_place) {
+    if (!pl.b.in_place) {
         p.tb = true;
         p.B = wb;
-        p.ldb = Kp;
+        p.ldb = jb.ldd;
+        p.pad_b = true;
     }
-    return launch_mfma16(p, inner_config);
+    return launch_mfma16(p, pl.inner);
 }
 
 }  // namespace migemm

@@ -16,16 +16,17 @@ using F5 = MfmaCfg<float, 64, 64, 2, 4, 16>;    // 8 waves of 32x16: two waves p
 using F6 = MfmaCfg<float, 128, 128, 2, 4, 16>;  // 8 waves of 64x32
 using F7 = MfmaCfg<float, 64, 32, 2, 2, 16>;    // 4 waves of 32x16, twice F2's workgroups
 // direct-staged (global -> LDS without registers, mfma16_direct.hpp with 32-bit
-// elements): <E, BM, BN, WM, WN, MF, STAGES, BK, GM, SCHED, FLAGS>; FLAGS 16: all
-// operand layouts, | 2: non-temporal C stores (chosen when C rows are whole lines)
-using D8 = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 18>;     // 8 waves of 32x16
-using D8P = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 16>;
-using D9 = DirectCfg<float, 64, 64, 2, 2, 16, 4, 32, 8, 2, 18>;     // 4 waves of 32x32
-using D9P = DirectCfg<float, 64, 64, 2, 2, 16, 4, 32, 8, 2, 16>;
-using D10 = DirectCfg<float, 128, 128, 2, 4, 16, 4, 32, 4, 2, 18>;  // 8 waves of 64x32
-using D10P = DirectCfg<float, 128, 128, 2, 4, 16, 4, 32, 4, 2, 16>;
-using D11 = DirectCfg<float, 128, 64, 2, 4, 16, 4, 32, 8, 2, 18>;   // 8 waves of 64x16
-using D11P = DirectCfg<float, 128, 64, 2, 4, 16, 4, 32, 8, 2, 16>;
+// elements): <E, BM, BN, WM, WN, MF, STAGES, BK, GM, SCHED, FLAGS>; FLAGS 48: all
+// operand layouts and K in whole 4-element chunks (a partial last k-tile is
+// zero-filled), | 2: non-temporal C stores (chosen when C rows are whole lines)
+using D8 = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 50>;     // 8 waves of 32x16
+using D8P = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 48>;
+using D9 = DirectCfg<float, 64, 64, 2, 2, 16, 4, 32, 8, 2, 50>;     // 4 waves of 32x32
+using D9P = DirectCfg<float, 64, 64, 2, 2, 16, 4, 32, 8, 2, 48>;
+using D10 = DirectCfg<float, 128, 128, 2, 4, 16, 4, 32, 4, 2, 50>;  // 8 waves of 64x32
+using D10P = DirectCfg<float, 128, 128, 2, 4, 16, 4, 32, 4, 2, 48>;
+using D11 = DirectCfg<float, 128, 64, 2, 4, 16, 4, 32, 8, 2, 50>;   // 8 waves of 64x16
+using D11P = DirectCfg<float, 128, 64, 2, 4, 16, 4, 32, 8, 2, 48>;
 
 // Rows of C that start whole 128-byte lines take non-temporal stores.
 inline bool c_whole_lines(const Epi& o) {

@@ -31,13 +31,14 @@
  * must not overlap A or B.
  *
  * Memory.  The library allocates no device memory.  FP16/BF16 operands that
- * the direct-staged kernel cannot read in place (K not a multiple of 64, rows
- * not 16-byte aligned in whole 16-byte chunks, a k-row image side not a
- * multiple of 8) are, for large products, best first copied into zero-padded
- * k-contiguous images; that path needs device scratch memory, which the caller
- * lends to migemm_gemm_ws (its size from migemm_workspace_size).  The other
- * entry points lend none, and such products then run in place on the
- * register-staged kernel: same result rules, lower speed.
+ * the direct-staged kernel cannot read in place (rows not 16-byte aligned in
+ * whole 16-byte chunks, K or a k-row image side not a multiple of 8) or reads
+ * slowly (k-contiguous rows that do not start on 128-byte lines) are, for
+ * large products, best first copied into zero-padded k-contiguous images;
+ * that path needs device scratch memory, which the caller lends to
+ * migemm_gemm_ws (its size from migemm_workspace_size).  The other entry
+ * points lend none, and such products then run in place: same result rules,
+ * lower speed.
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Work is enqueued asynchronously on it; no entry point waits on the

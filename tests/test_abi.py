@@ -244,15 +244,20 @@ def _selected(M, N, K, dt, lda, ldb, ws_bytes, op_a=0, op_b=0):
 
 
 def test_selection_packs_unreadable_16bit_operands():
-    """FP16/BF16 operands the direct kernel cannot read in place (K not a
-    multiple of 64, an odd leading dimension) go to the packed configurations
+    """FP16/BF16 operands the direct kernel cannot read in place (an odd
+    leading dimension, K not a multiple of 8) go to the packed configurations
     once the product is large enough and a large enough workspace is lent;
     without one, or when small, they stay on the register-staged kernel, and
-    aligned ones on the direct kernel."""
+    aligned ones on the direct kernel (K a multiple of 8 is enough for the
+    configurations that zero-fill a partial last k-tile)."""
     sel = lambda M, N, K, dt, lda, ldb: mg.migemm_select(M, N, K, dt, None, lda, None, ldb, None, N)
     big = 1 << 40
     assert _selected(2050, 2047, 2056, 1, 2056, 2047, big) == ("mfma16", 12)
-    assert _selected(8192, 8192, 8200, 2, 8200, 8192, big) == ("mfma16", 11)
+    # aligned with K = 8200: the 128x256 direct kernel reads it in place; with an
+    # odd ldb the copies are padded to K' = 8256 for the 256x256 ping-pong kernel
+    assert _selected(8192, 8192, 8200, 2, 8200, 8192, big) == ("mfma16", 13)
+    assert _selected(8192, 8192, 8200, 2, 8200, 8193, big) == ("mfma16", 11)
+    assert _selected(2048, 2048, 2056, 2, 2056, 2048, big) == ("mfma16", 7)
     assert _selected(4096, 4096, 4096, 2, 4096, 4097, big) == ("mfma16", 11)
     # no workspace (migemm_gemm, migemm_select) or too little: register-staged
     assert sel(2050, 2047, 2056, 1, 2056, 2047) == (mg.OK, mg.MFMA16, 2)
@@ -283,10 +288,12 @@ def test_fp32_selection():
     # direct-staged FP32: 64x64 tiles below a round of 128x128 tiles, 128x128 above
     assert sel(1024, 1024, 1024, 1024, 1024) == (mg.OK, mg.REGTILE_MFMA, 8)
     assert sel(4096, 4096, 4096, 4096, 4096) == (mg.OK, mg.REGTILE_MFMA, 10)
-    # rows not in whole 16-byte chunks, K not a multiple of 32, N not a multiple of 4:
+    # K a multiple of 4 (not of the 32-deep k-tile): still direct
+    assert sel(1024, 1024, 1000, 1000, 1024) == (mg.OK, mg.REGTILE_MFMA, 8)
+    # rows not in whole 16-byte chunks, K not a multiple of 4, N not a multiple of 4:
     # register-staged
     assert sel(1024, 1024, 1024, 1025, 1024) == (mg.OK, mg.REGTILE_MFMA, 2)
-    assert sel(1024, 1024, 1000, 1000, 1024) == (mg.OK, mg.REGTILE_MFMA, 2)
+    assert sel(1024, 1024, 1001, 1004, 1024) == (mg.OK, mg.REGTILE_MFMA, 2)
     assert sel(4096, 4094, 4096, 4096, 4094) == (mg.OK, mg.REGTILE_MFMA, 0)
     for c in (8, 9, 10, 11):
         assert mg.migemm_config_name(mg.REGTILE_MFMA, c).startswith("direct")
@@ -294,9 +301,19 @@ def test_fp32_selection():
 
 def test_workspace_size():
     ws = lambda *a: mg.migemm_workspace_size(*a)
-    # 2050 x 2047 x 2056 FP16, ldb = 2047: both operands packed with K' = 2112,
-    # A' (2050 x 2112, rounded to 256 bytes) then B' (2047 x 2112)
-    assert ws(-1, -1, 0, 0, 2050, 2047, 2056, 1, None, 2056, None, 2047) == (mg.OK, 17305728)
+    # 2050 x 2047 x 2056 FP16, ldb = 2047: both copied as k-contiguous images with
+    # rows on 128-byte lines (leading dimension 2112): A' (2050 x 2112, A's rows of
+    # 4112 bytes straddle lines; rounded up to 256 bytes) then B' (2047 x 2112)
+    c3r = (2050 * 2112 * 2 + 255) // 256 * 256 + 2047 * 2112 * 2
+    assert c3r == 17305728
+    assert ws(-1, -1, 0, 0, 2050, 2047, 2056, 1, None, 2056, None, 2047) == (mg.OK, c3r)
+    # K = 2052 (not a multiple of 8) and operands given transposed (A stored K x M
+    # with an odd leading dimension, B stored N x K): the same copies
+    assert ws(-1, -1, 0, 0, 2050, 2047, 2052, 1, None, 2052, None, 2047) == (mg.OK, c3r)
+    assert ws(-1, -1, 1, 1, 2050, 2047, 2052, 1, None, 2051, None, 2052) == (mg.OK, c3r)
+    # A on 128-byte lines (lda 2112), B's rows aligned but N = 2047: only B copied
+    assert ws(-1, -1, 0, 0, 2050, 2047, 2056, 1, None, 2112, None, 2048) == \
+        (mg.OK, 2047 * 2112 * 2)
     # K a multiple of 64 and A aligned: only B is copied
     assert ws(-1, -1, 0, 0, 4096, 4096, 4096, 2, None, 4096, None, 4097) == (mg.OK, 4096 * 4096 * 2)
     # aligned, FP32, INT8, small, empty: none
@@ -306,8 +323,9 @@ def test_workspace_size():
         M, N, K, dt, lda, ldb = a
         assert ws(-1, -1, 0, 0, M, N, K, dt, None, lda, None, ldb) == (mg.OK, 0), a
     # a forced packed configuration reports its copies; any other forced one none
-    assert ws(mg.MFMA16, 12, 0, 0, 512, 512, 200, 1, None, 200, None, 512)[1] == \
-        512 * 256 * 2 * 2
+    assert ws(mg.MFMA16, 12, 0, 0, 512, 512, 100, 1, None, 100, None, 512)[1] == 512 * 128 * 2
+    assert ws(mg.MFMA16, 12, 0, 0, 512, 512, 200, 1, None, 200, None, 512)[1] == 512 * 256 * 2
+    assert ws(mg.MFMA16, 12, 0, 0, 512, 512, 192, 1, None, 192, None, 512)[1] == 0
     assert ws(mg.MFMA16, 2, 0, 0, 2050, 2047, 2056, 1, None, 2056, None, 2047) == (mg.OK, 0)
     # argument errors as for the product
     assert ws(-1, -1, 0, 0, -1, 4, 4, 1, None, 4, None, 4)[0] == mg.ERR_INVALID_ARG
@@ -325,14 +343,22 @@ def test_describe():
     assert d["grid0"] == 1024 and d["block0"] == 512
     # on a machine with a GPU the kernel's attributes follow; without one, a note
     assert "regs0" in d or "resources0" in d
-    # the ragged product with a workspace: the copy, then 256 tiles of 128 x 128
-    # over rows 0..2047, then the last 2 rows on 128 workgroups of 16 columns
+    # the ragged product with a workspace: the copies (33 x 33 tiles of 64 x 64 for
+    # A', 32 x 33 for B'), then 256 tiles of 128 x 128 over rows 0..2047, then the
+    # last 2 rows on 128 workgroups of 16 columns
     st, text = mg.migemm_describe_ex(-1, -1, 0, 0, 2050, 2047, 2056, mg.F16, None, 2056, None,
                                      2047, mg.F32, 2047, 1 << 30)
     d = mg._parse_description(text)
     assert st == mg.OK and d["config"] == 12 and d["workspace_bytes"] == 17305728
-    assert d["launches"] == 3 and d["grid1"] == 256 and d["grid2"] == 128
+    assert d["launches"] == 3 and d["grid0"] == 33 * 33 + 32 * 33 and d["grid1"] == 256
+    assert d["grid2"] == 128 and d["block2"] == 1024
     assert d["workspace_lent"] == 1 << 30
+    # K a multiple of 8 but not of 64: configuration 7 runs its own direct kernel
+    # (8 waves); K not a multiple of 8: the register-staged 128x128 one (4 waves)
+    d = mg.describe(mg.MFMA16, 7, 0, 0, 300, 264, 72, mg.BF16, None, 72, None, 264, 0, 264, 0)
+    assert d["launches"] == 1 and d["grid0"] == 9 and d["block0"] == 512
+    d = mg.describe(mg.MFMA16, 7, 0, 0, 300, 264, 68, mg.BF16, None, 72, None, 264, 0, 264, 0)
+    assert d["launches"] == 1 and d["grid0"] == 9 and d["block0"] == 256
     # FP32 and INT8
     d = mg._parse_description(mg.migemm_describe(1024, 1024, 1024, mg.F32, 1024, 1024, 1024)[1])
     assert d["variant"] == "regtile_mfma" and d["launches"] == 1

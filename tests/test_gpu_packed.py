@@ -240,7 +240,12 @@ def test_split_tail_on_the_skinny_kernel():
              (2056, 2040, 128, True, False, 0, 7),
              (2049, 2048, 128, False, False, 2, 7),
              (2051, 2047, 100, False, False, 0, 12),
-             (2053, 2048, 96, True, True, 1, 12)]
+             (2053, 2048, 96, True, True, 1, 12),
+             # K a multiple of 8 but not of 32: partial last k-tile (direct) and
+             # partial last k-step (skinny); sixteen-wave skinny (B given transposed)
+             (2050, 2048, 136, False, False, 0, 7),
+             (2050, 2048, 2056, False, True, 0, 7),
+             (2050, 2047, 2056, False, False, 0, 12)]
     for (M, N, K, ta, tb, c_code, cfg) in cases:
         A, B = inputs.pair(M, N, K, dtype, "normal", seed=M + 3 * N + K + ta + 2 * tb)
         ref = oracle_ref(A, B, dtype)

@@ -128,10 +128,13 @@ def test_degenerate_shapes(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_k_trip_counts(dtype):
-    # 1..5 k-tiles plus a tail: exercises the double-buffer hand-off
+    # 1..5 k-tiles plus a tail: exercises the double-buffer hand-off; tails of
+    # whole 16-byte chunks take the direct kernel's zero-filled last k-tile,
+    # others the register-staged kernel
     bk = 32 if dtype == "f32" else 64
+    chunk = 4 if dtype == "f32" else 8
     for kt in range(1, 6):
-        for tail in (0, 1, bk - 1):
+        for tail in (0, 1, chunk, bk - chunk, bk - 1):
             K = kt * bk + tail
             A, B = inputs.pair(256, 256, K, dtype, "int", seed=K)
             say(f"k_trips {dtype} K={K}")
@@ -170,3 +173,63 @@ def test_direct_staging_edges(dtype):
             from gpu_helpers import oracle_ref
             ref = ref or oracle_ref(A, B, dtype)
             check(C, A, B, dtype, ref=ref)
+
+
+RAGGED_K_SHAPES = [(300, 264, 72, None, None), (1000, 520, 200, None, None),
+                   (256, 256, 8, None, None), (37, 8, 1096, None, None),
+                   (513, 776, 136, 144, 784), (129, 128, 1000, None, None),
+                   (2048, 64, 2056, None, None)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_direct_ragged_k(dtype):
+    """Direct-staged configurations that zero-fill a partial last k-tile: K a
+    multiple of the 16-byte chunk (8 elements, 4 for FP32) but not of the k-tile,
+    from one chunk (K = 8) to many k-tiles, with ragged M and N and padded leading
+    dimensions.  Every direct configuration runs each shape (those without the
+    partial k-tile take the register-staged kernel)."""
+    v = mg.REGTILE_MFMA if dtype == "f32" else mg.MFMA16
+    names = [mg.migemm_config_name(v, c) for c in range(mg.migemm_config_count(v))]
+    direct = [c for c, n in enumerate(names) if n.startswith("direct")]
+    assert direct
+    for (M, N, K, lda, ldb) in RAGGED_K_SHAPES:
+        if dtype == "f32":
+            K = K // 2  # still a multiple of 4, not of 32
+        A, B = inputs.pair(M, N, K, dtype, "normal", seed=3 * M + N + K)
+        ref = None
+        for c in direct:
+            say(f"ragged_k {dtype} {M}x{N}x{K} lda={lda} ldb={ldb} cfg={names[c]}")
+            C, _ = run_gemm(A, B, dtype, variant=v, config=c, lda=lda, ldb=ldb)
+            from gpu_helpers import oracle_ref
+            ref = ref or oracle_ref(A, B, dtype)
+            check(C, A, B, dtype, ref=ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_direct_ragged_k_layouts_and_general_output(dtype):
+    """The partial last k-tile in every operand layout (row images and k-row
+    images both end inside it), with the general output step into a 16-bit C and
+    small integers compared bit for bit."""
+    from gpu_helpers import check_ex, oracle_ref, padding_untouched, run_gemm_ex
+    v = mg.REGTILE_MFMA if dtype == "f32" else mg.MFMA16
+    cfgs = (8, 10) if dtype == "f32" else (7, 13, 16)
+    K = 100 if dtype == "f32" else 200
+    M, N = 264, 136
+    for kind in ("normal", "int"):
+        A, B = inputs.pair(M, N, K, dtype, kind, seed=K + (kind == "int"))
+        ref = oracle_ref(A, B, dtype)
+        old = (torch.rand((M, N), generator=torch.Generator().manual_seed(7)) - 0.5).to(
+            torch.bfloat16)
+        for ta in (False, True):
+            for tb in (False, True):
+                for c in cfgs:
+                    say(f"ragged_k layouts {dtype} {kind} ta={ta} tb={tb} cfg={c}")
+                    C, buf, mask = run_gemm_ex(A, B, dtype, 1.0, 0.0, 0, None, variant=v,
+                                               config=c, ta=ta, tb=tb)
+                    check_ex(C, A, B, dtype, 1.0, 0.0, 0, None, ref=ref, exact=kind == "int")
+                    assert padding_untouched(buf, mask)
+                    if kind == "normal":
+                        C, buf, mask = run_gemm_ex(A, B, dtype, 0.5, -1.0, 2, old, variant=v,
+                                                   config=c, ta=ta, tb=tb)
+                        check_ex(C, A, B, dtype, 0.5, -1.0, 2, old, ref=ref)
+                        assert padding_untouched(buf, mask)
