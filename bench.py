@@ -473,10 +473,12 @@ def _counter_rows(d):
 
 
 def digest_counters(w, fetch_dir, write_dir, reps):
-    """HBM bytes per launch of the selected kernel from two profile-mode counter runs
-    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled so that the 1 GiB device
-    copy of the same run reads as 1 GiB; median of the last `reps` (GEMM) dispatches.
-    The entry is written to the traffic summary under this workload."""
+    """HBM bytes per call of the selected configuration from two profile-mode counter
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled so that the 1 GiB
+    device copy of the same run reads as 1 GiB; the last `reps` calls' dispatches (one
+    per launch of the call) are summed per call and the median call is kept, with the
+    per-launch figures beside it.  The entry is written to the traffic summary under
+    this workload."""
     import statistics
     import dense_gemm_16_amd as mg
     from dense_gemm_16_amd import inputs
@@ -485,20 +487,28 @@ def digest_counters(w, fetch_dir, write_dir, reps):
     d = mg.describe(-1, -1, 0, 0, w.M, w.N, w.K, code, None, w.K, None, w.N, c_code, w.N,
                     1 << 40)
     kernel = f"{d['variant']}[{d['config_name']}]"
+    launches = int(d["launches"])
     gib_kib = float(1 << 20)
-    e = {"kernel": kernel, "source_hash": source_hash()}
+    e = {"kernel": kernel, "source_hash": source_hash(), "launches_per_call": launches}
     for label, d in (("fetch", fetch_dir), ("write", write_dir)):
         rows = _counter_rows(d)
         copies = [x for n, x in rows if "copyBuffer" in n]
-        gemm = rows[-reps:]
+        gemm = rows[-reps * launches:]
         if len(copies) < 2 or any("copyBuffer" in n for n, _ in gemm):
             raise SystemExit(f"bench.py: {d} does not hold a profile pass (copies then GEMMs)")
         cal = statistics.median(copies[-2:])
-        raw = statistics.median(x for _, x in gemm)
+        calls = [sum(x for _, x in gemm[i:i + launches]) for i in range(0, len(gemm), launches)]
+        raw = statistics.median(calls)
+        scale = gib_kib / cal * 1024
         e[f"{label}_kib_raw"] = raw
         e[f"copy_{label}_kib_raw"] = cal
         e[f"{label}_factor"] = round(gib_kib / cal, 5)
-        e[f"{label}_bytes_per_launch"] = int(round(raw * gib_kib / cal * 1024))
+        e[f"{label}_bytes_per_launch"] = int(round(raw * scale))
+        if launches > 1:
+            e[f"{label}_bytes_by_launch"] = [
+                [gemm[j][0][:80], int(round(statistics.median(
+                    gemm[i + j][1] for i in range(0, len(gemm), launches)) * scale))]
+                for j in range(launches)]
         e[f"{label}_kernel_in_csv"] = gemm[-1][0][:160]
     e["hbm_bytes_per_launch"] = e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
     e["note"] = (f"HBM read {e['fetch_bytes_per_launch'] / 1e9:.3f} GB + write "

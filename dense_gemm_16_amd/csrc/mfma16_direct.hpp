@@ -101,7 +101,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // have a whole k-tile of matrix work to land; bit 4 = also compiled for
 // operands given transposed (without it those run the register-staged kernel);
 // bit 5 = K need only be whole chunks: a last k-tile that K ends inside is
-// zero-filled in LDS past K (interleaved schedules).
+// zero-filled in LDS past K (interleaved schedules; compiled as a second
+// instantiation of the kernel, launched only for such K).
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
           int BK_ = 64, int GM_ = 8, int SCHED_ = 0, int FLAGS_ = 0>
 struct DirectCfg {
@@ -307,7 +308,9 @@ __device__ __forceinline__ void wait_then_barrier() {
 }
 
 // TA: A given transposed (stored K x M); TB: B given transposed (stored N x K).
-template <class Cfg, bool GEN, bool TA, bool TB>
+// KTAIL: K ends inside the last k-tile (configurations with flag bit 5 only; a
+// separate instantiation, so products with whole k-tiles run code without it).
+template <class Cfg, bool GEN, bool TA, bool TB, bool KTAIL = false>
 __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     int64_t M, int64_t N, int64_t K, const typename Cfg::E* __restrict__ A, int64_t lda,
     const typename Cfg::E* __restrict__ B, int64_t ldb, Epi out, int tiles_m, int tiles_n) {
@@ -351,12 +354,14 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     const int64_t a_step = TA ? BK * lda : BK;
     const int64_t b_step = TB ? BK : BK * ldb;
 
-    // With flag bit 5, K need not be a multiple of the k-tile: the last k-tile
-    // then holds `tail` of its BK k, and the rest of its LDS image is zeroed
-    // (zero_tail) before it is read, so those k add exact zero products.
-    // Without it tail is 0 and none of that code is compiled.
+    // KTAIL: K is not a multiple of the k-tile; the last k-tile holds `tail` of
+    // its BK k, and the rest of its LDS image is zeroed (zero_tail) before it is
+    // read, so those k add exact zero products.  Without it tail is 0 and none
+    // of that code is compiled.
+    static_assert(!KTAIL || ((Cfg::FLAGS & 32) != 0 && Cfg::SCHED != 4),
+                  "a partial last k-tile only where flag bit 5 asks for it");
     const int KT = static_cast<int>(ceil_div(K, BK));
-    const int tail = (Cfg::FLAGS & 32) ? static_cast<int>(K % BK) : 0;
+    const int tail = KTAIL ? static_cast<int>(K % BK) : 0;
 
     // For the last k-tile when K ends inside it: how far each of this wave's
     // per-lane load offsets moves back so that chunks or k-rows past K are
@@ -1028,7 +1033,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         if (early && kt + S < KT) issue(kt + S);
         slab_step(true, kt + 1, 0, F[0], F[1]);
     };
-    if constexpr ((Cfg::FLAGS & 32) != 0) {
+    if constexpr (KTAIL) {
         for (int kt = 0; kt + 2 < KT; ++kt) kstep(kt, std::false_type{});
         if (KT >= 2) kstep(KT - 2, std::true_type{});
     } else {
@@ -1087,9 +1092,14 @@ hipError_t launch_direct_cfg(const GemmArgs& g) {
     const E* A = static_cast<const E*>(g.A);
     const E* B = static_cast<const E*>(g.B);
     const int itm = static_cast<int>(tm), itn = static_cast<int>(tn);
+    // the partial-last-k-tile instantiation only where K ends inside a k-tile
+    constexpr bool kRagged = (Cfg::FLAGS & 32) != 0;
+    const bool ktail = kRagged && g.K % Cfg::BK != 0;
 #define MIGEMM_LAUNCH(TA_, TB_)                                                                \
-    return launch_kernel(g, mfma16_direct_kernel<Cfg, GEN, TA_, TB_>, grid, block, g.M, g.N,    \
-                         g.K, A, g.lda, B, g.ldb, g.out, itm, itn)
+    return ktail ? launch_kernel(g, mfma16_direct_kernel<Cfg, GEN, TA_, TB_, kRagged>, grid,   \
+                                 block, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn)    \
+                 : launch_kernel(g, mfma16_direct_kernel<Cfg, GEN, TA_, TB_, false>, grid,     \
+                                 block, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn)
     if constexpr (Cfg::LAYOUTS) {
         if (g.ta && g.tb)
             MIGEMM_LAUNCH(true, true);

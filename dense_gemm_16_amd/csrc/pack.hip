@@ -12,10 +12,10 @@
 // k-contiguous row image, A' (M x K) or B' (N x K, that is B transposed), rows
 // starting on 128-byte lines (leading dimension K rounded up to 64) and
 // zero-filled from K to the end of the row.  The direct kernel then multiplies the
-// copies and any operand left in place with the call's own M, N and K: it
-// clamps ragged M and N rows, zero-fills a partial last k-tile, and reads a
-// copy's last chunk whole; the output step writes C exactly as for the
-// unpacked call.
+// copies and any operand left in place with the call's own M and N, and K (K
+// rounded up to 64 when both operands are copies): it clamps ragged M and N
+// rows, zero-fills a partial last k-tile, and reads a copy's last chunk whole;
+// the output step writes C exactly as for the unpacked call.
 //
 // The copy is memory-bound: 2 bytes read and 2 written per element copied,
 // small beside the product for the shapes this path is selected for.  One
@@ -55,16 +55,30 @@ struct PackJob {
 // Workgroups stride over the 64 x 64 tiles of both jobs (job 0's tiles first).
 // Reads are 2-byte loads, a wavefront covering 128 contiguous source bytes
 // (any alignment); writes are 16-byte stores of 8 consecutive dst columns.
+//
+// Tile order.  A source row whose start is not on a 128-byte line puts each
+// 128-byte tile row across two lines, the second shared with the next tile
+// along the source's contiguous side.  Consecutive tile indices therefore run
+// along that side (dst rows for a transposed job, dst columns otherwise), and
+// the workgroups of one XCD (blockIdx modulo 8) take one contiguous range of
+// indices, so a shared line is fetched into that XCD's L2 once instead of into
+// two XCDs' L2s.
 __global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
     __shared__ uint32_t tile[kTile][kTile + 1];
     const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;   // reads: ty in 0..3
     const int wx = threadIdx.x % 8, wy = threadIdx.x / 8;           // writes: wy in 0..31
     const int64_t total = j0.tiles + j1.tiles;
-    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    const int64_t per = gridDim.x / kNumXcd;
+    const int64_t first = blockIdx.x < per * kNumXcd
+                              ? (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd
+                              : blockIdx.x;
+    for (int64_t t = first; t < total; t += gridDim.x) {
         const bool second = t >= j0.tiles;
         const PackJob& j = second ? j1 : j0;
         const int64_t tt = second ? t - j0.tiles : t;
-        const int64_t r0 = (tt / j.tiles_c) * kTile, c0 = (tt % j.tiles_c) * kTile;
+        const int64_t tiles_r = j.tiles / j.tiles_c;
+        const int64_t r0 = (j.trans ? tt % tiles_r : tt / j.tiles_c) * kTile;
+        const int64_t c0 = (j.trans ? tt / tiles_r : tt % j.tiles_c) * kTile;
         if (j.vec) {
             // 64 rows x 8 chunks of 16 bytes, two per work-item; the chunk that
             // straddles cols (cols not a multiple of 8) is read element by element
@@ -233,6 +247,9 @@ hipError_t launch_packed16(const GemmArgs& g, int pc, int fallback_config) {
     hipError_t e = launch_pack16(g, ja, jb);
     if (e != hipSuccess) return e;
     GemmArgs p = g;
+    // Both operands copies, zero-filled to K rounded up to 64: the product runs
+    // on whole k-tiles, without the partial-k-tile instantiation.
+    if (!pl.a.in_place && !pl.b.in_place) p.K = round_up(g.K, 64);
     if (!pl.a.in_place) {
         p.ta = false;
         p.A = wa;
