@@ -6,88 +6,134 @@
 // accumulation), shaped for a short, wide C: one workgroup per 16 columns of C,
 // its waves (sixteen or eight, see Shape) splitting K between them.  Each wave
 // takes every sixteenth (eighth) 32-deep k-step and runs one
-// v_mfma_f32_16x16x32 per step, with the fragments
-// loaded straight from global memory into registers (16 bytes per lane where the
-// operand is k-contiguous, eight 2-byte loads where it is not); rows of A past M
-// and k past K read as zeros, and columns of B past N are clamped (their outputs
-// are not stored).  The waves' partial 16 x 16 blocks are then summed through
-// LDS in wave order, so the result does not depend on timing.  A 128x128-tile
-// launch would instead walk all of K for two rows of C on 32 workgroups.
+// v_mfma_f32_16x16x32 per step; rows of A past M and k past K read as zeros.
+// The waves' partial 16 x 16 blocks are then summed through LDS in wave order,
+// so the result does not depend on timing.  A 128x128-tile launch would instead
+// walk all of K for two rows of C on 32 workgroups.
 //
-// A k-contiguous operand needs K a multiple of 8 (or to be a copy zero-filled to
-// one), so that each lane's 8-deep run of k can be read whole; the launcher
-// returns hipErrorInvalidValue otherwise.
-#include "mfma_gemm.hpp"
+// Every operand is read 16 bytes per lane, in one of two forms:
+// * k-contiguous (row-major A, B given transposed): a lane's 8 consecutive k of
+//   its row or column are one 16-byte run, loaded straight into the fragment;
+// * k as the row index (row-major B, A given transposed): a step's 32 k-rows x
+//   16 columns (32 bytes per k-row) are loaded as 64 chunks of 16 bytes, one
+//   per lane, written to a slot of the wave's own LDS area as a row-major 32 x 16
+//   block, and read back with two ds_read_b64_tr_b16, which hand each lane one
+//   column of four k-rows apiece.  Reading such an operand 2 bytes per lane
+//   along its columns instead took three times as long (a quarter of each
+//   128-byte line per load, and eight loads per fragment).
+// Columns of B are assigned to workgroups so that the eight XCDs each take one
+// contiguous range: the four 16-column blocks that share a 128-byte line of a
+// row-major B then share one XCD's L2.
+//
+// Requirements (the launcher returns hipErrorInvalidValue otherwise): operands
+// 16-byte aligned with leading dimensions a multiple of 8 elements; K a
+// multiple of 8 for a k-contiguous operand (or the operand a copy zero-filled to
+// one); N a multiple of 8 for row-major B and M for A given transposed, so that a
+// 16-byte chunk of a k-row is wholly inside the matrix or wholly outside it.
+#include "mfma16_direct.hpp"
 
 namespace migemm {
 namespace {
 
-// Both operands k-contiguous: sixteen waves of five k-steps per round (a lane
-// holds 40 registers of fragments).  Otherwise eight waves of four k-steps: the
-// strided 2-byte loads of an operand stored with k as its row index need more
-// address registers than sixteen waves per workgroup leave each lane.
+// Sixteen waves of five k-steps per round when A is k-contiguous (a lane holds
+// 40 registers of fragments); eight of four when A is given transposed, where
+// both operands may be staged through LDS.
 template <bool TA, bool TB> struct Shape {
-    static constexpr bool KC = !TA && TB;
-    static constexpr int kWaves = KC ? 16 : 8, kBatch = KC ? 5 : 4;
+    static constexpr int kWaves = TA ? 8 : 16, kBatch = TA ? 4 : 5;
+    static constexpr int kRowOps = (TA ? 1 : 0) + (TB ? 0 : 1);  // operands with k as row index
+    static constexpr int kSlots = kRowOps ? kBatch * kRowOps : 1;  // 1 KiB LDS slots per wave
 };
 
-// The 16-byte k-run [k0, k0 + 8) of row `row` of a k-contiguous operand (kc:
-// read whole, K being a multiple of 8 or the operand a copy zero-filled to one),
-// or of column `row` of an operand stored with k as its row index (k-rows at or
-// past K read as zeros).
-template <typename E, bool KC>
+// The 16-byte k-run [k0, k0 + 8) of row `row` of a k-contiguous operand.
+template <typename E>
 __device__ __forceinline__ u32x4 krun(const E* __restrict__ p, int64_t ld, int64_t row,
-                                      int64_t k0, int64_t K) {
-    if constexpr (KC) {
-        return *reinterpret_cast<const u32x4*>(p + row * ld + k0);
-    } else {
-        const uint16_t* q = reinterpret_cast<const uint16_t*>(p) + k0 * ld + row;
-        u32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = k0 + 2 * e < K ? q[(2 * e) * ld] : 0u;
-            const uint32_t hi = k0 + 2 * e + 1 < K ? q[(2 * e + 1) * ld] : 0u;
-            v[e] = lo | (hi << 16);
-        }
-        return v;
-    }
+                                      int64_t k0) {
+    return *reinterpret_cast<const u32x4*>(p + row * ld + k0);
+}
+
+// This lane's 16-byte chunk of k-step s of an operand stored with k as its row
+// index (cols columns, this workgroup's 16 starting at c0): k-row 32 s + lane / 2,
+// columns c0 + 8 (lane % 2) .. + 7; zeros past K or past cols.
+template <typename E>
+__device__ __forceinline__ u32x4 krow_chunk(const E* __restrict__ p, int64_t ld, int64_t cols,
+                                            int64_t c0, int64_t K, int64_t s, int lane) {
+    const int64_t kr = 32 * s + lane / 2, c = c0 + 8 * (lane % 2);
+    if (kr < K && c < cols) return *reinterpret_cast<const u32x4*>(p + kr * ld + c);
+    return u32x4{0u, 0u, 0u, 0u};
+}
+
+// Stages a step's 32 x 16 block (lane l's chunk at byte 16 l: k-row l / 2, 32
+// bytes per k-row) in this wave's slot and returns the fragment of lane (r, g)
+// = (lane % 16, lane / 16): column r of k-rows 8 g .. 8 g + 7.  In each 16-lane
+// group, lanes 4 i .. 4 i + 3 address the four 8-byte pieces of k-row 8 g + i
+// (+ 4 for the second read), and the transposing read returns column r of those
+// four k-rows to lane r.  The wave's LDS operations run in order, so the reads
+// see the write without a barrier.
+__device__ __forceinline__ u32x4 stage_krow(MIGEMM_LDS char* slot, u32x4 chunk, int lane) {
+    *(MIGEMM_LDS u32x4*)(slot + 16 * lane) = chunk;
+    const int r = lane % 16, g = lane / 16;
+    MIGEMM_LDS char* p = slot + (8 * g + r / 4) * 32 + 8 * (r % 4);
+    const u32x2 lo = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS s16x4*)p));
+    const u32x2 hi = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS s16x4*)(p + 4 * 32)));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // TA: A stored K x M; TB: B stored N x K (k contiguous).
 template <typename E, bool GEN, bool TA, bool TB>
-__global__ __launch_bounds__((Shape<TA, TB>::kWaves * kWave)) void skinny16_kernel(int64_t M, int64_t N, int64_t K,
-                                                                  const E* __restrict__ A,
-                                                                  int64_t lda,
-                                                                  const E* __restrict__ B,
-                                                                  int64_t ldb, Epi out) {
+__global__ __launch_bounds__((Shape<TA, TB>::kWaves * kWave)) void skinny16_kernel(
+    int64_t M, int64_t N, int64_t K, const E* __restrict__ A, int64_t lda,
+    const E* __restrict__ B, int64_t ldb, Epi out) {
     using Op = MfmaOp<E, 16>;
     using L = AccLayout<16>;
-    constexpr int kWaves = Shape<TA, TB>::kWaves, kBatch = Shape<TA, TB>::kBatch;
+    using Sh = Shape<TA, TB>;
+    constexpr int kWaves = Sh::kWaves, kBatch = Sh::kBatch;
     __shared__ f32x4 part[kWaves][kWave];
+    __shared__ u32x4 stage[Sh::kRowOps ? kWaves : 1][Sh::kSlots][kWave];
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int r = lane % 16, g = lane / 16;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
-    const int64_t n = min(n0 + r, N - 1);  // B column fed by this lane (clamped)
+    // column block: XCD x (blockIdx modulo 8) takes one contiguous range
+    const int64_t per = gridDim.x / kNumXcd;
+    const int64_t blk = blockIdx.x < per * kNumXcd
+                            ? (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd
+                            : blockIdx.x;
+    const int64_t n0 = blk * 16;
+    const int64_t n = min(n0 + r, N - 1);  // B column fed by this lane (clamped; k-contiguous B)
     const bool a_in = r < M;
+    MIGEMM_LDS char* const slots =
+        (MIGEMM_LDS char*)stage + (Sh::kRowOps ? wave : 0) * (Sh::kSlots * 1024);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int64_t steps = ceil_div(K, 32);
     // kBatch of this wave's steps per round, all their loads issued before the
     // first matrix instruction: one memory latency per round instead of per step
-    // (with both operands k-contiguous a K of up to 2560 takes one round)
+    // (sixteen waves of five steps take a K of up to 2560 in one round)
     for (int64_t s0 = wave; s0 < steps; s0 += kBatch * kWaves) {
         u32x4 a[kBatch], b[kBatch];
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
             const int64_t s = s0 + q * kWaves;
             a[q] = b[q] = u32x4{0u, 0u, 0u, 0u};
-            const int64_t k0 = s * 32 + 8 * g;
-            if (s < steps && k0 < K) {
-                if (a_in) a[q] = krun<E, !TA>(A, lda, r, k0, K);
-                b[q] = krun<E, TB>(B, ldb, n, k0, K);
+            if (s < steps) {
+                const int64_t k0 = s * 32 + 8 * g;
+                if constexpr (TA)
+                    a[q] = krow_chunk(A, lda, M, 0, K, s, lane);
+                else if (a_in && k0 < K)
+                    a[q] = krun(A, lda, r, k0);
+                if constexpr (TB) {
+                    if (k0 < K) b[q] = krun(B, ldb, n, k0);
+                } else {
+                    b[q] = krow_chunk(B, ldb, N, n0, K, s, lane);
+                }
             }
         }
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) Op::run(acc, a[q], b[q]);
+        for (int q = 0; q < kBatch; ++q) {
+            MIGEMM_LDS char* const slot = slots + q * Sh::kRowOps * 1024;
+            if constexpr (TA) a[q] = stage_krow(slot, a[q], lane);
+            if constexpr (!TB) b[q] = stage_krow(slot + (TA ? 1024 : 0), b[q], lane);
+            Op::run(acc, a[q], b[q]);
+        }
     }
     part[wave][lane] = acc;
     __syncthreads();
@@ -129,11 +175,14 @@ hipError_t launch_typed(const GemmArgs& g) {
 }  // namespace
 
 bool skinny16_fits(const GemmArgs& g) {
-    // k-contiguous operands are read 16 bytes at a time: aligned rows in whole
-    // chunks, K a multiple of 8 unless the operand is a zero-filled copy
+    // every operand is read in aligned 16-byte chunks: a k-contiguous one in
+    // whole chunks of k (K a multiple of 8 unless it is a zero-filled copy), one
+    // with k as its row index in whole chunks of its columns
     const bool k_whole = g.K % 8 == 0;
-    const bool a_ok = g.ta || (aligned16(g.A) && g.lda % 8 == 0 && (k_whole || g.pad_a));
-    const bool b_ok = !g.tb || (aligned16(g.B) && g.ldb % 8 == 0 && (k_whole || g.pad_b));
+    const bool a_ok = aligned16(g.A) && g.lda % 8 == 0 &&
+                      (g.ta ? g.M % 8 == 0 : (k_whole || g.pad_a));
+    const bool b_ok = aligned16(g.B) && g.ldb % 8 == 0 &&
+                      (g.tb ? (k_whole || g.pad_b) : g.N % 8 == 0);
     return g.M >= 1 && g.M <= 16 && g.N >= 1 && g.K > 0 && a_ok && b_ok &&
            ceil_div(g.N, 16) <= 0x7fffffff && (g.dtype == 1 || g.dtype == 2);
 }

@@ -63,6 +63,27 @@ def test_packed_odd_ld_and_misaligned(ta, tb):
                 check_ex(C, A, B, dtype, 1.0, 0.0, 0, None, ref=ref)
 
 
+def test_packed_transposing_copy_every_misalignment():
+    """The transposing copy (row-major B, A given transposed) reads each k-row's
+    64 elements as the 16-byte aligned chunks that cover them, so every start
+    position within a chunk occurs: element offsets 0 to 7 of the operand against
+    leading dimensions of every residue modulo 8, on shapes with ragged tiles in
+    both directions and a K that ends inside a tile."""
+    M, N, K = 130, 200, 150
+    for (ta, tb) in ((False, False), (True, True)):
+        A, B = inputs.pair(M, N, K, "bf16", "normal", seed=77 + ta)
+        ref = oracle_ref(A, B, "bf16")
+        for off in range(8):
+            for pad in range(8):
+                lda = (M if ta else K) + pad
+                ldb = (K if tb else N) + (pad + off) % 8
+                say(f"transposing copy {_name(ta, tb)} off={off} lda={lda} ldb={ldb}")
+                C, _, _ = run_gemm_ex(A, B, "bf16", 1.0, 0.0, 0, None, variant=mg.MFMA16,
+                                      config=12, ta=ta, tb=tb, lda=lda, ldb=ldb,
+                                      a_off=(off + 3) % 8, b_off=off)
+                check_ex(C, A, B, "bf16", 1.0, 0.0, 0, None, ref=ref)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_packed_general_output(dtype):
     M, N, K = 190, 321, 77
@@ -229,8 +250,9 @@ def test_split_tail_on_the_skinny_kernel():
     round of workgroups: 1 to 16 rows go to the skinny kernel (K split over the
     waves of each workgroup), more to the 64x64 tile.  Cases: 1, 4, 16 and 17 tail
     rows on the direct path; B given transposed (k-contiguous skinny loads); A
-    given transposed; the general output step into FP32 and BF16 C; and the
-    packed path (ragged K)."""
+    given transposed and row-major B (k-row chunks staged through LDS); the
+    general output step into FP32, FP16 and BF16 C; the packed path (ragged K);
+    and a row-major B the skinny kernel cannot read in 16-byte chunks."""
     dtype = "bf16"
     # (M, N, K, ta, tb, C dtype code, configuration)
     cases = [(2049, 2048, 128, False, False, 0, 7),
@@ -245,7 +267,17 @@ def test_split_tail_on_the_skinny_kernel():
              # partial last k-step (skinny); sixteen-wave skinny (B given transposed)
              (2050, 2048, 136, False, False, 0, 7),
              (2050, 2048, 2056, False, True, 0, 7),
-             (2050, 2047, 2056, False, False, 0, 12)]
+             (2050, 2047, 2056, False, False, 0, 12),
+             # row-major B and A given transposed staged through LDS (16-byte
+             # k-row chunks, transposing reads): sixteen tail rows of A^T, eight
+             # with B k-contiguous, a single 8-deep k-step, a 16-bit C
+             (2064, 2048, 2056, True, False, 0, 7),
+             (2056, 2040, 128, True, True, 0, 7),
+             (2049, 2048, 8, False, False, 0, 7),
+             (2052, 2000, 192, False, False, 1, 7),
+             # odd N, row-major B off its 16-byte boundary: the tail runs on the
+             # 64x64 configuration instead
+             (2050, 2047, 64, False, False, 0, 7)]
     for (M, N, K, ta, tb, c_code, cfg) in cases:
         A, B = inputs.pair(M, N, K, dtype, "normal", seed=M + 3 * N + K + ta + 2 * tb)
         ref = oracle_ref(A, B, dtype)
@@ -265,3 +297,9 @@ def test_split_tail_on_the_skinny_kernel():
                                          2048, 0, 2048, 0)
         d = mg._parse_description(text)
         assert st == mg.OK and d["launches"] == 2 and d["grid1"] == tail_grid, text
+    # sixteen waves unless A is given transposed (eight)
+    for (ta, block) in [(0, 1024), (1, 512)]:
+        st, text = mg.migemm_describe_ex(mg.MFMA16, 7, ta, 0, 2056, 2048, 128, 2, None,
+                                         2056 if ta else 128, None, 2048, 0, 2048, 0)
+        d = mg._parse_description(text)
+        assert st == mg.OK and d["launches"] == 2 and d["block1"] == block, text
