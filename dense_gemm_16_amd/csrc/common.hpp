@@ -63,6 +63,10 @@ struct GemmArgs {
     // up to a whole 16-byte chunk inside its leading dimension, so a kernel may
     // read that last chunk whole.
     bool pad_a = false, pad_b = false;
+    // Only for the skinny kernel: element (i, j) of this product is C[j * ldc +
+    // i], i.e. the call computes a block of C^T (the last columns of a product,
+    // as B^T A^T).
+    bool trans_c = false;
     // True unless the output step is the plain FP32 overwrite.
     bool general() const { return !(out.alpha == 1.0f && out.beta == 0.0f && out.c_dtype == 0); }
 };

@@ -27,9 +27,12 @@ template <typename E> struct Cfgs {
     using D8 = DirectCfg<E, 128, 128, 2, 2, 16, 4, 64>;             // 4 waves, 4 stages
     using D9 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 2>;    // gm4, interleave, nt C
     using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 30>;  // + AGPRs, early loads; all layouts
+    using D10P = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 28>; // D10 with plain C stores
     using D13 = DirectCfg<E, 128, 256, 2, 4, 16, 3, 64, 8, 2, 48>;  // 8 waves of 64x64, 3 stages; all layouts; ragged K
     using D14 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 22>;  // ping-pong (whole tiles), AGPRs, nt C; all layouts
+    using D14P = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 20>; // D14 with plain C stores
     using D15 = DirectCfg<E, 128, 256, 2, 4, 16, 2, 64, 8, 4, 22>;  // ping-pong 128x256 (whole tiles); all layouts
+    using D15P = DirectCfg<E, 128, 256, 2, 4, 16, 2, 64, 8, 4, 20>; // D15 with plain C stores
     using D16 = DirectCfg<E, 64, 64, 2, 4, 16, 4, 64, 8, 0, 58>;    // 8 waves of 32x16, 4 stages, early loads, nt C; all layouts; ragged K
     using D16P = DirectCfg<E, 64, 64, 2, 4, 16, 4, 64, 8, 0, 56>;   // D16 with plain C stores
 };
@@ -68,10 +71,16 @@ hipError_t launch_cfg16(const GemmArgs& g) {
                                     : direct_or<typename T::D7P, 2, GEN>(g);
     else if constexpr (C == 8) return direct_or<typename T::D8, 2, GEN>(g);
     else if constexpr (C == 9) return direct_or<typename T::D9, 0, GEN>(g);
-    else if constexpr (C == 10) return direct_or<typename T::D10, 0, GEN>(g);
+    else if constexpr (C == 10)
+        return c_whole_lines(g.out) ? direct_or<typename T::D10, 0, GEN>(g)
+                                    : direct_or<typename T::D10P, 0, GEN>(g);
     else if constexpr (C == 13) return direct_or<typename T::D13, 2, GEN>(g);
-    else if constexpr (C == 14) return direct_or<typename T::D14, 0, GEN>(g);
-    else if constexpr (C == 15) return direct_or<typename T::D15, 2, GEN>(g);
+    else if constexpr (C == 14)
+        return c_whole_lines(g.out) ? direct_or<typename T::D14, 0, GEN>(g)
+                                    : direct_or<typename T::D14P, 0, GEN>(g);
+    else if constexpr (C == 15)
+        return c_whole_lines(g.out) ? direct_or<typename T::D15, 2, GEN>(g)
+                                    : direct_or<typename T::D15P, 2, GEN>(g);
     else if constexpr (C == 16)
         return c_whole_lines(g.out) ? direct_or<typename T::D16, 3, GEN>(g)
                                     : direct_or<typename T::D16P, 3, GEN>(g);

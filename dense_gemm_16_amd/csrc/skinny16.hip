@@ -25,6 +25,12 @@
 // contiguous range: the four 16-column blocks that share a 128-byte line of a
 // row-major B then share one XCD's L2.
 //
+// The same kernel takes the last few columns of a product as the transposed
+// product C^T = B^T A^T (M and N swapped, B's column slab as the left operand,
+// A as the right one), writing element (i, j) to C[j * ldc + i] (trans_c): a
+// lane's four rows of a 16 x 16 block are then four consecutive elements of
+// one row of C.
+//
 // Requirements (the launcher returns hipErrorInvalidValue otherwise): operands
 // 16-byte aligned with leading dimensions a multiple of 8 elements; K a
 // multiple of 8 for a k-contiguous operand (or the operand a copy zero-filled to
@@ -80,8 +86,9 @@ __device__ __forceinline__ u32x4 stage_krow(MIGEMM_LDS char* slot, u32x4 chunk, 
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// TA: A stored K x M; TB: B stored N x K (k contiguous).
-template <typename E, bool GEN, bool TA, bool TB>
+// TA: A stored K x M; TB: B stored N x K (k contiguous); TC: C written
+// transposed.
+template <typename E, bool GEN, bool TA, bool TB, bool TC>
 __global__ __launch_bounds__((Shape<TA, TB>::kWaves * kWave)) void skinny16_kernel(
     int64_t M, int64_t N, int64_t K, const E* __restrict__ A, int64_t lda,
     const E* __restrict__ B, int64_t ldb, Epi out) {
@@ -150,17 +157,17 @@ __global__ __launch_bounds__((Shape<TA, TB>::kWaves * kWave)) void skinny16_kern
 #pragma unroll
     for (int e = 0; e < L::R; ++e) {
         const int64_t row = L::row(lane, e);
-        if (row < M) store_out<GEN>(out, row * out.ldc + col, sum[e]);
+        if (row < M) store_out<GEN>(out, TC ? col * out.ldc + row : row * out.ldc + col, sum[e]);
     }
 }
 
-template <typename E, bool GEN>
+template <typename E, bool GEN, bool TC>
 hipError_t launch_typed(const GemmArgs& g) {
     const dim3 grid(static_cast<unsigned>(ceil_div(g.N, 16)));
     const E* A = static_cast<const E*>(g.A);
     const E* B = static_cast<const E*>(g.B);
 #define MIGEMM_LAUNCH(TA_, TB_)                                                                \
-    return launch_kernel(g, skinny16_kernel<E, GEN, TA_, TB_>, grid,                          \
+    return launch_kernel(g, skinny16_kernel<E, GEN, TA_, TB_, TC>, grid,                      \
                          dim3(Shape<TA_, TB_>::kWaves * kWave), g.M, g.N, g.K, A, g.lda, B,   \
                          g.ldb, g.out)
     if (g.ta) {
@@ -170,6 +177,11 @@ hipError_t launch_typed(const GemmArgs& g) {
     if (g.tb) MIGEMM_LAUNCH(false, true);
     MIGEMM_LAUNCH(false, false);
 #undef MIGEMM_LAUNCH
+}
+
+template <typename E, bool GEN>
+hipError_t launch_out(const GemmArgs& g) {
+    return g.trans_c ? launch_typed<E, GEN, true>(g) : launch_typed<E, GEN, false>(g);
 }
 
 }  // namespace
@@ -190,8 +202,8 @@ bool skinny16_fits(const GemmArgs& g) {
 hipError_t launch_skinny16(const GemmArgs& g) {
     if (!skinny16_fits(g)) return hipErrorInvalidValue;
     if (g.general())
-        return g.dtype == 1 ? launch_typed<_Float16, true>(g) : launch_typed<bf16_t, true>(g);
-    return g.dtype == 1 ? launch_typed<_Float16, false>(g) : launch_typed<bf16_t, false>(g);
+        return g.dtype == 1 ? launch_out<_Float16, true>(g) : launch_out<bf16_t, true>(g);
+    return g.dtype == 1 ? launch_out<_Float16, false>(g) : launch_out<bf16_t, false>(g);
 }
 
 }  // namespace migemm

@@ -333,6 +333,32 @@ def test_workspace_size():
                                           None) == mg.ERR_INVALID_ARG
 
 
+def test_describe_split_bands():
+    """A last band of tile rows or columns that would start a second round of
+    workgroups runs as launches of its own after the whole tiles: up to 16 rows
+    on the skinny kernel (16 columns of C per workgroup, sixteen waves), up to 16
+    columns on the skinny kernel as the transposed product (16 rows of C per
+    workgroup; eight waves when B is row-major), wider tails on the 64x64 tile."""
+    def launches(M, N, K, cfg=-1):
+        d = mg.describe(-1 if cfg < 0 else mg.MFMA16, cfg, 0, 0, M, N, K, mg.BF16, None, K,
+                        None, N, 0, N, 0)
+        return d["config"], [(d[f"grid{i}"], d[f"block{i}"]) for i in range(d["launches"])]
+    # 256x256 tiles; whole tiles on the ping-pong kernel (8 waves, 512 work-items)
+    assert launches(4100, 4096, 4096) == (10, [(256, 512), (256, 1024)])
+    assert launches(4096, 4104, 4096) == (10, [(256, 512), (256, 512)])
+    assert launches(4100, 4104, 4096) == (10, [(256, 512), (257, 1024), (256, 512)])
+    assert launches(8192, 8200, 8192) == (10, [(1024, 512), (512, 512)])
+    # wider tails: one band of 64x64 tiles
+    assert launches(4160, 4096, 4096) == (10, [(256, 512), (64, 512)])
+    assert launches(4096, 4160, 4096) == (10, [(256, 512), (64, 512)])
+    # 128x128 tiles: eight tail columns
+    assert launches(2048, 2056, 2048) == (7, [(256, 512), (128, 512)])
+    # no split where the whole tiles alone would not save a round
+    assert launches(3080, 3072, 3072) == (13, [(300, 512)])
+    assert launches(4352, 4096, 4096) == (14, [(272, 512)])
+    assert launches(4096, 4096, 4096) == (14, [(256, 512)])
+
+
 def test_describe():
     st, text = mg.migemm_describe(8192, 8192, 8192, mg.BF16, 8192, 8192, 8192)
     assert st == mg.OK
