@@ -218,12 +218,26 @@ int64_t packed_k(int64_t K);
 // Alignment the packed path asks of a workspace.
 constexpr int64_t kWorkspaceAlign = 256;
 hipError_t launch_mfma_i8(const GemmArgs& a, int config);
-// FP16/BF16 products with 1 <= M <= 16 (k-contiguous operands: K a multiple of
-// 8, or zero-filled copies), K split over the
-// waves of each workgroup (skinny16.hip); skinny16_fits says whether these and
-// its alignment needs hold (hipErrorInvalidValue from the launcher otherwise).
-bool skinny16_fits(const GemmArgs& a);
-hipError_t launch_skinny16(const GemmArgs& a);
+// FP32, FP16 and BF16 products with 1 <= M <= 16, K split over the waves of
+// each workgroup (skinny.hip); skinny_fits says whether its alignment and
+// whole-chunk needs hold (hipErrorInvalidValue from the launcher otherwise).
+bool skinny_fits(const GemmArgs& a);
+hipError_t launch_skinny(const GemmArgs& a);
+
+// A tiled launch whose last band of tile rows or columns would start a round of
+// workgroups of its own (split.cpp): the whole tiles first, then the rows past
+// them, then the columns past them (rows [0, m_main) when the rows are split
+// too), each tail of up to 16 on the skinny kernel (the columns as the
+// transposed product), wider ones on a smaller tile.
+struct SplitPlan {
+    bool rows = false, cols = false;
+    int64_t m_main = 0, n_main = 0;
+};
+// Tiles of bm x bn on the 256 CUs; tails wider than max_tail are not split off.
+SplitPlan plan_split(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t max_tail);
+using CfgLauncher = hipError_t (*)(const GemmArgs&, int);
+hipError_t launch_split(const GemmArgs& g, const SplitPlan& p, CfgLauncher head, int head_config,
+                        CfgLauncher tail, int tail_config);
 // K == 0: the sum of products is 0 for every element; applies the output step to it.
 hipError_t launch_empty_product(const GemmArgs& a);
 

@@ -58,8 +58,26 @@ hipError_t launch_gen(const GemmArgs& g, int config) {
 int regtile_mfma_config_count() { return kCount; }
 const char* regtile_mfma_config_name(int c) { return (c >= 0 && c < kCount) ? kNames[c] : nullptr; }
 
-hipError_t launch_regtile_mfma(const GemmArgs& g, int config) {
+namespace {
+
+hipError_t launch_cfg(const GemmArgs& g, int config) {
     return g.general() ? launch_gen<true>(g, config) : launch_gen<false>(g, config);
+}
+
+}  // namespace
+
+// The direct 128x128 (configuration 10) and 64x64 (8) tiles: a last band of tile
+// rows or columns that would start a round of workgroups of its own is split
+// off (split.cpp).  Tails of up to 16 run on the skinny kernel; wider ones on
+// the 64x64 tile after the 128x128 one, and are left in place after the 64x64
+// one (a tail on the same tile costs what the extra round does).
+hipError_t launch_regtile_mfma(const GemmArgs& g, int config) {
+    if (config == 8 || config == 10) {
+        const int64_t t = config == 10 ? 128 : 64;
+        const SplitPlan p = plan_split(g.M, g.N, t, t, config == 10 ? t : 16);
+        if (p.rows || p.cols) return launch_split(g, p, launch_cfg, config, launch_cfg, 8);
+    }
+    return launch_cfg(g, config);
 }
 
 }  // namespace migemm

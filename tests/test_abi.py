@@ -338,9 +338,10 @@ def test_describe_split_bands():
     workgroups runs as launches of its own after the whole tiles: up to 16 rows
     on the skinny kernel (16 columns of C per workgroup, sixteen waves), up to 16
     columns on the skinny kernel as the transposed product (16 rows of C per
-    workgroup; eight waves when B is row-major), wider tails on the 64x64 tile."""
-    def launches(M, N, K, cfg=-1):
-        d = mg.describe(-1 if cfg < 0 else mg.MFMA16, cfg, 0, 0, M, N, K, mg.BF16, None, K,
+    workgroup; eight waves when B is row-major), wider tails on the 64x64 tile;
+    FP16/BF16 and FP32 alike."""
+    def launches(M, N, K, cfg=-1, dt=mg.BF16):
+        d = mg.describe(-1 if cfg < 0 else mg.MFMA16, cfg, 0, 0, M, N, K, dt, None, K,
                         None, N, 0, N, 0)
         return d["config"], [(d[f"grid{i}"], d[f"block{i}"]) for i in range(d["launches"])]
     # 256x256 tiles; whole tiles on the ping-pong kernel (8 waves, 512 work-items)
@@ -357,6 +358,15 @@ def test_describe_split_bands():
     assert launches(3080, 3072, 3072) == (13, [(300, 512)])
     assert launches(4352, 4096, 4096) == (14, [(272, 512)])
     assert launches(4096, 4096, 4096) == (14, [(256, 512)])
+    # FP32 on its matrix-core kernels: the 128x128 tile (configuration 10) and the
+    # 64x64 one (8) with tails of up to 16 on the FP32 skinny kernel; a wider
+    # tail of the 64x64 tile is left in place (it would cost the same round)
+    F32 = mg.F32
+    assert launches(2056, 2048, 2048, dt=F32) == (10, [(256, 512), (128, 1024)])
+    assert launches(2048, 2056, 2048, dt=F32) == (10, [(256, 512), (128, 512)])
+    assert launches(2100, 2048, 2048, dt=F32) == (10, [(256, 512), (32, 512)])
+    assert launches(1032, 1024, 1024, dt=F32) == (8, [(256, 512), (64, 1024)])
+    assert launches(1080, 1024, 1024, dt=F32) == (8, [(272, 512)])
 
 
 def test_describe():

@@ -31,8 +31,9 @@ def _r8(x):
     return (x + 7) // 8 * 8
 
 
-def _run(M, N, K, ta, tb, config, c_code=0, dtype="bf16", pad_c=0, seed=0):
-    A, B = inputs.pair(M, N, K, dtype, "normal", seed=seed + M + 3 * N + 7 * K + ta + 2 * tb)
+def _run(M, N, K, ta, tb, config, c_code=0, dtype="bf16", pad_c=0, seed=0, variant=mg.MFMA16,
+         dist="normal", exact=False):
+    A, B = inputs.pair(M, N, K, dtype, dist, seed=seed + M + 3 * N + 7 * K + ta + 2 * tb)
     ref = oracle_ref(A, B, dtype)
     alpha, beta = (1.0, 0.0) if c_code == 0 else (0.75, -1.25)
     old = None
@@ -41,11 +42,11 @@ def _run(M, N, K, ta, tb, config, c_code=0, dtype="bf16", pad_c=0, seed=0):
             {1: torch.float16, 2: torch.bfloat16}[c_code])
     lda = _r8(M if ta else K)
     ldb = _r8(K if tb else N)
-    say(f"split cfg={config} {_name(ta, tb)} {M}x{N}x{K} {dtype} c_dtype={c_code} "
-        f"lda={lda} ldb={ldb} ldc=N+{pad_c}")
-    C, buf, mask = run_gemm_ex(A, B, dtype, alpha, beta, c_code, old, variant=mg.MFMA16,
+    say(f"split variant={variant} cfg={config} {_name(ta, tb)} {M}x{N}x{K} {dtype} {dist} "
+        f"c_dtype={c_code} lda={lda} ldb={ldb} ldc=N+{pad_c}")
+    C, buf, mask = run_gemm_ex(A, B, dtype, alpha, beta, c_code, old, variant=variant,
                                config=config, ta=ta, tb=tb, lda=lda, ldb=ldb, ldc=N + pad_c)
-    check_ex(C, A, B, dtype, alpha, beta, c_code, old, ref=ref)
+    check_ex(C, A, B, dtype, alpha, beta, c_code, old, ref=ref, exact=exact)
     assert padding_untouched(buf, mask)
 
 
@@ -101,3 +102,27 @@ def test_split_after_packing():
                                    config=cfg, ta=ta, tb=tb)
         check_ex(C, A, B, "f16", 1.0, 0.0, 0, None, ref=ref)
         assert padding_untouched(buf, mask)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_split_fp32_every_layout(ta, tb):
+    """FP32 on the FP32 matrix-core kernels: the 128x128 tile (configuration 10)
+    with eight tail rows, eight tail columns and both, on the FP32 skinny kernel
+    (16-deep k-steps of four 16x16x4 instructions; k-row operands staged through
+    LDS and read back four k-rows at a time); K a multiple of 4 but not of the
+    16-deep step."""
+    _run(2056, 2048, 68, ta, tb, 10, dtype="f32", variant=mg.REGTILE_MFMA)
+    _run(2048, 2056, 68, ta, tb, 10, dtype="f32", variant=mg.REGTILE_MFMA)
+    _run(2056, 2056, 96, ta, tb, 10, dtype="f32", variant=mg.REGTILE_MFMA)
+
+
+def test_split_fp32_other_cases():
+    """FP32: the 64x64 tile (configuration 8) with tails of 8 rows or columns; a
+    52-row tail of the 128x128 tile on the 64x64 one; the general output step into
+    BF16 C; small-integer inputs, which must come out exact."""
+    v = mg.REGTILE_MFMA
+    _run(1032, 1024, 64, False, False, 8, dtype="f32", variant=v)
+    _run(1024, 1032, 64, True, True, 8, dtype="f32", variant=v)
+    _run(2100, 2048, 64, False, True, 10, dtype="f32", variant=v)
+    _run(2048, 2056, 64, False, False, 10, dtype="f32", variant=v, c_code=2, pad_c=3)
+    _run(2056, 2056, 64, True, False, 10, dtype="f32", variant=v, dist="int", exact=True)
