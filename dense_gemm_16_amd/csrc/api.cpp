@@ -425,7 +425,7 @@ int migemm_convert(int src_dtype, int dst_dtype, int64_t rows, int64_t cols, con
     if (!known_dtype(src_dtype) || !known_dtype(dst_dtype)) return MIGEMM_ERR_INVALID_ARG;
     if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return MIGEMM_ERR_INVALID_ARG;
     const int64_t min_ld = cols > 1 ? cols : 1;
-    if (lds < min_ld || ldd < min_ld || lds > kMaxLd || ldd > kMaxLd) return MIGEMM_ERR_INVALID_ARG;
+    if (lds < min_ld || ldd < min_ld || lds >= kMaxLd || ldd >= kMaxLd) return MIGEMM_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0) return MIGEMM_OK;
     if (!src || !dst) return MIGEMM_ERR_INVALID_ARG;
     uintptr_t s0, s1, d0, d1;

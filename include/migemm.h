@@ -298,7 +298,7 @@ int migemm_describe_ex(int variant, int config, int op_a, int op_b,
  * from src_dtype to dst_dtype (any of MIGEMM_F32, MIGEMM_F16, MIGEMM_BF16).
  * Widening is exact; narrowing rounds to nearest even (magnitudes beyond the
  * target's range become +-infinity, NaN stays NaN).  Both matrices are
- * row-major device arrays with leading dimensions lds, ldd >= max(1, cols)
+ * row-major device arrays with leading dimensions max(1, cols) <= lds, ldd < 2^32
  * (elements); elements between rows are not touched.  src and dst must not
  * overlap.  Same stream, ownership and error rules as migemm_gemm; rows == 0
  * or cols == 0 is a no-op.

@@ -161,7 +161,8 @@ def test_general_form_forced_variant_checks():
 
 @pytest.mark.parametrize("args", [
     dict(src_dtype=3), dict(dst_dtype=-1), dict(rows=-1), dict(cols=-1), dict(lds=9),
-    dict(ldd=9), dict(src=None), dict(dst=None), dict(rows=1 << 31),
+    dict(ldd=9), dict(src=None), dict(dst=None), dict(rows=1 << 31), dict(lds=1 << 32),
+    dict(ldd=1 << 32),
     dict(dst=P + 100),  # overlaps src (8 x 10 FP32 from P spans 320 bytes)
 ])
 def test_convert_invalid_arguments(args):
