@@ -731,9 +731,13 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 #pragma unroll
                     for (int r = 0; r < L::R; ++r)
                         if (inside(i, j, r)) {
-                        if constexpr (EB == 1)  // exact INT32 sums of 8-bit products
-                            store_i32_stream(static_cast<int32_t*>(out.C) + index(i, j, r), acc[i][j][r]);
-                        else
+                        if constexpr (EB == 1) {  // exact INT32 sums of 8-bit products
+                            int32_t* const p = static_cast<int32_t*>(out.C) + index(i, j, r);
+                            if constexpr (NT)
+                                store_i32_stream(p, acc[i][j][r]);
+                            else
+                                *p = acc[i][j][r];
+                        } else
                             store_out<false, NT>(out, index(i, j, r), acc[i][j][r]);
                     }
         } else {

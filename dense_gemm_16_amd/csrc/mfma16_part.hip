@@ -44,16 +44,6 @@ hipError_t direct_or(const GemmArgs& g) {
     return direct_fits<D>(g) ? launch_direct_cfg<D, GEN>(g) : launch_cfg16_any(g, F);
 }
 
-// Non-temporal C stores pay when every row of C starts a 128-byte line: the row
-// pieces that neighbouring 16x16 blocks store then fill whole lines.  Rows that
-// straddle lines (an odd ldc, say) split every piece into two partial-line
-// writes, which plain stores merge in L2 and non-temporal ones send on as they
-// are (the 2050 x 2047 FP16 product ran 18% slower with them).
-inline bool c_whole_lines(const Epi& o) {
-    const int64_t eb = (o.c_dtype == 1 || o.c_dtype == 2) ? 2 : 4;
-    return (o.ldc * eb) % 128 == 0 && (reinterpret_cast<uintptr_t>(o.C) & 127) == 0;
-}
-
 }  // namespace
 
 template <typename E, bool GEN, int C>

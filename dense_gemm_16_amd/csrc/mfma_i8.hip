@@ -39,7 +39,9 @@ constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 int mfma_i8_config_count() { return kCount; }
 const char* mfma_i8_config_name(int c) { return (c >= 0 && c < kCount) ? kNames[c] : nullptr; }
 
-hipError_t launch_mfma_i8(const GemmArgs& g, int config) {
+namespace {
+
+hipError_t launch_cfg(const GemmArgs& g, int config) {
     switch (config) {
         case 1: return launch_i8_cfg<1>(g);
         case 2: return launch_i8_cfg<2>(g);
@@ -47,6 +49,43 @@ hipError_t launch_mfma_i8(const GemmArgs& g, int config) {
         case 4: return launch_i8_cfg<4>(g);
         default: return launch_i8_cfg<0>(g);
     }
+}
+
+}  // namespace
+
+// Ragged shapes (split.cpp).  The direct ping-pong kernel (configuration 4)
+// takes whole 256x256 tiles only, and a shape with a partial last band of rows
+// or columns otherwise runs entirely on the register-staged 256x256 kernel
+// (configuration 3), 2.6 to 3.7 times slower at 8200 x 8192 x 8192 and 4100 x
+// 4096 x 4096.  So when the operands suit the direct kernel, the whole tiles
+// run on it and the rows and columns past them follow: up to 16 on the skinny
+// kernel, more on the 64x64 tile (configuration 2).  The 128x128 and 256x256
+// register-staged tiles split a last band that would start a round of its own,
+// as the other element types do; the 64x64 tile only for tails of up to 16.
+hipError_t launch_mfma_i8(const GemmArgs& g, int config) {
+    if (config == 3 || config == 4) {
+        const bool direct = g.K % 128 == 0 && aligned16(g.A) && aligned16(g.B) &&
+                            g.lda % 16 == 0 && g.ldb % 16 == 0;
+        SplitPlan p;
+        p.m_main = g.M / 256 * 256;
+        p.n_main = g.N / 256 * 256;
+        p.rows = p.m_main > 0 && p.m_main < g.M;
+        p.cols = p.n_main > 0 && p.n_main < g.N;
+        if (direct && p.m_main > 0 && p.n_main > 0 && (p.rows || p.cols)) {
+            if (!p.rows) p.m_main = g.M;
+            if (!p.cols) p.n_main = g.N;
+            return launch_split(g, p, launch_cfg, 4, launch_cfg, 2);
+        }
+    }
+    if (config <= 3 && config != 2) {
+        const int64_t t = config == 1 ? 128 : 256;
+        const SplitPlan p = plan_split(g.M, g.N, t, t, int64_t(1) << 62);
+        if (p.rows || p.cols) return launch_split(g, p, launch_cfg, config, launch_cfg, 2);
+    } else if (config == 2) {
+        const SplitPlan p = plan_split(g.M, g.N, 64, 64, 16);
+        if (p.rows || p.cols) return launch_split(g, p, launch_cfg, 2, launch_cfg, 2);
+    }
+    return launch_cfg(g, config);
 }
 
 }  // namespace migemm

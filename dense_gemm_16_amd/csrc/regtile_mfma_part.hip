@@ -28,11 +28,7 @@ using D10P = DirectCfg<float, 128, 128, 2, 4, 16, 4, 32, 4, 2, 48>;
 using D11 = DirectCfg<float, 128, 64, 2, 4, 16, 4, 32, 8, 2, 50>;   // 8 waves of 64x16
 using D11P = DirectCfg<float, 128, 64, 2, 4, 16, 4, 32, 8, 2, 48>;
 
-// Rows of C that start whole 128-byte lines take non-temporal stores.
-inline bool c_whole_lines(const Epi& o) {
-    const int64_t eb = (o.c_dtype == 1 || o.c_dtype == 2) ? 2 : 4;
-    return (o.ldc * eb) % 128 == 0 && (reinterpret_cast<uintptr_t>(o.C) & 127) == 0;
-}
+
 
 // The direct-staged configuration (NT stores or plain) where its preconditions
 // hold, else the register-staged configuration with index F.

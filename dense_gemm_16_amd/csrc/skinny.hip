@@ -1,14 +1,16 @@
-// skinny.hip -- products with at most 16 rows of C (M <= 16), FP32 or FP16/BF16
-// inputs: the last few rows (or, transposed, columns) of a product whose size
-// is just past a whole number of tile bands (a 2050-row product: rows 2048 and
-// 2049).
+// skinny.hip -- products with at most 16 rows of C (M <= 16), FP32, FP16/BF16
+// or INT8 inputs: the last few rows (or, transposed, columns) of a product whose
+// size is just past a whole number of tile bands (a 2050-row product: rows 2048
+// and 2049).
 //
 // The same C = A x B with FP32 sums (page "CUDA-Practice 09", section on FP32
-// accumulation), shaped for a short, wide C: one workgroup per 16 columns of C,
-// its waves (sixteen or eight, see Shape) splitting K between them.  A k-step is
-// one 16-byte chunk per lane of each operand: 32 deep for 16-bit elements (one
-// v_mfma_f32_16x16x32), 16 deep for FP32 (four v_mfma_f32_16x16x4_f32, element
-// e of every lane's chunk feeding instruction e, the same k order for A and B).
+// accumulation; exact INT32 sums for INT8), shaped for a short, wide C: one
+// workgroup per 16 columns of C, its waves (sixteen or eight, see Shape)
+// splitting K between them.  A k-step is one 16-byte chunk per lane of each
+// operand: 32 deep for 16-bit elements (one v_mfma_f32_16x16x32), 64 deep for
+// INT8 (one v_mfma_i32_16x16x64_i8), 16 deep for FP32 (four
+// v_mfma_f32_16x16x4_f32, element e of every lane's chunk feeding instruction
+// e, the same k order for A and B).
 // Each wave takes every sixteenth (eighth) k-step; rows of A past M and k past
 // K read as zeros.  The waves' partial 16 x 16 blocks are then summed through
 // LDS in wave order, so the result does not depend on timing.  A 128x128-tile
@@ -22,11 +24,12 @@
 //   columns are loaded as 64 chunks of 16 bytes, one per lane, written to a slot
 //   of the wave's own LDS area as a row-major block, and read back transposed:
 //   16-bit elements with two ds_read_b64_tr_b16, which hand each lane one column
-//   of four k-rows apiece; FP32 with four 4-byte reads, one per k-row (k-rows
-//   80 bytes apart, so that the four lane groups of a read fall on different
-//   banks).  Reading such an operand 2 bytes per lane along its columns instead
-//   took three times as long (a quarter of each 128-byte line per load, and
-//   eight loads per fragment).
+//   of four k-rows apiece; INT8 with two ds_read_b64_tr_b8 (one column of eight
+//   k-rows apiece); FP32 with four 4-byte reads, one per k-row (k-rows 80 bytes
+//   apart, so that the four lane groups of a read fall on different banks).
+//   Reading such an operand 2 bytes per lane along its columns instead took
+//   three times as long (a quarter of each 128-byte line per load, and eight
+//   loads per fragment).
 // Columns of B are assigned to workgroups so that the eight XCDs each take one
 // contiguous range: the 16-column blocks that share a 128-byte line of a
 // row-major B then share one XCD's L2.
@@ -38,10 +41,11 @@
 // one row of C.
 //
 // Requirements (the launcher returns hipErrorInvalidValue otherwise): operands
-// 16-byte aligned with leading dimensions in whole 16-byte chunks; K in whole
-// chunks for a k-contiguous operand (or the operand a copy zero-filled to one);
-// N in whole chunks for row-major B and M for A given transposed, so that a
-// chunk of a k-row is wholly inside the matrix or wholly outside it.
+// 16-byte aligned with leading dimensions in whole 16-byte chunks, and K in
+// whole chunks for a k-contiguous operand (or the operand a copy zero-filled to
+// one), so that its chunks along k are wholly inside the matrix or wholly past
+// K.  The side of an operand with k as its row index (N of row-major B, M of A
+// given transposed) may end inside a chunk.
 #include "mfma16_direct.hpp"
 
 namespace migemm {
@@ -54,8 +58,8 @@ template <typename E, bool TA, bool TB> struct Shape {
     static constexpr int EPC = 16 / sizeof(E);     // elements per 16-byte chunk
     static constexpr int KSTEP = 4 * EPC;          // k per step: four lane groups
     static constexpr int CPR = 16 / EPC;           // chunks per 16-column k-row
-    static constexpr int ROW_BYTES = EPC == 8 ? 32 : 80;  // a k-row in an LDS slot
-    static constexpr int SLOT = KSTEP * ROW_BYTES;        // 1 KiB (16-bit), 1280 B (FP32)
+    static constexpr int ROW_BYTES = EPC == 16 ? 16 : EPC == 8 ? 32 : 80;  // a k-row in an LDS slot
+    static constexpr int SLOT = KSTEP * ROW_BYTES;  // 1 KiB (8- and 16-bit), 1280 B (FP32)
     static constexpr int kRowOps = (TA ? 1 : 0) + (TB ? 0 : 1);  // operands with k as row index
     static constexpr int kSlots = kRowOps ? kBatch * kRowOps : 1;
 };
@@ -70,14 +74,39 @@ __device__ __forceinline__ u32x4 krun(const E* __restrict__ p, int64_t ld, int64
 // This lane's 16-byte chunk of k-step s of an operand stored with k as its row
 // index (cols columns, this workgroup's 16 starting at c0): k-row
 // KSTEP s + lane / CPR, columns c0 + EPC (lane % CPR) onwards; zeros past K or
-// past cols.
+// past cols.  A chunk that cols ends inside is read as its valid bytes only, in
+// at most four naturally aligned pieces (8, 4, 2 and 1 bytes, the chunk being
+// 16-byte aligned), so no byte past the matrix is touched.
 template <typename E, int KSTEP, int EPC>
 __device__ __forceinline__ u32x4 krow_chunk(const E* __restrict__ p, int64_t ld, int64_t cols,
                                             int64_t c0, int64_t K, int64_t s, int lane) {
     constexpr int CPR = 16 / EPC;
     const int64_t kr = KSTEP * s + lane / CPR, c = c0 + EPC * (lane % CPR);
-    if (kr < K && c < cols) return *reinterpret_cast<const u32x4*>(p + kr * ld + c);
-    return u32x4{0u, 0u, 0u, 0u};
+    if (kr >= K || c >= cols) return u32x4{0u, 0u, 0u, 0u};
+    const E* q = p + kr * ld + c;
+    if (c + EPC <= cols) return *reinterpret_cast<const u32x4*>(q);
+    const int nb = static_cast<int>(cols - c) * static_cast<int>(sizeof(E));  // 1 .. 15 bytes
+    const unsigned char* qb = reinterpret_cast<const unsigned char*>(q);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (nb & 8) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(qb);
+        v[0] = x[0];
+        v[1] = x[1];
+    }
+    const int o4 = nb & 8;  // offsets of the 4-, 2- and 1-byte pieces
+    const int o2 = o4 + (nb & 4), o1 = o2 + (nb & 2);
+    uint32_t w4 = 0u, w2 = 0u, w1 = 0u;
+    if (nb & 4) w4 = *reinterpret_cast<const uint32_t*>(qb + o4);
+    if (nb & 2) w2 = *reinterpret_cast<const uint16_t*>(qb + o2);
+    if (nb & 1) w1 = static_cast<uint32_t>(qb[o1]) << (8 * (o1 % 4));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // dword j collects the pieces that start in it (the 2-byte piece starts
+        // on a dword, the 1-byte piece anywhere)
+        v[j] |= (o4 / 4 == j && (nb & 4) ? w4 : 0u) | (o2 / 4 == j ? w2 : 0u) |
+                (o1 / 4 == j ? w1 : 0u);
+    }
+    return v;
 }
 
 // Stages a step's k-rows x 16 columns (lane l's chunk: k-row l / CPR, chunk
@@ -88,7 +117,19 @@ __device__ __forceinline__ u32x4 krow_chunk(const E* __restrict__ p, int64_t ld,
 template <int EPC>
 __device__ __forceinline__ u32x4 stage_krow(MIGEMM_LDS char* slot, u32x4 chunk, int lane) {
     const int r = lane % 16, g = lane / 16;
-    if constexpr (EPC == 8) {
+    if constexpr (EPC == 16) {
+        // 16-byte k-rows, one per lane.  In each 16-lane group, lanes 2 i and
+        // 2 i + 1 address the two 8-byte halves of k-row 16 g + i (+ 8 for the
+        // second read), and the transposing read returns column r of those eight
+        // k-rows to lane r.
+        *(MIGEMM_LDS u32x4*)(slot + 16 * lane) = chunk;
+        MIGEMM_LDS char* p = slot + (16 * g + r / 2) * 16 + 8 * (r % 2);
+        const u32x2 lo = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((MIGEMM_LDS i32x2*)p));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((MIGEMM_LDS i32x2*)(p + 8 * 16)));
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else if constexpr (EPC == 8) {
         // 32-byte k-rows.  In each 16-lane group, lanes 4 i .. 4 i + 3 address
         // the four 8-byte pieces of k-row 8 g + i (+ 4 for the second read), and
         // the transposing read returns column r of those four k-rows to lane r.
@@ -119,10 +160,11 @@ __global__ __launch_bounds__((Shape<E, TA, TB>::kWaves * kWave)) void skinny_ker
     int64_t M, int64_t N, int64_t K, const E* __restrict__ A, int64_t lda,
     const E* __restrict__ B, int64_t ldb, Epi out) {
     using Op = MfmaOp<E, 16>;
+    using Acc = typename Op::Acc;  // f32x4, or i32x4 for INT8
     using L = AccLayout<16>;
     using Sh = Shape<E, TA, TB>;
     constexpr int kWaves = Sh::kWaves, kBatch = Sh::kBatch, EPC = Sh::EPC, KSTEP = Sh::KSTEP;
-    __shared__ f32x4 part[kWaves][kWave];
+    __shared__ Acc part[kWaves][kWave];
     __shared__ __attribute__((aligned(16))) char stage[Sh::kRowOps ? kWaves : 1][Sh::kSlots * Sh::SLOT];
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int r = lane % 16, g = lane / 16;
@@ -136,7 +178,7 @@ __global__ __launch_bounds__((Shape<E, TA, TB>::kWaves * kWave)) void skinny_ker
     const bool a_in = r < M;
     MIGEMM_LDS char* const slots =
         (MIGEMM_LDS char*)&stage[0][0] + (Sh::kRowOps ? wave : 0) * (Sh::kSlots * Sh::SLOT);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    Acc acc = {};
     const int64_t steps = ceil_div(K, KSTEP);
     // kBatch of this wave's steps per round, all their loads issued before the
     // first matrix instruction: one memory latency per round instead of per step
@@ -170,10 +212,10 @@ __global__ __launch_bounds__((Shape<E, TA, TB>::kWaves * kWave)) void skinny_ker
     part[wave][lane] = acc;
     __syncthreads();
     if (wave != 0) return;
-    f32x4 sum = part[0][lane];
+    Acc sum = part[0][lane];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-        const f32x4 p = part[w][lane];
+        const Acc p = part[w][lane];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sum[e] += p[e];
     }
@@ -182,7 +224,12 @@ __global__ __launch_bounds__((Shape<E, TA, TB>::kWaves * kWave)) void skinny_ker
 #pragma unroll
     for (int e = 0; e < L::R; ++e) {
         const int64_t row = L::row(lane, e);
-        if (row < M) store_out<GEN>(out, TC ? col * out.ldc + row : row * out.ldc + col, sum[e]);
+        if (row >= M) continue;
+        const int64_t idx = TC ? col * out.ldc + row : row * out.ldc + col;
+        if constexpr (sizeof(E) == 1)
+            static_cast<int32_t*>(out.C)[idx] = sum[e];  // exact INT32 sums
+        else
+            store_out<GEN>(out, idx, sum[e]);
     }
 }
 
@@ -217,16 +264,15 @@ hipError_t launch_elem(const GemmArgs& g) {
 }  // namespace
 
 bool skinny_fits(const GemmArgs& g) {
-    if (g.dtype != 0 && g.dtype != 1 && g.dtype != 2) return false;
+    if (g.dtype != 0 && g.dtype != 1 && g.dtype != 2 && g.dtype != 3) return false;
+    if (g.dtype == 3 && g.out.c_dtype != 4) return false;  // INT8: INT32 C only
     // every operand is read in aligned 16-byte chunks: a k-contiguous one in
-    // whole chunks of k (unless it is a zero-filled copy), one with k as its row
-    // index in whole chunks of its columns
-    const int64_t epc = g.dtype == 0 ? 4 : 8;
+    // whole chunks of k (unless it is a zero-filled copy); one with k as its row
+    // index reads a last partial chunk of its columns element by element
+    const int64_t epc = g.dtype == 0 ? 4 : g.dtype == 3 ? 16 : 8;
     const bool k_whole = g.K % epc == 0;
-    const bool a_ok = aligned16(g.A) && g.lda % epc == 0 &&
-                      (g.ta ? g.M % epc == 0 : (k_whole || g.pad_a));
-    const bool b_ok = aligned16(g.B) && g.ldb % epc == 0 &&
-                      (g.tb ? (k_whole || g.pad_b) : g.N % epc == 0);
+    const bool a_ok = aligned16(g.A) && g.lda % epc == 0 && (g.ta || k_whole || g.pad_a);
+    const bool b_ok = aligned16(g.B) && g.ldb % epc == 0 && (!g.tb || k_whole || g.pad_b);
     return g.M >= 1 && g.M <= 16 && g.N >= 1 && g.K > 0 && a_ok && b_ok &&
            ceil_div(g.N, 16) <= 0x7fffffff;
 }
@@ -234,6 +280,7 @@ bool skinny_fits(const GemmArgs& g) {
 hipError_t launch_skinny(const GemmArgs& g) {
     if (!skinny_fits(g)) return hipErrorInvalidValue;
     if (g.dtype == 0) return launch_elem<float>(g);
+    if (g.dtype == 3) return launch_out<int8_t, false>(g);  // INT32 C, plain overwrite
     return g.dtype == 1 ? launch_elem<_Float16>(g) : launch_elem<bf16_t>(g);
 }
 

@@ -19,6 +19,7 @@
 //   skinny kernel, written transposed into C, more on a smaller tile.
 // The pieces run one after another on the call's stream.
 #include "common.hpp"
+#include "migemm.h"
 
 namespace migemm {
 
@@ -26,8 +27,14 @@ namespace {
 
 constexpr int64_t kCus = 256;
 
-int64_t elem_bytes(int dtype) { return dtype == 0 ? 4 : 2; }  // FP32 or 16-bit operands
-int64_t c_bytes(int c_dtype) { return (c_dtype == 1 || c_dtype == 2) ? 2 : 4; }
+// Bytes per element of A and B (FP32, FP16/BF16, INT8) and of C (FP32 or INT32,
+// FP16/BF16).
+int64_t elem_bytes(int dtype) {
+    return dtype == MIGEMM_F32 ? 4 : dtype == MIGEMM_I8 ? 1 : 2;
+}
+int64_t c_bytes(int c_dtype) {
+    return (c_dtype == MIGEMM_F16 || c_dtype == MIGEMM_BF16) ? 2 : 4;
+}
 
 }  // namespace
 

@@ -108,6 +108,30 @@ def test_whole_tiles_exact(ta, tb):
             assert bad.size == 0, f"{bad.size} differ; first {np.unravel_index(bad[0], C.shape)}"
 
 
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_ragged_bands_split_exact(ta, tb):
+    """A partial last band of 256-row tiles or 256-column tiles: the whole tiles
+    run on the direct ping-pong kernel, then the rows past them (up to 16 on the
+    skinny kernel, 64-deep k-steps, k-rows transposed through LDS; more on the
+    64x64 tile), then the columns past them (the transposed product on the
+    skinny kernel when they are whole 16-byte chunks, else the 64x64 tile); a
+    128x128-tile product one band past a round.  Selected automatically and with
+    configurations 3 and 4 asked for; bit-exact."""
+    cases = [(4100, 4096, 128), (4096, 4112, 128), (4100, 4112, 256), (4160, 4096, 128),
+             (4096, 4104, 128), (2056, 2048, 128)]
+    for (M, N, K) in cases:
+        A, B = inputs.pair(M, N, K, "i8", "uniform", seed=M + 2 * N + 3 * K + 7 * ta + 11 * tb)
+        want = _want(A, B)
+        lda = ((M if ta else K) + 15) // 16 * 16
+        ldb = ((K if tb else N) + 15) // 16 * 16
+        for (v, c) in [(-1, -1), (mg.MFMA_I8, 3), (mg.MFMA_I8, 4)]:
+            say(f"i8 split {_name(ta, tb)} {M}x{N}x{K} lda={lda} ldb={ldb} cfg={c}")
+            C, intact = run_i8(A, B, v, c, ta=ta, tb=tb, lda=lda, ldb=ldb)
+            assert intact
+            bad = np.flatnonzero(C != want)
+            assert bad.size == 0, f"{bad.size} differ; first {np.unravel_index(bad[0], C.shape)}"
+
+
 def test_whole_tiles_extreme_sums():
     """The largest K the direct configuration takes itself (a multiple of 128
     below 2^17): (-128)(-128) summed 130944 times is 2^31 - 2^21, still exact."""

@@ -126,3 +126,16 @@ def test_split_fp32_other_cases():
     _run(2100, 2048, 64, False, True, 10, dtype="f32", variant=v)
     _run(2048, 2056, 64, False, False, 10, dtype="f32", variant=v, c_code=2, pad_c=3)
     _run(2056, 2056, 64, True, False, 10, dtype="f32", variant=v, dist="int", exact=True)
+
+
+def test_split_tails_ending_inside_a_chunk():
+    """Tails whose k-row side ends inside a 16-byte chunk: the skinny kernel reads
+    that last chunk element by element.  Three columns past the whole tiles with
+    row-major B (the transposed product's left operand), four rows past them with
+    A given transposed, in FP16, BF16 and FP32 (configurations asked for on
+    operands with aligned, padded leading dimensions)."""
+    _run(4096, 4099, 64, False, False, 10, dtype="f16")
+    _run(4100, 4096, 64, True, True, 10)
+    _run(4100, 4099, 64, True, False, 10)
+    _run(2048, 2051, 64, False, False, 10, dtype="f32", variant=mg.REGTILE_MFMA)
+    _run(2054, 2048, 64, True, True, 10, dtype="f32", variant=mg.REGTILE_MFMA)
