@@ -369,15 +369,16 @@ def test_describe_split_bands():
     assert launches(1032, 1024, 1024, dt=F32) == (8, [(256, 512), (64, 1024)])
     assert launches(1080, 1024, 1024, dt=F32) == (8, [(272, 512)])
     # INT8: whole 256x256 tiles on the direct ping-pong kernel whenever the
-    # operands suit it, the rest after them (the skinny kernel up to 16, the
-    # register-staged 64x64 tile beyond, or where a tail is not whole chunks)
+    # operands suit it, the rest after them (the skinny kernel up to 16, also
+    # for a tail that ends inside a 16-byte chunk; the register-staged 64x64
+    # tile beyond)
     def launches_i8(M, N, K, ldb):
         d = mg.describe(-1, -1, 0, 0, M, N, K, mg.I8, None, K, None, ldb, mg.I32, N, 0)
         return d["config"], [(d[f"grid{i}"], d[f"block{i}"]) for i in range(d["launches"])]
     assert launches_i8(8192, 8192, 8192, 8192) == (4, [(1024, 512)])
     assert launches_i8(8200, 8192, 8192, 8192) == (3, [(1024, 512), (512, 1024)])
     assert launches_i8(8192, 8208, 8192, 8208) == (3, [(1024, 512), (512, 512)])
-    assert launches_i8(8192, 8200, 8192, 8208) == (3, [(1024, 512), (128, 256)])
+    assert launches_i8(8192, 8200, 8192, 8208) == (3, [(1024, 512), (512, 512)])
     assert launches_i8(8400, 8192, 8192, 8192) == (3, [(1024, 512), (512, 256)])
     assert launches_i8(2056, 2048, 2048, 2048) == (1, [(256, 256), (128, 1024)])
 
