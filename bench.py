@@ -56,6 +56,8 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 RESOURCES_FILE = os.path.join(ROOT, "dense_gemm_16_amd", "kernel_resources.json")
 SETTLE_MS = 200.0
+# Small, launch-bound workloads also timed as replays of a captured HIP graph.
+GRAPH_TIMED = ("c0-f16-256", "c1-f32-1024", "c2-f16-1024")
 EXTRA = ["c0-f16-256", "c1-f32-1024", "c1-f32-1024-int", "c2-f16-1024", "c3-f16-2048", "c3-bf16-2048",
          "c3r-f16-2050x2047x2056", "c4f-f32-4096", "s8-bf16-1024x8192x8192",
          "s2x4-bf16-4096x2048x8192"]
@@ -186,6 +188,44 @@ class Problem:
         est = self.time(3, 2)
         n = int(min(hi, max(lo, min_ms / max(est, 1e-4))))
         return self.time(n, 0), n
+
+    def graph_rate(self, per_graph=100, replays=5):
+        """The kernels' own rate without the host's per-call launch cost: `per_graph`
+        calls captured into one HIP graph on a side stream (default priority), then
+        the median ms per call over `replays` replays timed with HIP events.  Also
+        whether C after a replay equals C after an eager call, bit for bit (C is
+        poisoned before the replay; plain overwrites only)."""
+        import torch
+        mg = self.mg
+        self.launch()
+        torch.cuda.synchronize()
+        eager = self.C.clone()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=s):
+            args = self.args[:-1] + (torch.cuda.current_stream().cuda_stream,)
+            for _ in range(per_graph):
+                st = mg.migemm_gemm_ws(*args)
+                if st != mg.OK:
+                    raise RuntimeError(f"{self.w.name}: {mg.migemm_status_string(st)} in capture")
+        torch.cuda.synchronize()
+        self.C.fill_(float("nan") if self.C.is_floating_point() else -2147483641)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(self.C, eager))
+        times = []
+        for _ in range(replays):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            g.replay()
+            t1.record()
+            t1.synchronize()
+            times.append(t0.elapsed_time(t1) / per_graph)
+        del g
+        return statistics.median(times), same
 
     def settle(self, k, min_ms=SETTLE_MS):
         """Back-to-back launches from idle until min_ms have run.  Returns the
@@ -689,6 +729,16 @@ def main():
             log(f"extra {name}: {tf:.1f} TFLOPS on {px.kernel_name()}; oracle "
                 f"{extra[name]['oracle']['gflops']} GFLOPS on {extra[name]['oracle']['rows']} "
                 f"rows, {extra[name]['oracle']['gpu_rows_vs_oracle']}")
+            if name in GRAPH_TIMED:
+                # launch-bound sizes: the same calls replayed from a HIP graph
+                gms, same = px.graph_rate()
+                gtf = wx.flop / (gms * 1e-3) / 1e12
+                extra[name]["graph"] = {"tflops": round(gtf, 2), "ms": round(gms, 5),
+                                        "launches_per_graph": 100, "matches_eager": same}
+                log(f"extra {name} from a HIP graph: {gtf:.1f} TFLOPS ({gms * 1e3:.2f} us per call); "
+                    f"replay {'matches' if same else 'DIFFERS FROM'} the eager call")
+                if not same:
+                    raise SystemExit(f"bench.py: {name} replayed from a graph differs from the eager call")
             if not extra[name]["oracle"]["gpu_rows_ok"]:
                 raise SystemExit(f"bench.py: {name} does not match the oracle")
             if name == "c1-f32-1024":
