@@ -159,9 +159,9 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
     variant = MIGEMM_MFMA16;
     // Direct global->LDS staging needs 16-byte aligned operands with leading
     // dimensions a multiple of 8 elements, K a multiple of 8 (of the 64-deep
-    // k-tile for configurations 10, 14 and 15; configurations 7, 13 and 16
-    // zero-fill a last k-tile that K ends inside), and N (row-major B) or M (A
-    // given transposed) a multiple of 8; the launcher falls back to the
+    // k-tile for configurations 14 and 15; configurations 7, 13 and 16 zero-fill
+    // a last k-tile that K ends inside, 10 a first one), and N (row-major B) or M
+    // (A given transposed) a multiple of 8; the launcher falls back to the
     // register-staged kernel otherwise.  Other operands are packed into
     // zero-padded copies for the direct kernel once the product is large
     // enough for the extra copy launch to pay.
@@ -177,8 +177,9 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
     const bool whole256 = M % 256 == 0 && N % 256 == 0;
     if (direct && ktiles && tiles(256, 256) >= 256 && whole256)
         config = 14;  // direct 256x256x64, ping-pong wave groups (whole tiles only)
-    else if (direct && ktiles && tiles(256, 256) >= 256)
+    else if (direct && tiles(256, 256) >= 256)
         config = 10;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads
+                      // (a K that ends inside a k-tile: the partial k-tile first)
     else if (direct && ktiles && tiles(128, 256) >= 256 && M % 128 == 0 && N % 256 == 0)
         config = 15;  // direct 128x256x64, ping-pong wave groups (e.g. 1024x8192, 4096x2048)
     else if (direct && tiles(128, 256) >= 256)

@@ -102,7 +102,10 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // operands given transposed (without it those run the register-staged kernel);
 // bit 5 = K need only be whole chunks: a last k-tile that K ends inside is
 // zero-filled in LDS past K (interleaved schedules; compiled as a second
-// instantiation of the kernel, launched only for such K).
+// instantiation of the kernel, launched only for such K); bit 6 = the same with
+// the partial k-tile first instead (the k origin moved back so that the first
+// k-tile holds the K mod BK leftover k and every later one is whole): its loads
+// and zero fill happen in the prologue, so the k loop carries nothing for it.
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
           int BK_ = 64, int GM_ = 8, int SCHED_ = 0, int FLAGS_ = 0>
 struct DirectCfg {
@@ -133,8 +136,9 @@ struct DirectCfg {
     static_assert(SCHED == 0 || SCHED == 2 || SCHED == 4, "scheduling policy 0, 2 or 4");
     static_assert(SCHED != 4 || (WM == 2 && WN == 4 && STAGES == 2 && (FLAGS & 8) == 0),
                   "ping-pong: two groups of four waves, two stages, no early-load flag");
-    static_assert((FLAGS & ~62) == 0, "flags: bits 1 to 5");
-    static_assert(SCHED != 4 || (FLAGS & 32) == 0, "ping-pong: whole k-tiles");
+    static_assert((FLAGS & ~126) == 0, "flags: bits 1 to 6");
+    static_assert(SCHED != 4 || (FLAGS & 96) == 0, "ping-pong: whole k-tiles");
+    static_assert((FLAGS & 96) != 96, "a partial k-tile first or last, not both");
 };
 
 // One operand's LDS image (BX rows of M or N by BK of k, EB-byte elements).
@@ -250,6 +254,32 @@ __device__ __forceinline__ uint32_t tail_offset(uint32_t voff, int q, int wave, 
     }
 }
 
+// A partial first k-tile (flag bit 6): the k origin sits `shift` = BK - K mod BK
+// elements before k = 0, so the chunks (row image) or k-rows (k-row image) of
+// the first k-tile that start below `shift` lie before the operand.  Whether
+// the chunk that lane fetches in its q-th load is inside (K is a whole number of
+// chunks, so a chunk is wholly before k = 0 or wholly after it).
+template <class O>
+__device__ __forceinline__ bool head_valid(int q, int wave, int lane, int nw, int shift) {
+    const int r = O::RPI * (wave + q * nw) + lane / O::CH;
+    if constexpr (O::ROWS) return ((lane % O::CH) ^ swz_a<O::CH>(r)) * O::EPC >= shift;
+    return r >= shift;
+}
+// The lane's offset for the first k-tile: a chunk or k-row before k = 0 is
+// replaced by the one at k = 0, so the load stays inside the operand; its LDS
+// slot is zeroed once the load has landed.
+template <class O>
+__device__ __forceinline__ uint32_t head_offset(uint32_t voff, int q, int wave, int lane, int nw,
+                                                int shift, int64_t ld) {
+    const int r = O::RPI * (wave + q * nw) + lane / O::CH;
+    if constexpr (O::ROWS) {
+        const int chunk = (lane % O::CH) ^ swz_a<O::CH>(r), first = shift / O::EPC;
+        return chunk < first ? voff + static_cast<uint32_t>((first - chunk) * 16) : voff;
+    } else {
+        return r < shift ? voff + static_cast<uint32_t>((shift - r) * ld * (16 / O::EPC)) : voff;
+    }
+}
+
 // A wave-uniform address, moved to scalar registers (the direct loads take
 // their base from an SGPR pair).
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
@@ -310,7 +340,8 @@ __device__ __forceinline__ void wait_then_barrier() {
 // TA: A given transposed (stored K x M); TB: B given transposed (stored N x K).
 // KTAIL: K ends inside the last k-tile (configurations with flag bit 5 only; a
 // separate instantiation, so products with whole k-tiles run code without it).
-template <class Cfg, bool GEN, bool TA, bool TB, bool KTAIL = false>
+// KHEAD: the same with the partial k-tile first (flag bit 6).
+template <class Cfg, bool GEN, bool TA, bool TB, bool KTAIL = false, bool KHEAD = false>
 __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     int64_t M, int64_t N, int64_t K, const typename Cfg::E* __restrict__ A, int64_t lda,
     const typename Cfg::E* __restrict__ B, int64_t ldb, Epi out, int tiles_m, int tiles_n) {
@@ -348,11 +379,20 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     uint32_t a_voff[OA::PER], b_voff[OB::PER];
     direct_offsets<OA>(a_voff, wave, lane, NW, m0, ext_a, lda);
     direct_offsets<OB>(b_voff, wave, lane, NW, n0, ext_b, ldb);
-    // tile origins and the step from one k-tile to the next, in elements
-    const E* const a_tile = TA ? A + m0 : A + m0 * lda;
-    const E* const b_tile = TB ? B + n0 * ldb : B + n0;
+    // KHEAD: the k origin moves back by `shift` elements, so that k-tile kt
+    // covers k in [kt BK - shift, (kt + 1) BK - shift): the first k-tile holds
+    // the K mod BK leftover k (the rest of its image is zeroed, see zero_head)
+    // and every later one is whole, ending at K exactly.
+    static_assert(!KHEAD || (!KTAIL && (Cfg::FLAGS & 64) != 0 && Cfg::SCHED != 4),
+                  "a partial first k-tile only where flag bit 6 asks for it");
+    const int shift = KHEAD ? static_cast<int>((BK - K % BK) % BK) : 0;
+    // tile origins and the step from one k-tile to the next, in elements (with
+    // KHEAD the origin is a k position before the operand; only offsets that
+    // land inside it are ever added to it)
     const int64_t a_step = TA ? BK * lda : BK;
     const int64_t b_step = TB ? BK : BK * ldb;
+    const E* const a_tile = (TA ? A + m0 : A + m0 * lda) - (KHEAD ? shift * a_step / BK : 0);
+    const E* const b_tile = (TB ? B + n0 * ldb : B + n0) - (KHEAD ? shift * b_step / BK : 0);
 
     // KTAIL: K is not a multiple of the k-tile; the last k-tile holds `tail` of
     // its BK k, and the rest of its LDS image is zeroed (zero_tail) before it is
@@ -404,6 +444,32 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
 #pragma unroll
         for (int q = 0; q < OB::PER; ++q)
             if (!tail_valid<OB>(q, wave, lane, NW, tail))
+                *(MIGEMM_LDS u32x4*)(st + Cfg::STAGE_A + (wave + q * NW) * 1024 + 16 * lane) =
+                    u32x4{0u, 0u, 0u, 0u};
+    };
+    // KHEAD: k-tile 0's loads into stage 0, a chunk or k-row before k = 0
+    // replaced by the one at k = 0 (offsets computed here, in the prologue, and
+    // not kept), and the zero fill of those slots once the loads have landed.
+    auto issue_head = [&]() __attribute__((always_inline)) {
+        const uint32_t sa = lds_addr, sb = sa + Cfg::STAGE_A;
+#pragma unroll
+        for (int q = 0; q < OA::PER; ++q)
+            dma16(sa + (wave + q * NW) * 1024, a_tile,
+                  head_offset<OA>(a_voff[q], q, wave, lane, NW, shift, lda));
+#pragma unroll
+        for (int q = 0; q < OB::PER; ++q)
+            dma16(sb + (wave + q * NW) * 1024, b_tile,
+                  head_offset<OB>(b_voff[q], q, wave, lane, NW, shift, ldb));
+    };
+    auto zero_head = [&]() __attribute__((always_inline)) {
+        MIGEMM_LDS char* const st = (MIGEMM_LDS char*)smem;
+#pragma unroll
+        for (int q = 0; q < OA::PER; ++q)
+            if (!head_valid<OA>(q, wave, lane, NW, shift))
+                *(MIGEMM_LDS u32x4*)(st + (wave + q * NW) * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < OB::PER; ++q)
+            if (!head_valid<OB>(q, wave, lane, NW, shift))
                 *(MIGEMM_LDS u32x4*)(st + Cfg::STAGE_A + (wave + q * NW) * 1024 + 16 * lane) =
                     u32x4{0u, 0u, 0u, 0u};
     };
@@ -985,13 +1051,28 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     static_assert((kPro - 1) * NI <= 63, "vmcnt counts at most 63 loads");
 #pragma unroll
     for (int t = 0; t < kPro; ++t)
-        if (t < KT) issue(t);
-    if (KT == 1)
+        if (t < KT) {
+            if (KHEAD && t == 0)
+                issue_head();
+            else
+                issue(t);
+        }
+    if constexpr (KHEAD) {
+        // k-tile 0 has landed (later ones may still fly); its slots before
+        // k = 0 are zeroed before any wave reads it
+        if (KT >= kPro)
+            vm_wait<(kPro - 1) * NI>();
+        else
+            vm_wait<0>();
+        zero_head();
+        lds_wait_then_barrier();
+    } else if (KT == 1) {
         land_last(std::integral_constant<int, 0>{});
-    else if (KT >= kPro)
+    } else if (KT >= kPro) {
         wait_then_barrier<(kPro - 1) * NI>();
-    else
+    } else {
         wait_then_barrier<0>();
+    }
 
     // Two fragment buffers: slab s of every k-tile runs from F[s & 1] while the
     // next slab's fragments load into the other (SLABS is even, so slab 0 of
@@ -1076,13 +1157,18 @@ inline bool direct_ok(const GemmArgs& g, int kq, bool layouts, int epc = 8) {
            (g.ta ? g.lda < krow_ld : g.lda < row_ld) && (g.tb ? g.ldb < row_ld : g.ldb < krow_ld);
 }
 
-// direct_ok for configuration D: K a whole number of chunks with flag bit 5,
-// of k-tiles without.  The ping-pong schedule also needs whole tiles: its
-// successive loads of a row image step whole image rows from the first one,
-// with no clamp at the matrix edge.
+// direct_ok for configuration D: K a whole number of chunks with flag bit 5 or
+// 6, of k-tiles without (with bit 6 a whole number of chunks in every operand,
+// zero-filled copies included: the first k-tile's split falls between chunks).
+// The ping-pong schedule also needs whole tiles: its successive loads of a row
+// image step whole image rows from the first one, with no clamp at the matrix
+// edge.
 template <class D>
 bool direct_fits(const GemmArgs& g) {
-    return direct_ok(g, (D::FLAGS & 32) ? 16 / D::EB : D::BK, D::LAYOUTS, 16 / D::EB) &&
+    constexpr int kEpc = 16 / D::EB;
+    const bool ragged = (D::FLAGS & 96) != 0;
+    return direct_ok(g, ragged ? kEpc : D::BK, D::LAYOUTS, kEpc) &&
+           (!(D::FLAGS & 64) || g.K % kEpc == 0) &&
            (D::SCHED != 4 || (g.M % D::BM == 0 && g.N % D::BN == 0));
 }
 
@@ -1096,14 +1182,17 @@ hipError_t launch_direct_cfg(const GemmArgs& g) {
     const E* A = static_cast<const E*>(g.A);
     const E* B = static_cast<const E*>(g.B);
     const int itm = static_cast<int>(tm), itn = static_cast<int>(tn);
-    // the partial-last-k-tile instantiation only where K ends inside a k-tile
-    constexpr bool kRagged = (Cfg::FLAGS & 32) != 0;
-    const bool ktail = kRagged && g.K % Cfg::BK != 0;
+    // the partial-k-tile instantiation (last with flag bit 5, first with bit 6)
+    // only where K ends inside a k-tile
+    constexpr bool kTail = (Cfg::FLAGS & 32) != 0, kHead = (Cfg::FLAGS & 64) != 0;
+    const bool ragged = (kTail || kHead) && g.K % Cfg::BK != 0;
 #define MIGEMM_LAUNCH(TA_, TB_)                                                                \
-    return ktail ? launch_kernel(g, mfma16_direct_kernel<Cfg, GEN, TA_, TB_, kRagged>, grid,   \
-                                 block, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn)    \
-                 : launch_kernel(g, mfma16_direct_kernel<Cfg, GEN, TA_, TB_, false>, grid,     \
-                                 block, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, itn)
+    return ragged ? launch_kernel(g, mfma16_direct_kernel<Cfg, GEN, TA_, TB_, kTail, kHead>,  \
+                                  grid, block, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, \
+                                  itn)                                                        \
+                  : launch_kernel(g, mfma16_direct_kernel<Cfg, GEN, TA_, TB_, false, false>,  \
+                                  grid, block, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, \
+                                  itn)
     if constexpr (Cfg::LAYOUTS) {
         if (g.ta && g.tb)
             MIGEMM_LAUNCH(true, true);

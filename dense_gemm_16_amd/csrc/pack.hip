@@ -175,12 +175,13 @@ hipError_t launch_pack16(const GemmArgs& g, const PackJob& j0, const PackJob& j1
 
 // The direct configuration that packed configuration pc (11 or 12) runs.  11:
 // the 256x256 ping-pong kernel on whole tiles and whole k-tiles (configuration
-// 14), the 256x256 interleaved one (10) on other shapes with whole k-tiles, and
-// the 128x256 one (13, which zero-fills a partial last k-tile) when K is not a
-// multiple of 64.  12: the 128x128 one (7, with the partial k-tile too).
+// 14), else the 256x256 interleaved one (10, which runs a partial first k-tile
+// when K is whole 16-byte chunks), else the 128x256 one (13, which zero-fills a
+// partial last k-tile and reads a copy's zero-filled last chunk).  12: the
+// 128x128 one (7, with the partial last k-tile too).
 int inner_config(const GemmArgs& g, int pc) {
     if (pc == 12) return 7;
-    if (g.K % 64 != 0) return 13;
+    if (g.K % 64 != 0) return g.K % 8 == 0 ? 10 : 13;
     return (g.M % 256 == 0 && g.N % 256 == 0) ? 14 : 10;
 }
 

@@ -254,9 +254,10 @@ def test_selection_packs_unreadable_16bit_operands():
     sel = lambda M, N, K, dt, lda, ldb: mg.migemm_select(M, N, K, dt, None, lda, None, ldb, None, N)
     big = 1 << 40
     assert _selected(2050, 2047, 2056, 1, 2056, 2047, big) == ("mfma16", 12)
-    # aligned with K = 8200: the 128x256 direct kernel reads it in place; with an
-    # odd ldb the copies are padded to K' = 8256 for the 256x256 ping-pong kernel
-    assert _selected(8192, 8192, 8200, 2, 8200, 8192, big) == ("mfma16", 13)
+    # aligned with K = 8200: the 256x256 direct kernel reads it in place, its
+    # first k-tile the partial one; with an odd ldb the copies are padded to
+    # K' = 8256 for the 256x256 ping-pong kernel
+    assert _selected(8192, 8192, 8200, 2, 8200, 8192, big) == ("mfma16", 10)
     assert _selected(8192, 8192, 8200, 2, 8200, 8193, big) == ("mfma16", 11)
     assert _selected(2048, 2048, 2056, 2, 2056, 2048, big) == ("mfma16", 7)
     assert _selected(4096, 4096, 4096, 2, 4096, 4097, big) == ("mfma16", 11)

@@ -183,10 +183,11 @@ RAGGED_K_SHAPES = [(300, 264, 72, None, None), (1000, 520, 200, None, None),
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_direct_ragged_k(dtype):
-    """Direct-staged configurations that zero-fill a partial last k-tile: K a
-    multiple of the 16-byte chunk (8 elements, 4 for FP32) but not of the k-tile,
-    from one chunk (K = 8) to many k-tiles, with ragged M and N and padded leading
-    dimensions.  Every direct configuration runs each shape (those without the
+    """Direct-staged configurations that zero-fill a partial k-tile (the last one;
+    the first one for the 256x256 interleaved configuration 10): K a multiple of
+    the 16-byte chunk (8 elements, 4 for FP32) but not of the k-tile, from one
+    chunk (K = 8) to many k-tiles, with ragged M and N and padded leading
+    dimensions.  Every direct configuration runs each shape (those without a
     partial k-tile take the register-staged kernel)."""
     v = mg.REGTILE_MFMA if dtype == "f32" else mg.MFMA16
     names = [mg.migemm_config_name(v, c) for c in range(mg.migemm_config_count(v))]
@@ -207,12 +208,13 @@ def test_direct_ragged_k(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_direct_ragged_k_layouts_and_general_output(dtype):
-    """The partial last k-tile in every operand layout (row images and k-row
-    images both end inside it), with the general output step into a 16-bit C and
-    small integers compared bit for bit."""
+    """The partial k-tile in every operand layout (row images and k-row images
+    both end inside it; for configuration 10 both start inside its first
+    k-tile), with the general output step into a 16-bit C and small integers
+    compared bit for bit."""
     from gpu_helpers import check_ex, oracle_ref, padding_untouched, run_gemm_ex
     v = mg.REGTILE_MFMA if dtype == "f32" else mg.MFMA16
-    cfgs = (8, 10) if dtype == "f32" else (7, 13, 16)
+    cfgs = (8, 10) if dtype == "f32" else (7, 10, 13, 16)
     K = 100 if dtype == "f32" else 200
     M, N = 264, 136
     for kind in ("normal", "int"):
@@ -233,3 +235,25 @@ def test_direct_ragged_k_layouts_and_general_output(dtype):
                                                    config=c, ta=ta, tb=tb)
                         check_ex(C, A, B, dtype, 0.5, -1.0, 2, old, ref=ref)
                         assert padding_untouched(buf, mask)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_partial_first_k_tile_full_rounds(dtype):
+    """The 256x256 interleaved configuration selected for a K that ends inside a
+    k-tile: its first k-tile holds the K mod 64 leftover k (the rest of its LDS
+    image zero-filled in the prologue) and every later k-tile is whole.  Full
+    rounds of 256 workgroups, K from one chunk (a single, partial k-tile) to
+    several k-tiles with every leftover 8 .. 56, ragged M and N (the split of
+    the last bands runs after the whole tiles), compared with the oracle; small
+    integers bit for bit."""
+    from gpu_helpers import oracle_ref
+    for (M, N, K, dist) in [(4096, 4096, 8, "normal"), (4096, 4096, 200, "normal"),
+                            (4096, 4096, 136, "int"), (4100, 4104, 248, "normal"),
+                            (4096, 4096, 120, "int"), (4096, 4096, 328, "normal")]:
+        A, B = inputs.pair(M, N, K, dtype, dist, seed=M + N + K)
+        st, v, c = mg.migemm_select(M, N, K, inputs.DTYPE_CODES[dtype], None, K, None, N,
+                                    None, N)
+        assert st == mg.OK and (v, c) == (mg.MFMA16, 10), (v, c)
+        say(f"partial first k-tile {dtype} {M}x{N}x{K} {dist}")
+        C, _ = run_gemm(A, B, dtype)
+        check(C, A, B, dtype, exact=dist == "int", ref=oracle_ref(A, B, dtype))
