@@ -29,7 +29,7 @@ LIB = os.path.join(PKG, "libmigemm.so")
 RESOURCES = os.path.join(PKG, "kernel_resources.json")
 SOURCES = ["api.cpp", "mfma16.hip", "mfma_i8.hip", "regtile_mfma.hip", "naive.hip",
            "lds_tiled.hip", "regtile_valu.hip", "fill.hip", "convert.hip", "pack.hip",
-           "noalloc.hip", "skinny.hip", "split.cpp"]
+           "noalloc.hip", "skinny.hip", "split.cpp", "splitk.hip"]
 # The configuration tables' kernels are built from *_part.hip sources, once per
 # configuration (and element type and output form), so that the compiles run in
 # parallel and a change rebuilds only what it touches.

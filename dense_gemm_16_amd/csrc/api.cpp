@@ -28,6 +28,11 @@ constexpr int64_t kMaxLd = int64_t(1) << 32;  // leading dimensions must be belo
 // M * N * K from which a 16-bit product the direct kernel cannot read in place
 // is run on packed copies (pack.hip) rather than by the register-staged kernel.
 constexpr double kPackMinWork = 134217728.0;  // 2^27, e.g. 512^3
+// Shortest K for split-K: below it the second launch and the slices' FP32 sums
+// cost more than the longer walk of K by the 64x64 tile (BF16, 512 x 512 and
+// 1024 x 1024: 16.6 against 20.8 and 19.4 us at K = 4096; 23.3 against 21.6 and
+// 23.5 against 21.7 us at K = 6144).
+constexpr int64_t kSplitKMinK = 6144;
 
 struct Variant {
     const char* name;
@@ -175,6 +180,13 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
                       packed_k(M > N ? M : N) < (int64_t(1) << 23) &&
                       packed16_workspace_ok(g, pc);
     const bool whole256 = M % 256 == 0 && N % 256 == 0;
+    // split-K (splitk.hip): a k-sum long beside a product of few 128x128 tiles,
+    // where a workspace for the slices' FP32 sums is lent
+    const bool splitk = direct && tiles(128, 128) < 256 && K >= kSplitKMinK &&
+                        K >= 4 * (M > N ? M : N) && splitk16_workspace_bytes(g) > 0 &&
+                        g.ws != nullptr &&
+                        reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
+                        g.ws_bytes >= splitk16_workspace_bytes(g);
     if (direct && ktiles && tiles(256, 256) >= 256 && whole256)
         config = 14;  // direct 256x256x64, ping-pong wave groups (whole tiles only)
     else if (direct && tiles(256, 256) >= 256)
@@ -186,6 +198,8 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
         config = 13;  // direct 128x256x64, 8 waves of 64x64, 3 stages
     else if (direct && tiles(128, 128) >= 256)
         config = 7;   // direct 128x128x64, 8 waves, 4 stages, interleaved
+    else if (splitk)
+        config = 17;  // slices of K on the direct 128x128 tile, then their sum
     else if (direct)
         config = 16;  // direct 64x64x64, 8 waves: four times the workgroups (e.g. 1024^3)
     else if (pack)
@@ -248,8 +262,9 @@ hipError_t launch(const GemmArgs& g, int variant, int config) {
 // Workspace bytes the call's configuration uses when lent at least that many:
 // the packed FP16/BF16 configurations' copies, nothing for the others.
 int64_t config_workspace_bytes(const GemmArgs& g, int variant, int config) {
-    if (variant != MIGEMM_MFMA16 || (config != 11 && config != 12)) return 0;
+    if (variant != MIGEMM_MFMA16 || (config != 11 && config != 12 && config != 17)) return 0;
     if (g.M == 0 || g.N == 0 || g.K == 0) return 0;
+    if (config == 17) return splitk16_workspace_bytes(g);
     return packed16_workspace_bytes(g, config);
 }
 

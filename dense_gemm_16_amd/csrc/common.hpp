@@ -67,6 +67,10 @@ struct GemmArgs {
     // i], i.e. the call computes a block of C^T (the last columns of a product,
     // as B^T A^T).
     bool trans_c = false;
+    // Split-K (direct configurations with flag bit 7 only): the launch runs
+    // `splitk` slices of K (splitk_slice), slice y writing its plain FP32 sums to
+    // the y-th M x N block of out.C.  0 or 1: one ordinary launch.
+    int splitk = 0;
     // True unless the output step is the plain FP32 overwrite.
     bool general() const { return !(out.alpha == 1.0f && out.beta == 0.0f && out.c_dtype == 0); }
 };
@@ -96,6 +100,13 @@ hipError_t launch_kernel(const GemmArgs& g, void (*fn)(P...), dim3 grid, dim3 bl
 inline bool c_whole_lines(const Epi& o) {
     const int64_t eb = (o.c_dtype == 1 || o.c_dtype == 2) ? 2 : 4;
     return (o.ldc * eb) % 128 == 0 && (reinterpret_cast<uintptr_t>(o.C) & 127) == 0;
+}
+
+// Split-K: the k extent of each of `slices` slices of K, whole 64-deep k-tiles
+// (the last slice takes what is left).  With slices = ceil(K / splitk_slice(K,
+// s)) slices, every slice is non-empty and this gives the same extent again.
+__host__ __device__ inline int64_t splitk_slice(int64_t K, int64_t slices) {
+    return (K + slices - 1) / slices + 63 - ((K + slices - 1) / slices + 63) % 64;
 }
 
 // Storage of a bfloat16 element: its 16 bits.
@@ -231,6 +242,12 @@ int64_t packed_k(int64_t K);
 // Alignment the packed path asks of a workspace.
 constexpr int64_t kWorkspaceAlign = 256;
 hipError_t launch_mfma_i8(const GemmArgs& a, int config);
+// FP16/BF16 products as slices of K on the 128x128 direct tile into FP32
+// partial sums in the caller's workspace, then a reduction that sums them in
+// slice order and applies the output step (splitk.hip).
+int64_t splitk16_slices(const GemmArgs& g);
+int64_t splitk16_workspace_bytes(const GemmArgs& g);
+hipError_t launch_splitk16(const GemmArgs& g);
 // FP32, FP16 and BF16 products with 1 <= M <= 16, K split over the waves of
 // each workgroup (skinny.hip); skinny_fits says whether its alignment and
 // whole-chunk needs hold (hipErrorInvalidValue from the launcher otherwise).

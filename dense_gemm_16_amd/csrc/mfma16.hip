@@ -48,7 +48,8 @@ const char* const kNames[] = {
     "direct 128x256x64 8w 16x16x32 s3 ilv",
     "direct 256x256x64 8w 16x16x32 gm4 pingpong ntC agpr",
     "direct 128x256x64 8w 16x16x32 gm8 pingpong ntC agpr",
-    "direct 64x64x64 8w 16x16x32 s4 early ntC"};
+    "direct 64x64x64 8w 16x16x32 s4 early ntC",
+    "split-K: slices of K on config 7 into FP32 partials in the workspace, then their sum"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 template <typename E, bool GEN>
@@ -90,6 +91,14 @@ bool split_tile(int config, int64_t& bm, int64_t& bn) {
 }  // namespace
 
 hipError_t launch_mfma16(const GemmArgs& g, int config) {
+    if (config == 17) {
+        // without a usable workspace the ordinary 128x128 launch
+        const int64_t need = splitk16_workspace_bytes(g);
+        if (need == 0 || g.ws == nullptr ||
+            (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 || g.ws_bytes < need)
+            return launch_mfma16(g, 7);
+        return launch_splitk16(g);
+    }
     if (config == 11 || config == 12) {
         const int fallback = ceil_div(g.M, 128) * ceil_div(g.N, 128) >= 256 ? 2 : 3;
         return launch_packed16(g, config, fallback);

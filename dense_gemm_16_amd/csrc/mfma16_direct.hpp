@@ -105,7 +105,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // instantiation of the kernel, launched only for such K); bit 6 = the same with
 // the partial k-tile first instead (the k origin moved back so that the first
 // k-tile holds the K mod BK leftover k and every later one is whole): its loads
-// and zero fill happen in the prologue, so the k loop carries nothing for it.
+// and zero fill happen in the prologue, so the k loop carries nothing for it;
+// bit 7 = also compiled for split-K slices (GemmArgs::splitk).
 template <typename E_, int BM_, int BN_, int WM_, int WN_, int MF_, int STAGES_ = 2,
           int BK_ = 64, int GM_ = 8, int SCHED_ = 0, int FLAGS_ = 0>
 struct DirectCfg {
@@ -136,9 +137,11 @@ struct DirectCfg {
     static_assert(SCHED == 0 || SCHED == 2 || SCHED == 4, "scheduling policy 0, 2 or 4");
     static_assert(SCHED != 4 || (WM == 2 && WN == 4 && STAGES == 2 && (FLAGS & 8) == 0),
                   "ping-pong: two groups of four waves, two stages, no early-load flag");
-    static_assert((FLAGS & ~126) == 0, "flags: bits 1 to 6");
+    static_assert((FLAGS & ~254) == 0, "flags: bits 1 to 7");
     static_assert(SCHED != 4 || (FLAGS & 96) == 0, "ping-pong: whole k-tiles");
     static_assert((FLAGS & 96) != 96, "a partial k-tile first or last, not both");
+    static_assert((FLAGS & 128) == 0 || ((FLAGS & 16) != 0 && SCHED != 4),
+                  "split-K slices: every layout, interleaved schedules");
 };
 
 // One operand's LDS image (BX rows of M or N by BK of k, EB-byte elements).
@@ -341,10 +344,28 @@ __device__ __forceinline__ void wait_then_barrier() {
 // KTAIL: K ends inside the last k-tile (configurations with flag bit 5 only; a
 // separate instantiation, so products with whole k-tiles run code without it).
 // KHEAD: the same with the partial k-tile first (flag bit 6).
-template <class Cfg, bool GEN, bool TA, bool TB, bool KTAIL = false, bool KHEAD = false>
+// SPLITK: the grid is tiles x slices workgroups; workgroup w (renumbered
+// XCD-contiguous, so that one XCD takes whole slices, whose tiles share rows of
+// A and columns of B in its L2) takes tile w mod tiles of slice w / tiles of K
+// (whole 64-deep k-tiles, the last slice the rest, see splitk_slice) and writes
+// its FP32 sums, plain, to that slice's M x N block of out.C (leading dimension
+// N): the partial products that a reduction then sums.
+template <class Cfg, bool GEN, bool TA, bool TB, bool KTAIL = false, bool KHEAD = false,
+          bool SPLITK = false>
 __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     int64_t M, int64_t N, int64_t K, const typename Cfg::E* __restrict__ A, int64_t lda,
     const typename Cfg::E* __restrict__ B, int64_t ldb, Epi out, int tiles_m, int tiles_n) {
+    int tile = blockIdx.x;
+    if constexpr (SPLITK) {
+        const int tiles = tiles_m * tiles_n;
+        const int id = xcd_contiguous(blockIdx.x, gridDim.x), slice = id / tiles;
+        tile = id - slice * tiles;
+        const int64_t ks = splitk_slice(K, gridDim.x / tiles), k0 = slice * ks;
+        A += TA ? k0 * lda : k0;
+        B += TB ? k0 : k0 * ldb;
+        K = K - k0 < ks ? K - k0 : ks;
+        out.C = static_cast<float*>(out.C) + slice * M * N;
+    }
     using E = typename Cfg::E;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, MF = Cfg::MF, TM = Cfg::TM, TN = Cfg::TN;
     constexpr int NW = Cfg::NW, S = Cfg::STAGES, BK = Cfg::BK;
@@ -367,7 +388,10 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
     const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
 
     int pm, pn;
-    tile_coords<Cfg::GM>(blockIdx.x, tiles_m, tiles_n, pm, pn);
+    if constexpr (SPLITK)
+        band_coords<Cfg::GM>(tile, tiles_m, tiles_n, pm, pn);
+    else
+        tile_coords<Cfg::GM>(tile, tiles_m, tiles_n, pm, pn);
     const int64_t m0 = static_cast<int64_t>(pm) * BM;
     const int64_t n0 = static_cast<int64_t>(pn) * BN;
 
@@ -1186,6 +1210,34 @@ hipError_t launch_direct_cfg(const GemmArgs& g) {
     // only where K ends inside a k-tile
     constexpr bool kTail = (Cfg::FLAGS & 32) != 0, kHead = (Cfg::FLAGS & 64) != 0;
     const bool ragged = (kTail || kHead) && g.K % Cfg::BK != 0;
+    if constexpr ((Cfg::FLAGS & 128) != 0 && !GEN) {
+        // split-K slices: tiles x slices workgroups; every slice but the last
+        // is whole k-tiles, so the last decides the instantiation
+        if (g.splitk > 1) {
+            if (tm * tn * g.splitk > 0x7fffffff) return hipErrorInvalidValue;
+            const dim3 sgrid(static_cast<unsigned>(tm * tn * g.splitk));
+#define MIGEMM_SPLIT(TA_, TB_)                                                                 \
+    return ragged ? launch_kernel(g, mfma16_direct_kernel<Cfg, false, TA_, TB_, kTail, kHead,  \
+                                                          true>,                                \
+                                  sgrid, block, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, \
+                                  itn)                                                         \
+                  : launch_kernel(g, mfma16_direct_kernel<Cfg, false, TA_, TB_, false, false,  \
+                                                          true>,                                \
+                                  sgrid, block, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, \
+                                  itn)
+            if (g.ta && g.tb)
+                MIGEMM_SPLIT(true, true);
+            else if (g.ta)
+                MIGEMM_SPLIT(true, false);
+            else if (g.tb)
+                MIGEMM_SPLIT(false, true);
+            else
+                MIGEMM_SPLIT(false, false);
+#undef MIGEMM_SPLIT
+        }
+    } else {
+        if (g.splitk > 1) return hipErrorInvalidValue;  // not compiled for slices
+    }
 #define MIGEMM_LAUNCH(TA_, TB_)                                                                \
     return ragged ? launch_kernel(g, mfma16_direct_kernel<Cfg, GEN, TA_, TB_, kTail, kHead>,  \
                                   grid, block, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.out, itm, \

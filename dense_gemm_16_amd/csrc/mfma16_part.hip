@@ -22,8 +22,8 @@ template <typename E> struct Cfgs {
     // direct-staged: <E, BM, BN, WM, WN, MF, STAGES, BK, GM, SCHED, FLAGS>
     using D5 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64>;
     using D6 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64>;
-    using D7 = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 50>;   // 8 waves, interleave, gm4, nt C; all layouts; ragged K
-    using D7P = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 48>;  // D7 with plain C stores
+    using D7 = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 178>;  // 8 waves, interleave, gm4, nt C; all layouts; ragged K; split-K
+    using D7P = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 176>; // D7 with plain C stores
     using D8 = DirectCfg<E, 128, 128, 2, 2, 16, 4, 64>;             // 4 waves, 4 stages
     using D9 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 2>;    // gm4, interleave, nt C
     using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 94>;  // + AGPRs, early loads; all layouts; partial first k-tile

@@ -206,19 +206,30 @@ template <> struct Transpose<4> {  // 32-bit elements
     }
 };
 
-// Tile (pm, pn) processed by workgroup `bid`: XCD-contiguous ranges, GM-row bands.
-template <int GM>
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& pm, int& pn) {
-    const int total = tiles_m * tiles_n;
+// Workgroup `bid` of `total` renumbered so that each XCD (bid modulo 8, the
+// round-robin order in which workgroups are dealt to the XCDs) takes one
+// contiguous range of the new numbers; the last total mod 8 keep theirs.
+__device__ __forceinline__ int xcd_contiguous(int bid, int total) {
     const int per = total / kNumXcd;
-    int id = bid;
-    if (bid < per * kNumXcd) id = (bid % kNumXcd) * per + bid / kNumXcd;
+    return bid < per * kNumXcd ? (bid % kNumXcd) * per + bid / kNumXcd : bid;
+}
+
+// Tile (pm, pn) number `id` in GM-row bands: GM tile rows at a time, down the
+// rows of a band, then across its columns.
+template <int GM>
+__device__ __forceinline__ void band_coords(int id, int tiles_m, int tiles_n, int& pm, int& pn) {
     const int band = GM * tiles_n;
     const int first_m = (id / band) * GM;
     const int gm = min(tiles_m - first_m, GM);
     const int in = id % band;
     pm = first_m + in % gm;
     pn = in / gm;
+}
+
+// Tile (pm, pn) processed by workgroup `bid`: XCD-contiguous ranges, GM-row bands.
+template <int GM>
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& pm, int& pn) {
+    band_coords<GM>(xcd_contiguous(bid, tiles_m * tiles_n), tiles_m, tiles_n, pm, pn);
 }
 
 // One operand's staging: a BX x BK tile (BX rows of M or N, BK of k) from global
@@ -453,6 +464,7 @@ __global__ __launch_bounds__(Cfg::NT) void mfma_gemm_kernel(
 // plain FP32 overwrite (GEN == false) or the general output step.
 template <class Cfg, bool GEN>
 hipError_t launch_mfma_cfg(const GemmArgs& g) {
+    if (g.splitk > 1) return hipErrorInvalidValue;  // split-K runs on the direct kernel only
     using E = typename Cfg::E;
     constexpr int VEC = Cfg::VEC;
     const int64_t tm = ceil_div(g.M, Cfg::BM), tn = ceil_div(g.N, Cfg::BN);

@@ -9,9 +9,10 @@
 // device current) and kept; host code passes that address, never the array's
 // name, to the kernels.  No allocating call is made.
 //
-// Calls on one GPU share its array, which keeps the last call's contents: the
-// only user (the packed FP16/BF16 path) overwrites every byte it reads, zero
-// padding included, so nothing needs clearing.  Calls that overlap in time on
+// Calls on one GPU share its array, which keeps the last call's contents: its
+// users (the packed FP16/BF16 path, and split-K, whose slices each write their
+// whole M x N block of sums before the sum kernel reads them) overwrite every
+// byte they read, zero padding included, so nothing needs clearing.  Calls that overlap in time on
 // one GPU (two streams, or two host threads) race on the array.
 #include <mutex>
 

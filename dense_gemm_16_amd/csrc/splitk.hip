@@ -1,0 +1,101 @@
+// splitk.hip -- FP16/BF16 products whose M x N is small beside K: the sum over
+// k split into slices.
+//
+// C = A x B (page "CUDA-Practice 09", the definition of the row-major product)
+// is, element by element, the sum over k of A[i][k] B[k][j]; the sum splits
+// into slices of k, each summed on its own and the slice sums added.  With
+// 512 x 512 and K = 65536 the 128x128 tile gives 16 workgroups for 256 CUs, each
+// walking all of K; as 16 slices of 4096 (whole 64-deep k-tiles, the last slice
+// what is left) the same launch runs 256 workgroups, 16 per slice, each
+// writing its FP32 sums plainly to its slice's M x N block of the caller's
+// workspace.  A second kernel adds the slices of each element in slice order
+// (so the result does not depend on timing) and applies the output step
+// (alpha, beta, 16-bit C) to the total.  Both launch on the call's stream.
+//
+// The workgroups are renumbered so that each XCD takes whole slices: the tiles
+// of one slice share its rows of A and columns of B in that XCD's L2, and each
+// operand element is read from HBM about once (512 x 512 x 65536 BF16: 45 us,
+// against 69 us with the slices spread over all eight XCDs and 217 us for the
+// 64x64 tile without slices).
+//
+// Used where a workspace is lent (slices x M x N x 4 bytes), the operands suit
+// the direct kernel, K is at least 6144 and 4 max(M, N), and the 128x128 tile
+// would not fill a round of 256 workgroups.
+#include "mfma16_configs.hpp"
+#include "mfma16_direct.hpp"
+
+namespace migemm {
+namespace {
+
+constexpr int kThreads = 256;
+
+// out[idx] for 4 consecutive elements per work-item of the M x N result:
+// the sum of part[s][idx], s = 0 .. S - 1 in order, then the output step.
+template <bool GEN>
+__global__ __launch_bounds__(kThreads) void splitk_reduce(const float* __restrict__ part, int S,
+                                                          int64_t M, int64_t N, Epi out) {
+    const int64_t MN = M * N;
+    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
+    if (i0 >= MN) return;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (i0 + 4 <= MN && MN % 4 == 0) {  // 16-byte aligned in every slice
+        for (int s = 0; s < S; ++s) {
+            const f32x4 p = *reinterpret_cast<const f32x4*>(part + s * MN + i0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += p[e];
+        }
+    } else {
+        for (int s = 0; s < S; ++s)
+            for (int e = 0; i0 + e < MN; ++e) v[e] += part[s * MN + i0 + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + e;
+        if (i < MN) store_out<GEN>(out, (i / N) * out.ldc + i % N, v[e]);
+    }
+}
+
+int64_t tiles128(const GemmArgs& g) { return ceil_div(g.M, 128) * ceil_div(g.N, 128); }
+
+}  // namespace
+
+// Slices of K for this product: enough rows of 128x128 workgroups for one
+// round of 256 (2 to 16 of them), fewer where K runs out of whole k-tiles.
+int64_t splitk16_slices(const GemmArgs& g) {
+    const int64_t t = tiles128(g);
+    int64_t s = t > 0 ? 256 / t : 0;
+    s = s < 2 ? 2 : s > 16 ? 16 : s;
+    return ceil_div(g.K, splitk_slice(g.K, s));
+}
+
+// slices x M x N FP32 sums; 0 where split-K does not apply (fewer than two
+// slices, or M x N beyond 2^30)
+int64_t splitk16_workspace_bytes(const GemmArgs& g) {
+    const int64_t s = splitk16_slices(g);
+    if (s < 2 || g.M * g.N > (int64_t(1) << 30)) return 0;
+    return s * g.M * g.N * 4;
+}
+
+hipError_t launch_splitk16(const GemmArgs& g) {
+    const int64_t S = splitk16_slices(g), need = splitk16_workspace_bytes(g);
+    if (need == 0 || S > 16 || g.ws == nullptr ||
+        (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 || g.ws_bytes < need)
+        return hipErrorInvalidValue;
+    // the slices run on the direct kernel only; operands it cannot read in
+    // place take the ordinary 128x128 path instead
+    if (!direct_ok(g, 8, true, 8) || g.K % 8 != 0) return launch_mfma16(g, 7);
+    GemmArgs p = g;
+    p.splitk = static_cast<int>(S);
+    p.out = Epi{g.ws, g.N, 1.0f, 0.0f, 0};  // FP32 slice sums, plain, leading dimension N
+    hipError_t e = launch_cfg16_any(p, 7);
+    if (e != hipSuccess) return e;
+    const int64_t groups = ceil_div(ceil_div(g.M * g.N, 4), kThreads);
+    const float* part = static_cast<const float*>(g.ws);
+    if (g.general())
+        return launch_kernel(g, splitk_reduce<true>, dim3(static_cast<unsigned>(groups)),
+                             dim3(kThreads), part, static_cast<int>(S), g.M, g.N, g.out);
+    return launch_kernel(g, splitk_reduce<false>, dim3(static_cast<unsigned>(groups)),
+                         dim3(kThreads), part, static_cast<int>(S), g.M, g.N, g.out);
+}
+
+}  // namespace migemm

@@ -285,6 +285,49 @@ def test_selection_packs_unreadable_16bit_operands():
     assert _selected(8192, 8192, 8192, 2, 8192, 8192, big) == ("mfma16", 14)
 
 
+def test_selection_split_k():
+    """FP16/BF16 products of fewer than 256 tiles of 128x128 with K at least 6144
+    and 4 max(M, N) run as slices of K (configuration 17) when a workspace for
+    the slices' FP32 sums is lent: slices x M x N x 4 bytes, as many slices as
+    fill a round of 256 workgroups (2 to 16), fewer where K runs out of whole
+    64-deep k-tiles; otherwise the 64x64 tile."""
+    big = 1 << 40
+    sel = lambda M, N, K: mg.migemm_select(M, N, K, mg.BF16, None, K, None, N, None, N)
+    assert _selected(512, 512, 65536, 2, 65536, 512, big) == ("mfma16", 17)
+    assert sel(512, 512, 65536) == (mg.OK, mg.MFMA16, 16)  # no workspace
+    assert _selected(512, 512, 65536, 2, 65536, 512, 16 * 512 * 512 * 4) == ("mfma16", 17)
+    assert _selected(512, 512, 65536, 2, 65536, 512, 16 * 512 * 512 * 4 - 1) == ("mfma16", 16)
+    assert _selected(1024, 1024, 6144, 1, 6144, 1024, big) == ("mfma16", 17)
+    assert _selected(1024, 1024, 6136, 1, 6136, 1024, big) == ("mfma16", 16)  # K < 6144
+    assert _selected(2048, 1024, 8184, 1, 8184, 1024, big) == ("mfma16", 16)  # K < 4 max(M, N)
+    assert _selected(2048, 2048, 65536, 1, 65536, 2048, big) == ("mfma16", 7)  # 256 tiles
+    assert _selected(512, 512, 65540, 1, 65540, 512, big) == ("mfma16", 12)  # K % 8: copies
+    ws = lambda M, N, K: mg.migemm_workspace_size(-1, -1, 0, 0, M, N, K, 2, None, K, None, N)
+    assert ws(512, 512, 65536) == (mg.OK, 16 * 512 * 512 * 4)
+    assert ws(1024, 1024, 65536) == (mg.OK, 4 * 1024 * 1024 * 4)
+    assert ws(128, 128, 4160) == (mg.OK, 0)  # K < 6144
+    # configuration 17 asked for: K = 4160 on one tile, 13 slices of 320
+    assert mg.migemm_workspace_size(mg.MFMA16, 17, 0, 0, 128, 128, 4160, 2, None, 4160, None,
+                                    128) == (mg.OK, 13 * 128 * 128 * 4)
+    assert ws(2048, 1024, 16384) == (mg.OK, 2 * 2048 * 1024 * 4)
+    # two launches: 16 tiles x 16 slices of the 128x128 kernel, then the sum
+    # (4 elements per work-item, 256 work-items per workgroup)
+    st, text = mg.migemm_describe_ex(-1, -1, 0, 0, 512, 512, 65536, mg.BF16, None, 65536, None,
+                                     512, 0, 512, big)
+    d = mg._parse_description(text)
+    assert st == mg.OK and d["launches"] == 2 and d["grid0"] == 256 and d["block0"] == 512
+    assert d["grid1"] == 512 * 512 // 4 // 256 and d["block1"] == 256
+    # K = 8200 on 6 tiles: 15 slices of 576 (the last 136 deep)
+    d = mg.describe(mg.MFMA16, 17, 0, 0, 264, 200, 8200, mg.BF16, None, 8200, None, 200, 0, 200,
+                    big)
+    assert d["launches"] == 2 and d["grid0"] == 6 * 15
+    assert d["workspace_bytes"] == 15 * 264 * 200 * 4
+    # configuration 17 without a workspace: the 128x128 launch alone
+    d = mg.describe(mg.MFMA16, 17, 0, 0, 264, 200, 8200, mg.BF16, None, 8200, None, 200, 0, 200,
+                    0)
+    assert d["launches"] == 1 and d["grid0"] == 6
+
+
 def test_fp32_selection():
     sel = lambda M, N, K, lda, ldb: mg.migemm_select(M, N, K, mg.F32, None, lda, None, ldb, None, N)
     # direct-staged FP32: 64x64 tiles below a round of 128x128 tiles, 128x128 above

@@ -1,0 +1,125 @@
+"""Split-K (FP16/BF16 configuration 17): products whose M x N is a few 128x128
+tiles and whose K is long are summed as slices of K, one row of workgroups per
+slice writing FP32 sums into the lent workspace, then a second kernel adds the
+slices in order and applies the output step.  Compared element by element with
+the oracle: every layout, a K that ends inside a k-tile (only the last slice is
+partial), fewer slices than asked for where K runs out of whole k-tiles, the
+general output step into 16-bit C with a padded leading dimension, and the long
+products the selection sends here.  The result must not
+depend on timing: two calls give the same bits.  Without a workspace the
+configuration runs the ordinary 128x128 launch.
+"""
+import pytest
+import torch
+
+import dense_gemm_16_amd as mg
+from dense_gemm_16_amd import inputs
+from gpu_helpers import (DT_CODE, check_ex, oracle_ref, padding_untouched, run_gemm_ex, say,
+                         to_device_with_ld)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
+
+
+def _describe(M, N, K, dtype, ta, tb, lda, ldb, ws_bytes):
+    st, text = mg.migemm_describe_ex(-1, -1, int(ta), int(tb), M, N, K, DT_CODE[dtype], None,
+                                     lda, None, ldb, 0, N, ws_bytes)
+    assert st == mg.OK, text
+    return mg._parse_description(text)
+
+
+def _run(M, N, K, ta, tb, dtype="bf16", c_code=0, pad_c=0, config=17, seed=0):
+    A, B = inputs.pair(M, N, K, dtype, "normal", seed=seed + M + 3 * N + 5 * K + ta + 2 * tb)
+    ref = oracle_ref(A, B, dtype)
+    alpha, beta = (1.0, 0.0) if c_code == 0 else (-0.5, 1.25)
+    old = None
+    if c_code:
+        old = (torch.rand((M, N), generator=torch.Generator().manual_seed(K)) - 0.5).to(
+            {1: torch.float16, 2: torch.bfloat16}[c_code])
+    lda = M if ta else K
+    ldb = K if tb else N
+    say(f"splitk cfg={config} {'T' if ta else 'N'}{'T' if tb else 'N'} {M}x{N}x{K} {dtype} "
+        f"c_dtype={c_code} ldc=N+{pad_c}")
+    C, buf, mask = run_gemm_ex(A, B, dtype, alpha, beta, c_code, old, variant=mg.MFMA16,
+                               config=config, ta=ta, tb=tb, lda=lda, ldb=ldb, ldc=N + pad_c)
+    check_ex(C, A, B, dtype, alpha, beta, c_code, old, ref=ref)
+    assert padding_untouched(buf, mask)
+    return C
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_splitk_every_layout(ta, tb):
+    """256 x 256 x 16384: four tiles, 16 slices of 1024."""
+    d = _describe(256, 256, 16384, "bf16", ta, tb, 256 if ta else 16384, 16384 if tb else 256,
+                  1 << 30)
+    assert d["config"] == 17 and d["launches"] == 2 and d["grid0"] == 4 * 16
+    _run(256, 256, 16384, ta, tb)
+
+
+def test_splitk_ragged_k_and_fewer_slices():
+    """K = 8200 over 6 tiles: slices of 576, 15 of them, the last 136 deep (a
+    partial k-tile); K = 4160 on one tile: slices of 320, 13 of them; FP16 and
+    BF16, row and column counts that are not whole tiles."""
+    _run(264, 200, 8200, False, False)
+    _run(264, 200, 8200, True, True, dtype="f16")
+    _run(128, 128, 4160, False, True, dtype="f16")
+    _run(72, 40, 4104, True, False)
+
+
+def test_splitk_general_output():
+    """alpha * A x B + beta * C into FP16 and BF16 C with padded rows: the sum
+    kernel applies the output step to the total of the slices."""
+    _run(512, 384, 4096, False, False, c_code=1, pad_c=5)
+    _run(200, 328, 8192, True, False, dtype="f16", c_code=2, pad_c=8)
+    _run(384, 256, 4096, False, True, c_code=0, pad_c=3)
+
+
+def test_splitk_without_workspace_runs_the_128x128_launch():
+    A, B = inputs.pair(256, 256, 8192, "bf16", "normal", seed=11)
+    say("splitk cfg=17 without a workspace")
+    C, buf, mask = run_gemm_ex(A, B, "bf16", 1.0, 0.0, 0, None, variant=mg.MFMA16, config=17,
+                               ws=None)
+    check_ex(C, A, B, "bf16", 1.0, 0.0, 0, None)
+    assert padding_untouched(buf, mask)
+
+
+def test_splitk_same_bits_twice():
+    """The slices are added in a fixed order: two calls, the workspace poisoned in
+    between, give identical bits."""
+    M, N, K = 384, 256, 16384
+    A, B = inputs.pair(M, N, K, "f16", "normal", seed=12)
+    dA, _ = to_device_with_ld(A, K, 0)
+    dB, _ = to_device_with_ld(B, N, 0)
+    st, need = mg.migemm_workspace_size(-1, -1, 0, 0, M, N, K, 1, dA.data_ptr(), K,
+                                        dB.data_ptr(), N)
+    assert st == mg.OK and need == 16 * M * N * 4
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    out = []
+    for r in range(2):
+        ws.fill_(0xFF)  # NaN in every FP32 slot
+        C = torch.full((M, N), float("nan"), device="cuda")
+        say(f"splitk same bits: call {r}")
+        st = mg.migemm_gemm_ws(-1, -1, 0, 0, M, N, K, 1, dA.data_ptr(), K, dB.data_ptr(), N,
+                               1.0, 0.0, 0, C.data_ptr(), N, ws.data_ptr(), need, stream)
+        assert st == mg.OK
+        torch.cuda.synchronize()
+        out.append(C.cpu())
+    assert torch.equal(out[0].view(torch.int32), out[1].view(torch.int32))
+    check_ex(out[0], A, B, "f16", 1.0, 0.0, 0, None)
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(512, 512, 65536, "bf16"), (1024, 1024, 65536, "f16"),
+                                         (64, 64, 65536, "bf16"), (1000, 1016, 8200, "bf16")])
+def test_splitk_long_products(M, N, K, dtype):
+    """The long products the selection sends to split-K (16 slices of 4096; 4 of
+    16384; one tile in 16 slices; 64 tiles with a partial last k-tile), through
+    the automatic selection with the workspace it asks for; every element."""
+    d = _describe(M, N, K, dtype, False, False, K, N, 1 << 40)
+    assert d["config"] == 17, d
+    A, B = inputs.pair(M, N, K, dtype, "normal", seed=M + N + K)
+    say(f"splitk {M}x{N}x{K} {dtype} through the selection")
+    C, buf, mask = run_gemm_ex(A, B, dtype, 1.0, 0.0, 0, None)
+    check_ex(C, A, B, dtype, 1.0, 0.0, 0, None)
+    assert padding_untouched(buf, mask)

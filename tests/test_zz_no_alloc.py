@@ -4,7 +4,8 @@ both against the oracle.
 
 Two calls in a row on the packed path (ragged K, odd leading dimension of B),
 the second on a smaller product: it reuses the scratch array the first call
-filled, so any stale byte it read would show.  Then a product that needs no
+filled, so any stale byte it read would show; the same for split-K, whose
+slices' sums sit in the array.  Then a product that needs no
 scratch, and one that needs more than the array holds (rejected before any
 launch).
 """
@@ -51,6 +52,23 @@ def test_noalloc_matches_workspace_entry_point_twice():
             assert need < first, "the second product is the smaller one"
         first = need
         # same selection, same kernels, same summation order: identical bits
+        assert torch.equal(C_ws.view(torch.int32), C_na.view(torch.int32))
+        check_ex(C_na, A, B, dtype, 1.0, 0.0, 0, None)
+
+
+def test_noalloc_split_k_twice():
+    """Split-K keeps its slices' sums in the scratch array: two long products in a
+    row, the second smaller, each matching the workspace entry point bit for bit."""
+    first = None
+    for (M, N, K, dtype, seed) in [(512, 512, 16384, "bf16", 8), (264, 200, 8200, "f16", 9)]:
+        st, text = mg.migemm_describe_ex(-1, -1, 0, 0, M, N, K, DT_CODE[dtype], None, K, None, N,
+                                         0, N, mg.NOALLOC_SCRATCH_BYTES)
+        assert st == mg.OK and mg._parse_description(text)["config"] == 17
+        A, B, need, C_ws, C_na = _both(M, N, K, dtype, N, seed)
+        assert 0 < need <= mg.NOALLOC_SCRATCH_BYTES
+        if first is not None:
+            assert need < first, "the second product is the smaller one"
+        first = need
         assert torch.equal(C_ws.view(torch.int32), C_na.view(torch.int32))
         check_ex(C_na, A, B, dtype, 1.0, 0.0, 0, None)
 
