@@ -1,7 +1,7 @@
 """GPU parity on the benchmark workloads, in the launch configuration the benchmark
 times (migemm_gemm's own selection), against the CPU oracle.
 
-Workloads up to 2050 x 2047 x 2056 are compared in full here; the 8192^3,
+Workloads up to 2050 x 2047 x 2056, and 512 x 512 x 65536, are compared in full here; the 8192^3,
 4096^3 and one-GPU-share workloads in test_gpu_fullsize.py, also in full.
 """
 import pytest
@@ -12,7 +12,7 @@ from gpu_helpers import check, run_gemm, say
 pytestmark = pytest.mark.gpu
 
 FULL = ["c0-f16-256", "c1-f32-1024", "c1-f32-1024-int", "c2-f16-1024", "c3-f16-2048",
-        "c3-bf16-2048", "c3r-f16-2050x2047x2056"]
+        "c3-bf16-2048", "c3r-f16-2050x2047x2056", "lk-bf16-512x512x65536"]
 
 
 @pytest.mark.parametrize("name", FULL)
