@@ -60,11 +60,14 @@ def test_splitk_every_layout(ta, tb):
 def test_splitk_ragged_k_and_fewer_slices():
     """K = 8200 over 6 tiles: slices of 576, 15 of them, the last 136 deep (a
     partial k-tile); K = 4160 on one tile: slices of 320, 13 of them; FP16 and
-    BF16, row and column counts that are not whole tiles."""
+    BF16, row and column counts that are not whole tiles, and an M x N that is
+    not a multiple of 4 (the sum kernel then adds element by element)."""
     _run(264, 200, 8200, False, False)
     _run(264, 200, 8200, True, True, dtype="f16")
     _run(128, 128, 4160, False, True, dtype="f16")
     _run(72, 40, 4104, True, False)
+    # M x N not a multiple of 4: the sum kernel's element-wise path
+    _run(263, 199, 8200, False, True)
 
 
 def test_splitk_general_output():
