@@ -242,9 +242,17 @@ int64_t packed_k(int64_t K);
 // Alignment the packed path asks of a workspace.
 constexpr int64_t kWorkspaceAlign = 256;
 hipError_t launch_mfma_i8(const GemmArgs& a, int config);
-// FP16/BF16 products as slices of K on the 128x128 direct tile into FP32
-// partial sums in the caller's workspace, then a reduction that sums them in
-// slice order and applies the output step (splitk.hip).
+// FP16/BF16 products as slices of K on the 128x128 or 256x256 direct tile
+// into FP32 partial sums in the caller's workspace, then a reduction that sums
+// them in slice order and applies the output step (splitk.hip).
+struct SplitKPlan {
+    int config;      // the direct configuration that runs the slices: 7 or 10
+    int64_t slices;  // 2 to 16 (1 where K holds a single whole k-tile slice)
+};
+// shallowest slices for the 256x256 tile: in general, and where the 128x128
+// tile's slices would overshoot a round of 256 workgroups
+constexpr int64_t kMinSlice256 = 4096, kMinSlice256Overshoot = 1024;
+SplitKPlan splitk16_plan(const GemmArgs& g);
 int64_t splitk16_slices(const GemmArgs& g);
 int64_t splitk16_workspace_bytes(const GemmArgs& g);
 hipError_t launch_splitk16(const GemmArgs& g);

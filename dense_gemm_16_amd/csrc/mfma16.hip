@@ -49,7 +49,7 @@ const char* const kNames[] = {
     "direct 256x256x64 8w 16x16x32 gm4 pingpong ntC agpr",
     "direct 128x256x64 8w 16x16x32 gm8 pingpong ntC agpr",
     "direct 64x64x64 8w 16x16x32 s4 early ntC",
-    "split-K: slices of K on config 7 into FP32 partials in the workspace, then their sum"};
+    "split-K: slices of K on config 7 or 10 into FP32 partials in the workspace, then their sum"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 template <typename E, bool GEN>

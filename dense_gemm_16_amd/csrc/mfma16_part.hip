@@ -26,8 +26,8 @@ template <typename E> struct Cfgs {
     using D7P = DirectCfg<E, 128, 128, 2, 4, 16, 4, 64, 4, 2, 176>; // D7 with plain C stores
     using D8 = DirectCfg<E, 128, 128, 2, 2, 16, 4, 64>;             // 4 waves, 4 stages
     using D9 = DirectCfg<E, 256, 256, 2, 4, 32, 2, 64, 4, 2, 2>;    // gm4, interleave, nt C
-    using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 94>;  // + AGPRs, early loads; all layouts; partial first k-tile
-    using D10P = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 92>; // D10 with plain C stores
+    using D10 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 222>; // + AGPRs, early loads; all layouts; partial first k-tile; split-K
+    using D10P = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 2, 220>; // D10 with plain C stores
     using D13 = DirectCfg<E, 128, 256, 2, 4, 16, 3, 64, 8, 2, 48>;  // 8 waves of 64x64, 3 stages; all layouts; ragged K
     using D14 = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 22>;  // ping-pong (whole tiles), AGPRs, nt C; all layouts
     using D14P = DirectCfg<E, 256, 256, 2, 4, 16, 2, 64, 4, 4, 20>; // D14 with plain C stores

@@ -78,18 +78,41 @@ hipError_t launch_reduce(const GemmArgs& g, int S, const float* part) {
                          g.out);
 }
 
-int64_t tiles128(const GemmArgs& g) { return ceil_div(g.M, 128) * ceil_div(g.N, 128); }
+// Slices that, with `tiles` tiles each, make about one round of 256
+// workgroups: 2 to 16.
+int64_t round_slices(int64_t tiles) {
+    const int64_t s = tiles > 0 ? 256 / tiles : 0;
+    return s < 2 ? 2 : s > 16 ? 16 : s;
+}
 
 }  // namespace
 
-// Slices of K for this product: enough rows of 128x128 workgroups for one
-// round of 256 (2 to 16 of them), fewer where K runs out of whole k-tiles.
-int64_t splitk16_slices(const GemmArgs& g) {
-    const int64_t t = tiles128(g);
-    int64_t s = t > 0 ? 256 / t : 0;
-    s = s < 2 ? 2 : s > 16 ? 16 : s;
-    return ceil_div(g.K, splitk_slice(g.K, s));
+// The tile and the slice count for this product.  The 128x128 tile
+// (configuration 7) takes 2 to 16 slices, as many as make a round of 256
+// workgroups.  The 256x256 tile (configuration 10) runs a 64-deep k-tile, four
+// times the 128x128 tile's matrix work, in about 3 times its time (1.78 against
+// 0.60 us), but as 4 times as many slices its FP32 sums cost 4 times the
+// writes and reads; measured (BF16), it wins where its slices are at least
+// 4096 deep (1024 x 1024 x 65536: 141.9 against 150.2 us; 2048 x 1024 x 65536:
+// 243 against 308) and loses where they are 1024 or 2048 deep (1024 x 1024 x
+// 16384: 53.9 against 40.1; 1024 x 1024 x 32768: 76.3 against 71.2).  It is
+// also taken, with slices at least 1024 deep, where the 128x128 tile's two
+// slices overshoot a round (more than 128 tiles: 1536 x 1536 x 8192, 56.6
+// against 71.1 us).  Fewer slices where K runs out of whole k-tiles.
+SplitKPlan splitk16_plan(const GemmArgs& g) {
+    const int64_t t128 = ceil_div(g.M, 128) * ceil_div(g.N, 128);
+    const int64_t t256 = ceil_div(g.M, 256) * ceil_div(g.N, 256);
+    const int64_t s128 = round_slices(t128);
+    if (t256 >= 16) {
+        const int64_t ks = splitk_slice(g.K, round_slices(t256));
+        if (ks >= kMinSlice256 || (t128 * s128 > 256 && ks >= kMinSlice256Overshoot))
+            return SplitKPlan{10, ceil_div(g.K, ks)};
+    }
+    const int64_t ks = splitk_slice(g.K, s128);
+    return SplitKPlan{7, ceil_div(g.K, ks)};
 }
+
+int64_t splitk16_slices(const GemmArgs& g) { return splitk16_plan(g).slices; }
 
 // slices x M x N FP32 sums; 0 where split-K does not apply (fewer than two
 // slices, or M x N beyond 2^30)
@@ -100,7 +123,8 @@ int64_t splitk16_workspace_bytes(const GemmArgs& g) {
 }
 
 hipError_t launch_splitk16(const GemmArgs& g) {
-    const int64_t S = splitk16_slices(g), need = splitk16_workspace_bytes(g);
+    const SplitKPlan plan = splitk16_plan(g);
+    const int64_t S = plan.slices, need = splitk16_workspace_bytes(g);
     if (need == 0 || S > 16 || g.ws == nullptr ||
         (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 || g.ws_bytes < need)
         return hipErrorInvalidValue;
@@ -110,7 +134,7 @@ hipError_t launch_splitk16(const GemmArgs& g) {
     GemmArgs p = g;
     p.splitk = static_cast<int>(S);
     p.out = Epi{g.ws, g.N, 1.0f, 0.0f, 0};  // FP32 slice sums, plain, leading dimension N
-    hipError_t e = launch_cfg16_any(p, 7);
+    hipError_t e = launch_cfg16_any(p, plan.config);
     if (e != hipSuccess) return e;
     const float* part = static_cast<const float*>(g.ws);
     return g.general() ? launch_reduce<true>(g, static_cast<int>(S), part)

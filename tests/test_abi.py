@@ -304,12 +304,20 @@ def test_selection_split_k():
     assert _selected(512, 512, 65540, 1, 65540, 512, big) == ("mfma16", 12)  # K % 8: copies
     ws = lambda M, N, K: mg.migemm_workspace_size(-1, -1, 0, 0, M, N, K, 2, None, K, None, N)
     assert ws(512, 512, 65536) == (mg.OK, 16 * 512 * 512 * 4)
-    assert ws(1024, 1024, 65536) == (mg.OK, 4 * 1024 * 1024 * 4)
+    # 16 tiles of 256x256 in 16 slices of 4096 (the 256x256 tile, configuration 10)
+    assert ws(1024, 1024, 65536) == (mg.OK, 16 * 1024 * 1024 * 4)
+    # slices of the 256x256 tile would be 512 deep: 4 slices of the 128x128 tile
+    assert ws(1024, 1024, 8192) == (mg.OK, 4 * 1024 * 1024 * 4)
     assert ws(128, 128, 4160) == (mg.OK, 0)  # K < 6144
     # configuration 17 asked for: K = 4160 on one tile, 13 slices of 320
     assert mg.migemm_workspace_size(mg.MFMA16, 17, 0, 0, 128, 128, 4160, 2, None, 4160, None,
                                     128) == (mg.OK, 13 * 128 * 128 * 4)
+    # slices of the 256x256 tile would be 2048 deep: 2 slices of the 128x128 tile
     assert ws(2048, 1024, 16384) == (mg.OK, 2 * 2048 * 1024 * 4)
+    assert ws(2048, 1024, 65536) == (mg.OK, 8 * 2048 * 1024 * 4)
+    # 144 tiles of 128x128 in 2 slices would overshoot a round: 36 tiles of
+    # 256x256 in 7 slices of 1216
+    assert ws(1536, 1536, 8192) == (mg.OK, 7 * 1536 * 1536 * 4)
     # two launches: 16 tiles x 16 slices of the 128x128 kernel, then the sum
     # (4 elements per work-item, 256 work-items per workgroup)
     st, text = mg.migemm_describe_ex(-1, -1, 0, 0, 512, 512, 65536, mg.BF16, None, 65536, None,
@@ -322,6 +330,10 @@ def test_selection_split_k():
                     big)
     assert d["launches"] == 2 and d["grid0"] == 6 * 15
     assert d["workspace_bytes"] == 15 * 264 * 200 * 4
+    # 16 tiles of 256x256 x 16 slices, 512 threads (the 256x256 tile's 8 waves)
+    d = mg.describe(-1, -1, 0, 0, 1024, 1024, 65536, mg.BF16, None, 65536, None, 1024, 0, 1024,
+                    big)
+    assert d["config"] == 17 and d["grid0"] == 256 and d["block0"] == 512
     # configuration 17 without a workspace: the 128x128 launch alone
     d = mg.describe(mg.MFMA16, 17, 0, 0, 264, 200, 8200, mg.BF16, None, 8200, None, 200, 0, 200,
                     0)

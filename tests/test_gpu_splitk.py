@@ -1,6 +1,7 @@
 """Split-K (FP16/BF16 configuration 17): products whose M x N is a few 128x128
-tiles and whose K is long are summed as slices of K, one row of workgroups per
-slice writing FP32 sums into the lent workspace, then a second kernel adds the
+tiles and whose K is long are summed as slices of K, on the 128x128 tile or,
+with 16 or more 256x256 tiles, the 256x256 one, each slice's workgroups
+writing FP32 sums into the lent workspace, then a second kernel adds the
 slices in order and applies the output step.  Compared element by element with
 the oracle: every layout, a K that ends inside a k-tile (only the last slice is
 partial), fewer slices than asked for where K runs out of whole k-tiles, the
@@ -68,6 +69,21 @@ def test_splitk_ragged_k_and_fewer_slices():
     _run(72, 40, 4104, True, False)
     # M x N not a multiple of 4: the sum kernel's element-wise path
     _run(263, 199, 8200, False, True)
+
+
+def test_splitk_256x256_tile():
+    """The slices on the 256x256 tile (configuration 10): 16 tiles in 16 slices of
+    4096; 42 tiles (the 128x128 tile's 156 would overshoot a round in two
+    slices) in 6 slices of 1408 whose last is 1160 deep (a partial first k-tile
+    in that slice only); a ragged N with B given transposed; the general output
+    step into BF16 C."""
+    for (M, N, K, ta, tb, grid) in [(1024, 1024, 65536, False, False, 16 * 16),
+                                    (1544, 1536, 8200, True, False, 42 * 6),
+                                    (1536, 1543, 8192, False, True, 42 * 6)]:
+        d = _describe(M, N, K, "bf16", ta, tb, M if ta else K, K if tb else N, 1 << 40)
+        assert d["config"] == 17 and d["grid0"] == grid, d
+        _run(M, N, K, ta, tb)
+    _run(1536, 1536, 8192, True, True, dtype="f16", c_code=2, pad_c=8)
 
 
 def test_splitk_general_output():
