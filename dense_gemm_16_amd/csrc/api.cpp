@@ -31,7 +31,9 @@ constexpr double kPackMinWork = 134217728.0;  // 2^27, e.g. 512^3
 // Shortest K for split-K: below it the second launch and the slices' FP32 sums
 // cost more than the longer walk of K by the 64x64 tile (BF16, 512 x 512 and
 // 1024 x 1024: 16.6 against 20.8 and 19.4 us at K = 4096; 23.3 against 21.6 and
-// 23.5 against 21.7 us at K = 6144).
+// 23.5 against 21.7 us at K = 6144).  Twice that where more than 128 tiles of
+// 128x128 run as one partial round (1536 x 1536 x 8192: 56.6 us unsplit, 56.8
+// split; 1536 x 1536 x 16384: 82.8 split).
 constexpr int64_t kSplitKMinK = 6144;
 
 struct Variant {
@@ -181,8 +183,10 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
                       packed16_workspace_ok(g, pc);
     const bool whole256 = M % 256 == 0 && N % 256 == 0;
     // split-K (splitk.hip): a k-sum long beside a product of few 128x128 tiles,
-    // where a workspace for the slices' FP32 sums is lent
-    const bool splitk = direct && tiles(128, 128) < 256 && K >= kSplitKMinK &&
+    // where a workspace for the slices' FP32 sums is lent (twice as long where
+    // the 128x128 tile alone already fills more than half a round)
+    const bool splitk = direct && tiles(128, 128) < 256 &&
+                        K >= (tiles(128, 128) > 128 ? 2 * kSplitKMinK : kSplitKMinK) &&
                         K >= 4 * (M > N ? M : N) && splitk16_workspace_bytes(g) > 0 &&
                         g.ws != nullptr &&
                         reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
@@ -199,7 +203,9 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
     else if (direct && tiles(128, 128) >= 256)
         config = 7;   // direct 128x128x64, 8 waves, 4 stages, interleaved
     else if (splitk)
-        config = 17;  // slices of K on the direct 128x128 tile, then their sum
+        config = 17;  // slices of K on the direct 128x128 or 256x256 tile, then their sum
+    else if (direct && tiles(128, 128) > 128)
+        config = 7;   // one partial round of 128x128 tiles rather than 3 or 4 of 64x64
     else if (direct)
         config = 16;  // direct 64x64x64, 8 waves: four times the workgroups (e.g. 1024^3)
     else if (pack)

@@ -277,9 +277,14 @@ def test_selection_packs_unreadable_16bit_operands():
     assert sel(1000, 8192, 8192, 2, 8192, 8192) == (mg.OK, mg.MFMA16, 13)
     assert sel(4096, 4096, 4096, 2, 4096, 4096) == (mg.OK, mg.MFMA16, 14)
     assert sel(100, 100, 100, 1, 100, 100) == (mg.OK, mg.MFMA16, 3)
-    # fewer than 256 tiles of 128x128: the 64x64 direct tile
+    # at most 128 tiles of 128x128: the 64x64 direct tile; 129 to 255: one partial
+    # round of the 128x128 tile (the 64x64 one would take 3 or 4 rounds)
     assert sel(1024, 1024, 1024, 1, 1024, 1024) == (mg.OK, mg.MFMA16, 16)
     assert sel(256, 256, 256, 1, 256, 256) == (mg.OK, mg.MFMA16, 16)
+    assert sel(2048, 1024, 2048, 1, 2048, 1024) == (mg.OK, mg.MFMA16, 16)  # 128 tiles
+    assert sel(2048, 1032, 2048, 1, 2048, 1032) == (mg.OK, mg.MFMA16, 7)   # 144 tiles
+    assert sel(1536, 1536, 1536, 2, 1536, 1536) == (mg.OK, mg.MFMA16, 7)
+    assert sel(1792, 1792, 4096, 2, 4096, 1792) == (mg.OK, mg.MFMA16, 7)
     assert sel(2048, 2048, 2048, 0, 2049, 2048)[1] == mg.REGTILE_MFMA
     # aligned operands need no workspace: lending one changes nothing
     assert _selected(8192, 8192, 8192, 2, 8192, 8192, big) == ("mfma16", 14)
@@ -315,9 +320,11 @@ def test_selection_split_k():
     # slices of the 256x256 tile would be 2048 deep: 2 slices of the 128x128 tile
     assert ws(2048, 1024, 16384) == (mg.OK, 2 * 2048 * 1024 * 4)
     assert ws(2048, 1024, 65536) == (mg.OK, 8 * 2048 * 1024 * 4)
-    # 144 tiles of 128x128 in 2 slices would overshoot a round: 36 tiles of
-    # 256x256 in 7 slices of 1216
-    assert ws(1536, 1536, 8192) == (mg.OK, 7 * 1536 * 1536 * 4)
+    # more than 128 tiles of 128x128: split-K from K = 12288, and 144 tiles in 2
+    # slices would overshoot a round: 36 tiles of 256x256 in 7 slices of 2368
+    assert ws(1536, 1536, 8192) == (mg.OK, 0)
+    assert _selected(1536, 1536, 8192, 2, 8192, 1536, big) == ("mfma16", 7)
+    assert ws(1536, 1536, 16384) == (mg.OK, 7 * 1536 * 1536 * 4)
     # two launches: 16 tiles x 16 slices of the 128x128 kernel, then the sum
     # (4 elements per work-item, 256 work-items per workgroup)
     st, text = mg.migemm_describe_ex(-1, -1, 0, 0, 512, 512, 65536, mg.BF16, None, 65536, None,

@@ -23,9 +23,9 @@ pytestmark = pytest.mark.gpu
 LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
 
 
-def _describe(M, N, K, dtype, ta, tb, lda, ldb, ws_bytes):
-    st, text = mg.migemm_describe_ex(-1, -1, int(ta), int(tb), M, N, K, DT_CODE[dtype], None,
-                                     lda, None, ldb, 0, N, ws_bytes)
+def _describe(M, N, K, dtype, ta, tb, lda, ldb, ws_bytes, variant=-1, config=-1):
+    st, text = mg.migemm_describe_ex(variant, config, int(ta), int(tb), M, N, K, DT_CODE[dtype],
+                                     None, lda, None, ldb, 0, N, ws_bytes)
     assert st == mg.OK, text
     return mg._parse_description(text)
 
@@ -80,8 +80,9 @@ def test_splitk_256x256_tile():
     for (M, N, K, ta, tb, grid) in [(1024, 1024, 65536, False, False, 16 * 16),
                                     (1544, 1536, 8200, True, False, 42 * 6),
                                     (1536, 1543, 8192, False, True, 42 * 6)]:
-        d = _describe(M, N, K, "bf16", ta, tb, M if ta else K, K if tb else N, 1 << 40)
-        assert d["config"] == 17 and d["grid0"] == grid, d
+        d = _describe(M, N, K, "bf16", ta, tb, M if ta else K, K if tb else N, 1 << 40,
+                      mg.MFMA16, 17)
+        assert d["launches"] == 2 and d["grid0"] == grid, d
         _run(M, N, K, ta, tb)
     _run(1536, 1536, 8192, True, True, dtype="f16", c_code=2, pad_c=8)
 
