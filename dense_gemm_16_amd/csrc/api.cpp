@@ -28,6 +28,10 @@ constexpr int64_t kMaxLd = int64_t(1) << 32;  // leading dimensions must be belo
 // M * N * K from which a 16-bit product the direct kernel cannot read in place
 // is run on packed copies (pack.hip) rather than by the register-staged kernel.
 constexpr double kPackMinWork = 134217728.0;  // 2^27, e.g. 512^3
+// M * N * K from which an INT8 product of fewer than 256 tiles of 256x256 runs
+// on the direct 256x256 kernel (1792^3 = 5.75e9: 25.2 us against 31.0 for the
+// 64x64 tile; 2048 x 1024 x 2048 = 4.3e9: 26.7 against 20.9).
+constexpr double kI8DirectMinWork = 5.0e9;
 // Shortest K for split-K: below it the second launch and the slices' FP32 sums
 // cost more than the longer walk of K by the 64x64 tile (BF16, 512 x 512 and
 // 1024 x 1024: 16.6 against 20.8 and 19.4 us at K = 4096; 23.3 against 21.6 and
@@ -143,9 +147,23 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
         variant = MIGEMM_MFMA_I8;
         // whole 256x256 tiles with aligned operands: the direct ping-pong kernel;
         // otherwise the register-staged 256x256 with 32x32x32 instructions
-        // measured best in every layout at 8192^3
-        const bool whole = M % 256 == 0 && N % 256 == 0 && K % 128 == 0 && aligned;
-        config = tiles(256, 256) >= 256 ? (whole ? 4 : 3) : tiles(128, 128) >= 256 ? 1 : 2;
+        // measured best in every layout at 8192^3 (configuration 3, whose
+        // launcher runs the whole tiles of a ragged shape on the direct kernel
+        // when the operands suit it).  Below a round of 256x256 tiles the direct
+        // kernel still wins once the product is large or K long (one round of
+        // it takes about 12.7 us + 6.9 us per 1024 of K): 2048^3 26.9 us against
+        // 30.9 for the 64x64 tile, 3072^3 34.5 against 145 for the 128x128 one,
+        // 1024 x 1024 x 8192 68.7 against 138, 512 x 512 x 8192 68.2 against 99;
+        // smaller products keep the 64x64 tile (1536^3 20.2 against 23.3,
+        // 1024 x 1024 x 4096 35.1 against 40.7).
+        const bool direct = K % 128 == 0 && aligned;
+        const bool whole = M % 256 == 0 && N % 256 == 0 && direct;
+        const double work = static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K);
+        if (tiles(256, 256) >= 256 ||
+            (direct && M >= 256 && N >= 256 && (work >= kI8DirectMinWork || K >= 8192)))
+            config = whole ? 4 : 3;
+        else
+            config = tiles(128, 128) >= 256 ? 1 : 2;
         return;
     }
     if (dtype == MIGEMM_F32) {

@@ -443,7 +443,16 @@ def test_describe_split_bands():
     assert launches_i8(8192, 8208, 8192, 8208) == (3, [(1024, 512), (512, 512)])
     assert launches_i8(8192, 8200, 8192, 8208) == (3, [(1024, 512), (512, 512)])
     assert launches_i8(8400, 8192, 8192, 8192) == (3, [(1024, 512), (512, 256)])
-    assert launches_i8(2056, 2048, 2048, 2048) == (1, [(256, 256), (128, 1024)])
+    # below a round of 256x256 tiles too, once the product is large (M N K >= 5e9)
+    # or K long: 64 whole tiles on the direct kernel, then 8 rows on the skinny one
+    assert launches_i8(2056, 2048, 2048, 2048) == (3, [(64, 512), (128, 1024)])
+    assert launches_i8(3072, 3072, 3072, 3072) == (4, [(144, 512)])
+    assert launches_i8(512, 512, 8192, 512) == (4, [(4, 512)])
+    # smaller: the register-staged 64x64 tile (4 waves), also for K not a
+    # multiple of 128
+    assert launches_i8(1536, 1536, 1536, 1536) == (2, [(576, 256)])
+    assert launches_i8(1024, 1024, 4096, 1024) == (2, [(256, 256)])
+    assert launches_i8(3072, 3072, 3080, 3072)[0] == 1
 
 
 def test_describe():
