@@ -32,6 +32,12 @@ constexpr double kPackMinWork = 134217728.0;  // 2^27, e.g. 512^3
 // on the direct 256x256 kernel (1792^3 = 5.75e9: 25.2 us against 31.0 for the
 // 64x64 tile; 2048 x 1024 x 2048 = 4.3e9: 26.7 against 20.9).
 constexpr double kI8DirectMinWork = 5.0e9;
+// Shortest K for FP32 split-K.  An FP32 k-tile costs four times the matrix
+// cycles of a 16-bit one, so the slices' sums cost little beside it: split-K
+// measured faster on every product of at most 128 tiles of 64x64 tried from
+// K = 512 (512^3: 9.9 against 11.5 us; 512 x 512 x 2048: 16.5 against 38.0;
+// 1024 x 512 x 1024: 16.7 against 20.4; 512 x 512 x 65536: 288 against 1120).
+constexpr int64_t kSplitKMinK32 = 512;
 // Shortest K for split-K: below it the second launch and the slices' FP32 sums
 // cost more than the longer walk of K by the 64x64 tile (BF16, 512 x 512 and
 // 1024 x 1024: 16.6 against 20.8 and 19.4 us at K = 4096; 23.3 against 21.6 and
@@ -175,8 +181,14 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
         // at 4096^3 (128x128 tiles).  Other operands stage through registers.
         variant = MIGEMM_REGTILE_MFMA;
         const bool direct = aligned && K % 4 == 0 && (tb || N % 4 == 0) && (!ta || M % 4 == 0);
+        // split-K (configuration 12): at most half a round of 64x64 tiles, where a
+        // workspace for the slices' sums is lent
+        const bool splitk = direct && tiles(64, 64) <= 128 && K >= kSplitKMinK32 &&
+                            splitk32_workspace_bytes(g) > 0 && g.ws != nullptr &&
+                            reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
+                            g.ws_bytes >= splitk32_workspace_bytes(g);
         if (direct)
-            config = tiles(128, 128) >= 256 ? 10 : 8;
+            config = tiles(128, 128) >= 256 ? 10 : splitk ? 12 : 8;
         else
             config = tiles(128, 128) >= 256 ? 0 : 2;
         return;
@@ -286,8 +298,9 @@ hipError_t launch(const GemmArgs& g, int variant, int config) {
 // Workspace bytes the call's configuration uses when lent at least that many:
 // the packed FP16/BF16 configurations' copies, nothing for the others.
 int64_t config_workspace_bytes(const GemmArgs& g, int variant, int config) {
-    if (variant != MIGEMM_MFMA16 || (config != 11 && config != 12 && config != 17)) return 0;
     if (g.M == 0 || g.N == 0 || g.K == 0) return 0;
+    if (variant == MIGEMM_REGTILE_MFMA && config == 12) return splitk32_workspace_bytes(g);
+    if (variant != MIGEMM_MFMA16 || (config != 11 && config != 12 && config != 17)) return 0;
     if (config == 17) return splitk16_workspace_bytes(g);
     return packed16_workspace_bytes(g, config);
 }

@@ -256,6 +256,12 @@ SplitKPlan splitk16_plan(const GemmArgs& g);
 int64_t splitk16_slices(const GemmArgs& g);
 int64_t splitk16_workspace_bytes(const GemmArgs& g);
 hipError_t launch_splitk16(const GemmArgs& g);
+// The same for FP32 operands: slices on the direct 64x64 FP32 tile
+// (configuration 8 of the FP32 matrix-core variant), as many as make a round of
+// 256 workgroups (2 to 16).
+int64_t splitk32_slices(const GemmArgs& g);
+int64_t splitk32_workspace_bytes(const GemmArgs& g);
+hipError_t launch_splitk32(const GemmArgs& g);
 // FP32, FP16 and BF16 products with 1 <= M <= 16, K split over the waves of
 // each workgroup (skinny.hip); skinny_fits says whether its alignment and
 // whole-chunk needs hold (hipErrorInvalidValue from the launcher otherwise).

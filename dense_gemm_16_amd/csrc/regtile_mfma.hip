@@ -32,7 +32,9 @@ const char* const kNames[] = {"128x128x32 4w 16x16x4", "128x128x32 4w 32x32x2",
                               "direct 64x64x32 8w 16x16x4 s4 ilv ntC",
                               "direct 64x64x32 4w 16x16x4 s4 ilv ntC",
                               "direct 128x128x32 8w 16x16x4 gm4 s4 ilv ntC",
-                              "direct 128x64x32 8w 16x16x4 s4 ilv ntC"};
+                              "direct 128x64x32 8w 16x16x4 s4 ilv ntC",
+                              "split-K: slices of K on config 8 into FP32 partials in the "
+                              "workspace, then their sum"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 template <bool GEN>
@@ -72,6 +74,14 @@ hipError_t launch_cfg(const GemmArgs& g, int config) {
 // the 64x64 tile after the 128x128 one, and are left in place after the 64x64
 // one (a tail on the same tile costs what the extra round does).
 hipError_t launch_regtile_mfma(const GemmArgs& g, int config) {
+    if (config == 12) {
+        // without a usable workspace the ordinary 64x64 launch
+        const int64_t need = splitk32_workspace_bytes(g);
+        if (need == 0 || g.ws == nullptr ||
+            (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 || g.ws_bytes < need)
+            return launch_regtile_mfma(g, 8);
+        return launch_splitk32(g);
+    }
     if (config == 8 || config == 10) {
         const int64_t t = config == 10 ? 128 : 64;
         const SplitPlan p = plan_split(g.M, g.N, t, t, config == 10 ? t : 16);

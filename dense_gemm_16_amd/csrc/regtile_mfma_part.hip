@@ -19,8 +19,8 @@ using F7 = MfmaCfg<float, 64, 32, 2, 2, 16>;    // 4 waves of 32x16, twice F2's 
 // elements): <E, BM, BN, WM, WN, MF, STAGES, BK, GM, SCHED, FLAGS>; FLAGS 48: all
 // operand layouts and K in whole 4-element chunks (a partial last k-tile is
 // zero-filled), | 2: non-temporal C stores (chosen when C rows are whole lines)
-using D8 = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 50>;     // 8 waves of 32x16
-using D8P = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 48>;
+using D8 = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 178>;    // 8 waves of 32x16; split-K
+using D8P = DirectCfg<float, 64, 64, 2, 4, 16, 4, 32, 8, 2, 176>;
 using D9 = DirectCfg<float, 64, 64, 2, 2, 16, 4, 32, 8, 2, 50>;     // 4 waves of 32x32
 using D9P = DirectCfg<float, 64, 64, 2, 2, 16, 4, 32, 8, 2, 48>;
 using D10 = DirectCfg<float, 128, 128, 2, 4, 16, 4, 32, 4, 2, 50>;  // 8 waves of 64x32

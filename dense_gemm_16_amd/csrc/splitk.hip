@@ -122,6 +122,38 @@ int64_t splitk16_workspace_bytes(const GemmArgs& g) {
     return s * g.M * g.N * 4;
 }
 
+template <bool GEN, int C>
+hipError_t launch_f32_cfg(const GemmArgs& g);
+
+int64_t splitk32_slices(const GemmArgs& g) {
+    const int64_t ks = splitk_slice(g.K, round_slices(ceil_div(g.M, 64) * ceil_div(g.N, 64)));
+    return ceil_div(g.K, ks);
+}
+
+int64_t splitk32_workspace_bytes(const GemmArgs& g) {
+    const int64_t s = splitk32_slices(g);
+    if (s < 2 || g.M * g.N > (int64_t(1) << 30)) return 0;
+    return s * g.M * g.N * 4;
+}
+
+hipError_t launch_splitk32(const GemmArgs& g) {
+    const int64_t S = splitk32_slices(g), need = splitk32_workspace_bytes(g);
+    if (need == 0 || S > 16 || g.ws == nullptr ||
+        (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 || g.ws_bytes < need)
+        return hipErrorInvalidValue;
+    // the slices run on the direct kernel only (K whole 16-byte chunks of 4
+    // elements); other operands take the ordinary 64x64 path instead
+    if (!direct_ok(g, 4, true, 4)) return launch_regtile_mfma(g, 8);
+    GemmArgs p = g;
+    p.splitk = static_cast<int>(S);
+    p.out = Epi{g.ws, g.N, 1.0f, 0.0f, 0};
+    hipError_t e = launch_f32_cfg<false, 8>(p);
+    if (e != hipSuccess) return e;
+    const float* part = static_cast<const float*>(g.ws);
+    return g.general() ? launch_reduce<true>(g, static_cast<int>(S), part)
+                       : launch_reduce<false>(g, static_cast<int>(S), part);
+}
+
 hipError_t launch_splitk16(const GemmArgs& g) {
     const SplitKPlan plan = splitk16_plan(g);
     const int64_t S = plan.slices, need = splitk16_workspace_bytes(g);

@@ -347,6 +347,24 @@ def test_selection_split_k():
     assert d["launches"] == 1 and d["grid0"] == 6
 
 
+def test_selection_split_k_fp32():
+    """FP32 products of at most 128 tiles of 64x64 with K >= 512 run as slices of K
+    on the direct 64x64 FP32 tile (configuration 12) when a workspace is lent."""
+    big = 1 << 40
+    sel = lambda M, N, K: _selected(M, N, K, mg.F32, K, N, big)
+    assert sel(512, 512, 512) == ("regtile_mfma", 12)
+    assert sel(1024, 512, 1024) == ("regtile_mfma", 12)   # 128 tiles
+    assert sel(512, 512, 508) == ("regtile_mfma", 8)      # K < 512
+    assert sel(1024, 1024, 4096) == ("regtile_mfma", 8)   # 256 tiles: a full round
+    assert mg.migemm_select(512, 512, 4096, mg.F32, None, 4096, None, 512, None, 512) == (
+        mg.OK, mg.REGTILE_MFMA, 8)                        # no workspace
+    ws = lambda M, N, K: mg.migemm_workspace_size(-1, -1, 0, 0, M, N, K, mg.F32, None, K, None, N)
+    assert ws(512, 512, 65536) == (mg.OK, 4 * 512 * 512 * 4)    # 64 tiles, 4 slices
+    assert ws(256, 256, 16384) == (mg.OK, 16 * 256 * 256 * 4)   # 16 tiles, 16 slices
+    d = mg.describe(-1, -1, 0, 0, 768, 512, 8192, mg.F32, None, 8192, None, 512, 0, 512, big)
+    assert d["launches"] == 2 and d["grid0"] == 96 * 2 and d["block0"] == 512
+
+
 def test_fp32_selection():
     sel = lambda M, N, K, lda, ldb: mg.migemm_select(M, N, K, mg.F32, None, lda, None, ldb, None, N)
     # direct-staged FP32: 64x64 tiles below a round of 128x128 tiles, 128x128 above

@@ -30,7 +30,7 @@ def _describe(M, N, K, dtype, ta, tb, lda, ldb, ws_bytes, variant=-1, config=-1)
     return mg._parse_description(text)
 
 
-def _run(M, N, K, ta, tb, dtype="bf16", c_code=0, pad_c=0, config=17, seed=0):
+def _run(M, N, K, ta, tb, dtype="bf16", c_code=0, pad_c=0, config=17, seed=0, variant=mg.MFMA16):
     A, B = inputs.pair(M, N, K, dtype, "normal", seed=seed + M + 3 * N + 5 * K + ta + 2 * tb)
     ref = oracle_ref(A, B, dtype)
     alpha, beta = (1.0, 0.0) if c_code == 0 else (-0.5, 1.25)
@@ -42,7 +42,7 @@ def _run(M, N, K, ta, tb, dtype="bf16", c_code=0, pad_c=0, config=17, seed=0):
     ldb = K if tb else N
     say(f"splitk cfg={config} {'T' if ta else 'N'}{'T' if tb else 'N'} {M}x{N}x{K} {dtype} "
         f"c_dtype={c_code} ldc=N+{pad_c}")
-    C, buf, mask = run_gemm_ex(A, B, dtype, alpha, beta, c_code, old, variant=mg.MFMA16,
+    C, buf, mask = run_gemm_ex(A, B, dtype, alpha, beta, c_code, old, variant=variant,
                                config=config, ta=ta, tb=tb, lda=lda, ldb=ldb, ldc=N + pad_c)
     check_ex(C, A, B, dtype, alpha, beta, c_code, old, ref=ref)
     assert padding_untouched(buf, mask)
@@ -142,4 +142,33 @@ def test_splitk_long_products(M, N, K, dtype):
     say(f"splitk {M}x{N}x{K} {dtype} through the selection")
     C, buf, mask = run_gemm_ex(A, B, dtype, 1.0, 0.0, 0, None)
     check_ex(C, A, B, dtype, 1.0, 0.0, 0, None)
+    assert padding_untouched(buf, mask)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_splitk_fp32_every_layout(ta, tb):
+    """FP32 split-K (configuration 12 of the FP32 matrix-core variant): slices on
+    the direct 64x64 FP32 tile; 256 x 256 x 16384 is 16 tiles in 16 slices of
+    1024."""
+    v = mg.REGTILE_MFMA
+    d = _describe(256, 256, 16384, "f32", ta, tb, 256 if ta else 16384, 16384 if tb else 256,
+                  1 << 30, v, 12)
+    assert d["launches"] == 2 and d["grid0"] == 16 * 16, d
+    _run(256, 256, 16384, ta, tb, dtype="f32", config=12, variant=v)
+
+
+def test_splitk_fp32_ragged_and_general():
+    """FP32: K a multiple of 4 but not of the 32-deep k-tile (only the last slice
+    ends inside one), ragged M and N, the general output step into BF16 C with a
+    padded leading dimension, and the selection's own choice on a long product."""
+    v = mg.REGTILE_MFMA
+    _run(264, 200, 8196, False, False, dtype="f32", config=12, variant=v)
+    _run(200, 264, 8196, True, True, dtype="f32", config=12, variant=v)
+    _run(256, 192, 8192, False, True, dtype="f32", c_code=2, pad_c=8, config=12, variant=v)
+    d = _describe(512, 512, 65536, "f32", False, False, 65536, 512, 1 << 40)
+    assert d["variant"] == "regtile_mfma" and d["config"] == 12, d
+    A, B = inputs.pair(512, 512, 65536, "f32", "uniform", seed=13)
+    say("splitk fp32 512x512x65536 through the selection")
+    C, buf, mask = run_gemm_ex(A, B, "f32", 1.0, 0.0, 0, None)
+    check_ex(C, A, B, "f32", 1.0, 0.0, 0, None)
     assert padding_untouched(buf, mask)
