@@ -140,6 +140,42 @@ bool operands_aligned(const void* A, int64_t lda, const void* B, int64_t ldb, in
     return aligned16(A) && aligned16(B) && lda % epc == 0 && ldb % epc == 0;
 }
 
+}  // namespace
+
+// INT8 configuration.  direct: the operands suit the direct kernels (16-byte
+// aligned rows in whole chunks) and K is a multiple of the 128-deep k-tile;
+// direct16: the same with K a multiple of 16 only.
+//  * Whole 256x256 tiles: the direct ping-pong kernel (configuration 4).
+//  * A ragged shape whose last bands are at most 16 rows or columns, or any
+//    ragged shape of a round or more of 256x256 tiles: configuration 3, whose
+//    launcher runs the whole tiles on the ping-pong kernel and the bands after
+//    them (4100 x 4096 x 4096: 63.2 us, against 110.4 on configuration 6).
+//  * Below a round of 256x256 tiles the direct kernels win once the product is
+//    large or K long (one round takes about 12.7 us + 6.9 us per 1024 of K):
+//    2048^3 26.9 us against 30.9 for the 64x64 tile, 3072^3 34.5 against 145
+//    for the 128x128 one, 1024 x 1024 x 8192 68.7 against 138; and with wide
+//    last bands the interleaved direct kernel (configuration 6: clamped loads,
+//    guarded stores, a partial first k-tile) runs the whole shape in one
+//    launch: 2000 x 2000 x 2048 39.3 us against 108 for the split, 3008 x 3008
+//    x 3072 49.4 against 143.  It also takes K that is not a multiple of 128
+//    (2048 x 2048 x 2000: 32.6 us against 38.8 on zero-padded copies).
+//  * Smaller products: the register-staged 64x64 tile (1536^3 20.3 us against
+//    26.8 on configuration 6), or 128x128 from a round of its tiles.
+int i8_select(int64_t M, int64_t N, int64_t K, bool direct, bool direct16) {
+    auto tiles = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
+    const bool whole = M % 256 == 0 && N % 256 == 0;
+    const bool narrow = M % 256 <= 16 && N % 256 <= 16;  // last bands for the skinny kernel
+    const double work = static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K);
+    const bool big = tiles(256, 256) >= 256;
+    const bool large = M >= 256 && N >= 256 && (work >= kI8DirectMinWork || K >= 8192);
+    if (direct && (big || large)) return whole ? 4 : (big || narrow) ? 3 : 6;
+    if (direct16 && (big || large)) return 6;
+    if (big) return 3;
+    return tiles(128, 128) >= 256 ? 1 : 2;
+}
+
+namespace {
+
 // The selection table: a pure function of shape, dtype, operand layout and
 // alignment, and of whether the call lent a workspace large enough for the
 // packed path.  Sizes are bucketed by how many workgroup tiles a configuration
@@ -151,25 +187,18 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
     auto tiles = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
     if (dtype == MIGEMM_I8) {
         variant = MIGEMM_MFMA_I8;
-        // whole 256x256 tiles with aligned operands: the direct ping-pong kernel;
-        // otherwise the register-staged 256x256 with 32x32x32 instructions
-        // measured best in every layout at 8192^3 (configuration 3, whose
-        // launcher runs the whole tiles of a ragged shape on the direct kernel
-        // when the operands suit it).  Below a round of 256x256 tiles the direct
-        // kernel still wins once the product is large or K long (one round of
-        // it takes about 12.7 us + 6.9 us per 1024 of K): 2048^3 26.9 us against
-        // 30.9 for the 64x64 tile, 3072^3 34.5 against 145 for the 128x128 one,
-        // 1024 x 1024 x 8192 68.7 against 138, 512 x 512 x 8192 68.2 against 99;
-        // smaller products keep the 64x64 tile (1536^3 20.2 against 23.3,
-        // 1024 x 1024 x 4096 35.1 against 40.7).
-        const bool direct = K % 128 == 0 && aligned;
-        const bool whole = M % 256 == 0 && N % 256 == 0 && direct;
+        // Operands the direct kernels cannot read (K not a multiple of 16, rows
+        // off 16-byte boundaries) are read a byte at a time by the
+        // register-staged kernels (1000^3: 66.6 us against 11.4 for 1024^3);
+        // once the product is large enough and a workspace is lent they are
+        // copied into aligned zero-padded images first (configuration 5).
+        const bool direct = K % 128 == 0 && aligned, direct16 = K % 16 == 0 && aligned;
         const double work = static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K);
-        if (tiles(256, 256) >= 256 ||
-            (direct && M >= 256 && N >= 256 && (work >= kI8DirectMinWork || K >= 8192)))
-            config = whole ? 4 : 3;
-        else
-            config = tiles(128, 128) >= 256 ? 1 : 2;
+        const bool pack = !direct16 && work >= kPackMinWork &&
+                          ceil_div(K, 128) * 128 < (int64_t(1) << 21) && g.ws != nullptr &&
+                          reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
+                          g.ws_bytes >= packed8_workspace_bytes(g);
+        config = pack ? 5 : i8_select(M, N, K, direct, direct16);
         return;
     }
     if (dtype == MIGEMM_F32) {
@@ -300,6 +329,7 @@ hipError_t launch(const GemmArgs& g, int variant, int config) {
 int64_t config_workspace_bytes(const GemmArgs& g, int variant, int config) {
     if (g.M == 0 || g.N == 0 || g.K == 0) return 0;
     if (variant == MIGEMM_REGTILE_MFMA && config == 12) return splitk32_workspace_bytes(g);
+    if (variant == MIGEMM_MFMA_I8 && config == 5) return packed8_workspace_bytes(g);
     if (variant != MIGEMM_MFMA16 || (config != 11 && config != 12 && config != 17)) return 0;
     if (config == 17) return splitk16_workspace_bytes(g);
     return packed16_workspace_bytes(g, config);

@@ -242,6 +242,15 @@ int64_t packed_k(int64_t K);
 // Alignment the packed path asks of a workspace.
 constexpr int64_t kWorkspaceAlign = 256;
 hipError_t launch_mfma_i8(const GemmArgs& a, int config);
+// The INT8 configuration the selection gives this shape, with operands the
+// direct kernels read with K a multiple of 128 (direct) or of 16 (direct16)
+// (api.cpp).
+int i8_select(int64_t M, int64_t N, int64_t K, bool direct, bool direct16);
+// INT8 operands copied into aligned k-contiguous images, K zero-filled to a
+// multiple of 128, in packed8_workspace_bytes(a) of the lent workspace, then
+// the product of the copies (pack.hip; configuration 5 of the INT8 variant).
+int64_t packed8_workspace_bytes(const GemmArgs& a);
+hipError_t launch_packed8(const GemmArgs& a);
 // FP16/BF16 products as slices of K on the 128x128 or 256x256 direct tile
 // into FP32 partial sums in the caller's workspace, then a reduction that sums
 // them in slice order and applies the output step (splitk.hip).

@@ -31,7 +31,9 @@ namespace {
 
 const char* const kNames[] = {"256x256x128 8w 16x16x64", "128x128x128 4w 16x16x64",
                               "64x64x128 4w 16x16x64", "256x256x128 8w 32x32x32",
-                              "direct 256x256x128 8w 16x16x64 gm4 pingpong ntC agpr"};
+                              "direct 256x256x128 8w 16x16x64 gm4 pingpong ntC agpr",
+                              "packed: aligned zero-padded copies, then config 4, 3, 6, 1 or 2",
+                              "direct 256x256x128 8w 16x16x64 gm4 ilv ntC agpr early"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace
@@ -47,6 +49,7 @@ hipError_t launch_cfg(const GemmArgs& g, int config) {
         case 2: return launch_i8_cfg<2>(g);
         case 3: return launch_i8_cfg<3>(g);
         case 4: return launch_i8_cfg<4>(g);
+        case 6: return launch_i8_cfg<6>(g);
         default: return launch_i8_cfg<0>(g);
     }
 }
@@ -63,6 +66,7 @@ hipError_t launch_cfg(const GemmArgs& g, int config) {
 // register-staged tiles split a last band that would start a round of its own,
 // as the other element types do; the 64x64 tile only for tails of up to 16.
 hipError_t launch_mfma_i8(const GemmArgs& g, int config) {
+    if (config == 5) return launch_packed8(g);
     if (config == 3 || config == 4) {
         const bool direct = g.K % 128 == 0 && aligned16(g.A) && aligned16(g.B) &&
                             g.lda % 16 == 0 && g.ldb % 16 == 0;

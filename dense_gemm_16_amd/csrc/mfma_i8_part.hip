@@ -17,6 +17,11 @@ using I3 = MfmaCfg<int8_t, 256, 256, 2, 4, 32>;  // 8 waves, 32x32x32 instructio
 // stores for C rows that are not whole 128-byte lines
 using D4 = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 4, 22>;
 using D4P = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 4, 20>;
+// direct-staged, interleaved schedule: any M and N (clamped loads, guarded
+// stores), every layout, a partial first k-tile where K is not a multiple of
+// 128; D6P with plain C stores
+using D6 = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 2, 94>;
+using D6P = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 2, 92>;
 
 }  // namespace
 
@@ -30,6 +35,10 @@ hipError_t launch_i8_cfg(const GemmArgs& g) {
         return !direct_fits<D4>(g)   ? launch_mfma_i8(g, 0)
                : c_whole_lines(g.out) ? launch_direct_cfg<D4, false>(g)
                                       : launch_direct_cfg<D4P, false>(g);
+    else if constexpr (C == 6)
+        return !direct_fits<D6>(g)   ? launch_mfma_i8(g, 3)
+               : c_whole_lines(g.out) ? launch_direct_cfg<D6, false>(g)
+                                      : launch_direct_cfg<D6P, false>(g);
     else
         static_assert(C == 0, "no such configuration");
 }

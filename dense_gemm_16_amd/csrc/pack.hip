@@ -44,17 +44,19 @@ constexpr int kTile = 64;
 //   dst[r][c] = src(r, c) for c < cols, 0 for cols <= c < cols_out,
 //   src(r, c) = trans ? src[c * lds + r] : src[r * lds + c].
 struct PackJob {
-    const uint16_t* src;
+    const void* src;
     int64_t lds, rows, cols;
-    uint16_t* dst;
+    void* dst;
     int64_t ldd, cols_out, tiles_c, tiles;
     int trans;
     int vec;  // not transposed, rows 16-byte aligned: straight 16-byte copies
 };
 
 // Workgroups stride over the 64 x 64 tiles of both jobs (job 0's tiles first).
-// Reads are 2-byte loads, a wavefront covering 128 contiguous source bytes
-// (any alignment); writes are 16-byte stores of 8 consecutive dst columns.
+// T is the element (uint16_t for FP16/BF16, uint8_t for INT8).  Reads are
+// element loads, a wavefront covering 64 contiguous source elements (any
+// alignment); writes are 16-byte stores of EPC = 16 / sizeof(T) consecutive
+// dst columns.
 //
 // Tile order.  A source row whose start is not on a 128-byte line puts each
 // 128-byte tile row across two lines, the second shared with the next tile
@@ -63,10 +65,16 @@ struct PackJob {
 // the workgroups of one XCD (blockIdx modulo 8) take one contiguous range of
 // indices, so a shared line is fetched into that XCD's L2 once instead of into
 // two XCDs' L2s.
-__global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
+template <typename T>
+__global__ __launch_bounds__(256) void pack_kernel(PackJob j0, PackJob j1) {
+    constexpr int EPC = 16 / sizeof(T);       // elements per 16-byte chunk: 8 or 16
+    constexpr int CPR = kTile / EPC;          // chunks per tile row: 8 or 4
+    constexpr int RPP = 256 / CPR;            // tile rows per pass of 256 work-items
+    constexpr int PER = 4 / sizeof(T);        // elements per 32-bit word
+    constexpr int BITS = 8 * sizeof(T);
     __shared__ uint32_t tile[kTile][kTile + 1];
     const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;   // reads: ty in 0..3
-    const int wx = threadIdx.x % 8, wy = threadIdx.x / 8;           // writes: wy in 0..31
+    const int wx = threadIdx.x % CPR, wy = threadIdx.x / CPR;       // writes: wy < RPP
     const int64_t total = j0.tiles + j1.tiles;
     const int64_t per = gridDim.x / kNumXcd;
     const int64_t first = blockIdx.x < per * kNumXcd
@@ -79,23 +87,26 @@ __global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
         const int64_t tiles_r = j.tiles / j.tiles_c;
         const int64_t r0 = (j.trans ? tt % tiles_r : tt / j.tiles_c) * kTile;
         const int64_t c0 = (j.trans ? tt / tiles_r : tt % j.tiles_c) * kTile;
+        const T* const src = static_cast<const T*>(j.src);
+        T* const dst = static_cast<T*>(j.dst);
         if (j.vec) {
-            // 64 rows x 8 chunks of 16 bytes, two per work-item; the chunk that
-            // straddles cols (cols not a multiple of 8) is read element by element
+            // 64 rows x CPR chunks of 16 bytes, 64 / RPP per work-item; the chunk
+            // that straddles cols (cols not a multiple of EPC) is read element by
+            // element
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < kTile / RPP; ++i) {
                 const int q = threadIdx.x + 256 * i;
-                const int64_t r = r0 + q / 8, c = c0 + 8 * (q % 8);
+                const int64_t r = r0 + q / CPR, c = c0 + EPC * (q % CPR);
                 if (r >= j.rows || c >= j.cols_out) continue;
                 u32x4 w = {0u, 0u, 0u, 0u};
-                const uint16_t* s = j.src + r * j.lds + c;
-                if (c + 8 <= j.cols) {
+                const T* s = src + r * j.lds + c;
+                if (c + EPC <= j.cols) {
                     w = *reinterpret_cast<const u32x4*>(s);
                 } else if (c < j.cols) {
-                    for (int e = 0; e < 8 && c + e < j.cols; ++e)
-                        w[e / 2] |= static_cast<uint32_t>(s[e]) << (16 * (e % 2));
+                    for (int e = 0; e < EPC && c + e < j.cols; ++e)
+                        w[e / PER] |= static_cast<uint32_t>(s[e]) << (BITS * (e % PER));
                 }
-                *reinterpret_cast<u32x4*>(j.dst + r * j.ldd + c) = w;
+                *reinterpret_cast<u32x4*>(dst + r * j.ldd + c) = w;
             }
             continue;  // the whole workgroup takes this branch: no barrier is skipped
         }
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
 #pragma unroll
             for (int i = 0; i < kTile / 4; ++i) {
                 const int64_t c = c0 + ty + 4 * i, cc = c < j.cols ? c : j.cols - 1;
-                v[i] = j.src[cc * j.lds + rc];
+                v[i] = src[cc * j.lds + rc];
             }
 #pragma unroll
             for (int i = 0; i < kTile / 4; ++i) {
@@ -120,7 +131,7 @@ __global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
 #pragma unroll
             for (int i = 0; i < kTile / 4; ++i) {
                 const int64_t r = r0 + ty + 4 * i, rc = r < j.rows ? r : j.rows - 1;
-                v[i] = j.src[rc * j.lds + cc];
+                v[i] = src[rc * j.lds + cc];
             }
 #pragma unroll
             for (int i = 0; i < kTile / 4; ++i) {
@@ -130,15 +141,19 @@ __global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kTile / 32; ++i) {
-            const int rr = wy + 32 * i;
-            const int64_t r = r0 + rr, c = c0 + 8 * wx;
-            if (r < j.rows && c < j.cols_out) {  // cols_out is a multiple of 8
+        for (int i = 0; i < kTile / RPP; ++i) {
+            const int rr = wy + RPP * i;
+            const int64_t r = r0 + rr, c = c0 + EPC * wx;
+            if (r < j.rows && c < j.cols_out) {  // cols_out is a multiple of EPC
                 u32x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = tile[8 * wx + 2 * e][rr] | (tile[8 * wx + 2 * e + 1][rr] << 16);
-                *reinterpret_cast<u32x4*>(j.dst + r * j.ldd + c) = w;
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t word = 0u;
+#pragma unroll
+                    for (int b = 0; b < PER; ++b) word |= tile[EPC * wx + PER * e + b][rr] << (BITS * b);
+                    w[e] = word;
+                }
+                *reinterpret_cast<u32x4*>(dst + r * j.ldd + c) = w;
             }
         }
         __syncthreads();
@@ -148,29 +163,32 @@ __global__ __launch_bounds__(256) void pack16_kernel(PackJob j0, PackJob j1) {
 int64_t round_up(int64_t x, int64_t m) { return ceil_div(x, m) * m; }
 
 // Rows of dst start on 128-byte lines and are written whole (zero-filled from
-// cols to the leading dimension), so every line of the copy is written in full.
-PackJob make_job(const void* src, int64_t lds, int64_t rows, int64_t cols, bool trans, void* dst) {
-    const int64_t ldd = round_up(cols, 64), cols_out = ldd;
+// cols to the leading dimension, cols rounded up to 128 bytes of es-byte
+// elements), so every line of the copy is written in full.
+PackJob make_job(const void* src, int64_t lds, int64_t rows, int64_t cols, bool trans, void* dst,
+                 int es) {
+    const int64_t ldd = round_up(cols, 128 / es), cols_out = ldd;
     PackJob j;
-    j.src = static_cast<const uint16_t*>(src);
+    j.src = src;
     j.lds = lds;
     j.rows = rows;
     j.cols = cols;
-    j.dst = static_cast<uint16_t*>(dst);
+    j.dst = dst;
     j.ldd = ldd;
     j.cols_out = cols_out;
     j.tiles_c = ceil_div(cols_out, kTile);
     j.tiles = ceil_div(rows, kTile) * j.tiles_c;
     j.trans = trans ? 1 : 0;
-    j.vec = !trans && aligned16(src) && lds % 8 == 0;
+    j.vec = !trans && aligned16(src) && lds % (16 / es) == 0;
     return j;
 }
 
-hipError_t launch_pack16(const GemmArgs& g, const PackJob& j0, const PackJob& j1) {
+hipError_t launch_pack(const GemmArgs& g, const PackJob& j0, const PackJob& j1, int es) {
     const int64_t tiles = j0.tiles + j1.tiles;
     if (tiles == 0) return hipSuccess;
     const unsigned grid = static_cast<unsigned>(tiles < 65536 ? tiles : 65536);
-    return launch_kernel(g, pack16_kernel, dim3(grid), dim3(256), j0, j1);
+    return es == 1 ? launch_kernel(g, pack_kernel<uint8_t>, dim3(grid), dim3(256), j0, j1)
+                   : launch_kernel(g, pack_kernel<uint16_t>, dim3(grid), dim3(256), j0, j1);
 }
 
 // The direct configuration that packed configuration pc (11 or 12) runs.  11:
@@ -242,10 +260,10 @@ hipError_t launch_packed16(const GemmArgs& g, int pc, int fallback_config) {
     char* const wb = wa + pl.a_bytes;
     // A' (M x K): row-major A is copied, A given transposed (K x M) is transposed.
     // B' (N x K): row-major B (K x N) is transposed, B given transposed is copied.
-    const PackJob none = make_job(nullptr, 8, 0, 0, false, nullptr);
-    const PackJob ja = pl.a.in_place ? none : make_job(g.A, g.lda, g.M, g.K, g.ta, wa);
-    const PackJob jb = pl.b.in_place ? none : make_job(g.B, g.ldb, g.N, g.K, !g.tb, wb);
-    hipError_t e = launch_pack16(g, ja, jb);
+    const PackJob none = make_job(nullptr, 8, 0, 0, false, nullptr, 2);
+    const PackJob ja = pl.a.in_place ? none : make_job(g.A, g.lda, g.M, g.K, g.ta, wa, 2);
+    const PackJob jb = pl.b.in_place ? none : make_job(g.B, g.ldb, g.N, g.K, !g.tb, wb, 2);
+    hipError_t e = launch_pack(g, ja, jb, 2);
     if (e != hipSuccess) return e;
     GemmArgs p = g;
     // Both operands copies, zero-filled to K rounded up to 64: the product runs
@@ -264,6 +282,67 @@ hipError_t launch_packed16(const GemmArgs& g, int pc, int fallback_config) {
         p.pad_b = true;
     }
     return launch_mfma16(p, pl.inner);
+}
+
+// INT8 operands the direct kernel cannot read (a pointer off a 16-byte
+// boundary, a leading dimension that is not a whole number of 16-byte chunks, K
+// not a multiple of its 128-deep k-tile) are read by the register-staged INT8
+// kernels a byte at a time: 1000^3 took 66.6 us against 11.4 us for 1024^3.
+// Both operands are copied here as k-contiguous row images, A' (M x K') and B'
+// (N x K', B transposed), K' = K rounded up to 128 and zero-filled (each extra
+// term is an exact zero product, so the INT32 sums are those of the call), rows
+// on 128-byte lines; the product of the copies then takes the configuration
+// the selection gives aligned operands of that shape (i8_select).  (Aligned
+// operands with K a multiple of 16 need no copy: the interleaved direct kernel
+// takes a partial first k-tile.)  Either
+// operand already k-contiguous, aligned, on whole lines and with K a multiple
+// of 128 is read in place.
+int64_t packed8_workspace_bytes(const GemmArgs& g) {
+    const int64_t kp = round_up(g.K, 128);
+    const bool kt = g.K % 128 == 0;
+    const bool a_in = kt && !g.ta && aligned16(g.A) && g.lda % 128 == 0;
+    const bool b_in = kt && g.tb && aligned16(g.B) && g.ldb % 128 == 0;
+    const int64_t a = a_in ? 0 : round_up(g.M * kp, kWorkspaceAlign);
+    const int64_t b = b_in ? 0 : g.N * kp;
+    return a + b;
+}
+
+hipError_t launch_packed8(const GemmArgs& g) {
+    const int64_t kp = round_up(g.K, 128);
+    const bool kt = g.K % 128 == 0;
+    const bool a_in = kt && !g.ta && aligned16(g.A) && g.lda % 128 == 0;
+    const bool b_in = kt && g.tb && aligned16(g.B) && g.ldb % 128 == 0;
+    if (a_in && b_in) return launch_mfma_i8(g, i8_select(g.M, g.N, g.K, true, true));
+    const int64_t need = packed8_workspace_bytes(g);
+    if (g.ws == nullptr || (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 ||
+        g.ws_bytes < need) {
+        const bool aligned = aligned16(g.A) && aligned16(g.B) && g.lda % 16 == 0 &&
+                             g.ldb % 16 == 0;
+        return launch_mfma_i8(g, i8_select(g.M, g.N, g.K, kt && aligned,
+                                           g.K % 16 == 0 && aligned));
+    }
+    char* const wa = static_cast<char*>(g.ws);
+    char* const wb = wa + (a_in ? 0 : round_up(g.M * kp, kWorkspaceAlign));
+    const PackJob none = make_job(nullptr, 16, 0, 0, false, nullptr, 1);
+    const PackJob ja = a_in ? none : make_job(g.A, g.lda, g.M, g.K, g.ta, wa, 1);
+    const PackJob jb = b_in ? none : make_job(g.B, g.ldb, g.N, g.K, !g.tb, wb, 1);
+    hipError_t e = launch_pack(g, ja, jb, 1);
+    if (e != hipSuccess) return e;
+    GemmArgs p = g;
+    p.K = kp;
+    if (!a_in) {
+        p.ta = false;
+        p.A = wa;
+        p.lda = ja.ldd;
+        p.pad_a = true;
+    }
+    if (!b_in) {
+        p.tb = true;
+        p.B = wb;
+        p.ldb = jb.ldd;
+        p.pad_b = true;
+    }
+    return launch_mfma_i8(p, i8_select(p.M, p.N, p.K, true, true));
 }
 
 }  // namespace migemm

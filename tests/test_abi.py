@@ -201,9 +201,17 @@ def test_int8_selection():
     assert st == mg.OK and v == mg.MFMA_I8
     # whole 256 x 256 tiles, K a multiple of 128, 16-byte rows: the direct ping-pong
     # configuration; a leading dimension of half a chunk sends it to the register-staged one
+    # (without a workspace); K a multiple of 16 only: the interleaved direct kernel, which
+    # takes a partial first k-tile
     assert mg.migemm_select(8192, 8192, 8192, mg.I8, None, 8192, None, 8192, None, 8192)[2] == 4
     assert mg.migemm_select(8192, 8192, 8192, mg.I8, None, 8192, None, 8200, None, 8192)[2] == 3
-    assert mg.migemm_select(8192, 8192, 8000, mg.I8, None, 8000, None, 8192, None, 8192)[2] == 3
+    assert mg.migemm_select(8192, 8192, 8000, mg.I8, None, 8000, None, 8192, None, 8192)[2] == 6
+    assert mg.migemm_select(8192, 8192, 8008, mg.I8, None, 8008, None, 8192, None, 8192)[2] == 3
+    # below a round of 256x256 tiles, large, last bands wider than 16: configuration 6;
+    # at most 16: the split (whole tiles on the ping-pong kernel, the bands after them)
+    assert mg.migemm_select(2000, 2000, 2048, mg.I8, None, 2048, None, 2000, None, 2000)[2] == 6
+    assert mg.migemm_select(2056, 2048, 2048, mg.I8, None, 2048, None, 2048, None, 2048)[2] == 3
+    assert mg.migemm_select(1536, 1536, 1536, mg.I8, None, 1536, None, 1536, None, 1536)[2] == 2
 
 
 def test_empty_output_is_a_noop():
@@ -345,6 +353,30 @@ def test_selection_split_k():
     d = mg.describe(mg.MFMA16, 17, 0, 0, 264, 200, 8200, mg.BF16, None, 8200, None, 200, 0, 200,
                     0)
     assert d["launches"] == 1 and d["grid0"] == 6
+
+
+def test_selection_packs_unaligned_int8():
+    """INT8 operands the direct kernel cannot read (K not a multiple of 128, rows
+    off 16-byte boundaries) go to the packed configuration 5 once M N K >= 2^27
+    and a workspace is lent: each copied operand's rows x K rounded up to 128
+    bytes (A' first, rounded up to 256 bytes); an operand already k-contiguous,
+    on whole 128-byte lines and with K a multiple of 128 is read in place."""
+    big = 1 << 40
+    def sel(M, N, K, lda, ldb, ws):
+        d = mg.describe(-1, -1, 0, 0, M, N, K, mg.I8, None, lda, None, ldb, mg.I32, N, ws)
+        return d["variant"], d["config"]
+    assert sel(1000, 1000, 1000, 1000, 1000, big) == ("mfma_i8", 5)
+    assert sel(1000, 1000, 1000, 1000, 1000, 0) == ("mfma_i8", 2)       # no workspace
+    assert sel(400, 400, 400, 400, 400, big) == ("mfma_i8", 2)          # below 2^27
+    assert sel(1024, 1024, 1024, 1024, 1024, big) == ("mfma_i8", 2)     # aligned: in place
+    wsz = lambda M, N, K, lda, ldb: mg.migemm_workspace_size(-1, -1, 0, 0, M, N, K, mg.I8, None,
+                                                             lda, None, ldb)
+    assert wsz(1000, 1000, 1000, 1000, 1000) == (mg.OK, 1024000 + 1000 * 1024)
+    assert wsz(3000, 3000, 3072, 3072, 3000) == (mg.OK, 3000 * 3072)     # B' only
+    d = mg.describe(-1, -1, 0, 0, 1000, 1000, 1000, mg.I8, None, 1000, None, 1000, mg.I32, 1000,
+                    big)
+    # the copy (16 x 16 tiles of 64 x 64 for each operand), then the 64x64 tile
+    assert d["launches"] == 2 and d["grid0"] == 512 and d["grid1"] == 256
 
 
 def test_selection_split_k_fp32():

@@ -26,10 +26,12 @@ def _name(ta, tb):
 
 
 def run_i8(A, B, variant=-1, config=-1, ta=False, tb=False, lda=None, ldb=None, ldc=None,
-           a_off=0, b_off=0, c_off=0):
+           a_off=0, b_off=0, c_off=0, ws=False):
     """C = A x B (int8 CPU tensors, the product's operands; stored transposed on the
     GPU with ta / tb) through migemm_gemm_ex_variant with INT32 C inside a
-    sentinel-filled buffer.  Returns (C as int64 numpy, whether padding is intact)."""
+    sentinel-filled buffer, or through migemm_gemm_ws lending the workspace
+    migemm_workspace_size asks for (ws=True).  Returns (C as int64 numpy,
+    whether padding is intact)."""
     M, K = A.shape
     N = B.shape[1]
     sA = A.t().contiguous() if ta else A
@@ -46,10 +48,21 @@ def run_i8(A, B, variant=-1, config=-1, ta=False, tb=False, lda=None, ldb=None, 
     ldc = ldc or max(N, 1)
     cbuf = torch.full((c_off + max(M, 1) * ldc + 64,), SENTINEL, dtype=torch.int32, device="cuda")
     dC = cbuf[c_off:c_off + M * ldc].view(M, ldc)[:, :N]
-    st = mg.migemm_gemm_ex_variant(variant, config, int(ta), int(tb), M, N, K, mg.I8,
-                                   dAv.data_ptr() if K and M else None, lda,
-                                   dBv.data_ptr() if K and N else None, ldb, 1.0, 0.0, mg.I32,
-                                   dC.data_ptr(), ldc, torch.cuda.current_stream().cuda_stream)
+    pa = dAv.data_ptr() if K and M else None
+    pb = dBv.data_ptr() if K and N else None
+    stream = torch.cuda.current_stream().cuda_stream
+    if ws:
+        st, n = mg.migemm_workspace_size(variant, config, int(ta), int(tb), M, N, K, mg.I8, pa,
+                                         lda, pb, ldb)
+        assert st == mg.OK
+        wt = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+        st = mg.migemm_gemm_ws(variant, config, int(ta), int(tb), M, N, K, mg.I8, pa, lda, pb,
+                               ldb, 1.0, 0.0, mg.I32, dC.data_ptr(), ldc,
+                               wt.data_ptr() if n else None, n, stream)
+    else:
+        st = mg.migemm_gemm_ex_variant(variant, config, int(ta), int(tb), M, N, K, mg.I8, pa,
+                                       lda, pb, ldb, 1.0, 0.0, mg.I32, dC.data_ptr(), ldc,
+                                       stream)
     torch.cuda.synchronize()
     assert st == mg.OK, mg.migemm_status_string(st)
     mask = torch.zeros(cbuf.shape, dtype=torch.bool)
@@ -189,3 +202,82 @@ def test_empty_k_writes_zeros():
     B = torch.zeros((0, 9), dtype=torch.int8)
     C, intact = run_i8(A, B, ldc=12)
     assert intact and np.all(C == 0)
+
+
+def _packed_case(M, N, K, ta=False, tb=False, lda=None, ldb=None, a_off=0, b_off=0, config=-1):
+    A, B = inputs.pair(M, N, K, "i8", "uniform", seed=M + 5 * N + 7 * K + ta + 2 * tb)
+    want = _want(A, B)
+    v = -1 if config == -1 else mg.MFMA_I8
+    say(f"i8 packed {_name(ta, tb)} {M}x{N}x{K} lda={lda} ldb={ldb} off={a_off},{b_off} "
+        f"cfg={config}")
+    C, intact = run_i8(A, B, v, config, ta=ta, tb=tb, lda=lda, ldb=ldb, a_off=a_off, b_off=b_off,
+                       ws=True)
+    assert intact
+    bad = np.flatnonzero(C != want)
+    assert bad.size == 0, f"{bad.size} differ; first {np.unravel_index(bad[0], C.shape)}"
+
+
+def test_packed_selected_for_unaligned_operands():
+    """Operands the direct kernels cannot read (K not a multiple of 16, rows off
+    16-byte boundaries) with a workspace lent: the selection copies them into
+    aligned zero-padded images (configuration 5) and runs the product of the
+    copies, bit-exact: 1000^3 (then the 64x64 tile), 3000 x 3000 x 3072 with
+    ldb = 3000 (A read in place, B copied; then the whole shape on the
+    interleaved direct kernel), 4096 x 4096 x 4008 (both copied to K = 4096,
+    then the ping-pong kernel)."""
+    for (M, N, K, lda, ldb) in [(1000, 1000, 1000, 1000, 1000), (3000, 3000, 3072, 3072, 3000),
+                                (4096, 4096, 4008, 4016, 4096)]:
+        st, text = mg.migemm_describe_ex(-1, -1, 0, 0, M, N, K, mg.I8, None, lda, None, ldb,
+                                         mg.I32, N, 1 << 40)
+        assert st == mg.OK and mg._parse_description(text)["config"] == 5, text
+        _packed_case(M, N, K, lda=lda, ldb=ldb)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_packed_every_layout_exact(ta, tb):
+    """Configuration 5 asked for, every layout: K from 1 to past a k-tile, odd
+    leading dimensions and element offsets of 1 and 3 (every source row off its
+    16-byte boundary), ragged M and N."""
+    for (M, N, K, pad, off) in [(300, 257, 77, 3, 1), (600, 520, 1000, 5, 3), (64, 65, 1, 0, 0),
+                                (257, 300, 129, 9, 1), (512, 512, 256, 0, 0)]:
+        lda = (M if ta else K) + pad
+        ldb = (K if tb else N) + pad
+        _packed_case(M, N, K, ta, tb, lda, ldb, off, off, config=5)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_interleaved_direct_exact(ta, tb):
+    """Configuration 6, the direct 256x256 kernel with the interleaved schedule:
+    ragged M and N (clamped loads, guarded stores), K a multiple of 16 but not of
+    the 128-deep k-tile (a partial first k-tile), K = 16, padded leading
+    dimensions in whole 16-byte chunks; bit-exact."""
+    for (M, N, K, pad) in [(300, 264, 256, 0), (513, 640, 400, 16), (264, 296, 16, 0),
+                           (1000, 1000, 1008, 32), (256, 512, 384, 0)]:
+        A, B = inputs.pair(M, N, K, "i8", "uniform", seed=M + 2 * N + 5 * K + 7 * ta + 11 * tb)
+        want = _want(A, B)
+        lda = ((M if ta else K) + 15) // 16 * 16 + pad
+        ldb = ((K if tb else N) + 15) // 16 * 16 + pad
+        say(f"i8 interleaved {_name(ta, tb)} {M}x{N}x{K} lda={lda} ldb={ldb}")
+        C, intact = run_i8(A, B, mg.MFMA_I8, 6, ta=ta, tb=tb, lda=lda, ldb=ldb)
+        assert intact
+        bad = np.flatnonzero(C != want)
+        assert bad.size == 0, f"{bad.size} differ; first {np.unravel_index(bad[0], C.shape)}"
+
+
+def test_interleaved_direct_extreme_sums():
+    """Configuration 6 with K = 2^17 - 16 (a partial first k-tile of 112):
+    (-128)(-128) summed 131056 times, exact."""
+    M = N = 256
+    K = (1 << 17) - 16
+    A = torch.full((M, K), -128, dtype=torch.int8)
+    A[M // 2:] = 127
+    B = torch.full((K, N), -128, dtype=torch.int8)
+    B[:, N // 2:] = 127
+    want = np.empty((M, N), dtype=np.int64)
+    want[:M // 2, :N // 2] = 16384 * K
+    want[:M // 2, N // 2:] = -128 * 127 * K
+    want[M // 2:, :N // 2] = -128 * 127 * K
+    want[M // 2:, N // 2:] = 127 * 127 * K
+    say("i8 interleaved extremes K=131056")
+    C, intact = run_i8(A, B, mg.MFMA_I8, 6)
+    assert intact and np.array_equal(C, want)
