@@ -281,3 +281,42 @@ def test_interleaved_direct_extreme_sums():
     say("i8 interleaved extremes K=131056")
     C, intact = run_i8(A, B, mg.MFMA_I8, 6)
     assert intact and np.array_equal(C, want)
+
+
+@pytest.mark.parametrize("block", range(4))
+def test_random_cases_exact(block):
+    """Seeded random INT8 cases: sizes biased to multiples of 16, 128 and 256 and
+    one either side, every layout, padded leading dimensions and byte offsets
+    (0, 1, 3, 16), through the selection with or without a workspace or on one
+    configuration picked at random; bit-exact, padding of C untouched."""
+    rng = np.random.default_rng(7700 + block)
+
+    def dim(hi):
+        u = rng.random()
+        if u < 0.4:
+            return 16 * int(rng.integers(1, hi // 16 + 1))
+        if u < 0.7:
+            m = int(rng.choice([16, 128, 256]))
+            return int(min(hi, max(1, m * int(rng.integers(1, max(2, hi // m))) +
+                                   int(rng.integers(-1, 2)))))
+        return int(rng.integers(1, hi + 1))
+
+    for i in range(25):
+        M, N, K = dim(900), dim(900), dim(1400)
+        ta, tb = bool(rng.random() < 0.3), bool(rng.random() < 0.3)
+        pad = lambda: int(rng.choice([0, 0, 0, 16, 1, 3, 9]))
+        lda, ldb = (M if ta else K) + pad(), (K if tb else N) + pad()
+        off = int(rng.choice([0, 0, 0, 1, 3, 16]))
+        route = str(rng.choice(["auto", "auto_ws", "config"]))
+        v, c = -1, -1
+        if route == "config":
+            v, c = mg.MFMA_I8, int(rng.integers(0, mg.migemm_config_count(mg.MFMA_I8)))
+        A, B = inputs.pair(M, N, K, "i8", "uniform", seed=100 * block + i)
+        want = _want(A, B)
+        say(f"i8 random block {block} case {i}: {_name(ta, tb)} {M}x{N}x{K} lda={lda} "
+            f"ldb={ldb} off={off} {route} cfg={c}")
+        C, intact = run_i8(A, B, v, c, ta=ta, tb=tb, lda=lda, ldb=ldb, a_off=off, b_off=off,
+                           ws=route != "auto")
+        assert intact
+        bad = np.flatnonzero(C != want)
+        assert bad.size == 0, f"{bad.size} differ; first {np.unravel_index(bad[0], C.shape)}"
