@@ -32,6 +32,13 @@ constexpr double kPackMinWork = 134217728.0;  // 2^27, e.g. 512^3
 // on the direct 256x256 kernel (1792^3 = 5.75e9: 25.2 us against 31.0 for the
 // 64x64 tile; 2048 x 1024 x 2048 = 4.3e9: 26.7 against 20.9).
 constexpr double kI8DirectMinWork = 5.0e9;
+// INT8 split-K: at most 64 tiles of 256x256 and K at least 8192.  Measured
+// (us, split-K against the best other configuration): 512 x 512 x 8192 23.3
+// against 68.3, 1024 x 1024 x 8192 38.7 against 68.6, 2048 x 2048 x 8192 54.3
+// against 68.8, 256 x 256 x 65536 58.4 against 454; at K = 4096 and below it
+// does not pay (1024 x 1024 x 4096 36.3 against 35.0, 2048 x 2048 x 4096 43.0
+// against 41.0, 2048^3 37.9 against 26.8).
+constexpr int64_t kSplitK8MaxTiles = 64, kSplitK8MinK = 8192;
 // Shortest K for FP32 split-K.  An FP32 k-tile costs four times the matrix
 // cycles of a 16-bit one, so the slices' sums cost little beside it: split-K
 // measured faster on every product of at most 128 tiles of 64x64 tried from
@@ -198,7 +205,13 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
                           ceil_div(K, 128) * 128 < (int64_t(1) << 21) && g.ws != nullptr &&
                           reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
                           g.ws_bytes >= packed8_workspace_bytes(g);
-        config = pack ? 5 : i8_select(M, N, K, direct, direct16);
+        // split-K (configuration 7): few 256x256 tiles and a long K, where a
+        // workspace for the slices' INT32 sums is lent
+        const bool splitk = direct16 && tiles(256, 256) <= kSplitK8MaxTiles && K >= kSplitK8MinK &&
+                            splitk8_workspace_bytes(g) > 0 && g.ws != nullptr &&
+                            reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
+                            g.ws_bytes >= splitk8_workspace_bytes(g);
+        config = pack ? 5 : splitk ? 7 : i8_select(M, N, K, direct, direct16);
         return;
     }
     if (dtype == MIGEMM_F32) {
@@ -330,6 +343,7 @@ int64_t config_workspace_bytes(const GemmArgs& g, int variant, int config) {
     if (g.M == 0 || g.N == 0 || g.K == 0) return 0;
     if (variant == MIGEMM_REGTILE_MFMA && config == 12) return splitk32_workspace_bytes(g);
     if (variant == MIGEMM_MFMA_I8 && config == 5) return packed8_workspace_bytes(g);
+    if (variant == MIGEMM_MFMA_I8 && config == 7) return splitk8_workspace_bytes(g);
     if (variant != MIGEMM_MFMA16 || (config != 11 && config != 12 && config != 17)) return 0;
     if (config == 17) return splitk16_workspace_bytes(g);
     return packed16_workspace_bytes(g, config);

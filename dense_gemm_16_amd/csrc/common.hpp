@@ -102,11 +102,14 @@ inline bool c_whole_lines(const Epi& o) {
     return (o.ldc * eb) % 128 == 0 && (reinterpret_cast<uintptr_t>(o.C) & 127) == 0;
 }
 
-// Split-K: the k extent of each of `slices` slices of K, whole 64-deep k-tiles
-// (the last slice takes what is left).  With slices = ceil(K / splitk_slice(K,
-// s)) slices, every slice is non-empty and this gives the same extent again.
-__host__ __device__ inline int64_t splitk_slice(int64_t K, int64_t slices) {
-    return (K + slices - 1) / slices + 63 - ((K + slices - 1) / slices + 63) % 64;
+// Split-K: the k extent of each of `slices` slices of K, a whole number of
+// `unit` (64, or the 128-deep INT8 k-tile) (the last slice takes what is left).
+// With slices = ceil(K / splitk_slice(K, s, unit)) slices, every slice is
+// non-empty and this gives the same extent again (checked for every K below
+// 2^17 and s from 2 to 16).
+__host__ __device__ inline int64_t splitk_slice(int64_t K, int64_t slices, int64_t unit = 64) {
+    const int64_t c = (K + slices - 1) / slices;
+    return (c + unit - 1) / unit * unit;
 }
 
 // Storage of a bfloat16 element: its 16 bits.
@@ -271,6 +274,12 @@ hipError_t launch_splitk16(const GemmArgs& g);
 int64_t splitk32_slices(const GemmArgs& g);
 int64_t splitk32_workspace_bytes(const GemmArgs& g);
 hipError_t launch_splitk32(const GemmArgs& g);
+// The same for INT8 operands: slices (whole 128-deep k-tiles) on the
+// interleaved direct 256x256 INT8 tile (configuration 6), their exact INT32
+// sums added by an integer sum kernel (configuration 7 of the INT8 variant).
+int64_t splitk8_slices(const GemmArgs& g);
+int64_t splitk8_workspace_bytes(const GemmArgs& g);
+hipError_t launch_splitk8(const GemmArgs& g);
 // FP32, FP16 and BF16 products with 1 <= M <= 16, K split over the waves of
 // each workgroup (skinny.hip); skinny_fits says whether its alignment and
 // whole-chunk needs hold (hipErrorInvalidValue from the launcher otherwise).

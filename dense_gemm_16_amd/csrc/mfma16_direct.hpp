@@ -347,9 +347,10 @@ __device__ __forceinline__ void wait_then_barrier() {
 // SPLITK: the grid is tiles x slices workgroups; workgroup w (renumbered
 // XCD-contiguous, so that one XCD takes whole slices, whose tiles share rows of
 // A and columns of B in its L2) takes tile w mod tiles of slice w / tiles of K
-// (whole 64-deep k-tiles, the last slice the rest, see splitk_slice) and writes
-// its FP32 sums, plain, to that slice's M x N block of out.C (leading dimension
-// N): the partial products that a reduction then sums.
+// (a whole number of 64 k, or of the k-tile where it is deeper; the last slice
+// the rest, see splitk_slice) and writes its sums (FP32, INT32 for 8-bit
+// inputs), plain, to that slice's M x N block of out.C (leading dimension N):
+// the partial products that a reduction then sums.
 template <class Cfg, bool GEN, bool TA, bool TB, bool KTAIL = false, bool KHEAD = false,
           bool SPLITK = false>
 __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
@@ -360,7 +361,8 @@ __global__ __launch_bounds__(Cfg::NT) void mfma16_direct_kernel(
         const int tiles = tiles_m * tiles_n;
         const int id = xcd_contiguous(blockIdx.x, gridDim.x), slice = id / tiles;
         tile = id - slice * tiles;
-        const int64_t ks = splitk_slice(K, gridDim.x / tiles), k0 = slice * ks;
+        const int64_t ks = splitk_slice(K, gridDim.x / tiles, Cfg::BK < 64 ? 64 : Cfg::BK);
+        const int64_t k0 = slice * ks;
         A += TA ? k0 * lda : k0;
         B += TB ? k0 : k0 * ldb;
         K = K - k0 < ks ? K - k0 : ks;

@@ -33,7 +33,9 @@ const char* const kNames[] = {"256x256x128 8w 16x16x64", "128x128x128 4w 16x16x6
                               "64x64x128 4w 16x16x64", "256x256x128 8w 32x32x32",
                               "direct 256x256x128 8w 16x16x64 gm4 pingpong ntC agpr",
                               "packed: aligned zero-padded copies, then config 4, 3, 6, 1 or 2",
-                              "direct 256x256x128 8w 16x16x64 gm4 ilv ntC agpr early"};
+                              "direct 256x256x128 8w 16x16x64 gm4 ilv ntC agpr early",
+                              "split-K: slices of K on config 6 into INT32 partials in the "
+                              "workspace, then their sum"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 }  // namespace
@@ -67,6 +69,18 @@ hipError_t launch_cfg(const GemmArgs& g, int config) {
 // as the other element types do; the 64x64 tile only for tails of up to 16.
 hipError_t launch_mfma_i8(const GemmArgs& g, int config) {
     if (config == 5) return launch_packed8(g);
+    if (config == 7) {
+        // without a usable workspace the configuration the selection gives
+        const int64_t need = splitk8_workspace_bytes(g);
+        if (need == 0 || g.ws == nullptr ||
+            (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 || g.ws_bytes < need) {
+            const bool aligned = aligned16(g.A) && aligned16(g.B) && g.lda % 16 == 0 &&
+                                 g.ldb % 16 == 0;
+            return launch_mfma_i8(g, i8_select(g.M, g.N, g.K, aligned && g.K % 128 == 0,
+                                               aligned && g.K % 16 == 0));
+        }
+        return launch_splitk8(g);
+    }
     if (config == 3 || config == 4) {
         const bool direct = g.K % 128 == 0 && aligned16(g.A) && aligned16(g.B) &&
                             g.lda % 16 == 0 && g.ldb % 16 == 0;

@@ -20,8 +20,8 @@ using D4P = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 4, 20>;
 // direct-staged, interleaved schedule: any M and N (clamped loads, guarded
 // stores), every layout, a partial first k-tile where K is not a multiple of
 // 128; D6P with plain C stores
-using D6 = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 2, 94>;
-using D6P = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 2, 92>;
+using D6 = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 2, 222>;  // also split-K
+using D6P = DirectCfg<int8_t, 256, 256, 2, 4, 16, 2, 128, 4, 2, 220>;
 
 }  // namespace
 

@@ -29,6 +29,42 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// INT32 slice sums of an INT8 product: out[idx] = the sum of part[s][idx] over
+// the slices, written as INT32.  Each slice sum and the total are sums of at
+// most K < 2^17 products of magnitude at most 2^14, below 2^31: every addition
+// is exact, in any order.
+template <int SMAX>
+__global__ __launch_bounds__(kThreads) void splitk_reduce_i32(const int32_t* __restrict__ part,
+                                                              int S, int64_t M, int64_t N,
+                                                              Epi out) {
+    const int64_t MN = M * N;
+    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
+    if (i0 >= MN) return;
+    int32_t v[4] = {0, 0, 0, 0};
+    if (i0 + 4 <= MN && MN % 4 == 0) {
+        u32x4 p[SMAX];
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s)
+            p[s] = *reinterpret_cast<const u32x4*>(part + (s < S ? s : S - 1) * MN + i0);
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) {
+            if (s < S) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += static_cast<int32_t>(p[s][e]);
+            }
+        }
+    } else {
+        for (int s = 0; s < S; ++s)
+            for (int e = 0; i0 + e < MN && e < 4; ++e) v[e] += part[s * MN + i0 + e];
+    }
+    int32_t* const c = static_cast<int32_t*>(out.C);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + e;
+        if (i < MN) c[(i / N) * out.ldc + i % N] = v[e];
+    }
+}
+
 // out[idx] for 4 consecutive elements per work-item of the M x N result:
 // the sum of part[s][idx], s = 0 .. S - 1 in order, then the output step.
 // Every slice's 16 bytes are loaded before the first is added, so the S loads
@@ -124,6 +160,46 @@ int64_t splitk16_workspace_bytes(const GemmArgs& g) {
 
 template <bool GEN, int C>
 hipError_t launch_f32_cfg(const GemmArgs& g);
+template <int C>
+hipError_t launch_i8_cfg(const GemmArgs& g);
+
+int64_t splitk8_slices(const GemmArgs& g) {
+    const int64_t ks =
+        splitk_slice(g.K, round_slices(ceil_div(g.M, 256) * ceil_div(g.N, 256)), 128);
+    return ceil_div(g.K, ks);
+}
+
+int64_t splitk8_workspace_bytes(const GemmArgs& g) {
+    const int64_t s = splitk8_slices(g);
+    if (s < 2 || g.M * g.N > (int64_t(1) << 30)) return 0;
+    return s * g.M * g.N * 4;
+}
+
+hipError_t launch_splitk8(const GemmArgs& g) {
+    const int64_t S = splitk8_slices(g), need = splitk8_workspace_bytes(g);
+    if (need == 0 || S > 16 || g.ws == nullptr ||
+        (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 || g.ws_bytes < need)
+        return hipErrorInvalidValue;
+    // the slices run on the interleaved direct kernel only (K whole 16-byte
+    // chunks); other operands take the ordinary selection instead
+    if (!direct_ok(g, 16, true, 16) || g.K % 16 != 0) return launch_mfma_i8(g, 3);
+    GemmArgs p = g;
+    p.splitk = static_cast<int>(S);
+    p.out = Epi{g.ws, g.N, 1.0f, 0.0f, 4};  // INT32 slice sums, leading dimension N
+    hipError_t e = launch_i8_cfg<6>(p);
+    if (e != hipSuccess) return e;
+    const int32_t* part = static_cast<const int32_t*>(g.ws);
+    const dim3 grid(static_cast<unsigned>(ceil_div(ceil_div(g.M * g.N, 4), kThreads)));
+    const int s = static_cast<int>(S);
+    if (S <= 4)
+        return launch_kernel(g, splitk_reduce_i32<4>, grid, dim3(kThreads), part, s, g.M, g.N,
+                             g.out);
+    if (S <= 8)
+        return launch_kernel(g, splitk_reduce_i32<8>, grid, dim3(kThreads), part, s, g.M, g.N,
+                             g.out);
+    return launch_kernel(g, splitk_reduce_i32<16>, grid, dim3(kThreads), part, s, g.M, g.N,
+                         g.out);
+}
 
 int64_t splitk32_slices(const GemmArgs& g) {
     const int64_t ks = splitk_slice(g.K, round_slices(ceil_div(g.M, 64) * ceil_div(g.N, 64)));

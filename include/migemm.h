@@ -34,12 +34,13 @@
  * the direct-staged kernel cannot read in place (rows not 16-byte aligned in
  * whole 16-byte chunks, K or a k-row image side not a multiple of 8) or reads
  * slowly (k-contiguous rows that do not start on 128-byte lines) are, for
- * large products, best first copied into zero-padded k-contiguous images;
- * and FP32, FP16 and BF16 products whose M x N is a few tiles beside a long K
- * are best summed as slices of K whose FP32 sums are then added.  Both paths need
- * device scratch memory, which the caller lends to migemm_gemm_ws (its size
- * from migemm_workspace_size).  The other entry points lend none, and such
- * products then run in place: same result rules, lower speed.
+ * large products, best first copied into zero-padded k-contiguous images (so
+ * are INT8 operands the direct kernels cannot read); and products whose M x N
+ * is a few tiles beside a long K are best summed as slices of K whose sums are
+ * then added.  Both paths need device scratch memory, which the caller lends to
+ * migemm_gemm_ws (its size from migemm_workspace_size).  The other entry points
+ * lend none, and such products then run in place: same result rules, lower
+ * speed.
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Work is enqueued asynchronously on it; no entry point waits on the
@@ -212,12 +213,14 @@ int migemm_gemm_ex_variant(int variant, int config, int op_a, int op_b,
  * operands the direct-staged kernel cannot read in place are copied into
  * zero-padded k-contiguous images there (the padding adds only exact zero
  * terms to each sum, page "CUDA-Practice 09", the definition of the
- * row-major product), and products of few tiles with a long K (FP16/BF16:
+ * row-major product), INT8 operands off 16-byte boundaries or with K not a
+ * multiple of 16 likewise, and products of few tiles with a long K (FP16/BF16:
  * fewer than 256 tiles of 128 x 128, K at least 6144 and 4 max(M, N); FP32: at
- * most 128 tiles of 64 x 64, K at least 512) keep there the FP32 sums of 2 to
- * 16 slices of K (slices x M x N x 4 bytes), which a second kernel adds in
- * slice order, so the result does not depend on timing; a smaller, misaligned
- * or NULL workspace is not used and
+ * most 128 tiles of 64 x 64, K at least 512; INT8: at most 64 tiles of
+ * 256 x 256, K at least 8192) keep there the FP32 (INT32) sums of 2 to 16
+ * slices of K (slices x M x N x 4 bytes), which a second kernel adds in slice
+ * order, so the result does not depend on timing; a smaller, misaligned or
+ * NULL workspace is not used and
  * the call runs a configuration that needs none.  The selection depends on
  * whether a usable workspace was lent.  Negative workspace_bytes is
  * MIGEMM_ERR_INVALID_ARG; otherwise the rules of migemm_gemm_ex apply.

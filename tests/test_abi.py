@@ -379,6 +379,27 @@ def test_selection_packs_unaligned_int8():
     assert d["launches"] == 2 and d["grid0"] == 512 and d["grid1"] == 256
 
 
+def test_selection_split_k_int8():
+    """INT8 products of at most 64 tiles of 256x256 with K >= 8192 and operands the
+    direct kernels read run as slices of K (configuration 7) when a workspace
+    for their INT32 sums is lent: slices x M x N x 4 bytes, slices of whole
+    128-deep k-tiles."""
+    def sel(M, N, K, ws):
+        d = mg.describe(-1, -1, 0, 0, M, N, K, mg.I8, None, K, None, N, mg.I32, N, ws)
+        return d["config"], d["workspace_bytes"], d["launches"]
+    big = 1 << 40
+    assert sel(1024, 1024, 8192, big) == (7, 16 * 1024 * 1024 * 4, 2)
+    assert sel(512, 512, 8192, big) == (7, 16 * 512 * 512 * 4, 2)
+    assert sel(2048, 2048, 8192, big) == (7, 4 * 2048 * 2048 * 4, 2)
+    assert sel(1024, 1024, 8192, 0)[0] == 4                 # no workspace
+    assert sel(1024, 1024, 4096, big)[0] == 2               # K < 8192
+    assert sel(2304, 2304, 8192, big)[0] == 4               # 81 tiles
+    # K = 8208 (a multiple of 16, not of 128): 13 slices of 640, the last 528 deep
+    d = mg.describe(mg.MFMA_I8, 7, 0, 0, 256, 256, 8208, mg.I8, None, 8208, None, 256, mg.I32,
+                    256, big)
+    assert d["launches"] == 2 and d["grid0"] == 13 and d["workspace_bytes"] == 13 * 256 * 256 * 4
+
+
 def test_selection_split_k_fp32():
     """FP32 products of at most 128 tiles of 64x64 with K >= 512 run as slices of K
     on the direct 64x64 FP32 tile (configuration 12) when a workspace is lent."""

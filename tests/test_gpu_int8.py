@@ -320,3 +320,54 @@ def test_random_cases_exact(block):
         assert intact
         bad = np.flatnonzero(C != want)
         assert bad.size == 0, f"{bad.size} differ; first {np.unravel_index(bad[0], C.shape)}"
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_split_k_exact(ta, tb):
+    """Configuration 7: slices of K (whole 128-deep k-tiles, the last the rest) on
+    the interleaved direct kernel, their INT32 sums added by the integer sum
+    kernel; ragged M and N (whole 16-byte chunks where they are a contiguous
+    side), K a multiple of 16 only (the last slice starts with a partial
+    k-tile), every layout, and with both operands k-contiguous an M x N that is
+    not a multiple of 4; bit-exact."""
+    cases = [(256, 256, 8192), (304, 272, 4112), (272, 144, 2064), (64, 64, 16384)]
+    if not ta and tb:
+        cases.append((257, 129, 2064))
+    for (M, N, K) in cases:
+        A, B = inputs.pair(M, N, K, "i8", "uniform", seed=M + 3 * N + 5 * K + 7 * ta + 11 * tb)
+        want = _want(A, B)
+        lda = ((M if ta else K) + 15) // 16 * 16
+        ldb = ((K if tb else N) + 15) // 16 * 16
+        st, text = mg.migemm_describe_ex(mg.MFMA_I8, 7, int(ta), int(tb), M, N, K, mg.I8, None,
+                                         lda, None, ldb, mg.I32, N, 1 << 40)
+        assert st == mg.OK and mg._parse_description(text)["launches"] == 2, text
+        say(f"i8 split-K {_name(ta, tb)} {M}x{N}x{K} lda={lda} ldb={ldb}")
+        C, intact = run_i8(A, B, mg.MFMA_I8, 7, ta=ta, tb=tb, lda=lda, ldb=ldb, ws=True)
+        assert intact
+        bad = np.flatnonzero(C != want)
+        assert bad.size == 0, f"{bad.size} differ; first {np.unravel_index(bad[0], C.shape)}"
+
+
+def test_split_k_selected_and_extreme():
+    """The selection's split-K on 1024 x 1024 x 8192, and the extreme sums at the
+    K limit split over 16 slices (each slice sum and the total exact)."""
+    A, B = inputs.pair(1024, 1024, 8192, "i8", "uniform", seed=77)
+    st, text = mg.migemm_describe_ex(-1, -1, 0, 0, 1024, 1024, 8192, mg.I8, None, 8192, None,
+                                     1024, mg.I32, 1024, 1 << 40)
+    assert st == mg.OK and mg._parse_description(text)["config"] == 7, text
+    say("i8 split-K 1024x1024x8192 through the selection")
+    C, intact = run_i8(A, B, ws=True)
+    assert intact and np.array_equal(C, _want(A, B))
+    K = (1 << 17) - 16
+    A = torch.full((32, K), -128, dtype=torch.int8)
+    A[16:] = 127
+    B = torch.full((K, 32), -128, dtype=torch.int8)
+    B[:, 16:] = 127
+    want = np.empty((32, 32), dtype=np.int64)
+    want[:16, :16] = 16384 * K
+    want[:16, 16:] = -128 * 127 * K
+    want[16:, :16] = -128 * 127 * K
+    want[16:, 16:] = 127 * 127 * K
+    say("i8 split-K extremes K=131056")
+    C, intact = run_i8(A, B, mg.MFMA_I8, 7, ws=True)
+    assert intact and np.array_equal(C, want)
