@@ -68,8 +68,9 @@ struct GemmArgs {
     // as B^T A^T).
     bool trans_c = false;
     // Split-K (direct configurations with flag bit 7 only): the launch runs
-    // `splitk` slices of K (splitk_slice), slice y writing its plain FP32 sums to
-    // the y-th M x N block of out.C.  0 or 1: one ordinary launch.
+    // `splitk` slices of K (splitk_slice), slice y writing its plain sums (FP32,
+    // INT32 for 8-bit inputs) to the y-th M x N block of out.C.  0 or 1: one
+    // ordinary launch.
     int splitk = 0;
     // True unless the output step is the plain FP32 overwrite.
     bool general() const { return !(out.alpha == 1.0f && out.beta == 0.0f && out.c_dtype == 0); }

@@ -19,7 +19,9 @@
 // schedule and the 16-byte fragments carry over; row-major B is transposed by
 // 8-bit transposing LDS reads.  It needs whole 256 x 256 tiles, K a multiple of
 // 128, 16-byte aligned operands and leading dimensions in whole 16-byte chunks;
-// other shapes run configuration 0.
+// other shapes run configuration 0.  Configuration 6 is the interleaved direct
+// kernel on 8-bit elements (any M and N, K a multiple of 16), 5 copies operands
+// the direct kernels cannot read (pack.hip), and 7 sums slices of K (splitk.hip).
 #include "common.hpp"
 
 namespace migemm {

@@ -10,10 +10,11 @@
 // name, to the kernels.  No allocating call is made.
 //
 // Calls on one GPU share its array, which keeps the last call's contents: its
-// users (the packed FP16/BF16 path, and split-K, whose slices each write their
-// whole M x N block of sums before the sum kernel reads them) overwrite every
-// byte they read, zero padding included, so nothing needs clearing.  Calls that overlap in time on
-// one GPU (two streams, or two host threads) race on the array.
+// users (the copies of FP16/BF16 and INT8 operands, which write whole rows,
+// zero padding included, and split-K, whose slices each write their whole
+// M x N block of sums before the sum kernel reads them) overwrite every byte
+// they read, so nothing needs clearing.  Calls that overlap in time on one GPU
+// (two streams, or two host threads) race on the array.
 #include <mutex>
 
 #include "common.hpp"

@@ -1,5 +1,6 @@
-// pack.hip -- FP16/BF16 products whose operands the direct-staged kernel cannot
-// read in place, or reads slowly: a pointer off a 16-byte boundary, a leading
+// pack.hip -- FP16/BF16 products (and, at the end of this file, INT8 ones)
+// whose operands the direct-staged kernel cannot read in place, or reads
+// slowly: a pointer off a 16-byte boundary, a leading
 // dimension that is not a whole number of 16-byte chunks, a contiguous side (K
 // of a row-major A or of B given transposed, N of row-major B, M of A given
 // transposed) that ends inside a chunk, or k-contiguous rows that do not start

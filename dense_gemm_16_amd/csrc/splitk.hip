@@ -1,5 +1,5 @@
-// splitk.hip -- FP16/BF16 products whose M x N is small beside K: the sum over
-// k split into slices.
+// splitk.hip -- products whose M x N is small beside K: the sum over k split
+// into slices (FP16/BF16, FP32 and INT8).
 //
 // C = A x B (page "CUDA-Practice 09", the definition of the row-major product)
 // is, element by element, the sum over k of A[i][k] B[k][j]; the sum splits
@@ -18,9 +18,12 @@
 // against 69 us with the slices spread over all eight XCDs and 217 us for the
 // 64x64 tile without slices).
 //
-// Used where a workspace is lent (slices x M x N x 4 bytes), the operands suit
-// the direct kernel, K is at least 6144 and 4 max(M, N), and the 128x128 tile
-// would not fill a round of 256 workgroups.
+// FP16/BF16 split-K is used where a workspace is lent (slices x M x N x 4
+// bytes), the operands suit the direct kernel, K is at least 6144 and
+// 4 max(M, N), and the 128x128 tile would not fill a round of 256 workgroups.
+// FP32 products slice on the 64x64 FP32 tile and INT8 ones on the interleaved
+// 256x256 INT8 tile (INT32 sums, added exactly); their selection rules sit
+// with the selection table.
 #include "mfma16_configs.hpp"
 #include "mfma16_direct.hpp"
 
