@@ -1,7 +1,9 @@
 """Calls captured into a HIP graph (torch.cuda.CUDAGraph on a side stream) and
 replayed: the library only launches kernels on the caller's stream (no
 allocation, no host wait, no memset), so a captured call must produce, on every
-replay, exactly what the same call produces eagerly.  Between replays C is
+replay, exactly what the same call produces eagerly, also where a call is two
+launches sharing a workspace (copies then the product, slices then their
+sum).  Between replays C is
 reset (to its previous value for an update, else poisoned) by eager work on the
 stream and the program synchronises; each replay's C is compared bit for bit
 with the eager result.  Cases: a plain FP16 product,
@@ -54,6 +56,11 @@ def _case(M, N, K, dtype, alpha=1.0, beta=0.0, c_code=None, ldb=None):
     (1024, 1024, 1024, "f32", 1.0, 0.0, None, None),
     (512, 512, 512, "i8", 1.0, 0.0, None, None),
     (1000, 1032, 520, "bf16", 0.5, -1.25, 2, None),    # general output step, beta != 0
+    (512, 512, 16384, "bf16", 1.0, 0.0, None, None),   # split-K: slices, then their sum
+    (512, 384, 8192, "f16", -0.5, 0.75, 1, None),      # split-K with the general output step
+    (512, 512, 4096, "f32", 1.0, 0.0, None, None),     # FP32 split-K
+    (1000, 1000, 1000, "i8", 1.0, 0.0, None, None),    # INT8 copies, then the 64x64 tile
+    (512, 512, 8192, "i8", 1.0, 0.0, None, None),      # INT8 split-K
 ])
 def test_graph_replays_match_eager(M, N, K, dtype, alpha, beta, c_code, ldb):
     say(f"graph {M}x{N}x{K} {dtype} alpha={alpha} beta={beta} c_code={c_code} ldb={ldb}")
