@@ -152,6 +152,9 @@ WORKLOADS = {w.name: w for w in [
     # and over a 2 x 4 grid of (rows, columns) (timed as extra lines)
     Workload("s8-bf16-1024x8192x8192", 1024, 8192, 8192, "bf16", "normal", 6),
     Workload("s2x4-bf16-4096x2048x8192", 4096, 2048, 8192, "bf16", "normal", 7),
-    # a long K on a few tiles of C (summed as slices of K; timed as an extra line)
+    # a long K on a few tiles of C (summed as slices of K; timed as extra lines)
     Workload("lk-bf16-512x512x65536", 512, 512, 65536, "bf16", "normal", 8),
+    Workload("lk-f32-512x512x16384", 512, 512, 16384, "f32", "uniform", 9),
+    # INT8 rows of 1000 bytes, off 16-byte boundaries (copied first; an extra line)
+    Workload("i8u-1000", 1000, 1000, 1000, "i8", "uniform", 10, exact=True),
 ]}
