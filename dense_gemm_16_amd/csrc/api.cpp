@@ -229,8 +229,17 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
                             splitk32_workspace_bytes(g) > 0 && g.ws != nullptr &&
                             reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
                             g.ws_bytes >= splitk32_workspace_bytes(g);
+        // operands it cannot read: copied first (configuration 13) once the
+        // product is large enough and a workspace is lent
+        const double work = static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K);
+        const bool pack = !direct && work >= kPackMinWork &&
+                          ceil_div(K, 32) * 32 < (int64_t(1) << 21) && g.ws != nullptr &&
+                          reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
+                          g.ws_bytes >= packed32_workspace_bytes(g);
         if (direct)
             config = tiles(128, 128) >= 256 ? 10 : splitk ? 12 : 8;
+        else if (pack)
+            config = 13;
         else
             config = tiles(128, 128) >= 256 ? 0 : 2;
         return;
@@ -342,6 +351,7 @@ hipError_t launch(const GemmArgs& g, int variant, int config) {
 int64_t config_workspace_bytes(const GemmArgs& g, int variant, int config) {
     if (g.M == 0 || g.N == 0 || g.K == 0) return 0;
     if (variant == MIGEMM_REGTILE_MFMA && config == 12) return splitk32_workspace_bytes(g);
+    if (variant == MIGEMM_REGTILE_MFMA && config == 13) return packed32_workspace_bytes(g);
     if (variant == MIGEMM_MFMA_I8 && config == 5) return packed8_workspace_bytes(g);
     if (variant == MIGEMM_MFMA_I8 && config == 7) return splitk8_workspace_bytes(g);
     if (variant != MIGEMM_MFMA16 || (config != 11 && config != 12 && config != 17)) return 0;

@@ -255,6 +255,9 @@ int i8_select(int64_t M, int64_t N, int64_t K, bool direct, bool direct16);
 // the product of the copies (pack.hip; configuration 5 of the INT8 variant).
 int64_t packed8_workspace_bytes(const GemmArgs& a);
 hipError_t launch_packed8(const GemmArgs& a);
+// The same for FP32 operands (configuration 13 of the FP32 matrix-core variant).
+int64_t packed32_workspace_bytes(const GemmArgs& a);
+hipError_t launch_packed32(const GemmArgs& a);
 // FP16/BF16 products as slices of K on the 128x128 or 256x256 direct tile
 // into FP32 partial sums in the caller's workspace, then a reduction that sums
 // them in slice order and applies the output step (splitk.hip).

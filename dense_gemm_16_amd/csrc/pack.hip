@@ -188,8 +188,9 @@ hipError_t launch_pack(const GemmArgs& g, const PackJob& j0, const PackJob& j1, 
     const int64_t tiles = j0.tiles + j1.tiles;
     if (tiles == 0) return hipSuccess;
     const unsigned grid = static_cast<unsigned>(tiles < 65536 ? tiles : 65536);
-    return es == 1 ? launch_kernel(g, pack_kernel<uint8_t>, dim3(grid), dim3(256), j0, j1)
-                   : launch_kernel(g, pack_kernel<uint16_t>, dim3(grid), dim3(256), j0, j1);
+    if (es == 1) return launch_kernel(g, pack_kernel<uint8_t>, dim3(grid), dim3(256), j0, j1);
+    if (es == 4) return launch_kernel(g, pack_kernel<uint32_t>, dim3(grid), dim3(256), j0, j1);
+    return launch_kernel(g, pack_kernel<uint16_t>, dim3(grid), dim3(256), j0, j1);
 }
 
 // The direct configuration that packed configuration pc (11 or 12) runs.  11:
@@ -344,6 +345,78 @@ hipError_t launch_packed8(const GemmArgs& g) {
         p.pad_b = true;
     }
     return launch_mfma_i8(p, i8_select(p.M, p.N, p.K, true, true));
+}
+
+// FP32 operands the direct kernel cannot read (a pointer off a 16-byte
+// boundary, a leading dimension that is not a whole number of 4-element chunks,
+// a contiguous side that ends inside a chunk) are read element by element by
+// the register-staged FP32 kernels: 2049^3 took 399 us against 124 for 2048^3,
+// 1023^3 45.3 against 20.4.  They are copied here like the 16-bit and 8-bit
+// ones (4-byte elements, k-contiguous images with K zero-filled to a multiple
+// of the 32-deep FP32 k-tile, rows on 128-byte lines), then the direct FP32
+// kernel multiplies the copies: the 128x128 tile (configuration 10) from a
+// round of its tiles, else the 64x64 one (8).  An operand the direct kernel
+// reads in place (aligned, whole chunks, K a multiple of 4) is left in place.
+namespace {
+
+struct Plan32 {
+    bool a_in, b_in;
+    int64_t kp, a_bytes, b_bytes;
+};
+
+Plan32 plan32(const GemmArgs& g) {
+    Plan32 p;
+    const bool k4 = g.K % 4 == 0;
+    p.kp = round_up(g.K, 32);
+    p.a_in = k4 && aligned16(g.A) && g.lda % 4 == 0 && (!g.ta || g.M % 4 == 0);
+    p.b_in = k4 && aligned16(g.B) && g.ldb % 4 == 0 && (g.tb || g.N % 4 == 0);
+    p.a_bytes = p.a_in ? 0 : round_up(g.M * p.kp * 4, kWorkspaceAlign);
+    p.b_bytes = p.b_in ? 0 : g.N * p.kp * 4;
+    return p;
+}
+
+int inner32(const GemmArgs& g) {
+    return ceil_div(g.M, 128) * ceil_div(g.N, 128) >= 256 ? 10 : 8;
+}
+
+}  // namespace
+
+int64_t packed32_workspace_bytes(const GemmArgs& g) {
+    const Plan32 p = plan32(g);
+    return p.a_bytes + p.b_bytes;
+}
+
+hipError_t launch_packed32(const GemmArgs& g) {
+    const Plan32 pl = plan32(g);
+    const int64_t need = pl.a_bytes + pl.b_bytes;
+    if (need == 0) return launch_regtile_mfma(g, inner32(g));
+    if (g.ws == nullptr || (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 ||
+        g.ws_bytes < need)
+        return launch_regtile_mfma(g, inner32(g) == 10 ? 0 : 2);  // register-staged, in place
+    char* const wa = static_cast<char*>(g.ws);
+    char* const wb = wa + pl.a_bytes;
+    const PackJob none = make_job(nullptr, 4, 0, 0, false, nullptr, 4);
+    const PackJob ja = pl.a_in ? none : make_job(g.A, g.lda, g.M, g.K, g.ta, wa, 4);
+    const PackJob jb = pl.b_in ? none : make_job(g.B, g.ldb, g.N, g.K, !g.tb, wb, 4);
+    hipError_t e = launch_pack(g, ja, jb, 4);
+    if (e != hipSuccess) return e;
+    GemmArgs p = g;
+    // Both operands copies: whole k-tiles of zero-filled K.  One left in place:
+    // the call's K (the direct kernel zero-fills a partial last k-tile).
+    if (!pl.a_in && !pl.b_in) p.K = pl.kp;
+    if (!pl.a_in) {
+        p.ta = false;
+        p.A = wa;
+        p.lda = ja.ldd;
+        p.pad_a = true;
+    }
+    if (!pl.b_in) {
+        p.tb = true;
+        p.B = wb;
+        p.ldb = jb.ldd;
+        p.pad_b = true;
+    }
+    return launch_regtile_mfma(p, inner32(p));
 }
 
 }  // namespace migemm

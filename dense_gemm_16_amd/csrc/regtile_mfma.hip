@@ -34,7 +34,8 @@ const char* const kNames[] = {"128x128x32 4w 16x16x4", "128x128x32 4w 32x32x2",
                               "direct 128x128x32 8w 16x16x4 gm4 s4 ilv ntC",
                               "direct 128x64x32 8w 16x16x4 s4 ilv ntC",
                               "split-K: slices of K on config 8 into FP32 partials in the "
-                              "workspace, then their sum"};
+                              "workspace, then their sum",
+                              "packed: aligned zero-padded copies, then config 10 or 8"};
 constexpr int kCount = sizeof(kNames) / sizeof(kNames[0]);
 
 template <bool GEN>
@@ -74,6 +75,7 @@ hipError_t launch_cfg(const GemmArgs& g, int config) {
 // the 64x64 tile after the 128x128 one, and are left in place after the 64x64
 // one (a tail on the same tile costs what the extra round does).
 hipError_t launch_regtile_mfma(const GemmArgs& g, int config) {
+    if (config == 13) return launch_packed32(g);
     if (config == 12) {
         // without a usable workspace the ordinary 64x64 launch
         const int64_t need = splitk32_workspace_bytes(g);

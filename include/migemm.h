@@ -214,7 +214,8 @@ int migemm_gemm_ex_variant(int variant, int config, int op_a, int op_b,
  * zero-padded k-contiguous images there (the padding adds only exact zero
  * terms to each sum, page "CUDA-Practice 09", the definition of the
  * row-major product), INT8 operands off 16-byte boundaries or with K not a
- * multiple of 16 likewise, and products of few tiles with a long K (FP16/BF16:
+ * multiple of 16 likewise, FP32 ones off 16-byte boundaries or with K not a
+ * multiple of 4 (M x N x K at least 2^27) likewise, and products of few tiles with a long K (FP16/BF16:
  * fewer than 256 tiles of 128 x 128, K at least 6144 and 4 max(M, N); FP32: at
  * most 128 tiles of 64 x 64, K at least 512; INT8: at most 64 tiles of
  * 256 x 256, K at least 8192) keep there the FP32 (INT32) sums of 2 to 16

@@ -400,6 +400,20 @@ def test_selection_split_k_int8():
     assert d["launches"] == 2 and d["grid0"] == 13 and d["workspace_bytes"] == 13 * 256 * 256 * 4
 
 
+def test_selection_packs_unaligned_fp32():
+    """FP32 operands the direct kernel cannot read go to configuration 13 (copies)
+    once M N K >= 2^27 and a workspace is lent: each copied operand's rows x K
+    rounded up to 32 x 4 bytes, A' first rounded up to 256 bytes."""
+    big = 1 << 40
+    assert _selected(2049, 2049, 2049, mg.F32, 2049, 2049, big) == ("regtile_mfma", 13)
+    assert _selected(2049, 2049, 2049, mg.F32, 2049, 2049, 0) == ("regtile_mfma", 0)
+    assert _selected(400, 400, 401, mg.F32, 401, 400, big) == ("regtile_mfma", 2)   # < 2^27
+    ws = lambda M, N, K, lda, ldb: mg.migemm_workspace_size(-1, -1, 0, 0, M, N, K, mg.F32, None,
+                                                            lda, None, ldb)
+    assert ws(2049, 2049, 2049, 2049, 2049) == (mg.OK, 2 * 2049 * 2080 * 4 + 128)
+    assert ws(4096, 4096, 4096, 4097, 4097) == (mg.OK, 2 * 4096 * 4096 * 4)
+
+
 def test_selection_split_k_fp32():
     """FP32 products of at most 128 tiles of 64x64 with K >= 512 run as slices of K
     on the direct 64x64 FP32 tile (configuration 12) when a workspace is lent."""
@@ -452,7 +466,10 @@ def test_workspace_size():
     # K a multiple of 64 and A aligned: only B is copied
     assert ws(-1, -1, 0, 0, 4096, 4096, 4096, 2, None, 4096, None, 4097) == (mg.OK, 4096 * 4096 * 2)
     # aligned, FP32, INT8, small, empty: none
-    for a in [(8192, 8192, 8192, 2, 8192, 8192), (1024, 1024, 1024, 0, 1025, 1024),
+    # FP32 with A's rows not in whole 16-byte chunks: A copied, K rounded up to 32
+    assert ws(-1, -1, 0, 0, 1024, 1024, 1024, 0, None, 1025, None, 1024) == \
+        (mg.OK, 1024 * 1024 * 4)
+    for a in [(8192, 8192, 8192, 2, 8192, 8192), (1024, 1024, 1024, 0, 1024, 1024),
               (8192, 8192, 8192, 3, 8192, 8192), (100, 100, 100, 1, 101, 100),
               (0, 4096, 4096, 1, 4097, 4096), (4096, 4096, 0, 1, 1, 4097)]:
         M, N, K, dt, lda, ldb = a

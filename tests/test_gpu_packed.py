@@ -303,3 +303,49 @@ def test_split_tail_on_the_skinny_kernel():
                                          2056 if ta else 128, None, 2048, 0, 2048, 0)
         d = mg._parse_description(text)
         assert st == mg.OK and d["launches"] == 2 and d["block1"] == block, text
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_packed_fp32_every_layout(ta, tb):
+    """FP32 configuration 13: operands the direct FP32 kernel cannot read (odd
+    leading dimensions, element offsets of 1 and 3, K not a multiple of 4) are
+    copied into aligned images with K zero-filled to a multiple of 32, then the
+    direct FP32 kernel runs on the copies; from K = 1 to past several k-tiles,
+    ragged M and N, the general output step into BF16 C."""
+    v = mg.REGTILE_MFMA
+    for (M, N, K, pad, off) in [(1, 1, 1, 0, 0), (7, 9, 5, 0, 0), (203, 170, 301, 3, 1),
+                                (300, 264, 200, 5, 3), (257, 513, 130, 0, 0)]:
+        A, B = inputs.pair(M, N, K, "f32", "uniform", seed=M + 2 * N + 3 * K + 5 * ta + 7 * tb)
+        ref = oracle_ref(A, B, "f32")
+        lda = (M if ta else K) + pad
+        ldb = (K if tb else N) + pad
+        say(f"packed fp32 {_name(ta, tb)} {M}x{N}x{K} lda={lda} ldb={ldb} off={off}")
+        C, buf, mask = run_gemm_ex(A, B, "f32", 1.0, 0.0, 0, None, variant=v, config=13, ta=ta,
+                                   tb=tb, lda=lda, ldb=ldb, a_off=off, b_off=off)
+        check_ex(C, A, B, "f32", 1.0, 0.0, 0, None, ref=ref)
+        assert padding_untouched(buf, mask)
+    A, B = inputs.pair(300, 264, 203, "f32", "uniform", seed=17 + ta)
+    old = (torch.rand((300, 264), generator=torch.Generator().manual_seed(3)) - 0.5).to(
+        torch.bfloat16)
+    say(f"packed fp32 {_name(ta, tb)} general output")
+    C, buf, mask = run_gemm_ex(A, B, "f32", 0.5, -1.0, 2, old, variant=v, config=13, ta=ta, tb=tb,
+                               lda=(300 if ta else 203) + 1, ldb=(203 if tb else 264) + 1,
+                               ldc=264 + 3)
+    check_ex(C, A, B, "f32", 0.5, -1.0, 2, old)
+    assert padding_untouched(buf, mask)
+
+
+def test_packed_fp32_selected():
+    """The selection copies FP32 operands the direct kernel cannot read once the
+    product is large enough and a workspace is lent: 2049^3 (then the 128x128
+    tile on the whole tiles and the skinny kernel on the last row and column)
+    and 1023^3 (then the 64x64 tile)."""
+    for (M, N, K) in [(2049, 2049, 2049), (1023, 1023, 1023)]:
+        st, text = mg.migemm_describe_ex(-1, -1, 0, 0, M, N, K, mg.F32, None, K, None, N, 0, N,
+                                         1 << 40)
+        assert st == mg.OK and mg._parse_description(text)["config"] == 13, text
+        A, B = inputs.pair(M, N, K, "f32", "uniform", seed=M)
+        say(f"packed fp32 {M}x{N}x{K} through the selection")
+        C, buf, mask = run_gemm_ex(A, B, "f32", 1.0, 0.0, 0, None)
+        check_ex(C, A, B, "f32", 1.0, 0.0, 0, None)
+        assert padding_untouched(buf, mask)
