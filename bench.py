@@ -60,7 +60,7 @@ SETTLE_MS = 200.0
 GRAPH_TIMED = ("c0-f16-256", "c1-f32-1024", "c2-f16-1024")
 EXTRA = ["c0-f16-256", "c1-f32-1024", "c1-f32-1024-int", "c2-f16-1024", "c3-f16-2048", "c3-bf16-2048",
          "c3r-f16-2050x2047x2056", "c4f-f32-4096", "s8-bf16-1024x8192x8192",
-         "s2x4-bf16-4096x2048x8192", "lk-bf16-512x512x65536", "lk-f32-512x512x16384", "i8u-1000"]
+         "s2x4-bf16-4096x2048x8192", "lk-bf16-512x512x65536", "lk-f32-512x512x16384", "i8u-1000", "f32u-2049"]
 
 
 def log(msg):

@@ -157,4 +157,6 @@ WORKLOADS = {w.name: w for w in [
     Workload("lk-f32-512x512x16384", 512, 512, 16384, "f32", "uniform", 9),
     # INT8 rows of 1000 bytes, off 16-byte boundaries (copied first; an extra line)
     Workload("i8u-1000", 1000, 1000, 1000, "i8", "uniform", 10, exact=True),
+    # FP32 rows of 2049 elements, off 16-byte boundaries (copied first; an extra line)
+    Workload("f32u-2049", 2049, 2049, 2049, "f32", "uniform", 15),
 ]}

@@ -8,7 +8,8 @@ reset (to its previous value for an update, else poisoned) by eager work on the
 stream and the program synchronises; each replay's C is compared bit for bit
 with the eager result.  Cases: a plain FP16 product,
 the packed path with its copy launch and workspace, a split product (whole
-tiles, then the skinny tail), FP32, INT8, and the general output step with
+tiles, then the skinny tail), FP32 (in place, in slices of K, and copied),
+INT8, and the general output step with
 beta != 0 into BF16 C (so a replay that reads a stale C would show).
 """
 import pytest
@@ -61,6 +62,8 @@ def _case(M, N, K, dtype, alpha=1.0, beta=0.0, c_code=None, ldb=None):
     (512, 512, 4096, "f32", 1.0, 0.0, None, None),     # FP32 split-K
     (1000, 1000, 1000, "i8", 1.0, 0.0, None, None),    # INT8 copies, then the 64x64 tile
     (512, 512, 8192, "i8", 1.0, 0.0, None, None),      # INT8 split-K
+    (1023, 1023, 1023, "f32", 1.0, 0.0, None, None),   # FP32 copies, then the 64x64 tile
+    (2049, 2049, 2049, "f32", 0.5, -1.0, 2, None),     # FP32 copies, 128x128, general output
 ])
 def test_graph_replays_match_eager(M, N, K, dtype, alpha, beta, c_code, ldb):
     say(f"graph {M}x{N}x{K} {dtype} alpha={alpha} beta={beta} c_code={c_code} ldb={ldb}")

@@ -1,7 +1,7 @@
 """GPU parity on the benchmark workloads, in the launch configuration the benchmark
 times (migemm_gemm's own selection), against the CPU oracle.
 
-Workloads up to 2050 x 2047 x 2056, and the long-K and unaligned INT8 ones, are compared in full here; the 8192^3,
+Workloads up to 2050 x 2047 x 2056, and the long-K and unaligned INT8 and FP32 ones, are compared in full here; the 8192^3,
 4096^3 and one-GPU-share workloads in test_gpu_fullsize.py, also in full.
 """
 import numpy as np
@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 FULL = ["c0-f16-256", "c1-f32-1024", "c1-f32-1024-int", "c2-f16-1024", "c3-f16-2048",
         "c3-bf16-2048", "c3r-f16-2050x2047x2056", "lk-bf16-512x512x65536",
-        "lk-f32-512x512x16384", "i8u-1000"]
+        "lk-f32-512x512x16384", "i8u-1000", "f32u-2049"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -73,6 +73,24 @@ def test_noalloc_split_k_twice():
         check_ex(C_na, A, B, dtype, 1.0, 0.0, 0, None)
 
 
+def test_noalloc_fp32_copies_twice():
+    """FP32 operands the direct kernel cannot read are copied into the scratch
+    array: 2049^3, then the smaller 1023^3, each matching the workspace entry
+    point bit for bit."""
+    first = None
+    for (M, N, K, seed) in [(2049, 2049, 2049, 10), (1023, 1023, 1023, 11)]:
+        st, text = mg.migemm_describe_ex(-1, -1, 0, 0, M, N, K, mg.F32, None, K, None, N,
+                                         0, N, mg.NOALLOC_SCRATCH_BYTES)
+        assert st == mg.OK and mg._parse_description(text)["config"] == 13
+        A, B, need, C_ws, C_na = _both(M, N, K, "f32", N, seed)
+        assert 0 < need <= mg.NOALLOC_SCRATCH_BYTES
+        if first is not None:
+            assert need < first, "the second product is the smaller one"
+        first = need
+        assert torch.equal(C_ws.view(torch.int32), C_na.view(torch.int32))
+        check_ex(C_na, A, B, "f32", 1.0, 0.0, 0, None)
+
+
 def test_noalloc_without_scratch_need():
     A, B, need, C_ws, C_na = _both(512, 512, 512, "bf16", 512, 7)
     assert need == 0
