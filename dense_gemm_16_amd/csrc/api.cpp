@@ -237,7 +237,7 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
                           reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
                           g.ws_bytes >= packed32_workspace_bytes(g);
         if (direct)
-            config = tiles(128, 128) >= 256 ? 10 : splitk ? 12 : 8;
+            config = f32_direct_tile(M, N) == 10 ? 10 : splitk ? 12 : 8;
         else if (pack)
             config = 13;
         else

@@ -301,6 +301,9 @@ struct SplitPlan {
 };
 // Tiles of bm x bn on the 256 CUs; tails wider than max_tail are not split off.
 SplitPlan plan_split(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t max_tail);
+// The direct FP32 tile for an M x N product: 10 (128x128) or 8 (64x64), whichever
+// leaves fewer rounds of workgroups per CU (ties to the larger tile).
+int f32_direct_tile(int64_t M, int64_t N);
 using CfgLauncher = hipError_t (*)(const GemmArgs&, int);
 hipError_t launch_split(const GemmArgs& g, const SplitPlan& p, CfgLauncher head, int head_config,
                         CfgLauncher tail, int tail_config);

@@ -375,9 +375,7 @@ Plan32 plan32(const GemmArgs& g) {
     return p;
 }
 
-int inner32(const GemmArgs& g) {
-    return ceil_div(g.M, 128) * ceil_div(g.N, 128) >= 256 ? 10 : 8;
-}
+int inner32(const GemmArgs& g) { return f32_direct_tile(g.M, g.N); }
 
 }  // namespace
 
@@ -392,7 +390,7 @@ hipError_t launch_packed32(const GemmArgs& g) {
     if (need == 0) return launch_regtile_mfma(g, inner32(g));
     if (g.ws == nullptr || (reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign) != 0 ||
         g.ws_bytes < need)
-        return launch_regtile_mfma(g, inner32(g) == 10 ? 0 : 2);  // register-staged, in place
+        return launch_regtile_mfma(g, ceil_div(g.M, 128) * ceil_div(g.N, 128) >= 256 ? 0 : 2);
     char* const wa = static_cast<char*>(g.ws);
     char* const wb = wa + pl.a_bytes;
     const PackJob none = make_job(nullptr, 4, 0, 0, false, nullptr, 4);

@@ -63,6 +63,20 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t max_t
     return p;
 }
 
+int f32_direct_tile(int64_t M, int64_t N) {
+    // The 128x128 FP32 tile holds its CU alone (128 KiB of LDS); the 64x64 one runs
+    // two workgroups per CU at about the same rate per multiply-add, so one of its
+    // rounds (2 x 256 workgroups) is half the work of a 128x128 round.  The larger
+    // tile is kept when it fills a round and, after the ragged last bands are split
+    // off as the launch will do, needs at most half the smaller tile's rounds.
+    if (ceil_div(M, 128) * ceil_div(N, 128) < kCus) return 8;
+    auto rounds = [&](int64_t t, int64_t max_tail, int64_t slots) {
+        const SplitPlan p = plan_split(M, N, t, t, max_tail);
+        return ceil_div(ceil_div(p.m_main, t) * ceil_div(p.n_main, t), slots);
+    };
+    return 2 * rounds(128, 128, kCus) <= rounds(64, 16, 2 * kCus) ? 10 : 8;
+}
+
 hipError_t launch_split(const GemmArgs& g, const SplitPlan& p, CfgLauncher head, int head_config,
                         CfgLauncher tail, int tail_config) {
     const int64_t ea = elem_bytes(g.dtype), ec = c_bytes(g.out.c_dtype);

@@ -437,6 +437,13 @@ def test_fp32_selection():
     # direct-staged FP32: 64x64 tiles below a round of 128x128 tiles, 128x128 above
     assert sel(1024, 1024, 1024, 1024, 1024) == (mg.OK, mg.REGTILE_MFMA, 8)
     assert sel(4096, 4096, 4096, 4096, 4096) == (mg.OK, mg.REGTILE_MFMA, 10)
+    # 128x128 only where it needs at most half the rounds of the 64x64 tile (two
+    # workgroups per CU): 3008^3 is 3 rounds of 128x128 against 5 of 64x64; 2500^3
+    # 2 against 3 (after the 4-wide last band is split off); 6000^3 9 against 18
+    assert sel(3008, 3008, 3008, 3008, 3008) == (mg.OK, mg.REGTILE_MFMA, 8)
+    assert sel(2500, 2500, 2500, 2500, 2500) == (mg.OK, mg.REGTILE_MFMA, 8)
+    assert sel(6000, 6000, 6000, 6000, 6000) == (mg.OK, mg.REGTILE_MFMA, 10)
+    assert sel(2048, 2048, 2048, 2048, 2048) == (mg.OK, mg.REGTILE_MFMA, 10)
     # K a multiple of 4 (not of the 32-deep k-tile): still direct
     assert sel(1024, 1024, 1000, 1000, 1024) == (mg.OK, mg.REGTILE_MFMA, 8)
     # rows not in whole 16-byte chunks, K not a multiple of 4, N not a multiple of 4:
