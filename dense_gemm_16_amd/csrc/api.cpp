@@ -272,7 +272,23 @@ void select(const GemmArgs& g, bool aligned, int& variant, int& config) {
                         g.ws != nullptr &&
                         reinterpret_cast<uintptr_t>(g.ws) % kWorkspaceAlign == 0 &&
                         g.ws_bytes >= splitk16_workspace_bytes(g);
-    if (direct && ktiles && tiles(256, 256) >= 256 && whole256)
+    // Whole tiles below one round of 256x256 but at least one of 128x128: the
+    // tile whose rounds of workgroups (one per CU) cost least, from each tile's
+    // time per full round per unit of K (ns: 256x256 ping-pong 21.4 at 8192^3,
+    // 128x256 ping-pong 13.4 at 1024x8192x8192, 128x128 9.7 at 2048^3)
+    int small_whole = 0;
+    if (direct && ktiles && tiles(256, 256) < 256 && tiles(128, 128) >= 256 &&
+        M % 128 == 0 && N % 256 == 0) {
+        auto cost = [&](int64_t bm, int64_t bn, double ns) {
+            return static_cast<double>(ceil_div(tiles(bm, bn), 256)) * ns;
+        };
+        const double c7 = cost(128, 128, 9.7), c15 = cost(128, 256, 13.4);
+        const double c14 = whole256 ? cost(256, 256, 21.4) : 1e300;
+        small_whole = c14 <= c15 && c14 <= c7 ? 14 : c15 <= c7 ? 15 : 7;
+    }
+    if (small_whole)
+        config = small_whole;
+    else if (direct && ktiles && tiles(256, 256) >= 256 && whole256)
         config = 14;  // direct 256x256x64, ping-pong wave groups (whole tiles only)
     else if (direct && tiles(256, 256) >= 256)
         config = 10;  // direct 256x256x64, 8 waves, 16x16x32, AGPR accumulators, early loads

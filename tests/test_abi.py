@@ -432,6 +432,20 @@ def test_selection_split_k_fp32():
     assert d["launches"] == 2 and d["grid0"] == 96 * 2 and d["block0"] == 512
 
 
+def test_selection_whole_tiles_below_a_round():
+    """Whole tiles below one round of 256x256: rounds x time per round (256x256
+    21.4, 128x256 13.4, 128x128 9.7 ns per unit of K) picks the tile."""
+    sel = lambda M, N: mg.migemm_select(M, N, 4096, mg.BF16, None, 4096, None, N, None, N)[2]
+    assert sel(3072, 3072) == 14   # 1 round of 256x256 (144 tiles) against 2 of 128x256
+    assert sel(3584, 3584) == 14   # 196 tiles: 1 round against 2 of 128x256, 4 of 128x128
+    assert sel(2560, 2560) == 15   # 200 tiles of 128x256: 1 round against 2 of 128x128
+    assert sel(2304, 2304) == 15
+    assert sel(2048, 2048) == 7    # 256 tiles of 128x128: one round
+    assert sel(4096, 4096) == 14   # a round of 256x256 or more: unchanged
+    assert sel(1024, 8192) == 15
+    assert sel(3000, 3000) == 13   # not whole tiles: unchanged
+
+
 def test_fp32_selection():
     sel = lambda M, N, K, lda, ldb: mg.migemm_select(M, N, K, mg.F32, None, lda, None, ldb, None, N)
     # direct-staged FP32: 64x64 tiles below a round of 128x128 tiles, 128x128 above
